@@ -1,0 +1,275 @@
+"""Pins for the CPU oracle: each test checks it against something other than
+itself (library routines, closed forms, brute force, hand-worked fixtures)."""
+import os
+
+import numpy as np
+import pytest
+import torch
+
+import oracle as O
+import workloads
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+
+
+def _read_golden(name):
+    rows = []
+    with open(os.path.join(GOLDEN, name)) as f:
+        for line in f:
+            line = line.strip()
+            if line and not line.startswith("#"):
+                rows.append([p.strip() for p in line.split("|")])
+    return rows
+
+
+# ---------------------------------------------------------------- rounding
+def test_fp32_rounding_matches_numpy():
+    rng = np.random.default_rng(0)
+    x = np.concatenate([rng.standard_normal(20000) * 10.0 ** rng.integers(-40, 38, 20000),
+                        [1 + 2 ** -24, 1 + 3 * 2 ** -24, 2 ** -149 * 1.5, 2 ** -149 * 2.5, 3.5e38, -0.0]])
+    with np.errstate(over="ignore"):
+        ref = x.astype(np.float32).astype(np.float64)
+    np.testing.assert_array_equal(O.fp32(x), ref)
+
+
+def test_fp16_rounding_matches_numpy():
+    rng = np.random.default_rng(1)
+    x = np.concatenate([rng.standard_normal(20000) * 10.0 ** rng.integers(-9, 6, 20000),
+                        [65504.0, 65519.99, 65520.0, 2 ** -24 * 0.5, 2 ** -24 * 1.5, 2 ** -25 * 1.0001,
+                         1 + 2 ** -11, 1 + 3 * 2 ** -11]])
+    with np.errstate(over="ignore"):
+        ref = x.astype(np.float16).astype(np.float64)
+    np.testing.assert_array_equal(O.fp16(x), ref)
+
+
+def test_bf16_rounding_matches_torch():
+    rng = np.random.default_rng(2)
+    x32 = (rng.standard_normal(20000) * 10.0 ** rng.integers(-30, 30, 20000)).astype(np.float32)
+    # exact ties: 1 + 2^-8 and 1 + 3*2^-8 (bf16 has 7 stored fraction bits)
+    x32 = np.concatenate([x32, np.array([1 + 2 ** -8, 1 + 3 * 2 ** -8, -(1 + 2 ** -8)], np.float32)])
+    ref = torch.from_numpy(x32).to(torch.bfloat16).to(torch.float64).numpy()
+    np.testing.assert_array_equal(O.bf16(x32.astype(np.float64)), ref)
+
+
+# ---------------------------------------------------------------- smoothing
+def test_smoothing_closed_form():
+    # weight [N=3][K=4]; per-input-channel maxima over outputs: 1, 0.25, 2, 0.5
+    w = np.array([[1.0, -0.25, 0.5, 0.5],
+                  [-0.5, 0.125, -2.0, 0.25],
+                  [0.25, 0.0625, 1.0, -0.5]])
+    a = np.array([4.0, 9.0, 2.0, 0.0], np.float32)
+    si, lam = O.smoothing_factors(a, w)
+    # lambda = sqrt(a / w): 2, 6, 1, sqrt(1e-5 / 0.5) (eps floor on a)
+    expect = np.array([2.0, 6.0, 1.0, np.sqrt(1e-5 / 0.5)])
+    np.testing.assert_array_equal(si, np.float32(1.0 / expect).astype(np.float64))
+    np.testing.assert_allclose(lam * si, 1.0, rtol=2 ** -52)
+    # the smoothed weight has the factor on input channels (rows of W = weight^T)
+    W_hat = O.smooth_weight(w, lam)
+    np.testing.assert_allclose(W_hat, (lam[:, None] * w.T), rtol=0)
+
+
+# ---------------------------------------------------------------- invariants
+def _pow2_lambda_case(M=24, K=128, N=40, seed=5):
+    rng = np.random.default_rng(seed)
+    x = O.bf16(rng.standard_normal((M, K)) * 3)
+    w = O.bf16(rng.standard_normal((N, K)) * 0.02)
+    e = rng.integers(-3, 4, K)
+    wmax = np.abs(w).max(axis=0)
+    a = (wmax * 4.0 ** e).astype(np.float32)     # exact: bf16 * power of 4
+    return x, w, a, e
+
+
+def test_rank0_quant_off_is_exact_matmul():
+    """Rank 0, no quantization, power-of-two lambda: Y == X W bit for bit."""
+    x, w, a, e = _pow2_lambda_case()
+    p = O.prepare(w, a, rank=0)
+    np.testing.assert_array_equal(p["lam"], 2.0 ** e)
+    y = O.forward(x, p, out="f64", quantize=False)
+    np.testing.assert_array_equal(y, O.reference_fp64(x, w))
+
+
+@pytest.mark.parametrize("rank", [1, 8, 32])
+def test_lambda_cancels_any_rank(rank):
+    wl = workloads.custom_workload(64, 256, 96, seed=11, n_out=3)
+    x, w = wl.x, wl.layers[0].weight
+    p = O.prepare(w, wl.act_absmax(), rank=rank, round_factors=False)
+    y = O.forward(x, p, out="f64", quantize=False)
+    assert O.rel_fro(y, O.reference_fp64(x, w)) < 1e-13
+    # the branch must be present: dropping it leaves a large error
+    p2 = dict(p, L1=np.zeros_like(p["L1"]), L2=np.zeros_like(p["L2"]))
+    assert O.rel_fro(O.forward(x, p2, out="f64", quantize=False), O.reference_fp64(x, w)) > 1e-2
+
+
+def test_full_rank_leaves_zero_residual():
+    wl = workloads.custom_workload(32, 128, 64, seed=12)
+    p = O.prepare(wl.layers[0].weight, wl.act_absmax(), rank=64, round_factors=False)
+    assert np.linalg.norm(p["R"]) <= 1e-12 * np.linalg.norm(p["W_hat"])
+
+
+def test_eckart_young_against_eigh():
+    """Residual of the top-r split equals sqrt(sum of the discarded
+    eigenvalues of W_hat^T W_hat) and L1 L2 is the projection onto the top-r
+    left eigenvectors of W_hat W_hat^T (independent LAPACK routine)."""
+    wl = workloads.custom_workload(64, 192, 128, seed=13, n_out=6)
+    r = 16
+    p = O.prepare(wl.layers[0].weight, wl.act_absmax(), rank=r, round_factors=False)
+    Wh = p["W_hat"]
+    ev = np.sort(np.linalg.eigvalsh(Wh.T @ Wh))[::-1]
+    res = np.linalg.norm(Wh - p["L1"] @ p["L2"])
+    np.testing.assert_allclose(res, np.sqrt(ev[r:].sum()), rtol=1e-9)
+    evl, U = np.linalg.eigh(Wh @ Wh.T)
+    Ur = U[:, np.argsort(evl)[::-1][:r]]
+    np.testing.assert_allclose(p["L1"] @ p["L2"], Ur @ (Ur.T @ Wh), atol=1e-10 * np.abs(Wh).max())
+
+
+# ---------------------------------------------------------------- integer products
+def test_group_products_bruteforce():
+    rng = np.random.default_rng(21)
+    M, K, N = 8, 128, 8
+    qx = rng.integers(-8, 8, (M, K))
+    qw = rng.integers(-8, 8, (K, N))
+    qx[0, :64] = -8
+    qw[:64, 0] = -8                                 # the extreme P = 4096
+    P = O.w4a4_product_bruteforce(qx.tolist(), qw.tolist(), 64)
+    assert P[0][0][0] == 4096
+    ones_x = np.ones((M, 2))
+    ones_w = np.ones((2, N))
+    acc = O.w4a4_product(qx, ones_x, qw, ones_w, 64)
+    np.testing.assert_array_equal(acc, np.array(P[0]) + np.array(P[1]))
+    # non-uniform scales, each group weighted separately
+    sx = O.fp16(rng.uniform(0.01, 1, (M, 2)))
+    sw = O.fp16(rng.uniform(0.01, 1, (2, N)))
+    acc = O.w4a4_product(qx, sx, qw, sw, 64)
+    ref = sum(sx[:, g][:, None] * sw[g][None, :] * np.array(P[g], float) for g in range(2))
+    np.testing.assert_allclose(acc, ref, rtol=1e-14)
+
+
+def test_group_product_equals_dequantized_matmul():
+    rng = np.random.default_rng(22)
+    M, K, N, g = 16, 256, 24, 64
+    qx = rng.integers(-8, 8, (M, K))
+    qw = rng.integers(-8, 8, (K, N))
+    sx = O.fp16(rng.uniform(0.01, 1, (M, K // g)))
+    sw = O.fp16(rng.uniform(0.01, 1, (K // g, N)))
+    deq_x = qx * np.repeat(sx, g, axis=1)
+    deq_w = qw * np.repeat(sw, g, axis=0)
+    np.testing.assert_allclose(O.w4a4_product(qx, sx, qw, sw, g), deq_x @ deq_w, rtol=1e-12, atol=1e-12)
+
+
+# ---------------------------------------------------------------- quantizers
+def test_activation_quant_golden():
+    rows = _read_golden("act_quant_groups.txt")
+    x = np.zeros((1, 64 * len(rows)))
+    exp_s, exp_q = [], np.zeros(64 * len(rows), np.int64)
+    for r in rows:
+        g = int(r[0])
+        vals = [float(v) for v in r[1].split()]
+        x[0, 64 * g:64 * g + len(vals)] = vals
+        exp_s.append(float(r[2]))
+        codes = [int(v) for v in r[3].split()]
+        exp_q[64 * g:64 * g + len(codes)] = codes
+    q, s, _ = O.quantize_activation(x, np.ones(x.shape[1]), 64)
+    np.testing.assert_array_equal(s[0], exp_s)
+    np.testing.assert_array_equal(q[0], exp_q)
+
+
+def test_weight_quant_golden():
+    (r,) = _read_golden("weight_quant_group.txt")
+    vals = [float(v) for v in r[0].split()]
+    R = np.zeros((64, 1))
+    R[:len(vals), 0] = vals
+    q, s = O.quantize_weight_residual(R, 64)
+    assert s[0, 0] == float(r[1])
+    np.testing.assert_array_equal(q[:len(vals), 0], [int(v) for v in r[2].split()])
+    assert np.all(q[len(vals):, 0] == 0)
+
+
+def test_activation_quant_matches_float32_arithmetic():
+    """The fp64-emulated fp32 rounding points agree with numpy float32
+    arithmetic (IEEE single operations) on random smoothed data."""
+    wl = workloads.custom_workload(64, 512, 64, seed=23, n_out=5)
+    si, _ = O.smoothing_factors(wl.act_absmax(), wl.layers[0].weight)
+    q, s, xh = O.quantize_activation(wl.x, si, 64)
+    x32 = wl.x.astype(np.float32)
+    xh32 = x32 * si.astype(np.float32)[None, :]
+    a = np.abs(xh32.reshape(64, -1, 64)).max(-1)
+    s32 = a / np.float32(7.0)
+    s16 = s32.astype(np.float16).astype(np.float32)
+    rcp = np.where(s16 == 0, np.float32(0), np.float32(1.0) / np.where(s16 == 0, np.float32(1), s16))
+    q32 = np.clip(np.rint(xh32.reshape(64, -1, 64) * rcp[..., None]), -8, 7).reshape(64, -1)
+    np.testing.assert_array_equal(xh, xh32.astype(np.float64))
+    np.testing.assert_array_equal(s, s16.astype(np.float64))
+    np.testing.assert_array_equal(q, q32.astype(np.int64))
+
+
+def test_quantizer_properties():
+    rng = np.random.default_rng(24)
+    x = O.bf16(rng.standard_normal((32, 256)) * rng.uniform(0.1, 50, (32, 1)))
+    x[3, 64:128] = 0.0
+    q, s, xh = O.quantize_activation(x, np.ones(256), 64)
+    assert q.min() >= -7 and q.max() <= 7          # absmax/7 never yields -8
+    assert s[3, 1] == 0 and np.all(q[3, 64:128] == 0)
+    xg, qg = xh.reshape(32, 4, 64), q.reshape(32, 4, 64)
+    idx = np.abs(xg).argmax(-1)
+    top = np.take_along_axis(qg, idx[..., None], -1)[..., 0]
+    assert np.all((np.abs(top) == 7) | (s == 0))
+    err = np.abs(xg - qg * s[..., None])
+    assert np.all(err <= s[..., None] / 2 * (1 + 2 ** -9) + 1e-300)
+
+
+def test_pack_golden_and_roundtrip():
+    for r in _read_golden("pack_bytes.txt"):
+        codes = np.array([[int(v) for v in r[0].split()]])
+        expect = np.array([[int(v, 16) for v in r[1].split()]], np.uint8)
+        np.testing.assert_array_equal(O.pack_int4(codes), expect)
+    allc = np.arange(-8, 8)
+    grid = np.stack(np.meshgrid(allc, allc), -1).reshape(1, -1)
+    np.testing.assert_array_equal(O.unpack_int4(O.pack_int4(grid)), grid)
+
+
+def test_gelu_matches_torch():
+    x = np.linspace(-8, 8, 4001)
+    ref = torch.nn.functional.gelu(torch.from_numpy(x), approximate="tanh").numpy()
+    np.testing.assert_allclose(O.gelu_tanh(x), ref, rtol=1e-14, atol=1e-15)
+
+
+# ---------------------------------------------------------------- end to end
+def test_forward_matches_dequantized_definition():
+    """The whole forward equals dequantize(Q4(X_hat)) dequantize(Q4(R)) +
+    bf16(lora_act) L2 + bias, written with independent numpy pieces."""
+    wl = workloads.custom_workload(48, 256, 80, seed=25, n_out=3, bias=True)
+    L = wl.layers[0]
+    p = O.prepare(L.weight, wl.act_absmax(), rank=16)
+    Y, parts = O.forward(wl.x, p, bias=L.bias, out="f64", return_parts=True)
+    deq_x = parts["qx"] * np.repeat(parts["sx"], 64, axis=1)
+    deq_w = p["qw"] * np.repeat(p["sw"], 64, axis=0)
+    la = (O.bf16(parts["x_hat"]) @ p["L1"]).astype(np.float32).astype(np.float64)
+    la16 = torch.from_numpy(la.astype(np.float32)).to(torch.bfloat16).double().numpy()
+    ref = deq_x @ deq_w + la16 @ p["L2"] + L.bias[None, :]
+    np.testing.assert_allclose(Y, ref, rtol=1e-12, atol=1e-12)
+
+
+def test_error_story_low_rank_helps():
+    """no smoothing r=0 > smoothing r=0 > smoothing r=32 (error vs fp64 X W)."""
+    wl = workloads.make_workload("tiny")
+    x, w = wl.x, wl.layers[0].weight
+    ref = O.reference_fp64(x, w)
+    a = wl.act_absmax()
+    p_plain = O.prepare(w, np.abs(w).max(axis=0).astype(np.float32), rank=0)  # lambda = 1
+    assert np.all(p_plain["lam"] == 1.0)
+    e_plain = O.rel_fro(O.forward(x, p_plain), ref)
+    e_r0 = O.rel_fro(O.forward(x, O.prepare(w, a, rank=0)), ref)
+    e_r32 = O.rel_fro(O.forward(x, O.prepare(w, a, rank=32)), ref)
+    assert e_plain > e_r0 > e_r32
+    assert e_r32 < 0.1
+
+
+def test_prepared_bytes_closed_form():
+    wl = workloads.custom_workload(16, 256, 128, seed=26)
+    p = O.prepare(wl.layers[0].weight, wl.act_absmax(), rank=32)
+    nbytes = (O.pack_int4(p["qw"].T).nbytes + p["sw"].astype(np.float16).nbytes
+              + 2 * (p["L1"].size + p["L2"].size) + p["smooth_inv"].astype(np.float32).nbytes)
+    assert nbytes == O.prepared_bytes(256, 128, 32)
+    # FLUX MLP-up layer: ~3.6x smaller than bf16 (the card states about 4x)
+    ratio = 2 * 3072 * 12288 / O.prepared_bytes(3072, 12288, 32)
+    assert 3.5 < ratio < 3.7
