@@ -1,0 +1,230 @@
+#!/usr/bin/env python3
+"""Benchmark of the fused SVDQuant W4A4 + rank-r linear on one MI355X.
+
+A step is one pass of the forward hot path over one batch: kernel 1 (smooth +
+INT4 activation quantizer + down projection) then kernel 2 (W4A4 GEMM +
+dequant + up projection + bias), on the FLUX MLP up-projection layer
+(M = 4096 tokens, K = 3072, N = 12288, rank 32, group 64) unless --workload
+says otherwise.  Weight preparation (smoothing, SVD, 4-bit residual) is a
+one-time offline transform and runs before the timed region.
+
+Prints one JSON line.  value = effective TOPS = 2*M*N*K / (time per step);
+the low-rank flops are not credited.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "effective TOPS of fused W4A4+rank-32 linear (FLUX shapes); % INT8 MFMA peak"
+INT8_PEAK_TOPS = 5000.0      # MI355X dense INT8 MFMA, published
+HBM_PEAK_GBS = 8000.0        # MI355X HBM3E, published
+
+# name -> (generator workload, layer index, act, description)
+BENCH_WORKLOADS = {
+    "mlp_up": ("mlp_pair", 0, "none", "FLUX MLP up-projection 4096x3072x12288"),
+    "attn_out": ("attn_out", 0, "none", "FLUX attention-output projection 4096x3072x3072"),
+    "joint_qkv": ("joint_qkv", 0, "none", "FLUX joint-stream fused QKV 4608x3072x9216 (+bias)"),
+    "rank_sweep": ("rank_sweep", 0, "none", "4 images x 4096 tokens, 16384x3072x12288"),
+}
+
+
+def kernel_source_hash() -> str:
+    p = os.path.join(ROOT, "w4a4_rank_corrected_svdq_amd", "csrc", "svdq_kernels.hip")
+    return hashlib.sha256(open(p, "rb").read()).hexdigest()[:16]
+
+
+def k1_bytes(M, K, r):
+    """Compulsory HBM bytes of kernel 1: read X (bf16), smooth_inv, L1; write
+    codes, scales and lora_act."""
+    return 2 * M * K + 4 * K + 2 * r * K + M * K // 2 + 2 * (K // 64) * M + 4 * M * r
+
+
+def k2_bytes(M, N, K, r, bias):
+    return (M * K // 2 + 2 * (K // 64) * M + N * K // 2 + 2 * (K // 64) * N + 4 * M * r
+            + 2 * N * r + (2 * N if bias else 0) + 2 * M * N)
+
+
+def load_traffic(workload: str, rank: int):
+    """HBM traffic of kernel 2 measured by rocprofv3 PMC counters (committed
+    under profiles/), used only while the kernel source is unchanged."""
+    p = os.path.join(ROOT, "profiles", f"traffic_{workload}_r{rank}.json")
+    if not os.path.exists(p):
+        return None
+    d = json.load(open(p))
+    if d.get("kernel_source_sha") != kernel_source_hash():
+        return None
+    return d.get("k2_hbm_bytes")
+
+
+def cpu_baseline(wl, layer, rank, target_s):
+    """The oracle (as it stands) on a bounded sample of rows of the same
+    workload, timed on this host's cores."""
+    import oracle as O
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([d.get("num_threads", 1) for d in threadpool_info()] + [1])
+    except Exception:  # pragma: no cover
+        threads = os.cpu_count()
+    Lr = wl.layers[layer]
+    K, N = Lr.K, Lr.N
+    a = wl.act_absmax()
+    # preparation needs the SVD; rank-r factors from the oracle's own split
+    t0 = time.perf_counter()
+    po = O.prepare(Lr.weight, a, rank=rank)
+    t_prep = time.perf_counter() - t0
+    rows_per_chunk = 128
+    done_rows = 0
+    t_fwd = 0.0
+    x = wl.x
+    while t_fwd < target_s and done_rows < wl.M:
+        xr = x[done_rows:done_rows + rows_per_chunk]
+        t0 = time.perf_counter()
+        O.forward(xr, po, bias=Lr.bias)
+        t_fwd += time.perf_counter() - t0
+        done_rows += xr.shape[0]
+    tops = 2.0 * done_rows * N * K / t_fwd / 1e12
+    return {"value": tops, "unit": "TOPS", "cores": int(threads), "kind": "oracle",
+            "sample": f"oracle.forward (fp64 numpy W4A4 emulation) on the first {done_rows} of {wl.M} "
+                      f"rows of the same workload, {t_fwd:.1f} s; oracle prepare (LAPACK SVD) "
+                      f"took {t_prep:.1f} s and is not counted",
+            "host_cpu_count": os.cpu_count()}
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--workload", default="mlp_up", choices=sorted(BENCH_WORKLOADS))
+    ap.add_argument("--rank", type=int, default=32)
+    ap.add_argument("--no-overhead", action="store_true", help="skip the rank-0 comparison run")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-seconds", type=float, default=10.0)
+    args = ap.parse_args()
+
+    if args.gpus != 1:
+        print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}); this layer's "
+              "data-parallel path has no cross-GPU exchange, so per-GPU throughput is the "
+              "one-GPU figure.", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import workloads
+    import w4a4_rank_corrected_svdq_amd as S
+    from w4a4_rank_corrected_svdq_amd import _lib as L
+
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(1)
+    torch.cuda.set_device(0)
+    L.check(S.device_check(0), "device check")
+
+    gen_name, layer, act, desc = BENCH_WORKLOADS[args.workload]
+    wl = workloads.make_workload(gen_name)
+    Lr = wl.layers[layer]
+    M, K, N, r = wl.M, Lr.K, Lr.N, args.rank
+    act_id = L.SVDQ_ACT_GELU_TANH if act == "gelu_tanh" else L.SVDQ_ACT_NONE
+
+    def build_layer(rank):
+        prep = S.prepare_weights(Lr.weight_bits, wl.act_absmax(), rank=rank)
+        bias = None
+        if Lr.bias_bits is not None:
+            bias = torch.from_numpy(Lr.bias_bits.view(np.int16).copy()).view(torch.bfloat16)
+        return S.SVDQW4A4Linear(prep, bias, "cuda")
+
+    x = torch.from_numpy(wl.x_bits.view(np.int16).copy()).view(torch.bfloat16).cuda()
+
+    def run(lin, steps, warmup, events=False):
+        xc = torch.empty((M, K // 2), dtype=torch.uint8, device="cuda")
+        xs = torch.empty((K // 64, M), dtype=torch.float16, device="cuda")
+        la = torch.empty((M, lin.rank), dtype=torch.float32, device="cuda") if lin.rank else None
+        y = torch.empty((M, N), dtype=torch.bfloat16, device="cuda")
+
+        def step(mid=None):
+            S.quant_act_lora_down(x, lin.smooth_inv, lin.lora_down, lin.rank, act=act_id, out=(xc, xs, la))
+            if mid is not None:
+                mid.record()
+            S.gemm_w4a4_lora_up(xc, xs, lin.w_codes, lin.w_scales, la, lin.lora_up, lin.bias,
+                                M, N, K, lin.rank, out=y)
+
+        for _ in range(warmup):
+            step()
+        torch.cuda.synchronize()
+        ev = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(steps)]
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for i in range(steps):
+            if events:
+                ev[i][0].record()
+            step(ev[i][1] if events else None)
+            if events:
+                ev[i][2].record()
+        torch.cuda.synchronize()
+        wall = time.perf_counter() - t0
+        res = {"wall_s": wall}
+        if events:
+            res["k1_ms"] = float(np.mean([e[0].elapsed_time(e[1]) for e in ev]))
+            res["k2_ms"] = float(np.mean([e[1].elapsed_time(e[2]) for e in ev]))
+        return res
+
+    lin = build_layer(r)
+    res = run(lin, args.steps, args.warmup, events=True)
+    ms_per_step = res["wall_s"] * 1e3 / args.steps
+    ops = 2.0 * M * N * K
+    value = ops / (ms_per_step * 1e-3) / 1e12
+    k2_tops = ops / (res["k2_ms"] * 1e-3) / 1e12
+    k1_gbs = k1_bytes(M, K, r) / (res["k1_ms"] * 1e-3) / 1e9
+    traffic = load_traffic(args.workload, r)
+
+    out = {
+        "metric": METRIC,
+        "value": round(value, 2),
+        "unit": "TOPS",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "int4",
+        "data": "synthetic",
+        "config": {"workload": f"{desc}, rank {r}, group 64", "M": M, "K": K, "N": N, "rank": r,
+                   "group": 64, "bias": Lr.bias_bits is not None, "parallelism": "single GPU"},
+        "pct_int8_peak": round(100.0 * value / INT8_PEAK_TOPS, 2),
+        "roofline": {"bound": "mfma", "kernel": "k_gemm_w4a4_lora_up",
+                     "achieved": round(k2_tops, 2), "peak": INT8_PEAK_TOPS, "unit": "TOPS",
+                     "frac": round(k2_tops / INT8_PEAK_TOPS, 4), "traffic": traffic,
+                     "avg_launch_us": round(res["k2_ms"] * 1e3, 2),
+                     "algorithmic_ops_per_launch": ops},
+        "roofline_k1": {"bound": "hbm", "kernel": "k_quant_act_lora_down",
+                        "achieved": round(k1_gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                        "frac": round(k1_gbs / HBM_PEAK_GBS, 4),
+                        "avg_launch_us": round(res["k1_ms"] * 1e3, 2),
+                        "algorithmic_bytes_per_launch": k1_bytes(M, K, r)},
+    }
+    if not args.no_overhead and r > 0:
+        lin0 = build_layer(0)
+        res0 = run(lin0, args.steps, args.warmup, events=True)
+        ms0 = res0["wall_s"] * 1e3 / args.steps
+        out["low_rank_overhead"] = {
+            "rank0_ms_per_step": round(ms0, 5),
+            "overhead_frac": round(ms_per_step / ms0 - 1.0, 4),
+            "context": "pages: an unfused rank-32 branch costs +57% latency (NVIDIA, model card)"}
+    if not args.no_cpu_baseline:
+        out["cpu_baseline"] = cpu_baseline(wl, layer, r, args.cpu_seconds)
+    print(json.dumps(out))
+
+
+if __name__ == "__main__":
+    main()

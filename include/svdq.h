@@ -1,0 +1,170 @@
+/*
+ * svdq.h -- C ABI of the SVDQuant W4A4 linear with a rank-r 16-bit branch
+ * for AMD Instinct MI355X (gfx950).
+ *
+ * The layer computes
+ *     Y = Q4(X diag(lambda)^-1) Q4(R) + bf16(X diag(lambda)^-1 L1) L2 + bias
+ * where diag(lambda) W = L1 L2 + R (W in [K x N] math layout), L1 L2 is the
+ * top-r SVD of the smoothed weight and R is the 4-bit residual
+ * (svdq-int4-flux.1-depth-dev model card, "Quantization Method -- SVDQuant",
+ * stages 2 and 3; "Bringing Nunchaku 4-bit Diffusion Inference to
+ * Diffusers", "Background: SVDQuant and Nunchaku").
+ *
+ * Two device entry points follow the fusion the model card's "Nunchaku
+ * Engine Design" describes: the down projection runs in the same kernel as
+ * the activation quantizer (both read the 16-bit input), and the up
+ * projection runs in the epilogue of the 4-bit GEMM (both write the 16-bit
+ * output).
+ *
+ * Conventions for every function:
+ *  - Return value: SVDQ_OK (0) or a negative svdq_status.  Arguments are
+ *    validated on the host before anything is launched; on error nothing is
+ *    written and nothing is launched.
+ *  - Storage types: bf16 and fp16 values travel as their 16-bit patterns
+ *    (uint16_t / void*), packed INT4 codes as bytes holding two codes each,
+ *    low nibble = even k, two's complement (-8 .. 7).
+ *  - Weight layouts follow torch.nn.Linear: [out_features][in_features].
+ *  - The library never allocates or frees memory and keeps no pointer after
+ *    returning.  Device functions are asynchronous on the caller's stream
+ *    (a hipStream_t passed as void*; NULL = the default stream); buffers
+ *    must stay alive until the stream has finished.  Faults during execution
+ *    surface at the caller's next synchronization.
+ *  - Only group = 64 is supported.  K must be a positive multiple of 64,
+ *    N a positive multiple of 8, 0 <= rank <= min(K, N), rank % 16 == 0 and
+ *    rank <= SVDQ_MAX_RANK.  M >= 0 (M == 0 launches nothing).
+ *  - Thread safety: no mutable global state except a per-device cache of
+ *    the architecture check.
+ */
+#ifndef SVDQ_H
+#define SVDQ_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum svdq_status {
+  SVDQ_OK = 0,
+  SVDQ_ERR_INVALID_ARG = -1,        /* null pointer, negative or inconsistent size */
+  SVDQ_ERR_UNSUPPORTED_SHAPE = -2,  /* valid request this build does not implement */
+  SVDQ_ERR_UNSUPPORTED_DEVICE = -3, /* no device, or not gfx950 */
+  SVDQ_ERR_HIP = -4,                /* HIP runtime call or launch failed */
+  SVDQ_ERR_NUMERIC = -5             /* non-finite input, fp16 scale overflow, SVD failure */
+} svdq_status;
+
+enum { SVDQ_ACT_NONE = 0, SVDQ_ACT_GELU_TANH = 1 };
+enum { SVDQ_OUT_BF16 = 0, SVDQ_OUT_F32 = 1 };
+enum { SVDQ_GROUP = 64, SVDQ_MAX_RANK = 256 };
+
+/* Human-readable name of a status code (static storage, never NULL). */
+const char* svdq_status_string(int status);
+
+/* ABI version (major * 100 + minor). */
+int svdq_version(void);
+
+/* Validates that HIP device `hip_device` exists and is a gfx950 (MI355X).
+ * The pages' loader checks the GPU's capability when a quantized model is
+ * loaded and refuses with a clear error rather than computing wrong results
+ * ("Bringing Nunchaku 4-bit Diffusion Inference to Diffusers", "Hardware
+ * support"); every device entry point below performs this check (cached per
+ * device) and returns SVDQ_ERR_UNSUPPORTED_DEVICE before launching anything.
+ * The environment variable SVDQ_ASSUME_ARCH, when set, replaces the queried
+ * architecture name (to exercise the refusal path on any machine). */
+int svdq_device_check(int hip_device);
+
+/* Bytes of one prepared layer as produced by svdq_prepare_weights: packed
+ * codes N*K/2 + fp16 scales 2*(K/64)*N + bf16 factors 2*rank*(K+N) + fp32
+ * smooth_inv 4*K.  Validates the shape like the functions below. */
+int svdq_prepared_bytes(int K, int N, int rank, int group, size_t* bytes_out);
+
+/* Host, synchronous.  Offline preparation of one linear layer (stages 2 and
+ * 3 of "Quantization Method -- SVDQuant" plus the 4-bit residual).
+ *
+ *   weight     [N][K] bf16   the layer weight (torch.nn.Linear layout)
+ *   act_absmax [K]    fp32   calibration statistic max_m |X[m, k]| (>= 0)
+ *   alpha             fp32   smoothing strength in (0, 1); 0.5 is the default
+ *   rank, group              branch rank r and INT4 group (64)
+ * Outputs (caller-owned host buffers):
+ *   smooth_inv [K]       fp32  1/lambda_k with lambda_k =
+ *                              max(a_k,1e-5)^alpha / max(w_k,1e-5)^(1-alpha),
+ *                              w_k = max_n |weight[n][k]| (alpha = 0.5: sqrt(a/w))
+ *   w_codes    [N][K/2]  u8    INT4 codes of R (two per byte, low nibble = even k)
+ *   w_scales   [K/64][N] fp16  per (group, output channel): fp16(absmax/7)
+ *   lora_down  [rank][K] bf16  L1^T (= U_r Sigma_r transposed); may be NULL if rank == 0
+ *   lora_up    [N][rank] bf16  L2^T (= V_r); may be NULL if rank == 0
+ * with W_hat = diag(1/fp64(smooth_inv)) W, L1 L2 = top-r SVD of W_hat
+ * (randomized block subspace iteration with a one-sided Jacobi SVD of the
+ * projected block, fp64), R = W_hat - bf16(L1) bf16(L2) in fp64, and codes
+ * q = clamp(rne(R / s), -8, 7).  Returns SVDQ_ERR_NUMERIC on non-finite input,
+ * an fp16 scale overflow or a non-converged SVD. */
+int svdq_prepare_weights(const uint16_t* weight, int K, int N,
+                         const float* act_absmax, float alpha, int rank, int group,
+                         float* smooth_inv, uint8_t* w_codes, uint16_t* w_scales,
+                         uint16_t* lora_down, uint16_t* lora_up);
+
+/* As svdq_prepare_weights, with three extras:
+ *   lora_down_in [rank][K], lora_up_in [N][rank] (bf16, both or neither):
+ *       when given, the SVD is skipped and these factors are used (and copied
+ *       to lora_down / lora_up); the residual is taken against them.
+ *   sigma_out [rank] fp64 (nullable): the singular values of the split.
+ *   power_iters (<= 0: default 8) subspace iterations; seed: RNG seed of the
+ *       starting block (counter-based splitmix64 + Box-Muller). */
+int svdq_prepare_weights_ex(const uint16_t* weight, int K, int N,
+                            const float* act_absmax, float alpha, int rank, int group,
+                            const uint16_t* lora_down_in, const uint16_t* lora_up_in,
+                            int power_iters, uint64_t seed,
+                            float* smooth_inv, uint8_t* w_codes, uint16_t* w_scales,
+                            uint16_t* lora_down, uint16_t* lora_up, double* sigma_out);
+
+/* Device, asynchronous.  Kernel 1: fused smoothing + per-(token, group of 64)
+ * symmetric INT4 activation quantizer + low-rank down projection, reading
+ * each input element from HBM once (model card, "Nunchaku Engine Design":
+ * the down projection and the quantizer share their input).
+ *
+ *   x          [M][K]      bf16  input activations (with act = GELU_TANH,
+ *                                tanh-GELU is applied to x first, in fp32)
+ *   smooth_inv [K]         fp32
+ *   lora_down  [rank][K]   bf16  (NULL allowed when rank == 0)
+ * Outputs:
+ *   x_codes    [M][K/2]    u8    codes q = clamp(rne(fp32(x_hat * fp32(1/s))), -8, 7)
+ *   x_scales   [K/64][M]   fp16  s = fp16(fp32(absmax(x_hat over the group) / 7));
+ *                                an all-zero group gets s = 0 and codes 0
+ *   lora_act   [M][rank]   fp32  sum_k bf16(x_hat[m,k]) * lora_down[j][k]
+ *                                (NULL allowed when rank == 0)
+ * with x_hat = fp32(act(x) * smooth_inv).  |x_hat| above 7 * 65504 in a
+ * group overflows the fp16 scale to inf (codes 0); such inputs are outside
+ * the supported range. */
+int svdq_quant_act_lora_down(const void* x, const float* smooth_inv, const void* lora_down,
+                             int M, int K, int rank, int group, int act,
+                             void* x_codes, void* x_scales, float* lora_act,
+                             void* stream);
+
+/* Device, asynchronous.  Kernel 2: W4A4 GEMM on int8 MFMA with exact int32
+ * per-group products, per-group dequantization, and the up projection plus
+ * bias in the epilogue (model card, "Nunchaku Engine Design": the up
+ * projection and the 4-bit compute share their output).
+ *
+ *   x_codes  [M][K/2] u8, x_scales [K/64][M] fp16  (from kernel 1)
+ *   w_codes  [N][K/2] u8, w_scales [K/64][N] fp16  (from preparation)
+ *   lora_act [M][rank] fp32, lora_up [N][rank] bf16 (NULL allowed when rank == 0)
+ *   bias     [N] bf16 or NULL
+ * Output:
+ *   y        [M][N] bf16 (out_dtype = SVDQ_OUT_BF16) or fp32 (SVDQ_OUT_F32):
+ *            y = sum_g s_x[m,g] s_w[g,n] P_g[m,n]
+ *                + sum_j bf16(lora_act[m,j]) lora_up[n][j] + bias[n],
+ *            P_g = sum over the 64 k of group g of q_x q_w (exact int32),
+ *            accumulated in fp32 over g in increasing order, rounded to the
+ *            output type to nearest even. */
+int svdq_gemm_w4a4_lora_up(const void* x_codes, const void* x_scales,
+                           const void* w_codes, const void* w_scales,
+                           const float* lora_act, const void* lora_up, const void* bias,
+                           int M, int N, int K, int rank, int group, int out_dtype,
+                           void* y, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* SVDQ_H */

@@ -1,0 +1,12 @@
+"""SVDQuant W4A4 linear with a rank-r 16-bit branch, native to MI355X (gfx950).
+
+The compute lives in ``libsvdq.so`` (C ABI in ``include/svdq.h``); this
+package is its Python binding.
+"""
+from ._lib import SVDQError, lib  # noqa: F401
+from . import _lib as abi  # noqa: F401
+from .ops import (device_check, gemm_w4a4_lora_up, prepare_weights, prepared_bytes,  # noqa: F401
+                  quant_act_lora_down)
+from .linear import SVDQW4A4Linear  # noqa: F401
+
+__version__ = "0.1.0"

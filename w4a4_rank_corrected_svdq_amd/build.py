@@ -1,0 +1,68 @@
+"""Build the HIP/C++ library ``libsvdq.so`` in-tree for gfx950.
+
+Usage: ``python -m w4a4_rank_corrected_svdq_amd.build`` (or
+``__graft_entry__.build()``).  Always recompiles.
+"""
+from __future__ import annotations
+
+import os
+import shutil
+import subprocess
+import sys
+
+PKG = os.path.dirname(os.path.abspath(__file__))
+ROOT = os.path.dirname(PKG)
+CSRC = os.path.join(PKG, "csrc")
+INCLUDE = os.path.join(ROOT, "include")
+LIB = os.path.join(PKG, "libsvdq.so")
+BUILD = os.path.join(ROOT, "_build")
+
+HIP_SOURCES = ["svdq_kernels.hip", "svdq_abi.hip"]
+CXX_SOURCES = ["svdq_prepare.cpp"]
+
+# Packed-fp32 VALU forms are disabled for all device code; hipcc's host pass
+# warns that it does not know the feature, which is harmless.
+HIP_FLAGS = ["--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC", "-Wall",
+             "-ffp-contract=fast", "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops"]
+CXX_FLAGS = ["-O3", "-std=c++17", "-fPIC", "-Wall", "-ffp-contract=off", "-mavx2", "-mfma"]
+
+
+def _hipcc() -> str:
+    for cand in (os.environ.get("HIPCC"), "/opt/rocm/bin/hipcc", shutil.which("hipcc")):
+        if cand and os.path.exists(cand):
+            return cand
+    raise RuntimeError("hipcc not found; the HIP library cannot be built")
+
+
+def _run(cmd):
+    r = subprocess.run(cmd, stdout=subprocess.PIPE, stderr=subprocess.STDOUT, text=True)
+    out = "\n".join(l for l in r.stdout.splitlines() if "packed-fp32-ops" not in l)
+    if r.returncode != 0:
+        raise RuntimeError(f"build step failed ({r.returncode}): {' '.join(cmd)}\n{out}")
+    return out
+
+
+def build(verbose: bool = False) -> str:
+    os.makedirs(BUILD, exist_ok=True)
+    hipcc = _hipcc()
+    objs = []
+    for src in HIP_SOURCES:
+        obj = os.path.join(BUILD, src + ".o")
+        out = _run([hipcc, *HIP_FLAGS, "-I", INCLUDE, "-I", CSRC, "-c", os.path.join(CSRC, src), "-o", obj])
+        if verbose and out.strip():
+            print(out)
+        objs.append(obj)
+    for src in CXX_SOURCES:
+        obj = os.path.join(BUILD, src + ".o")
+        out = _run(["g++", *CXX_FLAGS, "-I", INCLUDE, "-I", CSRC, "-c", os.path.join(CSRC, src), "-o", obj])
+        if verbose and out.strip():
+            print(out)
+        objs.append(obj)
+    tmp = LIB + ".tmp"
+    _run([hipcc, "--offload-arch=gfx950", "-shared", "-fPIC", "-o", tmp, *objs, "-lpthread"])
+    os.replace(tmp, LIB)
+    return LIB
+
+
+if __name__ == "__main__":
+    print(build(verbose="-v" in sys.argv))

@@ -1,0 +1,116 @@
+// C ABI entry points of the device path: argument validation, the device
+// capability check, and dispatch to the kernel launchers.  See include/svdq.h.
+
+#include <hip/hip_runtime.h>
+
+#include <atomic>
+#include <cstdint>
+#include <cstdlib>
+#include <cstring>
+
+#include "svdq.h"
+#include "svdq_internal.h"
+
+namespace {
+
+constexpr int kMaxDevices = 64;
+// 0 = unknown, 1 = supported, 2 = unsupported
+std::atomic<int> g_device_ok[kMaxDevices];
+
+int query_device(int dev) {
+  int count = 0;
+  if (hipGetDeviceCount(&count) != hipSuccess || count <= 0) return SVDQ_ERR_UNSUPPORTED_DEVICE;
+  if (dev < 0 || dev >= count || dev >= kMaxDevices) return SVDQ_ERR_UNSUPPORTED_DEVICE;
+  const char* forced = std::getenv("SVDQ_ASSUME_ARCH");
+  char arch[256] = {0};
+  if (forced) {
+    std::strncpy(arch, forced, sizeof(arch) - 1);
+  } else {
+    hipDeviceProp_t prop;
+    if (hipGetDeviceProperties(&prop, dev) != hipSuccess) return SVDQ_ERR_HIP;
+    std::strncpy(arch, prop.gcnArchName, sizeof(arch) - 1);
+  }
+  // gcnArchName looks like "gfx950:sramecc+:xnack-"
+  return (std::strncmp(arch, "gfx950", 6) == 0 && (arch[6] == 0 || arch[6] == ':'))
+             ? SVDQ_OK
+             : SVDQ_ERR_UNSUPPORTED_DEVICE;
+}
+
+int current_device_check() {
+  int dev = -1;
+  int count = 0;
+  if (hipGetDeviceCount(&count) != hipSuccess || count <= 0) return SVDQ_ERR_UNSUPPORTED_DEVICE;
+  if (hipGetDevice(&dev) != hipSuccess) return SVDQ_ERR_HIP;
+  return svdq_device_check(dev);
+}
+
+inline bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+}  // namespace
+
+extern "C" const char* svdq_status_string(int status) {
+  switch (status) {
+    case SVDQ_OK: return "SVDQ_OK";
+    case SVDQ_ERR_INVALID_ARG: return "SVDQ_ERR_INVALID_ARG: null pointer, misaligned buffer, or inconsistent size";
+    case SVDQ_ERR_UNSUPPORTED_SHAPE: return "SVDQ_ERR_UNSUPPORTED_SHAPE: needs group 64, K % 64 == 0, N % 8 == 0, rank % 16 == 0, rank <= 256";
+    case SVDQ_ERR_UNSUPPORTED_DEVICE: return "SVDQ_ERR_UNSUPPORTED_DEVICE: no HIP device, or the device is not gfx950 (MI355X)";
+    case SVDQ_ERR_HIP: return "SVDQ_ERR_HIP: a HIP runtime call or kernel launch failed";
+    case SVDQ_ERR_NUMERIC: return "SVDQ_ERR_NUMERIC: non-finite input, fp16 scale overflow, or SVD did not converge";
+    default: return "SVDQ_ERR_UNKNOWN";
+  }
+}
+
+extern "C" int svdq_version(void) { return 100; }
+
+extern "C" int svdq_device_check(int hip_device) {
+  if (hip_device < 0 || hip_device >= kMaxDevices) return SVDQ_ERR_UNSUPPORTED_DEVICE;
+  const int cached = g_device_ok[hip_device].load(std::memory_order_relaxed);
+  if (cached == 1) return SVDQ_OK;
+  if (cached == 2) return SVDQ_ERR_UNSUPPORTED_DEVICE;
+  const int st = query_device(hip_device);
+  if (st == SVDQ_OK) g_device_ok[hip_device].store(1, std::memory_order_relaxed);
+  else if (st == SVDQ_ERR_UNSUPPORTED_DEVICE) g_device_ok[hip_device].store(2, std::memory_order_relaxed);
+  return st;
+}
+
+extern "C" int svdq_quant_act_lora_down(const void* x, const float* smooth_inv, const void* lora_down,
+                                        int M, int K, int rank, int group, int act, void* x_codes,
+                                        void* x_scales, float* lora_act, void* stream) {
+  if (M < 0) return SVDQ_ERR_INVALID_ARG;
+  if (K <= 0 || rank < 0 || rank > K || group <= 0) return SVDQ_ERR_INVALID_ARG;
+  if (group != SVDQ_GROUP || K % group != 0 || rank % 16 != 0 || rank > SVDQ_MAX_RANK)
+    return SVDQ_ERR_UNSUPPORTED_SHAPE;
+  int st;
+  if (act != SVDQ_ACT_NONE && act != SVDQ_ACT_GELU_TANH) return SVDQ_ERR_INVALID_ARG;
+  if (!x || !smooth_inv || !x_codes || !x_scales) return SVDQ_ERR_INVALID_ARG;
+  if (rank > 0 && (!lora_down || !lora_act)) return SVDQ_ERR_INVALID_ARG;
+  if (!aligned16(x) || !aligned16(smooth_inv) || !aligned16(x_codes) || !aligned16(x_scales) ||
+      (rank > 0 && (!aligned16(lora_down) || !aligned16(lora_act))))
+    return SVDQ_ERR_INVALID_ARG;
+  st = current_device_check();
+  if (st != SVDQ_OK) return st;
+  if (M == 0) return SVDQ_OK;
+  return svdq::launch_quant_act_lora_down(x, smooth_inv, lora_down, M, K, rank, act, x_codes, x_scales,
+                                          lora_act, stream);
+}
+
+extern "C" int svdq_gemm_w4a4_lora_up(const void* x_codes, const void* x_scales, const void* w_codes,
+                                      const void* w_scales, const float* lora_act, const void* lora_up,
+                                      const void* bias, int M, int N, int K, int rank, int group,
+                                      int out_dtype, void* y, void* stream) {
+  if (M < 0) return SVDQ_ERR_INVALID_ARG;
+  int st = svdq::validate_shape(K, N, rank, group);
+  if (st != SVDQ_OK) return st;
+  if (out_dtype != SVDQ_OUT_BF16 && out_dtype != SVDQ_OUT_F32) return SVDQ_ERR_INVALID_ARG;
+  if (!x_codes || !x_scales || !w_codes || !w_scales || !y) return SVDQ_ERR_INVALID_ARG;
+  if (rank > 0 && (!lora_act || !lora_up)) return SVDQ_ERR_INVALID_ARG;
+  if (!aligned16(x_codes) || !aligned16(x_scales) || !aligned16(w_codes) || !aligned16(w_scales) ||
+      !aligned16(y) || (bias && !aligned16(bias)) ||
+      (rank > 0 && (!aligned16(lora_act) || !aligned16(lora_up))))
+    return SVDQ_ERR_INVALID_ARG;
+  st = current_device_check();
+  if (st != SVDQ_OK) return st;
+  if (M == 0) return SVDQ_OK;
+  return svdq::launch_gemm_w4a4_lora_up(x_codes, x_scales, w_codes, w_scales, lora_act, lora_up, bias, M,
+                                        N, K, rank, out_dtype, y, stream);
+}

@@ -1,0 +1,19 @@
+// Internal declarations shared by the library's translation units.
+#pragma once
+#include <cstdint>
+
+namespace svdq {
+
+// Shape rules common to every entry point (see svdq.h).
+int validate_shape(int K, int N, int rank, int group);
+
+// Kernel launchers (svdq_kernels.hip).  Arguments already validated.
+int launch_quant_act_lora_down(const void* x, const float* smooth_inv, const void* lora_down, int M,
+                               int K, int rank, int act, void* x_codes, void* x_scales,
+                               float* lora_act, void* stream);
+int launch_gemm_w4a4_lora_up(const void* x_codes, const void* x_scales, const void* w_codes,
+                             const void* w_scales, const float* lora_act, const void* lora_up,
+                             const void* bias, int M, int N, int K, int rank, int out_dtype, void* y,
+                             void* stream);
+
+}  // namespace svdq

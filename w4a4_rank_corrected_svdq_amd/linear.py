@@ -1,0 +1,58 @@
+"""``SVDQW4A4Linear``: a prepared layer resident in device memory.
+
+Mirrors the pages' module-level interface (``SVDQW4A4Linear.from_linear``,
+"Quantizing models with structural rewrites" in "Bringing Nunchaku 4-bit
+Diffusion Inference to Diffusers"; precision / group_size / rank fields of the
+``quantization_config`` in "Native loading in Diffusers").  Preparation runs
+in the library's host code, the forward pass in its two HIP kernels.
+"""
+from __future__ import annotations
+
+from typing import Optional
+
+import numpy as np
+import torch
+
+from . import _lib as L
+from . import ops
+
+
+def _bits_to_bf16(bits: np.ndarray, device) -> torch.Tensor:
+    bits = np.ascontiguousarray(bits, dtype=np.uint16)
+    return torch.from_numpy(bits.view(np.int16).copy()).view(torch.bfloat16).to(device)
+
+
+def _to_dev(a: np.ndarray, device) -> torch.Tensor:
+    return torch.from_numpy(np.ascontiguousarray(a)).to(device)
+
+
+class SVDQW4A4Linear:
+    precision = "int4"
+
+    def __init__(self, prepared: dict, bias: Optional[torch.Tensor], device):
+        dev = torch.device(device)
+        self.K, self.N = prepared["K"], prepared["N"]
+        self.rank, self.group = prepared["rank"], prepared["group"]
+        self.smooth_inv = _to_dev(np.asarray(prepared["smooth_inv"], np.float32), dev)
+        self.w_codes = _to_dev(np.asarray(prepared["w_codes"], np.uint8), dev)
+        self.w_scales = _to_dev(np.asarray(prepared["w_scales"], np.float16), dev)
+        self.lora_down = _bits_to_bf16(prepared["lora_down"], dev) if self.rank else None
+        self.lora_up = _bits_to_bf16(prepared["lora_up"], dev) if self.rank else None
+        self.bias = None if bias is None else bias.detach().to(dev, torch.bfloat16).contiguous()
+
+    @classmethod
+    def from_linear(cls, linear: torch.nn.Linear, act_absmax, rank: int = 32, group: int = 64,
+                    alpha: float = 0.5, device="cuda"):
+        """Quantize a ``torch.nn.Linear`` (weight [out][in], bf16) given the
+        calibration statistic ``act_absmax`` [in] (max |x| per input channel)."""
+        w = linear.weight.detach().to(torch.bfloat16).cpu()
+        prep = ops.prepare_weights(w, np.asarray(act_absmax, np.float32), rank, group, alpha)
+        return cls(prep, linear.bias, device)
+
+    def forward(self, x: torch.Tensor, act: int = L.SVDQ_ACT_NONE, out_dtype: int = L.SVDQ_OUT_BF16):
+        M = x.shape[0]
+        xc, xs, la = ops.quant_act_lora_down(x, self.smooth_inv, self.lora_down, self.rank, self.group, act)
+        return ops.gemm_w4a4_lora_up(xc, xs, self.w_codes, self.w_scales, la, self.lora_up, self.bias,
+                                     M, self.N, self.K, self.rank, self.group, out_dtype)
+
+    __call__ = forward

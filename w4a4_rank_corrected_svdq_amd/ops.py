@@ -1,0 +1,158 @@
+"""Thin Python binding over the C ABI (argument marshalling only).
+
+Every step of the layer runs in ``libsvdq.so``: host preparation in its C++
+code, the forward pass in its two HIP kernels.  PyTorch provides device
+memory (``torch.empty``) and the current stream; nothing here computes.
+"""
+from __future__ import annotations
+
+import ctypes
+from typing import Optional
+
+import numpy as np
+import torch
+
+from . import _lib as L
+
+__all__ = ["prepare_weights", "quant_act_lora_down", "gemm_w4a4_lora_up", "prepared_bytes",
+           "device_check"]
+
+
+def _ptr(t) -> Optional[int]:
+    if t is None:
+        return None
+    if isinstance(t, np.ndarray):
+        if not t.flags.c_contiguous:
+            raise ValueError("host arrays passed to the library must be C-contiguous")
+        return t.ctypes.data
+    return t.data_ptr()
+
+
+def _dev_arg(name: str, t, dtype, shape, device) -> Optional[int]:
+    """Check a device tensor argument (dtype, shape, device, row-major
+    contiguity) and return its address."""
+    if t is None:
+        return None
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch tensor")
+    if t.dtype != dtype:
+        raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
+    if tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} must have shape {tuple(shape)}, got {tuple(t.shape)}")
+    if t.device != device:
+        raise ValueError(f"{name} is on {t.device}, expected {device}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous (row-major)")
+    return t.data_ptr()
+
+
+def _stream(device: torch.device) -> int:
+    return torch.cuda.current_stream(device).cuda_stream
+
+
+def device_check(device: int = 0) -> int:
+    return L.lib().svdq_device_check(int(device))
+
+
+def prepared_bytes(K: int, N: int, rank: int, group: int = 64) -> int:
+    out = ctypes.c_size_t(0)
+    L.check(L.lib().svdq_prepared_bytes(K, N, rank, group, ctypes.byref(out)), "svdq_prepared_bytes")
+    return int(out.value)
+
+
+def _bf16_bits(a) -> np.ndarray:
+    if isinstance(a, torch.Tensor):
+        if a.dtype != torch.bfloat16:
+            raise TypeError("expected a bfloat16 tensor")
+        return np.ascontiguousarray(a.detach().cpu().contiguous().view(torch.int16).numpy().view(np.uint16))
+    a = np.asarray(a)
+    if a.dtype != np.uint16:
+        raise TypeError("expected bf16 bit patterns (uint16)")
+    return np.ascontiguousarray(a)
+
+
+def prepare_weights(weight, act_absmax, rank: int = 32, group: int = 64, alpha: float = 0.5,
+                    factors=None, power_iters: int = 0, seed: int = 0x5356445175616E74,
+                    return_sigma: bool = False) -> dict:
+    """Host preparation (svdq_prepare_weights[_ex]).
+
+    weight: [N][K] bf16 (torch tensor or uint16 bits); act_absmax: [K] float32.
+    factors: optional (lora_down [r][K], lora_up [N][r]) bf16 bits to use
+    instead of the SVD.  Returns numpy arrays: smooth_inv f32 [K], w_codes u8
+    [N][K/2], w_scales f16 [K/64][N], lora_down bf16 bits [r][K], lora_up bf16
+    bits [N][r] (and sigma [r] f64)."""
+    w = _bf16_bits(weight)
+    N, K = w.shape
+    a = np.ascontiguousarray(np.asarray(act_absmax, dtype=np.float32).reshape(K))
+    si = np.empty(K, np.float32)
+    wc = np.empty((N, K // 2), np.uint8)
+    ws = np.empty((max(K // group, 0), N), np.float16)
+    ld = np.empty((rank, K), np.uint16)
+    lu = np.empty((N, rank), np.uint16)
+    sig = np.empty(max(rank, 1), np.float64)
+    fin = (None, None)
+    if factors is not None:
+        fin = tuple(np.ascontiguousarray(np.asarray(f, dtype=np.uint16)) for f in factors)
+        if fin[0].shape != (rank, K) or fin[1].shape != (N, rank):
+            raise ValueError("factors must be lora_down [rank][K] and lora_up [N][rank]")
+    st = L.lib().svdq_prepare_weights_ex(
+        _ptr(w), K, N, _ptr(a), float(alpha), rank, group, _ptr(fin[0]), _ptr(fin[1]),
+        int(power_iters), int(seed) & (2 ** 64 - 1), _ptr(si), _ptr(wc), _ptr(ws),
+        _ptr(ld) if rank else None, _ptr(lu) if rank else None, _ptr(sig))
+    L.check(st, "svdq_prepare_weights")
+    out = dict(smooth_inv=si, w_codes=wc, w_scales=ws, lora_down=ld, lora_up=lu,
+               rank=rank, group=group, K=K, N=N)
+    if return_sigma:
+        out["sigma"] = sig[:rank].copy()
+    return out
+
+
+def quant_act_lora_down(x: torch.Tensor, smooth_inv: torch.Tensor, lora_down: Optional[torch.Tensor],
+                        rank: int, group: int = 64, act: int = L.SVDQ_ACT_NONE, out=None):
+    """Kernel 1 on x's device and current stream.  x: [M][K] bfloat16.
+    Returns (x_codes u8 [M][K/2], x_scales f16 [K/64][M], lora_act f32 [M][rank])."""
+    if x.dtype != torch.bfloat16 or x.dim() != 2 or not x.is_cuda:
+        raise TypeError("x must be a 2-D bfloat16 CUDA tensor")
+    x = x.contiguous()
+    M, K = x.shape
+    dev = x.device
+    if out is None:
+        xc = torch.empty((M, K // 2), dtype=torch.uint8, device=dev)
+        xs = torch.empty((K // group, M), dtype=torch.float16, device=dev)
+        la = torch.empty((M, rank), dtype=torch.float32, device=dev) if rank else None
+    else:
+        xc, xs, la = out
+    G = K // group if group > 0 else 0
+    st = L.lib().svdq_quant_act_lora_down(
+        _dev_arg("x", x, torch.bfloat16, (M, K), dev),
+        _dev_arg("smooth_inv", smooth_inv, torch.float32, (K,), dev),
+        _dev_arg("lora_down", lora_down, torch.bfloat16, (rank, K), dev) if rank else None,
+        M, K, rank, group, act,
+        _dev_arg("x_codes", xc, torch.uint8, (M, K // 2), dev),
+        _dev_arg("x_scales", xs, torch.float16, (G, M), dev),
+        _dev_arg("lora_act", la, torch.float32, (M, rank), dev) if rank else None, _stream(dev))
+    L.check(st, "svdq_quant_act_lora_down")
+    return xc, xs, la
+
+
+def gemm_w4a4_lora_up(x_codes, x_scales, w_codes, w_scales, lora_act, lora_up, bias,
+                      M: int, N: int, K: int, rank: int, group: int = 64,
+                      out_dtype: int = L.SVDQ_OUT_BF16, out: Optional[torch.Tensor] = None):
+    """Kernel 2 on x_codes' device and current stream; returns y [M][N]."""
+    dev = x_codes.device
+    if out is None:
+        dt = torch.float32 if out_dtype == L.SVDQ_OUT_F32 else torch.bfloat16
+        out = torch.empty((M, N), dtype=dt, device=dev)
+    G = K // group if group > 0 else 0
+    dt = torch.float32 if out_dtype == L.SVDQ_OUT_F32 else torch.bfloat16
+    st = L.lib().svdq_gemm_w4a4_lora_up(
+        _dev_arg("x_codes", x_codes, torch.uint8, (M, K // 2), dev),
+        _dev_arg("x_scales", x_scales, torch.float16, (G, M), dev),
+        _dev_arg("w_codes", w_codes, torch.uint8, (N, K // 2), dev),
+        _dev_arg("w_scales", w_scales, torch.float16, (G, N), dev),
+        _dev_arg("lora_act", lora_act, torch.float32, (M, rank), dev) if rank else None,
+        _dev_arg("lora_up", lora_up, torch.bfloat16, (N, rank), dev) if rank else None,
+        _dev_arg("bias", bias, torch.bfloat16, (N,), dev),
+        M, N, K, rank, group, out_dtype, _dev_arg("y", out, dt, (M, N), dev), _stream(dev))
+    L.check(st, "svdq_gemm_w4a4_lora_up")
+    return out
