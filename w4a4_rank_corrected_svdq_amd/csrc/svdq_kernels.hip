@@ -179,190 +179,253 @@ __global__ __launch_bounds__(K1_WAVES * 64) void k_quant_act_lora_down(
 // =====================================================================
 // Kernel 2
 // =====================================================================
-// Block tile 128 x 128, 4 waves in a 2 x 2 arrangement (64 x 64 per wave,
-// 4 x 4 MFMA tiles of 16 x 16).  One group of 64 along K per step, double
-// buffered in LDS: A = 128 rows x 32 packed bytes, B = 128 columns x 32
-// packed bytes, plus the group's 128 + 128 fp16 scales.
+// Block tile 128 x 128 with 8 waves in a 4 (M) x 2 (N) arrangement; each
+// wave owns 32 x 64 outputs = two 32 x 32 MFMA tiles.  One group of 64 k is
+// two v_mfma_i32_32x32x32_i8 per tile (the 32x32 form sustains ~1.4x the
+// int8 rate of the 16x16x64 form on gfx950).  The K loop runs in stages of
+// two groups: a stage is loaded from HBM as packed nibbles into registers
+// one stage ahead, unpacked cooperatively (once per block) and written to a
+// double-buffered LDS tile as int8 operands, so the waves read ready MFMA
+// fragments with one 16-byte LDS read each.
+//
+// 32x32 MFMA layouts (wave64): A operand lane l holds row l % 32 and one K
+// slice chosen by l / 32; B operand lane l holds column l % 32 and the same
+// slice; C/D lane l holds column l % 32, rows 8b + 4(l / 32) + i in register
+// 4b + i (b, i = 0..3).
 //
 // Unpacking: a packed dword holds 8 codes (byte j = code 2j low, 2j+1 high).
-// (w << 4) & 0xF0F0F0F0 puts the even codes in the high nibble of each
-// byte and w & 0xF0F0F0F0 the odd ones, so every int8 lane of the MFMA
-// operand equals 16 * q with no sign extension; the product is 256 * P_g.
+// (w << 4) & 0xF0F0F0F0 puts the even codes in the high nibble of each byte
+// and w & 0xF0F0F0F0 the odd ones, so every int8 lane of the MFMA operand
+// equals 16 * q with no sign extension; the product is 256 * P_g.  A and B
+// use the same order of k inside the group, which the product ignores.
 //
-// Dequantization: the int8 MFMA's C operand is the constant 0x4B400000, the
-// bit pattern of 1.5 * 2^23.  |256 * P_g| <= 2^20 < 2^22, so the int32 result
-// read as fp32 is exactly 1.5 * 2^23 + 256 * P_g.  With a = s_w / 256 and
-// b = -1.5 * 2^23 * a (both exact in fp32), fma(D, a, b) = s_w * P_g exactly
-// (11 + 13 significant bits), and acc = fma(that, s_x, acc) adds the group.
+// Dequantization: the first MFMA of a group takes the constant 0x4B400000
+// (the bit pattern of 1.5 * 2^23) as its C operand and the second chains on
+// it.  |256 * P_g| <= 2^20 < 2^22, so the int32 result read as fp32 is
+// exactly 1.5 * 2^23 + 256 * P_g.  With a = s_w / 256 and
+// b = -1.5 * 2^23 * a (both exact in fp32, kept per column in LDS),
+// fma(D, a, b) = s_w * P_g exactly (11 + 13 significant bits), and
+// acc = fma(that, s_x, acc) adds the group with one rounding.
+//
+// LDS layout of an unpacked operand row: 64 bytes per group = four 16-byte
+// chunks, chunk c holding k slice c (16 codes).  Chunk c of row r is stored
+// at position c ^ (((r >> 1) ^ (r >> 3)) & 3): 16-byte reads of 16
+// consecutive rows and the loader's writes then touch every bank once per
+// pass, for 32- and 64-bank LDS alike.
 constexpr int K2_BM = 128;
 constexpr int K2_BN = 128;
+constexpr int K2_SG = 2;                      // groups per pipeline stage
+constexpr int K2_WAVES = 8;
+constexpr int K2_THREADS = K2_WAVES * 64;
+constexpr int K2_WM = 32;                     // wave tile rows
+constexpr int K2_WN = 64;                     // wave tile columns
+constexpr int K2_TJ = K2_WN / 32;             // 32x32 tiles per wave along N
 constexpr int MAGIC_I = 0x4B400000;
-constexpr float MAGIC_F = 12582912.0f;  // 1.5 * 2^23
+constexpr float MAGIC_F = 12582912.0f;         // 1.5 * 2^23
 
-__device__ __forceinline__ v4i unpack16(uint2 p) {
-  v4i r;
-  r[0] = static_cast<int>((p.x << 4) & 0xF0F0F0F0u);
-  r[1] = static_cast<int>(p.x & 0xF0F0F0F0u);
-  r[2] = static_cast<int>((p.y << 4) & 0xF0F0F0F0u);
-  r[3] = static_cast<int>(p.y & 0xF0F0F0F0u);
-  return r;
+typedef int v16i __attribute__((ext_vector_type(16)));
+typedef float v16f __attribute__((ext_vector_type(16)));
+
+struct K2Smem {
+  uint4 a[2][K2_SG][K2_BM][4];                 // unpacked A, 16 B chunks
+  uint4 b[2][K2_SG][K2_BN][4];
+  _Float16 sx[2][K2_SG][K2_BM];                // activation scales
+  float2 wc[2][K2_SG][K2_BN];                  // (s_w / 256, -1.5*2^23 * s_w / 256)
+};
+
+__device__ __forceinline__ int k2_swz(int row, int chunk) { return chunk ^ (((row >> 1) ^ (row >> 3)) & 3); }
+
+// Map the linear block index to an output tile so that the blocks of one
+// XCD (the hardware deals blocks round-robin over 8 XCDs) cover a compact
+// band of rows and share A panels and B panels in their L2.
+__device__ __forceinline__ void k2_tile(int nM, int nN, int& tm, int& tn) {
+  const int nb = nM * nN;
+  const int b = blockIdx.x;
+  int t = b;
+  if ((nb & 7) == 0) t = (b & 7) * (nb >> 3) + (b >> 3);
+  constexpr int GM = 4;
+  const int per = GM * nN;
+  const int grp = t / per;
+  const int first = grp * GM;
+  const int gm = min(GM, nM - first);
+  const int r = t - grp * per;
+  tm = first + r % gm;
+  tn = r / gm;
 }
 
 template <int OUT_F32, int NT>
-__global__ __launch_bounds__(256) void k_gemm_w4a4_lora_up(
+__global__ __launch_bounds__(K2_THREADS, 2) void k_gemm_w4a4_lora_up(
     const uint8_t* __restrict__ x_codes, const _Float16* __restrict__ x_scales,
     const uint8_t* __restrict__ w_codes, const _Float16* __restrict__ w_scales,
     const float* __restrict__ lora_act, const uint16_t* __restrict__ lora_up,
     const uint16_t* __restrict__ bias, int M, int N, int K, int rank, void* __restrict__ y) {
-  __shared__ uint4 sA[2][K2_BM * 2];   // [row][2 x 16 B]
-  __shared__ uint4 sB[2][K2_BN * 2];
-  __shared__ _Float16 sSx[2][K2_BM];
-  __shared__ _Float16 sSw[2][K2_BN];
+  extern __shared__ __align__(16) unsigned char k2_smem_raw[];
+  K2Smem& sm = *reinterpret_cast<K2Smem*>(k2_smem_raw);
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
-  const int wave = tid >> 6;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // wave-uniform
   const int wm = wave >> 1, wn = wave & 1;
-  const int n0 = blockIdx.x * K2_BN;
-  const int m0 = blockIdx.y * K2_BM;
+  const int nM = (M + K2_BM - 1) / K2_BM, nN = (N + K2_BN - 1) / K2_BN;
+  int tm, tn;
+  k2_tile(nM, nN, tm, tn);
+  const int m0 = tm * K2_BM, n0 = tn * K2_BN;
   const int G = K / GROUP;
+  const int S = (G + K2_SG - 1) / K2_SG;       // stages
   const size_t Kb = static_cast<size_t>(K) / 2;
 
-  // global -> LDS assignment: thread t moves 16 bytes of row t/2 for A and B
-  const int lrow = tid >> 1, lhalf = tid & 1;
-  const bool a_ok = (m0 + lrow) < M;
-  const bool b_ok = (n0 + lrow) < N;
-  const uint8_t* a_src = x_codes + static_cast<size_t>(a_ok ? m0 + lrow : 0) * Kb + lhalf * 16;
-  const uint8_t* b_src = w_codes + static_cast<size_t>(b_ok ? n0 + lrow : 0) * Kb + lhalf * 16;
+  // loader role: thread t moves 16 packed bytes (codes 32h .. 32h+31) of
+  // group gi of row/column lr for both A and B, and (for h = 0) the x scale,
+  // (for h = 1) the w scale of that row/column and group.  Loads go through
+  // buffer resources whose size is the operand's size, so rows past M or N
+  // read as zero; the byte offset is pushed out of range for groups past G.
+  const int lr = tid & 127, lgi = (wave >> 1) & 1, lh = wave >> 2;
+  const __amdgpu_buffer_rsrc_t a_rs = __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<uint8_t*>(x_codes), 0, static_cast<int>(static_cast<size_t>(M) * Kb), 0x00020000);
+  const __amdgpu_buffer_rsrc_t b_rs = __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<uint8_t*>(w_codes), 0, static_cast<int>(static_cast<size_t>(N) * Kb), 0x00020000);
+  const bool s_row_ok = lh == 0 ? (m0 + lr) < M : (n0 + lr) < N;
+  const __amdgpu_buffer_rsrc_t s_rs = __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<_Float16*>(lh == 0 ? x_scales : w_scales), 0,
+      static_cast<int>(static_cast<size_t>(G) * (lh == 0 ? M : N) * 2), 0x00020000);
+  const uint32_t a_off0 = static_cast<uint32_t>((m0 + lr) * Kb + lgi * 32 + lh * 16);
+  const uint32_t b_off0 = static_cast<uint32_t>((n0 + lr) * Kb + lgi * 32 + lh * 16);
+  const uint32_t s_off0 = static_cast<uint32_t>(2 * (lgi * (lh == 0 ? M : N) + (lh == 0 ? m0 : n0) + lr));
+  const uint32_t s_step = static_cast<uint32_t>(2 * K2_SG * (lh == 0 ? M : N));
+  constexpr uint32_t OOB = 0x80000000u;
 
-  auto load_stage = [&](int g, uint4& ra, uint4& rb, _Float16& rs) {
-    ra = a_ok ? *reinterpret_cast<const uint4*>(a_src + static_cast<size_t>(g) * 32) : make_uint4(0, 0, 0, 0);
-    rb = b_ok ? *reinterpret_cast<const uint4*>(b_src + static_cast<size_t>(g) * 32) : make_uint4(0, 0, 0, 0);
-    if (tid < K2_BM) {
-      rs = (m0 + tid < M) ? x_scales[static_cast<size_t>(g) * M + m0 + tid] : static_cast<_Float16>(0.f);
+  uint4 ra, rb;
+  _Float16 rs;
+  auto load_stage = [&](int st) {
+    const bool g_ok = st * K2_SG + lgi < G;
+    const uint32_t ko = static_cast<uint32_t>(st) * (K2_SG * 32);
+    ra = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(a_rs, g_ok ? a_off0 + ko : OOB, 0, 0));
+    rb = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(b_rs, g_ok ? b_off0 + ko : OOB, 0, 0));
+    const unsigned short sv = __builtin_amdgcn_raw_buffer_load_b16(
+        s_rs, (g_ok && s_row_ok) ? s_off0 + static_cast<uint32_t>(st) * s_step : OOB, 0, 0);
+    rs = __builtin_bit_cast(_Float16, sv);
+  };
+  auto store_stage = [&](int buf) {
+    sm.a[buf][lgi][lr][k2_swz(lr, 2 * lh)] =
+        make_uint4((ra.x << 4) & 0xF0F0F0F0u, ra.x & 0xF0F0F0F0u, (ra.y << 4) & 0xF0F0F0F0u, ra.y & 0xF0F0F0F0u);
+    sm.a[buf][lgi][lr][k2_swz(lr, 2 * lh + 1)] =
+        make_uint4((ra.z << 4) & 0xF0F0F0F0u, ra.z & 0xF0F0F0F0u, (ra.w << 4) & 0xF0F0F0F0u, ra.w & 0xF0F0F0F0u);
+    sm.b[buf][lgi][lr][k2_swz(lr, 2 * lh)] =
+        make_uint4((rb.x << 4) & 0xF0F0F0F0u, rb.x & 0xF0F0F0F0u, (rb.y << 4) & 0xF0F0F0F0u, rb.y & 0xF0F0F0F0u);
+    sm.b[buf][lgi][lr][k2_swz(lr, 2 * lh + 1)] =
+        make_uint4((rb.z << 4) & 0xF0F0F0F0u, rb.z & 0xF0F0F0F0u, (rb.w << 4) & 0xF0F0F0F0u, rb.w & 0xF0F0F0F0u);
+    if (lh == 0) {
+      sm.sx[buf][lgi][lr] = rs;
     } else {
-      const int c = tid - K2_BM;
-      rs = (n0 + c < N) ? w_scales[static_cast<size_t>(g) * N + n0 + c] : static_cast<_Float16>(0.f);
+      const float aw = static_cast<float>(rs) * (1.0f / 256.0f);
+      sm.wc[buf][lgi][lr] = make_float2(aw, -MAGIC_F * aw);
     }
   };
-  auto store_stage = [&](int buf, const uint4& ra, const uint4& rb, const _Float16& rs) {
-    sA[buf][tid] = ra;
-    sB[buf][tid] = rb;
-    if (tid < K2_BM) sSx[buf][tid] = rs;
-    else sSw[buf][tid - K2_BM] = rs;
-  };
 
-  v4f acc[4][4];
+  v16f acc[K2_TJ];
 #pragma unroll
-  for (int i = 0; i < 4; ++i)
+  for (int j = 0; j < K2_TJ; ++j)
 #pragma unroll
-    for (int j = 0; j < 4; ++j) acc[i][j] = v4f{0.f, 0.f, 0.f, 0.f};
+    for (int v = 0; v < 16; ++v) acc[j][v] = 0.f;
 
-  const v4i cmagic = {MAGIC_I, MAGIC_I, MAGIC_I, MAGIC_I};
+  v16i cmagic;
+#pragma unroll
+  for (int v = 0; v < 16; ++v) cmagic[v] = MAGIC_I;
+  const int fr = lane & 31;      // fragment row / column within a 32-tile
+  const int fk = lane >> 5;      // K slice within a 32-k half
 
-  {
-    uint4 ra, rb;
-    _Float16 rs;
-    load_stage(0, ra, rb, rs);
-    store_stage(0, ra, rb, rs);
-  }
+  load_stage(0);
+  store_stage(0);
   __syncthreads();
 
-  const int fr = lane & 15;      // fragment row / column within a 16-tile
-  const int fk = lane >> 4;      // K slice (8 packed bytes) within the group
-  for (int g = 0; g < G; ++g) {
-    const int buf = g & 1;
-    uint4 ra, rb;
-    _Float16 rs;
-    const bool more = (g + 1) < G;
-    if (more) load_stage(g + 1, ra, rb, rs);
-
-    const uint2* pA = reinterpret_cast<const uint2*>(&sA[buf][0]);
-    const uint2* pB = reinterpret_cast<const uint2*>(&sB[buf][0]);
-    v4i af[4], bfr[4];
-#pragma unroll
-    for (int i = 0; i < 4; ++i) af[i] = unpack16(pA[(wm * 64 + i * 16 + fr) * 4 + fk]);
-#pragma unroll
-    for (int j = 0; j < 4; ++j) bfr[j] = unpack16(pB[(wn * 64 + j * 16 + fr) * 4 + fk]);
-    float ca[4], cb[4];
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      ca[j] = static_cast<float>(sSw[buf][wn * 64 + j * 16 + fr]) * (1.0f / 256.0f);
-      cb[j] = -MAGIC_F * ca[j];
-    }
-    float sx[4][4];
-#pragma unroll
-    for (int i = 0; i < 4; ++i)
-#pragma unroll
-      for (int r = 0; r < 4; ++r) sx[i][r] = static_cast<float>(sSx[buf][wm * 64 + i * 16 + 4 * fk + r]);
+  const int arow = wm * K2_WM + fr;
+  for (int st = 0; st < S; ++st) {
+    const int buf = st & 1;
+    const bool more = (st + 1) < S;
+    if (more) load_stage(st + 1);
 
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
+    for (int gi = 0; gi < K2_SG; ++gi) {
+      if (st * K2_SG + gi >= G) break;
+      // fragments: half h of the group is k slice 2h + fk
+      const v4i a0 = __builtin_bit_cast(v4i, sm.a[buf][gi][arow][k2_swz(arow, fk)]);
+      const v4i a1 = __builtin_bit_cast(v4i, sm.a[buf][gi][arow][k2_swz(arow, 2 + fk)]);
+      v4i b0[K2_TJ], b1[K2_TJ];
+      float2 wcj[K2_TJ];
 #pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const v4i d = __builtin_amdgcn_mfma_i32_16x16x64_i8(af[i], bfr[j], cmagic, 0, 0, 0);
+      for (int j = 0; j < K2_TJ; ++j) {
+        const int c = wn * K2_WN + j * 32 + fr;
+        b0[j] = __builtin_bit_cast(v4i, sm.b[buf][gi][c][k2_swz(c, fk)]);
+        b1[j] = __builtin_bit_cast(v4i, sm.b[buf][gi][c][k2_swz(c, 2 + fk)]);
+        wcj[j] = sm.wc[buf][gi][c];
+      }
+      // activation scales of this lane's rows 8b + 4 fk + i
+      _Float16 sxr[16];
 #pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          const float t = __builtin_fmaf(__int_as_float(d[r]), ca[j], cb[j]);
-          acc[i][j][r] = __builtin_fmaf(t, sx[i][r], acc[i][j][r]);
+      for (int bb = 0; bb < 4; ++bb) {
+        const uint2 raw = *reinterpret_cast<const uint2*>(&sm.sx[buf][gi][wm * K2_WM + 8 * bb + 4 * fk]);
+        const _Float16* h = reinterpret_cast<const _Float16*>(&raw);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) sxr[4 * bb + i] = h[i];
+      }
+      v16i d[K2_TJ];
+#pragma unroll
+      for (int j = 0; j < K2_TJ; ++j) d[j] = __builtin_amdgcn_mfma_i32_32x32x32_i8(a0, b0[j], cmagic, 0, 0, 0);
+#pragma unroll
+      for (int j = 0; j < K2_TJ; ++j) d[j] = __builtin_amdgcn_mfma_i32_32x32x32_i8(a1, b1[j], d[j], 0, 0, 0);
+#pragma unroll
+      for (int j = 0; j < K2_TJ; ++j) {
+#pragma unroll
+        for (int v = 0; v < 16; ++v) {
+          const float tv = __builtin_fmaf(__int_as_float(d[j][v]), wcj[j].x, wcj[j].y);
+          acc[j][v] = __builtin_fmaf(tv, static_cast<float>(sxr[v]), acc[j][v]);
         }
       }
     }
 
-    if (more) store_stage(buf ^ 1, ra, rb, rs);
+    if (more) store_stage(buf ^ 1);
     __syncthreads();
   }
 
-  // ---- epilogue: up projection (bf16 MFMA, K = rank in slices of 32) + bias
+  // ---- epilogue: up projection (bf16 MFMA 32x32x16, K = rank in slices of
+  // 16) + bias.  lora_act rows are the A operand, lora_up rows the B operand.
   if constexpr (NT > 0) {
-    for (int kk = 0; kk < rank; kk += 32) {
+    const int r = m0 + wm * K2_WM + fr;
+    for (int kk = 0; kk < rank; kk += 16) {
       const int kl = kk + fk * 8;          // this lane's 8 k values
-      const bool k_ok = kl < rank;         // rank % 32 == 16: upper half padded
-      v8bf la[4], ub[4];
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int r = m0 + wm * 64 + i * 16 + fr;
-        float v[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
-        if (k_ok && r < M) {
-          const float4* p = reinterpret_cast<const float4*>(lora_act + static_cast<size_t>(r) * rank + kl);
-          const float4 v0 = p[0], v1 = p[1];
-          v[0] = v0.x; v[1] = v0.y; v[2] = v0.z; v[3] = v0.w;
-          v[4] = v1.x; v[5] = v1.y; v[6] = v1.z; v[7] = v1.w;
-        }
-        la[i] = pack_bf16x8(v);
+      float v[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+      if (r < M) {
+        const float4* p = reinterpret_cast<const float4*>(lora_act + static_cast<size_t>(r) * rank + kl);
+        const float4 v0 = p[0], v1 = p[1];
+        v[0] = v0.x; v[1] = v0.y; v[2] = v0.z; v[3] = v0.w;
+        v[4] = v1.x; v[5] = v1.y; v[6] = v1.z; v[7] = v1.w;
       }
+      const v8bf la = pack_bf16x8(v);
 #pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const int c = n0 + wn * 64 + j * 16 + fr;
+      for (int j = 0; j < K2_TJ; ++j) {
+        const int c = n0 + wn * K2_WN + j * 32 + fr;
         uint4 u = make_uint4(0, 0, 0, 0);
-        if (k_ok && c < N) u = *reinterpret_cast<const uint4*>(lora_up + static_cast<size_t>(c) * rank + kl);
-        ub[j] = __builtin_bit_cast(v8bf, u);
+        if (c < N) u = *reinterpret_cast<const uint4*>(lora_up + static_cast<size_t>(c) * rank + kl);
+        acc[j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(la, __builtin_bit_cast(v8bf, u), acc[j], 0, 0, 0);
       }
-#pragma unroll
-      for (int i = 0; i < 4; ++i)
-#pragma unroll
-        for (int j = 0; j < 4; ++j) acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(la[i], ub[j], acc[i][j], 0, 0, 0);
     }
   }
 
 #pragma unroll
-  for (int j = 0; j < 4; ++j) {
-    const int c = n0 + wn * 64 + j * 16 + fr;
+  for (int j = 0; j < K2_TJ; ++j) {
+    const int c = n0 + wn * K2_WN + j * 32 + fr;
     if (c >= N) continue;
     const float bv = bias ? bf16_bits_to_f32(bias[c]) : 0.f;
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-#pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const int row = m0 + wm * 64 + i * 16 + 4 * fk + r;
-        if (row < M) {
-          const float v = acc[i][j][r] + bv;
-          if (OUT_F32) {
-            reinterpret_cast<float*>(y)[static_cast<size_t>(row) * N + c] = v;
-          } else {
-            reinterpret_cast<uint16_t*>(y)[static_cast<size_t>(row) * N + c] =
-                static_cast<uint16_t>(f32_to_bf16_bits(v));
-          }
+    for (int v = 0; v < 16; ++v) {
+      const int row = m0 + wm * K2_WM + 8 * (v >> 2) + 4 * fk + (v & 3);
+      if (row < M) {
+        const float o = acc[j][v] + bv;
+        if (OUT_F32) {
+          reinterpret_cast<float*>(y)[static_cast<size_t>(row) * N + c] = o;
+        } else {
+          reinterpret_cast<uint16_t*>(y)[static_cast<size_t>(row) * N + c] =
+              static_cast<uint16_t>(f32_to_bf16_bits(o));
         }
       }
     }
@@ -387,18 +450,29 @@ int launch_k1(const void* x, const float* smooth_inv, const void* lora_down, int
   return hipGetLastError() == hipSuccess ? SVDQ_OK : SVDQ_ERR_HIP;
 }
 
+template <int OUT_F32, int NT>
+void launch_k2_kernel(const void* xc, const void* xs, const void* wc, const void* ws, const float* la,
+                      const void* lu, const void* bias, int M, int N, int K, int rank, void* y,
+                      hipStream_t st) {
+  // the stage buffers exceed the default 64 KB of dynamic LDS: opt in once
+  static const bool attr_ok = [] {
+    return hipFuncSetAttribute(reinterpret_cast<const void*>(k_gemm_w4a4_lora_up<OUT_F32, NT>),
+                               hipFuncAttributeMaxDynamicSharedMemorySize,
+                               static_cast<int>(sizeof(K2Smem))) == hipSuccess;
+  }();
+  (void)attr_ok;
+  const int nb = ((N + K2_BN - 1) / K2_BN) * ((M + K2_BM - 1) / K2_BM);
+  hipLaunchKernelGGL((k_gemm_w4a4_lora_up<OUT_F32, NT>), dim3(nb), dim3(K2_THREADS), sizeof(K2Smem), st,
+                     static_cast<const uint8_t*>(xc), static_cast<const _Float16*>(xs),
+                     static_cast<const uint8_t*>(wc), static_cast<const _Float16*>(ws), la,
+                     static_cast<const uint16_t*>(lu), static_cast<const uint16_t*>(bias), M, N, K, rank, y);
+}
+
 template <int OUT_F32>
 int launch_k2(const void* xc, const void* xs, const void* wc, const void* ws, const float* la,
               const void* lu, const void* bias, int M, int N, int K, int rank, void* y, hipStream_t st) {
-  const dim3 grid((N + K2_BN - 1) / K2_BN, (M + K2_BM - 1) / K2_BM), block(256);
-  auto go = [&](auto kern) {
-    hipLaunchKernelGGL(kern, grid, block, 0, st, static_cast<const uint8_t*>(xc),
-                       static_cast<const _Float16*>(xs), static_cast<const uint8_t*>(wc),
-                       static_cast<const _Float16*>(ws), la, static_cast<const uint16_t*>(lu),
-                       static_cast<const uint16_t*>(bias), M, N, K, rank, y);
-  };
-  if (rank == 0) go(k_gemm_w4a4_lora_up<OUT_F32, 0>);
-  else go(k_gemm_w4a4_lora_up<OUT_F32, 1>);
+  if (rank == 0) launch_k2_kernel<OUT_F32, 0>(xc, xs, wc, ws, la, lu, bias, M, N, K, rank, y, st);
+  else launch_k2_kernel<OUT_F32, 1>(xc, xs, wc, ws, la, lu, bias, M, N, K, rank, y, st);
   return hipGetLastError() == hipSuccess ? SVDQ_OK : SVDQ_ERR_HIP;
 }
 
