@@ -110,6 +110,8 @@ def main():
     ap.add_argument("--no-overhead", action="store_true", help="skip the rank-0 comparison run")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
+    ap.add_argument("--copy-probe", type=int, default=0, metavar="MIB",
+                    help="only run a plain device copy of MIB MiB (HBM counter calibration)")
     args = ap.parse_args()
 
     if args.gpus != 1:
@@ -127,6 +129,17 @@ def main():
         print("bench.py needs a GPU", file=sys.stderr)
         sys.exit(1)
     torch.cuda.set_device(0)
+    if args.copy_probe:
+        # a plain copy of known size: FETCH_SIZE / WRITE_SIZE of this kernel
+        # calibrate the counters read for the layer's kernels
+        n = args.copy_probe * (1 << 20)
+        src = torch.ones(n, dtype=torch.uint8, device="cuda")
+        dst = torch.empty_like(src)
+        for _ in range(max(args.steps, 1)):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_probe_bytes": n, "launches": max(args.steps, 1)}))
+        return
     L.check(S.device_check(0), "device check")
 
     gen_name, layer, act, desc = BENCH_WORKLOADS[args.workload]
