@@ -179,14 +179,15 @@ __global__ __launch_bounds__(K1_WAVES * 64) void k_quant_act_lora_down(
 // =====================================================================
 // Kernel 2
 // =====================================================================
-// Block tile 128 x 128 with 8 waves in a 4 (M) x 2 (N) arrangement; each
-// wave owns 32 x 64 outputs = two 32 x 32 MFMA tiles.  One group of 64 k is
-// two v_mfma_i32_32x32x32_i8 per tile (the 32x32 form sustains ~1.4x the
-// int8 rate of the 16x16x64 form on gfx950).  The K loop runs in stages of
-// two groups: a stage is loaded from HBM as packed nibbles into registers
-// one stage ahead, unpacked cooperatively (once per block) and written to a
+// Block tile 128 x 128, 4 waves in a 2 x 2 arrangement; each wave owns
+// 64 x 64 outputs = 2 x 2 tiles of 32 x 32.  One group of 64 k is two
+// v_mfma_i32_32x32x32_i8 per tile (the 32x32 form sustains ~1.4x the int8
+// rate of the 16x16x64 form on gfx950).  The K loop runs in stages of two
+// groups: a stage is loaded from HBM as packed nibbles into registers one
+// stage ahead, unpacked cooperatively (once per block) and written to a
 // double-buffered LDS tile as int8 operands, so the waves read ready MFMA
-// fragments with one 16-byte LDS read each.
+// fragments with one 16-byte LDS read each.  Two blocks share a CU, so one
+// block's barrier and load waits overlap the other's compute.
 //
 // 32x32 MFMA layouts (wave64): A operand lane l holds row l % 32 and one K
 // slice chosen by l / 32; B operand lane l holds column l % 32 and the same
@@ -211,15 +212,19 @@ __global__ __launch_bounds__(K1_WAVES * 64) void k_quant_act_lora_down(
 // chunks, chunk c holding k slice c (16 codes).  Chunk c of row r is stored
 // at position c ^ (((r >> 1) ^ (r >> 3)) & 3): 16-byte reads of 16
 // consecutive rows and the loader's writes then touch every bank once per
-// pass, for 32- and 64-bank LDS alike.
+// pass, for 32- and 64-bank LDS alike.  Activation scales are stored per
+// 32-row tile in the order a lane consumes them (rows 8b + 4h + i at
+// position 16h + 4b + i), so a lane fetches its 16 scales with two 16-byte
+// reads.
 constexpr int K2_BM = 128;
 constexpr int K2_BN = 128;
 constexpr int K2_SG = 2;                      // groups per pipeline stage
-constexpr int K2_WAVES = 8;
+constexpr int K2_WAVES = 4;
 constexpr int K2_THREADS = K2_WAVES * 64;
-constexpr int K2_WM = 32;                     // wave tile rows
+constexpr int K2_WM = 64;                     // wave tile rows
 constexpr int K2_WN = 64;                     // wave tile columns
-constexpr int K2_TJ = K2_WN / 32;             // 32x32 tiles per wave along N
+constexpr int K2_TI = K2_WM / 32;             // 32x32 tiles per wave along M
+constexpr int K2_TJ = K2_WN / 32;             // along N
 constexpr int MAGIC_I = 0x4B400000;
 constexpr float MAGIC_F = 12582912.0f;         // 1.5 * 2^23
 
@@ -229,11 +234,17 @@ typedef float v16f __attribute__((ext_vector_type(16)));
 struct K2Smem {
   uint4 a[2][K2_SG][K2_BM][4];                 // unpacked A, 16 B chunks
   uint4 b[2][K2_SG][K2_BN][4];
-  _Float16 sx[2][K2_SG][K2_BM];                // activation scales
+  _Float16 sx[2][K2_SG][K2_BM];                // activation scales, per 32-row tile in lane order
   float2 wc[2][K2_SG][K2_BN];                  // (s_w / 256, -1.5*2^23 * s_w / 256)
 };
 
 __device__ __forceinline__ int k2_swz(int row, int chunk) { return chunk ^ (((row >> 1) ^ (row >> 3)) & 3); }
+
+// position of row r's activation scale inside its 32-row tile (lane order)
+__device__ __forceinline__ int k2_sxpos(int r) {
+  const int rr = r & 31;
+  return (r & ~31) | (((rr >> 2) & 1) << 4) | ((rr >> 3) << 2) | (rr & 3);
+}
 
 // Map the linear block index to an output tile so that the blocks of one
 // XCD (the hardware deals blocks round-robin over 8 XCDs) cover a compact
@@ -251,6 +262,13 @@ __device__ __forceinline__ void k2_tile(int nM, int nN, int& tm, int& tn) {
   const int r = t - grp * per;
   tm = first + r % gm;
   tn = r / gm;
+}
+
+__device__ __forceinline__ uint4 unpack_lo(uint4 w) {  // codes 0..15 of a 32-code chunk
+  return make_uint4((w.x << 4) & 0xF0F0F0F0u, w.x & 0xF0F0F0F0u, (w.y << 4) & 0xF0F0F0F0u, w.y & 0xF0F0F0F0u);
+}
+__device__ __forceinline__ uint4 unpack_hi(uint4 w) {  // codes 16..31
+  return make_uint4((w.z << 4) & 0xF0F0F0F0u, w.z & 0xF0F0F0F0u, (w.w << 4) & 0xF0F0F0F0u, w.w & 0xF0F0F0F0u);
 }
 
 template <int OUT_F32, int NT>
@@ -274,63 +292,71 @@ __global__ __launch_bounds__(K2_THREADS, 2) void k_gemm_w4a4_lora_up(
   const int S = (G + K2_SG - 1) / K2_SG;       // stages
   const size_t Kb = static_cast<size_t>(K) / 2;
 
-  // loader role: thread t moves 16 packed bytes (codes 32h .. 32h+31) of
-  // group gi of row/column lr for both A and B, and (for h = 0) the x scale,
-  // (for h = 1) the w scale of that row/column and group.  Loads go through
-  // buffer resources whose size is the operand's size, so rows past M or N
-  // read as zero; the byte offset is pushed out of range for groups past G.
-  const int lr = tid & 127, lgi = (wave >> 1) & 1, lh = wave >> 2;
+  // Loader roles per stage (2 groups): thread t moves both 16-byte halves of
+  // the 32 packed bytes of (row t & 127, group (t >> 7) & 1) for A and for B,
+  // plus that row's x scale and that column's w scale.  Loads go through
+  // buffer resources sized to the operand, so rows past M or N read as zero;
+  // the byte offset is pushed out of range for groups past G.  Every
+  // wave-uniform role is derived from the wave index.
+  const int l_r = tid & 127, l_g = (wave >> 1) & 1;
   const __amdgpu_buffer_rsrc_t a_rs = __builtin_amdgcn_make_buffer_rsrc(
       const_cast<uint8_t*>(x_codes), 0, static_cast<int>(static_cast<size_t>(M) * Kb), 0x00020000);
   const __amdgpu_buffer_rsrc_t b_rs = __builtin_amdgcn_make_buffer_rsrc(
       const_cast<uint8_t*>(w_codes), 0, static_cast<int>(static_cast<size_t>(N) * Kb), 0x00020000);
-  const bool s_row_ok = lh == 0 ? (m0 + lr) < M : (n0 + lr) < N;
-  const __amdgpu_buffer_rsrc_t s_rs = __builtin_amdgcn_make_buffer_rsrc(
-      const_cast<_Float16*>(lh == 0 ? x_scales : w_scales), 0,
-      static_cast<int>(static_cast<size_t>(G) * (lh == 0 ? M : N) * 2), 0x00020000);
-  const uint32_t a_off0 = static_cast<uint32_t>((m0 + lr) * Kb + lgi * 32 + lh * 16);
-  const uint32_t b_off0 = static_cast<uint32_t>((n0 + lr) * Kb + lgi * 32 + lh * 16);
-  const uint32_t s_off0 = static_cast<uint32_t>(2 * (lgi * (lh == 0 ? M : N) + (lh == 0 ? m0 : n0) + lr));
-  const uint32_t s_step = static_cast<uint32_t>(2 * K2_SG * (lh == 0 ? M : N));
+  const __amdgpu_buffer_rsrc_t sx_rs = __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<_Float16*>(x_scales), 0, static_cast<int>(static_cast<size_t>(G) * M * 2), 0x00020000);
+  const __amdgpu_buffer_rsrc_t sw_rs = __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<_Float16*>(w_scales), 0, static_cast<int>(static_cast<size_t>(G) * N * 2), 0x00020000);
+  const uint32_t a_off0 = static_cast<uint32_t>((m0 + l_r) * Kb + l_g * 32);
+  const uint32_t b_off0 = static_cast<uint32_t>((n0 + l_r) * Kb + l_g * 32);
+  const bool sx_row_ok = (m0 + l_r) < M;
+  const bool sw_row_ok = (n0 + l_r) < N;
+  const uint32_t sx_off0 = static_cast<uint32_t>(2 * (l_g * M + m0 + l_r));
+  const uint32_t sw_off0 = static_cast<uint32_t>(2 * (l_g * N + n0 + l_r));
   constexpr uint32_t OOB = 0x80000000u;
 
-  uint4 ra, rb;
-  _Float16 rs;
+  uint4 ra0, ra1, rb0, rb1;
+  _Float16 rsx, rsw;
   auto load_stage = [&](int st) {
-    const bool g_ok = st * K2_SG + lgi < G;
     const uint32_t ko = static_cast<uint32_t>(st) * (K2_SG * 32);
-    ra = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(a_rs, g_ok ? a_off0 + ko : OOB, 0, 0));
-    rb = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(b_rs, g_ok ? b_off0 + ko : OOB, 0, 0));
-    const unsigned short sv = __builtin_amdgcn_raw_buffer_load_b16(
-        s_rs, (g_ok && s_row_ok) ? s_off0 + static_cast<uint32_t>(st) * s_step : OOB, 0, 0);
-    rs = __builtin_bit_cast(_Float16, sv);
+    const bool gok = st * K2_SG + l_g < G;
+    ra0 = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(a_rs, gok ? a_off0 + ko : OOB, 0, 0));
+    ra1 = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(a_rs, gok ? a_off0 + ko + 16 : OOB, 0, 0));
+    rb0 = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(b_rs, gok ? b_off0 + ko : OOB, 0, 0));
+    rb1 = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(b_rs, gok ? b_off0 + ko + 16 : OOB, 0, 0));
+    rsx = __builtin_bit_cast(_Float16, __builtin_amdgcn_raw_buffer_load_b16(
+        sx_rs, (gok && sx_row_ok) ? sx_off0 + static_cast<uint32_t>(st) * (2 * K2_SG * M) : OOB, 0, 0));
+    rsw = __builtin_bit_cast(_Float16, __builtin_amdgcn_raw_buffer_load_b16(
+        sw_rs, (gok && sw_row_ok) ? sw_off0 + static_cast<uint32_t>(st) * (2 * K2_SG * N) : OOB, 0, 0));
   };
   auto store_stage = [&](int buf) {
-    sm.a[buf][lgi][lr][k2_swz(lr, 2 * lh)] =
-        make_uint4((ra.x << 4) & 0xF0F0F0F0u, ra.x & 0xF0F0F0F0u, (ra.y << 4) & 0xF0F0F0F0u, ra.y & 0xF0F0F0F0u);
-    sm.a[buf][lgi][lr][k2_swz(lr, 2 * lh + 1)] =
-        make_uint4((ra.z << 4) & 0xF0F0F0F0u, ra.z & 0xF0F0F0F0u, (ra.w << 4) & 0xF0F0F0F0u, ra.w & 0xF0F0F0F0u);
-    sm.b[buf][lgi][lr][k2_swz(lr, 2 * lh)] =
-        make_uint4((rb.x << 4) & 0xF0F0F0F0u, rb.x & 0xF0F0F0F0u, (rb.y << 4) & 0xF0F0F0F0u, rb.y & 0xF0F0F0F0u);
-    sm.b[buf][lgi][lr][k2_swz(lr, 2 * lh + 1)] =
-        make_uint4((rb.z << 4) & 0xF0F0F0F0u, rb.z & 0xF0F0F0F0u, (rb.w << 4) & 0xF0F0F0F0u, rb.w & 0xF0F0F0F0u);
-    if (lh == 0) {
-      sm.sx[buf][lgi][lr] = rs;
-    } else {
-      const float aw = static_cast<float>(rs) * (1.0f / 256.0f);
-      sm.wc[buf][lgi][lr] = make_float2(aw, -MAGIC_F * aw);
-    }
+    sm.a[buf][l_g][l_r][k2_swz(l_r, 0)] = unpack_lo(ra0);
+    sm.a[buf][l_g][l_r][k2_swz(l_r, 1)] = unpack_hi(ra0);
+    sm.a[buf][l_g][l_r][k2_swz(l_r, 2)] = unpack_lo(ra1);
+    sm.a[buf][l_g][l_r][k2_swz(l_r, 3)] = unpack_hi(ra1);
+    sm.b[buf][l_g][l_r][k2_swz(l_r, 0)] = unpack_lo(rb0);
+    sm.b[buf][l_g][l_r][k2_swz(l_r, 1)] = unpack_hi(rb0);
+    sm.b[buf][l_g][l_r][k2_swz(l_r, 2)] = unpack_lo(rb1);
+    sm.b[buf][l_g][l_r][k2_swz(l_r, 3)] = unpack_hi(rb1);
+    sm.sx[buf][l_g][k2_sxpos(l_r)] = rsx;
+    const float aw = static_cast<float>(rsw) * (1.0f / 256.0f);
+    sm.wc[buf][l_g][l_r] = make_float2(aw, -MAGIC_F * aw);
   };
 
-  v16f acc[K2_TJ];
+  v16f acc[K2_TI][K2_TJ];
 #pragma unroll
-  for (int j = 0; j < K2_TJ; ++j)
+  for (int i = 0; i < K2_TI; ++i)
 #pragma unroll
-    for (int v = 0; v < 16; ++v) acc[j][v] = 0.f;
+    for (int j = 0; j < K2_TJ; ++j)
+#pragma unroll
+      for (int v = 0; v < 16; ++v) acc[i][j][v] = 0.f;
 
   v16i cmagic;
 #pragma unroll
   for (int v = 0; v < 16; ++v) cmagic[v] = MAGIC_I;
+  // opaque to the optimizer: kept in 16 VGPRs instead of being rebuilt from
+  // scalar constants before every MFMA that reads it
+  asm volatile("" : "+v"(cmagic));
   const int fr = lane & 31;      // fragment row / column within a 32-tile
   const int fk = lane >> 5;      // K slice within a 32-k half
 
@@ -338,7 +364,6 @@ __global__ __launch_bounds__(K2_THREADS, 2) void k_gemm_w4a4_lora_up(
   store_stage(0);
   __syncthreads();
 
-  const int arow = wm * K2_WM + fr;
   for (int st = 0; st < S; ++st) {
     const int buf = st & 1;
     const bool more = (st + 1) < S;
@@ -347,38 +372,51 @@ __global__ __launch_bounds__(K2_THREADS, 2) void k_gemm_w4a4_lora_up(
 #pragma unroll
     for (int gi = 0; gi < K2_SG; ++gi) {
       if (st * K2_SG + gi >= G) break;
-      // fragments: half h of the group is k slice 2h + fk
-      const v4i a0 = __builtin_bit_cast(v4i, sm.a[buf][gi][arow][k2_swz(arow, fk)]);
-      const v4i a1 = __builtin_bit_cast(v4i, sm.a[buf][gi][arow][k2_swz(arow, 2 + fk)]);
-      v4i b0[K2_TJ], b1[K2_TJ];
-      float2 wcj[K2_TJ];
+      v4i af[K2_TI][2], bfr[K2_TJ][2];
+#pragma unroll
+      for (int i = 0; i < K2_TI; ++i) {
+        const int r = wm * K2_WM + i * 32 + fr;
+        af[i][0] = __builtin_bit_cast(v4i, sm.a[buf][gi][r][k2_swz(r, fk)]);
+        af[i][1] = __builtin_bit_cast(v4i, sm.a[buf][gi][r][k2_swz(r, 2 + fk)]);
+      }
 #pragma unroll
       for (int j = 0; j < K2_TJ; ++j) {
         const int c = wn * K2_WN + j * 32 + fr;
-        b0[j] = __builtin_bit_cast(v4i, sm.b[buf][gi][c][k2_swz(c, fk)]);
-        b1[j] = __builtin_bit_cast(v4i, sm.b[buf][gi][c][k2_swz(c, 2 + fk)]);
-        wcj[j] = sm.wc[buf][gi][c];
+        bfr[j][0] = __builtin_bit_cast(v4i, sm.b[buf][gi][c][k2_swz(c, fk)]);
+        bfr[j][1] = __builtin_bit_cast(v4i, sm.b[buf][gi][c][k2_swz(c, 2 + fk)]);
       }
-      // activation scales of this lane's rows 8b + 4 fk + i
-      _Float16 sxr[16];
+      float2 wcj[K2_TJ];
 #pragma unroll
-      for (int bb = 0; bb < 4; ++bb) {
-        const uint2 raw = *reinterpret_cast<const uint2*>(&sm.sx[buf][gi][wm * K2_WM + 8 * bb + 4 * fk]);
-        const _Float16* h = reinterpret_cast<const _Float16*>(&raw);
+      for (int j = 0; j < K2_TJ; ++j) wcj[j] = sm.wc[buf][gi][wn * K2_WN + j * 32 + fr];
+      // this lane's 16 activation scales per row tile: positions 16 fk .. 16 fk + 15
+      uint4 sxr[K2_TI][2];
 #pragma unroll
-        for (int i = 0; i < 4; ++i) sxr[4 * bb + i] = h[i];
+      for (int i = 0; i < K2_TI; ++i) {
+        const uint4* p = reinterpret_cast<const uint4*>(&sm.sx[buf][gi][wm * K2_WM + i * 32 + 16 * fk]);
+        sxr[i][0] = p[0];
+        sxr[i][1] = p[1];
       }
-      v16i d[K2_TJ];
+      v16i d[K2_TI][K2_TJ];
 #pragma unroll
-      for (int j = 0; j < K2_TJ; ++j) d[j] = __builtin_amdgcn_mfma_i32_32x32x32_i8(a0, b0[j], cmagic, 0, 0, 0);
+      for (int i = 0; i < K2_TI; ++i)
 #pragma unroll
-      for (int j = 0; j < K2_TJ; ++j) d[j] = __builtin_amdgcn_mfma_i32_32x32x32_i8(a1, b1[j], d[j], 0, 0, 0);
+        for (int j = 0; j < K2_TJ; ++j)
+          d[i][j] = __builtin_amdgcn_mfma_i32_32x32x32_i8(af[i][0], bfr[j][0], cmagic, 0, 0, 0);
 #pragma unroll
-      for (int j = 0; j < K2_TJ; ++j) {
+      for (int i = 0; i < K2_TI; ++i)
 #pragma unroll
-        for (int v = 0; v < 16; ++v) {
-          const float tv = __builtin_fmaf(__int_as_float(d[j][v]), wcj[j].x, wcj[j].y);
-          acc[j][v] = __builtin_fmaf(tv, static_cast<float>(sxr[v]), acc[j][v]);
+        for (int j = 0; j < K2_TJ; ++j)
+          d[i][j] = __builtin_amdgcn_mfma_i32_32x32x32_i8(af[i][1], bfr[j][1], d[i][j], 0, 0, 0);
+#pragma unroll
+      for (int i = 0; i < K2_TI; ++i) {
+        const _Float16* sh = reinterpret_cast<const _Float16*>(&sxr[i][0]);
+#pragma unroll
+        for (int j = 0; j < K2_TJ; ++j) {
+#pragma unroll
+          for (int v = 0; v < 16; ++v) {
+            const float tv = __builtin_fmaf(__int_as_float(d[i][j][v]), wcj[j].x, wcj[j].y);
+            acc[i][j][v] = __builtin_fmaf(tv, static_cast<float>(sh[v]), acc[i][j][v]);
+          }
         }
       }
     }
@@ -390,23 +428,30 @@ __global__ __launch_bounds__(K2_THREADS, 2) void k_gemm_w4a4_lora_up(
   // ---- epilogue: up projection (bf16 MFMA 32x32x16, K = rank in slices of
   // 16) + bias.  lora_act rows are the A operand, lora_up rows the B operand.
   if constexpr (NT > 0) {
-    const int r = m0 + wm * K2_WM + fr;
     for (int kk = 0; kk < rank; kk += 16) {
       const int kl = kk + fk * 8;          // this lane's 8 k values
-      float v[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
-      if (r < M) {
-        const float4* p = reinterpret_cast<const float4*>(lora_act + static_cast<size_t>(r) * rank + kl);
-        const float4 v0 = p[0], v1 = p[1];
-        v[0] = v0.x; v[1] = v0.y; v[2] = v0.z; v[3] = v0.w;
-        v[4] = v1.x; v[5] = v1.y; v[6] = v1.z; v[7] = v1.w;
+      v8bf la[K2_TI];
+#pragma unroll
+      for (int i = 0; i < K2_TI; ++i) {
+        const int r = m0 + wm * K2_WM + i * 32 + fr;
+        float v[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+        if (r < M) {
+          const float4* p = reinterpret_cast<const float4*>(lora_act + static_cast<size_t>(r) * rank + kl);
+          const float4 v0 = p[0], v1 = p[1];
+          v[0] = v0.x; v[1] = v0.y; v[2] = v0.z; v[3] = v0.w;
+          v[4] = v1.x; v[5] = v1.y; v[6] = v1.z; v[7] = v1.w;
+        }
+        la[i] = pack_bf16x8(v);
       }
-      const v8bf la = pack_bf16x8(v);
 #pragma unroll
       for (int j = 0; j < K2_TJ; ++j) {
         const int c = n0 + wn * K2_WN + j * 32 + fr;
         uint4 u = make_uint4(0, 0, 0, 0);
         if (c < N) u = *reinterpret_cast<const uint4*>(lora_up + static_cast<size_t>(c) * rank + kl);
-        acc[j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(la, __builtin_bit_cast(v8bf, u), acc[j], 0, 0, 0);
+        const v8bf ub = __builtin_bit_cast(v8bf, u);
+#pragma unroll
+        for (int i = 0; i < K2_TI; ++i)
+          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(la[i], ub, acc[i][j], 0, 0, 0);
       }
     }
   }
@@ -417,15 +462,18 @@ __global__ __launch_bounds__(K2_THREADS, 2) void k_gemm_w4a4_lora_up(
     if (c >= N) continue;
     const float bv = bias ? bf16_bits_to_f32(bias[c]) : 0.f;
 #pragma unroll
-    for (int v = 0; v < 16; ++v) {
-      const int row = m0 + wm * K2_WM + 8 * (v >> 2) + 4 * fk + (v & 3);
-      if (row < M) {
-        const float o = acc[j][v] + bv;
-        if (OUT_F32) {
-          reinterpret_cast<float*>(y)[static_cast<size_t>(row) * N + c] = o;
-        } else {
-          reinterpret_cast<uint16_t*>(y)[static_cast<size_t>(row) * N + c] =
-              static_cast<uint16_t>(f32_to_bf16_bits(o));
+    for (int i = 0; i < K2_TI; ++i) {
+#pragma unroll
+      for (int v = 0; v < 16; ++v) {
+        const int row = m0 + wm * K2_WM + i * 32 + 8 * (v >> 2) + 4 * fk + (v & 3);
+        if (row < M) {
+          const float o = acc[i][j][v] + bv;
+          if (OUT_F32) {
+            reinterpret_cast<float*>(y)[static_cast<size_t>(row) * N + c] = o;
+          } else {
+            reinterpret_cast<uint16_t*>(y)[static_cast<size_t>(row) * N + c] =
+                static_cast<uint16_t>(f32_to_bf16_bits(o));
+          }
         }
       }
     }
