@@ -180,7 +180,11 @@ __global__ __launch_bounds__(K1_WAVES * 64) void k_quant_act_lora_down(
 // Kernel 2
 // =====================================================================
 // Block tile 128 x 128, 4 waves in a 2 x 2 arrangement; each wave owns
-// 64 x 64 outputs = 2 x 2 tiles of 32 x 32.  One group of 64 k is two
+// 64 x 64 outputs = 2 x 2 tiles of 32 x 32.  Each tile is computed
+// transposed, Y^T = W^T X^T: the weight fragment is the MFMA A operand and
+// the activation fragment the B operand, so in the 32x32 result layout a lane
+// holds one output row and runs of four consecutive output columns, which
+// the epilogue stores as 8-byte bf16 chunks.  One group of 64 k is two
 // v_mfma_i32_32x32x32_i8 per tile (the 32x32 form sustains ~1.4x the int8
 // rate of the 16x16x64 form on gfx950).  The K loop runs in stages of two
 // groups: a stage is loaded from HBM as packed nibbles into registers one
@@ -192,7 +196,8 @@ __global__ __launch_bounds__(K1_WAVES * 64) void k_quant_act_lora_down(
 // 32x32 MFMA layouts (wave64): A operand lane l holds row l % 32 and one K
 // slice chosen by l / 32; B operand lane l holds column l % 32 and the same
 // slice; C/D lane l holds column l % 32, rows 8b + 4(l / 32) + i in register
-// 4b + i (b, i = 0..3).
+// 4b + i (b, i = 0..3).  Here D rows are output columns n, D columns are
+// output rows m.
 //
 // Unpacking: a packed dword holds 8 codes (byte j = code 2j low, 2j+1 high).
 // (w << 4) & 0xF0F0F0F0 puts the even codes in the high nibble of each byte
@@ -203,17 +208,18 @@ __global__ __launch_bounds__(K1_WAVES * 64) void k_quant_act_lora_down(
 // Dequantization: the first MFMA of a group takes the constant 0x4B400000
 // (the bit pattern of 1.5 * 2^23) as its C operand and the second chains on
 // it.  |256 * P_g| <= 2^20 < 2^22, so the int32 result read as fp32 is
-// exactly 1.5 * 2^23 + 256 * P_g.  With a = s_w / 256 and
-// b = -1.5 * 2^23 * a (both exact in fp32, kept per column in LDS),
-// fma(D, a, b) = s_w * P_g exactly (11 + 13 significant bits), and
-// acc = fma(that, s_x, acc) adds the group with one rounding.
+// exactly 1.5 * 2^23 + 256 * P_g.  With a = s_x / 256 and
+// b = -1.5 * 2^23 * a (both exact in fp32, kept per output row in LDS),
+// fma(D, a, b) = s_x * P_g exactly (11 + 13 significant bits), and
+// acc = fma(that, s_w, acc) adds the group with one rounding of
+// s_x s_w P_g + acc.
 //
 // LDS layout of an unpacked operand row: 64 bytes per group = four 16-byte
 // chunks, chunk c holding k slice c (16 codes).  Chunk c of row r is stored
 // at position c ^ (((r >> 1) ^ (r >> 3)) & 3): 16-byte reads of 16
 // consecutive rows and the loader's writes then touch every bank once per
-// pass, for 32- and 64-bank LDS alike.  Activation scales are stored per
-// 32-row tile in the order a lane consumes them (rows 8b + 4h + i at
+// pass, for 32- and 64-bank LDS alike.  Weight scales are stored per 32-
+// column tile in the order a lane consumes them (columns 8b + 4h + i at
 // position 16h + 4b + i), so a lane fetches its 16 scales with two 16-byte
 // reads.
 constexpr int K2_BM = 128;
@@ -221,8 +227,8 @@ constexpr int K2_BN = 128;
 constexpr int K2_SG = 2;                      // groups per pipeline stage
 constexpr int K2_WAVES = 4;
 constexpr int K2_THREADS = K2_WAVES * 64;
-constexpr int K2_WM = 64;                     // wave tile rows
-constexpr int K2_WN = 64;                     // wave tile columns
+constexpr int K2_WM = 64;                     // wave tile rows (m)
+constexpr int K2_WN = 64;                     // wave tile columns (n)
 constexpr int K2_TI = K2_WM / 32;             // 32x32 tiles per wave along M
 constexpr int K2_TJ = K2_WN / 32;             // along N
 constexpr int MAGIC_I = 0x4B400000;
@@ -232,18 +238,18 @@ typedef int v16i __attribute__((ext_vector_type(16)));
 typedef float v16f __attribute__((ext_vector_type(16)));
 
 struct K2Smem {
-  uint4 a[2][K2_SG][K2_BM][4];                 // unpacked A, 16 B chunks
-  uint4 b[2][K2_SG][K2_BN][4];
-  _Float16 sx[2][K2_SG][K2_BM];                // activation scales, per 32-row tile in lane order
-  float2 wc[2][K2_SG][K2_BN];                  // (s_w / 256, -1.5*2^23 * s_w / 256)
+  uint4 a[2][K2_SG][K2_BM][4];                 // unpacked activations, 16 B chunks
+  uint4 b[2][K2_SG][K2_BN][4];                 // unpacked weights
+  float2 xc[2][K2_SG][K2_BM];                  // (s_x / 256, -1.5*2^23 * s_x / 256) per row
+  _Float16 sw[2][K2_SG][K2_BN];                // weight scales, per 32-column tile in lane order
 };
 
 __device__ __forceinline__ int k2_swz(int row, int chunk) { return chunk ^ (((row >> 1) ^ (row >> 3)) & 3); }
 
-// position of row r's activation scale inside its 32-row tile (lane order)
-__device__ __forceinline__ int k2_sxpos(int r) {
-  const int rr = r & 31;
-  return (r & ~31) | (((rr >> 2) & 1) << 4) | ((rr >> 3) << 2) | (rr & 3);
+// position of column c's weight scale inside its 32-column tile (lane order)
+__device__ __forceinline__ int k2_swpos(int c) {
+  const int cc = c & 31;
+  return (c & ~31) | (((cc >> 2) & 1) << 4) | ((cc >> 3) << 2) | (cc & 3);
 }
 
 // Map the linear block index to an output tile so that the blocks of one
@@ -293,11 +299,12 @@ __global__ __launch_bounds__(K2_THREADS, 2) void k_gemm_w4a4_lora_up(
   const size_t Kb = static_cast<size_t>(K) / 2;
 
   // Loader roles per stage (2 groups): thread t moves both 16-byte halves of
-  // the 32 packed bytes of (row t & 127, group (t >> 7) & 1) for A and for B,
-  // plus that row's x scale and that column's w scale.  Loads go through
-  // buffer resources sized to the operand, so rows past M or N read as zero;
-  // the byte offset is pushed out of range for groups past G.  Every
-  // wave-uniform role is derived from the wave index.
+  // the 32 packed bytes of (row t & 127, group (t >> 7) & 1) for the
+  // activations and for the weights, plus that row's x scale and that
+  // column's w scale.  Loads go through buffer resources sized to the
+  // operand, so rows past M or N read as zero; the byte offset is pushed
+  // out of range for groups past G.  Wave-uniform roles come from the wave
+  // index.
   const int l_r = tid & 127, l_g = (wave >> 1) & 1;
   const __amdgpu_buffer_rsrc_t a_rs = __builtin_amdgcn_make_buffer_rsrc(
       const_cast<uint8_t*>(x_codes), 0, static_cast<int>(static_cast<size_t>(M) * Kb), 0x00020000);
@@ -338,9 +345,9 @@ __global__ __launch_bounds__(K2_THREADS, 2) void k_gemm_w4a4_lora_up(
     sm.b[buf][l_g][l_r][k2_swz(l_r, 1)] = unpack_hi(rb0);
     sm.b[buf][l_g][l_r][k2_swz(l_r, 2)] = unpack_lo(rb1);
     sm.b[buf][l_g][l_r][k2_swz(l_r, 3)] = unpack_hi(rb1);
-    sm.sx[buf][l_g][k2_sxpos(l_r)] = rsx;
-    const float aw = static_cast<float>(rsw) * (1.0f / 256.0f);
-    sm.wc[buf][l_g][l_r] = make_float2(aw, -MAGIC_F * aw);
+    const float ax = static_cast<float>(rsx) * (1.0f / 256.0f);
+    sm.xc[buf][l_g][l_r] = make_float2(ax, -MAGIC_F * ax);
+    sm.sw[buf][l_g][k2_swpos(l_r)] = rsw;
   };
 
   v16f acc[K2_TI][K2_TJ];
@@ -372,49 +379,49 @@ __global__ __launch_bounds__(K2_THREADS, 2) void k_gemm_w4a4_lora_up(
 #pragma unroll
     for (int gi = 0; gi < K2_SG; ++gi) {
       if (st * K2_SG + gi >= G) break;
-      v4i af[K2_TI][2], bfr[K2_TJ][2];
+      v4i xf[K2_TI][2], wf[K2_TJ][2];
 #pragma unroll
       for (int i = 0; i < K2_TI; ++i) {
         const int r = wm * K2_WM + i * 32 + fr;
-        af[i][0] = __builtin_bit_cast(v4i, sm.a[buf][gi][r][k2_swz(r, fk)]);
-        af[i][1] = __builtin_bit_cast(v4i, sm.a[buf][gi][r][k2_swz(r, 2 + fk)]);
+        xf[i][0] = __builtin_bit_cast(v4i, sm.a[buf][gi][r][k2_swz(r, fk)]);
+        xf[i][1] = __builtin_bit_cast(v4i, sm.a[buf][gi][r][k2_swz(r, 2 + fk)]);
       }
 #pragma unroll
       for (int j = 0; j < K2_TJ; ++j) {
         const int c = wn * K2_WN + j * 32 + fr;
-        bfr[j][0] = __builtin_bit_cast(v4i, sm.b[buf][gi][c][k2_swz(c, fk)]);
-        bfr[j][1] = __builtin_bit_cast(v4i, sm.b[buf][gi][c][k2_swz(c, 2 + fk)]);
+        wf[j][0] = __builtin_bit_cast(v4i, sm.b[buf][gi][c][k2_swz(c, fk)]);
+        wf[j][1] = __builtin_bit_cast(v4i, sm.b[buf][gi][c][k2_swz(c, 2 + fk)]);
       }
-      float2 wcj[K2_TJ];
+      float2 xci[K2_TI];
 #pragma unroll
-      for (int j = 0; j < K2_TJ; ++j) wcj[j] = sm.wc[buf][gi][wn * K2_WN + j * 32 + fr];
-      // this lane's 16 activation scales per row tile: positions 16 fk .. 16 fk + 15
-      uint4 sxr[K2_TI][2];
+      for (int i = 0; i < K2_TI; ++i) xci[i] = sm.xc[buf][gi][wm * K2_WM + i * 32 + fr];
+      // this lane's 16 weight scales per column tile: positions 16 fk .. 16 fk + 15
+      uint4 swr[K2_TJ][2];
 #pragma unroll
-      for (int i = 0; i < K2_TI; ++i) {
-        const uint4* p = reinterpret_cast<const uint4*>(&sm.sx[buf][gi][wm * K2_WM + i * 32 + 16 * fk]);
-        sxr[i][0] = p[0];
-        sxr[i][1] = p[1];
+      for (int j = 0; j < K2_TJ; ++j) {
+        const uint4* p = reinterpret_cast<const uint4*>(&sm.sw[buf][gi][wn * K2_WN + j * 32 + 16 * fk]);
+        swr[j][0] = p[0];
+        swr[j][1] = p[1];
       }
       v16i d[K2_TI][K2_TJ];
 #pragma unroll
       for (int i = 0; i < K2_TI; ++i)
 #pragma unroll
         for (int j = 0; j < K2_TJ; ++j)
-          d[i][j] = __builtin_amdgcn_mfma_i32_32x32x32_i8(af[i][0], bfr[j][0], cmagic, 0, 0, 0);
+          d[i][j] = __builtin_amdgcn_mfma_i32_32x32x32_i8(wf[j][0], xf[i][0], cmagic, 0, 0, 0);
 #pragma unroll
       for (int i = 0; i < K2_TI; ++i)
 #pragma unroll
         for (int j = 0; j < K2_TJ; ++j)
-          d[i][j] = __builtin_amdgcn_mfma_i32_32x32x32_i8(af[i][1], bfr[j][1], d[i][j], 0, 0, 0);
+          d[i][j] = __builtin_amdgcn_mfma_i32_32x32x32_i8(wf[j][1], xf[i][1], d[i][j], 0, 0, 0);
 #pragma unroll
       for (int i = 0; i < K2_TI; ++i) {
-        const _Float16* sh = reinterpret_cast<const _Float16*>(&sxr[i][0]);
 #pragma unroll
         for (int j = 0; j < K2_TJ; ++j) {
+          const _Float16* sh = reinterpret_cast<const _Float16*>(&swr[j][0]);
 #pragma unroll
           for (int v = 0; v < 16; ++v) {
-            const float tv = __builtin_fmaf(__int_as_float(d[i][j][v]), wcj[j].x, wcj[j].y);
+            const float tv = __builtin_fmaf(__int_as_float(d[i][j][v]), xci[i].x, xci[i].y);
             acc[i][j][v] = __builtin_fmaf(tv, static_cast<float>(sh[v]), acc[i][j][v]);
           }
         }
@@ -426,7 +433,8 @@ __global__ __launch_bounds__(K2_THREADS, 2) void k_gemm_w4a4_lora_up(
   }
 
   // ---- epilogue: up projection (bf16 MFMA 32x32x16, K = rank in slices of
-  // 16) + bias.  lora_act rows are the A operand, lora_up rows the B operand.
+  // 16), transposed like the main product: lora_up rows are the A operand,
+  // lora_act rows the B operand.
   if constexpr (NT > 0) {
     for (int kk = 0; kk < rank; kk += 16) {
       const int kl = kk + fk * 8;          // this lane's 8 k values
@@ -451,31 +459,80 @@ __global__ __launch_bounds__(K2_THREADS, 2) void k_gemm_w4a4_lora_up(
         const v8bf ub = __builtin_bit_cast(v8bf, u);
 #pragma unroll
         for (int i = 0; i < K2_TI; ++i)
-          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(la[i], ub, acc[i][j], 0, 0, 0);
+          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ub, la[i], acc[i][j], 0, 0, 0);
       }
     }
   }
 
-#pragma unroll
-  for (int j = 0; j < K2_TJ; ++j) {
-    const int c = n0 + wn * K2_WN + j * 32 + fr;
-    if (c >= N) continue;
-    const float bv = bias ? bf16_bits_to_f32(bias[c]) : 0.f;
+  // ---- bias and store.  A lane holds output row m and columns
+  // 8b + 4 fk + (0..3) of each 32-column tile.  bf16 output goes through
+  // LDS (free after the K loop's last barrier): each wave writes its 64 x 64
+  // tile with 8-byte writes, then stores whole 128-byte row segments, eight
+  // rows per instruction.  16-byte chunk c of tile row r sits at chunk
+  // c ^ (r & 7), which keeps both LDS passes free of bank conflicts.
+  if (OUT_F32) {
 #pragma unroll
     for (int i = 0; i < K2_TI; ++i) {
+      const int row = m0 + wm * K2_WM + i * 32 + fr;
+      if (row >= M) continue;
 #pragma unroll
-      for (int v = 0; v < 16; ++v) {
-        const int row = m0 + wm * K2_WM + i * 32 + 8 * (v >> 2) + 4 * fk + (v & 3);
-        if (row < M) {
-          const float o = acc[i][j][v] + bv;
-          if (OUT_F32) {
-            reinterpret_cast<float*>(y)[static_cast<size_t>(row) * N + c] = o;
-          } else {
-            reinterpret_cast<uint16_t*>(y)[static_cast<size_t>(row) * N + c] =
-                static_cast<uint16_t>(f32_to_bf16_bits(o));
+      for (int j = 0; j < K2_TJ; ++j) {
+#pragma unroll
+        for (int bb = 0; bb < 4; ++bb) {
+          const int c = n0 + wn * K2_WN + j * 32 + 8 * bb + 4 * fk;   // N % 8 == 0: all four in or out
+          if (c >= N) continue;
+          float o[4];
+#pragma unroll
+          for (int e = 0; e < 4; ++e) o[e] = acc[i][j][4 * bb + e];
+          if (bias) {
+            const uint2 bv = *reinterpret_cast<const uint2*>(bias + c);
+            o[0] += bf16_bits_to_f32(bv.x & 0xFFFFu);
+            o[1] += bf16_bits_to_f32(bv.x >> 16);
+            o[2] += bf16_bits_to_f32(bv.y & 0xFFFFu);
+            o[3] += bf16_bits_to_f32(bv.y >> 16);
           }
+          *reinterpret_cast<float4*>(reinterpret_cast<float*>(y) + static_cast<size_t>(row) * N + c) =
+              make_float4(o[0], o[1], o[2], o[3]);
         }
       }
+    }
+  } else {
+    uint2* tile = reinterpret_cast<uint2*>(k2_smem_raw) + wave * (K2_WM * K2_WN / 4);  // 64 x 64 bf16
+#pragma unroll
+    for (int i = 0; i < K2_TI; ++i) {
+      const int rl = i * 32 + fr;
+#pragma unroll
+      for (int j = 0; j < K2_TJ; ++j) {
+#pragma unroll
+        for (int bb = 0; bb < 4; ++bb) {
+          const int c = n0 + wn * K2_WN + j * 32 + 8 * bb + 4 * fk;
+          float o[4];
+#pragma unroll
+          for (int e = 0; e < 4; ++e) o[e] = acc[i][j][4 * bb + e];
+          if (bias && c < N) {
+            const uint2 bv = *reinterpret_cast<const uint2*>(bias + c);
+            o[0] += bf16_bits_to_f32(bv.x & 0xFFFFu);
+            o[1] += bf16_bits_to_f32(bv.x >> 16);
+            o[2] += bf16_bits_to_f32(bv.y & 0xFFFFu);
+            o[3] += bf16_bits_to_f32(bv.y >> 16);
+          }
+          const int chunk = j * 4 + bb;                 // 16-byte chunk of the 128-byte tile row
+          tile[rl * 16 + ((chunk ^ (rl & 7)) << 1) + fk] =
+              make_uint2(f32_to_bf16_bits(o[0]) | (f32_to_bf16_bits(o[1]) << 16),
+                         f32_to_bf16_bits(o[2]) | (f32_to_bf16_bits(o[3]) << 16));
+        }
+      }
+    }
+    const uint4* tile4 = reinterpret_cast<const uint4*>(tile);
+    const int cl = lane & 7;                            // 16-byte chunk this lane stores
+    const int col = n0 + wn * K2_WN + cl * 8;
+#pragma unroll
+    for (int it = 0; it < K2_WM / 8; ++it) {
+      const int rl = it * 8 + (lane >> 3);
+      const uint4 v = tile4[rl * 8 + (cl ^ (rl & 7))];
+      const int row = m0 + wm * K2_WM + rl;
+      if (row < M && col < N)
+        *reinterpret_cast<uint4*>(reinterpret_cast<uint16_t*>(y) + static_cast<size_t>(row) * N + col) = v;
     }
   }
 }
