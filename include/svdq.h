@@ -135,7 +135,8 @@ int svdq_prepare_weights_ex(const uint16_t* weight, int K, int N,
  *                                (NULL allowed when rank == 0)
  * with x_hat = fp32(act(x) * smooth_inv).  |x_hat| above 7 * 65504 in a
  * group overflows the fp16 scale to inf (codes 0); such inputs are outside
- * the supported range. */
+ * the supported range.  K is limited to 32768 (smooth_inv is staged in LDS);
+ * larger K returns SVDQ_ERR_UNSUPPORTED_SHAPE. */
 int svdq_quant_act_lora_down(const void* x, const float* smooth_inv, const void* lora_down,
                              int M, int K, int rank, int group, int act,
                              void* x_codes, void* x_scales, float* lora_act,

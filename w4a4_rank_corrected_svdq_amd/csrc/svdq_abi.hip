@@ -78,7 +78,7 @@ extern "C" int svdq_quant_act_lora_down(const void* x, const float* smooth_inv, 
                                         void* x_scales, float* lora_act, void* stream) {
   if (M < 0) return SVDQ_ERR_INVALID_ARG;
   if (K <= 0 || rank < 0 || rank > K || group <= 0) return SVDQ_ERR_INVALID_ARG;
-  if (group != SVDQ_GROUP || K % group != 0 || rank % 16 != 0 || rank > SVDQ_MAX_RANK)
+  if (group != SVDQ_GROUP || K % group != 0 || rank % 16 != 0 || rank > SVDQ_MAX_RANK || K > 32768)
     return SVDQ_ERR_UNSUPPORTED_SHAPE;
   int st;
   if (act != SVDQ_ACT_NONE && act != SVDQ_ACT_GELU_TANH) return SVDQ_ERR_INVALID_ARG;

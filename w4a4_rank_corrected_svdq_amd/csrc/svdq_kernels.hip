@@ -57,21 +57,32 @@ __device__ __forceinline__ float gelu_tanh(float x) {
 // =====================================================================
 // Kernel 1
 // =====================================================================
-// Block: 16 token rows, 8 waves; wave w handles groups w, w+8, ... of K.
-// Lane l works on row (l % 16) and the 16 consecutive k of its group at
-// offset 16*(l/16); the four lanes of a row reduce the group absmax with two
-// cross-lane exchanges.  The down projection treats the lane's 16 values as
-// two 16x16x32 bf16 MFMA A-operands (k offsets 0..7 and 8..15 of its slice).
-constexpr int K1_WAVES = 8;
+// Block: 16 token rows, 16 waves (8 for ranks above 64); wave w handles
+// groups w, w+W, ... of K in batches of up to 2 groups whose loads are all
+// issued before any is used, so a CU keeps enough bytes in flight to stream HBM.  smooth_inv is
+// staged once per block in LDS.  Lane l works on row (l % 16) and the 16
+// consecutive k of its group at offset 16*(l/16); the four lanes of a row
+// reduce the group absmax with two cross-lane exchanges.  The down
+// projection treats the lane's 16 values as two 16x16x32 bf16 MFMA A
+// operands (k offsets 0..7 and 8..15 of its slice); the waves' partial sums
+// are reduced through LDS in wave order.
 constexpr int K1_ROWS = 16;
+constexpr int K1_MAX_WAVES = 16;
+// 16 waves per block for ranks up to 64 (4 waves per SIMD hide the load
+// latency); 8 waves above, where the down-projection accumulators need the
+// registers.
+template <int NT> constexpr int k1_waves() { return NT <= 4 ? 16 : 8; }
 
 template <int ACT, int NT>
-__global__ __launch_bounds__(K1_WAVES * 64) void k_quant_act_lora_down(
+__global__ __launch_bounds__(k1_waves<NT>() * 64) void k_quant_act_lora_down(
     const uint16_t* __restrict__ x, const float* __restrict__ smooth_inv,
     const uint16_t* __restrict__ lora_down, int M, int K, int rank,
     uint8_t* __restrict__ x_codes, _Float16* __restrict__ x_scales, float* __restrict__ lora_act) {
-  __shared__ float red[K1_WAVES][2][16][16];
+  extern __shared__ __align__(16) unsigned char k1_smem_raw[];
+  float* s_si = reinterpret_cast<float*>(k1_smem_raw);                  // [K]
+  float(*red)[2][16][16] = reinterpret_cast<float(*)[2][16][16]>(s_si + K);  // [waves][2][16][16]
 
+  constexpr int K1_WAVES = k1_waves<NT>();
   const int lane = threadIdx.x & 63;
   const int wave = threadIdx.x >> 6;
   const int m0 = blockIdx.x * K1_ROWS;
@@ -81,67 +92,83 @@ __global__ __launch_bounds__(K1_WAVES * 64) void k_quant_act_lora_down(
   const int G = K / GROUP;
   const int ntiles = rank >> 4;
 
+  for (int k = threadIdx.x * 4; k < K; k += K1_WAVES * 64 * 4)
+    *reinterpret_cast<float4*>(s_si + k) = *reinterpret_cast<const float4*>(smooth_inv + k);
+  __syncthreads();
+
   v4f acc[NT > 0 ? NT : 1];
 #pragma unroll
   for (int t = 0; t < (NT > 0 ? NT : 1); ++t) acc[t] = v4f{0.f, 0.f, 0.f, 0.f};
 
   const uint16_t* xrow = x + static_cast<size_t>(row_ok ? row : 0) * K;
+  constexpr int K1_BATCH = NT <= 2 ? 2 : 1;
 
-  for (int g = wave; g < G; g += K1_WAVES) {
-    const int k0 = g * GROUP + kq;
-    uint4 raw0 = make_uint4(0, 0, 0, 0), raw1 = make_uint4(0, 0, 0, 0);
-    if (row_ok) {
-      raw0 = *reinterpret_cast<const uint4*>(xrow + k0);
-      raw1 = *reinterpret_cast<const uint4*>(xrow + k0 + 8);
-    }
-    const float4* sp = reinterpret_cast<const float4*>(smooth_inv + k0);
-    float4 s4[4] = {sp[0], sp[1], sp[2], sp[3]};
-    const float* sv = reinterpret_cast<const float*>(s4);
-    uint32_t w[8] = {raw0.x, raw0.y, raw0.z, raw0.w, raw1.x, raw1.y, raw1.z, raw1.w};
-    float xh[16];
+  for (int g0 = wave; g0 < G; g0 += K1_WAVES * K1_BATCH) {
+    uint4 raw[K1_BATCH][2];
 #pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      float lo = bf16_bits_to_f32(w[i] & 0xFFFFu);
-      float hi = bf16_bits_to_f32(w[i] >> 16);
-      if (ACT == SVDQ_ACT_GELU_TANH) {
-        lo = gelu_tanh(lo);
-        hi = gelu_tanh(hi);
+    for (int b = 0; b < K1_BATCH; ++b) {
+      const int g = g0 + b * K1_WAVES;
+      raw[b][0] = raw[b][1] = make_uint4(0, 0, 0, 0);
+      if (row_ok && g < G) {
+        raw[b][0] = *reinterpret_cast<const uint4*>(xrow + g * GROUP + kq);
+        raw[b][1] = *reinterpret_cast<const uint4*>(xrow + g * GROUP + kq + 8);
       }
-      xh[2 * i] = lo * sv[2 * i];
-      xh[2 * i + 1] = hi * sv[2 * i + 1];
     }
-    float amax = 0.f;
 #pragma unroll
-    for (int i = 0; i < 16; ++i) amax = fmaxf(amax, fabsf(xh[i]));
-    amax = fmaxf(amax, __shfl_xor(amax, 16));
-    amax = fmaxf(amax, __shfl_xor(amax, 32));
-    const float s32 = amax / 7.0f;
-    const _Float16 sh = static_cast<_Float16>(s32);
-    const float sf = static_cast<float>(sh);
-    const float rcp = (sf == 0.f) ? 0.f : 1.0f / sf;
-    uint32_t p0 = 0, p1 = 0;
+    for (int b = 0; b < K1_BATCH; ++b) {
+      const int g = g0 + b * K1_WAVES;
+      if (g >= G) break;
+      const int k0 = g * GROUP + kq;
+      const float4* sp = reinterpret_cast<const float4*>(s_si + k0);
+      float4 s4[4] = {sp[0], sp[1], sp[2], sp[3]};
+      const float* sv = reinterpret_cast<const float*>(s4);
+      const uint32_t w[8] = {raw[b][0].x, raw[b][0].y, raw[b][0].z, raw[b][0].w,
+                             raw[b][1].x, raw[b][1].y, raw[b][1].z, raw[b][1].w};
+      float xh[16];
 #pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      const float q0 = fminf(fmaxf(rintf(xh[i] * rcp), -8.f), 7.f);
-      const float q1 = fminf(fmaxf(rintf(xh[8 + i] * rcp), -8.f), 7.f);
-      p0 |= (static_cast<uint32_t>(static_cast<int>(q0)) & 0xFu) << (4 * i);
-      p1 |= (static_cast<uint32_t>(static_cast<int>(q1)) & 0xFu) << (4 * i);
-    }
-    if (row_ok) {
-      *reinterpret_cast<uint2*>(x_codes + static_cast<size_t>(row) * (K / 2) + (k0 >> 1)) = make_uint2(p0, p1);
-      if (lane < 16) x_scales[static_cast<size_t>(g) * M + row] = sh;
-    }
-    if constexpr (NT > 0) {
-      const v8bf a0 = pack_bf16x8(xh);
-      const v8bf a1 = pack_bf16x8(xh + 8);
+      for (int i = 0; i < 8; ++i) {
+        float lo = bf16_bits_to_f32(w[i] & 0xFFFFu);
+        float hi = bf16_bits_to_f32(w[i] >> 16);
+        if (ACT == SVDQ_ACT_GELU_TANH) {
+          lo = gelu_tanh(lo);
+          hi = gelu_tanh(hi);
+        }
+        xh[2 * i] = lo * sv[2 * i];
+        xh[2 * i + 1] = hi * sv[2 * i + 1];
+      }
+      float amax = 0.f;
 #pragma unroll
-      for (int t = 0; t < NT; ++t) {
-        if (t < ntiles) {
-          const uint16_t* bp = lora_down + static_cast<size_t>(t * 16 + (lane & 15)) * K + k0;
-          const v8bf b0 = __builtin_bit_cast(v8bf, *reinterpret_cast<const uint4*>(bp));
-          const v8bf b1 = __builtin_bit_cast(v8bf, *reinterpret_cast<const uint4*>(bp + 8));
-          acc[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a0, b0, acc[t], 0, 0, 0);
-          acc[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a1, b1, acc[t], 0, 0, 0);
+      for (int i = 0; i < 16; ++i) amax = fmaxf(amax, fabsf(xh[i]));
+      amax = fmaxf(amax, __shfl_xor(amax, 16));
+      amax = fmaxf(amax, __shfl_xor(amax, 32));
+      const float s32 = amax / 7.0f;
+      const _Float16 sh = static_cast<_Float16>(s32);
+      const float sf = static_cast<float>(sh);
+      const float rcp = (sf == 0.f) ? 0.f : 1.0f / sf;
+      uint32_t p0 = 0, p1 = 0;
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        const float q0 = fminf(fmaxf(rintf(xh[i] * rcp), -8.f), 7.f);
+        const float q1 = fminf(fmaxf(rintf(xh[8 + i] * rcp), -8.f), 7.f);
+        p0 |= (static_cast<uint32_t>(static_cast<int>(q0)) & 0xFu) << (4 * i);
+        p1 |= (static_cast<uint32_t>(static_cast<int>(q1)) & 0xFu) << (4 * i);
+      }
+      if (row_ok) {
+        *reinterpret_cast<uint2*>(x_codes + static_cast<size_t>(row) * (K / 2) + (k0 >> 1)) = make_uint2(p0, p1);
+        if (lane < 16) x_scales[static_cast<size_t>(g) * M + row] = sh;
+      }
+      if constexpr (NT > 0) {
+        const v8bf a0 = pack_bf16x8(xh);
+        const v8bf a1 = pack_bf16x8(xh + 8);
+#pragma unroll
+        for (int t = 0; t < NT; ++t) {
+          if (t < ntiles) {
+            const uint16_t* bp = lora_down + static_cast<size_t>(t * 16 + (lane & 15)) * K + k0;
+            const v8bf b0 = __builtin_bit_cast(v8bf, *reinterpret_cast<const uint4*>(bp));
+            const v8bf b1 = __builtin_bit_cast(v8bf, *reinterpret_cast<const uint4*>(bp + 8));
+            acc[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a0, b0, acc[t], 0, 0, 0);
+            acc[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a1, b1, acc[t], 0, 0, 0);
+          }
         }
       }
     }
@@ -162,14 +189,16 @@ __global__ __launch_bounds__(K1_WAVES * 64) void k_quant_act_lora_down(
         }
       }
       __syncthreads();
-      const int tt = threadIdx.x >> 8;         // 0..1
-      const int r = (threadIdx.x >> 4) & 15;   // row in tile
-      const int c = threadIdx.x & 15;          // col in tile
-      if (t0 + tt < ntiles && m0 + r < M) {
-        float s = 0.f;
+      if (threadIdx.x < 512) {
+        const int tt = threadIdx.x >> 8;         // 0..1
+        const int r = (threadIdx.x >> 4) & 15;   // row in tile
+        const int c = threadIdx.x & 15;          // col in tile
+        if (t0 + tt < ntiles && m0 + r < M) {
+          float s = 0.f;
 #pragma unroll
-        for (int wv = 0; wv < K1_WAVES; ++wv) s += red[wv][tt][r][c];
-        lora_act[static_cast<size_t>(m0 + r) * rank + (t0 + tt) * 16 + c] = s;
+          for (int wv = 0; wv < K1_WAVES; ++wv) s += red[wv][tt][r][c];
+          lora_act[static_cast<size_t>(m0 + r) * rank + (t0 + tt) * 16 + c] = s;
+        }
       }
       __syncthreads();
     }
@@ -537,21 +566,29 @@ __global__ __launch_bounds__(K2_THREADS, 2) void k_gemm_w4a4_lora_up(
   }
 }
 
+template <int ACT, int NT>
+void launch_k1_kernel(const void* x, const float* smooth_inv, const void* lora_down, int M, int K, int rank,
+                      void* x_codes, void* x_scales, float* lora_act, size_t smem, hipStream_t st) {
+  auto kern = k_quant_act_lora_down<ACT, NT>;
+  if (smem > 64 * 1024)
+    (void)hipFuncSetAttribute(reinterpret_cast<const void*>(kern), hipFuncAttributeMaxDynamicSharedMemorySize,
+                              static_cast<int>(smem));
+  hipLaunchKernelGGL(kern, dim3((M + K1_ROWS - 1) / K1_ROWS), dim3(k1_waves<NT>() * 64), smem, st,
+                     static_cast<const uint16_t*>(x), smooth_inv, static_cast<const uint16_t*>(lora_down), M, K,
+                     rank, static_cast<uint8_t*>(x_codes), static_cast<_Float16*>(x_scales), lora_act);
+}
+
 template <int ACT>
 int launch_k1(const void* x, const float* smooth_inv, const void* lora_down, int M, int K, int rank,
               void* x_codes, void* x_scales, float* lora_act, hipStream_t st) {
-  const dim3 grid((M + K1_ROWS - 1) / K1_ROWS), block(K1_WAVES * 64);
+  const size_t smem = static_cast<size_t>(K) * sizeof(float) + sizeof(float) * K1_MAX_WAVES * 2 * 16 * 16;
+  if (smem > 160 * 1024) return SVDQ_ERR_UNSUPPORTED_SHAPE;
   const int nt = rank / 16;
-  auto go = [&](auto kern) {
-    hipLaunchKernelGGL(kern, grid, block, 0, st, static_cast<const uint16_t*>(x), smooth_inv,
-                       static_cast<const uint16_t*>(lora_down), M, K, rank,
-                       static_cast<uint8_t*>(x_codes), static_cast<_Float16*>(x_scales), lora_act);
-  };
-  if (nt == 0) go(k_quant_act_lora_down<ACT, 0>);
-  else if (nt <= 2) go(k_quant_act_lora_down<ACT, 2>);
-  else if (nt <= 4) go(k_quant_act_lora_down<ACT, 4>);
-  else if (nt <= 8) go(k_quant_act_lora_down<ACT, 8>);
-  else go(k_quant_act_lora_down<ACT, 16>);
+  if (nt == 0) launch_k1_kernel<ACT, 0>(x, smooth_inv, lora_down, M, K, rank, x_codes, x_scales, lora_act, smem, st);
+  else if (nt <= 2) launch_k1_kernel<ACT, 2>(x, smooth_inv, lora_down, M, K, rank, x_codes, x_scales, lora_act, smem, st);
+  else if (nt <= 4) launch_k1_kernel<ACT, 4>(x, smooth_inv, lora_down, M, K, rank, x_codes, x_scales, lora_act, smem, st);
+  else if (nt <= 8) launch_k1_kernel<ACT, 8>(x, smooth_inv, lora_down, M, K, rank, x_codes, x_scales, lora_act, smem, st);
+  else launch_k1_kernel<ACT, 16>(x, smooth_inv, lora_down, M, K, rank, x_codes, x_scales, lora_act, smem, st);
   return hipGetLastError() == hipSuccess ? SVDQ_OK : SVDQ_ERR_HIP;
 }
 
