@@ -157,13 +157,23 @@ def main():
 
     x = torch.from_numpy(wl.x_bits.view(np.int16).copy()).view(torch.bfloat16).cuda()
 
-    def run(lin, steps, warmup, events=False):
+    def run(lin, steps, warmup, events=False, unfused=False):
         xc = torch.empty((M, K // 2), dtype=torch.uint8, device="cuda")
         xs = torch.empty((K // 64, M), dtype=torch.float16, device="cuda")
         la = torch.empty((M, lin.rank), dtype=torch.float32, device="cuda") if lin.rank else None
         y = torch.empty((M, N), dtype=torch.bfloat16, device="cuda")
 
         def step(mid=None):
+            if unfused:
+                # the low-rank branch as two extra passes: 4-bit path at
+                # rank 0, then down projection (re-reads x) and up
+                # projection (reads and rewrites y)
+                S.quant_act_lora_down(x, lin.smooth_inv, None, 0, act=act_id, out=(xc, xs, None))
+                S.gemm_w4a4_lora_up(xc, xs, lin.w_codes, lin.w_scales, None, None, lin.bias,
+                                    M, N, K, 0, out=y)
+                S.lora_down(x, lin.smooth_inv, lin.lora_down, lin.rank, act=act_id, out=la)
+                S.lora_up_add(la, lin.lora_up, y)
+                return
             S.quant_act_lora_down(x, lin.smooth_inv, lin.lora_down, lin.rank, act=act_id, out=(xc, xs, la))
             if mid is not None:
                 mid.record()
@@ -230,9 +240,13 @@ def main():
         lin0 = build_layer(0)
         res0 = run(lin0, args.steps, args.warmup, events=True)
         ms0 = res0["wall_s"] * 1e3 / args.steps
+        resu = run(lin, args.steps, args.warmup, unfused=True)
+        msu = resu["wall_s"] * 1e3 / args.steps
         out["low_rank_overhead"] = {
             "rank0_ms_per_step": round(ms0, 5),
             "overhead_frac": round(ms_per_step / ms0 - 1.0, 4),
+            "unfused_ms_per_step": round(msu, 5),
+            "unfused_overhead_frac": round(msu / ms0 - 1.0, 4),
             "context": "pages: an unfused rank-32 branch costs +57% latency (NVIDIA, model card)"}
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(wl, layer, r, args.cpu_seconds)

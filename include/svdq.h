@@ -164,6 +164,24 @@ int svdq_gemm_w4a4_lora_up(const void* x_codes, const void* x_scales,
                            int M, int N, int K, int rank, int group, int out_dtype,
                            void* y, void* stream);
 
+/* Device, asynchronous.  The unfused low-rank branch, kept as the reference
+ * for the fusion the model card's "Nunchaku Engine Design" describes (its
+ * section (a): running the rank-32 branch naively costs an extra read of
+ * the 16-bit input for the down projection and an extra write of the 16-bit
+ * output for the up projection).  Used with the two kernels above at
+ * rank 0, they compute the same layer with those extra HBM passes:
+ *
+ * svdq_lora_down: lora_act [M][rank] fp32 = sum_k bf16(x_hat[m,k]) *
+ *   lora_down[j][k], x_hat = fp32(act(x) * smooth_inv), reading x [M][K]
+ *   bf16 again (no codes or scales are written).  Same limits as
+ *   svdq_quant_act_lora_down; rank >= 16.
+ * svdq_lora_up_add: y [M][N] bf16, read and rewritten in place:
+ *   y = bf16(y + sum_j bf16(lora_act[m,j]) * lora_up[n][j]).  rank >= 16. */
+int svdq_lora_down(const void* x, const float* smooth_inv, const void* lora_down, int M, int K,
+                   int rank, int group, int act, float* lora_act, void* stream);
+int svdq_lora_up_add(const float* lora_act, const void* lora_up, int M, int N, int rank, void* y,
+                     void* stream);
+
 #ifdef __cplusplus
 }
 #endif

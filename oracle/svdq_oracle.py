@@ -46,6 +46,9 @@ Readings where the pages are silent (each also listed in the design doc):
   R8  Output Y = bf16(acc + bf16(lora_act) L2 + bias), round to nearest even.
   R9  Optional tanh-GELU (textbook tanh form) on the bf16 input of the
       quantizer, in fp32, before smoothing (MLP pair chain).
+  R10 The unfused comparison path (``forward_unfused``) stores the 4-bit
+      GEMM's output plus bias as bf16 before the up projection adds to it,
+      and rounds to bf16 again: the 16-bit output is written twice.
 
 Emulating one fp32 operation by computing it in fp64 and rounding once to
 fp32 gives the correctly rounded fp32 result for +, -, *, / and sqrt, since
@@ -60,7 +63,7 @@ __all__ = [
     "smoothing_factors", "smooth_weight", "low_rank_split", "quantize_groups",
     "quantize_weight_residual", "prepare", "gelu_tanh", "quantize_activation",
     "pack_int4", "unpack_int4", "lora_down", "w4a4_product",
-    "w4a4_product_bruteforce", "forward", "reference_fp64", "rel_fro",
+    "w4a4_product_bruteforce", "forward", "forward_unfused", "reference_fp64", "rel_fro",
     "prepared_bytes",
 ]
 
@@ -345,6 +348,28 @@ def forward(x, prep, bias=None, act: str = "none", out: str = "bf16",
     if return_parts:
         return Y, dict(qx=qx, sx=sx, x_hat=x_hat, lora_act=la, acc=acc, y=y)
     return Y
+
+
+def forward_unfused(x, prep, bias=None, act: str = "none", semantics: str = "gpu") -> np.ndarray:
+    """The layer with its low-rank branch run as two separate passes, the
+    naive arrangement the model card's "Nunchaku Engine Design" (a)
+    measures against the fused one: the 4-bit GEMM writes its 16-bit output
+    (bias included), a separate down projection re-reads X, and a separate
+    up projection reads that output back, adds bf16(lora_act) L2 and writes
+    it again.  The result differs from ``forward`` only by the extra bf16
+    rounding of the intermediate output (reading R10).  Returns bf16 values.
+    """
+    x = np.asarray(x, dtype=np.float64)
+    group = prep["group"]
+    qx, sx, x_hat = quantize_activation(x, prep["smooth_inv"], group, act, semantics)
+    y0 = w4a4_product(qx, sx, prep["qw"], prep["sw"], group)
+    if bias is not None:
+        y0 = y0 + np.asarray(bias, dtype=np.float64)[None, :]
+    y0 = bf16(y0)
+    if prep["L1"].shape[1] == 0:
+        return y0
+    la = lora_down(x_hat, prep["L1"])
+    return bf16(y0 + bf16(la) @ prep["L2"])
 
 
 def reference_fp64(x, weight_nk, bias=None, act: str = "none") -> np.ndarray:

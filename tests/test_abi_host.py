@@ -84,6 +84,21 @@ def test_device_entry_validation_precedes_device_use():
     assert g(p[0], p[1], p[2], p[3], p[4], p[5], None, 16, 64, 128, 16, 64, 2, p[6], None) == L.SVDQ_ERR_INVALID_ARG
     assert g(p[0], p[1], p[2], p[3], None, None, None, 16, 64, 128, 16, 64, 0, p[6], None) == L.SVDQ_ERR_INVALID_ARG
     assert g(p[0], p[1], p[2], p[3], p[4], p[5], p[7] + 8, 16, 64, 128, 16, 64, 0, p[6], None) == L.SVDQ_ERR_INVALID_ARG
+    d = L.lib().svdq_lora_down
+    u = L.lib().svdq_lora_up_add
+    assert d(p[0], p[1], p[2], 16, 128, 0, 64, 0, p[3], None) == L.SVDQ_ERR_INVALID_ARG       # rank 0
+    assert d(p[0], p[1], p[2], 16, 128, 24, 64, 0, p[3], None) == L.SVDQ_ERR_UNSUPPORTED_SHAPE
+    assert d(p[0], p[1], p[2], 16, 96, 32, 64, 0, p[3], None) == L.SVDQ_ERR_UNSUPPORTED_SHAPE
+    assert d(p[0], p[1], p[2], 16, 32768 + 64, 32, 64, 0, p[3], None) == L.SVDQ_ERR_UNSUPPORTED_SHAPE
+    assert d(p[0], p[1], None, 16, 128, 32, 64, 0, p[3], None) == L.SVDQ_ERR_INVALID_ARG
+    assert d(p[0], p[1], p[2], 16, 128, 32, 64, 3, p[3], None) == L.SVDQ_ERR_INVALID_ARG
+    assert d(p[0], p[1], p[2], 16, 128, 32, 64, 0, p[3] + 4, None) == L.SVDQ_ERR_INVALID_ARG
+    assert u(p[0], p[1], 16, 128, 0, p[2], None) == L.SVDQ_ERR_INVALID_ARG                    # rank 0
+    assert u(p[0], p[1], 16, 100, 16, p[2], None) == L.SVDQ_ERR_UNSUPPORTED_SHAPE
+    assert u(p[0], p[1], 16, 128, 24, p[2], None) == L.SVDQ_ERR_UNSUPPORTED_SHAPE
+    assert u(p[0], p[1], 16, 16, 32, p[2], None) == L.SVDQ_ERR_INVALID_ARG                    # rank > N
+    assert u(p[0], None, 16, 128, 16, p[2], None) == L.SVDQ_ERR_INVALID_ARG
+    assert u(p[0], p[1], -1, 128, 16, p[2], None) == L.SVDQ_ERR_INVALID_ARG
 
 
 REFUSAL_SCRIPT = r"""
@@ -96,7 +111,9 @@ p = [b + 256 * i for i in range(8)]
 r1 = L.lib().svdq_quant_act_lora_down(p[0], p[1], p[2], 16, 128, 32, 64, 0, p[3], p[4], p[5], None)
 r2 = L.lib().svdq_gemm_w4a4_lora_up(p[0], p[1], p[2], p[3], p[4], p[5], None, 16, 64, 128, 16, 64, 0, p[6], None)
 r3 = L.lib().svdq_device_check(0)
-print(r1, r2, r3)
+r4 = L.lib().svdq_lora_down(p[0], p[1], p[2], 16, 128, 32, 64, 0, p[3], None)
+r5 = L.lib().svdq_lora_up_add(p[0], p[1], 16, 128, 16, p[2], None)
+print(r1, r2, r3, r4, r5)
 """
 
 
@@ -108,7 +125,7 @@ def test_unsupported_device_is_refused():
     r = subprocess.run([sys.executable, "-c", REFUSAL_SCRIPT.format(root=ROOT)], env=env,
                        capture_output=True, text=True, timeout=120)
     assert r.returncode == 0, r.stderr
-    assert r.stdout.split() == [str(L.SVDQ_ERR_UNSUPPORTED_DEVICE)] * 3
+    assert r.stdout.split() == [str(L.SVDQ_ERR_UNSUPPORTED_DEVICE)] * 5
 
 
 # ------------------------------------------------------------ host preparation
@@ -221,3 +238,10 @@ def test_binding_rejects_non_contiguous_host_arrays():
         ops.prepare_weights(w.astype(np.float32), np.ones(128, np.float32), rank=0)
     with pytest.raises(ValueError):
         ops._ptr(np.zeros((8, 8), np.float32).T)
+
+
+def test_kernel1_k_limit():
+    """smooth_inv is staged in LDS: K above 32768 is refused before any device use."""
+    buf, p = _fake(8)
+    q = L.lib().svdq_quant_act_lora_down
+    assert q(p[0], p[1], p[2], 16, 32768 + 64, 32, 64, 0, p[3], p[4], p[5], None) == L.SVDQ_ERR_UNSUPPORTED_SHAPE

@@ -66,7 +66,8 @@ def y_to_np(y):
 
 
 # ------------------------------------------------------------------ kernel 2: integer core
-@pytest.mark.parametrize("M,N,K", [(300, 264, 256), (16, 128, 64), (129, 8, 128), (1, 136, 192)])
+@pytest.mark.parametrize("M,N,K", [(300, 264, 256), (16, 128, 64), (129, 8, 128), (1, 136, 192),
+                                   (200, 1032, 12288)])
 def test_int32_group_products_bit_exact(M, N, K):
     """Unit scales, rank 0, fp32 output: y = sum_k q_x q_w is an integer below
     2^24, so it is exact in fp32 whatever the order; compared bit for bit
@@ -162,7 +163,8 @@ def test_k1_zero_and_tiny_inputs():
 
 # ------------------------------------------------------------------ kernel 2 full epilogue
 @pytest.mark.parametrize("rank,bias,out", [(0, False, "bf16"), (16, True, "bf16"), (32, False, "bf16"),
-                                           (32, True, "f32"), (64, True, "bf16"), (128, False, "bf16")])
+                                           (32, True, "f32"), (64, True, "bf16"), (128, False, "bf16"),
+                                           (256, True, "bf16"), (48, False, "f32")])
 def test_k2_output_parity(rank, bias, out):
     M, K, N = 300, 512, 264
     wl, Lr, po, abi = _small_case(M, K, N, rank, seed=44 + rank, bias=bias)
@@ -222,6 +224,79 @@ def test_mlp_chain_gelu_small():
                                act=L.SVDQ_ACT_GELU_TANH)
     y_dn = run_k2(*x2[:2], ad, x2[2], None, M)
     assert O.rel_fro(y_to_np(y_dn), y_dn_o) < Y_TOL
+
+
+# ------------------------------------------------------------------ unfused comparison path
+def run_unfused(x_bits, abi, bias_bits, M, act=L.SVDQ_ACT_NONE):
+    """Kernel 1 and kernel 2 at rank 0, then the separate down projection
+    (re-reading x) and the separate up projection (read-modify-write of y)."""
+    r, N, K = abi["rank"], abi["N"], abi["K"]
+    x = dev_bf16(x_bits)
+    si = dev(abi["smooth_inv"])
+    xc, xs, _ = S.quant_act_lora_down(x, si, None, 0, act=act)
+    y = S.gemm_w4a4_lora_up(xc, xs, dev(abi["w_codes"]), dev(abi["w_scales"]), None, None,
+                            dev_bf16(bias_bits) if bias_bits is not None else None, M, N, K, 0)
+    la = S.lora_down(x, si, dev_bf16(abi["lora_down"]), r, act=act)
+    S.lora_up_add(la, dev_bf16(abi["lora_up"]), y)
+    torch.cuda.synchronize()
+    return xc, xs, la, y
+
+
+@pytest.mark.parametrize("M,K,N,rank,bias", [(300, 512, 264, 32, True), (1, 64, 24, 16, False),
+                                             (129, 1024, 520, 64, True), (64, 256, 136, 128, False),
+                                             (33, 512, 256, 256, True)])
+def test_unfused_branch_parity(M, K, N, rank, bias):
+    """The unfused path against the oracle's unfused forward; its down
+    projection is bit-identical to the fused kernel 1's (same kernel, no
+    quantizer), and its 4-bit codes and scales to the fused ones."""
+    wl, Lr, po, abi = _small_case(M, K, N, rank, seed=49 + M, bias=bias)
+    bb = Lr.bias_bits if bias else None
+    xc, xs, la, y = run_unfused(wl.x_bits, abi, bb, M)
+    xc1, xs1, la1 = run_k1(wl.x_bits, abi["smooth_inv"], abi["lora_down"], rank)
+    np.testing.assert_array_equal(xc.cpu().numpy(), xc1.cpu().numpy())
+    np.testing.assert_array_equal(xs.cpu().numpy(), xs1.cpu().numpy())
+    np.testing.assert_array_equal(la.cpu().numpy(), la1.cpu().numpy())
+    q, s, xh = O.quantize_activation(wl.x, po["smooth_inv"], 64)
+    assert O.rel_fro(la.double().cpu().numpy(), O.lora_down(xh, po["L1"])) < LORA_TOL
+    Yo = O.forward_unfused(wl.x, po, bias=Lr.bias if bias else None)
+    assert O.rel_fro(to_np_bf16(y), Yo) < Y_TOL
+
+
+def test_lora_up_add_in_place_parity():
+    """The standalone up projection on oracle inputs: y0 bf16 and lora_act
+    taken from the oracle, result against bf16(y0 + bf16(lora_act) L2)."""
+    M, K, N, r = 200, 256, 392, 48
+    wl, Lr, po, abi = _small_case(M, K, N, r, seed=50, bias=True)
+    rng = np.random.default_rng(51)
+    y0 = O.bf16(rng.standard_normal((M, N)) * 4)
+    la = O.fp32(rng.standard_normal((M, r)) * 3)
+    y = dev_bf16(f64_to_bf16_bits(y0))
+    S.lora_up_add(dev(la.astype(np.float32)), dev_bf16(abi["lora_up"]), y)
+    torch.cuda.synchronize()
+    ref = O.bf16(y0 + O.bf16(la) @ po["L2"])
+    got = to_np_bf16(y)
+    assert O.rel_fro(got, ref) < Y_TOL
+    # at most a 1-ulp flip where fp32 summation order meets a rounding boundary
+    assert (got != ref).mean() < 0.01
+
+
+def test_unfused_full_size_sampled_rows():
+    """The unfused path at the FLUX MLP-up shape [4096 x 3072] -> 12288,
+    rank 32, sampled rows against the oracle's unfused forward."""
+    wl = workloads.make_workload("mlp_pair")
+    Lr = wl.layers[0]
+    M, K, N, r = wl.M, Lr.K, Lr.N, 32
+    rng = np.random.default_rng(9)
+    a = wl.act_absmax()
+    si, lam = O.smoothing_factors(a, Lr.weight)
+    l1, l2 = _synthetic_factors(K, N, r, rng, scale=float(np.abs(lam).mean() * 0.02))
+    po = O.prepare(Lr.weight, a, rank=r, factors=(l1, l2))
+    abi = oracle_prep_to_abi(po)
+    xc, xs, la, y = run_unfused(wl.x_bits, abi, Lr.bias_bits, M)
+    rows = _sample_rows(M, rng)
+    Yo = O.forward_unfused(wl.x[rows], po, bias=Lr.bias)
+    assert O.rel_fro(to_np_bf16(y[torch.from_numpy(rows).cuda()]), Yo) < Y_TOL
+    assert torch.isfinite(y.float()).all()
 
 
 # ------------------------------------------------------------------ FLUX shapes, sampled rows

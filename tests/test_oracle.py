@@ -273,3 +273,63 @@ def test_prepared_bytes_closed_form():
     # FLUX MLP-up layer: ~3.6x smaller than bf16 (the card states about 4x)
     ratio = 2 * 3072 * 12288 / O.prepared_bytes(3072, 12288, 32)
     assert 3.5 < ratio < 3.7
+
+
+# ---------------------------------------------------------------- unfused comparison path
+def _hand_prep(K=64, N=8, rank=16):
+    """smooth_inv = 1, weight codes and scales and factors set by hand."""
+    qw = np.zeros((K, N))
+    sw = np.ones((K // 64, N))
+    L1 = np.zeros((K, rank))
+    L2 = np.zeros((rank, N))
+    return dict(group=64, smooth_inv=np.ones(K, np.float32), qw=qw, sw=sw, L1=L1, L2=L2)
+
+
+def test_unfused_double_rounding_worked_example():
+    """Worked by hand.  Row 0 of X is (7, 1, 0, ...): absmax 7, scale 1,
+    codes (7, 1).  Weight column 0 has codes (7, 7) and scale 4, so the 4-bit
+    product is 4 * (7*7 + 1*7) = 224; bias 33 makes 257.  L1[1, 0] = 1 and
+    L2[0, 0] = 1 give a low-rank term of exactly 1.
+    Fused: bf16(257 + 1) = 258 (representable: 8 significant bits).
+    Unfused: bf16(257) = 256 (257 lies halfway between 256 and 258; ties go
+    to the even significand, 256), then bf16(256 + 1) = 256 again."""
+    p = _hand_prep()
+    p["qw"][0, 0] = p["qw"][1, 0] = 7
+    p["sw"][0, 0] = 4.0
+    p["L1"][1, 0] = 1.0
+    p["L2"][0, 0] = 1.0
+    x = np.zeros((2, 64))
+    x[0, 0], x[0, 1] = 7.0, 1.0
+    bias = np.zeros(8)
+    bias[0] = 33.0
+    fused = O.forward(x, p, bias=bias)
+    unfused = O.forward_unfused(x, p, bias=bias)
+    assert fused[0, 0] == 258.0
+    assert unfused[0, 0] == 256.0
+    # every other output is an exactly representable small integer: no rounding anywhere
+    mask = np.ones_like(fused, bool)
+    mask[0, 0] = False
+    np.testing.assert_array_equal(fused[mask], unfused[mask])
+    assert unfused[1, 0] == 33.0 and unfused[0, 1] == 0.0
+
+
+def _half_ulp_bf16(v):
+    e = np.floor(np.log2(np.maximum(np.abs(v), 2.0 ** -126)))
+    return 2.0 ** (e - 8)
+
+
+def test_unfused_within_two_roundings_of_exact():
+    """Random layer: the unfused path is the exact fused value rounded twice,
+    so |unfused - exact| <= half an ulp of the intermediate plus half an ulp
+    of the result; at rank 0 it coincides with the fused forward."""
+    wl = workloads.custom_workload(64, 256, 96, seed=27, n_out=3, bias=True)
+    L = wl.layers[0]
+    p = O.prepare(L.weight, wl.act_absmax(), rank=32)
+    exact, parts = O.forward(wl.x, p, bias=L.bias, out="f64", return_parts=True)
+    y0 = parts["acc"] + L.bias[None, :]
+    un = O.forward_unfused(wl.x, p, bias=L.bias)
+    bound = _half_ulp_bf16(y0) + _half_ulp_bf16(un) * (1 + 1e-12)
+    assert np.all(np.abs(un - exact) <= bound)
+    assert np.any(un != O.forward(wl.x, p, bias=L.bias))  # the extra rounding shows
+    p0 = O.prepare(L.weight, wl.act_absmax(), rank=0)
+    np.testing.assert_array_equal(O.forward_unfused(wl.x, p0, bias=L.bias), O.forward(wl.x, p0, bias=L.bias))

@@ -39,6 +39,8 @@ SIGNATURES = {
                                      _p, _p, _p, _p, _p, _p]),
     "svdq_quant_act_lora_down": (_i, [_p, _p, _p, _i, _i, _i, _i, _i, _p, _p, _p, _p]),
     "svdq_gemm_w4a4_lora_up": (_i, [_p, _p, _p, _p, _p, _p, _p, _i, _i, _i, _i, _i, _i, _p, _p]),
+    "svdq_lora_down": (_i, [_p, _p, _p, _i, _i, _i, _i, _i, _p, _p]),
+    "svdq_lora_up_add": (_i, [_p, _p, _i, _i, _i, _p, _p]),
 }
 
 

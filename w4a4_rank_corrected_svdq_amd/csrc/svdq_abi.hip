@@ -114,3 +114,30 @@ extern "C" int svdq_gemm_w4a4_lora_up(const void* x_codes, const void* x_scales,
   return svdq::launch_gemm_w4a4_lora_up(x_codes, x_scales, w_codes, w_scales, lora_act, lora_up, bias, M,
                                         N, K, rank, out_dtype, y, stream);
 }
+
+extern "C" int svdq_lora_down(const void* x, const float* smooth_inv, const void* lora_down, int M, int K,
+                              int rank, int group, int act, float* lora_act, void* stream) {
+  if (M < 0 || K <= 0 || rank <= 0 || rank > K || group <= 0) return SVDQ_ERR_INVALID_ARG;
+  if (group != SVDQ_GROUP || K % group != 0 || rank % 16 != 0 || rank > SVDQ_MAX_RANK || K > 32768)
+    return SVDQ_ERR_UNSUPPORTED_SHAPE;
+  if (act != SVDQ_ACT_NONE && act != SVDQ_ACT_GELU_TANH) return SVDQ_ERR_INVALID_ARG;
+  if (!x || !smooth_inv || !lora_down || !lora_act) return SVDQ_ERR_INVALID_ARG;
+  if (!aligned16(x) || !aligned16(smooth_inv) || !aligned16(lora_down) || !aligned16(lora_act))
+    return SVDQ_ERR_INVALID_ARG;
+  const int st = current_device_check();
+  if (st != SVDQ_OK) return st;
+  if (M == 0) return SVDQ_OK;
+  return svdq::launch_lora_down(x, smooth_inv, lora_down, M, K, rank, act, lora_act, stream);
+}
+
+extern "C" int svdq_lora_up_add(const float* lora_act, const void* lora_up, int M, int N, int rank, void* y,
+                                void* stream) {
+  if (M < 0 || N <= 0 || rank <= 0 || rank > N) return SVDQ_ERR_INVALID_ARG;
+  if (N % 8 != 0 || rank % 16 != 0 || rank > SVDQ_MAX_RANK) return SVDQ_ERR_UNSUPPORTED_SHAPE;
+  if (!lora_act || !lora_up || !y) return SVDQ_ERR_INVALID_ARG;
+  if (!aligned16(lora_act) || !aligned16(lora_up) || !aligned16(y)) return SVDQ_ERR_INVALID_ARG;
+  const int st = current_device_check();
+  if (st != SVDQ_OK) return st;
+  if (M == 0) return SVDQ_OK;
+  return svdq::launch_lora_up_add(lora_act, lora_up, M, N, rank, y, stream);
+}

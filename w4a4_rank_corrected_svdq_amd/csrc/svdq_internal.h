@@ -11,6 +11,9 @@ int validate_shape(int K, int N, int rank, int group);
 int launch_quant_act_lora_down(const void* x, const float* smooth_inv, const void* lora_down, int M,
                                int K, int rank, int act, void* x_codes, void* x_scales,
                                float* lora_act, void* stream);
+int launch_lora_down(const void* x, const float* smooth_inv, const void* lora_down, int M, int K, int rank,
+                     int act, float* lora_act, void* stream);
+int launch_lora_up_add(const float* lora_act, const void* lora_up, int M, int N, int rank, void* y, void* stream);
 int launch_gemm_w4a4_lora_up(const void* x_codes, const void* x_scales, const void* w_codes,
                              const void* w_scales, const float* lora_act, const void* lora_up,
                              const void* bias, int M, int N, int K, int rank, int out_dtype, void* y,

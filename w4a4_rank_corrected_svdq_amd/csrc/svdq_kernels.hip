@@ -57,6 +57,9 @@ __device__ __forceinline__ float gelu_tanh(float x) {
 // =====================================================================
 // Kernel 1
 // =====================================================================
+// With QUANT = false the kernel computes only the down projection (the
+// unfused reference path, which reads X a second time).
+//
 // Block: 16 token rows, 16 waves (8 for ranks above 64); wave w handles
 // groups w, w+W, ... of K in batches of up to 2 groups whose loads are all
 // issued before any is used, so a CU keeps enough bytes in flight to stream HBM.  smooth_inv is
@@ -73,7 +76,7 @@ constexpr int K1_MAX_WAVES = 16;
 // registers.
 template <int NT> constexpr int k1_waves() { return NT <= 4 ? 16 : 8; }
 
-template <int ACT, int NT>
+template <int ACT, int NT, bool QUANT>
 __global__ __launch_bounds__(k1_waves<NT>() * 64) void k_quant_act_lora_down(
     const uint16_t* __restrict__ x, const float* __restrict__ smooth_inv,
     const uint16_t* __restrict__ lora_down, int M, int K, int rank,
@@ -136,26 +139,28 @@ __global__ __launch_bounds__(k1_waves<NT>() * 64) void k_quant_act_lora_down(
         xh[2 * i] = lo * sv[2 * i];
         xh[2 * i + 1] = hi * sv[2 * i + 1];
       }
-      float amax = 0.f;
-#pragma unroll
-      for (int i = 0; i < 16; ++i) amax = fmaxf(amax, fabsf(xh[i]));
-      amax = fmaxf(amax, __shfl_xor(amax, 16));
-      amax = fmaxf(amax, __shfl_xor(amax, 32));
-      const float s32 = amax / 7.0f;
-      const _Float16 sh = static_cast<_Float16>(s32);
-      const float sf = static_cast<float>(sh);
-      const float rcp = (sf == 0.f) ? 0.f : 1.0f / sf;
-      uint32_t p0 = 0, p1 = 0;
-#pragma unroll
-      for (int i = 0; i < 8; ++i) {
-        const float q0 = fminf(fmaxf(rintf(xh[i] * rcp), -8.f), 7.f);
-        const float q1 = fminf(fmaxf(rintf(xh[8 + i] * rcp), -8.f), 7.f);
-        p0 |= (static_cast<uint32_t>(static_cast<int>(q0)) & 0xFu) << (4 * i);
-        p1 |= (static_cast<uint32_t>(static_cast<int>(q1)) & 0xFu) << (4 * i);
-      }
-      if (row_ok) {
-        *reinterpret_cast<uint2*>(x_codes + static_cast<size_t>(row) * (K / 2) + (k0 >> 1)) = make_uint2(p0, p1);
-        if (lane < 16) x_scales[static_cast<size_t>(g) * M + row] = sh;
+      if constexpr (QUANT) {
+        float amax = 0.f;
+  #pragma unroll
+        for (int i = 0; i < 16; ++i) amax = fmaxf(amax, fabsf(xh[i]));
+        amax = fmaxf(amax, __shfl_xor(amax, 16));
+        amax = fmaxf(amax, __shfl_xor(amax, 32));
+        const float s32 = amax / 7.0f;
+        const _Float16 sh = static_cast<_Float16>(s32);
+        const float sf = static_cast<float>(sh);
+        const float rcp = (sf == 0.f) ? 0.f : 1.0f / sf;
+        uint32_t p0 = 0, p1 = 0;
+  #pragma unroll
+        for (int i = 0; i < 8; ++i) {
+          const float q0 = fminf(fmaxf(rintf(xh[i] * rcp), -8.f), 7.f);
+          const float q1 = fminf(fmaxf(rintf(xh[8 + i] * rcp), -8.f), 7.f);
+          p0 |= (static_cast<uint32_t>(static_cast<int>(q0)) & 0xFu) << (4 * i);
+          p1 |= (static_cast<uint32_t>(static_cast<int>(q1)) & 0xFu) << (4 * i);
+        }
+        if (row_ok) {
+          *reinterpret_cast<uint2*>(x_codes + static_cast<size_t>(row) * (K / 2) + (k0 >> 1)) = make_uint2(p0, p1);
+          if (lane < 16) x_scales[static_cast<size_t>(g) * M + row] = sh;
+        }
       }
       if constexpr (NT > 0) {
         const v8bf a0 = pack_bf16x8(xh);
@@ -566,10 +571,10 @@ __global__ __launch_bounds__(K2_THREADS, 2) void k_gemm_w4a4_lora_up(
   }
 }
 
-template <int ACT, int NT>
+template <int ACT, int NT, bool QUANT>
 void launch_k1_kernel(const void* x, const float* smooth_inv, const void* lora_down, int M, int K, int rank,
                       void* x_codes, void* x_scales, float* lora_act, size_t smem, hipStream_t st) {
-  auto kern = k_quant_act_lora_down<ACT, NT>;
+  auto kern = k_quant_act_lora_down<ACT, NT, QUANT>;
   if (smem > 64 * 1024)
     (void)hipFuncSetAttribute(reinterpret_cast<const void*>(kern), hipFuncAttributeMaxDynamicSharedMemorySize,
                               static_cast<int>(smem));
@@ -578,18 +583,93 @@ void launch_k1_kernel(const void* x, const float* smooth_inv, const void* lora_d
                      rank, static_cast<uint8_t*>(x_codes), static_cast<_Float16*>(x_scales), lora_act);
 }
 
-template <int ACT>
+template <int ACT, bool QUANT>
 int launch_k1(const void* x, const float* smooth_inv, const void* lora_down, int M, int K, int rank,
               void* x_codes, void* x_scales, float* lora_act, hipStream_t st) {
   const size_t smem = static_cast<size_t>(K) * sizeof(float) + sizeof(float) * K1_MAX_WAVES * 2 * 16 * 16;
   if (smem > 160 * 1024) return SVDQ_ERR_UNSUPPORTED_SHAPE;
   const int nt = rank / 16;
-  if (nt == 0) launch_k1_kernel<ACT, 0>(x, smooth_inv, lora_down, M, K, rank, x_codes, x_scales, lora_act, smem, st);
-  else if (nt <= 2) launch_k1_kernel<ACT, 2>(x, smooth_inv, lora_down, M, K, rank, x_codes, x_scales, lora_act, smem, st);
-  else if (nt <= 4) launch_k1_kernel<ACT, 4>(x, smooth_inv, lora_down, M, K, rank, x_codes, x_scales, lora_act, smem, st);
-  else if (nt <= 8) launch_k1_kernel<ACT, 8>(x, smooth_inv, lora_down, M, K, rank, x_codes, x_scales, lora_act, smem, st);
-  else launch_k1_kernel<ACT, 16>(x, smooth_inv, lora_down, M, K, rank, x_codes, x_scales, lora_act, smem, st);
+  if (nt == 0) launch_k1_kernel<ACT, 0, QUANT>(x, smooth_inv, lora_down, M, K, rank, x_codes, x_scales, lora_act, smem, st);
+  else if (nt <= 2) launch_k1_kernel<ACT, 2, QUANT>(x, smooth_inv, lora_down, M, K, rank, x_codes, x_scales, lora_act, smem, st);
+  else if (nt <= 4) launch_k1_kernel<ACT, 4, QUANT>(x, smooth_inv, lora_down, M, K, rank, x_codes, x_scales, lora_act, smem, st);
+  else if (nt <= 8) launch_k1_kernel<ACT, 8, QUANT>(x, smooth_inv, lora_down, M, K, rank, x_codes, x_scales, lora_act, smem, st);
+  else launch_k1_kernel<ACT, 16, QUANT>(x, smooth_inv, lora_down, M, K, rank, x_codes, x_scales, lora_act, smem, st);
   return hipGetLastError() == hipSuccess ? SVDQ_OK : SVDQ_ERR_HIP;
+}
+
+// ---------------------------------------------------------------------
+// Unfused up projection (reference path for the fusion ablation):
+// y = bf16(y + bf16(lora_act) lora_up^T), reading and rewriting the 16-bit
+// output.  Block 128 x 128, 4 waves of 64 x 64, bf16 MFMA 32x32x16 computing
+// the transposed tile (lora_up rows as the A operand) so a lane holds one
+// output row and runs of four columns, loaded and stored as 8-byte chunks.
+__global__ __launch_bounds__(256) void k_lora_up_add(const float* __restrict__ lora_act,
+                                                     const uint16_t* __restrict__ lora_up, int M, int N,
+                                                     int rank, uint16_t* __restrict__ y) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int fr = lane & 31, fk = lane >> 5;
+  const int nN = (N + 127) / 128;
+  const int m0 = (blockIdx.x / nN) * 128 + (wave >> 1) * 64;
+  const int n0 = (blockIdx.x % nN) * 128 + (wave & 1) * 64;
+  v16f acc[2][2];
+#pragma unroll
+  for (int i = 0; i < 2; ++i) {
+    const int row = m0 + i * 32 + fr;
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+#pragma unroll
+      for (int bb = 0; bb < 4; ++bb) {
+        const int c = n0 + j * 32 + 8 * bb + 4 * fk;
+        uint2 v = make_uint2(0, 0);
+        if (row < M && c < N) v = *reinterpret_cast<const uint2*>(y + static_cast<size_t>(row) * N + c);
+        acc[i][j][4 * bb + 0] = bf16_bits_to_f32(v.x & 0xFFFFu);
+        acc[i][j][4 * bb + 1] = bf16_bits_to_f32(v.x >> 16);
+        acc[i][j][4 * bb + 2] = bf16_bits_to_f32(v.y & 0xFFFFu);
+        acc[i][j][4 * bb + 3] = bf16_bits_to_f32(v.y >> 16);
+      }
+    }
+  }
+  for (int kk = 0; kk < rank; kk += 16) {
+    const int kl = kk + fk * 8;
+    v8bf la[2];
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+      const int r = m0 + i * 32 + fr;
+      float v[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+      if (r < M) {
+        const float4* p = reinterpret_cast<const float4*>(lora_act + static_cast<size_t>(r) * rank + kl);
+        const float4 v0 = p[0], v1 = p[1];
+        v[0] = v0.x; v[1] = v0.y; v[2] = v0.z; v[3] = v0.w;
+        v[4] = v1.x; v[5] = v1.y; v[6] = v1.z; v[7] = v1.w;
+      }
+      la[i] = pack_bf16x8(v);
+    }
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+      const int c = n0 + j * 32 + fr;
+      uint4 u = make_uint4(0, 0, 0, 0);
+      if (c < N) u = *reinterpret_cast<const uint4*>(lora_up + static_cast<size_t>(c) * rank + kl);
+      const v8bf ub = __builtin_bit_cast(v8bf, u);
+#pragma unroll
+      for (int i = 0; i < 2; ++i) acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ub, la[i], acc[i][j], 0, 0, 0);
+    }
+  }
+#pragma unroll
+  for (int i = 0; i < 2; ++i) {
+    const int row = m0 + i * 32 + fr;
+    if (row >= M) continue;
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+#pragma unroll
+      for (int bb = 0; bb < 4; ++bb) {
+        const int c = n0 + j * 32 + 8 * bb + 4 * fk;
+        if (c >= N) continue;
+        const uint32_t lo = f32_to_bf16_bits(acc[i][j][4 * bb + 0]) | (f32_to_bf16_bits(acc[i][j][4 * bb + 1]) << 16);
+        const uint32_t hi = f32_to_bf16_bits(acc[i][j][4 * bb + 2]) | (f32_to_bf16_bits(acc[i][j][4 * bb + 3]) << 16);
+        *reinterpret_cast<uint2*>(y + static_cast<size_t>(row) * N + c) = make_uint2(lo, hi);
+      }
+    }
+  }
 }
 
 template <int OUT_F32, int NT>
@@ -627,8 +707,24 @@ int launch_quant_act_lora_down(const void* x, const float* smooth_inv, const voi
                                float* lora_act, void* stream) {
   hipStream_t st = static_cast<hipStream_t>(stream);
   if (act == SVDQ_ACT_GELU_TANH)
-    return launch_k1<SVDQ_ACT_GELU_TANH>(x, smooth_inv, lora_down, M, K, rank, x_codes, x_scales, lora_act, st);
-  return launch_k1<SVDQ_ACT_NONE>(x, smooth_inv, lora_down, M, K, rank, x_codes, x_scales, lora_act, st);
+    return launch_k1<SVDQ_ACT_GELU_TANH, true>(x, smooth_inv, lora_down, M, K, rank, x_codes, x_scales, lora_act, st);
+  return launch_k1<SVDQ_ACT_NONE, true>(x, smooth_inv, lora_down, M, K, rank, x_codes, x_scales, lora_act, st);
+}
+
+int launch_lora_down(const void* x, const float* smooth_inv, const void* lora_down, int M, int K, int rank,
+                     int act, float* lora_act, void* stream) {
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  if (act == SVDQ_ACT_GELU_TANH)
+    return launch_k1<SVDQ_ACT_GELU_TANH, false>(x, smooth_inv, lora_down, M, K, rank, nullptr, nullptr, lora_act, st);
+  return launch_k1<SVDQ_ACT_NONE, false>(x, smooth_inv, lora_down, M, K, rank, nullptr, nullptr, lora_act, st);
+}
+
+int launch_lora_up_add(const float* lora_act, const void* lora_up, int M, int N, int rank, void* y, void* stream) {
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  const int nb = ((M + 127) / 128) * ((N + 127) / 128);
+  hipLaunchKernelGGL(k_lora_up_add, dim3(nb), dim3(256), 0, st, lora_act, static_cast<const uint16_t*>(lora_up), M,
+                     N, rank, static_cast<uint16_t*>(y));
+  return hipGetLastError() == hipSuccess ? SVDQ_OK : SVDQ_ERR_HIP;
 }
 
 int launch_gemm_w4a4_lora_up(const void* x_codes, const void* x_scales, const void* w_codes,

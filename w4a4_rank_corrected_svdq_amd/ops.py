@@ -15,7 +15,7 @@ import torch
 from . import _lib as L
 
 __all__ = ["prepare_weights", "quant_act_lora_down", "gemm_w4a4_lora_up", "prepared_bytes",
-           "device_check"]
+           "device_check", "lora_down", "lora_up_add"]
 
 
 def _ptr(t) -> Optional[int]:
@@ -156,3 +156,33 @@ def gemm_w4a4_lora_up(x_codes, x_scales, w_codes, w_scales, lora_act, lora_up, b
         M, N, K, rank, group, out_dtype, _dev_arg("y", out, dt, (M, N), dev), _stream(dev))
     L.check(st, "svdq_gemm_w4a4_lora_up")
     return out
+
+
+def lora_down(x: torch.Tensor, smooth_inv: torch.Tensor, lora_down_w: torch.Tensor, rank: int,
+              group: int = 64, act: int = L.SVDQ_ACT_NONE, out: Optional[torch.Tensor] = None):
+    """Unfused down projection (reads x again): lora_act [M][rank] fp32."""
+    x = x.contiguous()
+    M, K = x.shape
+    dev = x.device
+    if out is None:
+        out = torch.empty((M, rank), dtype=torch.float32, device=dev)
+    st = L.lib().svdq_lora_down(
+        _dev_arg("x", x, torch.bfloat16, (M, K), dev),
+        _dev_arg("smooth_inv", smooth_inv, torch.float32, (K,), dev),
+        _dev_arg("lora_down", lora_down_w, torch.bfloat16, (rank, K), dev),
+        M, K, rank, group, act, _dev_arg("lora_act", out, torch.float32, (M, rank), dev), _stream(dev))
+    L.check(st, "svdq_lora_down")
+    return out
+
+
+def lora_up_add(lora_act: torch.Tensor, lora_up_w: torch.Tensor, y: torch.Tensor):
+    """Unfused up projection: y = bf16(y + bf16(lora_act) lora_up^T), in place."""
+    M, rank = lora_act.shape
+    N = y.shape[1]
+    dev = y.device
+    st = L.lib().svdq_lora_up_add(
+        _dev_arg("lora_act", lora_act, torch.float32, (M, rank), dev),
+        _dev_arg("lora_up", lora_up_w, torch.bfloat16, (N, rank), dev),
+        M, N, rank, _dev_arg("y", y, torch.bfloat16, (M, N), dev), _stream(dev))
+    L.check(st, "svdq_lora_up_add")
+    return y
