@@ -400,3 +400,21 @@ def test_linear_module_with_oracle_prepared_arrays():
     y = lin(dev_bf16(wl.x_bits))
     torch.cuda.synchronize()
     assert O.rel_fro(to_np_bf16(y), O.forward(wl.x, po, bias=Lr.bias)) < Y_TOL
+
+
+def test_checkpoint_round_trip_forward(tmp_path):
+    """A layer saved to a checkpoint and loaded back computes bit-identical
+    outputs, and matches the oracle on the prepared arrays it holds."""
+    from w4a4_rank_corrected_svdq_amd import checkpoint as C
+    M, K, N = 64, 512, 264
+    wl = workloads.custom_workload(M, K, N, seed=62, n_out=4, bias=True)
+    Lr = wl.layers[0]
+    p = S.prepare_weights(Lr.weight_bits, wl.act_absmax(), rank=32)
+    path = str(tmp_path / "ckpt.safetensors")
+    C.save_prepared(path, {"proj": p}, {"proj": Lr.bias_bits})
+    lin0 = S.SVDQW4A4Linear(p, torch.from_numpy(Lr.bias_bits.view(np.int16).copy()).view(torch.bfloat16), "cuda")
+    lin1 = C.load_linears(path)["proj"]
+    x = dev_bf16(wl.x_bits)
+    y0, y1 = lin0(x), lin1(x)
+    torch.cuda.synchronize()
+    np.testing.assert_array_equal(y0.view(torch.int16).cpu().numpy(), y1.view(torch.int16).cpu().numpy())

@@ -8,5 +8,6 @@ from . import _lib as abi  # noqa: F401
 from .ops import (device_check, gemm_w4a4_lora_up, lora_down, lora_up_add,  # noqa: F401
                   prepare_weights, prepared_bytes, quant_act_lora_down)
 from .linear import SVDQW4A4Linear  # noqa: F401
+from .checkpoint import load_linears, load_prepared, save_prepared  # noqa: F401
 
 __version__ = "0.1.0"
