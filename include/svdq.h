@@ -182,6 +182,60 @@ int svdq_lora_down(const void* x, const float* smooth_inv, const void* lora_down
 int svdq_lora_up_add(const float* lora_act, const void* lora_up, int M, int N, int rank, void* y,
                      void* stream);
 
+/* ------------------------------------------------------------------------
+ * 4-bit float variant (MXFP4).  The pages offer the layer with INT4 and with
+ * 4-bit float operands ("Bringing Nunchaku 4-bit Diffusion Inference to
+ * Diffusers", "Background: SVDQuant and Nunchaku"; the ``precision`` field
+ * of "Native loading in Diffusers").  The float encoding here is the one
+ * gfx950's matrix cores apply natively, OCP Microscaling MXFP4: FP4 E2M1
+ * elements (magnitudes 0, 0.5, 1, 1.5, 2, 3, 4, 6; two per byte, low nibble
+ * = even k, sign in bit 3) with one E8M0 scale byte 2^(s - 127) per block of
+ * 32 consecutive k.  A block's scale is 2^e, e = floor(log2(amax)) - 2
+ * clamped to [-127, 127] (e = -127 for an all-zero block); elements are
+ * v / 2^e rounded to nearest E2M1 with ties to the even code and saturation
+ * at 6, and a value that rounds to zero is code 0.  Smoothing, the low-rank
+ * branch and the conventions above are those of the INT4 layer.  K must be
+ * a multiple of 128 (and at most 32768 for the activation kernel).
+ * ------------------------------------------------------------------------ */
+
+/* Bytes of one MXFP4-prepared layer: codes N*K/2 + scales (K/32)*N + bf16
+ * factors 2*rank*(K+N) + fp32 smooth_inv 4*K. */
+int svdq_prepared_bytes_mxfp4(int K, int N, int rank, size_t* bytes_out);
+
+/* Host, synchronous.  As svdq_prepare_weights_ex with the residual R
+ * quantized to MXFP4 per (output channel, block of 32 along K):
+ *   w_codes  [N][K/2]  u8  E2M1 codes
+ *   w_scales [N][K/32] u8  E8M0 scales, row-major per output channel */
+int svdq_prepare_weights_mxfp4(const uint16_t* weight, int K, int N,
+                               const float* act_absmax, float alpha, int rank,
+                               const uint16_t* lora_down_in, const uint16_t* lora_up_in,
+                               int power_iters, uint64_t seed,
+                               float* smooth_inv, uint8_t* w_codes, uint8_t* w_scales,
+                               uint16_t* lora_down, uint16_t* lora_up, double* sigma_out);
+
+/* Device, asynchronous.  Kernel 1 with the MXFP4 quantizer: x_hat as for
+ * INT4 (fp32), then per (token, block of 32) the block scale and E2M1 codes
+ * above; the down projection is unchanged.
+ *   x_codes  [M][K/2]  u8  E2M1 codes
+ *   x_scales [M][K/32] u8  E8M0 scales, row-major per token
+ *   lora_act [M][rank] fp32 (NULL allowed when rank == 0) */
+int svdq_quant_act_lora_down_mxfp4(const void* x, const float* smooth_inv, const void* lora_down,
+                                   int M, int K, int rank, int act,
+                                   void* x_codes, void* x_scales, float* lora_act, void* stream);
+
+/* Device, asynchronous.  Kernel 2 for MXFP4 operands on the block-scaled FP4
+ * MFMA (v_mfma_scale_f32_32x32x64_f8f6f4), which applies both scales and
+ * accumulates in fp32:
+ *   y = sum_b 2^(ex[m,b] + ew[n,b]) sum_{k in b} qx[m,k] qw[n,k]
+ *       + sum_j bf16(lora_act[m,j]) lora_up[n][j] + bias[n],
+ * rounded to bf16 (or stored fp32).  The MFMA's summation order inside an
+ * instruction is the hardware's; across instructions k increases. */
+int svdq_gemm_mxfp4_lora_up(const void* x_codes, const void* x_scales,
+                            const void* w_codes, const void* w_scales,
+                            const float* lora_act, const void* lora_up, const void* bias,
+                            int M, int N, int K, int rank, int out_dtype,
+                            void* y, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

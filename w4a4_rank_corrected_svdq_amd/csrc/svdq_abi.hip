@@ -46,6 +46,10 @@ int current_device_check() {
 
 inline bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 
+// The kernels address each operand through a buffer resource whose size
+// field is a signed 32-bit byte count.
+inline bool fits_buffer(int64_t rows, int64_t bytes_per_row) { return rows * bytes_per_row <= INT32_MAX; }
+
 }  // namespace
 
 extern "C" const char* svdq_status_string(int status) {
@@ -108,6 +112,7 @@ extern "C" int svdq_gemm_w4a4_lora_up(const void* x_codes, const void* x_scales,
       !aligned16(y) || (bias && !aligned16(bias)) ||
       (rank > 0 && (!aligned16(lora_act) || !aligned16(lora_up))))
     return SVDQ_ERR_INVALID_ARG;
+  if (!fits_buffer(M, K / 2) || !fits_buffer(N, K / 2)) return SVDQ_ERR_UNSUPPORTED_SHAPE;
   st = current_device_check();
   if (st != SVDQ_OK) return st;
   if (M == 0) return SVDQ_OK;
@@ -140,4 +145,44 @@ extern "C" int svdq_lora_up_add(const float* lora_act, const void* lora_up, int 
   if (st != SVDQ_OK) return st;
   if (M == 0) return SVDQ_OK;
   return svdq::launch_lora_up_add(lora_act, lora_up, M, N, rank, y, stream);
+}
+
+extern "C" int svdq_quant_act_lora_down_mxfp4(const void* x, const float* smooth_inv, const void* lora_down,
+                                              int M, int K, int rank, int act, void* x_codes, void* x_scales,
+                                              float* lora_act, void* stream) {
+  if (M < 0 || K <= 0 || rank < 0 || rank > K) return SVDQ_ERR_INVALID_ARG;
+  if (K % 128 != 0 || rank % 16 != 0 || rank > SVDQ_MAX_RANK || K > 32768) return SVDQ_ERR_UNSUPPORTED_SHAPE;
+  if (act != SVDQ_ACT_NONE && act != SVDQ_ACT_GELU_TANH) return SVDQ_ERR_INVALID_ARG;
+  if (!x || !smooth_inv || !x_codes || !x_scales) return SVDQ_ERR_INVALID_ARG;
+  if (rank > 0 && (!lora_down || !lora_act)) return SVDQ_ERR_INVALID_ARG;
+  if (!aligned16(x) || !aligned16(smooth_inv) || !aligned16(x_codes) || !aligned16(x_scales) ||
+      (rank > 0 && (!aligned16(lora_down) || !aligned16(lora_act))))
+    return SVDQ_ERR_INVALID_ARG;
+  const int st = current_device_check();
+  if (st != SVDQ_OK) return st;
+  if (M == 0) return SVDQ_OK;
+  return svdq::launch_quant_act_lora_down_mxfp4(x, smooth_inv, lora_down, M, K, rank, act, x_codes, x_scales,
+                                                lora_act, stream);
+}
+
+extern "C" int svdq_gemm_mxfp4_lora_up(const void* x_codes, const void* x_scales, const void* w_codes,
+                                       const void* w_scales, const float* lora_act, const void* lora_up,
+                                       const void* bias, int M, int N, int K, int rank, int out_dtype,
+                                       void* y, void* stream) {
+  if (M < 0) return SVDQ_ERR_INVALID_ARG;
+  int st = svdq::validate_shape_mx(K, N, rank);
+  if (st != SVDQ_OK) return st;
+  if (out_dtype != SVDQ_OUT_BF16 && out_dtype != SVDQ_OUT_F32) return SVDQ_ERR_INVALID_ARG;
+  if (!x_codes || !x_scales || !w_codes || !w_scales || !y) return SVDQ_ERR_INVALID_ARG;
+  if (rank > 0 && (!lora_act || !lora_up)) return SVDQ_ERR_INVALID_ARG;
+  if (!aligned16(x_codes) || !aligned16(x_scales) || !aligned16(w_codes) || !aligned16(w_scales) ||
+      !aligned16(y) || (bias && !aligned16(bias)) ||
+      (rank > 0 && (!aligned16(lora_act) || !aligned16(lora_up))))
+    return SVDQ_ERR_INVALID_ARG;
+  if (!fits_buffer(M, K / 2) || !fits_buffer(N, K / 2)) return SVDQ_ERR_UNSUPPORTED_SHAPE;
+  st = current_device_check();
+  if (st != SVDQ_OK) return st;
+  if (M == 0) return SVDQ_OK;
+  return svdq::launch_gemm_mxfp4_lora_up(x_codes, x_scales, w_codes, w_scales, lora_act, lora_up, bias, M, N,
+                                         K, rank, out_dtype, y, stream);
 }

@@ -1,0 +1,67 @@
+// Device helpers shared by the HIP translation units of the library.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace {
+
+typedef int v4i __attribute__((ext_vector_type(4)));
+typedef float v4f __attribute__((ext_vector_type(4)));
+typedef short v8s __attribute__((ext_vector_type(8)));
+typedef __bf16 v8bf __attribute__((ext_vector_type(8)));
+typedef int v8i __attribute__((ext_vector_type(8)));
+typedef int v16i __attribute__((ext_vector_type(16)));
+typedef float v16f __attribute__((ext_vector_type(16)));
+
+constexpr int GROUP = 64;
+
+__device__ __forceinline__ float bf16_bits_to_f32(uint32_t h) { return __uint_as_float(h << 16); }
+
+// fp32 -> bf16 bits, round to nearest even (finite inputs).
+__device__ __forceinline__ uint32_t f32_to_bf16_bits(float f) {
+  __bf16 b = static_cast<__bf16>(f);
+  return static_cast<uint32_t>(__builtin_bit_cast(unsigned short, b));
+}
+
+__device__ __forceinline__ v8bf pack_bf16x8(const float* v) {
+  v8s s;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) s[i] = static_cast<short>(f32_to_bf16_bits(v[i]));
+  return __builtin_bit_cast(v8bf, s);
+}
+
+__device__ __forceinline__ float gelu_tanh(float x) {
+  const float k0 = 0.7978845608028654f;  // sqrt(2/pi)
+  const float u = k0 * (x + 0.044715f * x * x * x);
+  return 0.5f * x * (1.0f + tanhf(u));
+}
+
+// FP4 E2M1 code of v: nearest of 0, 0.5, 1, 1.5, 2, 3, 4, 6 with ties to the
+// even code (mantissa bit 0), saturating at 6; the sign bit is set only for
+// a nonzero result, so values that round to zero give code 0.
+__device__ __forceinline__ uint32_t e2m1_code(float v) {
+  const float a = fabsf(v);
+  uint32_t c = (a > 0.25f) + (a >= 0.75f) + (a > 1.25f) + (a >= 1.75f) + (a > 2.5f) + (a >= 3.5f) + (a > 5.0f);
+  return c | ((v < 0.f && c != 0u) ? 8u : 0u);
+}
+
+// Map the linear block index to an output tile so that the blocks of one
+// XCD (the hardware deals blocks round-robin over 8 XCDs) cover a compact
+// band of rows and share A panels and B panels in their L2.
+__device__ __forceinline__ void xcd_tile(int nM, int nN, int& tm, int& tn) {
+  const int nb = nM * nN;
+  const int b = blockIdx.x;
+  int t = b;
+  if ((nb & 7) == 0) t = (b & 7) * (nb >> 3) + (b >> 3);
+  constexpr int GM = 4;
+  const int per = GM * nN;
+  const int grp = t / per;
+  const int first = grp * GM;
+  const int gm = min(GM, nM - first);
+  const int r = t - grp * per;
+  tm = first + r % gm;
+  tn = r / gm;
+}
+
+}  // namespace

@@ -6,6 +6,8 @@ namespace svdq {
 
 // Shape rules common to every entry point (see svdq.h).
 int validate_shape(int K, int N, int rank, int group);
+// Shape rules of the MXFP4 entry points (K a multiple of 128).
+int validate_shape_mx(int K, int N, int rank);
 
 // Kernel launchers (svdq_kernels.hip).  Arguments already validated.
 int launch_quant_act_lora_down(const void* x, const float* smooth_inv, const void* lora_down, int M,
@@ -18,5 +20,14 @@ int launch_gemm_w4a4_lora_up(const void* x_codes, const void* x_scales, const vo
                              const void* w_scales, const float* lora_act, const void* lora_up,
                              const void* bias, int M, int N, int K, int rank, int out_dtype, void* y,
                              void* stream);
+
+int launch_quant_act_lora_down_mxfp4(const void* x, const float* smooth_inv, const void* lora_down, int M,
+                                     int K, int rank, int act, void* x_codes, void* x_scales,
+                                     float* lora_act, void* stream);
+// svdq_mx_kernels.hip
+int launch_gemm_mxfp4_lora_up(const void* x_codes, const void* x_scales, const void* w_codes,
+                              const void* w_scales, const float* lora_act, const void* lora_up,
+                              const void* bias, int M, int N, int K, int rank, int out_dtype, void* y,
+                              void* stream);
 
 }  // namespace svdq

@@ -24,41 +24,16 @@
 #include "svdq.h"
 #include "svdq_internal.h"
 
+#include "svdq_device.h"
+
 namespace {
-
-typedef int v4i __attribute__((ext_vector_type(4)));
-typedef float v4f __attribute__((ext_vector_type(4)));
-typedef short v8s __attribute__((ext_vector_type(8)));
-typedef __bf16 v8bf __attribute__((ext_vector_type(8)));
-
-constexpr int GROUP = 64;
-
-__device__ __forceinline__ float bf16_bits_to_f32(uint32_t h) { return __uint_as_float(h << 16); }
-
-// fp32 -> bf16 bits, round to nearest even (finite inputs).
-__device__ __forceinline__ uint32_t f32_to_bf16_bits(float f) {
-  __bf16 b = static_cast<__bf16>(f);
-  return static_cast<uint32_t>(__builtin_bit_cast(unsigned short, b));
-}
-
-__device__ __forceinline__ v8bf pack_bf16x8(const float* v) {
-  v8s s;
-#pragma unroll
-  for (int i = 0; i < 8; ++i) s[i] = static_cast<short>(f32_to_bf16_bits(v[i]));
-  return __builtin_bit_cast(v8bf, s);
-}
-
-__device__ __forceinline__ float gelu_tanh(float x) {
-  const float k0 = 0.7978845608028654f;  // sqrt(2/pi)
-  const float u = k0 * (x + 0.044715f * x * x * x);
-  return 0.5f * x * (1.0f + tanhf(u));
-}
 
 // =====================================================================
 // Kernel 1
 // =====================================================================
-// With QUANT = false the kernel computes only the down projection (the
-// unfused reference path, which reads X a second time).
+// QM selects the quantizer: INT4 (group 64, fp16 scale), MXFP4 (E2M1
+// elements, E8M0 scale per 32) or none, which leaves only the down
+// projection (the unfused reference path, which reads X a second time).
 //
 // Block: 16 token rows, 16 waves (8 for ranks above 64); wave w handles
 // groups w, w+W, ... of K in batches of up to 2 groups whose loads are all
@@ -76,11 +51,13 @@ constexpr int K1_MAX_WAVES = 16;
 // registers.
 template <int NT> constexpr int k1_waves() { return NT <= 4 ? 16 : 8; }
 
-template <int ACT, int NT, bool QUANT>
+enum { Q_NONE = 0, Q_INT4 = 1, Q_MXFP4 = 2 };
+
+template <int ACT, int NT, int QM>
 __global__ __launch_bounds__(k1_waves<NT>() * 64) void k_quant_act_lora_down(
     const uint16_t* __restrict__ x, const float* __restrict__ smooth_inv,
     const uint16_t* __restrict__ lora_down, int M, int K, int rank,
-    uint8_t* __restrict__ x_codes, _Float16* __restrict__ x_scales, float* __restrict__ lora_act) {
+    uint8_t* __restrict__ x_codes, void* __restrict__ x_scales_v, float* __restrict__ lora_act) {
   extern __shared__ __align__(16) unsigned char k1_smem_raw[];
   float* s_si = reinterpret_cast<float*>(k1_smem_raw);                  // [K]
   float(*red)[2][16][16] = reinterpret_cast<float(*)[2][16][16]>(s_si + K);  // [waves][2][16][16]
@@ -139,9 +116,10 @@ __global__ __launch_bounds__(k1_waves<NT>() * 64) void k_quant_act_lora_down(
         xh[2 * i] = lo * sv[2 * i];
         xh[2 * i + 1] = hi * sv[2 * i + 1];
       }
-      if constexpr (QUANT) {
+      if constexpr (QM == Q_INT4) {
+        _Float16* x_scales = static_cast<_Float16*>(x_scales_v);
         float amax = 0.f;
-  #pragma unroll
+#pragma unroll
         for (int i = 0; i < 16; ++i) amax = fmaxf(amax, fabsf(xh[i]));
         amax = fmaxf(amax, __shfl_xor(amax, 16));
         amax = fmaxf(amax, __shfl_xor(amax, 32));
@@ -150,7 +128,7 @@ __global__ __launch_bounds__(k1_waves<NT>() * 64) void k_quant_act_lora_down(
         const float sf = static_cast<float>(sh);
         const float rcp = (sf == 0.f) ? 0.f : 1.0f / sf;
         uint32_t p0 = 0, p1 = 0;
-  #pragma unroll
+#pragma unroll
         for (int i = 0; i < 8; ++i) {
           const float q0 = fminf(fmaxf(rintf(xh[i] * rcp), -8.f), 7.f);
           const float q1 = fminf(fmaxf(rintf(xh[8 + i] * rcp), -8.f), 7.f);
@@ -160,6 +138,30 @@ __global__ __launch_bounds__(k1_waves<NT>() * 64) void k_quant_act_lora_down(
         if (row_ok) {
           *reinterpret_cast<uint2*>(x_codes + static_cast<size_t>(row) * (K / 2) + (k0 >> 1)) = make_uint2(p0, p1);
           if (lane < 16) x_scales[static_cast<size_t>(g) * M + row] = sh;
+        }
+      } else if constexpr (QM == Q_MXFP4) {
+        // MXFP4: blocks of 32 k are the lane pairs (l, l ^ 16).  Scale
+        // 2^e with e = floor(log2 amax) - 2 read off the exponent field,
+        // clamped at -127 (zero and tiny blocks); x_hat * 2^-e is exact.
+        uint8_t* x_scales = static_cast<uint8_t*>(x_scales_v);
+        float amax = 0.f;
+#pragma unroll
+        for (int i = 0; i < 16; ++i) amax = fmaxf(amax, fabsf(xh[i]));
+        amax = fmaxf(amax, __shfl_xor(amax, 16));
+        const int ebits = static_cast<int>(__float_as_uint(amax) >> 23);   // amax >= 0
+        const int e = max(ebits - 129, -127);
+        const float f = __uint_as_float(static_cast<uint32_t>(127 - e) << 23);
+        uint32_t p0 = 0, p1 = 0;
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+          const uint32_t c = e2m1_code(xh[i] * f);
+          if (i < 8) p0 |= c << (4 * i);
+          else p1 |= c << (4 * (i - 8));
+        }
+        if (row_ok) {
+          *reinterpret_cast<uint2*>(x_codes + static_cast<size_t>(row) * (K / 2) + (k0 >> 1)) = make_uint2(p0, p1);
+          if (((lane >> 4) & 1) == 0)
+            x_scales[static_cast<size_t>(row) * (K / 32) + (k0 >> 5)] = static_cast<uint8_t>(e + 127);
         }
       }
       if constexpr (NT > 0) {
@@ -268,8 +270,6 @@ constexpr int K2_TJ = K2_WN / 32;             // along N
 constexpr int MAGIC_I = 0x4B400000;
 constexpr float MAGIC_F = 12582912.0f;         // 1.5 * 2^23
 
-typedef int v16i __attribute__((ext_vector_type(16)));
-typedef float v16f __attribute__((ext_vector_type(16)));
 
 struct K2Smem {
   uint4 a[2][K2_SG][K2_BM][4];                 // unpacked activations, 16 B chunks
@@ -284,24 +284,6 @@ __device__ __forceinline__ int k2_swz(int row, int chunk) { return chunk ^ (((ro
 __device__ __forceinline__ int k2_swpos(int c) {
   const int cc = c & 31;
   return (c & ~31) | (((cc >> 2) & 1) << 4) | ((cc >> 3) << 2) | (cc & 3);
-}
-
-// Map the linear block index to an output tile so that the blocks of one
-// XCD (the hardware deals blocks round-robin over 8 XCDs) cover a compact
-// band of rows and share A panels and B panels in their L2.
-__device__ __forceinline__ void k2_tile(int nM, int nN, int& tm, int& tn) {
-  const int nb = nM * nN;
-  const int b = blockIdx.x;
-  int t = b;
-  if ((nb & 7) == 0) t = (b & 7) * (nb >> 3) + (b >> 3);
-  constexpr int GM = 4;
-  const int per = GM * nN;
-  const int grp = t / per;
-  const int first = grp * GM;
-  const int gm = min(GM, nM - first);
-  const int r = t - grp * per;
-  tm = first + r % gm;
-  tn = r / gm;
 }
 
 __device__ __forceinline__ uint4 unpack_lo(uint4 w) {  // codes 0..15 of a 32-code chunk
@@ -326,7 +308,7 @@ __global__ __launch_bounds__(K2_THREADS, 2) void k_gemm_w4a4_lora_up(
   const int wm = wave >> 1, wn = wave & 1;
   const int nM = (M + K2_BM - 1) / K2_BM, nN = (N + K2_BN - 1) / K2_BN;
   int tm, tn;
-  k2_tile(nM, nN, tm, tn);
+  xcd_tile(nM, nN, tm, tn);
   const int m0 = tm * K2_BM, n0 = tn * K2_BN;
   const int G = K / GROUP;
   const int S = (G + K2_SG - 1) / K2_SG;       // stages
@@ -557,6 +539,9 @@ __global__ __launch_bounds__(K2_THREADS, 2) void k_gemm_w4a4_lora_up(
         }
       }
     }
+    // the reads below are of another type than the writes above: keep the
+    // compiler from moving them across (the hardware orders one wave's LDS ops)
+    asm volatile("" ::: "memory");
     const uint4* tile4 = reinterpret_cast<const uint4*>(tile);
     const int cl = lane & 7;                            // 16-byte chunk this lane stores
     const int col = n0 + wn * K2_WN + cl * 8;
@@ -571,29 +556,29 @@ __global__ __launch_bounds__(K2_THREADS, 2) void k_gemm_w4a4_lora_up(
   }
 }
 
-template <int ACT, int NT, bool QUANT>
+template <int ACT, int NT, int QM>
 void launch_k1_kernel(const void* x, const float* smooth_inv, const void* lora_down, int M, int K, int rank,
                       void* x_codes, void* x_scales, float* lora_act, size_t smem, hipStream_t st) {
-  auto kern = k_quant_act_lora_down<ACT, NT, QUANT>;
+  auto kern = k_quant_act_lora_down<ACT, NT, QM>;
   if (smem > 64 * 1024)
     (void)hipFuncSetAttribute(reinterpret_cast<const void*>(kern), hipFuncAttributeMaxDynamicSharedMemorySize,
                               static_cast<int>(smem));
   hipLaunchKernelGGL(kern, dim3((M + K1_ROWS - 1) / K1_ROWS), dim3(k1_waves<NT>() * 64), smem, st,
                      static_cast<const uint16_t*>(x), smooth_inv, static_cast<const uint16_t*>(lora_down), M, K,
-                     rank, static_cast<uint8_t*>(x_codes), static_cast<_Float16*>(x_scales), lora_act);
+                     rank, static_cast<uint8_t*>(x_codes), x_scales, lora_act);
 }
 
-template <int ACT, bool QUANT>
+template <int ACT, int QM>
 int launch_k1(const void* x, const float* smooth_inv, const void* lora_down, int M, int K, int rank,
               void* x_codes, void* x_scales, float* lora_act, hipStream_t st) {
   const size_t smem = static_cast<size_t>(K) * sizeof(float) + sizeof(float) * K1_MAX_WAVES * 2 * 16 * 16;
   if (smem > 160 * 1024) return SVDQ_ERR_UNSUPPORTED_SHAPE;
   const int nt = rank / 16;
-  if (nt == 0) launch_k1_kernel<ACT, 0, QUANT>(x, smooth_inv, lora_down, M, K, rank, x_codes, x_scales, lora_act, smem, st);
-  else if (nt <= 2) launch_k1_kernel<ACT, 2, QUANT>(x, smooth_inv, lora_down, M, K, rank, x_codes, x_scales, lora_act, smem, st);
-  else if (nt <= 4) launch_k1_kernel<ACT, 4, QUANT>(x, smooth_inv, lora_down, M, K, rank, x_codes, x_scales, lora_act, smem, st);
-  else if (nt <= 8) launch_k1_kernel<ACT, 8, QUANT>(x, smooth_inv, lora_down, M, K, rank, x_codes, x_scales, lora_act, smem, st);
-  else launch_k1_kernel<ACT, 16, QUANT>(x, smooth_inv, lora_down, M, K, rank, x_codes, x_scales, lora_act, smem, st);
+  if (nt == 0) launch_k1_kernel<ACT, 0, QM>(x, smooth_inv, lora_down, M, K, rank, x_codes, x_scales, lora_act, smem, st);
+  else if (nt <= 2) launch_k1_kernel<ACT, 2, QM>(x, smooth_inv, lora_down, M, K, rank, x_codes, x_scales, lora_act, smem, st);
+  else if (nt <= 4) launch_k1_kernel<ACT, 4, QM>(x, smooth_inv, lora_down, M, K, rank, x_codes, x_scales, lora_act, smem, st);
+  else if (nt <= 8) launch_k1_kernel<ACT, 8, QM>(x, smooth_inv, lora_down, M, K, rank, x_codes, x_scales, lora_act, smem, st);
+  else launch_k1_kernel<ACT, 16, QM>(x, smooth_inv, lora_down, M, K, rank, x_codes, x_scales, lora_act, smem, st);
   return hipGetLastError() == hipSuccess ? SVDQ_OK : SVDQ_ERR_HIP;
 }
 
@@ -707,16 +692,25 @@ int launch_quant_act_lora_down(const void* x, const float* smooth_inv, const voi
                                float* lora_act, void* stream) {
   hipStream_t st = static_cast<hipStream_t>(stream);
   if (act == SVDQ_ACT_GELU_TANH)
-    return launch_k1<SVDQ_ACT_GELU_TANH, true>(x, smooth_inv, lora_down, M, K, rank, x_codes, x_scales, lora_act, st);
-  return launch_k1<SVDQ_ACT_NONE, true>(x, smooth_inv, lora_down, M, K, rank, x_codes, x_scales, lora_act, st);
+    return launch_k1<SVDQ_ACT_GELU_TANH, Q_INT4>(x, smooth_inv, lora_down, M, K, rank, x_codes, x_scales, lora_act, st);
+  return launch_k1<SVDQ_ACT_NONE, Q_INT4>(x, smooth_inv, lora_down, M, K, rank, x_codes, x_scales, lora_act, st);
+}
+
+int launch_quant_act_lora_down_mxfp4(const void* x, const float* smooth_inv, const void* lora_down, int M,
+                                     int K, int rank, int act, void* x_codes, void* x_scales,
+                                     float* lora_act, void* stream) {
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  if (act == SVDQ_ACT_GELU_TANH)
+    return launch_k1<SVDQ_ACT_GELU_TANH, Q_MXFP4>(x, smooth_inv, lora_down, M, K, rank, x_codes, x_scales, lora_act, st);
+  return launch_k1<SVDQ_ACT_NONE, Q_MXFP4>(x, smooth_inv, lora_down, M, K, rank, x_codes, x_scales, lora_act, st);
 }
 
 int launch_lora_down(const void* x, const float* smooth_inv, const void* lora_down, int M, int K, int rank,
                      int act, float* lora_act, void* stream) {
   hipStream_t st = static_cast<hipStream_t>(stream);
   if (act == SVDQ_ACT_GELU_TANH)
-    return launch_k1<SVDQ_ACT_GELU_TANH, false>(x, smooth_inv, lora_down, M, K, rank, nullptr, nullptr, lora_act, st);
-  return launch_k1<SVDQ_ACT_NONE, false>(x, smooth_inv, lora_down, M, K, rank, nullptr, nullptr, lora_act, st);
+    return launch_k1<SVDQ_ACT_GELU_TANH, Q_NONE>(x, smooth_inv, lora_down, M, K, rank, nullptr, nullptr, lora_act, st);
+  return launch_k1<SVDQ_ACT_NONE, Q_NONE>(x, smooth_inv, lora_down, M, K, rank, nullptr, nullptr, lora_act, st);
 }
 
 int launch_lora_up_add(const float* lora_act, const void* lora_up, int M, int N, int rank, void* y, void* stream) {

@@ -287,7 +287,23 @@ int validate_shape(int K, int N, int rank, int group) {
   return SVDQ_OK;
 }
 
+int validate_shape_mx(int K, int N, int rank) {
+  if (K <= 0 || N <= 0 || rank < 0) return SVDQ_ERR_INVALID_ARG;
+  if (rank > K || rank > N) return SVDQ_ERR_INVALID_ARG;
+  if (K % 128 != 0 || N % 8 != 0 || rank % 16 != 0 || rank > SVDQ_MAX_RANK) return SVDQ_ERR_UNSUPPORTED_SHAPE;
+  return SVDQ_OK;
+}
+
 }  // namespace svdq
+
+extern "C" int svdq_prepared_bytes_mxfp4(int K, int N, int rank, size_t* bytes_out) {
+  if (!bytes_out) return SVDQ_ERR_INVALID_ARG;
+  const int st = svdq::validate_shape_mx(K, N, rank);
+  if (st != SVDQ_OK) return st;
+  const size_t k = static_cast<size_t>(K), n = static_cast<size_t>(N), r = static_cast<size_t>(rank);
+  *bytes_out = n * k / 2 + (k / 32) * n + 2 * r * (k + n) + 4 * k;
+  return SVDQ_OK;
+}
 
 extern "C" int svdq_prepared_bytes(int K, int N, int rank, int group, size_t* bytes_out) {
   if (!bytes_out) return SVDQ_ERR_INVALID_ARG;
@@ -298,17 +314,15 @@ extern "C" int svdq_prepared_bytes(int K, int N, int rank, int group, size_t* by
   return SVDQ_OK;
 }
 
-extern "C" int svdq_prepare_weights_ex(const uint16_t* weight, int K, int N, const float* act_absmax,
-                                       float alpha, int rank, int group, const uint16_t* lora_down_in,
-                                       const uint16_t* lora_up_in, int power_iters, uint64_t seed,
-                                       float* smooth_inv, uint8_t* w_codes, uint16_t* w_scales,
-                                       uint16_t* lora_down, uint16_t* lora_up, double* sigma_out) {
-  int st = svdq::validate_shape(K, N, rank, group);
-  if (st != SVDQ_OK) return st;
-  if (!weight || !act_absmax || !smooth_inv || !w_codes || !w_scales) return SVDQ_ERR_INVALID_ARG;
-  if (rank > 0 && (!lora_down || !lora_up)) return SVDQ_ERR_INVALID_ARG;
-  if ((lora_down_in == nullptr) != (lora_up_in == nullptr)) return SVDQ_ERR_INVALID_ARG;
-  if (!(alpha > 0.0f && alpha < 1.0f)) return SVDQ_ERR_INVALID_ARG;
+namespace {
+
+// Stages 2 and 3 shared by both encodings: smoothing factors, the low-rank
+// split (or the given factors) and the fp64 residual A = W_hat - L1 L2,
+// stored [N][K].  Inputs are checked for finiteness first.
+int smooth_split_residual(const uint16_t* weight, int K, int N, const float* act_absmax, float alpha,
+                          int rank, const uint16_t* lora_down_in, const uint16_t* lora_up_in,
+                          int power_iters, uint64_t seed, float* smooth_inv, uint16_t* lora_down,
+                          uint16_t* lora_up, double* sigma_out, std::vector<double>& A) {
   const size_t NK = static_cast<size_t>(N) * K;
   if (!all_finite_bf16(weight, NK)) return SVDQ_ERR_NUMERIC;
   for (int k = 0; k < K; ++k)
@@ -335,7 +349,7 @@ extern "C" int svdq_prepare_weights_ex(const uint16_t* weight, int K, int N, con
     smooth_inv[k] = si;
     lam[k] = 1.0 / static_cast<double>(si);
   }
-  std::vector<double> A(NK);
+  A.assign(NK, 0.0);
   parallel_for(N, 64, [&](int64_t lo, int64_t hi) {
     for (int64_t n = lo; n < hi; ++n)
       for (int k = 0; k < K; ++k)
@@ -410,6 +424,27 @@ extern "C" int svdq_prepare_weights_ex(const uint16_t* weight, int K, int N, con
     });
   }
 
+  return SVDQ_OK;
+}
+
+}  // namespace
+
+extern "C" int svdq_prepare_weights_ex(const uint16_t* weight, int K, int N, const float* act_absmax,
+                                       float alpha, int rank, int group, const uint16_t* lora_down_in,
+                                       const uint16_t* lora_up_in, int power_iters, uint64_t seed,
+                                       float* smooth_inv, uint8_t* w_codes, uint16_t* w_scales,
+                                       uint16_t* lora_down, uint16_t* lora_up, double* sigma_out) {
+  int st = svdq::validate_shape(K, N, rank, group);
+  if (st != SVDQ_OK) return st;
+  if (!weight || !act_absmax || !smooth_inv || !w_codes || !w_scales) return SVDQ_ERR_INVALID_ARG;
+  if (rank > 0 && (!lora_down || !lora_up)) return SVDQ_ERR_INVALID_ARG;
+  if ((lora_down_in == nullptr) != (lora_up_in == nullptr)) return SVDQ_ERR_INVALID_ARG;
+  if (!(alpha > 0.0f && alpha < 1.0f)) return SVDQ_ERR_INVALID_ARG;
+  std::vector<double> A;
+  st = smooth_split_residual(weight, K, N, act_absmax, alpha, rank, lora_down_in, lora_up_in, power_iters, seed,
+                             smooth_inv, lora_down, lora_up, sigma_out, A);
+  if (st != SVDQ_OK) return st;
+
   // ---- 4-bit residual: per (group, output channel) symmetric, fp16 scale
   const int G = K / group;
   std::atomic<int> bad{0};
@@ -449,4 +484,52 @@ extern "C" int svdq_prepare_weights(const uint16_t* weight, int K, int N, const 
   return svdq_prepare_weights_ex(weight, K, N, act_absmax, alpha, rank, group, nullptr, nullptr, 0,
                                  0x5356445175616E74ull, smooth_inv, w_codes, w_scales, lora_down,
                                  lora_up, nullptr);
+}
+
+extern "C" int svdq_prepare_weights_mxfp4(const uint16_t* weight, int K, int N, const float* act_absmax,
+                                          float alpha, int rank, const uint16_t* lora_down_in,
+                                          const uint16_t* lora_up_in, int power_iters, uint64_t seed,
+                                          float* smooth_inv, uint8_t* w_codes, uint8_t* w_scales,
+                                          uint16_t* lora_down, uint16_t* lora_up, double* sigma_out) {
+  int st = svdq::validate_shape_mx(K, N, rank);
+  if (st != SVDQ_OK) return st;
+  if (!weight || !act_absmax || !smooth_inv || !w_codes || !w_scales) return SVDQ_ERR_INVALID_ARG;
+  if (rank > 0 && (!lora_down || !lora_up)) return SVDQ_ERR_INVALID_ARG;
+  if ((lora_down_in == nullptr) != (lora_up_in == nullptr)) return SVDQ_ERR_INVALID_ARG;
+  if (!(alpha > 0.0f && alpha < 1.0f)) return SVDQ_ERR_INVALID_ARG;
+  std::vector<double> A;
+  st = smooth_split_residual(weight, K, N, act_absmax, alpha, rank, lora_down_in, lora_up_in, power_iters, seed,
+                             smooth_inv, lora_down, lora_up, sigma_out, A);
+  if (st != SVDQ_OK) return st;
+
+  // ---- MXFP4 residual: per (output channel, block of 32 along K), scale
+  // 2^e with e = floor(log2 amax) - 2 clamped to [-127, 127] (-127 for an
+  // all-zero block), elements rounded to E2M1 with ties to even and
+  // saturation at 6; a value rounding to zero is code 0.
+  const int B = K / 32;
+  parallel_for(N, 16, [&](int64_t lo, int64_t hi) {
+    for (int64_t n = lo; n < hi; ++n) {
+      const double* r = &A[n * K];
+      uint8_t* dst = w_codes + n * (K / 2);
+      for (int b = 0; b < B; ++b) {
+        double amax = 0.0;
+        for (int k = b * 32; k < (b + 1) * 32; ++k) amax = std::max(amax, std::fabs(r[k]));
+        int e = amax == 0.0 ? -127 : std::ilogb(amax) - 2;
+        e = std::max(-127, std::min(127, e));
+        w_scales[n * B + b] = static_cast<uint8_t>(e + 127);
+        for (int k = b * 32; k < (b + 1) * 32; k += 2) {
+          uint32_t c[2];
+          for (int t = 0; t < 2; ++t) {
+            const double v = std::ldexp(r[k + t], -e);
+            const double a = std::fabs(v);
+            uint32_t q = (a > 0.25) + (a >= 0.75) + (a > 1.25) + (a >= 1.75) + (a > 2.5) + (a >= 3.5) + (a > 5.0);
+            if (v < 0.0 && q != 0) q |= 8u;
+            c[t] = q;
+          }
+          dst[k / 2] = static_cast<uint8_t>(c[0] | (c[1] << 4));
+        }
+      }
+    }
+  });
+  return SVDQ_OK;
 }

@@ -15,7 +15,8 @@ import torch
 from . import _lib as L
 
 __all__ = ["prepare_weights", "quant_act_lora_down", "gemm_w4a4_lora_up", "prepared_bytes",
-           "device_check", "lora_down", "lora_up_add"]
+           "device_check", "lora_down", "lora_up_add", "prepared_bytes_mxfp4", "prepare_weights_mxfp4",
+           "quant_act_lora_down_mxfp4", "gemm_mxfp4_lora_up"]
 
 
 def _ptr(t) -> Optional[int]:
@@ -186,3 +187,90 @@ def lora_up_add(lora_act: torch.Tensor, lora_up_w: torch.Tensor, y: torch.Tensor
         M, N, rank, _dev_arg("y", y, torch.bfloat16, (M, N), dev), _stream(dev))
     L.check(st, "svdq_lora_up_add")
     return y
+
+
+# ---------------------------------------------------------------- MXFP4 variant
+def prepared_bytes_mxfp4(K: int, N: int, rank: int) -> int:
+    out = ctypes.c_size_t(0)
+    L.check(L.lib().svdq_prepared_bytes_mxfp4(K, N, rank, ctypes.byref(out)), "svdq_prepared_bytes_mxfp4")
+    return int(out.value)
+
+
+def prepare_weights_mxfp4(weight, act_absmax, rank: int = 32, alpha: float = 0.5, factors=None,
+                          power_iters: int = 0, seed: int = 0x5356445175616E74,
+                          return_sigma: bool = False) -> dict:
+    """Host preparation with the MXFP4 residual (svdq_prepare_weights_mxfp4).
+    Returns numpy arrays: smooth_inv f32 [K], w_codes u8 [N][K/2] (E2M1),
+    w_scales u8 [N][K/32] (E8M0), lora_down / lora_up bf16 bits."""
+    w = _bf16_bits(weight)
+    N, K = w.shape
+    a = np.ascontiguousarray(np.asarray(act_absmax, dtype=np.float32).reshape(K))
+    si = np.empty(K, np.float32)
+    wc = np.empty((N, K // 2), np.uint8)
+    ws = np.empty((N, max(K // 32, 0)), np.uint8)
+    ld = np.empty((rank, K), np.uint16)
+    lu = np.empty((N, rank), np.uint16)
+    sig = np.empty(max(rank, 1), np.float64)
+    fin = (None, None)
+    if factors is not None:
+        fin = tuple(np.ascontiguousarray(np.asarray(f, dtype=np.uint16)) for f in factors)
+        if fin[0].shape != (rank, K) or fin[1].shape != (N, rank):
+            raise ValueError("factors must be lora_down [rank][K] and lora_up [N][rank]")
+    st = L.lib().svdq_prepare_weights_mxfp4(
+        _ptr(w), K, N, _ptr(a), float(alpha), rank, _ptr(fin[0]), _ptr(fin[1]),
+        int(power_iters), int(seed) & (2 ** 64 - 1), _ptr(si), _ptr(wc), _ptr(ws),
+        _ptr(ld) if rank else None, _ptr(lu) if rank else None, _ptr(sig))
+    L.check(st, "svdq_prepare_weights_mxfp4")
+    out = dict(smooth_inv=si, w_codes=wc, w_scales=ws, lora_down=ld, lora_up=lu,
+               rank=rank, group=32, K=K, N=N, precision="mxfp4")
+    if return_sigma:
+        out["sigma"] = sig[:rank].copy()
+    return out
+
+
+def quant_act_lora_down_mxfp4(x: torch.Tensor, smooth_inv: torch.Tensor, lora_down: Optional[torch.Tensor],
+                              rank: int, act: int = L.SVDQ_ACT_NONE, out=None):
+    """Kernel 1 with the MXFP4 quantizer.  Returns (x_codes u8 [M][K/2],
+    x_scales u8 [M][K/32], lora_act f32 [M][rank])."""
+    if x.dtype != torch.bfloat16 or x.dim() != 2 or not x.is_cuda:
+        raise TypeError("x must be a 2-D bfloat16 CUDA tensor")
+    x = x.contiguous()
+    M, K = x.shape
+    dev = x.device
+    if out is None:
+        xc = torch.empty((M, K // 2), dtype=torch.uint8, device=dev)
+        xs = torch.empty((M, K // 32), dtype=torch.uint8, device=dev)
+        la = torch.empty((M, rank), dtype=torch.float32, device=dev) if rank else None
+    else:
+        xc, xs, la = out
+    st = L.lib().svdq_quant_act_lora_down_mxfp4(
+        _dev_arg("x", x, torch.bfloat16, (M, K), dev),
+        _dev_arg("smooth_inv", smooth_inv, torch.float32, (K,), dev),
+        _dev_arg("lora_down", lora_down, torch.bfloat16, (rank, K), dev) if rank else None,
+        M, K, rank, act,
+        _dev_arg("x_codes", xc, torch.uint8, (M, K // 2), dev),
+        _dev_arg("x_scales", xs, torch.uint8, (M, K // 32), dev),
+        _dev_arg("lora_act", la, torch.float32, (M, rank), dev) if rank else None, _stream(dev))
+    L.check(st, "svdq_quant_act_lora_down_mxfp4")
+    return xc, xs, la
+
+
+def gemm_mxfp4_lora_up(x_codes, x_scales, w_codes, w_scales, lora_act, lora_up, bias,
+                       M: int, N: int, K: int, rank: int, out_dtype: int = L.SVDQ_OUT_BF16,
+                       out: Optional[torch.Tensor] = None):
+    """Kernel 2 for MXFP4 operands; returns y [M][N]."""
+    dev = x_codes.device
+    dt = torch.float32 if out_dtype == L.SVDQ_OUT_F32 else torch.bfloat16
+    if out is None:
+        out = torch.empty((M, N), dtype=dt, device=dev)
+    st = L.lib().svdq_gemm_mxfp4_lora_up(
+        _dev_arg("x_codes", x_codes, torch.uint8, (M, K // 2), dev),
+        _dev_arg("x_scales", x_scales, torch.uint8, (M, K // 32), dev),
+        _dev_arg("w_codes", w_codes, torch.uint8, (N, K // 2), dev),
+        _dev_arg("w_scales", w_scales, torch.uint8, (N, K // 32), dev),
+        _dev_arg("lora_act", lora_act, torch.float32, (M, rank), dev) if rank else None,
+        _dev_arg("lora_up", lora_up, torch.bfloat16, (N, rank), dev) if rank else None,
+        _dev_arg("bias", bias, torch.bfloat16, (N,), dev),
+        M, N, K, rank, out_dtype, _dev_arg("y", out, dt, (M, N), dev), _stream(dev))
+    L.check(st, "svdq_gemm_mxfp4_lora_up")
+    return out
