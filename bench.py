@@ -9,7 +9,10 @@ says otherwise.  Weight preparation (smoothing, SVD, 4-bit residual) is a
 one-time offline transform and runs before the timed region.
 
 Prints one JSON line.  value = effective TOPS = 2*M*N*K / (time per step);
-the low-rank flops are not credited.
+the low-rank flops are not credited.  --precision int4 (default) measures
+the INT4 layer (group 64, fp16 scales); the same line carries the MXFP4
+variant (E2M1 codes, E8M0 scale per 32, block-scaled FP4 MFMA) measured on
+the same workload, unless --no-variants.
 """
 from __future__ import annotations
 
@@ -27,6 +30,7 @@ sys.path.insert(0, ROOT)
 
 METRIC = "effective TOPS of fused W4A4+rank-32 linear (FLUX shapes); % INT8 MFMA peak"
 INT8_PEAK_TOPS = 5000.0      # MI355X dense INT8 MFMA, published
+FP4_PEAK_TFLOPS = 10100.0    # MI355X dense FP4 / FP6 MFMA, published
 HBM_PEAK_GBS = 8000.0        # MI355X HBM3E, published
 
 # name -> (generator workload, layer index, act, description)
@@ -39,25 +43,34 @@ BENCH_WORKLOADS = {
 
 
 def kernel_source_hash() -> str:
-    p = os.path.join(ROOT, "w4a4_rank_corrected_svdq_amd", "csrc", "svdq_kernels.hip")
-    return hashlib.sha256(open(p, "rb").read()).hexdigest()[:16]
+    h = hashlib.sha256()
+    for f in ("svdq_kernels.hip", "svdq_mx_kernels.hip", "svdq_device.h"):
+        h.update(open(os.path.join(ROOT, "w4a4_rank_corrected_svdq_amd", "csrc", f), "rb").read())
+    return h.hexdigest()[:16]
 
 
-def k1_bytes(M, K, r):
+def scale_bytes(K, precision):
+    """Scale bytes per row: fp16 per 64 (INT4) or one E8M0 byte per 32 (MXFP4)."""
+    return 2 * (K // 64) if precision == "int4" else K // 32
+
+
+def k1_bytes(M, K, r, precision="int4"):
     """Compulsory HBM bytes of kernel 1: read X (bf16), smooth_inv, L1; write
     codes, scales and lora_act."""
-    return 2 * M * K + 4 * K + 2 * r * K + M * K // 2 + 2 * (K // 64) * M + 4 * M * r
+    return 2 * M * K + 4 * K + 2 * r * K + M * K // 2 + scale_bytes(K, precision) * M + 4 * M * r
 
 
-def k2_bytes(M, N, K, r, bias):
-    return (M * K // 2 + 2 * (K // 64) * M + N * K // 2 + 2 * (K // 64) * N + 4 * M * r
+def k2_bytes(M, N, K, r, bias, precision="int4"):
+    sb = scale_bytes(K, precision)
+    return (M * K // 2 + sb * M + N * K // 2 + sb * N + 4 * M * r
             + 2 * N * r + (2 * N if bias else 0) + 2 * M * N)
 
 
-def load_traffic(workload: str, rank: int):
+def load_traffic(workload: str, rank: int, precision: str = "int4"):
     """HBM traffic of kernel 2 measured by rocprofv3 PMC counters (committed
     under profiles/), used only while the kernel source is unchanged."""
-    p = os.path.join(ROOT, "profiles", f"traffic_{workload}_r{rank}.json")
+    tag = "" if precision == "int4" else f"_{precision}"
+    p = os.path.join(ROOT, "profiles", f"traffic_{workload}_r{rank}{tag}.json")
     if not os.path.exists(p):
         return None
     d = json.load(open(p))
@@ -66,7 +79,7 @@ def load_traffic(workload: str, rank: int):
     return d.get("k2_hbm_bytes")
 
 
-def cpu_baseline(wl, layer, rank, target_s):
+def cpu_baseline(wl, layer, rank, target_s, precision="int4"):
     """The oracle (as it stands) on a bounded sample of rows of the same
     workload, timed on this host's cores."""
     import oracle as O
@@ -80,7 +93,8 @@ def cpu_baseline(wl, layer, rank, target_s):
     a = wl.act_absmax()
     # preparation needs the SVD; rank-r factors from the oracle's own split
     t0 = time.perf_counter()
-    po = O.prepare(Lr.weight, a, rank=rank)
+    po = O.prepare(Lr.weight, a, rank=rank) if precision == "int4" else O.mx.prepare_mx(Lr.weight, a, rank=rank)
+    fwd = O.forward if precision == "int4" else O.mx.forward_mx
     t_prep = time.perf_counter() - t0
     rows_per_chunk = 128
     done_rows = 0
@@ -89,12 +103,12 @@ def cpu_baseline(wl, layer, rank, target_s):
     while t_fwd < target_s and done_rows < wl.M:
         xr = x[done_rows:done_rows + rows_per_chunk]
         t0 = time.perf_counter()
-        O.forward(xr, po, bias=Lr.bias)
+        fwd(xr, po, bias=Lr.bias)
         t_fwd += time.perf_counter() - t0
         done_rows += xr.shape[0]
     tops = 2.0 * done_rows * N * K / t_fwd / 1e12
     return {"value": tops, "unit": "TOPS", "cores": int(threads), "kind": "oracle",
-            "sample": f"oracle.forward (fp64 numpy W4A4 emulation) on the first {done_rows} of {wl.M} "
+            "sample": f"oracle forward ({precision}, fp64 numpy emulation) on the first {done_rows} of {wl.M} "
                       f"rows of the same workload, {t_fwd:.1f} s; oracle prepare (LAPACK SVD) "
                       f"took {t_prep:.1f} s and is not counted",
             "host_cpu_count": os.cpu_count()}
@@ -107,8 +121,12 @@ def main():
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--workload", default="mlp_up", choices=sorted(BENCH_WORKLOADS))
     ap.add_argument("--rank", type=int, default=32)
+    ap.add_argument("--precision", default="int4", choices=["int4", "mxfp4"],
+                    help="int4: INT4 group 64 with fp16 scales (the headline layer); "
+                         "mxfp4: E2M1 codes with E8M0 scales per 32 on the block-scaled FP4 MFMA")
     ap.add_argument("--no-overhead", action="store_true", help="skip the rank-0 comparison run")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-variants", action="store_true", help="skip the MXFP4 variant run")
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
     ap.add_argument("--copy-probe", type=int, default=0, metavar="MIB",
                     help="only run a plain device copy of MIB MiB (HBM counter calibration)")
@@ -148,8 +166,13 @@ def main():
     M, K, N, r = wl.M, Lr.K, Lr.N, args.rank
     act_id = L.SVDQ_ACT_GELU_TANH if act == "gelu_tanh" else L.SVDQ_ACT_NONE
 
+    prec = args.precision
+
     def build_layer(rank):
-        prep = S.prepare_weights(Lr.weight_bits, wl.act_absmax(), rank=rank)
+        if prec == "mxfp4":
+            prep = S.prepare_weights_mxfp4(Lr.weight_bits, wl.act_absmax(), rank=rank)
+        else:
+            prep = S.prepare_weights(Lr.weight_bits, wl.act_absmax(), rank=rank)
         bias = None
         if Lr.bias_bits is not None:
             bias = torch.from_numpy(Lr.bias_bits.view(np.int16).copy()).view(torch.bfloat16)
@@ -159,7 +182,10 @@ def main():
 
     def run(lin, steps, warmup, events=False, unfused=False):
         xc = torch.empty((M, K // 2), dtype=torch.uint8, device="cuda")
-        xs = torch.empty((K // 64, M), dtype=torch.float16, device="cuda")
+        if lin.precision == "mxfp4":
+            xs = torch.empty((M, K // 32), dtype=torch.uint8, device="cuda")
+        else:
+            xs = torch.empty((K // 64, M), dtype=torch.float16, device="cuda")
         la = torch.empty((M, lin.rank), dtype=torch.float32, device="cuda") if lin.rank else None
         y = torch.empty((M, N), dtype=torch.bfloat16, device="cuda")
 
@@ -173,6 +199,14 @@ def main():
                                     M, N, K, 0, out=y)
                 S.lora_down(x, lin.smooth_inv, lin.lora_down, lin.rank, act=act_id, out=la)
                 S.lora_up_add(la, lin.lora_up, y)
+                return
+            if lin.precision == "mxfp4":
+                S.quant_act_lora_down_mxfp4(x, lin.smooth_inv, lin.lora_down, lin.rank, act=act_id,
+                                            out=(xc, xs, la))
+                if mid is not None:
+                    mid.record()
+                S.gemm_mxfp4_lora_up(xc, xs, lin.w_codes, lin.w_scales, la, lin.lora_up, lin.bias,
+                                     M, N, K, lin.rank, out=y)
                 return
             S.quant_act_lora_down(x, lin.smooth_inv, lin.lora_down, lin.rank, act=act_id, out=(xc, xs, la))
             if mid is not None:
@@ -200,15 +234,35 @@ def main():
             res["k2_ms"] = float(np.mean([e[1].elapsed_time(e[2]) for e in ev]))
         return res
 
-    lin = build_layer(r)
-    res = run(lin, args.steps, args.warmup, events=True)
-    ms_per_step = res["wall_s"] * 1e3 / args.steps
-    ops = 2.0 * M * N * K
-    value = ops / (ms_per_step * 1e-3) / 1e12
-    k2_tops = ops / (res["k2_ms"] * 1e-3) / 1e12
-    k1_gbs = k1_bytes(M, K, r) / (res["k1_ms"] * 1e-3) / 1e9
-    traffic = load_traffic(args.workload, r)
+    def measure(precision):
+        nonlocal prec
+        prec = precision
+        lin = build_layer(r)
+        res = run(lin, args.steps, args.warmup, events=True)
+        ms = res["wall_s"] * 1e3 / args.steps
+        ops = 2.0 * M * N * K
+        k2_rate = ops / (res["k2_ms"] * 1e-3) / 1e12
+        k1_gbs = k1_bytes(M, K, r, precision) / (res["k1_ms"] * 1e-3) / 1e9
+        peak, unit = (INT8_PEAK_TOPS, "TOPS") if precision == "int4" else (FP4_PEAK_TFLOPS, "TFLOP/s")
+        kname = "k_gemm_w4a4_lora_up" if precision == "int4" else "k_gemm_mxfp4_lora_up"
+        return lin, ms, {
+            "value": ops / (ms * 1e-3) / 1e12,
+            "roofline": {"bound": "mfma", "kernel": kname,
+                         "achieved": round(k2_rate, 2), "peak": peak, "unit": unit,
+                         "frac": round(k2_rate / peak, 4), "traffic": load_traffic(args.workload, r, precision),
+                         "avg_launch_us": round(res["k2_ms"] * 1e3, 2),
+                         "algorithmic_ops_per_launch": ops,
+                         "algorithmic_hbm_bytes_per_launch": k2_bytes(M, N, K, r, Lr.bias_bits is not None,
+                                                                      precision)},
+            "roofline_k1": {"bound": "hbm", "kernel": "k_quant_act_lora_down",
+                            "achieved": round(k1_gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                            "frac": round(k1_gbs / HBM_PEAK_GBS, 4),
+                            "avg_launch_us": round(res["k1_ms"] * 1e3, 2),
+                            "algorithmic_bytes_per_launch": k1_bytes(M, K, r, precision)},
+        }
 
+    lin, ms_per_step, main_m = measure(args.precision)
+    value = main_m["value"]
     out = {
         "metric": METRIC,
         "value": round(value, 2),
@@ -220,36 +274,35 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "int4",
+        "dtype": "int4" if args.precision == "int4" else "fp4 (mxfp4)",
         "data": "synthetic",
-        "config": {"workload": f"{desc}, rank {r}, group 64", "M": M, "K": K, "N": N, "rank": r,
-                   "group": 64, "bias": Lr.bias_bits is not None, "parallelism": "single GPU"},
+        "config": {"workload": f"{desc}, rank {r}, " + ("INT4 group 64" if args.precision == "int4"
+                                                        else "MXFP4 block 32"),
+                   "M": M, "K": K, "N": N, "rank": r, "precision": args.precision,
+                   "group": 64 if args.precision == "int4" else 32,
+                   "bias": Lr.bias_bits is not None, "parallelism": "single GPU"},
         "pct_int8_peak": round(100.0 * value / INT8_PEAK_TOPS, 2),
-        "roofline": {"bound": "mfma", "kernel": "k_gemm_w4a4_lora_up",
-                     "achieved": round(k2_tops, 2), "peak": INT8_PEAK_TOPS, "unit": "TOPS",
-                     "frac": round(k2_tops / INT8_PEAK_TOPS, 4), "traffic": traffic,
-                     "avg_launch_us": round(res["k2_ms"] * 1e3, 2),
-                     "algorithmic_ops_per_launch": ops},
-        "roofline_k1": {"bound": "hbm", "kernel": "k_quant_act_lora_down",
-                        "achieved": round(k1_gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                        "frac": round(k1_gbs / HBM_PEAK_GBS, 4),
-                        "avg_launch_us": round(res["k1_ms"] * 1e3, 2),
-                        "algorithmic_bytes_per_launch": k1_bytes(M, K, r)},
+        "roofline": main_m["roofline"],
+        "roofline_k1": main_m["roofline_k1"],
     }
     if not args.no_overhead and r > 0:
         lin0 = build_layer(0)
         res0 = run(lin0, args.steps, args.warmup, events=True)
         ms0 = res0["wall_s"] * 1e3 / args.steps
-        resu = run(lin, args.steps, args.warmup, unfused=True)
-        msu = resu["wall_s"] * 1e3 / args.steps
-        out["low_rank_overhead"] = {
-            "rank0_ms_per_step": round(ms0, 5),
-            "overhead_frac": round(ms_per_step / ms0 - 1.0, 4),
-            "unfused_ms_per_step": round(msu, 5),
-            "unfused_overhead_frac": round(msu / ms0 - 1.0, 4),
-            "context": "pages: an unfused rank-32 branch costs +57% latency (NVIDIA, model card)"}
+        ov = {"rank0_ms_per_step": round(ms0, 5), "overhead_frac": round(ms_per_step / ms0 - 1.0, 4)}
+        if args.precision == "int4":
+            resu = run(lin, args.steps, args.warmup, unfused=True)
+            msu = resu["wall_s"] * 1e3 / args.steps
+            ov.update(unfused_ms_per_step=round(msu, 5), unfused_overhead_frac=round(msu / ms0 - 1.0, 4))
+        ov["context"] = "pages: an unfused rank-32 branch costs +57% latency (NVIDIA, model card)"
+        out["low_rank_overhead"] = ov
+    if args.precision == "int4" and not args.no_variants:
+        _, ms_mx, mx_m = measure("mxfp4")
+        out["mxfp4_variant"] = {"value": round(mx_m["value"], 2), "unit": "TFLOP/s (effective, 2MNK)",
+                                "ms_per_step": round(ms_mx, 5), "roofline": mx_m["roofline"],
+                                "roofline_k1": mx_m["roofline_k1"]}
     if not args.no_cpu_baseline:
-        out["cpu_baseline"] = cpu_baseline(wl, layer, r, args.cpu_seconds)
+        out["cpu_baseline"] = cpu_baseline(wl, layer, r, args.cpu_seconds, args.precision)
     print(json.dumps(out))
 
 

@@ -11,19 +11,24 @@
 // and packed codes are MFMA operands as they sit in memory.
 //
 // k_gemm_mxfp4_lora_up: Y = MXFP4 product + bf16(lora_act) L2 + bias.
-//   Block tile 128 (m) x 256 (n), 4 waves in 2 x 2, wave tile 64 x 128 =
-//   2 x 4 MFMA tiles of 32 x 32, computed transposed (weight rows are the
-//   MFMA A operand, activation rows the B operand) so a lane ends with one
-//   output row and runs of four output columns.  The K loop runs in stages
-//   of 128 k (two MFMA k-steps of 64), loaded from HBM one stage ahead into
-//   registers and stored to a double-buffered LDS tile; each fragment is one
-//   16-byte LDS read.
+//   Block tile BM (m) x 256 (n) with BM / 32 waves, each owning 64 x 128
+//   outputs = 2 x 4 MFMA tiles of 32 x 32, computed transposed (weight rows
+//   are the MFMA A operand, activation rows the B operand) so a lane ends
+//   with one output row and runs of four output columns.  BM = 256 (8
+//   waves, one block per CU) for large M; BM = 128 (4 waves, two blocks per
+//   CU) when 256-row tiles would leave CUs idle.
+//   The K loop runs in stages of 128 k (two MFMA k-steps of 64).  Operands
+//   move from HBM straight into a ring of NS LDS stage buffers with LDS-DMA
+//   buffer loads (no registers involved), NS - 1 stages ahead of the stage
+//   being multiplied, so enough bytes are in flight to cover the memory
+//   latency; a stage is released by one barrier per stage.
 //
 // Operand layout of the 32x32x64 FP4 MFMA (wave64): lane l supplies row
 // l % 32 and the 32 k of block l / 32 (16 bytes, element j in nibble j, low
 // nibble first) together with that (row, block)'s E8M0 scale in its scale
 // register; C/D as for every 32x32 MFMA: lane l holds column l % 32, rows
-// 8b + 4(l / 32) + i in register 4b + i.
+// 8b + 4(l / 32) + i in register 4b + i.  An LDS-DMA load writes lane l's
+// bytes at the wave's LDS base + size * l.
 
 #include <hip/hip_runtime.h>
 #include <stdint.h>
@@ -34,110 +39,176 @@
 
 namespace {
 
-constexpr int MX_BM = 128;                   // block tile rows (m)
 constexpr int MX_BN = 256;                   // block tile columns (n)
 constexpr int MX_WM = 64;                    // wave tile rows
 constexpr int MX_WN = 128;                   // wave tile columns
 constexpr int MX_TI = MX_WM / 32;            // 32x32 tiles per wave along m
 constexpr int MX_TJ = MX_WN / 32;            // along n
 constexpr int MX_KS = 128;                   // k per stage
-constexpr int MX_THREADS = 256;
 
-// LDS: codes as four 16-byte chunks per row and stage (chunk c = k 32c ..
-// 32c + 31 of the stage = one MFMA block), chunk c of row r at position
-// c ^ (((r >> 1) ^ (r >> 3)) & 3) so that fragment reads and loader writes
-// spread over all banks; scales as one dword per row and stage (the four
-// E8M0 bytes of the stage's blocks).
-struct MxSmem {
-  uint4 a[2][MX_BM][4];
-  uint4 b[2][MX_BN][4];
-  uint32_t sa[2][MX_BM];
-  uint32_t sb[2][MX_BN];
+
+// Per-stage LDS layout (bytes): activation codes [BM rows][64], weight codes
+// [256 rows][64], activation scales [BM] dwords, weight scales [256] dwords,
+// one dummy dword row [64] for padding scale loads.  Codes: 16-byte chunk
+// c (= k 32c .. 32c + 31 of the stage, one MFMA block) of row r sits at
+// chunk c ^ (((r >> 1) ^ (r >> 3)) & 3), which spreads fragment reads over
+// all banks; the DMA loads apply that permutation on the global side.
+template <int BM>
+struct MxCfg {
+  static constexpr int WAVES = BM / 32;
+  static constexpr int THREADS = WAVES * 64;
+  static constexpr int NS = BM == 256 ? 4 : 3;                   // ring depth
+  static constexpr int A_BYTES = BM * 64;
+  static constexpr int B_BYTES = MX_BN * 64;
+  static constexpr int SA_OFF = A_BYTES + B_BYTES;
+  static constexpr int SB_OFF = SA_OFF + BM * 4;
+  static constexpr int DUMMY_OFF = SB_OFF + MX_BN * 4;
+  static constexpr int STAGE_BYTES = DUMMY_OFF + 256;
+  static constexpr int A_INSTR = BM / 16 / WAVES;                // 1 KB code loads per wave
+  static constexpr int B_INSTR = MX_BN / 16 / WAVES;
+  static constexpr int S_TOTAL = BM / 64 + MX_BN / 64;           // 256-byte scale loads
+  static constexpr int S_INSTR = (S_TOTAL + WAVES - 1) / WAVES;
+  static constexpr int P = A_INSTR + B_INSTR + S_INSTR;          // DMA loads per wave per stage
+  static constexpr size_t SMEM_MAIN = static_cast<size_t>(NS) * STAGE_BYTES;
+  static constexpr size_t SMEM_EPI = static_cast<size_t>(WAVES) * MX_WM * MX_WN * 2;
+  static_assert(SMEM_EPI <= SMEM_MAIN, "the output tiles reuse the stage ring");
 };
-constexpr size_t MX_SMEM_MAIN = sizeof(MxSmem);
-constexpr size_t MX_SMEM_EPI = static_cast<size_t>(4) * MX_WM * MX_WN * 2;   // bf16 output tiles
-constexpr size_t MX_SMEM = MX_SMEM_MAIN > MX_SMEM_EPI ? MX_SMEM_MAIN : MX_SMEM_EPI;
 
 __device__ __forceinline__ int mx_swz(int row, int chunk) { return chunk ^ (((row >> 1) ^ (row >> 3)) & 3); }
 
-template <int OUT_F32, int HAS_RANK>
-__global__ __launch_bounds__(MX_THREADS, 2) void k_gemm_mxfp4_lora_up(
+// Buffer descriptor (raw, stride 0) in four scalar registers: byte base,
+// size in bytes (accesses at or past it read zeros), default format word.
+struct MxRsrc {
+  v4i w;
+};
+__device__ __forceinline__ MxRsrc mx_rsrc(const void* base, uint32_t bytes) {
+  const uint64_t a = reinterpret_cast<uint64_t>(base);
+  MxRsrc r;
+  r.w[0] = __builtin_amdgcn_readfirstlane(static_cast<int>(a & 0xFFFFFFFFu));
+  r.w[1] = __builtin_amdgcn_readfirstlane(static_cast<int>((a >> 32) & 0xFFFFu));
+  r.w[2] = __builtin_amdgcn_readfirstlane(static_cast<int>(bytes));
+  r.w[3] = 0x00020000;
+  return r;
+}
+
+// LDS-DMA buffer loads: lane l's `size` bytes at byte offset voff of the
+// buffer land at LDS address lds_addr + size * l.  Issued from inline
+// assembly so that the compiler does not treat the pending LDS writes as
+// aliasing every later LDS read (it would wait for all of them); the kernel
+// waits for them itself with s_waitcnt vmcnt before the barrier that
+// publishes a stage.  s_nop 4 covers the wait states after M0 and scalar
+// register writes that a buffer load reading them needs.  No register is
+// written, so nothing stays in flight towards a register.
+__device__ __forceinline__ void mx_dma16(const MxRsrc& r, uint32_t lds_addr, uint32_t voff) {
+  asm volatile("s_mov_b32 m0, %0\n\ts_nop 4\n\tbuffer_load_dwordx4 %1, %2, 0 offen lds"
+               :: "s"(lds_addr), "v"(voff), "s"(r.w) : "memory", "m0");
+}
+__device__ __forceinline__ void mx_dma4(const MxRsrc& r, uint32_t lds_addr, uint32_t voff) {
+  asm volatile("s_mov_b32 m0, %0\n\ts_nop 4\n\tbuffer_load_dword %1, %2, 0 offen lds"
+               :: "s"(lds_addr), "v"(voff), "s"(r.w) : "memory", "m0");
+}
+
+// s_waitcnt immediate: vmcnt = v (0..63), expcnt and lgkmcnt = 0.
+constexpr int waitcnt_vm_lgkm0(int v) { return (v & 0xF) | ((v >> 4) << 14) | (0x0 << 4) | (0x0 << 8); }
+
+template <int OUT_F32, int HAS_RANK, int BM>
+__global__ __launch_bounds__(MxCfg<BM>::THREADS, BM == 256 ? 1 : 2) void k_gemm_mxfp4_lora_up(
     const uint8_t* __restrict__ x_codes, const uint8_t* __restrict__ x_scales,
     const uint8_t* __restrict__ w_codes, const uint8_t* __restrict__ w_scales,
     const float* __restrict__ lora_act, const uint16_t* __restrict__ lora_up,
     const uint16_t* __restrict__ bias, int M, int N, int K, int rank, void* __restrict__ y) {
-  extern __shared__ __align__(16) unsigned char mx_smem_raw[];
-  MxSmem& sm = *reinterpret_cast<MxSmem*>(mx_smem_raw);
+  using C = MxCfg<BM>;
+  // A statically sized ring (not dynamic LDS): with the slot as the first
+  // index the compiler can prove that different slots do not overlap.
+  __shared__ __align__(16) unsigned char ring[C::NS][C::STAGE_BYTES];
+  unsigned char* const mx_smem_raw = &ring[0][0];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int wm = wave >> 1, wn = wave & 1;
-  const int nM = (M + MX_BM - 1) / MX_BM, nN = (N + MX_BN - 1) / MX_BN;
+  const int nM = (M + BM - 1) / BM, nN = (N + MX_BN - 1) / MX_BN;
   int tm, tn;
   xcd_tile(nM, nN, tm, tn);
-  const int m0 = tm * MX_BM, n0 = tn * MX_BN;
+  const int m0 = tm * BM, n0 = tn * MX_BN;
   const int S = K / MX_KS;
   const uint32_t Kb = static_cast<uint32_t>(K) / 2;     // code bytes per row
   const uint32_t Ks = static_cast<uint32_t>(K) / 32;    // scale bytes per row
-
-  // Loader roles: thread t moves 16-byte chunk (t & 3) of activation rows
-  // (t >> 2) + 64 i (i < 2) and of weight rows (t >> 2) + 64 i (i < 4), the
-  // scale dword of weight row t and, for t < 128, of activation row t.
-  // Buffer resources sized to each operand turn rows past M or N into zeros.
-  const __amdgpu_buffer_rsrc_t a_rs = __builtin_amdgcn_make_buffer_rsrc(
-      const_cast<uint8_t*>(x_codes), 0, static_cast<int>(static_cast<size_t>(M) * Kb), 0x00020000);
-  const __amdgpu_buffer_rsrc_t b_rs = __builtin_amdgcn_make_buffer_rsrc(
-      const_cast<uint8_t*>(w_codes), 0, static_cast<int>(static_cast<size_t>(N) * Kb), 0x00020000);
-  const __amdgpu_buffer_rsrc_t sa_rs = __builtin_amdgcn_make_buffer_rsrc(
-      const_cast<uint8_t*>(x_scales), 0, static_cast<int>(static_cast<size_t>(M) * Ks), 0x00020000);
-  const __amdgpu_buffer_rsrc_t sb_rs = __builtin_amdgcn_make_buffer_rsrc(
-      const_cast<uint8_t*>(w_scales), 0, static_cast<int>(static_cast<size_t>(N) * Ks), 0x00020000);
-  const int l_r = tid >> 2, l_c = tid & 3;
   constexpr uint32_t OOB = 0x80000000u;
-  uint32_t a_off[2], b_off[4];
-#pragma unroll
-  for (int i = 0; i < 2; ++i) {
-    const int r = m0 + l_r + 64 * i;
-    a_off[i] = r < M ? static_cast<uint32_t>(r) * Kb + 16u * l_c : OOB;
-  }
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const int r = n0 + l_r + 64 * i;
-    b_off[i] = r < N ? static_cast<uint32_t>(r) * Kb + 16u * l_c : OOB;
-  }
-  const uint32_t sa_off = (tid < MX_BM && m0 + tid < M) ? static_cast<uint32_t>(m0 + tid) * Ks : OOB;
-  const uint32_t sb_off = (n0 + tid < N) ? static_cast<uint32_t>(n0 + tid) * Ks : OOB;
 
-  uint4 ra[2], rb[4];
-  uint32_t rsa, rsb;
-  auto load_stage = [&](int st) {
+  const MxRsrc a_rs = mx_rsrc(x_codes, static_cast<uint32_t>(static_cast<size_t>(M) * Kb));
+  const MxRsrc b_rs = mx_rsrc(w_codes, static_cast<uint32_t>(static_cast<size_t>(N) * Kb));
+  const MxRsrc sa_rs = mx_rsrc(x_scales, static_cast<uint32_t>(static_cast<size_t>(M) * Ks));
+  const MxRsrc sb_rs = mx_rsrc(w_scales, static_cast<uint32_t>(static_cast<size_t>(N) * Ks));
+
+  // DMA roles.  Code load i of this wave covers 16 rows (1 KB): lane l
+  // fetches row 16q + l / 4, chunk (l & 3) ^ swz(row), landing in slot l & 3.
+  // Scale load j (of the stage's BM / 64 + 4) covers 64 rows of one operand.
+  uint32_t a_off[C::A_INSTR], b_off[C::B_INSTR], s_off[C::S_INSTR];
+#pragma unroll
+  for (int i = 0; i < C::A_INSTR; ++i) {
+    const int q = wave * C::A_INSTR + i;
+    const int r = 16 * q + (lane >> 2);
+    const int c = (lane & 3) ^ (((r >> 1) ^ (r >> 3)) & 3);
+    a_off[i] = (m0 + r < M) ? static_cast<uint32_t>(m0 + r) * Kb + 16u * c : OOB;
+  }
+#pragma unroll
+  for (int i = 0; i < C::B_INSTR; ++i) {
+    const int q = wave * C::B_INSTR + i;
+    const int r = 16 * q + (lane >> 2);
+    const int c = (lane & 3) ^ (((r >> 1) ^ (r >> 3)) & 3);
+    b_off[i] = (n0 + r < N) ? static_cast<uint32_t>(n0 + r) * Kb + 16u * c : OOB;
+  }
+  bool s_is_a[C::S_INSTR];
+  int s_lds[C::S_INSTR];
+#pragma unroll
+  for (int i = 0; i < C::S_INSTR; ++i) {
+    const int j = wave * C::S_INSTR + i;            // wave-uniform
+    if (j < BM / 64) {
+      const int r = 64 * j + lane;
+      s_is_a[i] = true;
+      s_off[i] = (m0 + r < M) ? static_cast<uint32_t>(m0 + r) * Ks : OOB;
+      s_lds[i] = C::SA_OFF + 256 * j;
+    } else if (j < C::S_TOTAL) {
+      const int r = 64 * (j - BM / 64) + lane;
+      s_is_a[i] = false;
+      s_off[i] = (n0 + r < N) ? static_cast<uint32_t>(n0 + r) * Ks : OOB;
+      s_lds[i] = C::SB_OFF + 256 * (j - BM / 64);
+    } else {                                        // padding: keeps every wave's count equal
+      s_is_a[i] = true;
+      s_off[i] = OOB;
+      s_lds[i] = C::DUMMY_OFF;
+    }
+  }
+
+  // LDS byte addresses (wave-uniform) of this wave's DMA targets in slot 0.
+  const uint32_t ring0 = static_cast<uint32_t>(reinterpret_cast<uintptr_t>(&ring[0][0]));
+  uint32_t a_lds[C::A_INSTR], b_lds[C::B_INSTR], s_lds_a[C::S_INSTR];
+#pragma unroll
+  for (int i = 0; i < C::A_INSTR; ++i)
+    a_lds[i] = __builtin_amdgcn_readfirstlane(ring0 + 1024 * (wave * C::A_INSTR + i));
+#pragma unroll
+  for (int i = 0; i < C::B_INSTR; ++i)
+    b_lds[i] = __builtin_amdgcn_readfirstlane(ring0 + C::A_BYTES + 1024 * (wave * C::B_INSTR + i));
+#pragma unroll
+  for (int i = 0; i < C::S_INSTR; ++i) s_lds_a[i] = __builtin_amdgcn_readfirstlane(ring0 + s_lds[i]);
+
+  // Issue the DMA loads of stage st into ring slot `slot` = st % NS (zeros
+  // past K).
+  auto issue_stage = [&](int st, int slot) {
+    const uint32_t so_lds = static_cast<uint32_t>(slot) * C::STAGE_BYTES;
+    const bool live = st < S;
     const uint32_t ko = static_cast<uint32_t>(st) * (MX_KS / 2);
     const uint32_t so = static_cast<uint32_t>(st) * (MX_KS / 32);
 #pragma unroll
-    for (int i = 0; i < 2; ++i)
-      ra[i] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(
-                                            a_rs, a_off[i] == OOB ? OOB : a_off[i] + ko, 0, 0));
+    for (int i = 0; i < C::A_INSTR; ++i)
+      mx_dma16(a_rs, a_lds[i] + so_lds, (live && a_off[i] != OOB) ? a_off[i] + ko : OOB);
 #pragma unroll
-    for (int i = 0; i < 4; ++i)
-      rb[i] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(
-                                            b_rs, b_off[i] == OOB ? OOB : b_off[i] + ko, 0, 0));
-    rsa = __builtin_amdgcn_raw_buffer_load_b32(sa_rs, sa_off == OOB ? OOB : sa_off + so, 0, 0);
-    rsb = __builtin_amdgcn_raw_buffer_load_b32(sb_rs, sb_off == OOB ? OOB : sb_off + so, 0, 0);
-  };
-  auto store_stage = [&](int buf) {
+    for (int i = 0; i < C::B_INSTR; ++i)
+      mx_dma16(b_rs, b_lds[i] + so_lds, (live && b_off[i] != OOB) ? b_off[i] + ko : OOB);
 #pragma unroll
-    for (int i = 0; i < 2; ++i) {
-      const int r = l_r + 64 * i;
-      sm.a[buf][r][mx_swz(r, l_c)] = ra[i];
-    }
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int r = l_r + 64 * i;
-      sm.b[buf][r][mx_swz(r, l_c)] = rb[i];
-    }
-    if (tid < MX_BM) sm.sa[buf][tid] = rsa;
-    sm.sb[buf][tid] = rsb;
+    for (int i = 0; i < C::S_INSTR; ++i)
+      mx_dma4(s_is_a[i] ? sa_rs : sb_rs, s_lds_a[i] + so_lds, (live && s_off[i] != OOB) ? s_off[i] + so : OOB);
   };
 
   v16f acc[MX_TI][MX_TJ];
@@ -151,53 +222,67 @@ __global__ __launch_bounds__(MX_THREADS, 2) void k_gemm_mxfp4_lora_up(
   const int fr = lane & 31;      // fragment row within a 32-row tile
   const int fk = lane >> 5;      // which 32-k block of the k-step
 
-  load_stage(0);
-  store_stage(0);
-  __syncthreads();
+#pragma unroll
+  for (int st = 0; st < C::NS - 1; ++st) issue_stage(st, st);
 
-  for (int st = 0; st < S; ++st) {
-    const int buf = st & 1;
-    const bool more = (st + 1) < S;
-    if (more) load_stage(st + 1);
+  for (int st0 = 0; st0 < S; st0 += C::NS) {
+#pragma unroll
+    for (int u = 0; u < C::NS; ++u) {
+      const int st = st0 + u;
+      if (st >= S) break;
+      // stage st has landed once at most (NS - 2) stages of this wave's
+      // loads are outstanding; every wave waits for its own loads, then the
+      // barrier makes all of them visible and frees slot (st - 1) % NS, which
+      // this wave's finished reads of the previous stage no longer need.
+      __builtin_amdgcn_s_waitcnt(waitcnt_vm_lgkm0(C::P * (C::NS - 2)));
+      __builtin_amdgcn_s_barrier();
+      asm volatile("" ::: "memory");
+      issue_stage(st + C::NS - 1, (u + C::NS - 1) % C::NS);
 
-    uint32_t sxw[MX_TI], sww[MX_TJ];
+      const unsigned char* base = ring[u];
+      const uint4* sa4 = reinterpret_cast<const uint4*>(base);
+      const uint4* sb4 = reinterpret_cast<const uint4*>(base + C::A_BYTES);
+      const uint32_t* sas = reinterpret_cast<const uint32_t*>(base + C::SA_OFF);
+      const uint32_t* sbs = reinterpret_cast<const uint32_t*>(base + C::SB_OFF);
+      uint32_t sxw[MX_TI], sww[MX_TJ];
 #pragma unroll
-    for (int i = 0; i < MX_TI; ++i) sxw[i] = sm.sa[buf][wm * MX_WM + i * 32 + fr];
+      for (int i = 0; i < MX_TI; ++i) sxw[i] = sas[wm * MX_WM + i * 32 + fr];
 #pragma unroll
-    for (int j = 0; j < MX_TJ; ++j) sww[j] = sm.sb[buf][wn * MX_WN + j * 32 + fr];
+      for (int j = 0; j < MX_TJ; ++j) sww[j] = sbs[wn * MX_WN + j * 32 + fr];
 #pragma unroll
-    for (int ks = 0; ks < MX_KS / 64; ++ks) {
-      const int chunk = 2 * ks + fk;
-      v8i xf[MX_TI], wf[MX_TJ];
+      for (int ks = 0; ks < MX_KS / 64; ++ks) {
+        const int chunk = 2 * ks + fk;
+        v8i xf[MX_TI], wf[MX_TJ];
 #pragma unroll
-      for (int i = 0; i < MX_TI; ++i) {
-        const int r = wm * MX_WM + i * 32 + fr;
-        const uint4 u = sm.a[buf][r][mx_swz(r, chunk)];
-        xf[i] = v8i{static_cast<int>(u.x), static_cast<int>(u.y), static_cast<int>(u.z), static_cast<int>(u.w),
-                    0, 0, 0, 0};
-      }
-#pragma unroll
-      for (int j = 0; j < MX_TJ; ++j) {
-        const int c = wn * MX_WN + j * 32 + fr;
-        const uint4 u = sm.b[buf][c][mx_swz(c, chunk)];
-        wf[j] = v8i{static_cast<int>(u.x), static_cast<int>(u.y), static_cast<int>(u.z), static_cast<int>(u.w),
-                    0, 0, 0, 0};
-      }
-#pragma unroll
-      for (int i = 0; i < MX_TI; ++i) {
-        const int sx = static_cast<int>(__builtin_amdgcn_ubfe(sxw[i], 8 * chunk, 8));
+        for (int i = 0; i < MX_TI; ++i) {
+          const int r = wm * MX_WM + i * 32 + fr;
+          const uint4 v = sa4[r * 4 + mx_swz(r, chunk)];
+          xf[i] = v8i{static_cast<int>(v.x), static_cast<int>(v.y), static_cast<int>(v.z), static_cast<int>(v.w),
+                      0, 0, 0, 0};
+        }
 #pragma unroll
         for (int j = 0; j < MX_TJ; ++j) {
-          const int sw = static_cast<int>(__builtin_amdgcn_ubfe(sww[j], 8 * chunk, 8));
-          // cbsz = blgp = 4: both operands FP4 E2M1
-          acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(wf[j], xf[i], acc[i][j], 4, 4, 0, sw, 0, sx);
+          const int c = wn * MX_WN + j * 32 + fr;
+          const uint4 v = sb4[c * 4 + mx_swz(c, chunk)];
+          wf[j] = v8i{static_cast<int>(v.x), static_cast<int>(v.y), static_cast<int>(v.z), static_cast<int>(v.w),
+                      0, 0, 0, 0};
+        }
+#pragma unroll
+        for (int i = 0; i < MX_TI; ++i) {
+          const int sx = static_cast<int>(__builtin_amdgcn_ubfe(sxw[i], 8 * chunk, 8));
+#pragma unroll
+          for (int j = 0; j < MX_TJ; ++j) {
+            const int sw = static_cast<int>(__builtin_amdgcn_ubfe(sww[j], 8 * chunk, 8));
+            // cbsz = blgp = 4: both operands FP4 E2M1
+            acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(wf[j], xf[i], acc[i][j], 4, 4, 0, sw, 0, sx);
+          }
         }
       }
     }
-
-    if (more) store_stage(buf ^ 1);
-    __syncthreads();
   }
+  // drain the padding loads issued past the last stage before LDS is reused
+  __builtin_amdgcn_s_waitcnt(waitcnt_vm_lgkm0(0));
+  __syncthreads();
 
   // ---- epilogue: up projection on bf16 MFMA 32x32x16 (K = rank in slices
   // of 16), transposed like the main product.
@@ -306,22 +391,31 @@ __global__ __launch_bounds__(MX_THREADS, 2) void k_gemm_mxfp4_lora_up(
   }
 }
 
-template <int OUT_F32, int HAS_RANK>
+template <int OUT_F32, int HAS_RANK, int BM>
 int launch_mx_kernel(const void* x_codes, const void* x_scales, const void* w_codes, const void* w_scales,
                      const float* lora_act, const void* lora_up, const void* bias, int M, int N, int K,
                      int rank, void* y, hipStream_t st) {
-  auto kern = k_gemm_mxfp4_lora_up<OUT_F32, HAS_RANK>;
-  static const bool attr_ok = [&] {
-    return hipFuncSetAttribute(reinterpret_cast<const void*>(kern), hipFuncAttributeMaxDynamicSharedMemorySize,
-                               static_cast<int>(MX_SMEM)) == hipSuccess;
-  }();
-  if (!attr_ok) return SVDQ_ERR_HIP;
-  const int nb = ((M + MX_BM - 1) / MX_BM) * ((N + MX_BN - 1) / MX_BN);
-  hipLaunchKernelGGL(kern, dim3(nb), dim3(MX_THREADS), MX_SMEM, st, static_cast<const uint8_t*>(x_codes),
+  using C = MxCfg<BM>;
+  auto kern = k_gemm_mxfp4_lora_up<OUT_F32, HAS_RANK, BM>;
+  const int nb = ((M + BM - 1) / BM) * ((N + MX_BN - 1) / MX_BN);
+  hipLaunchKernelGGL(kern, dim3(nb), dim3(C::THREADS), 0, st, static_cast<const uint8_t*>(x_codes),
                      static_cast<const uint8_t*>(x_scales), static_cast<const uint8_t*>(w_codes),
                      static_cast<const uint8_t*>(w_scales), lora_act, static_cast<const uint16_t*>(lora_up),
                      static_cast<const uint16_t*>(bias), M, N, K, rank, y);
   return hipGetLastError() == hipSuccess ? SVDQ_OK : SVDQ_ERR_HIP;
+}
+
+template <int OUT_F32, int HAS_RANK>
+int launch_mx(const void* x_codes, const void* x_scales, const void* w_codes, const void* w_scales,
+              const float* lora_act, const void* lora_up, const void* bias, int M, int N, int K, int rank,
+              void* y, hipStream_t st) {
+  // 256-row tiles when they still give every CU at least one block
+  const long nb256 = static_cast<long>((M + 255) / 256) * ((N + MX_BN - 1) / MX_BN);
+  if (nb256 >= 256)
+    return launch_mx_kernel<OUT_F32, HAS_RANK, 256>(x_codes, x_scales, w_codes, w_scales, lora_act, lora_up, bias,
+                                                     M, N, K, rank, y, st);
+  return launch_mx_kernel<OUT_F32, HAS_RANK, 128>(x_codes, x_scales, w_codes, w_scales, lora_act, lora_up, bias,
+                                                   M, N, K, rank, y, st);
 }
 
 }  // namespace
@@ -335,12 +429,12 @@ int launch_gemm_mxfp4_lora_up(const void* x_codes, const void* x_scales, const v
   hipStream_t st = static_cast<hipStream_t>(stream);
   if (out_dtype == SVDQ_OUT_F32) {
     if (rank > 0)
-      return launch_mx_kernel<1, 1>(x_codes, x_scales, w_codes, w_scales, lora_act, lora_up, bias, M, N, K, rank, y, st);
-    return launch_mx_kernel<1, 0>(x_codes, x_scales, w_codes, w_scales, lora_act, lora_up, bias, M, N, K, rank, y, st);
+      return launch_mx<1, 1>(x_codes, x_scales, w_codes, w_scales, lora_act, lora_up, bias, M, N, K, rank, y, st);
+    return launch_mx<1, 0>(x_codes, x_scales, w_codes, w_scales, lora_act, lora_up, bias, M, N, K, rank, y, st);
   }
   if (rank > 0)
-    return launch_mx_kernel<0, 1>(x_codes, x_scales, w_codes, w_scales, lora_act, lora_up, bias, M, N, K, rank, y, st);
-  return launch_mx_kernel<0, 0>(x_codes, x_scales, w_codes, w_scales, lora_act, lora_up, bias, M, N, K, rank, y, st);
+    return launch_mx<0, 1>(x_codes, x_scales, w_codes, w_scales, lora_act, lora_up, bias, M, N, K, rank, y, st);
+  return launch_mx<0, 0>(x_codes, x_scales, w_codes, w_scales, lora_act, lora_up, bias, M, N, K, rank, y, st);
 }
 
 }  // namespace svdq
