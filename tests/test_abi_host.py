@@ -113,7 +113,9 @@ r2 = L.lib().svdq_gemm_w4a4_lora_up(p[0], p[1], p[2], p[3], p[4], p[5], None, 16
 r3 = L.lib().svdq_device_check(0)
 r4 = L.lib().svdq_lora_down(p[0], p[1], p[2], 16, 128, 32, 64, 0, p[3], None)
 r5 = L.lib().svdq_lora_up_add(p[0], p[1], 16, 128, 16, p[2], None)
-print(r1, r2, r3, r4, r5)
+r6 = L.lib().svdq_quant_act_lora_down_mxfp4(p[0], p[1], p[2], 16, 128, 32, 0, p[3], p[4], p[5], None)
+r7 = L.lib().svdq_gemm_mxfp4_lora_up(p[0], p[1], p[2], p[3], p[4], p[5], None, 16, 64, 128, 16, 0, p[6], None)
+print(r1, r2, r3, r4, r5, r6, r7)
 """
 
 
@@ -125,7 +127,7 @@ def test_unsupported_device_is_refused():
     r = subprocess.run([sys.executable, "-c", REFUSAL_SCRIPT.format(root=ROOT)], env=env,
                        capture_output=True, text=True, timeout=120)
     assert r.returncode == 0, r.stderr
-    assert r.stdout.split() == [str(L.SVDQ_ERR_UNSUPPORTED_DEVICE)] * 5
+    assert r.stdout.split() == [str(L.SVDQ_ERR_UNSUPPORTED_DEVICE)] * 7
 
 
 # ------------------------------------------------------------ host preparation
