@@ -46,6 +46,14 @@ Readings where the pages are silent (each also listed in the design doc):
   R8  Output Y = bf16(acc + bf16(lora_act) L2 + bias), round to nearest even.
   R9  Optional tanh-GELU (textbook tanh form) on the bf16 input of the
       quantizer, in fp32, before smoothing (MLP pair chain).
+  R11 Fused QKV operator (the Diffusers page, "Quantizing models with
+      structural rewrites": the fused operator consumes the QKV projection,
+      the Q/K normalization and the rotary embeddings together): the
+      projection's output is [Q | K | V] along N, each H heads of 128; Q and K
+      heads get RMSNorm over the head (eps 1e-6, a learnable weight per
+      element) and then the rotary embedding on adjacent pairs (2i, 2i+1)
+      with per-token angle tables; V is left as projected.  Both act on the
+      fp32 projection before the single bf16 rounding of the output.
   R10 The unfused comparison path (``forward_unfused``) stores the 4-bit
       GEMM's output plus bias as bf16 before the up projection adds to it,
       and rounds to bf16 again: the 16-bit output is written twice.
@@ -64,6 +72,7 @@ __all__ = [
     "quantize_weight_residual", "prepare", "gelu_tanh", "quantize_activation",
     "pack_int4", "unpack_int4", "lora_down", "w4a4_product",
     "w4a4_product_bruteforce", "forward", "forward_unfused", "reference_fp64", "rel_fro",
+    "rms_norm", "rope", "forward_qkv",
     "prepared_bytes",
 ]
 
@@ -370,6 +379,47 @@ def forward_unfused(x, prep, bias=None, act: str = "none", semantics: str = "gpu
         return y0
     la = lora_down(x_hat, prep["L1"])
     return bf16(y0 + bf16(la) @ prep["L2"])
+
+
+def rms_norm(v, g, eps: float = 1e-6) -> np.ndarray:
+    """RMSNorm over the last axis: v / sqrt(mean(v^2) + eps) * g (fp64)."""
+    v = np.asarray(v, dtype=np.float64)
+    return v / np.sqrt(np.mean(v * v, axis=-1, keepdims=True) + eps) * np.asarray(g, dtype=np.float64)
+
+
+def rope(v, cos, sin) -> np.ndarray:
+    """Rotary embedding on adjacent pairs of the last axis: pair i of a row
+    turns by the angle whose cosine and sine are cos[row, i], sin[row, i].
+    v: [M, H, D]; cos, sin: [M, D/2] (shared by the heads)."""
+    v = np.asarray(v, dtype=np.float64)
+    c = np.asarray(cos, dtype=np.float64)[:, None, :]
+    s = np.asarray(sin, dtype=np.float64)[:, None, :]
+    v0, v1 = v[..., 0::2], v[..., 1::2]
+    out = np.empty_like(v)
+    out[..., 0::2] = v0 * c - v1 * s
+    out[..., 1::2] = v1 * c + v0 * s
+    return out
+
+
+def forward_qkv(x, prep, bias, norm_q, norm_k, cos=None, sin=None, eps: float = 1e-6,
+                head_dim: int = 128, act: str = "none", out: str = "bf16") -> np.ndarray:
+    """The fused QKV operator (reading R11): projection (as ``forward``, kept
+    in fp64), per-head RMSNorm of Q and K, rotary embedding of Q and K, one
+    rounding of the whole [M][3 H D] output."""
+    y = forward(x, prep, bias=bias, act=act, out="f64")
+    M, N = y.shape
+    if N % (3 * head_dim):
+        raise ValueError("N must be 3 * heads * head_dim")
+    HD = N // 3
+    H = HD // head_dim
+    res = y.copy()
+    for part, g in ((0, norm_q), (1, norm_k)):
+        t = y[:, part * HD:(part + 1) * HD].reshape(M, H, head_dim)
+        t = rms_norm(t, g, eps)
+        if cos is not None:
+            t = rope(t, cos, sin)
+        res[:, part * HD:(part + 1) * HD] = t.reshape(M, HD)
+    return {"bf16": bf16, "f32": fp32, "f64": lambda v: v}[out](res)
 
 
 def reference_fp64(x, weight_nk, bias=None, act: str = "none") -> np.ndarray:

@@ -333,3 +333,53 @@ def test_unfused_within_two_roundings_of_exact():
     assert np.any(un != O.forward(wl.x, p, bias=L.bias))  # the extra rounding shows
     p0 = O.prepare(L.weight, wl.act_absmax(), rank=0)
     np.testing.assert_array_equal(O.forward_unfused(wl.x, p0, bias=L.bias), O.forward(wl.x, p0, bias=L.bias))
+
+
+# ---------------------------------------------------------------- fused QKV epilogue
+def test_rms_norm_matches_torch_and_closed_form():
+    rng = np.random.default_rng(28)
+    v = rng.standard_normal((5, 3, 128)) * 3
+    g = 1 + 0.1 * rng.standard_normal(128)
+    ref = torch.nn.functional.rms_norm(torch.from_numpy(v), (128,), torch.from_numpy(g), eps=1e-6).numpy()
+    np.testing.assert_allclose(O.rms_norm(v, g, 1e-6), ref, rtol=1e-13, atol=1e-13)
+    # hand-worked: a head of all 2s has rms 2 and normalizes to g (eps 0)
+    np.testing.assert_allclose(O.rms_norm(np.full(128, 2.0), g, 0.0), g, rtol=1e-15)
+    # scale invariance
+    np.testing.assert_allclose(O.rms_norm(7 * v, g, 0.0), O.rms_norm(v, g, 0.0), rtol=1e-13)
+
+
+def test_rope_is_complex_rotation():
+    rng = np.random.default_rng(29)
+    M, H, D = 6, 2, 128
+    v = rng.standard_normal((M, H, D))
+    ang = rng.uniform(-np.pi, np.pi, (M, D // 2))
+    out = O.rope(v, np.cos(ang), np.sin(ang))
+    z = (v[..., 0::2] + 1j * v[..., 1::2]) * np.exp(1j * ang)[:, None, :]
+    np.testing.assert_allclose(out[..., 0::2], z.real, rtol=1e-13, atol=1e-13)
+    np.testing.assert_allclose(out[..., 1::2], z.imag, rtol=1e-13, atol=1e-13)
+    # quarter turn maps (a, b) to (-b, a); pair norms are preserved
+    q = O.rope(v, np.zeros((M, D // 2)), np.ones((M, D // 2)))
+    np.testing.assert_array_equal(q[..., 0::2], -v[..., 1::2])
+    np.testing.assert_array_equal(q[..., 1::2], v[..., 0::2])
+    np.testing.assert_allclose(np.hypot(out[..., 0::2], out[..., 1::2]), np.hypot(v[..., 0::2], v[..., 1::2]),
+                               rtol=1e-13)
+
+
+def test_forward_qkv_composition():
+    """V columns are the plain projection bit for bit; with unit norm weights
+    and zero angles, Q and K heads have unit RMS before rounding."""
+    wl = workloads.custom_workload(40, 256, 768, seed=30, n_out=3, bias=True)
+    L = wl.layers[0]
+    p = O.prepare(L.weight, wl.act_absmax(), rank=16)
+    ones = np.ones(128)
+    cos = np.ones((40, 64))
+    sin = np.zeros((40, 64))
+    Y = O.forward_qkv(wl.x, p, L.bias, ones, ones, cos, sin, out="f64")
+    plain = O.forward(wl.x, p, bias=L.bias, out="f64")
+    np.testing.assert_array_equal(Y[:, 512:], plain[:, 512:])
+    heads = Y[:, :512].reshape(40, 4, 128)
+    np.testing.assert_allclose(np.sqrt(np.mean(heads ** 2, axis=-1)), 1.0, rtol=1e-5)  # eps = 1e-6
+    # rotating then normalizing equals normalizing then rotating (rotation keeps the RMS)
+    ang = np.random.default_rng(31).uniform(0, 6, (40, 64))
+    Yr = O.forward_qkv(wl.x, p, L.bias, ones, ones, np.cos(ang), np.sin(ang), out="f64")
+    np.testing.assert_allclose(np.sqrt(np.mean(Yr[:, :512].reshape(40, 4, 128) ** 2, axis=-1)), 1.0, rtol=1e-5)

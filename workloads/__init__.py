@@ -177,3 +177,41 @@ def make_workload(name: str, M: Optional[int] = None) -> Workload:
             kw["text_rows"] = max(1, M * kw["text_rows"] // kw["M"])
         kw["M"] = M
     return custom_workload(name=name, **kw)
+
+
+# --------------------------------------------------------------------------
+# Inputs of the fused QKV epilogue (per-head Q/K RMSNorm + rotary embedding)
+# --------------------------------------------------------------------------
+def rope_tables(text_rows: int, image_side: int, head_dim: int = 128, theta: float = 10000.0,
+                axes=(16, 56, 56)):
+    """cos / sin tables [M][head_dim/2] (float32) with FLUX's layout of
+    positions: text tokens at (0, 0, 0), image tokens at (0, h, w) on an
+    image_side x image_side grid; the head dimension is split over three
+    position axes of widths ``axes`` and pair j of an axis of width d turns by
+    pos * theta^(-2j/d).  These are input data of the operator (the model
+    computes them), drawn here with the FLUX-style structure."""
+    assert sum(axes) == head_dim
+    M = text_rows + image_side * image_side
+    pos = np.zeros((M, 3))
+    hh, ww = np.meshgrid(np.arange(image_side), np.arange(image_side), indexing="ij")
+    pos[text_rows:, 1] = hh.reshape(-1)
+    pos[text_rows:, 2] = ww.reshape(-1)
+    angles = []
+    for a, d in enumerate(axes):
+        j = np.arange(d // 2)
+        omega = theta ** (-2.0 * j / d)
+        angles.append(pos[:, a:a + 1] * omega[None, :])
+    ang = np.concatenate(angles, axis=1)
+    return np.cos(ang).astype(np.float32), np.sin(ang).astype(np.float32)
+
+
+def norm_weights(head_dim: int = 128, seed: int = 5):
+    """RMSNorm weights for Q and K as bf16 bit patterns and their values:
+    1 + N(0, 0.1^2), rounded to bf16."""
+    rng = np.random.default_rng(seed)
+    out = []
+    for _ in range(2):
+        v = (1.0 + 0.1 * rng.standard_normal(head_dim)).astype(np.float32)
+        bits = bf16_bits_from_f32(v)
+        out.append((bits, bf16_bits_to_f64(bits)))
+    return out
