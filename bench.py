@@ -114,6 +114,52 @@ def cpu_baseline(wl, layer, rank, target_s, precision="int4"):
             "host_cpu_count": os.cpu_count()}
 
 
+def bench_qkv(S, L, workloads, r, steps, warmup):
+    """The joint-stream QKV projection (4608 x 3072 -> 9216, bias) with the
+    fused per-head Q/K RMSNorm + rotary epilogue, against the same step with
+    the plain epilogue."""
+    import torch
+    wl = workloads.make_workload("joint_qkv")
+    Lr = wl.layers[0]
+    M, K, N = wl.M, Lr.K, Lr.N
+    prep = S.prepare_weights(Lr.weight_bits, wl.act_absmax(), rank=r)
+    lin = S.SVDQW4A4Linear(prep, torch.from_numpy(Lr.bias_bits.view(np.int16).copy()).view(torch.bfloat16), "cuda")
+    (qb, _), (kb, _) = workloads.norm_weights()
+    cos, sin = workloads.rope_tables(512, 64)
+    gq = torch.from_numpy(qb.view(np.int16).copy()).view(torch.bfloat16).cuda()
+    gk = torch.from_numpy(kb.view(np.int16).copy()).view(torch.bfloat16).cuda()
+    cos_d, sin_d = torch.from_numpy(cos).cuda(), torch.from_numpy(sin).cuda()
+    x = torch.from_numpy(wl.x_bits.view(np.int16).copy()).view(torch.bfloat16).cuda()
+    xc = torch.empty((M, K // 2), dtype=torch.uint8, device="cuda")
+    xs = torch.empty((K // 64, M), dtype=torch.float16, device="cuda")
+    la = torch.empty((M, r), dtype=torch.float32, device="cuda") if r else None
+    y = torch.empty((M, N), dtype=torch.bfloat16, device="cuda")
+
+    def timed(fused):
+        def step():
+            S.quant_act_lora_down(x, lin.smooth_inv, lin.lora_down, r, out=(xc, xs, la))
+            if fused:
+                S.gemm_w4a4_lora_up_qkv(xc, xs, lin.w_codes, lin.w_scales, la, lin.lora_up, lin.bias, gq, gk,
+                                        cos_d, sin_d, M, N, K, r, out=y)
+            else:
+                S.gemm_w4a4_lora_up(xc, xs, lin.w_codes, lin.w_scales, la, lin.lora_up, lin.bias, M, N, K, r, out=y)
+        for _ in range(warmup):
+            step()
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for _ in range(steps):
+            step()
+        torch.cuda.synchronize()
+        return (time.perf_counter() - t0) * 1e3 / steps
+
+    plain_ms, fused_ms = timed(False), timed(True)
+    ops = 2.0 * M * N * K
+    return {"workload": "FLUX joint-stream QKV 4608x3072x9216 (+bias), rank 32, 24 heads of 128",
+            "plain_ms_per_step": round(plain_ms, 5), "fused_ms_per_step": round(fused_ms, 5),
+            "fused_effective_tops": round(ops / (fused_ms * 1e-3) / 1e12, 2),
+            "epilogue_overhead_frac": round(fused_ms / plain_ms - 1.0, 4)}
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__)
     ap.add_argument("--gpus", type=int, default=1)
@@ -301,6 +347,8 @@ def main():
         out["mxfp4_variant"] = {"value": round(mx_m["value"], 2), "unit": "TFLOP/s (effective, 2MNK)",
                                 "ms_per_step": round(ms_mx, 5), "roofline": mx_m["roofline"],
                                 "roofline_k1": mx_m["roofline_k1"]}
+    if args.precision == "int4" and not args.no_variants:
+        out["qkv_fused_epilogue"] = bench_qkv(S, L, workloads, r, args.steps, args.warmup)
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(wl, layer, r, args.cpu_seconds, args.precision)
     print(json.dumps(out))

@@ -56,7 +56,7 @@ typedef enum svdq_status {
 
 enum { SVDQ_ACT_NONE = 0, SVDQ_ACT_GELU_TANH = 1 };
 enum { SVDQ_OUT_BF16 = 0, SVDQ_OUT_F32 = 1 };
-enum { SVDQ_GROUP = 64, SVDQ_MAX_RANK = 256 };
+enum { SVDQ_GROUP = 64, SVDQ_MAX_RANK = 256, SVDQ_QKV_HEAD_DIM = 128 };
 
 /* Human-readable name of a status code (static storage, never NULL). */
 const char* svdq_status_string(int status);
@@ -163,6 +163,32 @@ int svdq_gemm_w4a4_lora_up(const void* x_codes, const void* x_scales,
                            const float* lora_act, const void* lora_up, const void* bias,
                            int M, int N, int K, int rank, int group, int out_dtype,
                            void* y, void* stream);
+
+/* Device, asynchronous.  Kernel 2 with the fused QKV epilogue: the operator
+ * that consumes the QKV projection, the Q/K normalization and the rotary
+ * embedding together ("Bringing Nunchaku 4-bit Diffusion Inference to
+ * Diffusers", "Quantizing models with structural rewrites").  The weight is
+ * the concatenation [W_q; W_k; W_v] along the output dimension (in that
+ * order), so N = 3 * heads * 128 (head dimension SVDQ_QKV_HEAD_DIM).  After
+ * the projection (exactly as svdq_gemm_w4a4_lora_up, bias included, in
+ * fp32), every Q head and every K head h of row m is
+ *     t = y[m, head] / sqrt(mean(y[m, head]^2) + eps) * g      (g = norm_q or norm_k)
+ * then, when rope_cos / rope_sin are given, each adjacent pair (2i, 2i+1)
+ * of the head turns by the row's angle i:
+ *     (t0, t1) -> (t0 cos - t1 sin, t1 cos + t0 sin),  cos = rope_cos[m][i], sin = rope_sin[m][i].
+ * V heads are stored as projected.  One rounding to the output type at the end.
+ *   norm_q, norm_k [128] bf16    RMSNorm weights
+ *   rope_cos, rope_sin [M][64] fp32 (both NULL: no rotation)
+ *   eps >= 0 (finite)
+ * Other arguments, layouts and errors as svdq_gemm_w4a4_lora_up; N not a
+ * multiple of 384 returns SVDQ_ERR_UNSUPPORTED_SHAPE. */
+int svdq_gemm_w4a4_lora_up_qkv(const void* x_codes, const void* x_scales,
+                               const void* w_codes, const void* w_scales,
+                               const float* lora_act, const void* lora_up, const void* bias,
+                               const void* norm_q, const void* norm_k,
+                               const float* rope_cos, const float* rope_sin, float eps,
+                               int M, int N, int K, int rank, int group, int out_dtype,
+                               void* y, void* stream);
 
 /* Device, asynchronous.  The unfused low-rank branch, kept as the reference
  * for the fusion the model card's "Nunchaku Engine Design" describes (its

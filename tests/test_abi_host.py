@@ -84,6 +84,13 @@ def test_device_entry_validation_precedes_device_use():
     assert g(p[0], p[1], p[2], p[3], p[4], p[5], None, 16, 64, 128, 16, 64, 2, p[6], None) == L.SVDQ_ERR_INVALID_ARG
     assert g(p[0], p[1], p[2], p[3], None, None, None, 16, 64, 128, 16, 64, 0, p[6], None) == L.SVDQ_ERR_INVALID_ARG
     assert g(p[0], p[1], p[2], p[3], p[4], p[5], p[7] + 8, 16, 64, 128, 16, 64, 0, p[6], None) == L.SVDQ_ERR_INVALID_ARG
+    qk = L.lib().svdq_gemm_w4a4_lora_up_qkv
+    #        xc    xs    wc    ws    la    lu    bias  nq    nk    cos   sin   eps   M   N    K    r   g   out y
+    assert qk(p[0], p[1], p[2], p[3], p[4], p[5], None, p[6], p[7], p[8], p[9], 1e-6, 16, 256, 128, 16, 64, 0, p[6], None) == L.SVDQ_ERR_UNSUPPORTED_SHAPE
+    assert qk(p[0], p[1], p[2], p[3], p[4], p[5], None, None, p[7], p[8], p[9], 1e-6, 16, 384, 128, 16, 64, 0, p[6], None) == L.SVDQ_ERR_INVALID_ARG
+    assert qk(p[0], p[1], p[2], p[3], p[4], p[5], None, p[6], p[7], p[8], None, 1e-6, 16, 384, 128, 16, 64, 0, p[6], None) == L.SVDQ_ERR_INVALID_ARG
+    assert qk(p[0], p[1], p[2], p[3], p[4], p[5], None, p[6], p[7], p[8], p[9], -1.0, 16, 384, 128, 16, 64, 0, p[6], None) == L.SVDQ_ERR_INVALID_ARG
+    assert qk(p[0], p[1], p[2], p[3], p[4], p[5], None, p[6], p[7] + 2, None, None, 1e-6, 16, 384, 128, 16, 64, 0, p[6], None) == L.SVDQ_ERR_INVALID_ARG
     d = L.lib().svdq_lora_down
     u = L.lib().svdq_lora_up_add
     assert d(p[0], p[1], p[2], 16, 128, 0, 64, 0, p[3], None) == L.SVDQ_ERR_INVALID_ARG       # rank 0
@@ -115,7 +122,9 @@ r4 = L.lib().svdq_lora_down(p[0], p[1], p[2], 16, 128, 32, 64, 0, p[3], None)
 r5 = L.lib().svdq_lora_up_add(p[0], p[1], 16, 128, 16, p[2], None)
 r6 = L.lib().svdq_quant_act_lora_down_mxfp4(p[0], p[1], p[2], 16, 128, 32, 0, p[3], p[4], p[5], None)
 r7 = L.lib().svdq_gemm_mxfp4_lora_up(p[0], p[1], p[2], p[3], p[4], p[5], None, 16, 64, 128, 16, 0, p[6], None)
-print(r1, r2, r3, r4, r5, r6, r7)
+r8 = L.lib().svdq_gemm_w4a4_lora_up_qkv(p[0], p[1], p[2], p[3], p[4], p[5], None, p[6], p[7], None, None, 1e-6,
+                                        16, 384, 128, 16, 64, 0, p[6], None)
+print(r1, r2, r3, r4, r5, r6, r7, r8)
 """
 
 
@@ -127,7 +136,7 @@ def test_unsupported_device_is_refused():
     r = subprocess.run([sys.executable, "-c", REFUSAL_SCRIPT.format(root=ROOT)], env=env,
                        capture_output=True, text=True, timeout=120)
     assert r.returncode == 0, r.stderr
-    assert r.stdout.split() == [str(L.SVDQ_ERR_UNSUPPORTED_DEVICE)] * 7
+    assert r.stdout.split() == [str(L.SVDQ_ERR_UNSUPPORTED_DEVICE)] * 8
 
 
 # ------------------------------------------------------------ host preparation

@@ -418,3 +418,73 @@ def test_checkpoint_round_trip_forward(tmp_path):
     y0, y1 = lin0(x), lin1(x)
     torch.cuda.synchronize()
     np.testing.assert_array_equal(y0.view(torch.int16).cpu().numpy(), y1.view(torch.int16).cpu().numpy())
+
+
+# ------------------------------------------------------------------ fused QKV epilogue
+def _qkv_inputs(M, seed, rope=True):
+    (qb, qv), (kb, kv) = workloads.norm_weights(seed=seed)
+    if rope:
+        ang = np.random.default_rng(seed).uniform(-np.pi, np.pi, (M, 64))
+        cos, sin = np.cos(ang).astype(np.float32), np.sin(ang).astype(np.float32)
+    else:
+        cos = sin = None
+    return qb, qv, kb, kv, cos, sin
+
+
+def run_qkv(xc, xs, abi, la, bias_bits, M, qb, kb, cos, sin, out_dtype=L.SVDQ_OUT_BF16):
+    r = abi["rank"]
+    y = S.gemm_w4a4_lora_up_qkv(xc, xs, dev(abi["w_codes"]), dev(abi["w_scales"]), la,
+                                dev_bf16(abi["lora_up"]) if r else None,
+                                dev_bf16(bias_bits) if bias_bits is not None else None,
+                                dev_bf16(qb), dev_bf16(kb),
+                                dev(cos) if cos is not None else None, dev(sin) if sin is not None else None,
+                                M, abi["N"], abi["K"], r, out_dtype=out_dtype)
+    torch.cuda.synchronize()
+    return y
+
+
+@pytest.mark.parametrize("M,heads,rank,bias,rope,out", [(300, 2, 32, True, True, "bf16"),
+                                                        (300, 2, 32, True, True, "f32"),
+                                                        (64, 1, 0, False, False, "bf16"),
+                                                        (129, 3, 16, True, False, "f32")])
+def test_qkv_epilogue_parity(M, heads, rank, bias, rope, out):
+    """Projection + per-head Q/K RMSNorm + rotary embedding against the
+    oracle's fused QKV operator; V columns bit-identical to the plain kernel."""
+    K, N = 512, 3 * heads * 128
+    wl, Lr, po, abi = _small_case(M, K, N, rank, seed=52 + M, bias=bias)
+    qb, qv, kb, kv, cos, sin = _qkv_inputs(M, 53 + M, rope)
+    Yo, parts = O.forward(wl.x, po, bias=Lr.bias, out="f64", return_parts=True)
+    ref = O.forward_qkv(wl.x, po, Lr.bias, qv, kv, cos, sin, out=out)
+    xc = dev(O.pack_int4(parts["qx"]))
+    xs = dev(parts["sx"].T.astype(np.float16))
+    la = dev(parts["lora_act"].astype(np.float32)) if rank else None
+    od = L.SVDQ_OUT_F32 if out == "f32" else L.SVDQ_OUT_BF16
+    y = run_qkv(xc, xs, abi, la, Lr.bias_bits if bias else None, M, qb, kb, cos, sin, out_dtype=od)
+    e = O.rel_fro(y_to_np(y), ref)
+    assert e < (1e-5 if out == "f32" else Y_TOL), e
+    plain = run_k2(xc, xs, abi, la, Lr.bias_bits if bias else None, M, out_dtype=od)
+    v0 = 2 * heads * 128
+    np.testing.assert_array_equal(y[:, v0:].float().cpu().numpy(), plain[:, v0:].float().cpu().numpy())
+
+
+def test_qkv_full_size_sampled_rows():
+    """The joint-stream QKV shape (4096 image + 512 text rows, 3072 -> 9216,
+    rank 32, bias) with FLUX-style rotary tables, both kernels in the launch
+    configuration the benchmark times, sampled rows against the oracle."""
+    wl = workloads.make_workload("joint_qkv")
+    Lr = wl.layers[0]
+    M, K, N, r = wl.M, Lr.K, Lr.N, 32
+    rng = np.random.default_rng(11)
+    a = wl.act_absmax()
+    si, lam = O.smoothing_factors(a, Lr.weight)
+    l1, l2 = _synthetic_factors(K, N, r, rng, scale=float(np.abs(lam).mean() * 0.02))
+    po = O.prepare(Lr.weight, a, rank=r, factors=(l1, l2))
+    abi = oracle_prep_to_abi(po)
+    (qb, qv), (kb, kv) = workloads.norm_weights(seed=12)
+    cos, sin = workloads.rope_tables(512, 64)
+    xc, xs, la = run_k1(wl.x_bits, abi["smooth_inv"], abi["lora_down"], r)
+    y = run_qkv(xc, xs, abi, la, Lr.bias_bits, M, qb, kb, cos, sin)
+    rows = _sample_rows(M, rng)
+    ref = O.forward_qkv(wl.x[rows], po, Lr.bias, qv, kv, cos[rows], sin[rows])
+    assert O.rel_fro(to_np_bf16(y[torch.from_numpy(rows).cuda()]), ref) < Y_TOL
+    assert torch.isfinite(y.float()).all()

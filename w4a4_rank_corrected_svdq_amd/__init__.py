@@ -5,7 +5,8 @@ package is its Python binding.
 """
 from ._lib import SVDQError, lib  # noqa: F401
 from . import _lib as abi  # noqa: F401
-from .ops import (device_check, gemm_mxfp4_lora_up, gemm_w4a4_lora_up, lora_down,  # noqa: F401
+from .ops import (device_check, gemm_mxfp4_lora_up, gemm_w4a4_lora_up, gemm_w4a4_lora_up_qkv,  # noqa: F401
+                  lora_down,
                   lora_up_add, prepare_weights, prepare_weights_mxfp4, prepared_bytes,
                   prepared_bytes_mxfp4, quant_act_lora_down, quant_act_lora_down_mxfp4)
 from .linear import SVDQW4A4Linear  # noqa: F401

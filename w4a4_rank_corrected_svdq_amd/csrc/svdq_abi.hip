@@ -2,6 +2,7 @@
 // capability check, and dispatch to the kernel launchers.  See include/svdq.h.
 
 #include <hip/hip_runtime.h>
+#include <cmath>
 
 #include <atomic>
 #include <cstdint>
@@ -185,4 +186,31 @@ extern "C" int svdq_gemm_mxfp4_lora_up(const void* x_codes, const void* x_scales
   if (M == 0) return SVDQ_OK;
   return svdq::launch_gemm_mxfp4_lora_up(x_codes, x_scales, w_codes, w_scales, lora_act, lora_up, bias, M, N,
                                          K, rank, out_dtype, y, stream);
+}
+
+extern "C" int svdq_gemm_w4a4_lora_up_qkv(const void* x_codes, const void* x_scales, const void* w_codes,
+                                          const void* w_scales, const float* lora_act, const void* lora_up,
+                                          const void* bias, const void* norm_q, const void* norm_k,
+                                          const float* rope_cos, const float* rope_sin, float eps, int M, int N,
+                                          int K, int rank, int group, int out_dtype, void* y, void* stream) {
+  if (M < 0) return SVDQ_ERR_INVALID_ARG;
+  int st = svdq::validate_shape(K, N, rank, group);
+  if (st != SVDQ_OK) return st;
+  if (N % (3 * SVDQ_QKV_HEAD_DIM) != 0) return SVDQ_ERR_UNSUPPORTED_SHAPE;
+  if (out_dtype != SVDQ_OUT_BF16 && out_dtype != SVDQ_OUT_F32) return SVDQ_ERR_INVALID_ARG;
+  if (!(eps >= 0.0f) || !std::isfinite(eps)) return SVDQ_ERR_INVALID_ARG;
+  if (!x_codes || !x_scales || !w_codes || !w_scales || !y || !norm_q || !norm_k) return SVDQ_ERR_INVALID_ARG;
+  if ((rope_cos == nullptr) != (rope_sin == nullptr)) return SVDQ_ERR_INVALID_ARG;
+  if (rank > 0 && (!lora_act || !lora_up)) return SVDQ_ERR_INVALID_ARG;
+  if (!aligned16(x_codes) || !aligned16(x_scales) || !aligned16(w_codes) || !aligned16(w_scales) ||
+      !aligned16(y) || (bias && !aligned16(bias)) || !aligned16(norm_q) || !aligned16(norm_k) ||
+      (rope_cos && (!aligned16(rope_cos) || !aligned16(rope_sin))) ||
+      (rank > 0 && (!aligned16(lora_act) || !aligned16(lora_up))))
+    return SVDQ_ERR_INVALID_ARG;
+  if (!fits_buffer(M, K / 2) || !fits_buffer(N, K / 2)) return SVDQ_ERR_UNSUPPORTED_SHAPE;
+  st = current_device_check();
+  if (st != SVDQ_OK) return st;
+  if (M == 0) return SVDQ_OK;
+  return svdq::launch_gemm_w4a4_lora_up_qkv(x_codes, x_scales, w_codes, w_scales, lora_act, lora_up, bias, norm_q,
+                                            norm_k, rope_cos, rope_sin, eps, M, N, K, rank, out_dtype, y, stream);
 }

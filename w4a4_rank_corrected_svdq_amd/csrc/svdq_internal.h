@@ -21,6 +21,11 @@ int launch_gemm_w4a4_lora_up(const void* x_codes, const void* x_scales, const vo
                              const void* bias, int M, int N, int K, int rank, int out_dtype, void* y,
                              void* stream);
 
+int launch_gemm_w4a4_lora_up_qkv(const void* x_codes, const void* x_scales, const void* w_codes,
+                                 const void* w_scales, const float* lora_act, const void* lora_up,
+                                 const void* bias, const void* norm_q, const void* norm_k, const float* rope_cos,
+                                 const float* rope_sin, float eps, int M, int N, int K, int rank, int out_dtype,
+                                 void* y, void* stream);
 int launch_quant_act_lora_down_mxfp4(const void* x, const float* smooth_inv, const void* lora_down, int M,
                                      int K, int rank, int act, void* x_codes, void* x_scales,
                                      float* lora_act, void* stream);

@@ -293,12 +293,23 @@ __device__ __forceinline__ uint4 unpack_hi(uint4 w) {  // codes 16..31
   return make_uint4((w.z << 4) & 0xF0F0F0F0u, w.z & 0xF0F0F0F0u, (w.w << 4) & 0xF0F0F0F0u, w.w & 0xF0F0F0F0u);
 }
 
-template <int OUT_F32, int NT>
+// Arguments of the fused QKV epilogue: RMSNorm weights of Q and K heads
+// (bf16, 128 each), rotary tables cos / sin [M][64] (NULL: no rotation).
+struct QkvArgs {
+  const uint16_t* gq;
+  const uint16_t* gk;
+  const float* cos;
+  const float* sin;
+  float eps;
+};
+constexpr int QKV_HEAD = 128;
+
+template <int OUT_F32, int NT, int EPI>
 __global__ __launch_bounds__(K2_THREADS, 2) void k_gemm_w4a4_lora_up(
     const uint8_t* __restrict__ x_codes, const _Float16* __restrict__ x_scales,
     const uint8_t* __restrict__ w_codes, const _Float16* __restrict__ w_scales,
     const float* __restrict__ lora_act, const uint16_t* __restrict__ lora_up,
-    const uint16_t* __restrict__ bias, int M, int N, int K, int rank, void* __restrict__ y) {
+    const uint16_t* __restrict__ bias, int M, int N, int K, int rank, void* __restrict__ y, QkvArgs qa) {
   extern __shared__ __align__(16) unsigned char k2_smem_raw[];
   K2Smem& sm = *reinterpret_cast<K2Smem*>(k2_smem_raw);
 
@@ -480,12 +491,85 @@ __global__ __launch_bounds__(K2_THREADS, 2) void k_gemm_w4a4_lora_up(
     }
   }
 
-  // ---- bias and store.  A lane holds output row m and columns
-  // 8b + 4 fk + (0..3) of each 32-column tile.  bf16 output goes through
-  // LDS (free after the K loop's last barrier): each wave writes its 64 x 64
-  // tile with 8-byte writes, then stores whole 128-byte row segments, eight
-  // rows per instruction.  16-byte chunk c of tile row r sits at chunk
-  // c ^ (r & 7), which keeps both LDS passes free of bank conflicts.
+  // ---- bias, then (fused QKV only) per-head RMSNorm and rotary embedding
+  // of the Q and K heads.  A lane holds output row m and columns
+  // 8b + 4 fk + (0..3) of each 32-column tile.
+  if (bias) {
+#pragma unroll
+    for (int j = 0; j < K2_TJ; ++j) {
+#pragma unroll
+      for (int bb = 0; bb < 4; ++bb) {
+        const int c = n0 + wn * K2_WN + j * 32 + 8 * bb + 4 * fk;   // N % 8 == 0: all four in or out
+        if (c >= N) continue;
+        const uint2 bv = *reinterpret_cast<const uint2*>(bias + c);
+        const float b4[4] = {bf16_bits_to_f32(bv.x & 0xFFFFu), bf16_bits_to_f32(bv.x >> 16),
+                             bf16_bits_to_f32(bv.y & 0xFFFFu), bf16_bits_to_f32(bv.y >> 16)};
+#pragma unroll
+        for (int i = 0; i < K2_TI; ++i)
+#pragma unroll
+          for (int e = 0; e < 4; ++e) acc[i][j][4 * bb + e] += b4[e];
+      }
+    }
+  }
+  if constexpr (EPI == 1) {
+    // The block's 128 columns are one head (N = 3 * heads * 128, block tiles
+    // aligned to heads).  Q heads come first, then K heads, then V heads,
+    // which are left as projected.  This condition is uniform per block.
+    const int HD = N / 3;
+    if (n0 < 2 * HD) {
+      const uint16_t* g = n0 < HD ? qa.gq : qa.gk;
+      // sum of squares of each row over the head: this lane's 32 columns,
+      // the partner lane's other 32 (lane ^ 32), the other wave's 64 via LDS
+      float* red = reinterpret_cast<float*>(k2_smem_raw + K2_WAVES * K2_WM * K2_WN * 2);
+      float ss[K2_TI];
+#pragma unroll
+      for (int i = 0; i < K2_TI; ++i) {
+        float t = 0.f;
+#pragma unroll
+        for (int j = 0; j < K2_TJ; ++j)
+#pragma unroll
+          for (int v = 0; v < 16; ++v) t = fmaf(acc[i][j][v], acc[i][j][v], t);
+        ss[i] = t + __shfl_xor(t, 32);
+        if (fk == 0) red[((wm * K2_TI + i) * 2 + wn) * 32 + fr] = ss[i];
+      }
+      __syncthreads();
+#pragma unroll
+      for (int i = 0; i < K2_TI; ++i) {
+        const float tot = red[((wm * K2_TI + i) * 2 + 0) * 32 + fr] + red[((wm * K2_TI + i) * 2 + 1) * 32 + fr];
+        const float scale = 1.0f / sqrtf(tot * (1.0f / QKV_HEAD) + qa.eps);
+        const int row = m0 + wm * K2_WM + i * 32 + fr;
+        const bool rot = qa.cos != nullptr && row < M;
+#pragma unroll
+        for (int j = 0; j < K2_TJ; ++j) {
+#pragma unroll
+          for (int bb = 0; bb < 4; ++bb) {
+            const int ch = wn * K2_WN + j * 32 + 8 * bb + 4 * fk;        // column within the head
+            const uint2 gv = *reinterpret_cast<const uint2*>(g + ch);
+            const float g4[4] = {bf16_bits_to_f32(gv.x & 0xFFFFu), bf16_bits_to_f32(gv.x >> 16),
+                                 bf16_bits_to_f32(gv.y & 0xFFFFu), bf16_bits_to_f32(gv.y >> 16)};
+            float o[4];
+#pragma unroll
+            for (int e = 0; e < 4; ++e) o[e] = acc[i][j][4 * bb + e] * scale * g4[e];
+            if (rot) {
+              const float2 cs = *reinterpret_cast<const float2*>(qa.cos + static_cast<size_t>(row) * 64 + (ch >> 1));
+              const float2 sn = *reinterpret_cast<const float2*>(qa.sin + static_cast<size_t>(row) * 64 + (ch >> 1));
+              const float a0 = o[0] * cs.x - o[1] * sn.x, a1 = o[1] * cs.x + o[0] * sn.x;
+              const float a2 = o[2] * cs.y - o[3] * sn.y, a3 = o[3] * cs.y + o[2] * sn.y;
+              o[0] = a0; o[1] = a1; o[2] = a2; o[3] = a3;
+            }
+#pragma unroll
+            for (int e = 0; e < 4; ++e) acc[i][j][4 * bb + e] = o[e];
+          }
+        }
+      }
+    }
+  }
+
+  // ---- store.  bf16 output goes through LDS (free after the K loop's last
+  // barrier): each wave writes its 64 x 64 tile with 8-byte writes, then
+  // stores whole 128-byte row segments, eight rows per instruction.
+  // 16-byte chunk c of tile row r sits at chunk c ^ (r & 7), which keeps
+  // both LDS passes free of bank conflicts.
   if (OUT_F32) {
 #pragma unroll
     for (int i = 0; i < K2_TI; ++i) {
@@ -495,20 +579,10 @@ __global__ __launch_bounds__(K2_THREADS, 2) void k_gemm_w4a4_lora_up(
       for (int j = 0; j < K2_TJ; ++j) {
 #pragma unroll
         for (int bb = 0; bb < 4; ++bb) {
-          const int c = n0 + wn * K2_WN + j * 32 + 8 * bb + 4 * fk;   // N % 8 == 0: all four in or out
+          const int c = n0 + wn * K2_WN + j * 32 + 8 * bb + 4 * fk;
           if (c >= N) continue;
-          float o[4];
-#pragma unroll
-          for (int e = 0; e < 4; ++e) o[e] = acc[i][j][4 * bb + e];
-          if (bias) {
-            const uint2 bv = *reinterpret_cast<const uint2*>(bias + c);
-            o[0] += bf16_bits_to_f32(bv.x & 0xFFFFu);
-            o[1] += bf16_bits_to_f32(bv.x >> 16);
-            o[2] += bf16_bits_to_f32(bv.y & 0xFFFFu);
-            o[3] += bf16_bits_to_f32(bv.y >> 16);
-          }
           *reinterpret_cast<float4*>(reinterpret_cast<float*>(y) + static_cast<size_t>(row) * N + c) =
-              make_float4(o[0], o[1], o[2], o[3]);
+              make_float4(acc[i][j][4 * bb], acc[i][j][4 * bb + 1], acc[i][j][4 * bb + 2], acc[i][j][4 * bb + 3]);
         }
       }
     }
@@ -521,17 +595,9 @@ __global__ __launch_bounds__(K2_THREADS, 2) void k_gemm_w4a4_lora_up(
       for (int j = 0; j < K2_TJ; ++j) {
 #pragma unroll
         for (int bb = 0; bb < 4; ++bb) {
-          const int c = n0 + wn * K2_WN + j * 32 + 8 * bb + 4 * fk;
           float o[4];
 #pragma unroll
           for (int e = 0; e < 4; ++e) o[e] = acc[i][j][4 * bb + e];
-          if (bias && c < N) {
-            const uint2 bv = *reinterpret_cast<const uint2*>(bias + c);
-            o[0] += bf16_bits_to_f32(bv.x & 0xFFFFu);
-            o[1] += bf16_bits_to_f32(bv.x >> 16);
-            o[2] += bf16_bits_to_f32(bv.y & 0xFFFFu);
-            o[3] += bf16_bits_to_f32(bv.y >> 16);
-          }
           const int chunk = j * 4 + bb;                 // 16-byte chunk of the 128-byte tile row
           tile[rl * 16 + ((chunk ^ (rl & 7)) << 1) + fk] =
               make_uint2(f32_to_bf16_bits(o[0]) | (f32_to_bf16_bits(o[1]) << 16),
@@ -657,29 +723,35 @@ __global__ __launch_bounds__(256) void k_lora_up_add(const float* __restrict__ l
   }
 }
 
-template <int OUT_F32, int NT>
+// LDS: the stage buffers, and in the epilogue the four 64 x 64 bf16 output
+// tiles followed by the QKV epilogue's row sums (4 waves x 2 tiles x 32 rows).
+constexpr size_t K2_SMEM_EPI = static_cast<size_t>(K2_WAVES) * K2_WM * K2_WN * 2 + K2_WAVES * K2_TI * 32 * 4;
+constexpr size_t K2_SMEM = sizeof(K2Smem) > K2_SMEM_EPI ? sizeof(K2Smem) : K2_SMEM_EPI;
+
+template <int OUT_F32, int NT, int EPI>
 void launch_k2_kernel(const void* xc, const void* xs, const void* wc, const void* ws, const float* la,
                       const void* lu, const void* bias, int M, int N, int K, int rank, void* y,
-                      hipStream_t st) {
+                      const QkvArgs& qa, hipStream_t st) {
   // the stage buffers exceed the default 64 KB of dynamic LDS: opt in once
   static const bool attr_ok = [] {
-    return hipFuncSetAttribute(reinterpret_cast<const void*>(k_gemm_w4a4_lora_up<OUT_F32, NT>),
+    return hipFuncSetAttribute(reinterpret_cast<const void*>(k_gemm_w4a4_lora_up<OUT_F32, NT, EPI>),
                                hipFuncAttributeMaxDynamicSharedMemorySize,
-                               static_cast<int>(sizeof(K2Smem))) == hipSuccess;
+                               static_cast<int>(K2_SMEM)) == hipSuccess;
   }();
   (void)attr_ok;
   const int nb = ((N + K2_BN - 1) / K2_BN) * ((M + K2_BM - 1) / K2_BM);
-  hipLaunchKernelGGL((k_gemm_w4a4_lora_up<OUT_F32, NT>), dim3(nb), dim3(K2_THREADS), sizeof(K2Smem), st,
+  hipLaunchKernelGGL((k_gemm_w4a4_lora_up<OUT_F32, NT, EPI>), dim3(nb), dim3(K2_THREADS), K2_SMEM, st,
                      static_cast<const uint8_t*>(xc), static_cast<const _Float16*>(xs),
                      static_cast<const uint8_t*>(wc), static_cast<const _Float16*>(ws), la,
-                     static_cast<const uint16_t*>(lu), static_cast<const uint16_t*>(bias), M, N, K, rank, y);
+                     static_cast<const uint16_t*>(lu), static_cast<const uint16_t*>(bias), M, N, K, rank, y, qa);
 }
 
-template <int OUT_F32>
+template <int OUT_F32, int EPI>
 int launch_k2(const void* xc, const void* xs, const void* wc, const void* ws, const float* la,
-              const void* lu, const void* bias, int M, int N, int K, int rank, void* y, hipStream_t st) {
-  if (rank == 0) launch_k2_kernel<OUT_F32, 0>(xc, xs, wc, ws, la, lu, bias, M, N, K, rank, y, st);
-  else launch_k2_kernel<OUT_F32, 1>(xc, xs, wc, ws, la, lu, bias, M, N, K, rank, y, st);
+              const void* lu, const void* bias, int M, int N, int K, int rank, void* y, const QkvArgs& qa,
+              hipStream_t st) {
+  if (rank == 0) launch_k2_kernel<OUT_F32, 0, EPI>(xc, xs, wc, ws, la, lu, bias, M, N, K, rank, y, qa, st);
+  else launch_k2_kernel<OUT_F32, 1, EPI>(xc, xs, wc, ws, la, lu, bias, M, N, K, rank, y, qa, st);
   return hipGetLastError() == hipSuccess ? SVDQ_OK : SVDQ_ERR_HIP;
 }
 
@@ -726,9 +798,23 @@ int launch_gemm_w4a4_lora_up(const void* x_codes, const void* x_scales, const vo
                              const void* bias, int M, int N, int K, int rank, int out_dtype, void* y,
                              void* stream) {
   hipStream_t st = static_cast<hipStream_t>(stream);
+  const QkvArgs qa{nullptr, nullptr, nullptr, nullptr, 0.f};
   if (out_dtype == SVDQ_OUT_F32)
-    return launch_k2<1>(x_codes, x_scales, w_codes, w_scales, lora_act, lora_up, bias, M, N, K, rank, y, st);
-  return launch_k2<0>(x_codes, x_scales, w_codes, w_scales, lora_act, lora_up, bias, M, N, K, rank, y, st);
+    return launch_k2<1, 0>(x_codes, x_scales, w_codes, w_scales, lora_act, lora_up, bias, M, N, K, rank, y, qa, st);
+  return launch_k2<0, 0>(x_codes, x_scales, w_codes, w_scales, lora_act, lora_up, bias, M, N, K, rank, y, qa, st);
+}
+
+int launch_gemm_w4a4_lora_up_qkv(const void* x_codes, const void* x_scales, const void* w_codes,
+                                 const void* w_scales, const float* lora_act, const void* lora_up,
+                                 const void* bias, const void* norm_q, const void* norm_k, const float* rope_cos,
+                                 const float* rope_sin, float eps, int M, int N, int K, int rank, int out_dtype,
+                                 void* y, void* stream) {
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  const QkvArgs qa{static_cast<const uint16_t*>(norm_q), static_cast<const uint16_t*>(norm_k), rope_cos, rope_sin,
+                   eps};
+  if (out_dtype == SVDQ_OUT_F32)
+    return launch_k2<1, 1>(x_codes, x_scales, w_codes, w_scales, lora_act, lora_up, bias, M, N, K, rank, y, qa, st);
+  return launch_k2<0, 1>(x_codes, x_scales, w_codes, w_scales, lora_act, lora_up, bias, M, N, K, rank, y, qa, st);
 }
 
 }  // namespace svdq

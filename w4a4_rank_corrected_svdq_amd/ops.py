@@ -16,7 +16,7 @@ from . import _lib as L
 
 __all__ = ["prepare_weights", "quant_act_lora_down", "gemm_w4a4_lora_up", "prepared_bytes",
            "device_check", "lora_down", "lora_up_add", "prepared_bytes_mxfp4", "prepare_weights_mxfp4",
-           "quant_act_lora_down_mxfp4", "gemm_mxfp4_lora_up"]
+           "quant_act_lora_down_mxfp4", "gemm_mxfp4_lora_up", "gemm_w4a4_lora_up_qkv"]
 
 
 def _ptr(t) -> Optional[int]:
@@ -273,4 +273,31 @@ def gemm_mxfp4_lora_up(x_codes, x_scales, w_codes, w_scales, lora_act, lora_up, 
         _dev_arg("bias", bias, torch.bfloat16, (N,), dev),
         M, N, K, rank, out_dtype, _dev_arg("y", out, dt, (M, N), dev), _stream(dev))
     L.check(st, "svdq_gemm_mxfp4_lora_up")
+    return out
+
+
+def gemm_w4a4_lora_up_qkv(x_codes, x_scales, w_codes, w_scales, lora_act, lora_up, bias, norm_q, norm_k,
+                          rope_cos, rope_sin, M: int, N: int, K: int, rank: int, eps: float = 1e-6,
+                          group: int = 64, out_dtype: int = L.SVDQ_OUT_BF16, out: Optional[torch.Tensor] = None):
+    """Kernel 2 with the fused QKV epilogue (per-head Q/K RMSNorm + rotary
+    embedding); returns y [M][N] with N = 3 * heads * 128."""
+    dev = x_codes.device
+    dt = torch.float32 if out_dtype == L.SVDQ_OUT_F32 else torch.bfloat16
+    if out is None:
+        out = torch.empty((M, N), dtype=dt, device=dev)
+    G = K // group if group > 0 else 0
+    st = L.lib().svdq_gemm_w4a4_lora_up_qkv(
+        _dev_arg("x_codes", x_codes, torch.uint8, (M, K // 2), dev),
+        _dev_arg("x_scales", x_scales, torch.float16, (G, M), dev),
+        _dev_arg("w_codes", w_codes, torch.uint8, (N, K // 2), dev),
+        _dev_arg("w_scales", w_scales, torch.float16, (G, N), dev),
+        _dev_arg("lora_act", lora_act, torch.float32, (M, rank), dev) if rank else None,
+        _dev_arg("lora_up", lora_up, torch.bfloat16, (N, rank), dev) if rank else None,
+        _dev_arg("bias", bias, torch.bfloat16, (N,), dev),
+        _dev_arg("norm_q", norm_q, torch.bfloat16, (128,), dev),
+        _dev_arg("norm_k", norm_k, torch.bfloat16, (128,), dev),
+        _dev_arg("rope_cos", rope_cos, torch.float32, (M, 64), dev),
+        _dev_arg("rope_sin", rope_sin, torch.float32, (M, 64), dev),
+        float(eps), M, N, K, rank, group, out_dtype, _dev_arg("y", out, dt, (M, N), dev), _stream(dev))
+    L.check(st, "svdq_gemm_w4a4_lora_up_qkv")
     return out
