@@ -215,3 +215,38 @@ def norm_weights(head_dim: int = 128, seed: int = 5):
         bits = bf16_bits_from_f32(v)
         out.append((bits, bf16_bits_to_f64(bits)))
     return out
+
+
+# --------------------------------------------------------------------------
+# AWQ W4A16 modulation-layer inputs
+# --------------------------------------------------------------------------
+def _silu(v):
+    return v / (1.0 + np.exp(-v))
+
+
+def awq_workload(M: int, K: int = 3072, N: int = 18432, Mc: int = 32, seed: int = 6, n_out: int = 8):
+    """FLUX adaLN modulation projection (conditioning vector -> 6 x hidden).
+    Inputs are SiLU of a Gaussian with log-normal per-channel magnitudes
+    (exp(N(0, 0.75^2))) and ``n_out`` channels x10, which is what makes the
+    activation-aware scaling matter; the calibration rows are ``Mc`` further
+    draws of the same distribution.  Weights N(0, 0.02^2) and bias
+    N(0, 0.01^2), all rounded to bf16.  Returns a dict of bit patterns and
+    values."""
+    rng = np.random.default_rng(seed)
+    mag = np.exp(0.75 * rng.standard_normal(K))
+    mag[rng.choice(K, n_out, replace=False)] *= 10.0
+    w = rng.standard_normal((N, K)).astype(np.float32) * 0.02
+    b = rng.standard_normal(N).astype(np.float32) * 0.01
+
+    def draw(rows):
+        return _silu(rng.standard_normal((rows, K)) * mag[None, :]).astype(np.float32)
+
+    x = draw(M)
+    xc = draw(Mc)
+    out = {}
+    for name, v in (("x", x), ("x_cal", xc), ("weight", w), ("bias", b)):
+        bits = bf16_bits_from_f32(v)
+        out[name + "_bits"] = bits
+        out[name] = bf16_bits_to_f64(bits)
+    out.update(M=M, K=K, N=N, Mc=Mc)
+    return out
