@@ -56,7 +56,7 @@ typedef enum svdq_status {
 
 enum { SVDQ_ACT_NONE = 0, SVDQ_ACT_GELU_TANH = 1 };
 enum { SVDQ_OUT_BF16 = 0, SVDQ_OUT_F32 = 1 };
-enum { SVDQ_GROUP = 64, SVDQ_MAX_RANK = 256, SVDQ_QKV_HEAD_DIM = 128 };
+enum { SVDQ_GROUP = 64, SVDQ_MAX_RANK = 256, SVDQ_QKV_HEAD_DIM = 128, SVDQ_AWQ_MAX_ROWS = 16 };
 
 /* Human-readable name of a status code (static storage, never NULL). */
 const char* svdq_status_string(int status);
@@ -261,6 +261,43 @@ int svdq_gemm_mxfp4_lora_up(const void* x_codes, const void* x_scales,
                             const float* lora_act, const void* lora_up, const void* bias,
                             int M, int N, int K, int rank, int out_dtype,
                             void* y, void* stream);
+
+/* ------------------------------------------------------------------------
+ * AWQ W4A16 linear: 4-bit weights, 16-bit activations, for the adaptive
+ * normalization / modulation projections ("Bringing Nunchaku 4-bit Diffusion
+ * Inference to Diffusers", "Introducing Nunchaku Lite"; int4, group 64 in
+ * "Native loading in Diffusers").  These layers see a few rows (the
+ * conditioning vectors), so the path streams the weight once at HBM rate.
+ * ------------------------------------------------------------------------ */
+
+/* Host, synchronous.  Activation-aware weight quantization of one layer.
+ *   weight [N][K] bf16, x_cal [Mc][K] bf16 calibration activations
+ *   alpha: < 0 searches {k / 20.0 : k = 0..19} (fp64); otherwise used as given (< 1)
+ * Channel scale t_k = max(a_k, 1e-4)^alpha / sqrt(max t * min t) with
+ * a_k = mean_m |x_cal[m][k]|; alpha minimizes the calibration output error
+ * sum (x_cal W^T - x_cal diag(t)^-1 Q(W diag(t))^T)^2 (first minimum).
+ * Per (output channel, group of 64) of W diag(t), t := 1 / fp64(inv_scale):
+ * s = fp16(max(max - min, 1e-5) / 15), z = clamp(rne(-min / s), 0, 15),
+ * q = clamp(rne(w / s) + z, 0, 15).  Outputs (caller-owned host buffers):
+ *   inv_scale [K] fp32 (1 / t), w_codes [N][K/2] u8 (unsigned codes, low
+ *   nibble = even k), w_scales [N][K/64] fp16, w_zeros [N][K/64] u8,
+ *   alpha_out (nullable).  N % 16 == 0, K % 64 == 0. */
+int svdq_awq_prepare(const uint16_t* weight, int K, int N, const uint16_t* x_cal, int Mc, double alpha,
+                     int group, float* inv_scale, uint8_t* w_codes, uint16_t* w_scales,
+                     uint8_t* w_zeros, double* alpha_out);
+
+/* Device, asynchronous.  x_hat [M][K] bf16 = bf16(fp32(x * inv_scale)) and
+ * xsum [K/64][16] fp32: per group and row, the sum of the group's x_hat in
+ * increasing k (rows M..15 are written as 0).  M <= 16. */
+int svdq_awq_quant_act(const void* x, const float* inv_scale, int M, int K, void* x_hat, float* xsum,
+                       void* stream);
+
+/* Device, asynchronous.  y [M][N] bf16 = bf16(sum_g s[n][g] (sum_{k in g}
+ * q[n][k] x_hat[m][k] - z[n][g] xsum[g][m]) + bias[n]) with fp32 sums; the
+ * inner sums run on bf16 MFMA.  M <= 16, N % 16 == 0, K % 64 == 0; bias
+ * nullable. */
+int svdq_awq_gemv(const void* x_hat, const float* xsum, const void* w_codes, const void* w_scales,
+                  const void* w_zeros, const void* bias, int M, int N, int K, void* y, void* stream);
 
 #ifdef __cplusplus
 }

@@ -1,0 +1,109 @@
+"""GPU parity of the AWQ W4A16 path (through the C ABI) against the AWQ oracle.
+
+Bars: x_hat bit-exact; xsum equal to the fp32 sum in increasing k; output
+within 1e-3 relative Frobenius of the oracle's bf16 output (the inner sums
+run on bf16 MFMA with fp32 accumulation; the oracle sums in fp64).
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle as O
+import workloads
+from oracle import awq_oracle as A
+from tests._helpers import bf16_bits_to_f64
+
+S = pytest.importorskip("w4a4_rank_corrected_svdq_amd")
+
+pytestmark = pytest.mark.gpu
+
+Y_TOL = 1e-3
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _device():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    assert S.device_check(0) == 0, "device is not gfx950"
+    torch.cuda.set_device(0)
+
+
+def dev(a):
+    return torch.from_numpy(np.ascontiguousarray(a)).cuda()
+
+
+def dev_bf16(bits):
+    return torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).view(torch.bfloat16).cuda()
+
+
+def to_np_bf16(t):
+    return bf16_bits_to_f64(t.view(torch.int16).cpu().numpy().view(np.uint16))
+
+
+def _pack(q):
+    return (q[:, 0::2] | (q[:, 1::2] << 4)).astype(np.uint8)
+
+
+def _case(M, K, N, seed, alpha=None):
+    wl = workloads.awq_workload(M, K=K, N=N, Mc=16, seed=seed)
+    po = A.awq_prepare(wl["weight"], wl["x_cal"], alpha=alpha)
+    return wl, po
+
+
+def _run(wl, po, bias=True):
+    M, K, N = wl["M"], wl["K"], wl["N"]
+    xh, xs = S.awq_quant_act(dev_bf16(wl["x_bits"]), dev(po["inv_scale"].astype(np.float32)))
+    y = S.awq_gemv(xh, xs, dev(_pack(po["q"])), dev(po["s"].astype(np.float16)), dev(po["z"].astype(np.uint8)),
+                   dev_bf16(wl["bias_bits"]) if bias else None, M, N, K)
+    torch.cuda.synchronize()
+    return xh, xs, y
+
+
+@pytest.mark.parametrize("M,K", [(1, 512), (5, 3072), (16, 192)])
+def test_awq_quant_act_exact(M, K):
+    wl, po = _case(M, K, 32, seed=60 + M, alpha=0.5)
+    xh, xs, _ = _run(wl, po)
+    x_hat = O.bf16(O.fp32(wl["x"] * po["inv_scale"][None, :]))
+    np.testing.assert_array_equal(to_np_bf16(xh), x_hat)
+    sums = np.zeros((K // 64, 16), np.float32)
+    for g in range(K // 64):
+        sums[g, :M] = np.cumsum(x_hat[:, 64 * g:64 * g + 64].astype(np.float32), axis=1, dtype=np.float32)[:, -1]
+    np.testing.assert_array_equal(xs.cpu().numpy(), sums)
+
+
+@pytest.mark.parametrize("M,K,N,bias", [(1, 512, 272, True), (3, 3072, 128, True), (16, 1024, 64, False),
+                                        (7, 64, 16, True), (2, 4096, 48, False)])
+def test_awq_gemv_parity(M, K, N, bias):
+    wl, po = _case(M, K, N, seed=70 + M + K)
+    _, _, y = _run(wl, po, bias)
+    ref = A.awq_forward(wl["x"], po, bias=wl["bias"] if bias else None)
+    assert O.rel_fro(to_np_bf16(y), ref) < Y_TOL
+
+
+@pytest.mark.parametrize("M", [1, 2])
+def test_awq_full_size_modulation(M):
+    """FLUX double-block modulation projection 3072 -> 18432 with bias, the
+    benchmark's launch configuration; the whole output against the oracle."""
+    wl, po = _case(M, 3072, 18432, seed=80 + M)
+    _, _, y = _run(wl, po)
+    ref = A.awq_forward(wl["x"], po, bias=wl["bias"])
+    assert O.rel_fro(to_np_bf16(y), ref) < Y_TOL
+    assert torch.isfinite(y.float()).all()
+
+
+def test_awq_module_and_error_story():
+    """Library-prepared layer: the searched alpha beats plain round-to-nearest
+    (alpha = 0) against fp64 x W^T, measured on the GPU output."""
+    wl = workloads.awq_workload(16, K=1024, N=512, Mc=32, seed=90)
+    ref = wl["x"] @ wl["weight"].T + wl["bias"][None, :]
+    lin = torch.nn.Linear(1024, 512, bias=True)
+    with torch.no_grad():
+        lin.weight.copy_(torch.from_numpy(wl["weight"]))
+        lin.bias.copy_(torch.from_numpy(wl["bias"]))
+    x = dev_bf16(wl["x_bits"])
+    xc = torch.from_numpy(wl["x_cal_bits"].view(np.int16).copy()).view(torch.bfloat16)
+    errs = {}
+    for alpha in (-1.0, 0.0):
+        m = S.AWQW4A16Linear.from_linear(lin, xc, alpha=alpha)
+        errs[alpha] = O.rel_fro(to_np_bf16(m(x)), ref)
+    assert errs[-1.0] < errs[0.0] < 0.1, errs

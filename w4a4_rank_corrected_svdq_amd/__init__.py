@@ -5,11 +5,11 @@ package is its Python binding.
 """
 from ._lib import SVDQError, lib  # noqa: F401
 from . import _lib as abi  # noqa: F401
-from .ops import (device_check, gemm_mxfp4_lora_up, gemm_w4a4_lora_up, gemm_w4a4_lora_up_qkv,  # noqa: F401
+from .ops import (awq_gemv, awq_prepare, awq_quant_act, device_check, gemm_mxfp4_lora_up, gemm_w4a4_lora_up, gemm_w4a4_lora_up_qkv,  # noqa: F401
                   lora_down,
                   lora_up_add, prepare_weights, prepare_weights_mxfp4, prepared_bytes,
                   prepared_bytes_mxfp4, quant_act_lora_down, quant_act_lora_down_mxfp4)
-from .linear import SVDQW4A4Linear  # noqa: F401
+from .linear import AWQW4A16Linear, SVDQW4A4Linear  # noqa: F401
 from .checkpoint import load_linears, load_prepared, save_prepared  # noqa: F401
 
 __version__ = "0.1.0"

@@ -43,6 +43,9 @@ SIGNATURES = {
     "svdq_lora_up_add": (_i, [_p, _p, _i, _i, _i, _p, _p]),
     "svdq_gemm_w4a4_lora_up_qkv": (_i, [_p, _p, _p, _p, _p, _p, _p, _p, _p, _p, _p, ctypes.c_float,
                                         _i, _i, _i, _i, _i, _i, _p, _p]),
+    "svdq_awq_prepare": (_i, [_p, _i, _i, _p, _i, ctypes.c_double, _i, _p, _p, _p, _p, _p]),
+    "svdq_awq_quant_act": (_i, [_p, _p, _i, _i, _p, _p, _p]),
+    "svdq_awq_gemv": (_i, [_p, _p, _p, _p, _p, _p, _i, _i, _i, _p, _p]),
     "svdq_prepared_bytes_mxfp4": (_i, [_i, _i, _i, ctypes.POINTER(ctypes.c_size_t)]),
     "svdq_prepare_weights_mxfp4": (_i, [_p, _i, _i, _p, ctypes.c_float, _i, _p, _p, _i, ctypes.c_uint64,
                                         _p, _p, _p, _p, _p, _p]),

@@ -214,3 +214,29 @@ extern "C" int svdq_gemm_w4a4_lora_up_qkv(const void* x_codes, const void* x_sca
   return svdq::launch_gemm_w4a4_lora_up_qkv(x_codes, x_scales, w_codes, w_scales, lora_act, lora_up, bias, norm_q,
                                             norm_k, rope_cos, rope_sin, eps, M, N, K, rank, out_dtype, y, stream);
 }
+
+extern "C" int svdq_awq_quant_act(const void* x, const float* inv_scale, int M, int K, void* x_hat, float* xsum,
+                                  void* stream) {
+  if (M < 0 || K <= 0) return SVDQ_ERR_INVALID_ARG;
+  if (K % SVDQ_GROUP != 0 || M > SVDQ_AWQ_MAX_ROWS) return SVDQ_ERR_UNSUPPORTED_SHAPE;
+  if (!x || !inv_scale || !x_hat || !xsum) return SVDQ_ERR_INVALID_ARG;
+  if (!aligned16(x) || !aligned16(inv_scale) || !aligned16(x_hat) || !aligned16(xsum)) return SVDQ_ERR_INVALID_ARG;
+  const int st = current_device_check();
+  if (st != SVDQ_OK) return st;
+  return svdq::launch_awq_quant_act(x, inv_scale, M, K, x_hat, xsum, stream);
+}
+
+extern "C" int svdq_awq_gemv(const void* x_hat, const float* xsum, const void* w_codes, const void* w_scales,
+                             const void* w_zeros, const void* bias, int M, int N, int K, void* y, void* stream) {
+  if (M < 0 || N <= 0 || K <= 0) return SVDQ_ERR_INVALID_ARG;
+  if (K % SVDQ_GROUP != 0 || N % 16 != 0 || M > SVDQ_AWQ_MAX_ROWS) return SVDQ_ERR_UNSUPPORTED_SHAPE;
+  if (!x_hat || !xsum || !w_codes || !w_scales || !w_zeros || !y) return SVDQ_ERR_INVALID_ARG;
+  if (!aligned16(x_hat) || !aligned16(xsum) || !aligned16(w_codes) || !aligned16(w_scales) || !aligned16(w_zeros) ||
+      !aligned16(y) || (bias && !aligned16(bias)))
+    return SVDQ_ERR_INVALID_ARG;
+  if (!fits_buffer(N, K / 2) || !fits_buffer(M, 2LL * K)) return SVDQ_ERR_UNSUPPORTED_SHAPE;
+  const int st = current_device_check();
+  if (st != SVDQ_OK) return st;
+  if (M == 0) return SVDQ_OK;
+  return svdq::launch_awq_gemv(x_hat, xsum, w_codes, w_scales, w_zeros, bias, M, N, K, y, stream);
+}

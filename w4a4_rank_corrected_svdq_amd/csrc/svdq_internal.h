@@ -35,4 +35,10 @@ int launch_gemm_mxfp4_lora_up(const void* x_codes, const void* x_scales, const v
                               const void* bias, int M, int N, int K, int rank, int out_dtype, void* y,
                               void* stream);
 
+// svdq_awq_kernels.hip
+int launch_awq_quant_act(const void* x, const float* inv_scale, int M, int K, void* x_hat, float* xsum,
+                         void* stream);
+int launch_awq_gemv(const void* x_hat, const float* xsum, const void* w_codes, const void* w_scales,
+                    const void* w_zeros, const void* bias, int M, int N, int K, void* y, void* stream);
+
 }  // namespace svdq

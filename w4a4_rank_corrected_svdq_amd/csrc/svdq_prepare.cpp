@@ -533,3 +533,151 @@ extern "C" int svdq_prepare_weights_mxfp4(const uint16_t* weight, int K, int N, 
   });
   return SVDQ_OK;
 }
+
+// ---------------------------------------------------------------------------
+// AWQ W4A16 preparation ("Bringing Nunchaku 4-bit Diffusion Inference to
+// Diffusers", "Introducing Nunchaku Lite": 4-bit weights with 16-bit
+// activations for the modulation projections; "Native loading in Diffusers":
+// int4, group 64).  Activation-aware channel scale t_k = max(a_k, 1e-4)^alpha
+// normalized by sqrt(max t * min t), a_k = mean |x_cal[:, k]|; alpha from a
+// 20-point grid minimizing the calibration output error unless given;
+// asymmetric unsigned INT4 per (output channel, group of 64) of W diag(t).
+namespace {
+
+struct AwqGroupQuant {
+  uint16_t s_bits;
+  double s;
+  int z;
+};
+
+inline AwqGroupQuant awq_group(const double* w, int n) {
+  double mx = w[0], mn = w[0];
+  for (int i = 1; i < n; ++i) {
+    mx = std::max(mx, w[i]);
+    mn = std::min(mn, w[i]);
+  }
+  AwqGroupQuant g;
+  g.s_bits = to_fp16(std::max(mx - mn, 1e-5) / 15.0);
+  g.s = fp16_value(g.s_bits);
+  g.z = static_cast<int>(std::max(0.0, std::min(15.0, std::nearbyint(-mn / g.s))));
+  return g;
+}
+
+inline int awq_code(double w, const AwqGroupQuant& g) {
+  return static_cast<int>(std::max(0.0, std::min(15.0, std::nearbyint(w / g.s) + g.z)));
+}
+
+// Channel scale for one alpha: stored inverse (fp32) and the fp64 scale the
+// weight side uses, t = 1 / fp64(inv).
+void awq_scales(const std::vector<double>& a, double alpha, std::vector<float>& inv, std::vector<double>& t) {
+  const size_t K = a.size();
+  std::vector<double> u(K);
+  double mx = 0.0, mn = INFINITY;
+  for (size_t k = 0; k < K; ++k) {
+    u[k] = std::pow(std::max(a[k], 1e-4), alpha);
+    mx = std::max(mx, u[k]);
+    mn = std::min(mn, u[k]);
+  }
+  const double norm = std::sqrt(mx * mn);
+  inv.resize(K);
+  t.resize(K);
+  for (size_t k = 0; k < K; ++k) {
+    inv[k] = static_cast<float>(1.0 / (u[k] / norm));
+    t[k] = 1.0 / static_cast<double>(inv[k]);
+  }
+}
+
+}  // namespace
+
+extern "C" int svdq_awq_prepare(const uint16_t* weight, int K, int N, const uint16_t* x_cal, int Mc, double alpha,
+                                int group, float* inv_scale, uint8_t* w_codes, uint16_t* w_scales,
+                                uint8_t* w_zeros, double* alpha_out) {
+  if (K <= 0 || N <= 0 || Mc <= 0 || group <= 0) return SVDQ_ERR_INVALID_ARG;
+  if (group != SVDQ_GROUP || K % group != 0 || N % 16 != 0) return SVDQ_ERR_UNSUPPORTED_SHAPE;
+  if (!weight || !x_cal || !inv_scale || !w_codes || !w_scales || !w_zeros) return SVDQ_ERR_INVALID_ARG;
+  if (!(alpha < 1.0) || std::isnan(alpha)) return SVDQ_ERR_INVALID_ARG;   // alpha < 0: search
+  const size_t NK = static_cast<size_t>(N) * K;
+  if (!all_finite_bf16(weight, NK) || !all_finite_bf16(x_cal, static_cast<size_t>(Mc) * K)) return SVDQ_ERR_NUMERIC;
+  std::vector<double> W(NK), X(static_cast<size_t>(Mc) * K), a(K, 0.0);
+  for (size_t i = 0; i < NK; ++i) W[i] = bf16_value(weight[i]);
+  for (size_t i = 0; i < X.size(); ++i) X[i] = bf16_value(x_cal[i]);
+  for (int m = 0; m < Mc; ++m)
+    for (int k = 0; k < K; ++k) a[k] += std::fabs(X[static_cast<size_t>(m) * K + k]);
+  for (int k = 0; k < K; ++k) a[k] /= Mc;
+  const int G = K / group;
+
+  double chosen = alpha;
+  if (alpha < 0.0) {
+    // reference outputs X W^T on the calibration rows
+    std::vector<double> ref(static_cast<size_t>(Mc) * N);
+    parallel_for(N, 64, [&](int64_t lo, int64_t hi) {
+      for (int64_t n = lo; n < hi; ++n)
+        for (int m = 0; m < Mc; ++m) {
+          const double* x = &X[static_cast<size_t>(m) * K];
+          const double* w = &W[n * K];
+          double s = 0.0;
+          for (int k = 0; k < K; ++k) s += x[k] * w[k];
+          ref[static_cast<size_t>(m) * N + n] = s;
+        }
+    });
+    double best = INFINITY;
+    for (int gi = 0; gi < 20; ++gi) {
+      const double al = gi / 20.0;
+      std::vector<float> inv;
+      std::vector<double> t;
+      awq_scales(a, al, inv, t);
+      std::vector<double> part(N, 0.0);
+      parallel_for(N, 16, [&](int64_t lo, int64_t hi) {
+        std::vector<double> wq(K), ws(group);
+        for (int64_t n = lo; n < hi; ++n) {
+          for (int g = 0; g < G; ++g) {
+            for (int i = 0; i < group; ++i) ws[i] = W[n * K + g * group + i] * t[g * group + i];
+            const AwqGroupQuant q = awq_group(ws.data(), group);
+            for (int i = 0; i < group; ++i)
+              wq[g * group + i] = (awq_code(ws[i], q) - q.z) * q.s * static_cast<double>(inv[g * group + i]);
+          }
+          double e = 0.0;
+          for (int m = 0; m < Mc; ++m) {
+            const double* x = &X[static_cast<size_t>(m) * K];
+            double s = 0.0;
+            for (int k = 0; k < K; ++k) s += x[k] * wq[k];
+            const double d = ref[static_cast<size_t>(m) * N + n] - s;
+            e += d * d;
+          }
+          part[n] = e;
+        }
+      });
+      double loss = 0.0;
+      for (int n = 0; n < N; ++n) loss += part[n];
+      if (loss < best) {
+        best = loss;
+        chosen = al;
+      }
+    }
+  }
+  std::vector<float> inv;
+  std::vector<double> t;
+  awq_scales(a, chosen, inv, t);
+  for (int k = 0; k < K; ++k) {
+    if (!std::isfinite(inv[k]) || !(inv[k] > 0.0f)) return SVDQ_ERR_NUMERIC;
+    inv_scale[k] = inv[k];
+  }
+  std::atomic<int> bad{0};
+  parallel_for(N, 16, [&](int64_t lo, int64_t hi) {
+    std::vector<double> ws(group);
+    for (int64_t n = lo; n < hi; ++n)
+      for (int g = 0; g < G; ++g) {
+        for (int i = 0; i < group; ++i) ws[i] = W[n * K + g * group + i] * t[g * group + i];
+        const AwqGroupQuant q = awq_group(ws.data(), group);
+        if (!std::isfinite(q.s)) bad.store(1);
+        w_scales[n * G + g] = q.s_bits;
+        w_zeros[n * G + g] = static_cast<uint8_t>(q.z);
+        uint8_t* dst = w_codes + n * (K / 2) + g * (group / 2);
+        for (int i = 0; i < group; i += 2)
+          dst[i / 2] = static_cast<uint8_t>(awq_code(ws[i], q) | (awq_code(ws[i + 1], q) << 4));
+      }
+  });
+  if (bad.load()) return SVDQ_ERR_NUMERIC;
+  if (alpha_out) *alpha_out = chosen;
+  return SVDQ_OK;
+}

@@ -71,3 +71,34 @@ class SVDQW4A4Linear:
                                      M, self.N, self.K, self.rank, self.group, out_dtype)
 
     __call__ = forward
+
+
+class AWQW4A16Linear:
+    """AWQ W4A16 layer (the pages' runtime layer name for the modulation
+    projections): 4-bit weights with activation-aware channel scales, bf16
+    activations, a few rows per call."""
+
+    def __init__(self, prepared: dict, bias: Optional[torch.Tensor], device):
+        dev = torch.device(device)
+        self.K, self.N, self.group = prepared["K"], prepared["N"], prepared["group"]
+        self.alpha = prepared.get("alpha")
+        self.inv_scale = _to_dev(np.asarray(prepared["inv_scale"], np.float32), dev)
+        self.w_codes = _to_dev(np.asarray(prepared["w_codes"], np.uint8), dev)
+        self.w_scales = _to_dev(np.asarray(prepared["w_scales"], np.float16), dev)
+        self.w_zeros = _to_dev(np.asarray(prepared["w_zeros"], np.uint8), dev)
+        self.bias = None if bias is None else bias.detach().to(dev, torch.bfloat16).contiguous()
+
+    @classmethod
+    def from_linear(cls, linear: torch.nn.Linear, x_cal, alpha: float = -1.0, device="cuda"):
+        """Quantize a ``torch.nn.Linear`` given calibration activations
+        ``x_cal`` [Mc][in] (bf16); alpha < 0 searches the grid."""
+        w = linear.weight.detach().to(torch.bfloat16).cpu()
+        xc = torch.as_tensor(x_cal).to(torch.bfloat16).cpu()
+        return cls(ops.awq_prepare(w, xc, alpha), linear.bias, device)
+
+    def forward(self, x: torch.Tensor):
+        M = x.shape[0]
+        xh, xs = ops.awq_quant_act(x, self.inv_scale)
+        return ops.awq_gemv(xh, xs, self.w_codes, self.w_scales, self.w_zeros, self.bias, M, self.N, self.K)
+
+    __call__ = forward

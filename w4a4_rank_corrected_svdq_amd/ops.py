@@ -16,7 +16,8 @@ from . import _lib as L
 
 __all__ = ["prepare_weights", "quant_act_lora_down", "gemm_w4a4_lora_up", "prepared_bytes",
            "device_check", "lora_down", "lora_up_add", "prepared_bytes_mxfp4", "prepare_weights_mxfp4",
-           "quant_act_lora_down_mxfp4", "gemm_mxfp4_lora_up", "gemm_w4a4_lora_up_qkv"]
+           "quant_act_lora_down_mxfp4", "gemm_mxfp4_lora_up", "gemm_w4a4_lora_up_qkv", "awq_prepare",
+           "awq_quant_act", "awq_gemv"]
 
 
 def _ptr(t) -> Optional[int]:
@@ -300,4 +301,66 @@ def gemm_w4a4_lora_up_qkv(x_codes, x_scales, w_codes, w_scales, lora_act, lora_u
         _dev_arg("rope_sin", rope_sin, torch.float32, (M, 64), dev),
         float(eps), M, N, K, rank, group, out_dtype, _dev_arg("y", out, dt, (M, N), dev), _stream(dev))
     L.check(st, "svdq_gemm_w4a4_lora_up_qkv")
+    return out
+
+
+# ---------------------------------------------------------------- AWQ W4A16
+def awq_prepare(weight, x_cal, alpha: float = -1.0, group: int = 64) -> dict:
+    """Host AWQ preparation (svdq_awq_prepare).  weight [N][K] and x_cal
+    [Mc][K] bf16 (tensors or uint16 bits); alpha < 0 searches the grid.
+    Returns numpy arrays: inv_scale f32 [K], w_codes u8 [N][K/2], w_scales
+    f16 [N][K/64], w_zeros u8 [N][K/64], and alpha."""
+    w = _bf16_bits(weight)
+    xc = _bf16_bits(x_cal)
+    N, K = w.shape
+    Mc = xc.shape[0]
+    if xc.shape[1] != K:
+        raise ValueError("x_cal must be [Mc][K]")
+    inv = np.empty(K, np.float32)
+    wc = np.empty((N, K // 2), np.uint8)
+    ws = np.empty((N, max(K // group, 0)), np.float16)
+    wz = np.empty((N, max(K // group, 0)), np.uint8)
+    al = ctypes.c_double(0.0)
+    st = L.lib().svdq_awq_prepare(_ptr(w), K, N, _ptr(xc), Mc, float(alpha), group, _ptr(inv), _ptr(wc),
+                                  _ptr(ws), _ptr(wz), ctypes.addressof(al))
+    L.check(st, "svdq_awq_prepare")
+    return dict(inv_scale=inv, w_codes=wc, w_scales=ws, w_zeros=wz, alpha=float(al.value), K=K, N=N, group=group)
+
+
+def awq_quant_act(x: torch.Tensor, inv_scale: torch.Tensor, out=None):
+    """x_hat [M][K] bf16 and xsum [K/64][16] fp32 (svdq_awq_quant_act)."""
+    if x.dtype != torch.bfloat16 or x.dim() != 2 or not x.is_cuda:
+        raise TypeError("x must be a 2-D bfloat16 CUDA tensor")
+    x = x.contiguous()
+    M, K = x.shape
+    dev = x.device
+    if out is None:
+        xh = torch.empty((M, K), dtype=torch.bfloat16, device=dev)
+        xs = torch.empty((K // 64, 16), dtype=torch.float32, device=dev)
+    else:
+        xh, xs = out
+    st = L.lib().svdq_awq_quant_act(_dev_arg("x", x, torch.bfloat16, (M, K), dev),
+                                    _dev_arg("inv_scale", inv_scale, torch.float32, (K,), dev), M, K,
+                                    _dev_arg("x_hat", xh, torch.bfloat16, (M, K), dev),
+                                    _dev_arg("xsum", xs, torch.float32, (K // 64, 16), dev), _stream(dev))
+    L.check(st, "svdq_awq_quant_act")
+    return xh, xs
+
+
+def awq_gemv(x_hat, xsum, w_codes, w_scales, w_zeros, bias, M: int, N: int, K: int,
+             out: Optional[torch.Tensor] = None):
+    """y [M][N] bf16 (svdq_awq_gemv)."""
+    dev = x_hat.device
+    if out is None:
+        out = torch.empty((M, N), dtype=torch.bfloat16, device=dev)
+    G = K // 64
+    st = L.lib().svdq_awq_gemv(
+        _dev_arg("x_hat", x_hat, torch.bfloat16, (M, K), dev),
+        _dev_arg("xsum", xsum, torch.float32, (G, 16), dev),
+        _dev_arg("w_codes", w_codes, torch.uint8, (N, K // 2), dev),
+        _dev_arg("w_scales", w_scales, torch.float16, (N, G), dev),
+        _dev_arg("w_zeros", w_zeros, torch.uint8, (N, G), dev),
+        _dev_arg("bias", bias, torch.bfloat16, (N,), dev),
+        M, N, K, _dev_arg("y", out, torch.bfloat16, (M, N), dev), _stream(dev))
+    L.check(st, "svdq_awq_gemv")
     return out
