@@ -160,6 +160,47 @@ def bench_qkv(S, L, workloads, r, steps, warmup):
             "epilogue_overhead_frac": round(fused_ms / plain_ms - 1.0, 4)}
 
 
+def bench_awq(S, workloads, steps, warmup, M=1):
+    """AWQ W4A16 on the FLUX double-block modulation projection (3072 ->
+    18432, bias), M conditioning rows: HBM-bound on the weight read."""
+    import torch
+    wl = workloads.awq_workload(M, K=3072, N=18432, Mc=16, seed=7)
+    K, N = wl["K"], wl["N"]
+    prep = S.awq_prepare(wl["weight_bits"], wl["x_cal_bits"])
+    lin = S.AWQW4A16Linear(prep, torch.from_numpy(wl["bias_bits"].view(np.int16).copy()).view(torch.bfloat16), "cuda")
+    x = torch.from_numpy(wl["x_bits"].view(np.int16).copy()).view(torch.bfloat16).cuda()
+    xh = torch.empty((M, K), dtype=torch.bfloat16, device="cuda")
+    xs = torch.empty((K // 64, 16), dtype=torch.float32, device="cuda")
+    y = torch.empty((M, N), dtype=torch.bfloat16, device="cuda")
+    st = torch.cuda.current_stream()
+
+    def step(ev=None):
+        S.awq_quant_act(x, lin.inv_scale, out=(xh, xs))
+        if ev is not None:
+            ev[0].record(st)
+        S.awq_gemv(xh, xs, lin.w_codes, lin.w_scales, lin.w_zeros, lin.bias, M, N, K, out=y)
+        if ev is not None:
+            ev[1].record(st)
+
+    for _ in range(warmup):
+        step()
+    torch.cuda.synchronize()
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(steps)]
+    t0 = time.perf_counter()
+    for i in range(steps):
+        step(evs[i])
+    torch.cuda.synchronize()
+    ms = (time.perf_counter() - t0) * 1e3 / steps
+    gemv_ms = float(np.mean([e[0].elapsed_time(e[1]) for e in evs]))
+    nbytes = N * K // 2 + 2 * N * (K // 64) + N * (K // 64) + 2 * M * K + 4 * (K // 64) * 16 + 2 * N + 2 * M * N
+    gbs = nbytes / (gemv_ms * 1e-3) / 1e9
+    return {"workload": f"FLUX modulation projection 3072 -> 18432 (+bias), M = {M}, AWQ INT4 group 64",
+            "alpha": prep["alpha"], "ms_per_step": round(ms, 5),
+            "roofline": {"bound": "hbm", "kernel": "k_awq_gemv", "achieved": round(gbs, 1),
+                         "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(gbs / HBM_PEAK_GBS, 4),
+                         "avg_launch_us": round(gemv_ms * 1e3, 2), "algorithmic_bytes_per_launch": nbytes}}
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__)
     ap.add_argument("--gpus", type=int, default=1)
@@ -349,6 +390,7 @@ def main():
                                 "roofline_k1": mx_m["roofline_k1"]}
     if args.precision == "int4" and not args.no_variants:
         out["qkv_fused_epilogue"] = bench_qkv(S, L, workloads, r, args.steps, args.warmup)
+        out["awq_w4a16"] = bench_awq(S, workloads, max(args.steps, 20), args.warmup)
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(wl, layer, r, args.cpu_seconds, args.precision)
     print(json.dumps(out))

@@ -281,7 +281,7 @@ int svdq_gemm_mxfp4_lora_up(const void* x_codes, const void* x_scales,
  * q = clamp(rne(w / s) + z, 0, 15).  Outputs (caller-owned host buffers):
  *   inv_scale [K] fp32 (1 / t), w_codes [N][K/2] u8 (unsigned codes, low
  *   nibble = even k), w_scales [N][K/64] fp16, w_zeros [N][K/64] u8,
- *   alpha_out (nullable).  N % 16 == 0, K % 64 == 0. */
+ *   alpha_out (nullable).  N % 32 == 0, K % 64 == 0. */
 int svdq_awq_prepare(const uint16_t* weight, int K, int N, const uint16_t* x_cal, int Mc, double alpha,
                      int group, float* inv_scale, uint8_t* w_codes, uint16_t* w_scales,
                      uint8_t* w_zeros, double* alpha_out);
@@ -294,7 +294,7 @@ int svdq_awq_quant_act(const void* x, const float* inv_scale, int M, int K, void
 
 /* Device, asynchronous.  y [M][N] bf16 = bf16(sum_g s[n][g] (sum_{k in g}
  * q[n][k] x_hat[m][k] - z[n][g] xsum[g][m]) + bias[n]) with fp32 sums; the
- * inner sums run on bf16 MFMA.  M <= 16, N % 16 == 0, K % 64 == 0; bias
+ * inner sums run on bf16 MFMA.  M <= 16, N % 32 == 0, K % 64 == 0; bias
  * nullable. */
 int svdq_awq_gemv(const void* x_hat, const float* xsum, const void* w_codes, const void* w_scales,
                   const void* w_zeros, const void* bias, int M, int N, int K, void* y, void* stream);

@@ -42,9 +42,9 @@ def test_awq_entry_validation_precedes_device_use():
     assert qa(p[0], p[1], 17, 128, p[2], p[3], None) == L.SVDQ_ERR_UNSUPPORTED_SHAPE       # M > 16
     assert qa(p[0], p[1], 4, 96, p[2], p[3], None) == L.SVDQ_ERR_UNSUPPORTED_SHAPE
     assert qa(None, p[1], 4, 128, p[2], p[3], None) == L.SVDQ_ERR_INVALID_ARG
-    assert gv(p[0], p[1], p[2], p[3], p[4], None, 4, 24, 128, p[5], None) == L.SVDQ_ERR_UNSUPPORTED_SHAPE
+    assert gv(p[0], p[1], p[2], p[3], p[4], None, 4, 48, 128, p[5], None) == L.SVDQ_ERR_UNSUPPORTED_SHAPE
     assert gv(p[0], p[1], p[2], p[3], None, None, 4, 32, 128, p[5], None) == L.SVDQ_ERR_INVALID_ARG
     assert gv(p[0], p[1], p[2], p[3], p[4], p[6] + 2, 4, 32, 128, p[5], None) == L.SVDQ_ERR_INVALID_ARG
     assert gv(p[0], p[1], p[2], p[3], p[4], None, -1, 32, 128, p[5], None) == L.SVDQ_ERR_INVALID_ARG
     with pytest.raises(S.SVDQError):
-        S.awq_prepare(np.zeros((24, 128), np.uint16), np.zeros((4, 128), np.uint16))    # N % 16
+        S.awq_prepare(np.zeros((48, 128), np.uint16), np.zeros((4, 128), np.uint16))    # N % 32

@@ -71,8 +71,8 @@ def test_awq_quant_act_exact(M, K):
     np.testing.assert_array_equal(xs.cpu().numpy(), sums)
 
 
-@pytest.mark.parametrize("M,K,N,bias", [(1, 512, 272, True), (3, 3072, 128, True), (16, 1024, 64, False),
-                                        (7, 64, 16, True), (2, 4096, 48, False)])
+@pytest.mark.parametrize("M,K,N,bias", [(1, 512, 288, True), (3, 3072, 128, True), (16, 1024, 64, False),
+                                        (7, 64, 32, True), (2, 4160, 96, False), (9, 8192, 64, True)])
 def test_awq_gemv_parity(M, K, N, bias):
     wl, po = _case(M, K, N, seed=70 + M + K)
     _, _, y = _run(wl, po, bias)

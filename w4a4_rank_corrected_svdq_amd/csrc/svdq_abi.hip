@@ -229,7 +229,7 @@ extern "C" int svdq_awq_quant_act(const void* x, const float* inv_scale, int M, 
 extern "C" int svdq_awq_gemv(const void* x_hat, const float* xsum, const void* w_codes, const void* w_scales,
                              const void* w_zeros, const void* bias, int M, int N, int K, void* y, void* stream) {
   if (M < 0 || N <= 0 || K <= 0) return SVDQ_ERR_INVALID_ARG;
-  if (K % SVDQ_GROUP != 0 || N % 16 != 0 || M > SVDQ_AWQ_MAX_ROWS) return SVDQ_ERR_UNSUPPORTED_SHAPE;
+  if (K % SVDQ_GROUP != 0 || N % 32 != 0 || M > SVDQ_AWQ_MAX_ROWS) return SVDQ_ERR_UNSUPPORTED_SHAPE;
   if (!x_hat || !xsum || !w_codes || !w_scales || !w_zeros || !y) return SVDQ_ERR_INVALID_ARG;
   if (!aligned16(x_hat) || !aligned16(xsum) || !aligned16(w_codes) || !aligned16(w_scales) || !aligned16(w_zeros) ||
       !aligned16(y) || (bias && !aligned16(bias)))

@@ -9,22 +9,23 @@
 //   row), X_g = sum of the group's x_hat values in fp32 in increasing k,
 //   laid out [K/64][16] (rows M..15 zero).
 // k_awq_gemv: Y = bf16(sum_g s_g (sum_{k in g} q x_hat - z_g X_g) + bias) for
-//   M <= 16 rows.  The inner sums run on bf16 MFMA 16x16x32: a nibble q
+//   M <= 16 rows.  The inner sums run on bf16 MFMA 32x32x16: a nibble q
 //   becomes the bf16 value 128 + q by OR-ing it into the bit pattern 0x4300
-//   (128 = 1.0 x 2^7 has seven free mantissa bits), so one MFMA pair per group
-//   gives D = sum (128 + q) x_hat exactly per product, and the kernel
-//   subtracts (128 + z_g) X_g.  A wave owns 16 output columns and a quarter of
-//   K; the four waves of a block split K and add their partial results in LDS
-//   in wave order.  Every weight load of a wave's K range is issued before
-//   any is used, which keeps enough bytes in flight to stream HBM.
+//   (128 = 1.0 x 2^7 has seven free mantissa bits), so four MFMAs per group
+//   give D = sum (128 + q) x_hat exactly per product, and the kernel
+//   subtracts (128 + z_g) X_g.  A block owns 32 output columns; its waves
+//   split K in chunks of 8 groups and add their partial results in LDS in
+//   wave order.  All loads of a chunk (16 contiguous code bytes per lane and
+//   group) are issued before any is used, which keeps enough bytes in flight
+//   to stream HBM.
 //
-// MFMA 16x16x32 bf16 layouts (wave64): A lane l holds row l % 16, 8 values
-// of k chosen by l / 16; B lane l holds column l % 16 and the same k; D lane
-// l holds column l % 16, rows 4 (l / 16) + i.  Here rows are the M input
-// rows, columns the output channels, and lane group h = l / 16 takes k =
-// 64 g + 16 h + 8 t + (0..7) in the t-th MFMA of group g (any permutation of
-// k applied to both operands leaves the product unchanged), so each lane
-// reads 8 contiguous code bytes per group.
+// MFMA 32x32x16 bf16 layouts (wave64): A lane l holds row l % 32 and 8
+// values of k chosen by l / 32; B lane l holds column l % 32 and the same k;
+// D lane l holds column l % 32, rows 8 b + 4 (l / 32) + i in register
+// 4 b + i.  Here rows are the input rows (M <= 16, the rest read as zero),
+// columns the output channels, and lane half h = l / 32 takes k = 64 g +
+// 32 h + 8 t + (0..7) in the t-th MFMA of group g (any permutation of k
+// applied to both operands leaves the product unchanged).
 
 #include <hip/hip_runtime.h>
 #include <stdint.h>
@@ -36,9 +37,6 @@
 namespace {
 
 constexpr int AWQ_GROUP = 64;
-constexpr int AWQ_COLS = 16;        // output columns per block
-constexpr int AWQ_WAVES = 4;        // K split per block
-constexpr int AWQ_CHUNK = 16;       // groups whose weight loads are in flight together
 constexpr int AWQ_MAX_ROWS = 16;
 
 __global__ __launch_bounds__(256) void k_awq_act(const uint16_t* __restrict__ x, const float* __restrict__ inv_scale,
@@ -50,13 +48,30 @@ __global__ __launch_bounds__(256) void k_awq_act(const uint16_t* __restrict__ x,
   const int g = t / AWQ_MAX_ROWS, m = t % AWQ_MAX_ROWS;
   float s = 0.f;
   if (m < M) {
-    const uint16_t* xr = x + static_cast<size_t>(m) * K + g * AWQ_GROUP;
-    uint16_t* hr = x_hat + static_cast<size_t>(m) * K + g * AWQ_GROUP;
-    for (int i = 0; i < AWQ_GROUP; ++i) {
-      const uint32_t b = f32_to_bf16_bits(bf16_bits_to_f32(xr[i]) * inv_scale[g * AWQ_GROUP + i]);
-      hr[i] = static_cast<uint16_t>(b);
-      s += bf16_bits_to_f32(b);
+    // the group's 64 inputs and scales arrive with 8 + 16 vector loads issued
+    // together; the sum then runs in increasing k
+    const uint4* xr = reinterpret_cast<const uint4*>(x + static_cast<size_t>(m) * K + g * AWQ_GROUP);
+    const float4* sr = reinterpret_cast<const float4*>(inv_scale + g * AWQ_GROUP);
+    uint4 xv[8];
+    float4 sv[16];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) xv[i] = xr[i];
+#pragma unroll
+    for (int i = 0; i < 16; ++i) sv[i] = sr[i];
+    const uint32_t* xw = reinterpret_cast<const uint32_t*>(xv);
+    const float* sf = reinterpret_cast<const float*>(sv);
+    uint32_t hv[32];
+#pragma unroll
+    for (int i = 0; i < 32; ++i) {
+      const uint32_t b0 = f32_to_bf16_bits(bf16_bits_to_f32(xw[i] & 0xFFFFu) * sf[2 * i]);
+      const uint32_t b1 = f32_to_bf16_bits(bf16_bits_to_f32(xw[i] >> 16) * sf[2 * i + 1]);
+      s += bf16_bits_to_f32(b0);
+      s += bf16_bits_to_f32(b1);
+      hv[i] = b0 | (b1 << 16);
     }
+    uint4* hr = reinterpret_cast<uint4*>(x_hat + static_cast<size_t>(m) * K + g * AWQ_GROUP);
+#pragma unroll
+    for (int i = 0; i < 8; ++i) hr[i] = make_uint4(hv[4 * i], hv[4 * i + 1], hv[4 * i + 2], hv[4 * i + 3]);
   }
   xsum[t] = s;
 }
@@ -72,18 +87,25 @@ __device__ __forceinline__ v8bf awq_nibbles_to_bf16(uint32_t w) {
   return __builtin_bit_cast(v8bf, make_uint4(d[0], d[1], d[2], d[3]));
 }
 
-__global__ __launch_bounds__(AWQ_WAVES * 64) void k_awq_gemv(
+// Block = one tile of 32 output columns; its W waves split K in chunks of 8
+// groups (wave w takes chunks w, w + W, ...).  Lane l = 32 h + c: column
+// n0 + c; per group g it loads 16 bytes of codes (k in [64 g + 32 h, +32))
+// and four 16-byte activation fragments (the same k, row c), then runs four
+// 32x32x16 bf16 MFMAs (k offsets 8 t of each half), so both halves of every
+// MFMA lie in group g.  D lane l holds column n0 + c and rows 8 b + 4 h + i.
+template <bool VEC_SCALES>
+__global__ __launch_bounds__(VEC_SCALES ? 1024 : 512) void k_awq_gemv(
     const uint16_t* __restrict__ x_hat, const float* __restrict__ xsum, const uint8_t* __restrict__ w_codes,
     const _Float16* __restrict__ w_scales, const uint8_t* __restrict__ w_zeros, const uint16_t* __restrict__ bias,
     int M, int N, int K, uint16_t* __restrict__ y) {
-  __shared__ float part[AWQ_WAVES][64][4];
+  __shared__ float part[16][64][8];
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  const int col = lane & 15, h = lane >> 4;
-  const int n = blockIdx.x * AWQ_COLS + col;                 // N % 16 == 0: always < N
+  const int W = blockDim.x >> 6;
+  const int c = lane & 31, h = lane >> 5;
+  const int n = blockIdx.x * 32 + c;                          // N % 32 == 0: always < N
   const int G = K / AWQ_GROUP;
-  const int per = (G + AWQ_WAVES - 1) / AWQ_WAVES;
-  const int g_begin = wave * per, g_end = min(G, g_begin + per);
+  const int chunks = (G + 7) / 8;
   const uint32_t Kb = static_cast<uint32_t>(K) / 2;
 
   const __amdgpu_buffer_rsrc_t w_rs = __builtin_amdgcn_make_buffer_rsrc(
@@ -91,50 +113,84 @@ __global__ __launch_bounds__(AWQ_WAVES * 64) void k_awq_gemv(
   // activation rows past M read as zero
   const __amdgpu_buffer_rsrc_t x_rs = __builtin_amdgcn_make_buffer_rsrc(
       const_cast<uint16_t*>(x_hat), 0, static_cast<int>(static_cast<size_t>(M) * K * 2), 0x00020000);
-  const uint32_t w_row = static_cast<uint32_t>(n) * Kb + 8u * h;
-  const uint32_t x_row = static_cast<uint32_t>(col) * K * 2 + 32u * h;   // A operand row = lane % 16
+  const __amdgpu_buffer_rsrc_t s_rs = __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<_Float16*>(w_scales), 0, static_cast<int>(static_cast<size_t>(N) * G * 2), 0x00020000);
+  const __amdgpu_buffer_rsrc_t z_rs = __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<uint8_t*>(w_zeros), 0, static_cast<int>(static_cast<size_t>(N) * G), 0x00020000);
+  const uint32_t w_row = static_cast<uint32_t>(n) * Kb + 16u * h;
+  const uint32_t x_row = static_cast<uint32_t>(c) * K * 2 + 64u * h;   // A operand row = lane % 32
 
-  v4f acc = {0.f, 0.f, 0.f, 0.f};
-  for (int c0 = g_begin; c0 < g_end; c0 += AWQ_CHUNK) {
-    uint2 wv[AWQ_CHUNK];
+  v16f acc;
 #pragma unroll
-    for (int c = 0; c < AWQ_CHUNK; ++c) {
-      const int g = c0 + c;
-      wv[c] = make_uint2(0, 0);
-      if (g < g_end)
-        wv[c] = __builtin_bit_cast(uint2, __builtin_amdgcn_raw_buffer_load_b64(w_rs, w_row + 32u * g, 0, 0));
+  for (int v = 0; v < 16; ++v) acc[v] = 0.f;
+  for (int ch = wave; ch < chunks; ch += W) {
+    const int g0 = ch * 8;
+    // all loads of the chunk first; groups past G read as zeros and get scale 0
+    uint4 wv[8];
+    uint4 xa[8][4];
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      const bool ok = g0 + j < G;
+      wv[j] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(
+                                            w_rs, ok ? w_row + 32u * (g0 + j) : 0x80000000u, 0, 0));
+#pragma unroll
+      for (int t = 0; t < 4; ++t)
+        xa[j][t] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(
+                                                 x_rs, ok ? x_row + 128u * (g0 + j) + 16u * t : 0x80000000u, 0, 0));
+    }
+    // scales (8 fp16) and zero points (8 bytes) of the chunk: one 16-byte and
+    // one 8-byte load when rows start on 16-byte boundaries (G % 8 == 0),
+    // else one load per group (past the row's end: unused values)
+    const uint32_t so = static_cast<uint32_t>(n) * G + g0;
+    _Float16 scl[8];
+    uint8_t zpt[8];
+    if constexpr (VEC_SCALES) {
+      const uint4 sv = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(s_rs, 2u * so, 0, 0));
+      const uint2 zv = __builtin_bit_cast(uint2, __builtin_amdgcn_raw_buffer_load_b64(z_rs, so, 0, 0));
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        scl[j] = reinterpret_cast<const _Float16*>(&sv)[j];
+        zpt[j] = reinterpret_cast<const uint8_t*>(&zv)[j];
+      }
     }
 #pragma unroll
-    for (int c = 0; c < AWQ_CHUNK; ++c) {
-      const int g = c0 + c;
-      if (g >= g_end) break;
-      const uint32_t xo = x_row + 128u * g;
-      const v8bf a0 = __builtin_bit_cast(v8bf, __builtin_amdgcn_raw_buffer_load_b128(x_rs, xo, 0, 0));
-      const v8bf a1 = __builtin_bit_cast(v8bf, __builtin_amdgcn_raw_buffer_load_b128(x_rs, xo + 16u, 0, 0));
-      v4f d = {0.f, 0.f, 0.f, 0.f};
-      d = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a0, awq_nibbles_to_bf16(wv[c].x), d, 0, 0, 0);
-      d = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a1, awq_nibbles_to_bf16(wv[c].y), d, 0, 0, 0);
-      const float s = static_cast<float>(w_scales[static_cast<size_t>(n) * G + g]);
-      const float cz = 128.0f + static_cast<float>(w_zeros[static_cast<size_t>(n) * G + g]);
-      const float4 xs = *reinterpret_cast<const float4*>(xsum + g * AWQ_MAX_ROWS + 4 * h);
-      acc[0] = fmaf(s, fmaf(-cz, xs.x, d[0]), acc[0]);
-      acc[1] = fmaf(s, fmaf(-cz, xs.y, d[1]), acc[1]);
-      acc[2] = fmaf(s, fmaf(-cz, xs.z, d[2]), acc[2]);
-      acc[3] = fmaf(s, fmaf(-cz, xs.w, d[3]), acc[3]);
+    for (int j = 0; j < 8; ++j) {
+      const int g = min(g0 + j, G - 1);
+      const uint32_t* wd = reinterpret_cast<const uint32_t*>(&wv[j]);
+      v16f d;
+#pragma unroll
+      for (int v = 0; v < 16; ++v) d[v] = 0.f;
+#pragma unroll
+      for (int t = 0; t < 4; ++t)
+        d = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(v8bf, xa[j][t]), awq_nibbles_to_bf16(wd[t]), d,
+                                                   0, 0, 0);
+      if constexpr (!VEC_SCALES) {   // one load per group, at its use
+        scl[j] = __builtin_bit_cast(_Float16, __builtin_amdgcn_raw_buffer_load_b16(s_rs, 2u * (so + j), 0, 0));
+        zpt[j] = __builtin_amdgcn_raw_buffer_load_b8(z_rs, so + j, 0, 0);
+      }
+      const float s = (g0 + j < G) ? static_cast<float>(scl[j]) : 0.0f;
+      const float cz = 128.0f + static_cast<float>(zpt[j]);
+      const float4 x0 = *reinterpret_cast<const float4*>(xsum + g * AWQ_MAX_ROWS + 4 * h);
+      const float4 x1 = *reinterpret_cast<const float4*>(xsum + g * AWQ_MAX_ROWS + 8 + 4 * h);
+      const float xs[8] = {x0.x, x0.y, x0.z, x0.w, x1.x, x1.y, x1.z, x1.w};
+#pragma unroll
+      for (int b = 0; b < 2; ++b)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) acc[4 * b + i] = fmaf(s, fmaf(-cz, xs[4 * b + i], d[4 * b + i]), acc[4 * b + i]);
     }
   }
+  // rows 0..15 live in registers 0..7 (b = 0, 1); rows 16..31 are padding
 #pragma unroll
-  for (int i = 0; i < 4; ++i) part[wave][lane][i] = acc[i];
+  for (int v = 0; v < 8; ++v) part[wave][lane][v] = acc[v];
   __syncthreads();
   if (wave == 0) {
+    const float bb = bias ? bf16_bits_to_f32(bias[n]) : 0.0f;
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      float v = part[0][lane][i];
-#pragma unroll
-      for (int w = 1; w < AWQ_WAVES; ++w) v += part[w][lane][i];
-      const int m = 4 * h + i;
-      if (bias) v += bf16_bits_to_f32(bias[n]);
-      if (m < M) y[static_cast<size_t>(m) * N + n] = static_cast<uint16_t>(f32_to_bf16_bits(v));
+    for (int v = 0; v < 8; ++v) {
+      float t = part[0][lane][v];
+      for (int w = 1; w < W; ++w) t += part[w][lane][v];
+      const int m = 8 * (v >> 2) + 4 * h + (v & 3);
+      if (m < M) y[static_cast<size_t>(m) * N + n] = static_cast<uint16_t>(f32_to_bf16_bits(t + bb));
     }
   }
 }
@@ -155,8 +211,13 @@ int launch_awq_quant_act(const void* x, const float* inv_scale, int M, int K, vo
 int launch_awq_gemv(const void* x_hat, const float* xsum, const void* w_codes, const void* w_scales,
                     const void* w_zeros, const void* bias, int M, int N, int K, void* y, void* stream) {
   hipStream_t st = static_cast<hipStream_t>(stream);
-  hipLaunchKernelGGL(k_awq_gemv, dim3(N / AWQ_COLS), dim3(AWQ_WAVES * 64), 0, st, static_cast<const uint16_t*>(x_hat),
-                     xsum, static_cast<const uint8_t*>(w_codes), static_cast<const _Float16*>(w_scales),
+  const int chunks = (K / AWQ_GROUP + 7) / 8;
+  const bool vec = (K / AWQ_GROUP) % 8 == 0;
+  const int max_waves = vec ? 16 : 8;                // the per-group scale loads need more registers
+  const int waves = chunks < max_waves ? chunks : max_waves;
+  auto kern = vec ? k_awq_gemv<true> : k_awq_gemv<false>;
+  hipLaunchKernelGGL(kern, dim3(N / 32), dim3(waves * 64), 0, st, static_cast<const uint16_t*>(x_hat), xsum,
+                     static_cast<const uint8_t*>(w_codes), static_cast<const _Float16*>(w_scales),
                      static_cast<const uint8_t*>(w_zeros), static_cast<const uint16_t*>(bias), M, N, K,
                      static_cast<uint16_t*>(y));
   return hipGetLastError() == hipSuccess ? SVDQ_OK : SVDQ_ERR_HIP;

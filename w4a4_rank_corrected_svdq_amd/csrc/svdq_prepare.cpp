@@ -593,7 +593,7 @@ extern "C" int svdq_awq_prepare(const uint16_t* weight, int K, int N, const uint
                                 int group, float* inv_scale, uint8_t* w_codes, uint16_t* w_scales,
                                 uint8_t* w_zeros, double* alpha_out) {
   if (K <= 0 || N <= 0 || Mc <= 0 || group <= 0) return SVDQ_ERR_INVALID_ARG;
-  if (group != SVDQ_GROUP || K % group != 0 || N % 16 != 0) return SVDQ_ERR_UNSUPPORTED_SHAPE;
+  if (group != SVDQ_GROUP || K % group != 0 || N % 32 != 0) return SVDQ_ERR_UNSUPPORTED_SHAPE;
   if (!weight || !x_cal || !inv_scale || !w_codes || !w_scales || !w_zeros) return SVDQ_ERR_INVALID_ARG;
   if (!(alpha < 1.0) || std::isnan(alpha)) return SVDQ_ERR_INVALID_ARG;   // alpha < 0: search
   const size_t NK = static_cast<size_t>(N) * K;
