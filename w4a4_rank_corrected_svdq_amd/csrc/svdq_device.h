@@ -64,4 +64,39 @@ __device__ __forceinline__ void xcd_tile(int nM, int nN, int& tm, int& tn) {
   tn = r / gm;
 }
 
+// Buffer descriptor (raw, stride 0) in four scalar registers: byte base,
+// size in bytes (accesses at or past it read zeros), default format word.
+struct DmaRsrc {
+  v4i w;
+};
+__device__ __forceinline__ DmaRsrc dma_rsrc(const void* base, uint32_t bytes) {
+  const uint64_t a = reinterpret_cast<uint64_t>(base);
+  DmaRsrc r;
+  r.w[0] = __builtin_amdgcn_readfirstlane(static_cast<int>(a & 0xFFFFFFFFu));
+  r.w[1] = __builtin_amdgcn_readfirstlane(static_cast<int>((a >> 32) & 0xFFFFu));
+  r.w[2] = __builtin_amdgcn_readfirstlane(static_cast<int>(bytes));
+  r.w[3] = 0x00020000;
+  return r;
+}
+
+// LDS-DMA buffer loads: lane l's `size` bytes at byte offset voff of the
+// buffer land at LDS address lds_addr + size * l.  Issued from inline
+// assembly so that the compiler does not treat the pending LDS writes as
+// aliasing every later LDS read (it would wait for all of them); the kernel
+// waits for them itself with s_waitcnt vmcnt before the barrier that
+// publishes a stage.  s_nop 4 covers the wait states after M0 and scalar
+// register writes that a buffer load reading them needs.  No register is
+// written, so nothing stays in flight towards a register.
+__device__ __forceinline__ void dma16(const DmaRsrc& r, uint32_t lds_addr, uint32_t voff) {
+  asm volatile("s_mov_b32 m0, %0\n\ts_nop 4\n\tbuffer_load_dwordx4 %1, %2, 0 offen lds"
+               :: "s"(lds_addr), "v"(voff), "s"(r.w) : "memory", "m0");
+}
+__device__ __forceinline__ void dma4(const DmaRsrc& r, uint32_t lds_addr, uint32_t voff) {
+  asm volatile("s_mov_b32 m0, %0\n\ts_nop 4\n\tbuffer_load_dword %1, %2, 0 offen lds"
+               :: "s"(lds_addr), "v"(voff), "s"(r.w) : "memory", "m0");
+}
+
+// s_waitcnt immediate: vmcnt = v (0..63), expcnt and lgkmcnt = 0.
+constexpr int waitcnt_vm_lgkm0(int v) { return (v & 0xF) | ((v >> 4) << 14) | (0x0 << 4) | (0x0 << 8); }
+
 }  // namespace

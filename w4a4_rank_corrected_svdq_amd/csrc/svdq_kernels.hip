@@ -216,24 +216,22 @@ __global__ __launch_bounds__(k1_waves<NT>() * 64) void k_quant_act_lora_down(
 // Kernel 2
 // =====================================================================
 // Block tile 128 x 128, 4 waves in a 2 x 2 arrangement; each wave owns
-// 64 x 64 outputs = 2 x 2 tiles of 32 x 32.  Each tile is computed
+// 64 x 64 outputs = 4 x 4 tiles of 16 x 16.  Each tile is computed
 // transposed, Y^T = W^T X^T: the weight fragment is the MFMA A operand and
-// the activation fragment the B operand, so in the 32x32 result layout a lane
-// holds one output row and runs of four consecutive output columns, which
-// the epilogue stores as 8-byte bf16 chunks.  One group of 64 k is two
-// v_mfma_i32_32x32x32_i8 per tile (the 32x32 form sustains ~1.4x the int8
-// rate of the 16x16x64 form on gfx950).  The K loop runs in stages of two
-// groups: a stage is loaded from HBM as packed nibbles into registers one
-// stage ahead, unpacked cooperatively (once per block) and written to a
-// double-buffered LDS tile as int8 operands, so the waves read ready MFMA
-// fragments with one 16-byte LDS read each.  Two blocks share a CU, so one
-// block's barrier and load waits overlap the other's compute.
+// the activation fragment the B operand, so a lane holds one output row and
+// runs of four consecutive output columns, which the epilogue stores as
+// 8-byte bf16 chunks.  One group of 64 k is one v_mfma_i32_16x16x64_i8 per
+// tile.  The K loop runs in stages of two groups: a stage is loaded from HBM
+// as packed nibbles into registers one stage ahead, unpacked cooperatively
+// (once per block) and written to a double-buffered LDS tile as int8
+// operands, so the waves read ready MFMA fragments with one 16-byte LDS read
+// each.  Two blocks share a CU, so one block's barrier and load waits
+// overlap the other's compute.
 //
-// 32x32 MFMA layouts (wave64): A operand lane l holds row l % 32 and one K
-// slice chosen by l / 32; B operand lane l holds column l % 32 and the same
-// slice; C/D lane l holds column l % 32, rows 8b + 4(l / 32) + i in register
-// 4b + i (b, i = 0..3).  Here D rows are output columns n, D columns are
-// output rows m.
+// 16x16x64 layouts (wave64): A operand lane l holds row l % 16 and the
+// 16-k slice l / 16; B operand lane l holds column l % 16 and the same
+// slice; C/D lane l holds column l % 16, rows 4 (l / 16) + e in register e.
+// Here D rows are output columns n, D columns are output rows m.
 //
 // Unpacking: a packed dword holds 8 codes (byte j = code 2j low, 2j+1 high).
 // (w << 4) & 0xF0F0F0F0 puts the even codes in the high nibble of each byte
@@ -241,23 +239,30 @@ __global__ __launch_bounds__(k1_waves<NT>() * 64) void k_quant_act_lora_down(
 // equals 16 * q with no sign extension; the product is 256 * P_g.  A and B
 // use the same order of k inside the group, which the product ignores.
 //
-// Dequantization: the first MFMA of a group takes the constant 0x4B400000
-// (the bit pattern of 1.5 * 2^23) as its C operand and the second chains on
-// it.  |256 * P_g| <= 2^20 < 2^22, so the int32 result read as fp32 is
-// exactly 1.5 * 2^23 + 256 * P_g.  With a = s_x / 256 and
-// b = -1.5 * 2^23 * a (both exact in fp32, kept per output row in LDS),
-// fma(D, a, b) = s_x * P_g exactly (11 + 13 significant bits), and
-// acc = fma(that, s_w, acc) adds the group with one rounding of
-// s_x s_w P_g + acc.
+// Dequantization: every group's MFMA takes the constant 0x4B400000 (the bit
+// pattern of 1.5 * 2^23) as its C operand.  |256 * P_g| <= 2^20 < 2^22, so
+// the int32 result read as fp32 is exactly 1.5 * 2^23 + 256 * P_g.  With
+// a = s_x / 256 and b = -1.5 * 2^23 * a (both exact in fp32, kept per output
+// row in LDS), fma(D, a, b) = s_x * P_g exactly (11 + 13 significant bits),
+// and acc = fma(that, s_w, acc) adds the group with one rounding of
+// s_x s_w P_g + acc.  Both are plain fp32 FMAs, which gfx950 issues at twice
+// the rate of the mixed-precision form; the weight scales are therefore kept
+// as fp32 in LDS (four consecutive columns per 16-byte read).
+//
+// Schedule: per group the 16 tiles run in a fixed order, and a tile is
+// dequantized two tiles after its MFMA was issued (results in a ring of
+// four), so the VALU never waits out an MFMA's latency; the second group's
+// fragments are read from LDS while the first group computes.  On gfx950 an
+// int8 MFMA and fp32 VALU work of the same SIMD do not run concurrently
+// (measured: their times add, also with independent operands, at 2 and 4
+// waves per SIMD), so the kernel's floor is the MFMA time plus two FMAs per
+// output and group.
 //
 // LDS layout of an unpacked operand row: 64 bytes per group = four 16-byte
 // chunks, chunk c holding k slice c (16 codes).  Chunk c of row r is stored
-// at position c ^ (((r >> 1) ^ (r >> 3)) & 3): 16-byte reads of 16
-// consecutive rows and the loader's writes then touch every bank once per
-// pass, for 32- and 64-bank LDS alike.  Weight scales are stored per 32-
-// column tile in the order a lane consumes them (columns 8b + 4h + i at
-// position 16h + 4b + i), so a lane fetches its 16 scales with two 16-byte
-// reads.
+// at position c ^ (((r >> 1) ^ (r >> 3)) & 3), which spreads the loader's
+// row-wise writes over the banks; a fragment read (16 consecutive rows, all
+// four chunks) covers one contiguous kilobyte either way.
 constexpr int K2_BM = 128;
 constexpr int K2_BN = 128;
 constexpr int K2_SG = 2;                      // groups per pipeline stage
@@ -265,8 +270,9 @@ constexpr int K2_WAVES = 4;
 constexpr int K2_THREADS = K2_WAVES * 64;
 constexpr int K2_WM = 64;                     // wave tile rows (m)
 constexpr int K2_WN = 64;                     // wave tile columns (n)
-constexpr int K2_TI = K2_WM / 32;             // 32x32 tiles per wave along M
-constexpr int K2_TJ = K2_WN / 32;             // along N
+constexpr int K2_TB = K2_WM / 16;             // 16-row activation tiles per wave (m)
+constexpr int K2_TA = K2_WN / 16;             // 16-column weight tiles per wave (n)
+constexpr int K2_NTILE = K2_TA * K2_TB;
 constexpr int MAGIC_I = 0x4B400000;
 constexpr float MAGIC_F = 12582912.0f;         // 1.5 * 2^23
 
@@ -275,16 +281,10 @@ struct K2Smem {
   uint4 a[2][K2_SG][K2_BM][4];                 // unpacked activations, 16 B chunks
   uint4 b[2][K2_SG][K2_BN][4];                 // unpacked weights
   float2 xc[2][K2_SG][K2_BM];                  // (s_x / 256, -1.5*2^23 * s_x / 256) per row
-  _Float16 sw[2][K2_SG][K2_BN];                // weight scales, per 32-column tile in lane order
+  float sw[2][K2_SG][K2_BN];                   // weight scales (fp32) per column
 };
 
 __device__ __forceinline__ int k2_swz(int row, int chunk) { return chunk ^ (((row >> 1) ^ (row >> 3)) & 3); }
-
-// position of column c's weight scale inside its 32-column tile (lane order)
-__device__ __forceinline__ int k2_swpos(int c) {
-  const int cc = c & 31;
-  return (c & ~31) | (((cc >> 2) & 1) << 4) | ((cc >> 3) << 2) | (cc & 3);
-}
 
 __device__ __forceinline__ uint4 unpack_lo(uint4 w) {  // codes 0..15 of a 32-code chunk
   return make_uint4((w.x << 4) & 0xF0F0F0F0u, w.x & 0xF0F0F0F0u, (w.y << 4) & 0xF0F0F0F0u, w.y & 0xF0F0F0F0u);
@@ -303,6 +303,171 @@ struct QkvArgs {
   float eps;
 };
 constexpr int QKV_HEAD = 128;
+
+// Epilogue of kernel 2: up projection, bias, fused QKV normalization and
+// rotation, store.  acc[a][b][e] holds output row
+// m0 + wm*64 + 16b + (lane & 15), column n0 + wn*64 + 16a + 4(lane >> 4) + e.
+// All threads of the block call it (the QKV form has a barrier); the LDS
+// passed in is free.
+template <int OUT_F32, int NT, int EPI>
+__device__ __forceinline__ void k2_epilogue(v4f (&acc)[K2_TA][K2_TB], unsigned char* k2_smem_raw, int m0, int n0,
+                                            const float* __restrict__ lora_act,
+                                            const uint16_t* __restrict__ lora_up,
+                                            const uint16_t* __restrict__ bias, int M, int N, int rank,
+                                            void* __restrict__ y, const QkvArgs& qa) {
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int wm = wave >> 1, wn = wave & 1;
+  const int lr = lane & 15, lq = lane >> 4;
+  // ---- epilogue: up projection (bf16 MFMA 16x16x32, K = rank in slices of
+  // 32; ranks are multiples of 16, so the lanes of a slice past the rank
+  // load zeros), transposed like the main product: lora_up rows are the A
+  // operand, lora_act rows the B operand.
+  if constexpr (NT > 0) {
+    for (int kk = 0; kk < rank; kk += 32) {
+      const int kl = kk + lq * 8;          // this lane's 8 k values
+      const bool kin = kl < rank;
+      v8bf la[K2_TB];
+#pragma unroll
+      for (int b = 0; b < K2_TB; ++b) {
+        const int r = m0 + wm * K2_WM + b * 16 + lr;
+        float v[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+        if (kin && r < M) {
+          const float4* p = reinterpret_cast<const float4*>(lora_act + static_cast<size_t>(r) * rank + kl);
+          const float4 v0 = p[0], v1 = p[1];
+          v[0] = v0.x; v[1] = v0.y; v[2] = v0.z; v[3] = v0.w;
+          v[4] = v1.x; v[5] = v1.y; v[6] = v1.z; v[7] = v1.w;
+        }
+        la[b] = pack_bf16x8(v);
+      }
+#pragma unroll
+      for (int a = 0; a < K2_TA; ++a) {
+        const int c = n0 + wn * K2_WN + a * 16 + lr;
+        uint4 u = make_uint4(0, 0, 0, 0);
+        if (kin && c < N) u = *reinterpret_cast<const uint4*>(lora_up + static_cast<size_t>(c) * rank + kl);
+        const v8bf ub = __builtin_bit_cast(v8bf, u);
+#pragma unroll
+        for (int b = 0; b < K2_TB; ++b)
+          acc[a][b] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ub, la[b], acc[a][b], 0, 0, 0);
+      }
+    }
+  }
+
+  // ---- bias, then (fused QKV only) per-head RMSNorm and rotary embedding
+  // of the Q and K heads.  A lane holds output rows m0 + wm*64 + 16b + lr
+  // and, in each 16-column tile a, columns 16a + 4lq + (0..3).
+  if (bias) {
+#pragma unroll
+    for (int a = 0; a < K2_TA; ++a) {
+      const int c = n0 + wn * K2_WN + a * 16 + 4 * lq;   // N % 8 == 0: all four in or out
+      if (c >= N) continue;
+      const uint2 bv = *reinterpret_cast<const uint2*>(bias + c);
+      const float b4[4] = {bf16_bits_to_f32(bv.x & 0xFFFFu), bf16_bits_to_f32(bv.x >> 16),
+                           bf16_bits_to_f32(bv.y & 0xFFFFu), bf16_bits_to_f32(bv.y >> 16)};
+#pragma unroll
+      for (int b = 0; b < K2_TB; ++b)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) acc[a][b][e] += b4[e];
+    }
+  }
+  if constexpr (EPI == 1) {
+    // The block's 128 columns are one head (N = 3 * heads * 128, block tiles
+    // aligned to heads).  Q heads come first, then K heads, then V heads,
+    // which are left as projected.  This condition is uniform per block.
+    const int HD = N / 3;
+    if (n0 < 2 * HD) {
+      const uint16_t* g = n0 < HD ? qa.gq : qa.gk;
+      // sum of squares of each row over the head: this lane's 16 columns,
+      // the other three lane quads' 48 (lane ^ 16, lane ^ 32), the other
+      // wave's 64 via LDS
+      float* red = reinterpret_cast<float*>(k2_smem_raw + K2_WAVES * K2_WM * K2_WN * 2);
+#pragma unroll
+      for (int b = 0; b < K2_TB; ++b) {
+        float t = 0.f;
+#pragma unroll
+        for (int a = 0; a < K2_TA; ++a)
+#pragma unroll
+          for (int e = 0; e < 4; ++e) t = fmaf(acc[a][b][e], acc[a][b][e], t);
+        t += __shfl_xor(t, 16);
+        t += __shfl_xor(t, 32);
+        if (lq == 0) red[((wm * K2_TB + b) * 2 + wn) * 16 + lr] = t;
+      }
+      __syncthreads();
+#pragma unroll
+      for (int b = 0; b < K2_TB; ++b) {
+        const float tot = red[((wm * K2_TB + b) * 2 + 0) * 16 + lr] + red[((wm * K2_TB + b) * 2 + 1) * 16 + lr];
+        const float scale = 1.0f / sqrtf(tot * (1.0f / QKV_HEAD) + qa.eps);
+        const int row = m0 + wm * K2_WM + b * 16 + lr;
+        const bool rot = qa.cos != nullptr && row < M;
+#pragma unroll
+        for (int a = 0; a < K2_TA; ++a) {
+          const int ch = wn * K2_WN + a * 16 + 4 * lq;        // column within the head
+          const uint2 gv = *reinterpret_cast<const uint2*>(g + ch);
+          const float g4[4] = {bf16_bits_to_f32(gv.x & 0xFFFFu), bf16_bits_to_f32(gv.x >> 16),
+                               bf16_bits_to_f32(gv.y & 0xFFFFu), bf16_bits_to_f32(gv.y >> 16)};
+          float o[4];
+#pragma unroll
+          for (int e = 0; e < 4; ++e) o[e] = acc[a][b][e] * scale * g4[e];
+          if (rot) {
+            const float2 cs = *reinterpret_cast<const float2*>(qa.cos + static_cast<size_t>(row) * 64 + (ch >> 1));
+            const float2 sn = *reinterpret_cast<const float2*>(qa.sin + static_cast<size_t>(row) * 64 + (ch >> 1));
+            const float a0 = o[0] * cs.x - o[1] * sn.x, a1 = o[1] * cs.x + o[0] * sn.x;
+            const float a2 = o[2] * cs.y - o[3] * sn.y, a3 = o[3] * cs.y + o[2] * sn.y;
+            o[0] = a0; o[1] = a1; o[2] = a2; o[3] = a3;
+          }
+#pragma unroll
+          for (int e = 0; e < 4; ++e) acc[a][b][e] = o[e];
+        }
+      }
+    }
+  }
+
+  // ---- store.  bf16 output goes through LDS (free after the K loop's last
+  // barrier): each wave writes its 64 x 64 tile with 8-byte writes, then
+  // stores whole 128-byte row segments, eight rows per instruction.
+  // 16-byte chunk c of tile row r sits at chunk c ^ (r & 7).
+  if (OUT_F32) {
+#pragma unroll
+    for (int b = 0; b < K2_TB; ++b) {
+      const int row = m0 + wm * K2_WM + b * 16 + lr;
+      if (row >= M) continue;
+#pragma unroll
+      for (int a = 0; a < K2_TA; ++a) {
+        const int c = n0 + wn * K2_WN + a * 16 + 4 * lq;
+        if (c >= N) continue;
+        *reinterpret_cast<float4*>(reinterpret_cast<float*>(y) + static_cast<size_t>(row) * N + c) =
+            make_float4(acc[a][b][0], acc[a][b][1], acc[a][b][2], acc[a][b][3]);
+      }
+    }
+  } else {
+    uint2* tile = reinterpret_cast<uint2*>(k2_smem_raw) + wave * (K2_WM * K2_WN / 4);  // 64 x 64 bf16
+#pragma unroll
+    for (int b = 0; b < K2_TB; ++b) {
+      const int rl = b * 16 + lr;
+#pragma unroll
+      for (int a = 0; a < K2_TA; ++a) {
+        const int chunk = 2 * a + (lq >> 1);          // 16-byte chunk of the 128-byte tile row
+        tile[rl * 16 + ((chunk ^ (rl & 7)) << 1) + (lq & 1)] =
+            make_uint2(f32_to_bf16_bits(acc[a][b][0]) | (f32_to_bf16_bits(acc[a][b][1]) << 16),
+                       f32_to_bf16_bits(acc[a][b][2]) | (f32_to_bf16_bits(acc[a][b][3]) << 16));
+      }
+    }
+    // the reads below are of another type than the writes above: keep the
+    // compiler from moving them across (the hardware orders one wave's LDS ops)
+    asm volatile("" ::: "memory");
+    const uint4* tile4 = reinterpret_cast<const uint4*>(tile);
+    const int cl = lane & 7;                            // 16-byte chunk this lane stores
+    const int col = n0 + wn * K2_WN + cl * 8;
+#pragma unroll
+    for (int it = 0; it < K2_WM / 8; ++it) {
+      const int rl = it * 8 + (lane >> 3);
+      const uint4 v = tile4[rl * 8 + (cl ^ (rl & 7))];
+      const int row = m0 + wm * K2_WM + rl;
+      if (row < M && col < N)
+        *reinterpret_cast<uint4*>(reinterpret_cast<uint16_t*>(y) + static_cast<size_t>(row) * N + col) = v;
+    }
+  }}
 
 template <int OUT_F32, int NT, int EPI>
 __global__ __launch_bounds__(K2_THREADS, 2) void k_gemm_w4a4_lora_up(
@@ -330,9 +495,10 @@ __global__ __launch_bounds__(K2_THREADS, 2) void k_gemm_w4a4_lora_up(
   // activations and for the weights, plus that row's x scale and that
   // column's w scale.  Loads go through buffer resources sized to the
   // operand, so rows past M or N read as zero; the byte offset is pushed
-  // out of range for groups past G.  Wave-uniform roles come from the wave
-  // index.
+  // out of range for groups past G (and for the stage after the last), so
+  // such a group has zero codes and zero scales and adds exactly zero.
   const int l_r = tid & 127, l_g = (wave >> 1) & 1;
+  constexpr uint32_t OOB = 0x80000000u;
   const __amdgpu_buffer_rsrc_t a_rs = __builtin_amdgcn_make_buffer_rsrc(
       const_cast<uint8_t*>(x_codes), 0, static_cast<int>(static_cast<size_t>(M) * Kb), 0x00020000);
   const __amdgpu_buffer_rsrc_t b_rs = __builtin_amdgcn_make_buffer_rsrc(
@@ -341,27 +507,28 @@ __global__ __launch_bounds__(K2_THREADS, 2) void k_gemm_w4a4_lora_up(
       const_cast<_Float16*>(x_scales), 0, static_cast<int>(static_cast<size_t>(G) * M * 2), 0x00020000);
   const __amdgpu_buffer_rsrc_t sw_rs = __builtin_amdgcn_make_buffer_rsrc(
       const_cast<_Float16*>(w_scales), 0, static_cast<int>(static_cast<size_t>(G) * N * 2), 0x00020000);
+  // Per-lane byte offsets of stage 0 (2^31 for a scale row past M or N);
+  // a stage adds a wave-uniform amount, and a group past G loads from
+  // offset 2^31, past every buffer, which returns zeros.
   const uint32_t a_off0 = static_cast<uint32_t>((m0 + l_r) * Kb + l_g * 32);
   const uint32_t b_off0 = static_cast<uint32_t>((n0 + l_r) * Kb + l_g * 32);
-  const bool sx_row_ok = (m0 + l_r) < M;
-  const bool sw_row_ok = (n0 + l_r) < N;
-  const uint32_t sx_off0 = static_cast<uint32_t>(2 * (l_g * M + m0 + l_r));
-  const uint32_t sw_off0 = static_cast<uint32_t>(2 * (l_g * N + n0 + l_r));
-  constexpr uint32_t OOB = 0x80000000u;
+  const uint32_t sx_off0 = (m0 + l_r) < M ? static_cast<uint32_t>(2 * (l_g * M + m0 + l_r)) : OOB;
+  const uint32_t sw_off0 = (n0 + l_r) < N ? static_cast<uint32_t>(2 * (l_g * N + n0 + l_r)) : OOB;
 
   uint4 ra0, ra1, rb0, rb1;
   _Float16 rsx, rsw;
   auto load_stage = [&](int st) {
+    const bool gok = st * K2_SG + l_g < G;     // wave-uniform
     const uint32_t ko = static_cast<uint32_t>(st) * (K2_SG * 32);
-    const bool gok = st * K2_SG + l_g < G;
-    ra0 = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(a_rs, gok ? a_off0 + ko : OOB, 0, 0));
-    ra1 = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(a_rs, gok ? a_off0 + ko + 16 : OOB, 0, 0));
-    rb0 = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(b_rs, gok ? b_off0 + ko : OOB, 0, 0));
-    rb1 = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(b_rs, gok ? b_off0 + ko + 16 : OOB, 0, 0));
-    rsx = __builtin_bit_cast(_Float16, __builtin_amdgcn_raw_buffer_load_b16(
-        sx_rs, (gok && sx_row_ok) ? sx_off0 + static_cast<uint32_t>(st) * (2 * K2_SG * M) : OOB, 0, 0));
-    rsw = __builtin_bit_cast(_Float16, __builtin_amdgcn_raw_buffer_load_b16(
-        sw_rs, (gok && sw_row_ok) ? sw_off0 + static_cast<uint32_t>(st) * (2 * K2_SG * N) : OOB, 0, 0));
+    const uint32_t ao = gok ? a_off0 + ko : OOB, bo = gok ? b_off0 + ko : OOB;
+    const uint32_t xo = (gok && sx_off0 != OOB) ? sx_off0 + static_cast<uint32_t>(st) * (2 * K2_SG * M) : OOB;
+    const uint32_t wo = (gok && sw_off0 != OOB) ? sw_off0 + static_cast<uint32_t>(st) * (2 * K2_SG * N) : OOB;
+    ra0 = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(a_rs, ao, 0, 0));
+    ra1 = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(a_rs, ao + 16, 0, 0));
+    rb0 = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(b_rs, bo, 0, 0));
+    rb1 = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(b_rs, bo + 16, 0, 0));
+    rsx = __builtin_bit_cast(_Float16, __builtin_amdgcn_raw_buffer_load_b16(sx_rs, xo, 0, 0));
+    rsw = __builtin_bit_cast(_Float16, __builtin_amdgcn_raw_buffer_load_b16(sw_rs, wo, 0, 0));
   };
   auto store_stage = [&](int buf) {
     sm.a[buf][l_g][l_r][k2_swz(l_r, 0)] = unpack_lo(ra0);
@@ -374,252 +541,106 @@ __global__ __launch_bounds__(K2_THREADS, 2) void k_gemm_w4a4_lora_up(
     sm.b[buf][l_g][l_r][k2_swz(l_r, 3)] = unpack_hi(rb1);
     const float ax = static_cast<float>(rsx) * (1.0f / 256.0f);
     sm.xc[buf][l_g][l_r] = make_float2(ax, -MAGIC_F * ax);
-    sm.sw[buf][l_g][k2_swpos(l_r)] = rsw;
+    sm.sw[buf][l_g][l_r] = static_cast<float>(rsw);
   };
 
-  v16f acc[K2_TI][K2_TJ];
+  v4f acc[K2_TA][K2_TB];
 #pragma unroll
-  for (int i = 0; i < K2_TI; ++i)
+  for (int a = 0; a < K2_TA; ++a)
 #pragma unroll
-    for (int j = 0; j < K2_TJ; ++j)
-#pragma unroll
-      for (int v = 0; v < 16; ++v) acc[i][j][v] = 0.f;
+    for (int b = 0; b < K2_TB; ++b) acc[a][b] = v4f{0.f, 0.f, 0.f, 0.f};
 
-  v16i cmagic;
-#pragma unroll
-  for (int v = 0; v < 16; ++v) cmagic[v] = MAGIC_I;
-  // opaque to the optimizer: kept in 16 VGPRs instead of being rebuilt from
+  v4i cmagic = v4i{MAGIC_I, MAGIC_I, MAGIC_I, MAGIC_I};
+  // opaque to the optimizer: kept in 4 VGPRs instead of being rebuilt from
   // scalar constants before every MFMA that reads it
   asm volatile("" : "+v"(cmagic));
-  const int fr = lane & 31;      // fragment row / column within a 32-tile
-  const int fk = lane >> 5;      // K slice within a 32-k half
+  const int lr = lane & 15;      // fragment row / output column within a 16-tile
+  const int lq = lane >> 4;      // k slice / output row quad
+
+  // Fragments and scales of one group, read from LDS: the lane's weight
+  // rows (n) wn*64 + 16a + lr, activation rows (m) wm*64 + 16b + lr, the
+  // activation scale pairs of those rows and the weight scales of the four
+  // output columns 16a + 4lq .. +3 it accumulates.
+  struct Frags {
+    v4i w[K2_TA];
+    v4i x[K2_TB];
+    float2 xc[K2_TB];
+    float4 sw[K2_TA];
+  };
+  auto read_frags = [&](int buf, int gi, Frags& f) {
+#pragma unroll
+    for (int a = 0; a < K2_TA; ++a) {
+      const int c = wn * K2_WN + a * 16 + lr;
+      f.w[a] = __builtin_bit_cast(v4i, sm.b[buf][gi][c][k2_swz(c, lq)]);
+    }
+#pragma unroll
+    for (int b = 0; b < K2_TB; ++b) {
+      const int r = wm * K2_WM + b * 16 + lr;
+      f.x[b] = __builtin_bit_cast(v4i, sm.a[buf][gi][r][k2_swz(r, lq)]);
+    }
+#pragma unroll
+    for (int b = 0; b < K2_TB; ++b) f.xc[b] = sm.xc[buf][gi][wm * K2_WM + b * 16 + lr];
+#pragma unroll
+    for (int a = 0; a < K2_TA; ++a)
+      f.sw[a] = *reinterpret_cast<const float4*>(&sm.sw[buf][gi][wn * K2_WN + a * 16 + 4 * lq]);
+  };
+  // acc += s_w * (s_x * P): two fp32 FMAs per output
+  auto deq = [&](float2 xc, float4 sw, const v4i& d, v4f& ac) {
+    const float s4[4] = {sw.x, sw.y, sw.z, sw.w};
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const float tv = __builtin_fmaf(__int_as_float(d[e]), xc.x, xc.y);
+      ac[e] = __builtin_fmaf(tv, s4[e], ac[e]);
+    }
+  };
 
   load_stage(0);
   store_stage(0);
   __syncthreads();
 
+  static_assert(K2_SG == 2, "the stage body below holds two groups");
+  // Tiles t = 0 .. 31 of a stage (group t / 16, weight tile (t % 16) / 4,
+  // activation tile t % 4): the MFMA of tile t is issued, then tile t - 2 is
+  // dequantized; results rotate through a ring of four, so the last two
+  // tiles of a stage are dequantized at the start of the next one, after
+  // the barrier, while the new fragments are still in flight.  Before the
+  // first stage the pending tiles are zero contributions (scale pair 0, 0
+  // maps the magic constant to exactly 0).
+  constexpr int LAG = 2, RING = 4;
+  static_assert((2 * K2_NTILE) % RING == 0, "ring slots repeat per stage");
+  Frags f0, f1;
+  read_frags(0, 0, f0);
+#pragma unroll
+  for (int b = 0; b < K2_TB; ++b) f1.xc[b] = make_float2(0.f, 0.f);
+#pragma unroll
+  for (int a = 0; a < K2_TA; ++a) f1.sw[a] = make_float4(0.f, 0.f, 0.f, 0.f);
+  v4i dr[RING];
+#pragma unroll
+  for (int i = 0; i < RING; ++i) dr[i] = cmagic;
+  auto deq_tile = [&](int q) {                 // q in 0 .. 31 of the stage whose fragments f0 / f1 hold
+    const int u = q % K2_NTILE, a = u / K2_TB, b = u % K2_TB;
+    const Frags& f = q < K2_NTILE ? f0 : f1;
+    deq(f.xc[b], f.sw[a], dr[q % RING], acc[a][b]);
+  };
   for (int st = 0; st < S; ++st) {
     const int buf = st & 1;
-    const bool more = (st + 1) < S;
-    if (more) load_stage(st + 1);
-
+    load_stage(st + 1);
 #pragma unroll
-    for (int gi = 0; gi < K2_SG; ++gi) {
-      if (st * K2_SG + gi >= G) break;
-      v4i xf[K2_TI][2], wf[K2_TJ][2];
-#pragma unroll
-      for (int i = 0; i < K2_TI; ++i) {
-        const int r = wm * K2_WM + i * 32 + fr;
-        xf[i][0] = __builtin_bit_cast(v4i, sm.a[buf][gi][r][k2_swz(r, fk)]);
-        xf[i][1] = __builtin_bit_cast(v4i, sm.a[buf][gi][r][k2_swz(r, 2 + fk)]);
-      }
-#pragma unroll
-      for (int j = 0; j < K2_TJ; ++j) {
-        const int c = wn * K2_WN + j * 32 + fr;
-        wf[j][0] = __builtin_bit_cast(v4i, sm.b[buf][gi][c][k2_swz(c, fk)]);
-        wf[j][1] = __builtin_bit_cast(v4i, sm.b[buf][gi][c][k2_swz(c, 2 + fk)]);
-      }
-      float2 xci[K2_TI];
-#pragma unroll
-      for (int i = 0; i < K2_TI; ++i) xci[i] = sm.xc[buf][gi][wm * K2_WM + i * 32 + fr];
-      // this lane's 16 weight scales per column tile: positions 16 fk .. 16 fk + 15
-      uint4 swr[K2_TJ][2];
-#pragma unroll
-      for (int j = 0; j < K2_TJ; ++j) {
-        const uint4* p = reinterpret_cast<const uint4*>(&sm.sw[buf][gi][wn * K2_WN + j * 32 + 16 * fk]);
-        swr[j][0] = p[0];
-        swr[j][1] = p[1];
-      }
-      v16i d[K2_TI][K2_TJ];
-#pragma unroll
-      for (int i = 0; i < K2_TI; ++i)
-#pragma unroll
-        for (int j = 0; j < K2_TJ; ++j)
-          d[i][j] = __builtin_amdgcn_mfma_i32_32x32x32_i8(wf[j][0], xf[i][0], cmagic, 0, 0, 0);
-#pragma unroll
-      for (int i = 0; i < K2_TI; ++i)
-#pragma unroll
-        for (int j = 0; j < K2_TJ; ++j)
-          d[i][j] = __builtin_amdgcn_mfma_i32_32x32x32_i8(wf[j][1], xf[i][1], d[i][j], 0, 0, 0);
-#pragma unroll
-      for (int i = 0; i < K2_TI; ++i) {
-#pragma unroll
-        for (int j = 0; j < K2_TJ; ++j) {
-          const _Float16* sh = reinterpret_cast<const _Float16*>(&swr[j][0]);
-#pragma unroll
-          for (int v = 0; v < 16; ++v) {
-            const float tv = __builtin_fmaf(__int_as_float(d[i][j][v]), xci[i].x, xci[i].y);
-            acc[i][j][v] = __builtin_fmaf(tv, static_cast<float>(sh[v]), acc[i][j][v]);
-          }
-        }
-      }
+    for (int t = 0; t < 2 * K2_NTILE; ++t) {
+      const int u = t % K2_NTILE, a = u / K2_TB, b = u % K2_TB;
+      const Frags& f = t < K2_NTILE ? f0 : f1;
+      dr[t % RING] = __builtin_amdgcn_mfma_i32_16x16x64_i8(f.w[a], f.x[b], cmagic, 0, 0, 0);
+      deq_tile(t >= LAG ? t - LAG : 2 * K2_NTILE - LAG + t);   // t < LAG: the previous stage's last tiles
+      if (t == LAG) read_frags(buf, 1, f1);
     }
-
-    if (more) store_stage(buf ^ 1);
+    store_stage(buf ^ 1);
     __syncthreads();
+    read_frags(buf ^ 1, 0, f0);
   }
+#pragma unroll
+  for (int q = 2 * K2_NTILE - LAG; q < 2 * K2_NTILE; ++q) deq_tile(q);
 
-  // ---- epilogue: up projection (bf16 MFMA 32x32x16, K = rank in slices of
-  // 16), transposed like the main product: lora_up rows are the A operand,
-  // lora_act rows the B operand.
-  if constexpr (NT > 0) {
-    for (int kk = 0; kk < rank; kk += 16) {
-      const int kl = kk + fk * 8;          // this lane's 8 k values
-      v8bf la[K2_TI];
-#pragma unroll
-      for (int i = 0; i < K2_TI; ++i) {
-        const int r = m0 + wm * K2_WM + i * 32 + fr;
-        float v[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
-        if (r < M) {
-          const float4* p = reinterpret_cast<const float4*>(lora_act + static_cast<size_t>(r) * rank + kl);
-          const float4 v0 = p[0], v1 = p[1];
-          v[0] = v0.x; v[1] = v0.y; v[2] = v0.z; v[3] = v0.w;
-          v[4] = v1.x; v[5] = v1.y; v[6] = v1.z; v[7] = v1.w;
-        }
-        la[i] = pack_bf16x8(v);
-      }
-#pragma unroll
-      for (int j = 0; j < K2_TJ; ++j) {
-        const int c = n0 + wn * K2_WN + j * 32 + fr;
-        uint4 u = make_uint4(0, 0, 0, 0);
-        if (c < N) u = *reinterpret_cast<const uint4*>(lora_up + static_cast<size_t>(c) * rank + kl);
-        const v8bf ub = __builtin_bit_cast(v8bf, u);
-#pragma unroll
-        for (int i = 0; i < K2_TI; ++i)
-          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ub, la[i], acc[i][j], 0, 0, 0);
-      }
-    }
-  }
-
-  // ---- bias, then (fused QKV only) per-head RMSNorm and rotary embedding
-  // of the Q and K heads.  A lane holds output row m and columns
-  // 8b + 4 fk + (0..3) of each 32-column tile.
-  if (bias) {
-#pragma unroll
-    for (int j = 0; j < K2_TJ; ++j) {
-#pragma unroll
-      for (int bb = 0; bb < 4; ++bb) {
-        const int c = n0 + wn * K2_WN + j * 32 + 8 * bb + 4 * fk;   // N % 8 == 0: all four in or out
-        if (c >= N) continue;
-        const uint2 bv = *reinterpret_cast<const uint2*>(bias + c);
-        const float b4[4] = {bf16_bits_to_f32(bv.x & 0xFFFFu), bf16_bits_to_f32(bv.x >> 16),
-                             bf16_bits_to_f32(bv.y & 0xFFFFu), bf16_bits_to_f32(bv.y >> 16)};
-#pragma unroll
-        for (int i = 0; i < K2_TI; ++i)
-#pragma unroll
-          for (int e = 0; e < 4; ++e) acc[i][j][4 * bb + e] += b4[e];
-      }
-    }
-  }
-  if constexpr (EPI == 1) {
-    // The block's 128 columns are one head (N = 3 * heads * 128, block tiles
-    // aligned to heads).  Q heads come first, then K heads, then V heads,
-    // which are left as projected.  This condition is uniform per block.
-    const int HD = N / 3;
-    if (n0 < 2 * HD) {
-      const uint16_t* g = n0 < HD ? qa.gq : qa.gk;
-      // sum of squares of each row over the head: this lane's 32 columns,
-      // the partner lane's other 32 (lane ^ 32), the other wave's 64 via LDS
-      float* red = reinterpret_cast<float*>(k2_smem_raw + K2_WAVES * K2_WM * K2_WN * 2);
-      float ss[K2_TI];
-#pragma unroll
-      for (int i = 0; i < K2_TI; ++i) {
-        float t = 0.f;
-#pragma unroll
-        for (int j = 0; j < K2_TJ; ++j)
-#pragma unroll
-          for (int v = 0; v < 16; ++v) t = fmaf(acc[i][j][v], acc[i][j][v], t);
-        ss[i] = t + __shfl_xor(t, 32);
-        if (fk == 0) red[((wm * K2_TI + i) * 2 + wn) * 32 + fr] = ss[i];
-      }
-      __syncthreads();
-#pragma unroll
-      for (int i = 0; i < K2_TI; ++i) {
-        const float tot = red[((wm * K2_TI + i) * 2 + 0) * 32 + fr] + red[((wm * K2_TI + i) * 2 + 1) * 32 + fr];
-        const float scale = 1.0f / sqrtf(tot * (1.0f / QKV_HEAD) + qa.eps);
-        const int row = m0 + wm * K2_WM + i * 32 + fr;
-        const bool rot = qa.cos != nullptr && row < M;
-#pragma unroll
-        for (int j = 0; j < K2_TJ; ++j) {
-#pragma unroll
-          for (int bb = 0; bb < 4; ++bb) {
-            const int ch = wn * K2_WN + j * 32 + 8 * bb + 4 * fk;        // column within the head
-            const uint2 gv = *reinterpret_cast<const uint2*>(g + ch);
-            const float g4[4] = {bf16_bits_to_f32(gv.x & 0xFFFFu), bf16_bits_to_f32(gv.x >> 16),
-                                 bf16_bits_to_f32(gv.y & 0xFFFFu), bf16_bits_to_f32(gv.y >> 16)};
-            float o[4];
-#pragma unroll
-            for (int e = 0; e < 4; ++e) o[e] = acc[i][j][4 * bb + e] * scale * g4[e];
-            if (rot) {
-              const float2 cs = *reinterpret_cast<const float2*>(qa.cos + static_cast<size_t>(row) * 64 + (ch >> 1));
-              const float2 sn = *reinterpret_cast<const float2*>(qa.sin + static_cast<size_t>(row) * 64 + (ch >> 1));
-              const float a0 = o[0] * cs.x - o[1] * sn.x, a1 = o[1] * cs.x + o[0] * sn.x;
-              const float a2 = o[2] * cs.y - o[3] * sn.y, a3 = o[3] * cs.y + o[2] * sn.y;
-              o[0] = a0; o[1] = a1; o[2] = a2; o[3] = a3;
-            }
-#pragma unroll
-            for (int e = 0; e < 4; ++e) acc[i][j][4 * bb + e] = o[e];
-          }
-        }
-      }
-    }
-  }
-
-  // ---- store.  bf16 output goes through LDS (free after the K loop's last
-  // barrier): each wave writes its 64 x 64 tile with 8-byte writes, then
-  // stores whole 128-byte row segments, eight rows per instruction.
-  // 16-byte chunk c of tile row r sits at chunk c ^ (r & 7), which keeps
-  // both LDS passes free of bank conflicts.
-  if (OUT_F32) {
-#pragma unroll
-    for (int i = 0; i < K2_TI; ++i) {
-      const int row = m0 + wm * K2_WM + i * 32 + fr;
-      if (row >= M) continue;
-#pragma unroll
-      for (int j = 0; j < K2_TJ; ++j) {
-#pragma unroll
-        for (int bb = 0; bb < 4; ++bb) {
-          const int c = n0 + wn * K2_WN + j * 32 + 8 * bb + 4 * fk;
-          if (c >= N) continue;
-          *reinterpret_cast<float4*>(reinterpret_cast<float*>(y) + static_cast<size_t>(row) * N + c) =
-              make_float4(acc[i][j][4 * bb], acc[i][j][4 * bb + 1], acc[i][j][4 * bb + 2], acc[i][j][4 * bb + 3]);
-        }
-      }
-    }
-  } else {
-    uint2* tile = reinterpret_cast<uint2*>(k2_smem_raw) + wave * (K2_WM * K2_WN / 4);  // 64 x 64 bf16
-#pragma unroll
-    for (int i = 0; i < K2_TI; ++i) {
-      const int rl = i * 32 + fr;
-#pragma unroll
-      for (int j = 0; j < K2_TJ; ++j) {
-#pragma unroll
-        for (int bb = 0; bb < 4; ++bb) {
-          float o[4];
-#pragma unroll
-          for (int e = 0; e < 4; ++e) o[e] = acc[i][j][4 * bb + e];
-          const int chunk = j * 4 + bb;                 // 16-byte chunk of the 128-byte tile row
-          tile[rl * 16 + ((chunk ^ (rl & 7)) << 1) + fk] =
-              make_uint2(f32_to_bf16_bits(o[0]) | (f32_to_bf16_bits(o[1]) << 16),
-                         f32_to_bf16_bits(o[2]) | (f32_to_bf16_bits(o[3]) << 16));
-        }
-      }
-    }
-    // the reads below are of another type than the writes above: keep the
-    // compiler from moving them across (the hardware orders one wave's LDS ops)
-    asm volatile("" ::: "memory");
-    const uint4* tile4 = reinterpret_cast<const uint4*>(tile);
-    const int cl = lane & 7;                            // 16-byte chunk this lane stores
-    const int col = n0 + wn * K2_WN + cl * 8;
-#pragma unroll
-    for (int it = 0; it < K2_WM / 8; ++it) {
-      const int rl = it * 8 + (lane >> 3);
-      const uint4 v = tile4[rl * 8 + (cl ^ (rl & 7))];
-      const int row = m0 + wm * K2_WM + rl;
-      if (row < M && col < N)
-        *reinterpret_cast<uint4*>(reinterpret_cast<uint16_t*>(y) + static_cast<size_t>(row) * N + col) = v;
-    }
-  }
+  k2_epilogue<OUT_F32, NT, EPI>(acc, k2_smem_raw, m0, n0, lora_act, lora_up, bias, M, N, rank, y, qa);
 }
 
 template <int ACT, int NT, int QM>
@@ -724,8 +745,8 @@ __global__ __launch_bounds__(256) void k_lora_up_add(const float* __restrict__ l
 }
 
 // LDS: the stage buffers, and in the epilogue the four 64 x 64 bf16 output
-// tiles followed by the QKV epilogue's row sums (4 waves x 2 tiles x 32 rows).
-constexpr size_t K2_SMEM_EPI = static_cast<size_t>(K2_WAVES) * K2_WM * K2_WN * 2 + K2_WAVES * K2_TI * 32 * 4;
+// tiles followed by the QKV epilogue's row sums (4 waves x 4 tiles x 16 rows).
+constexpr size_t K2_SMEM_EPI = static_cast<size_t>(K2_WAVES) * K2_WM * K2_WN * 2 + K2_WAVES * K2_TB * 16 * 4;
 constexpr size_t K2_SMEM = sizeof(K2Smem) > K2_SMEM_EPI ? sizeof(K2Smem) : K2_SMEM_EPI;
 
 template <int OUT_F32, int NT, int EPI>

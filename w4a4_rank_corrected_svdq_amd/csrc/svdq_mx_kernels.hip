@@ -76,41 +76,6 @@ struct MxCfg {
 
 __device__ __forceinline__ int mx_swz(int row, int chunk) { return chunk ^ (((row >> 1) ^ (row >> 3)) & 3); }
 
-// Buffer descriptor (raw, stride 0) in four scalar registers: byte base,
-// size in bytes (accesses at or past it read zeros), default format word.
-struct MxRsrc {
-  v4i w;
-};
-__device__ __forceinline__ MxRsrc mx_rsrc(const void* base, uint32_t bytes) {
-  const uint64_t a = reinterpret_cast<uint64_t>(base);
-  MxRsrc r;
-  r.w[0] = __builtin_amdgcn_readfirstlane(static_cast<int>(a & 0xFFFFFFFFu));
-  r.w[1] = __builtin_amdgcn_readfirstlane(static_cast<int>((a >> 32) & 0xFFFFu));
-  r.w[2] = __builtin_amdgcn_readfirstlane(static_cast<int>(bytes));
-  r.w[3] = 0x00020000;
-  return r;
-}
-
-// LDS-DMA buffer loads: lane l's `size` bytes at byte offset voff of the
-// buffer land at LDS address lds_addr + size * l.  Issued from inline
-// assembly so that the compiler does not treat the pending LDS writes as
-// aliasing every later LDS read (it would wait for all of them); the kernel
-// waits for them itself with s_waitcnt vmcnt before the barrier that
-// publishes a stage.  s_nop 4 covers the wait states after M0 and scalar
-// register writes that a buffer load reading them needs.  No register is
-// written, so nothing stays in flight towards a register.
-__device__ __forceinline__ void mx_dma16(const MxRsrc& r, uint32_t lds_addr, uint32_t voff) {
-  asm volatile("s_mov_b32 m0, %0\n\ts_nop 4\n\tbuffer_load_dwordx4 %1, %2, 0 offen lds"
-               :: "s"(lds_addr), "v"(voff), "s"(r.w) : "memory", "m0");
-}
-__device__ __forceinline__ void mx_dma4(const MxRsrc& r, uint32_t lds_addr, uint32_t voff) {
-  asm volatile("s_mov_b32 m0, %0\n\ts_nop 4\n\tbuffer_load_dword %1, %2, 0 offen lds"
-               :: "s"(lds_addr), "v"(voff), "s"(r.w) : "memory", "m0");
-}
-
-// s_waitcnt immediate: vmcnt = v (0..63), expcnt and lgkmcnt = 0.
-constexpr int waitcnt_vm_lgkm0(int v) { return (v & 0xF) | ((v >> 4) << 14) | (0x0 << 4) | (0x0 << 8); }
-
 template <int OUT_F32, int HAS_RANK, int BM>
 __global__ __launch_bounds__(MxCfg<BM>::THREADS, BM == 256 ? 1 : 2) void k_gemm_mxfp4_lora_up(
     const uint8_t* __restrict__ x_codes, const uint8_t* __restrict__ x_scales,
@@ -136,10 +101,10 @@ __global__ __launch_bounds__(MxCfg<BM>::THREADS, BM == 256 ? 1 : 2) void k_gemm_
   const uint32_t Ks = static_cast<uint32_t>(K) / 32;    // scale bytes per row
   constexpr uint32_t OOB = 0x80000000u;
 
-  const MxRsrc a_rs = mx_rsrc(x_codes, static_cast<uint32_t>(static_cast<size_t>(M) * Kb));
-  const MxRsrc b_rs = mx_rsrc(w_codes, static_cast<uint32_t>(static_cast<size_t>(N) * Kb));
-  const MxRsrc sa_rs = mx_rsrc(x_scales, static_cast<uint32_t>(static_cast<size_t>(M) * Ks));
-  const MxRsrc sb_rs = mx_rsrc(w_scales, static_cast<uint32_t>(static_cast<size_t>(N) * Ks));
+  const DmaRsrc a_rs = dma_rsrc(x_codes, static_cast<uint32_t>(static_cast<size_t>(M) * Kb));
+  const DmaRsrc b_rs = dma_rsrc(w_codes, static_cast<uint32_t>(static_cast<size_t>(N) * Kb));
+  const DmaRsrc sa_rs = dma_rsrc(x_scales, static_cast<uint32_t>(static_cast<size_t>(M) * Ks));
+  const DmaRsrc sb_rs = dma_rsrc(w_scales, static_cast<uint32_t>(static_cast<size_t>(N) * Ks));
 
   // DMA roles.  Code load i of this wave covers 16 rows (1 KB): lane l
   // fetches row 16q + l / 4, chunk (l & 3) ^ swz(row), landing in slot l & 3.
@@ -202,13 +167,13 @@ __global__ __launch_bounds__(MxCfg<BM>::THREADS, BM == 256 ? 1 : 2) void k_gemm_
     const uint32_t so = static_cast<uint32_t>(st) * (MX_KS / 32);
 #pragma unroll
     for (int i = 0; i < C::A_INSTR; ++i)
-      mx_dma16(a_rs, a_lds[i] + so_lds, (live && a_off[i] != OOB) ? a_off[i] + ko : OOB);
+      dma16(a_rs, a_lds[i] + so_lds, (live && a_off[i] != OOB) ? a_off[i] + ko : OOB);
 #pragma unroll
     for (int i = 0; i < C::B_INSTR; ++i)
-      mx_dma16(b_rs, b_lds[i] + so_lds, (live && b_off[i] != OOB) ? b_off[i] + ko : OOB);
+      dma16(b_rs, b_lds[i] + so_lds, (live && b_off[i] != OOB) ? b_off[i] + ko : OOB);
 #pragma unroll
     for (int i = 0; i < C::S_INSTR; ++i)
-      mx_dma4(s_is_a[i] ? sa_rs : sb_rs, s_lds_a[i] + so_lds, (live && s_off[i] != OOB) ? s_off[i] + so : OOB);
+      dma4(s_is_a[i] ? sa_rs : sb_rs, s_lds_a[i] + so_lds, (live && s_off[i] != OOB) ? s_off[i] + so : OOB);
   };
 
   v16f acc[MX_TI][MX_TJ];
