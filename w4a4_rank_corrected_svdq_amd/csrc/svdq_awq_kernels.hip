@@ -195,6 +195,156 @@ __global__ __launch_bounds__(VEC_SCALES ? 1024 : 512) void k_awq_gemv(
   }
 }
 
+
+// ---------------------------------------------------------------------
+// Streaming form (K % 256 == 0).  A block owns 32 output columns and walks K
+// in slots of 4 groups; each slot's bytes travel from HBM straight into a
+// ring of AWD_NS LDS slots with LDS-DMA buffer loads (AWD_NS - 1 slots in
+// flight), so a CU keeps tens of KB of weights in flight without holding
+// them in registers: the 32 weight rows (128 bytes each), the 16 activation
+// rows (512 bytes each; rows past M read as zero), the scales, zero points
+// and row sums of the 4 groups.  Wave w computes group w of every slot
+// (four 32x32x16 bf16 MFMAs, then the same dequantization as above) and the
+// waves' partial results are added in LDS in wave order.
+constexpr int AWD_NS = 4;
+constexpr int AWD_W = 0;                       // slot layout (bytes): weights [32 rows][128]
+constexpr int AWD_X = 4096;                    //   activations [16 rows][512]
+constexpr int AWD_S = 12288;                   //   scales [32 rows][4] fp16
+constexpr int AWD_Z = 12544;                   //   zero points [32 rows][4] u8 (+128 bytes of padding loads)
+constexpr int AWD_XS = 12800;                  //   row sums [4 groups][16] fp32
+constexpr int AWD_DUMMY = 13056;               //   target of the padding load
+constexpr int AWD_SLOT = 13312;
+constexpr int AWD_P = 4;                       // DMA loads per wave per slot
+static_assert(AWD_NS * AWD_SLOT <= 160 * 1024 / 3, "three blocks per CU");
+
+__global__ __launch_bounds__(256) void k_awq_gemv_stream(
+    const uint16_t* __restrict__ x_hat, const float* __restrict__ xsum, const uint8_t* __restrict__ w_codes,
+    const _Float16* __restrict__ w_scales, const uint8_t* __restrict__ w_zeros, const uint16_t* __restrict__ bias,
+    int M, int N, int K, uint16_t* __restrict__ y) {
+  __shared__ __align__(16) unsigned char ring[AWD_NS][AWD_SLOT];
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(static_cast<int>(threadIdx.x) >> 6);
+  const int c = lane & 31, h = lane >> 5;
+  const int n0 = blockIdx.x * 32;
+  const int G = K / AWQ_GROUP;
+  const int S = G / 4;
+  const uint32_t Kb = static_cast<uint32_t>(K) / 2;
+  constexpr uint32_t OOB = 0x80000000u;
+
+  const DmaRsrc w_rs = dma_rsrc(w_codes, static_cast<uint32_t>(static_cast<size_t>(N) * Kb));
+  const DmaRsrc x_rs = dma_rsrc(x_hat, static_cast<uint32_t>(static_cast<size_t>(M) * K * 2));
+  // the small array this wave moves (wave-uniform choice, kept in scalar registers)
+  const void* sm_base = wave == 0 ? static_cast<const void*>(w_scales)
+                                  : wave == 1 ? static_cast<const void*>(w_zeros) : static_cast<const void*>(xsum);
+  const uint32_t sm_bytes = static_cast<uint32_t>(wave == 0   ? static_cast<size_t>(N) * G * 2
+                                                  : wave == 1 ? static_cast<size_t>(N) * G
+                                                              : static_cast<size_t>(G) * AWQ_MAX_ROWS * 4);
+  const DmaRsrc sm_rs = dma_rsrc(sm_base, sm_bytes);
+
+  // DMA roles.  Weights: wave w moves rows 8w .. 8w + 7 (lane l: row
+  // 8w + l / 8, landing at 16-byte position l % 8 of the row, which holds
+  // chunk (l % 8) ^ (row % 8) of the slot's 128 bytes).  Activations: rows
+  // 2w, 2w + 1 and 2w + 8, 2w + 9 (lane l: row + l / 32, position l % 32,
+  // holding chunk (l % 32) ^ (row % 16)).  The XOR placements keep the
+  // fragment reads below free of bank conflicts.  One 256-byte load per wave
+  // for the small arrays: wave 0 the scales (lane l: row l / 2, 4 bytes),
+  // wave 1 the zero points (lanes 0..31), wave 2 the row sums, wave 3 a
+  // padding load of zeros, so that every wave issues AWD_P loads per slot.
+  const int wr = 8 * wave + (lane >> 3);
+  const uint32_t w_off0 = static_cast<uint32_t>(n0 + wr) * Kb + 16u * static_cast<uint32_t>((lane & 7) ^ (wr & 7));
+  const int xra = 2 * wave + (lane >> 5), xrb = xra + 8;
+  const uint32_t xq = 16u * static_cast<uint32_t>(lane & 31);
+  const uint32_t xa_off0 = xra < M ? static_cast<uint32_t>(xra) * K * 2 + (xq ^ (16u * (xra & 15))) : OOB;
+  const uint32_t xb_off0 = xrb < M ? static_cast<uint32_t>(xrb) * K * 2 + (xq ^ (16u * (xrb & 15))) : OOB;
+  uint32_t sm_off0 = OOB, sm_step = 0;
+  if (wave == 0) {
+    sm_off0 = static_cast<uint32_t>(n0 + (lane >> 1)) * G * 2 + 4u * (lane & 1);
+    sm_step = 8;
+  } else if (wave == 1) {
+    sm_off0 = lane < 32 ? static_cast<uint32_t>(n0 + lane) * G : OOB;
+    sm_step = 4;
+  } else if (wave == 2) {
+    sm_off0 = 4u * lane;
+    sm_step = 4 * AWQ_MAX_ROWS * 4;
+  }
+  const uint32_t ring0 = static_cast<uint32_t>(reinterpret_cast<uintptr_t>(&ring[0][0]));
+  const uint32_t w_lds = __builtin_amdgcn_readfirstlane(ring0 + AWD_W + 1024 * wave);
+  const uint32_t xa_lds = __builtin_amdgcn_readfirstlane(ring0 + AWD_X + 1024 * wave);
+  const uint32_t xb_lds = __builtin_amdgcn_readfirstlane(ring0 + AWD_X + 4096 + 1024 * wave);
+  const uint32_t sm_lds = __builtin_amdgcn_readfirstlane(
+      ring0 + (wave == 0 ? AWD_S : wave == 1 ? AWD_Z : wave == 2 ? AWD_XS : AWD_DUMMY));
+  auto issue = [&](int s, int slot) {
+    const uint32_t so = static_cast<uint32_t>(slot) * AWD_SLOT;
+    const bool live = s < S;
+    dma16(w_rs, w_lds + so, live ? w_off0 + 128u * s : OOB);
+    dma16(x_rs, xa_lds + so, (live && xa_off0 != OOB) ? xa_off0 + 512u * s : OOB);
+    dma16(x_rs, xb_lds + so, (live && xb_off0 != OOB) ? xb_off0 + 512u * s : OOB);
+    dma4(sm_rs, sm_lds + so, (live && sm_off0 != OOB) ? sm_off0 + sm_step * s : OOB);
+  };
+
+  v16f acc;
+#pragma unroll
+  for (int v = 0; v < 16; ++v) acc[v] = 0.f;
+  const int j = wave;                            // group of the slot this wave computes
+  const int wp = 16 * ((2 * j + h) ^ (c & 7));   // position of the lane's 16 code bytes in its weight row
+  const int cr = c & 15;
+
+#pragma unroll
+  for (int s = 0; s < AWD_NS - 1; ++s) issue(s, s);
+  int slot = 0;
+  for (int s = 0; s < S; ++s) {
+    // slot s has landed once at most NS - 2 slots of this wave's loads are
+    // outstanding; the barrier publishes it and frees the slot of s - 1
+    __builtin_amdgcn_s_waitcnt(waitcnt_vm_lgkm0(AWD_P * (AWD_NS - 2)));
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
+    issue(s + AWD_NS - 1, slot == 0 ? AWD_NS - 1 : slot - 1);
+    const unsigned char* base = ring[slot];
+    const uint4 wq = *reinterpret_cast<const uint4*>(base + AWD_W + c * 128 + wp);
+    uint4 xa[4];
+#pragma unroll
+    for (int t = 0; t < 4; ++t) {
+      const int q = 8 * j + 4 * h + t;
+      const uint4 v = *reinterpret_cast<const uint4*>(base + AWD_X + cr * 512 + 16 * (q ^ cr));
+      xa[t] = c < 16 ? v : make_uint4(0u, 0u, 0u, 0u);   // A rows 16..31 are padding
+    }
+    const float sc = static_cast<float>(*reinterpret_cast<const _Float16*>(base + AWD_S + c * 8 + 2 * j));
+    const float cz = 128.0f + static_cast<float>(base[AWD_Z + 4 * c + j]);
+    const float4 x0 = *reinterpret_cast<const float4*>(base + AWD_XS + 64 * j + 16 * h);
+    const float4 x1 = *reinterpret_cast<const float4*>(base + AWD_XS + 64 * j + 32 + 16 * h);
+    const uint32_t* wd = reinterpret_cast<const uint32_t*>(&wq);
+    v16f d0, d1;
+#pragma unroll
+    for (int v = 0; v < 16; ++v) { d0[v] = 0.f; d1[v] = 0.f; }
+    // two independent chains of two MFMAs
+    d0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(v8bf, xa[0]), awq_nibbles_to_bf16(wd[0]), d0, 0, 0, 0);
+    d1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(v8bf, xa[1]), awq_nibbles_to_bf16(wd[1]), d1, 0, 0, 0);
+    d0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(v8bf, xa[2]), awq_nibbles_to_bf16(wd[2]), d0, 0, 0, 0);
+    d1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(v8bf, xa[3]), awq_nibbles_to_bf16(wd[3]), d1, 0, 0, 0);
+    const float xs[8] = {x0.x, x0.y, x0.z, x0.w, x1.x, x1.y, x1.z, x1.w};
+#pragma unroll
+    for (int v = 0; v < 8; ++v) acc[v] = fmaf(sc, fmaf(-cz, xs[v], d0[v] + d1[v]), acc[v]);
+    slot = slot == AWD_NS - 1 ? 0 : slot + 1;
+  }
+  // loads past the last slot land before the ring is reused for the sums
+  __builtin_amdgcn_s_waitcnt(waitcnt_vm_lgkm0(0));
+  __syncthreads();
+  float (*part)[64][8] = reinterpret_cast<float (*)[64][8]>(&ring[0][0]);
+#pragma unroll
+  for (int v = 0; v < 8; ++v) part[wave][lane][v] = acc[v];
+  __syncthreads();
+  if (wave == 0) {
+    const int n = n0 + c;
+    const float bb = bias ? bf16_bits_to_f32(bias[n]) : 0.0f;
+#pragma unroll
+    for (int v = 0; v < 8; ++v) {
+      const float t = ((part[0][lane][v] + part[1][lane][v]) + part[2][lane][v]) + part[3][lane][v];
+      const int m = 8 * (v >> 2) + 4 * h + (v & 3);
+      if (m < M) y[static_cast<size_t>(m) * N + n] = static_cast<uint16_t>(f32_to_bf16_bits(t + bb));
+    }
+  }
+}
+
 }  // namespace
 
 namespace svdq {
@@ -211,6 +361,13 @@ int launch_awq_quant_act(const void* x, const float* inv_scale, int M, int K, vo
 int launch_awq_gemv(const void* x_hat, const float* xsum, const void* w_codes, const void* w_scales,
                     const void* w_zeros, const void* bias, int M, int N, int K, void* y, void* stream) {
   hipStream_t st = static_cast<hipStream_t>(stream);
+  if ((K / AWQ_GROUP) % 4 == 0) {
+    hipLaunchKernelGGL(k_awq_gemv_stream, dim3(N / 32), dim3(256), 0, st, static_cast<const uint16_t*>(x_hat), xsum,
+                       static_cast<const uint8_t*>(w_codes), static_cast<const _Float16*>(w_scales),
+                       static_cast<const uint8_t*>(w_zeros), static_cast<const uint16_t*>(bias), M, N, K,
+                       static_cast<uint16_t*>(y));
+    return hipGetLastError() == hipSuccess ? SVDQ_OK : SVDQ_ERR_HIP;
+  }
   const int chunks = (K / AWQ_GROUP + 7) / 8;
   const bool vec = (K / AWQ_GROUP) % 8 == 0;
   const int max_waves = vec ? 16 : 8;                // the per-group scale loads need more registers
