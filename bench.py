@@ -196,7 +196,7 @@ def bench_awq(S, workloads, steps, warmup, M=1):
     gbs = nbytes / (gemv_ms * 1e-3) / 1e9
     return {"workload": f"FLUX modulation projection 3072 -> 18432 (+bias), M = {M}, AWQ INT4 group 64",
             "alpha": prep["alpha"], "ms_per_step": round(ms, 5),
-            "roofline": {"bound": "hbm", "kernel": "k_awq_gemv", "achieved": round(gbs, 1),
+            "roofline": {"bound": "hbm", "kernel": "k_awq_gemv_stream", "achieved": round(gbs, 1),
                          "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(gbs / HBM_PEAK_GBS, 4),
                          "avg_launch_us": round(gemv_ms * 1e3, 2), "algorithmic_bytes_per_launch": nbytes}}
 
