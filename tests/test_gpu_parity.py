@@ -67,7 +67,7 @@ def y_to_np(y):
 
 # ------------------------------------------------------------------ kernel 2: integer core
 @pytest.mark.parametrize("M,N,K", [(300, 264, 256), (16, 128, 64), (129, 8, 128), (1, 136, 192),
-                                   (200, 1032, 12288)])
+                                   (200, 1032, 12288), (4000, 4104, 320)])
 def test_int32_group_products_bit_exact(M, N, K):
     """Unit scales, rank 0, fp32 output: y = sum_k q_x q_w is an integer below
     2^24, so it is exact in fp32 whatever the order; compared bit for bit
@@ -178,6 +178,33 @@ def test_k2_output_parity(rank, bias, out):
     assert e < Y_TOL, e
     if out == "f32":
         assert e < 1e-5, e
+
+
+# Kernel 2 has two tile forms: 256 x 256 (8 waves) when M is even and the
+# grid has at least 256 such tiles, 128 x 128 otherwise.  These cases put the
+# large form on ragged M and N edges (4000 = 15.6 tiles, 4104 = 16.03 tiles)
+# with an odd group count (K = 192) and every epilogue option, and compare
+# every output with the oracle.
+LARGE_FORM = (4000, 192, 4104)
+
+
+@pytest.mark.parametrize("rank,bias,out", [(0, False, "bf16"), (32, True, "bf16"), (48, True, "f32")])
+def test_k2_large_form_parity(rank, bias, out):
+    M, K, N = LARGE_FORM
+    wl, Lr, po, abi = _small_case(M, K, N, rank, seed=60 + rank, bias=bias)
+    Yo, parts = O.forward(wl.x, po, bias=Lr.bias, out=("f32" if out == "f32" else "bf16"), return_parts=True)
+    xc = dev(O.pack_int4(parts["qx"]))
+    xs = dev(parts["sx"].T.astype(np.float16))
+    la = dev(parts["lora_act"].astype(np.float32)) if rank else None
+    od = L.SVDQ_OUT_F32 if out == "f32" else L.SVDQ_OUT_BF16
+    y = run_k2(xc, xs, abi, la, Lr.bias_bits if bias else None, M, out_dtype=od)
+    e = O.rel_fro(y_to_np(y), Yo)
+    assert e < Y_TOL, e
+    if out == "f32":
+        assert e < 1e-5, e
+    again = run_k2(xc, xs, abi, la, Lr.bias_bits if bias else None, M, out_dtype=od)
+    assert torch.equal(y.view(torch.int16) if y.dtype == torch.bfloat16 else y.view(torch.int32),
+                       again.view(torch.int16) if again.dtype == torch.bfloat16 else again.view(torch.int32))
 
 
 @pytest.mark.parametrize("shape", [(300, 512, 264), (128, 1024, 512), (5, 256, 1032)])
@@ -463,6 +490,30 @@ def test_qkv_epilogue_parity(M, heads, rank, bias, rope, out):
     e = O.rel_fro(y_to_np(y), ref)
     assert e < (1e-5 if out == "f32" else Y_TOL), e
     plain = run_k2(xc, xs, abi, la, Lr.bias_bits if bias else None, M, out_dtype=od)
+    v0 = 2 * heads * 128
+    np.testing.assert_array_equal(y[:, v0:].float().cpu().numpy(), plain[:, v0:].float().cpu().numpy())
+
+
+@pytest.mark.parametrize("out", ["bf16", "f32"])
+def test_qkv_large_form_parity(out):
+    """The fused QKV epilogue on the 256 x 256 form: 11 heads (N = 4224, so
+    one block holds the last Q head and the first K head, and the last block
+    column is half full), rank 16, bias, rotary tables; every output against
+    the oracle, V columns bit-identical to the plain kernel."""
+    M, K, heads, rank = 4096, 256, 11, 16
+    N = 3 * heads * 128
+    wl, Lr, po, abi = _small_case(M, K, N, rank, seed=62, bias=True)
+    qb, qv, kb, kv, cos, sin = _qkv_inputs(M, 63, True)
+    Yo, parts = O.forward(wl.x, po, bias=Lr.bias, out="f64", return_parts=True)
+    ref = O.forward_qkv(wl.x, po, Lr.bias, qv, kv, cos, sin, out=out)
+    xc = dev(O.pack_int4(parts["qx"]))
+    xs = dev(parts["sx"].T.astype(np.float16))
+    la = dev(parts["lora_act"].astype(np.float32))
+    od = L.SVDQ_OUT_F32 if out == "f32" else L.SVDQ_OUT_BF16
+    y = run_qkv(xc, xs, abi, la, Lr.bias_bits, M, qb, kb, cos, sin, out_dtype=od)
+    e = O.rel_fro(y_to_np(y), ref)
+    assert e < (1e-5 if out == "f32" else Y_TOL), e
+    plain = run_k2(xc, xs, abi, la, Lr.bias_bits, M, out_dtype=od)
     v0 = 2 * heads * 128
     np.testing.assert_array_equal(y[:, v0:].float().cpu().numpy(), plain[:, v0:].float().cpu().numpy())
 

@@ -470,7 +470,7 @@ __device__ __forceinline__ void k2_epilogue(v4f (&acc)[K2_TA][K2_TB], unsigned c
   }}
 
 template <int OUT_F32, int NT, int EPI>
-__global__ __launch_bounds__(K2_THREADS, 2) void k_gemm_w4a4_lora_up(
+__global__ __launch_bounds__(K2_THREADS, 2) void k_gemm_w4a4_lora_up_t128(
     const uint8_t* __restrict__ x_codes, const _Float16* __restrict__ x_scales,
     const uint8_t* __restrict__ w_codes, const _Float16* __restrict__ w_scales,
     const float* __restrict__ lora_act, const uint16_t* __restrict__ lora_up,
@@ -643,6 +643,424 @@ __global__ __launch_bounds__(K2_THREADS, 2) void k_gemm_w4a4_lora_up(
   k2_epilogue<OUT_F32, NT, EPI>(acc, k2_smem_raw, m0, n0, lora_act, lora_up, bias, M, N, rank, y, qa);
 }
 
+// ---------------------------------------------------------------------
+// Kernel 2, large form: block tile 256 (m) x 256 (n), 8 waves in a 4 x 2
+// grid, each owning 64 (m) x 128 (n) outputs = 4 x 8 tiles of 16 x 16
+// computed transposed as above.  A wave's 128 columns are one head of the
+// fused QKV layout, so its per-head normalization stays inside the wave.
+//
+// Operands are not staged through registers: packed codes and the raw fp16
+// scales move from HBM straight into a ring of KT_NS LDS stage buffers with
+// LDS-DMA buffer loads (no registers, no unpack pass), and each lane unpacks
+// the 8 packed bytes of its own fragment when it reads them (three ALU ops
+// per packed dword).  Stage = two groups (128 k).  At the top of stage u the
+// loads of stage u + 1 have landed as well; during stage u every thread
+// converts two of stage u + 1's scales in place to fp32 (s_x / 256 for the
+// activations, s_w for the weights), which the next barrier publishes, so
+// the only vector-memory operations in the loop are the DMA loads, counted
+// exactly by the explicit s_waitcnt.
+//
+// Stage layout (bytes): activation codes [256 rows][64], weight codes
+// [256 rows][64] (16-byte chunk c = group c / 2, packed bytes 16 (c % 2) ..
+// + 15 of that group, at position c ^ swz(row)), then one dword per scale:
+// activations [2 groups][256], weights [2 groups][256].  A raw scale dword
+// is the aligned pair holding the scale (x_scales and w_scales are read as
+// pairs, so M must be even here; N is a multiple of 8).
+constexpr int KT_BM = 256;
+constexpr int KT_BN = 256;
+constexpr int KT_WAVES = 8;
+constexpr int KT_THREADS = KT_WAVES * 64;
+constexpr int KT_WM = 64;
+constexpr int KT_WN = 128;
+constexpr int KT_TB = KT_WM / 16;             // activation fragments per wave (m)
+constexpr int KT_TA = KT_WN / 16;             // weight fragments per wave (n)
+constexpr int KT_NS = 4;                      // ring depth (stages)
+constexpr int KT_X_BYTES = KT_BM * 64;
+constexpr int KT_W_BYTES = KT_BN * 64;
+constexpr int KT_SX_OFF = KT_X_BYTES + KT_W_BYTES;
+constexpr int KT_SW_OFF = KT_SX_OFF + 2 * KT_BM * 4;
+constexpr int KT_STAGE = KT_SW_OFF + 2 * KT_BN * 4;
+constexpr int KT_X_INSTR = KT_BM / 16 / KT_WAVES;                      // 1 KB code loads per wave
+constexpr int KT_W_INSTR = KT_BN / 16 / KT_WAVES;
+constexpr int KT_S_INSTR = (2 * KT_BM / 64 + 2 * KT_BN / 64) / KT_WAVES;  // 256-byte scale loads
+constexpr int KT_P = KT_X_INSTR + KT_W_INSTR + KT_S_INSTR;             // DMA loads per wave per stage
+static_assert(KT_S_INSTR * KT_WAVES == 2 * KT_BM / 64 + 2 * KT_BN / 64, "equal DMA counts per wave");
+static_assert(KT_STAGE % 16 == 0, "stage buffers stay 16-byte aligned");
+static_assert(KT_WAVES * KT_WM * KT_WN * 2 <= KT_NS * KT_STAGE, "the output tiles reuse the stage ring");
+static_assert(2 * (KT_BM + KT_BN) == 2 * KT_THREADS, "two scale conversions per thread per stage");
+
+// Epilogue of the large form: up projection, bias, fused QKV normalization
+// and rotation, store.  acc[a][b][e] holds output row m0 + 64 wm + 16b +
+// (lane & 15), column n0 + 128 wn + 16a + 4(lane >> 4) + e.  The LDS passed
+// in is free.
+template <int OUT_F32, int NT, int EPI>
+__device__ __forceinline__ void kt_epilogue(v4f (&acc)[KT_TA][KT_TB], unsigned char* smem, int m0, int n0,
+                                            const float* __restrict__ lora_act,
+                                            const uint16_t* __restrict__ lora_up,
+                                            const uint16_t* __restrict__ bias, int M, int N, int rank,
+                                            void* __restrict__ y, const QkvArgs& qa) {
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int wm = wave >> 1, wn = wave & 1;
+  const int lr = lane & 15, lq = lane >> 4;
+  const int mw = m0 + wm * KT_WM, nw = n0 + wn * KT_WN;
+  // up projection: bf16 MFMA 16x16x32 over the rank in slices of 32 (ranks
+  // are multiples of 16, so the lanes of a slice past the rank load zeros);
+  // lora_up rows are the A operand, lora_act rows the B operand
+  if constexpr (NT > 0) {
+    for (int kk = 0; kk < rank; kk += 32) {
+      const int kl = kk + lq * 8;
+      const bool kin = kl < rank;
+      v8bf la[KT_TB];
+#pragma unroll
+      for (int b = 0; b < KT_TB; ++b) {
+        const int r = mw + b * 16 + lr;
+        float v[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+        if (kin && r < M) {
+          const float4* p = reinterpret_cast<const float4*>(lora_act + static_cast<size_t>(r) * rank + kl);
+          const float4 v0 = p[0], v1 = p[1];
+          v[0] = v0.x; v[1] = v0.y; v[2] = v0.z; v[3] = v0.w;
+          v[4] = v1.x; v[5] = v1.y; v[6] = v1.z; v[7] = v1.w;
+        }
+        la[b] = pack_bf16x8(v);
+      }
+#pragma unroll
+      for (int a = 0; a < KT_TA; ++a) {
+        const int c = nw + a * 16 + lr;
+        uint4 u = make_uint4(0, 0, 0, 0);
+        if (kin && c < N) u = *reinterpret_cast<const uint4*>(lora_up + static_cast<size_t>(c) * rank + kl);
+        const v8bf ub = __builtin_bit_cast(v8bf, u);
+#pragma unroll
+        for (int b = 0; b < KT_TB; ++b)
+          acc[a][b] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ub, la[b], acc[a][b], 0, 0, 0);
+      }
+    }
+  }
+  if (bias) {
+#pragma unroll
+    for (int a = 0; a < KT_TA; ++a) {
+      const int c = nw + a * 16 + 4 * lq;      // N % 8 == 0: all four in or out
+      if (c >= N) continue;
+      const uint2 bv = *reinterpret_cast<const uint2*>(bias + c);
+      const float b4[4] = {bf16_bits_to_f32(bv.x & 0xFFFFu), bf16_bits_to_f32(bv.x >> 16),
+                           bf16_bits_to_f32(bv.y & 0xFFFFu), bf16_bits_to_f32(bv.y >> 16)};
+#pragma unroll
+      for (int b = 0; b < KT_TB; ++b)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) acc[a][b][e] += b4[e];
+    }
+  }
+  if constexpr (EPI == 1) {
+    // The wave's 128 columns are one head (N = 3 * heads * 128): Q heads,
+    // then K heads, then V heads, which are left as projected.
+    const int HD = N / 3;
+    if (nw < 2 * HD) {
+      const uint16_t* g = nw < HD ? qa.gq : qa.gk;
+#pragma unroll
+      for (int b = 0; b < KT_TB; ++b) {
+        // sum of squares of the row over the head: this lane's 32 columns
+        // and the other three lane quads' (lane ^ 16, lane ^ 32)
+        float t = 0.f;
+#pragma unroll
+        for (int a = 0; a < KT_TA; ++a)
+#pragma unroll
+          for (int e = 0; e < 4; ++e) t = fmaf(acc[a][b][e], acc[a][b][e], t);
+        t += __shfl_xor(t, 16);
+        t += __shfl_xor(t, 32);
+        const float scale = 1.0f / sqrtf(t * (1.0f / QKV_HEAD) + qa.eps);
+        const int row = mw + b * 16 + lr;
+        const bool rot = qa.cos != nullptr && row < M;
+#pragma unroll
+        for (int a = 0; a < KT_TA; ++a) {
+          const int ch = a * 16 + 4 * lq;                      // column within the head
+          const uint2 gv = *reinterpret_cast<const uint2*>(g + ch);
+          const float g4[4] = {bf16_bits_to_f32(gv.x & 0xFFFFu), bf16_bits_to_f32(gv.x >> 16),
+                               bf16_bits_to_f32(gv.y & 0xFFFFu), bf16_bits_to_f32(gv.y >> 16)};
+          float o[4];
+#pragma unroll
+          for (int e = 0; e < 4; ++e) o[e] = acc[a][b][e] * scale * g4[e];
+          if (rot) {
+            const float2 cs = *reinterpret_cast<const float2*>(qa.cos + static_cast<size_t>(row) * 64 + (ch >> 1));
+            const float2 sn = *reinterpret_cast<const float2*>(qa.sin + static_cast<size_t>(row) * 64 + (ch >> 1));
+            const float a0 = o[0] * cs.x - o[1] * sn.x, a1 = o[1] * cs.x + o[0] * sn.x;
+            const float a2 = o[2] * cs.y - o[3] * sn.y, a3 = o[3] * cs.y + o[2] * sn.y;
+            o[0] = a0; o[1] = a1; o[2] = a2; o[3] = a3;
+          }
+#pragma unroll
+          for (int e = 0; e < 4; ++e) acc[a][b][e] = o[e];
+        }
+      }
+    }
+  }
+  if (OUT_F32) {
+#pragma unroll
+    for (int b = 0; b < KT_TB; ++b) {
+      const int row = mw + b * 16 + lr;
+      if (row >= M) continue;
+#pragma unroll
+      for (int a = 0; a < KT_TA; ++a) {
+        const int c = nw + a * 16 + 4 * lq;
+        if (c >= N) continue;
+        *reinterpret_cast<float4*>(reinterpret_cast<float*>(y) + static_cast<size_t>(row) * N + c) =
+            make_float4(acc[a][b][0], acc[a][b][1], acc[a][b][2], acc[a][b][3]);
+      }
+    }
+  } else {
+    // bf16 through LDS: each wave writes its 64 x 128 tile with 8-byte
+    // writes, then stores whole 256-byte row segments, four rows per
+    // instruction; 16-byte chunk c of tile row r sits at chunk c ^ (r & 15).
+    uint2* tile = reinterpret_cast<uint2*>(smem) + wave * (KT_WM * KT_WN / 4);
+#pragma unroll
+    for (int b = 0; b < KT_TB; ++b) {
+      const int rl = b * 16 + lr;
+#pragma unroll
+      for (int a = 0; a < KT_TA; ++a) {
+        const int chunk = 2 * a + (lq >> 1);
+        tile[rl * 32 + ((chunk ^ (rl & 15)) << 1) + (lq & 1)] =
+            make_uint2(f32_to_bf16_bits(acc[a][b][0]) | (f32_to_bf16_bits(acc[a][b][1]) << 16),
+                       f32_to_bf16_bits(acc[a][b][2]) | (f32_to_bf16_bits(acc[a][b][3]) << 16));
+      }
+    }
+    // the reads below are of another type than the writes above: keep the
+    // compiler from moving them across (the hardware orders one wave's LDS ops)
+    asm volatile("" ::: "memory");
+    const uint4* tile4 = reinterpret_cast<const uint4*>(tile);
+    const int cl = lane & 15;
+    const int col = nw + cl * 8;
+#pragma unroll
+    for (int it = 0; it < KT_WM / 4; ++it) {
+      const int rl = it * 4 + (lane >> 4);
+      const uint4 v = tile4[rl * 16 + (cl ^ (rl & 15))];
+      const int row = mw + rl;
+      if (row < M && col < N)
+        *reinterpret_cast<uint4*>(reinterpret_cast<uint16_t*>(y) + static_cast<size_t>(row) * N + col) = v;
+    }
+  }
+}
+
+__device__ __forceinline__ v4i unpack_b64(uint2 w) {   // 16 packed codes -> 16 int8 lanes of 16q
+  return v4i{static_cast<int>((w.x << 4) & 0xF0F0F0F0u), static_cast<int>(w.x & 0xF0F0F0F0u),
+             static_cast<int>((w.y << 4) & 0xF0F0F0F0u), static_cast<int>(w.y & 0xF0F0F0F0u)};
+}
+
+template <int OUT_F32, int NT, int EPI>
+__global__ __launch_bounds__(KT_THREADS, 1) void k_gemm_w4a4_lora_up(
+    const uint8_t* __restrict__ x_codes, const _Float16* __restrict__ x_scales,
+    const uint8_t* __restrict__ w_codes, const _Float16* __restrict__ w_scales,
+    const float* __restrict__ lora_act, const uint16_t* __restrict__ lora_up,
+    const uint16_t* __restrict__ bias, int M, int N, int K, int rank, void* __restrict__ y, QkvArgs qa) {
+  // statically sized ring: with the slot as the first index the compiler
+  // can tell the slots apart
+  __shared__ __align__(16) unsigned char ring[KT_NS][KT_STAGE];
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int wm = wave >> 1, wn = wave & 1;
+  const int nM = (M + KT_BM - 1) / KT_BM, nN = (N + KT_BN - 1) / KT_BN;
+  int tm, tn;
+  xcd_tile(nM, nN, tm, tn);
+  const int m0 = tm * KT_BM, n0 = tn * KT_BN;
+  const int G = K / GROUP;
+  const int S = (G + 1) / 2;
+  const uint32_t Kb = static_cast<uint32_t>(K) / 2;
+  constexpr uint32_t OOB = 0x80000000u;
+
+  const DmaRsrc x_rs = dma_rsrc(x_codes, static_cast<uint32_t>(static_cast<size_t>(M) * Kb));
+  const DmaRsrc w_rs = dma_rsrc(w_codes, static_cast<uint32_t>(static_cast<size_t>(N) * Kb));
+  const DmaRsrc sx_rs = dma_rsrc(x_scales, static_cast<uint32_t>(static_cast<size_t>(G) * M * 2));
+  const DmaRsrc sw_rs = dma_rsrc(w_scales, static_cast<uint32_t>(static_cast<size_t>(G) * N * 2));
+
+  // DMA roles.  Code load i of this wave covers 16 rows (1 KB): lane l
+  // fetches row 16q + l / 4, logical chunk (l & 3) ^ swz(row), landing at
+  // position l & 3; a chunk of a group past G, or a row past M / N, reads as
+  // zero.  Scale load j covers 64 consecutive rows of one group and operand:
+  // lane l fetches the aligned dword holding that row's fp16 scale.
+  uint32_t x_off[KT_X_INSTR], w_off[KT_W_INSTR], s_off[KT_S_INSTR], s_step[KT_S_INSTR];
+  int x_grp[KT_X_INSTR], w_grp[KT_W_INSTR], s_grp[KT_S_INSTR];
+  bool s_is_x[KT_S_INSTR];
+  uint32_t x_lds[KT_X_INSTR], w_lds[KT_W_INSTR], s_lds[KT_S_INSTR];
+  const uint32_t ring0 = static_cast<uint32_t>(reinterpret_cast<uintptr_t>(&ring[0][0]));
+#pragma unroll
+  for (int i = 0; i < KT_X_INSTR; ++i) {
+    const int q = wave * KT_X_INSTR + i;
+    const int r = 16 * q + (lane >> 2);
+    const int c = (lane & 3) ^ k2_swz(r, 0);
+    x_off[i] = (m0 + r < M) ? static_cast<uint32_t>(m0 + r) * Kb + 16u * c : OOB;
+    x_grp[i] = c >> 1;
+    x_lds[i] = __builtin_amdgcn_readfirstlane(ring0 + 1024 * q);
+  }
+#pragma unroll
+  for (int i = 0; i < KT_W_INSTR; ++i) {
+    const int q = wave * KT_W_INSTR + i;
+    const int r = 16 * q + (lane >> 2);
+    const int c = (lane & 3) ^ k2_swz(r, 0);
+    w_off[i] = (n0 + r < N) ? static_cast<uint32_t>(n0 + r) * Kb + 16u * c : OOB;
+    w_grp[i] = c >> 1;
+    w_lds[i] = __builtin_amdgcn_readfirstlane(ring0 + KT_X_BYTES + 1024 * q);
+  }
+#pragma unroll
+  for (int i = 0; i < KT_S_INSTR; ++i) {
+    const int j = wave * KT_S_INSTR + i;                       // wave-uniform
+    const bool isx = j < 2 * KT_BM / 64;
+    const int jj = isx ? j : j - 2 * KT_BM / 64;
+    const int gi = jj >> 2, ch = jj & 3;                       // 4 loads of 64 rows per group
+    const int r = 64 * ch + lane;
+    const int base = isx ? m0 : n0, lim = isx ? M : N;
+    const uint32_t e0 = static_cast<uint32_t>(gi) * static_cast<uint32_t>(lim) + static_cast<uint32_t>(base + r);
+    s_is_x[i] = isx;
+    s_grp[i] = gi;
+    s_off[i] = (base + r < lim) ? 4u * (e0 >> 1) : OOB;
+    s_step[i] = 4u * static_cast<uint32_t>(lim);               // two groups = 2 * lim scales further
+    s_lds[i] = __builtin_amdgcn_readfirstlane(ring0 + (isx ? KT_SX_OFF : KT_SW_OFF) + 4 * (gi * 256 + 64 * ch));
+  }
+
+  // Issue the DMA loads of stage st into ring slot st % KT_NS.
+  auto issue_stage = [&](int st) {
+    const uint32_t so = static_cast<uint32_t>(st % KT_NS) * KT_STAGE;
+    const bool live = st < S;
+    const uint32_t ko = static_cast<uint32_t>(st) * 64u;
+#pragma unroll
+    for (int i = 0; i < KT_X_INSTR; ++i) {
+      const bool ok = live && x_off[i] != OOB && 2 * st + x_grp[i] < G;
+      dma16(x_rs, x_lds[i] + so, ok ? x_off[i] + ko : OOB);
+    }
+#pragma unroll
+    for (int i = 0; i < KT_W_INSTR; ++i) {
+      const bool ok = live && w_off[i] != OOB && 2 * st + w_grp[i] < G;
+      dma16(w_rs, w_lds[i] + so, ok ? w_off[i] + ko : OOB);
+    }
+#pragma unroll
+    for (int i = 0; i < KT_S_INSTR; ++i) {
+      const bool ok = live && s_off[i] != OOB && 2 * st + s_grp[i] < G;
+      dma4(s_is_x[i] ? sx_rs : sw_rs, s_lds[i] + so, ok ? s_off[i] + static_cast<uint32_t>(st) * s_step[i] : OOB);
+    }
+  };
+  // Convert the raw scale dwords of a landed stage to fp32 in place: thread
+  // t owns activation scale t (group t / 256, row t % 256) and weight scale
+  // t; the fp16 value is the half (row & 1) of its dword (M, N, m0 and n0
+  // even).
+  auto convert_stage = [&](int st) {
+    uint32_t* sc = reinterpret_cast<uint32_t*>(&ring[st % KT_NS][KT_SX_OFF]);
+    const uint32_t dx = sc[tid], dw = sc[KT_THREADS + tid];
+    const int sh = 16 * (tid & 1);
+    const float fx = static_cast<float>(__builtin_bit_cast(_Float16, static_cast<uint16_t>(dx >> sh)));
+    const float fw = static_cast<float>(__builtin_bit_cast(_Float16, static_cast<uint16_t>(dw >> sh)));
+    sc[tid] = __float_as_uint(fx * (1.0f / 256.0f));
+    sc[KT_THREADS + tid] = __float_as_uint(fw);
+  };
+
+  v4f acc[KT_TA][KT_TB];
+#pragma unroll
+  for (int a = 0; a < KT_TA; ++a)
+#pragma unroll
+    for (int b = 0; b < KT_TB; ++b) acc[a][b] = v4f{0.f, 0.f, 0.f, 0.f};
+  v4i cmagic = v4i{MAGIC_I, MAGIC_I, MAGIC_I, MAGIC_I};
+  asm volatile("" : "+v"(cmagic));
+
+  const int lr = lane & 15, lq = lane >> 4;
+  // Per-lane byte offsets in a stage of this lane's fragment reads: the 8
+  // packed bytes 8 lq .. 8 lq + 7 of group gi of row r sit in logical chunk
+  // 2 gi + lq / 2 at byte 8 (lq & 1).  swz(r) depends on the row bits 1..4,
+  // so rows 32 apart share it: one offset per (group, tile parity).
+  uint32_t fx_off[2][2], fw_off[2][2];
+#pragma unroll
+  for (int gi = 0; gi < 2; ++gi)
+#pragma unroll
+    for (int p = 0; p < 2; ++p) {
+      const int rx = wm * KT_WM + 16 * p + lr, rw = wn * KT_WN + 16 * p + lr;
+      fx_off[gi][p] = rx * 64 + 16 * ((2 * gi + (lq >> 1)) ^ k2_swz(rx, 0)) + 8 * (lq & 1);
+      fw_off[gi][p] = KT_X_BYTES + rw * 64 + 16 * ((2 * gi + (lq >> 1)) ^ k2_swz(rw, 0)) + 8 * (lq & 1);
+    }
+  const uint32_t xs_off = KT_SX_OFF + 4 * (wm * KT_WM + lr);
+  const uint32_t ws_off = KT_SW_OFF + 4 * (wn * KT_WN + 4 * lq);
+
+  v4i fx[KT_TB], fw[2];
+  float2 xc[2][KT_TB];
+  float4 swr[4];
+  v4i dr[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    dr[i] = cmagic;
+    swr[i] = make_float4(0.f, 0.f, 0.f, 0.f);
+  }
+#pragma unroll
+  for (int b = 0; b < KT_TB; ++b) xc[0][b] = xc[1][b] = make_float2(0.f, 0.f);
+
+  auto rd_x = [&](const unsigned char* s, int gi) {   // activation fragments and scales of group gi
+#pragma unroll
+    for (int b = 0; b < KT_TB; ++b) {
+      fx[b] = unpack_b64(*reinterpret_cast<const uint2*>(s + fx_off[gi][b & 1] + (b >> 1) * 2048));
+      const float ax = *reinterpret_cast<const float*>(s + xs_off + gi * 1024 + 64 * b);
+      xc[gi][b] = make_float2(ax, -MAGIC_F * ax);
+    }
+  };
+  auto rd_w = [&](const unsigned char* s, int gi, int a, v4i& f, float4& sw) {
+    f = unpack_b64(*reinterpret_cast<const uint2*>(s + fw_off[gi][a & 1] + (a >> 1) * 2048));
+    sw = *reinterpret_cast<const float4*>(s + ws_off + gi * 1024 + 64 * a);
+  };
+  // acc += s_w * (s_x * P): two fp32 FMAs per output (see the 128 x 128 form)
+  auto deq = [&](float2 c, float4 sw, const v4i& d, v4f& ac) {
+    const float s4[4] = {sw.x, sw.y, sw.z, sw.w};
+#pragma unroll
+    for (int e = 0; e < 4; ++e) ac[e] = __builtin_fmaf(__builtin_fmaf(__int_as_float(d[e]), c.x, c.y), s4[e], ac[e]);
+  };
+  // tile q of a stage (0 .. 63): group q / 32, weight fragment (q / 4) % 8,
+  // activation fragment q % 4
+  auto deq_tile = [&](int q) {
+    const int gi = q >> 5, a = (q >> 2) & 7, b = q & 3;
+    deq(xc[gi][b], swr[a & 3], dr[q & 3], acc[a][b]);
+  };
+
+  // stages 0 .. 2 in flight; stage 0 landed and its scales converted
+#pragma unroll
+  for (int st = 0; st < KT_NS - 1; ++st) issue_stage(st);
+  __builtin_amdgcn_s_waitcnt(waitcnt_vm_lgkm0(KT_P * (KT_NS - 2)));
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+  convert_stage(0);
+
+  for (int u = 0; u < S; ++u) {
+    // stage u + 1 has landed once one stage of this wave's loads is still
+    // outstanding; the barrier publishes it with stage u's fp32 scales and
+    // frees slot (u - 1) % KT_NS, which every wave has finished reading
+    __builtin_amdgcn_s_waitcnt(waitcnt_vm_lgkm0(KT_P * (KT_NS - 3)));
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
+    issue_stage(u + KT_NS - 1);
+    convert_stage(u + 1);
+
+    const unsigned char* s = ring[u % KT_NS];
+    rd_x(s, 0);
+    rd_w(s, 0, 0, fw[0], swr[0]);
+    // Tile t: the MFMA of t is issued, then tile t - 2 is dequantized (the
+    // two last tiles of a stage at the start of the next one; before the
+    // first stage these are zero contributions: scale pair (0, 0) maps the
+    // magic constant to exactly 0).  The next weight fragment is read one
+    // fragment (four tiles) ahead; group 1's activation fragment b is read
+    // right after its last use in group 0.
+#pragma unroll
+    for (int t = 0; t < 64; ++t) {
+      const int gi = t >> 5, a = (t >> 2) & 7, b = t & 3, idx = t >> 2;
+      dr[t & 3] = __builtin_amdgcn_mfma_i32_16x16x64_i8(fw[idx & 1], fx[b], cmagic, 0, 0, 0);
+      if (b == 0 && idx < 15) rd_w(s, (idx + 1) >> 3, (idx + 1) & 7, fw[(idx + 1) & 1], swr[(idx + 1) & 3]);
+      deq_tile((t + 62) & 63);
+      if (gi == 0 && a == 7) {
+        fx[b] = unpack_b64(*reinterpret_cast<const uint2*>(s + fx_off[1][b & 1] + (b >> 1) * 2048));
+        const float ax = *reinterpret_cast<const float*>(s + xs_off + 1024 + 64 * b);
+        xc[1][b] = make_float2(ax, -MAGIC_F * ax);
+      }
+    }
+  }
+  deq_tile(62);
+  deq_tile(63);
+  // drain the padding loads issued past the last stage before LDS is reused
+  __builtin_amdgcn_s_waitcnt(waitcnt_vm_lgkm0(0));
+  __syncthreads();
+  kt_epilogue<OUT_F32, NT, EPI>(acc, &ring[0][0], m0, n0, lora_act, lora_up, bias, M, N, rank, y, qa);
+}
+
 template <int ACT, int NT, int QM>
 void launch_k1_kernel(const void* x, const float* smooth_inv, const void* lora_down, int M, int K, int rank,
                       void* x_codes, void* x_scales, float* lora_act, size_t smem, hipStream_t st) {
@@ -750,29 +1168,50 @@ constexpr size_t K2_SMEM_EPI = static_cast<size_t>(K2_WAVES) * K2_WM * K2_WN * 2
 constexpr size_t K2_SMEM = sizeof(K2Smem) > K2_SMEM_EPI ? sizeof(K2Smem) : K2_SMEM_EPI;
 
 template <int OUT_F32, int NT, int EPI>
-void launch_k2_kernel(const void* xc, const void* xs, const void* wc, const void* ws, const float* la,
-                      const void* lu, const void* bias, int M, int N, int K, int rank, void* y,
-                      const QkvArgs& qa, hipStream_t st) {
+void launch_k2_t128(const void* xc, const void* xs, const void* wc, const void* ws, const float* la,
+                    const void* lu, const void* bias, int M, int N, int K, int rank, void* y,
+                    const QkvArgs& qa, hipStream_t st) {
   // the stage buffers exceed the default 64 KB of dynamic LDS: opt in once
   static const bool attr_ok = [] {
-    return hipFuncSetAttribute(reinterpret_cast<const void*>(k_gemm_w4a4_lora_up<OUT_F32, NT, EPI>),
+    return hipFuncSetAttribute(reinterpret_cast<const void*>(k_gemm_w4a4_lora_up_t128<OUT_F32, NT, EPI>),
                                hipFuncAttributeMaxDynamicSharedMemorySize,
                                static_cast<int>(K2_SMEM)) == hipSuccess;
   }();
   (void)attr_ok;
   const int nb = ((N + K2_BN - 1) / K2_BN) * ((M + K2_BM - 1) / K2_BM);
-  hipLaunchKernelGGL((k_gemm_w4a4_lora_up<OUT_F32, NT, EPI>), dim3(nb), dim3(K2_THREADS), K2_SMEM, st,
+  hipLaunchKernelGGL((k_gemm_w4a4_lora_up_t128<OUT_F32, NT, EPI>), dim3(nb), dim3(K2_THREADS), K2_SMEM, st,
                      static_cast<const uint8_t*>(xc), static_cast<const _Float16*>(xs),
                      static_cast<const uint8_t*>(wc), static_cast<const _Float16*>(ws), la,
                      static_cast<const uint16_t*>(lu), static_cast<const uint16_t*>(bias), M, N, K, rank, y, qa);
 }
 
+template <int OUT_F32, int NT, int EPI>
+void launch_k2_t256(const void* xc, const void* xs, const void* wc, const void* ws, const float* la,
+                    const void* lu, const void* bias, int M, int N, int K, int rank, void* y,
+                    const QkvArgs& qa, hipStream_t st) {
+  const int nb = ((N + KT_BN - 1) / KT_BN) * ((M + KT_BM - 1) / KT_BM);
+  hipLaunchKernelGGL((k_gemm_w4a4_lora_up<OUT_F32, NT, EPI>), dim3(nb), dim3(KT_THREADS), 0, st,
+                     static_cast<const uint8_t*>(xc), static_cast<const _Float16*>(xs),
+                     static_cast<const uint8_t*>(wc), static_cast<const _Float16*>(ws), la,
+                     static_cast<const uint16_t*>(lu), static_cast<const uint16_t*>(bias), M, N, K, rank, y, qa);
+}
+
+// 256 x 256 tiles when they give every CU at least one block and M is even
+// (that form reads the activation scales as aligned pairs); 128 x 128 tiles
+// otherwise.
 template <int OUT_F32, int EPI>
 int launch_k2(const void* xc, const void* xs, const void* wc, const void* ws, const float* la,
               const void* lu, const void* bias, int M, int N, int K, int rank, void* y, const QkvArgs& qa,
               hipStream_t st) {
-  if (rank == 0) launch_k2_kernel<OUT_F32, 0, EPI>(xc, xs, wc, ws, la, lu, bias, M, N, K, rank, y, qa, st);
-  else launch_k2_kernel<OUT_F32, 1, EPI>(xc, xs, wc, ws, la, lu, bias, M, N, K, rank, y, qa, st);
+  const long nb256 = static_cast<long>((M + KT_BM - 1) / KT_BM) * ((N + KT_BN - 1) / KT_BN);
+  const bool big = (M % 2 == 0) && nb256 >= 256;
+  if (big) {
+    if (rank == 0) launch_k2_t256<OUT_F32, 0, EPI>(xc, xs, wc, ws, la, lu, bias, M, N, K, rank, y, qa, st);
+    else launch_k2_t256<OUT_F32, 1, EPI>(xc, xs, wc, ws, la, lu, bias, M, N, K, rank, y, qa, st);
+  } else {
+    if (rank == 0) launch_k2_t128<OUT_F32, 0, EPI>(xc, xs, wc, ws, la, lu, bias, M, N, K, rank, y, qa, st);
+    else launch_k2_t128<OUT_F32, 1, EPI>(xc, xs, wc, ws, la, lu, bias, M, N, K, rank, y, qa, st);
+  }
   return hipGetLastError() == hipSuccess ? SVDQ_OK : SVDQ_ERR_HIP;
 }
 
