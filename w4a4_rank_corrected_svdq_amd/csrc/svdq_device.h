@@ -98,5 +98,8 @@ __device__ __forceinline__ void dma4(const DmaRsrc& r, uint32_t lds_addr, uint32
 
 // s_waitcnt immediate: vmcnt = v (0..63), expcnt and lgkmcnt = 0.
 constexpr int waitcnt_vm_lgkm0(int v) { return (v & 0xF) | ((v >> 4) << 14) | (0x0 << 4) | (0x0 << 8); }
+// s_waitcnt immediate: vmcnt = v (0..63) only; expcnt and lgkmcnt at their
+// maxima (no wait).
+constexpr int waitcnt_vm(int v) { return (v & 0xF) | ((v >> 4) << 14) | (0x7 << 4) | (0xF << 8); }
 
 }  // namespace

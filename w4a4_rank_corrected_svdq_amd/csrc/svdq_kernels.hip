@@ -215,6 +215,11 @@ __global__ __launch_bounds__(k1_waves<NT>() * 64) void k_quant_act_lora_down(
 // =====================================================================
 // Kernel 2
 // =====================================================================
+// Two tile forms.  The small form (k_gemm_w4a4_lora_up_t128), described
+// here, serves odd M and grids with fewer than 256 tiles of 256 x 256; the
+// large form further below keeps its arithmetic and changes how operands
+// reach LDS.
+//
 // Block tile 128 x 128, 4 waves in a 2 x 2 arrangement; each wave owns
 // 64 x 64 outputs = 4 x 4 tiles of 16 x 16.  Each tile is computed
 // transposed, Y^T = W^T X^T: the weight fragment is the MFMA A operand and
@@ -757,6 +762,12 @@ __device__ __forceinline__ void kt_epilogue(v4f (&acc)[KT_TA][KT_TB], unsigned c
     const int HD = N / 3;
     if (nw < 2 * HD) {
       const uint16_t* g = nw < HD ? qa.gq : qa.gk;
+      // the lane's norm weights (columns 16a + 4lq .. + 3 of the head, the
+      // same for every row), loaded once
+      uint2 gv[KT_TA];
+#pragma unroll
+      for (int a = 0; a < KT_TA; ++a) gv[a] = *reinterpret_cast<const uint2*>(g + a * 16 + 4 * lq);
+      const bool rot = qa.cos != nullptr;                      // uniform
 #pragma unroll
       for (int b = 0; b < KT_TB; ++b) {
         // sum of squares of the row over the head: this lane's 32 columns
@@ -769,14 +780,14 @@ __device__ __forceinline__ void kt_epilogue(v4f (&acc)[KT_TA][KT_TB], unsigned c
         t += __shfl_xor(t, 16);
         t += __shfl_xor(t, 32);
         const float scale = 1.0f / sqrtf(t * (1.0f / QKV_HEAD) + qa.eps);
-        const int row = mw + b * 16 + lr;
-        const bool rot = qa.cos != nullptr && row < M;
+        // rows past M are never stored: they read row M - 1's factors, so
+        // the rotation needs no per-lane branch
+        const int row = min(mw + b * 16 + lr, M - 1);
 #pragma unroll
         for (int a = 0; a < KT_TA; ++a) {
           const int ch = a * 16 + 4 * lq;                      // column within the head
-          const uint2 gv = *reinterpret_cast<const uint2*>(g + ch);
-          const float g4[4] = {bf16_bits_to_f32(gv.x & 0xFFFFu), bf16_bits_to_f32(gv.x >> 16),
-                               bf16_bits_to_f32(gv.y & 0xFFFFu), bf16_bits_to_f32(gv.y >> 16)};
+          const float g4[4] = {bf16_bits_to_f32(gv[a].x & 0xFFFFu), bf16_bits_to_f32(gv[a].x >> 16),
+                               bf16_bits_to_f32(gv[a].y & 0xFFFFu), bf16_bits_to_f32(gv[a].y >> 16)};
           float o[4];
 #pragma unroll
           for (int e = 0; e < 4; ++e) o[e] = acc[a][b][e] * scale * g4[e];
@@ -988,13 +999,13 @@ __global__ __launch_bounds__(KT_THREADS, 1) void k_gemm_w4a4_lora_up(
 #pragma unroll
   for (int b = 0; b < KT_TB; ++b) xc[0][b] = xc[1][b] = make_float2(0.f, 0.f);
 
-  auto rd_x = [&](const unsigned char* s, int gi) {   // activation fragments and scales of group gi
+  // Packed code fragments of a stage's first group (activation fragments
+  // 0 .. 3 and weight fragment 0), read before the barrier that opens it.
+  uint2 px[KT_TB], pw;
+  auto rd_first_codes = [&](const unsigned char* s) {
 #pragma unroll
-    for (int b = 0; b < KT_TB; ++b) {
-      fx[b] = unpack_b64(*reinterpret_cast<const uint2*>(s + fx_off[gi][b & 1] + (b >> 1) * 2048));
-      const float ax = *reinterpret_cast<const float*>(s + xs_off + gi * 1024 + 64 * b);
-      xc[gi][b] = make_float2(ax, -MAGIC_F * ax);
-    }
+    for (int b = 0; b < KT_TB; ++b) px[b] = *reinterpret_cast<const uint2*>(s + fx_off[0][b & 1] + (b >> 1) * 2048);
+    pw = *reinterpret_cast<const uint2*>(s + fw_off[0][0]);
   };
   auto rd_w = [&](const unsigned char* s, int gi, int a, v4i& f, float4& sw) {
     f = unpack_b64(*reinterpret_cast<const uint2*>(s + fw_off[gi][a & 1] + (a >> 1) * 2048));
@@ -1020,20 +1031,31 @@ __global__ __launch_bounds__(KT_THREADS, 1) void k_gemm_w4a4_lora_up(
   __builtin_amdgcn_s_barrier();
   asm volatile("" ::: "memory");
   convert_stage(0);
+  rd_first_codes(ring[0]);
+  __builtin_amdgcn_s_waitcnt(waitcnt_vm_lgkm0(KT_P * (KT_NS - 2)));
 
   for (int u = 0; u < S; ++u) {
     // stage u + 1 has landed once one stage of this wave's loads is still
     // outstanding; the barrier publishes it with stage u's fp32 scales and
-    // frees slot (u - 1) % KT_NS, which every wave has finished reading
-    __builtin_amdgcn_s_waitcnt(waitcnt_vm_lgkm0(KT_P * (KT_NS - 3)));
+    // frees slot (u - 1) % KT_NS, which every wave has finished reading.
+    // LDS operations need no wait here: the scale writes of the previous
+    // stage's conversion precede reads that were waited for, and the code
+    // fragments read for this stage may still be in flight.
+    __builtin_amdgcn_s_waitcnt(waitcnt_vm(KT_P * (KT_NS - 3)));
     __builtin_amdgcn_s_barrier();
     asm volatile("" ::: "memory");
     issue_stage(u + KT_NS - 1);
     convert_stage(u + 1);
 
     const unsigned char* s = ring[u % KT_NS];
-    rd_x(s, 0);
-    rd_w(s, 0, 0, fw[0], swr[0]);
+#pragma unroll
+    for (int b = 0; b < KT_TB; ++b) {
+      fx[b] = unpack_b64(px[b]);
+      const float ax = *reinterpret_cast<const float*>(s + xs_off + 64 * b);
+      xc[0][b] = make_float2(ax, -MAGIC_F * ax);
+    }
+    fw[0] = unpack_b64(pw);
+    swr[0] = *reinterpret_cast<const float4*>(s + ws_off);
     // Tile t: the MFMA of t is issued, then tile t - 2 is dequantized (the
     // two last tiles of a stage at the start of the next one; before the
     // first stage these are zero contributions: scale pair (0, 0) maps the
@@ -1052,6 +1074,8 @@ __global__ __launch_bounds__(KT_THREADS, 1) void k_gemm_w4a4_lora_up(
         xc[1][b] = make_float2(ax, -MAGIC_F * ax);
       }
     }
+    // stage u + 1's codes landed before this stage began
+    rd_first_codes(ring[(u + 1) % KT_NS]);
   }
   deq_tile(62);
   deq_tile(63);
