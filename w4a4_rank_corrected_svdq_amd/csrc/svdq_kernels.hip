@@ -694,22 +694,39 @@ static_assert(KT_STAGE % 16 == 0, "stage buffers stay 16-byte aligned");
 static_assert(KT_WAVES * KT_WM * KT_WN * 2 <= KT_NS * KT_STAGE, "the output tiles reuse the stage ring");
 static_assert(2 * (KT_BM + KT_BN) == 2 * KT_THREADS, "two scale conversions per thread per stage");
 
-// Epilogue of the large form: up projection, bias, fused QKV normalization
-// and rotation, store.  acc[a][b][e] holds output row m0 + 64 wm + 16b +
-// (lane & 15), column n0 + 128 wn + 16a + 4(lane >> 4) + e.  The LDS passed
-// in is free.
-template <int OUT_F32, int NT, int EPI>
-__device__ __forceinline__ void kt_epilogue(v4f (&acc)[KT_TA][KT_TB], unsigned char* smem, int m0, int n0,
+// Start values of the large form's accumulators: bias, then the up
+// projection (X_hat L1) L2 on bf16 MFMA.  Computed before the K loop, while
+// the first stages load, so that the latency of these reads is not exposed
+// at the end of the tile.  acc[a][b][e] is output row m0 + 64 wm + 16b +
+// (lane & 15), column n0 + 128 wn + 16a + 4(lane >> 4) + e.
+template <int NT>
+__device__ __forceinline__ void kt_init_acc(v4f (&acc)[KT_TA][KT_TB], int m0, int n0,
                                             const float* __restrict__ lora_act,
                                             const uint16_t* __restrict__ lora_up,
-                                            const uint16_t* __restrict__ bias, int M, int N, int rank,
-                                            void* __restrict__ y, const QkvArgs& qa) {
-  const int tid = threadIdx.x;
-  const int lane = tid & 63;
-  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+                                            const uint16_t* __restrict__ bias, int M, int N, int rank) {
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(static_cast<int>(threadIdx.x) >> 6);
   const int wm = wave >> 1, wn = wave & 1;
   const int lr = lane & 15, lq = lane >> 4;
   const int mw = m0 + wm * KT_WM, nw = n0 + wn * KT_WN;
+#pragma unroll
+  for (int a = 0; a < KT_TA; ++a)
+#pragma unroll
+    for (int b = 0; b < KT_TB; ++b) acc[a][b] = v4f{0.f, 0.f, 0.f, 0.f};
+  if (bias) {
+#pragma unroll
+    for (int a = 0; a < KT_TA; ++a) {
+      const int c = nw + a * 16 + 4 * lq;      // N % 8 == 0: all four in or out
+      if (c >= N) continue;
+      const uint2 bv = *reinterpret_cast<const uint2*>(bias + c);
+      const float b4[4] = {bf16_bits_to_f32(bv.x & 0xFFFFu), bf16_bits_to_f32(bv.x >> 16),
+                           bf16_bits_to_f32(bv.y & 0xFFFFu), bf16_bits_to_f32(bv.y >> 16)};
+#pragma unroll
+      for (int b = 0; b < KT_TB; ++b)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) acc[a][b][e] = b4[e];
+    }
+  }
   // up projection: bf16 MFMA 16x16x32 over the rank in slices of 32 (ranks
   // are multiples of 16, so the lanes of a slice past the rank load zeros);
   // lora_up rows are the A operand, lora_act rows the B operand
@@ -742,20 +759,21 @@ __device__ __forceinline__ void kt_epilogue(v4f (&acc)[KT_TA][KT_TB], unsigned c
       }
     }
   }
-  if (bias) {
-#pragma unroll
-    for (int a = 0; a < KT_TA; ++a) {
-      const int c = nw + a * 16 + 4 * lq;      // N % 8 == 0: all four in or out
-      if (c >= N) continue;
-      const uint2 bv = *reinterpret_cast<const uint2*>(bias + c);
-      const float b4[4] = {bf16_bits_to_f32(bv.x & 0xFFFFu), bf16_bits_to_f32(bv.x >> 16),
-                           bf16_bits_to_f32(bv.y & 0xFFFFu), bf16_bits_to_f32(bv.y >> 16)};
-#pragma unroll
-      for (int b = 0; b < KT_TB; ++b)
-#pragma unroll
-        for (int e = 0; e < 4; ++e) acc[a][b][e] += b4[e];
-    }
-  }
+}
+
+// Epilogue of the large form: fused QKV normalization and rotation, store
+// (bias and the up projection are already in the accumulators).  acc[a][b][e] holds output row m0 + 64 wm + 16b +
+// (lane & 15), column n0 + 128 wn + 16a + 4(lane >> 4) + e.  The LDS passed
+// in is free.
+template <int OUT_F32, int EPI>
+__device__ __forceinline__ void kt_epilogue(v4f (&acc)[KT_TA][KT_TB], unsigned char* smem, int m0, int n0,
+                                            int M, int N, void* __restrict__ y, const QkvArgs& qa) {
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int wm = wave >> 1, wn = wave & 1;
+  const int lr = lane & 15, lq = lane >> 4;
+  const int mw = m0 + wm * KT_WM, nw = n0 + wn * KT_WN;
   if constexpr (EPI == 1) {
     // The wave's 128 columns are one head (N = 3 * heads * 128): Q heads,
     // then K heads, then V heads, which are left as projected.
@@ -963,10 +981,6 @@ __global__ __launch_bounds__(KT_THREADS, 1) void k_gemm_w4a4_lora_up(
   };
 
   v4f acc[KT_TA][KT_TB];
-#pragma unroll
-  for (int a = 0; a < KT_TA; ++a)
-#pragma unroll
-    for (int b = 0; b < KT_TB; ++b) acc[a][b] = v4f{0.f, 0.f, 0.f, 0.f};
   v4i cmagic = v4i{MAGIC_I, MAGIC_I, MAGIC_I, MAGIC_I};
   asm volatile("" : "+v"(cmagic));
 
@@ -1024,9 +1038,11 @@ __global__ __launch_bounds__(KT_THREADS, 1) void k_gemm_w4a4_lora_up(
     deq(xc[gi][b], swr[a & 3], dr[q & 3], acc[a][b]);
   };
 
-  // stages 0 .. 2 in flight; stage 0 landed and its scales converted
+  // stages 0 .. 2 in flight; bias and up projection into the accumulators
+  // meanwhile; stage 0 landed and its scales converted
 #pragma unroll
   for (int st = 0; st < KT_NS - 1; ++st) issue_stage(st);
+  kt_init_acc<NT>(acc, m0, n0, lora_act, lora_up, bias, M, N, rank);
   __builtin_amdgcn_s_waitcnt(waitcnt_vm_lgkm0(KT_P * (KT_NS - 2)));
   __builtin_amdgcn_s_barrier();
   asm volatile("" ::: "memory");
@@ -1082,7 +1098,7 @@ __global__ __launch_bounds__(KT_THREADS, 1) void k_gemm_w4a4_lora_up(
   // drain the padding loads issued past the last stage before LDS is reused
   __builtin_amdgcn_s_waitcnt(waitcnt_vm_lgkm0(0));
   __syncthreads();
-  kt_epilogue<OUT_F32, NT, EPI>(acc, &ring[0][0], m0, n0, lora_act, lora_up, bias, M, N, rank, y, qa);
+  kt_epilogue<OUT_F32, EPI>(acc, &ring[0][0], m0, n0, M, N, y, qa);
 }
 
 template <int ACT, int NT, int QM>
