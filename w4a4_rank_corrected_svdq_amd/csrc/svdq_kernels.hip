@@ -945,9 +945,9 @@ __global__ __launch_bounds__(KT_THREADS, 1) void k_gemm_w4a4_lora_up(
     s_lds[i] = __builtin_amdgcn_readfirstlane(ring0 + (isx ? KT_SX_OFF : KT_SW_OFF) + 4 * (gi * 256 + 64 * ch));
   }
 
-  // Issue the DMA loads of stage st into ring slot st % KT_NS.
-  auto issue_stage = [&](int st) {
-    const uint32_t so = static_cast<uint32_t>(st % KT_NS) * KT_STAGE;
+  // Issue the DMA loads of stage st into ring slot `slot` = st % KT_NS.
+  auto issue_stage = [&](int st, int slot) {
+    const uint32_t so = static_cast<uint32_t>(slot) * KT_STAGE;
     const bool live = st < S;
     const uint32_t ko = static_cast<uint32_t>(st) * 64u;
 #pragma unroll
@@ -970,8 +970,8 @@ __global__ __launch_bounds__(KT_THREADS, 1) void k_gemm_w4a4_lora_up(
   // t owns activation scale t (group t / 256, row t % 256) and weight scale
   // t; the fp16 value is the half (row & 1) of its dword (M, N, m0 and n0
   // even).
-  auto convert_stage = [&](int st) {
-    uint32_t* sc = reinterpret_cast<uint32_t*>(&ring[st % KT_NS][KT_SX_OFF]);
+  auto convert_stage = [&](int slot) {
+    uint32_t* sc = reinterpret_cast<uint32_t*>(&ring[slot][KT_SX_OFF]);
     const uint32_t dx = sc[tid], dw = sc[KT_THREADS + tid];
     const int sh = 16 * (tid & 1);
     const float fx = static_cast<float>(__builtin_bit_cast(_Float16, static_cast<uint16_t>(dx >> sh)));
@@ -1041,7 +1041,7 @@ __global__ __launch_bounds__(KT_THREADS, 1) void k_gemm_w4a4_lora_up(
   // stages 0 .. 2 in flight; bias and up projection into the accumulators
   // meanwhile; stage 0 landed and its scales converted
 #pragma unroll
-  for (int st = 0; st < KT_NS - 1; ++st) issue_stage(st);
+  for (int st = 0; st < KT_NS - 1; ++st) issue_stage(st, st);
   kt_init_acc<NT>(acc, m0, n0, lora_act, lora_up, bias, M, N, rank);
   __builtin_amdgcn_s_waitcnt(waitcnt_vm_lgkm0(KT_P * (KT_NS - 2)));
   __builtin_amdgcn_s_barrier();
@@ -1060,8 +1060,8 @@ __global__ __launch_bounds__(KT_THREADS, 1) void k_gemm_w4a4_lora_up(
     __builtin_amdgcn_s_waitcnt(waitcnt_vm(KT_P * (KT_NS - 3)));
     __builtin_amdgcn_s_barrier();
     asm volatile("" ::: "memory");
-    issue_stage(u + KT_NS - 1);
-    convert_stage(u + 1);
+    issue_stage(u + KT_NS - 1, (u + KT_NS - 1) % KT_NS);
+    convert_stage((u + 1) % KT_NS);
 
     const unsigned char* s = ring[u % KT_NS];
 #pragma unroll

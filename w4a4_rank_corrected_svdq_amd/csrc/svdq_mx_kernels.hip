@@ -177,18 +177,63 @@ __global__ __launch_bounds__(MxCfg<BM>::THREADS, BM == 256 ? 1 : 2) void k_gemm_
   };
 
   v16f acc[MX_TI][MX_TJ];
-#pragma unroll
-  for (int i = 0; i < MX_TI; ++i)
-#pragma unroll
-    for (int j = 0; j < MX_TJ; ++j)
-#pragma unroll
-      for (int v = 0; v < 16; ++v) acc[i][j][v] = 0.f;
-
   const int fr = lane & 31;      // fragment row within a 32-row tile
   const int fk = lane >> 5;      // which 32-k block of the k-step
 
 #pragma unroll
   for (int st = 0; st < C::NS - 1; ++st) issue_stage(st, st);
+
+  // The accumulators start as bias + bf16(lora_act) L2, computed while the
+  // first stages load: a lane holds output row m0 + 64 wm + 32 i + fr and
+  // columns 32 j + 8 bb + 4 fk + (0..3) of each 32-column tile.  The up
+  // projection runs on bf16 MFMA 32x32x16 (K = rank in slices of 16),
+  // transposed like the main product.
+#pragma unroll
+  for (int i = 0; i < MX_TI; ++i)
+#pragma unroll
+    for (int j = 0; j < MX_TJ; ++j)
+#pragma unroll
+      for (int bb = 0; bb < 4; ++bb) {
+        const int c = n0 + wn * MX_WN + j * 32 + 8 * bb + 4 * fk;
+        float b4[4] = {0.f, 0.f, 0.f, 0.f};
+        if (bias && c < N) {
+          const uint2 bv = *reinterpret_cast<const uint2*>(bias + c);
+          b4[0] = bf16_bits_to_f32(bv.x & 0xFFFFu);
+          b4[1] = bf16_bits_to_f32(bv.x >> 16);
+          b4[2] = bf16_bits_to_f32(bv.y & 0xFFFFu);
+          b4[3] = bf16_bits_to_f32(bv.y >> 16);
+        }
+#pragma unroll
+        for (int e = 0; e < 4; ++e) acc[i][j][4 * bb + e] = b4[e];
+      }
+  if constexpr (HAS_RANK) {
+    for (int kk = 0; kk < rank; kk += 16) {
+      const int kl = kk + fk * 8;
+      v8bf la[MX_TI];
+#pragma unroll
+      for (int i = 0; i < MX_TI; ++i) {
+        const int r = m0 + wm * MX_WM + i * 32 + fr;
+        float v[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+        if (r < M) {
+          const float4* p = reinterpret_cast<const float4*>(lora_act + static_cast<size_t>(r) * rank + kl);
+          const float4 v0 = p[0], v1 = p[1];
+          v[0] = v0.x; v[1] = v0.y; v[2] = v0.z; v[3] = v0.w;
+          v[4] = v1.x; v[5] = v1.y; v[6] = v1.z; v[7] = v1.w;
+        }
+        la[i] = pack_bf16x8(v);
+      }
+#pragma unroll
+      for (int j = 0; j < MX_TJ; ++j) {
+        const int c = n0 + wn * MX_WN + j * 32 + fr;
+        uint4 u = make_uint4(0, 0, 0, 0);
+        if (c < N) u = *reinterpret_cast<const uint4*>(lora_up + static_cast<size_t>(c) * rank + kl);
+        const v8bf ub = __builtin_bit_cast(v8bf, u);
+#pragma unroll
+        for (int i = 0; i < MX_TI; ++i)
+          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ub, la[i], acc[i][j], 0, 0, 0);
+      }
+    }
+  }
 
   for (int st0 = 0; st0 < S; st0 += C::NS) {
 #pragma unroll
@@ -249,39 +294,7 @@ __global__ __launch_bounds__(MxCfg<BM>::THREADS, BM == 256 ? 1 : 2) void k_gemm_
   __builtin_amdgcn_s_waitcnt(waitcnt_vm_lgkm0(0));
   __syncthreads();
 
-  // ---- epilogue: up projection on bf16 MFMA 32x32x16 (K = rank in slices
-  // of 16), transposed like the main product.
-  const int fk8 = fk;
-  if constexpr (HAS_RANK) {
-    for (int kk = 0; kk < rank; kk += 16) {
-      const int kl = kk + fk8 * 8;
-      v8bf la[MX_TI];
-#pragma unroll
-      for (int i = 0; i < MX_TI; ++i) {
-        const int r = m0 + wm * MX_WM + i * 32 + fr;
-        float v[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
-        if (r < M) {
-          const float4* p = reinterpret_cast<const float4*>(lora_act + static_cast<size_t>(r) * rank + kl);
-          const float4 v0 = p[0], v1 = p[1];
-          v[0] = v0.x; v[1] = v0.y; v[2] = v0.z; v[3] = v0.w;
-          v[4] = v1.x; v[5] = v1.y; v[6] = v1.z; v[7] = v1.w;
-        }
-        la[i] = pack_bf16x8(v);
-      }
-#pragma unroll
-      for (int j = 0; j < MX_TJ; ++j) {
-        const int c = n0 + wn * MX_WN + j * 32 + fr;
-        uint4 u = make_uint4(0, 0, 0, 0);
-        if (c < N) u = *reinterpret_cast<const uint4*>(lora_up + static_cast<size_t>(c) * rank + kl);
-        const v8bf ub = __builtin_bit_cast(v8bf, u);
-#pragma unroll
-        for (int i = 0; i < MX_TI; ++i)
-          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ub, la[i], acc[i][j], 0, 0, 0);
-      }
-    }
-  }
-
-  // ---- bias and store.  A lane holds output row m and columns
+  // ---- store.  A lane holds output row m and columns
   // 8b + 4 fk + (0..3) of each 32-column tile.  bf16 output goes through
   // LDS: each wave writes its 64 x 128 tile with 8-byte writes, then stores
   // whole 256-byte row segments, four rows per instruction; 16-byte chunk
@@ -300,13 +313,6 @@ __global__ __launch_bounds__(MxCfg<BM>::THREADS, BM == 256 ? 1 : 2) void k_gemm_
           float o[4];
 #pragma unroll
           for (int e = 0; e < 4; ++e) o[e] = acc[i][j][4 * bb + e];
-          if (bias) {
-            const uint2 bv = *reinterpret_cast<const uint2*>(bias + c);
-            o[0] += bf16_bits_to_f32(bv.x & 0xFFFFu);
-            o[1] += bf16_bits_to_f32(bv.x >> 16);
-            o[2] += bf16_bits_to_f32(bv.y & 0xFFFFu);
-            o[3] += bf16_bits_to_f32(bv.y >> 16);
-          }
           *reinterpret_cast<float4*>(reinterpret_cast<float*>(y) + static_cast<size_t>(row) * N + c) =
               make_float4(o[0], o[1], o[2], o[3]);
         }
@@ -325,13 +331,6 @@ __global__ __launch_bounds__(MxCfg<BM>::THREADS, BM == 256 ? 1 : 2) void k_gemm_
           float o[4];
 #pragma unroll
           for (int e = 0; e < 4; ++e) o[e] = acc[i][j][4 * bb + e];
-          if (bias && c < N) {
-            const uint2 bv = *reinterpret_cast<const uint2*>(bias + c);
-            o[0] += bf16_bits_to_f32(bv.x & 0xFFFFu);
-            o[1] += bf16_bits_to_f32(bv.x >> 16);
-            o[2] += bf16_bits_to_f32(bv.y & 0xFFFFu);
-            o[3] += bf16_bits_to_f32(bv.y >> 16);
-          }
           const int chunk = j * 4 + bb;                 // 16-byte chunk of the 256-byte tile row
           tile[rl * 32 + ((chunk ^ (rl & 15)) << 1) + fk] =
               make_uint2(f32_to_bf16_bits(o[0]) | (f32_to_bf16_bits(o[1]) << 16),
