@@ -181,7 +181,7 @@ def test_k2_output_parity(rank, bias, out):
 
 
 # Kernel 2 has two tile forms: 256 x 256 (8 waves) when M is even and the
-# grid has at least 256 such tiles, 128 x 128 otherwise.  These cases put the
+# grid has at least 192 such tiles, 128 x 128 otherwise.  These cases put the
 # large form on ragged M and N edges (4000 = 15.6 tiles, 4104 = 16.03 tiles)
 # with an odd group count (K = 192) and every epilogue option, and compare
 # every output with the oracle.

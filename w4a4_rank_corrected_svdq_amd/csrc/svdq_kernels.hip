@@ -216,7 +216,7 @@ __global__ __launch_bounds__(k1_waves<NT>() * 64) void k_quant_act_lora_down(
 // Kernel 2
 // =====================================================================
 // Two tile forms.  The small form (k_gemm_w4a4_lora_up_t128), described
-// here, serves odd M and grids with fewer than 256 tiles of 256 x 256; the
+// here, serves odd M and grids with fewer than 192 tiles of 256 x 256; the
 // large form further below keeps its arithmetic and changes how operands
 // reach LDS.
 //
@@ -1236,15 +1236,17 @@ void launch_k2_t256(const void* xc, const void* xs, const void* wc, const void* 
                      static_cast<const uint16_t*>(lu), static_cast<const uint16_t*>(bias), M, N, K, rank, y, qa);
 }
 
-// 256 x 256 tiles when they give every CU at least one block and M is even
-// (that form reads the activation scales as aligned pairs); 128 x 128 tiles
-// otherwise.
+// 256 x 256 tiles when they occupy at least three quarters of the CUs and M
+// is even (that form reads the activation scales as aligned pairs); 128 x 128
+// tiles otherwise.  At 192 tiles of 256 x 256 (M = 4096, N = 3072) the two
+// forms take the same time for K = 3072 and the large one is 4 % faster for
+// K = 12288; far below that the small form's extra blocks win.
 template <int OUT_F32, int EPI>
 int launch_k2(const void* xc, const void* xs, const void* wc, const void* ws, const float* la,
               const void* lu, const void* bias, int M, int N, int K, int rank, void* y, const QkvArgs& qa,
               hipStream_t st) {
   const long nb256 = static_cast<long>((M + KT_BM - 1) / KT_BM) * ((N + KT_BN - 1) / KT_BN);
-  const bool big = (M % 2 == 0) && nb256 >= 256;
+  const bool big = (M % 2 == 0) && nb256 >= 192;
   if (big) {
     if (rank == 0) launch_k2_t256<OUT_F32, 0, EPI>(xc, xs, wc, ws, la, lu, bias, M, N, K, rank, y, qa, st);
     else launch_k2_t256<OUT_F32, 1, EPI>(xc, xs, wc, ws, la, lu, bias, M, N, K, rank, y, qa, st);
