@@ -183,14 +183,18 @@ def test_k2_output_parity(rank, bias, out):
 # Kernel 2 has two tile forms: 256 x 256 (8 waves) when M is even and the
 # grid has at least 192 such tiles, 128 x 128 otherwise.  These cases put the
 # large form on ragged M and N edges (4000 = 15.6 tiles, 4104 = 16.03 tiles)
-# with an odd group count (K = 192) and every epilogue option, and compare
+# with odd and single group counts and every epilogue option, and compare
 # every output with the oracle.
-LARGE_FORM = (4000, 192, 4104)
+LARGE_FORM = (4000, 4104)
 
 
-@pytest.mark.parametrize("rank,bias,out", [(0, False, "bf16"), (32, True, "bf16"), (48, True, "f32")])
-def test_k2_large_form_parity(rank, bias, out):
-    M, K, N = LARGE_FORM
+@pytest.mark.parametrize("rank,bias,out,K", [(0, False, "bf16", 192), (32, True, "bf16", 192),
+                                             (48, True, "f32", 192), (16, False, "bf16", 64),
+                                             (32, False, "f32", 128), (256, True, "bf16", 320)])
+def test_k2_large_form_parity(rank, bias, out, K):
+    """K = 64 and 128 are one stage (the second group of K = 64 is past K);
+    rank 256 runs the up projection in eight slices before the K loop."""
+    M, N = LARGE_FORM
     wl, Lr, po, abi = _small_case(M, K, N, rank, seed=60 + rank, bias=bias)
     Yo, parts = O.forward(wl.x, po, bias=Lr.bias, out=("f32" if out == "f32" else "bf16"), return_parts=True)
     xc = dev(O.pack_int4(parts["qx"]))
