@@ -63,11 +63,11 @@ __global__ __launch_bounds__(256) void k_awq_act(const uint16_t* __restrict__ x,
     uint32_t hv[32];
 #pragma unroll
     for (int i = 0; i < 32; ++i) {
-      const uint32_t b0 = f32_to_bf16_bits(bf16_bits_to_f32(xw[i] & 0xFFFFu) * sf[2 * i]);
-      const uint32_t b1 = f32_to_bf16_bits(bf16_bits_to_f32(xw[i] >> 16) * sf[2 * i + 1]);
-      s += bf16_bits_to_f32(b0);
-      s += bf16_bits_to_f32(b1);
-      hv[i] = b0 | (b1 << 16);
+      const uint32_t p = bf16x2_bits(bf16_bits_to_f32(xw[i] & 0xFFFFu) * sf[2 * i],
+                                     bf16_bits_to_f32(xw[i] >> 16) * sf[2 * i + 1]);
+      s += bf16_bits_to_f32(p & 0xFFFFu);
+      s += bf16_bits_to_f32(p >> 16);
+      hv[i] = p;
     }
     uint4* hr = reinterpret_cast<uint4*>(x_hat + static_cast<size_t>(m) * K + g * AWQ_GROUP);
 #pragma unroll

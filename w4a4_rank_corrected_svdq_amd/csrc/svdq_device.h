@@ -24,11 +24,19 @@ __device__ __forceinline__ uint32_t f32_to_bf16_bits(float f) {
   return static_cast<uint32_t>(__builtin_bit_cast(unsigned short, b));
 }
 
+typedef float v2f __attribute__((ext_vector_type(2)));
+typedef __bf16 v2bf __attribute__((ext_vector_type(2)));
+
+// Two fp32 -> one dword of bf16 bits (a in the low half), round to nearest
+// even: one v_cvt_pk_bf16_f32.
+__device__ __forceinline__ uint32_t bf16x2_bits(float a, float b) {
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector(v2f{a, b}, v2bf));
+}
+
 __device__ __forceinline__ v8bf pack_bf16x8(const float* v) {
-  v8s s;
-#pragma unroll
-  for (int i = 0; i < 8; ++i) s[i] = static_cast<short>(f32_to_bf16_bits(v[i]));
-  return __builtin_bit_cast(v8bf, s);
+  const uint4 u = make_uint4(bf16x2_bits(v[0], v[1]), bf16x2_bits(v[2], v[3]), bf16x2_bits(v[4], v[5]),
+                             bf16x2_bits(v[6], v[7]));
+  return __builtin_bit_cast(v8bf, u);
 }
 
 __device__ __forceinline__ float gelu_tanh(float x) {

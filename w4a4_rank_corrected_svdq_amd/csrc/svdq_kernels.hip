@@ -454,8 +454,8 @@ __device__ __forceinline__ void k2_epilogue(v4f (&acc)[K2_TA][K2_TB], unsigned c
       for (int a = 0; a < K2_TA; ++a) {
         const int chunk = 2 * a + (lq >> 1);          // 16-byte chunk of the 128-byte tile row
         tile[rl * 16 + ((chunk ^ (rl & 7)) << 1) + (lq & 1)] =
-            make_uint2(f32_to_bf16_bits(acc[a][b][0]) | (f32_to_bf16_bits(acc[a][b][1]) << 16),
-                       f32_to_bf16_bits(acc[a][b][2]) | (f32_to_bf16_bits(acc[a][b][3]) << 16));
+            make_uint2(bf16x2_bits(acc[a][b][0], acc[a][b][1]),
+                       bf16x2_bits(acc[a][b][2], acc[a][b][3]));
       }
     }
     // the reads below are of another type than the writes above: keep the
@@ -847,8 +847,8 @@ __device__ __forceinline__ void kt_epilogue(v4f (&acc)[KT_TA][KT_TB], unsigned c
       for (int a = 0; a < KT_TA; ++a) {
         const int chunk = 2 * a + (lq >> 1);
         tile[rl * 32 + ((chunk ^ (rl & 15)) << 1) + (lq & 1)] =
-            make_uint2(f32_to_bf16_bits(acc[a][b][0]) | (f32_to_bf16_bits(acc[a][b][1]) << 16),
-                       f32_to_bf16_bits(acc[a][b][2]) | (f32_to_bf16_bits(acc[a][b][3]) << 16));
+            make_uint2(bf16x2_bits(acc[a][b][0], acc[a][b][1]),
+                       bf16x2_bits(acc[a][b][2], acc[a][b][3]));
       }
     }
     // the reads below are of another type than the writes above: keep the
@@ -1194,8 +1194,8 @@ __global__ __launch_bounds__(256) void k_lora_up_add(const float* __restrict__ l
       for (int bb = 0; bb < 4; ++bb) {
         const int c = n0 + j * 32 + 8 * bb + 4 * fk;
         if (c >= N) continue;
-        const uint32_t lo = f32_to_bf16_bits(acc[i][j][4 * bb + 0]) | (f32_to_bf16_bits(acc[i][j][4 * bb + 1]) << 16);
-        const uint32_t hi = f32_to_bf16_bits(acc[i][j][4 * bb + 2]) | (f32_to_bf16_bits(acc[i][j][4 * bb + 3]) << 16);
+        const uint32_t lo = bf16x2_bits(acc[i][j][4 * bb + 0], acc[i][j][4 * bb + 1]);
+        const uint32_t hi = bf16x2_bits(acc[i][j][4 * bb + 2], acc[i][j][4 * bb + 3]);
         *reinterpret_cast<uint2*>(y + static_cast<size_t>(row) * N + c) = make_uint2(lo, hi);
       }
     }

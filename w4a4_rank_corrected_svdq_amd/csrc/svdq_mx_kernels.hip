@@ -333,8 +333,8 @@ __global__ __launch_bounds__(MxCfg<BM>::THREADS, BM == 256 ? 1 : 2) void k_gemm_
           for (int e = 0; e < 4; ++e) o[e] = acc[i][j][4 * bb + e];
           const int chunk = j * 4 + bb;                 // 16-byte chunk of the 256-byte tile row
           tile[rl * 32 + ((chunk ^ (rl & 15)) << 1) + fk] =
-              make_uint2(f32_to_bf16_bits(o[0]) | (f32_to_bf16_bits(o[1]) << 16),
-                         f32_to_bf16_bits(o[2]) | (f32_to_bf16_bits(o[3]) << 16));
+              make_uint2(bf16x2_bits(o[0], o[1]),
+                         bf16x2_bits(o[2], o[3]));
         }
       }
     }
