@@ -38,7 +38,7 @@ COLD_ITERS = 20
 # MI355X the step time falls from ~305 to ~260 us over the first ~30 ms of
 # sustained work (and rises again after about a second idle), so a fixed
 # number of warmup steps alone can leave the timed steps in that ramp.
-SETTLE_S = 0.05
+SETTLE_S = 0.1
 
 
 def settle(step, seconds=SETTLE_S):
