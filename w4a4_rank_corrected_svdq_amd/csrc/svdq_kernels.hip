@@ -778,6 +778,33 @@ __device__ __forceinline__ void kt_epilogue(v4f (&acc)[KT_TA][KT_TB], unsigned c
     // The wave's 128 columns are one head (N = 3 * heads * 128): Q heads,
     // then K heads, then V heads, which are left as projected.
     const int HD = N / 3;
+    const bool rot = qa.cos != nullptr;                        // uniform
+    // The rotary factors of the block's 256 rows go to LDS with coalesced
+    // 16-byte loads, all issued before any is stored: 16-byte chunk c of row
+    // r sits at chunk c ^ (r & 15) of its 256-byte row, which keeps the
+    // per-lane reads below free of bank conflicts.  Rows past M read row
+    // M - 1 (never stored).  Blocks whose columns are all V skip it.
+    float4* lcs = reinterpret_cast<float4*>(smem);              // [256][16] cos
+    float4* lsn = lcs + KT_BM * 16;                             // [256][16] sin
+    const bool stage = rot && n0 < 2 * HD;                      // uniform per block
+    if (stage) {
+      constexpr int IT = KT_BM * 16 / KT_THREADS;
+      float4 cv[IT], sv[IT];
+#pragma unroll
+      for (int j = 0; j < IT; ++j) {
+        const int i = tid + j * KT_THREADS, r = i >> 4, c = i & 15;
+        const size_t row = static_cast<size_t>(min(m0 + r, M - 1));
+        cv[j] = reinterpret_cast<const float4*>(qa.cos + row * 64)[c];
+        sv[j] = reinterpret_cast<const float4*>(qa.sin + row * 64)[c];
+      }
+#pragma unroll
+      for (int j = 0; j < IT; ++j) {
+        const int i = tid + j * KT_THREADS, r = i >> 4, c = i & 15;
+        lcs[r * 16 + (c ^ (r & 15))] = cv[j];
+        lsn[r * 16 + (c ^ (r & 15))] = sv[j];
+      }
+      __syncthreads();
+    }
     if (nw < 2 * HD) {
       const uint16_t* g = nw < HD ? qa.gq : qa.gk;
       // the lane's norm weights (columns 16a + 4lq .. + 3 of the head, the
@@ -785,7 +812,6 @@ __device__ __forceinline__ void kt_epilogue(v4f (&acc)[KT_TA][KT_TB], unsigned c
       uint2 gv[KT_TA];
 #pragma unroll
       for (int a = 0; a < KT_TA; ++a) gv[a] = *reinterpret_cast<const uint2*>(g + a * 16 + 4 * lq);
-      const bool rot = qa.cos != nullptr;                      // uniform
 #pragma unroll
       for (int b = 0; b < KT_TB; ++b) {
         // sum of squares of the row over the head: this lane's 32 columns
@@ -798,20 +824,20 @@ __device__ __forceinline__ void kt_epilogue(v4f (&acc)[KT_TA][KT_TB], unsigned c
         t += __shfl_xor(t, 16);
         t += __shfl_xor(t, 32);
         const float scale = 1.0f / sqrtf(t * (1.0f / QKV_HEAD) + qa.eps);
-        // rows past M are never stored: they read row M - 1's factors, so
-        // the rotation needs no per-lane branch
-        const int row = min(mw + b * 16 + lr, M - 1);
+        const int rl = wm * KT_WM + b * 16 + lr;               // row within the block
 #pragma unroll
         for (int a = 0; a < KT_TA; ++a) {
-          const int ch = a * 16 + 4 * lq;                      // column within the head
           const float g4[4] = {bf16_bits_to_f32(gv[a].x & 0xFFFFu), bf16_bits_to_f32(gv[a].x >> 16),
                                bf16_bits_to_f32(gv[a].y & 0xFFFFu), bf16_bits_to_f32(gv[a].y >> 16)};
           float o[4];
 #pragma unroll
           for (int e = 0; e < 4; ++e) o[e] = acc[a][b][e] * scale * g4[e];
           if (rot) {
-            const float2 cs = *reinterpret_cast<const float2*>(qa.cos + static_cast<size_t>(row) * 64 + (ch >> 1));
-            const float2 sn = *reinterpret_cast<const float2*>(qa.sin + static_cast<size_t>(row) * 64 + (ch >> 1));
+            // columns 16a + 4lq .. + 3 rotate by factors 8a + 2lq and + 1:
+            // chunk 2a + lq / 2 of the row, half lq % 2
+            const int pos = rl * 16 + ((2 * a + (lq >> 1)) ^ (rl & 15));
+            const float2 cs = reinterpret_cast<const float2*>(lcs + pos)[lq & 1];
+            const float2 sn = reinterpret_cast<const float2*>(lsn + pos)[lq & 1];
             const float a0 = o[0] * cs.x - o[1] * sn.x, a1 = o[1] * cs.x + o[0] * sn.x;
             const float a2 = o[2] * cs.y - o[3] * sn.y, a3 = o[3] * cs.y + o[2] * sn.y;
             o[0] = a0; o[1] = a1; o[2] = a2; o[3] = a3;
@@ -821,6 +847,7 @@ __device__ __forceinline__ void kt_epilogue(v4f (&acc)[KT_TA][KT_TB], unsigned c
         }
       }
     }
+    if (stage && !OUT_F32) __syncthreads();                     // the output tiles below reuse this LDS
   }
   if (OUT_F32) {
 #pragma unroll
