@@ -35,7 +35,9 @@ namespace {
 // elements, E8M0 scale per 32) or none, which leaves only the down
 // projection (the unfused reference path, which reads X a second time).
 //
-// Block: 16 token rows, 16 waves (8 for ranks above 64); wave w handles
+// Block: 16 token rows, 16 waves (8 for ranks above 64, and when the grid
+// has more blocks than the device has CUs: two 8-wave blocks then share a CU
+// instead of leaving a second round of blocks); wave w handles
 // groups w, w+W, ... of K in batches of up to 2 groups whose loads are all
 // issued before any is used, so a CU keeps enough bytes in flight to stream HBM.  smooth_inv is
 // staged once per block in LDS.  Lane l works on row (l % 16) and the 16
@@ -62,7 +64,7 @@ __global__ __launch_bounds__(k1_waves<NT>() * 64) void k_quant_act_lora_down(
   float* s_si = reinterpret_cast<float*>(k1_smem_raw);                  // [K]
   float(*red)[2][16][16] = reinterpret_cast<float(*)[2][16][16]>(s_si + K);  // [waves][2][16][16]
 
-  constexpr int K1_WAVES = k1_waves<NT>();
+  const int nwaves = blockDim.x >> 6;                   // k1_waves<NT>() or 8 (uniform)
   const int lane = threadIdx.x & 63;
   const int wave = threadIdx.x >> 6;
   const int m0 = blockIdx.x * K1_ROWS;
@@ -72,7 +74,7 @@ __global__ __launch_bounds__(k1_waves<NT>() * 64) void k_quant_act_lora_down(
   const int G = K / GROUP;
   const int ntiles = rank >> 4;
 
-  for (int k = threadIdx.x * 4; k < K; k += K1_WAVES * 64 * 4)
+  for (int k = threadIdx.x * 4; k < K; k += blockDim.x * 4)
     *reinterpret_cast<float4*>(s_si + k) = *reinterpret_cast<const float4*>(smooth_inv + k);
   __syncthreads();
 
@@ -83,11 +85,11 @@ __global__ __launch_bounds__(k1_waves<NT>() * 64) void k_quant_act_lora_down(
   const uint16_t* xrow = x + static_cast<size_t>(row_ok ? row : 0) * K;
   constexpr int K1_BATCH = NT <= 2 ? 2 : 1;
 
-  for (int g0 = wave; g0 < G; g0 += K1_WAVES * K1_BATCH) {
+  for (int g0 = wave; g0 < G; g0 += nwaves * K1_BATCH) {
     uint4 raw[K1_BATCH][2];
 #pragma unroll
     for (int b = 0; b < K1_BATCH; ++b) {
-      const int g = g0 + b * K1_WAVES;
+      const int g = g0 + b * nwaves;
       raw[b][0] = raw[b][1] = make_uint4(0, 0, 0, 0);
       if (row_ok && g < G) {
         raw[b][0] = *reinterpret_cast<const uint4*>(xrow + g * GROUP + kq);
@@ -96,7 +98,7 @@ __global__ __launch_bounds__(k1_waves<NT>() * 64) void k_quant_act_lora_down(
     }
 #pragma unroll
     for (int b = 0; b < K1_BATCH; ++b) {
-      const int g = g0 + b * K1_WAVES;
+      const int g = g0 + b * nwaves;
       if (g >= G) break;
       const int k0 = g * GROUP + kq;
       const float4* sp = reinterpret_cast<const float4*>(s_si + k0);
@@ -202,8 +204,7 @@ __global__ __launch_bounds__(k1_waves<NT>() * 64) void k_quant_act_lora_down(
         const int c = threadIdx.x & 15;          // col in tile
         if (t0 + tt < ntiles && m0 + r < M) {
           float s = 0.f;
-#pragma unroll
-          for (int wv = 0; wv < K1_WAVES; ++wv) s += red[wv][tt][r][c];
+          for (int wv = 0; wv < nwaves; ++wv) s += red[wv][tt][r][c];
           lora_act[static_cast<size_t>(m0 + r) * rank + (t0 + tt) * 16 + c] = s;
         }
       }
@@ -1128,6 +1129,19 @@ __global__ __launch_bounds__(KT_THREADS, 1) void k_gemm_w4a4_lora_up(
   kt_epilogue<OUT_F32, EPI>(acc, &ring[0][0], m0, n0, M, N, y, qa);
 }
 
+// Compute units of the current device (cached per device).
+int device_cu_count() {
+  static int cached[64] = {};
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
+  if (cached[dev] == 0) {
+    int n = 0;
+    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0) n = 256;
+    cached[dev] = n;
+  }
+  return cached[dev];
+}
+
 template <int ACT, int NT, int QM>
 void launch_k1_kernel(const void* x, const float* smooth_inv, const void* lora_down, int M, int K, int rank,
                       void* x_codes, void* x_scales, float* lora_act, size_t smem, hipStream_t st) {
@@ -1135,7 +1149,11 @@ void launch_k1_kernel(const void* x, const float* smooth_inv, const void* lora_d
   if (smem > 64 * 1024)
     (void)hipFuncSetAttribute(reinterpret_cast<const void*>(kern), hipFuncAttributeMaxDynamicSharedMemorySize,
                               static_cast<int>(smem));
-  hipLaunchKernelGGL(kern, dim3((M + K1_ROWS - 1) / K1_ROWS), dim3(k1_waves<NT>() * 64), smem, st,
+  // Grids larger than the CU count run 8-wave blocks, two per CU, instead of
+  // a second round of 16-wave blocks.
+  const int blocks = (M + K1_ROWS - 1) / K1_ROWS;
+  const int waves = (k1_waves<NT>() == 16 && blocks > device_cu_count()) ? 8 : k1_waves<NT>();
+  hipLaunchKernelGGL(kern, dim3(blocks), dim3(waves * 64), smem, st,
                      static_cast<const uint16_t*>(x), smooth_inv, static_cast<const uint16_t*>(lora_down), M, K,
                      rank, static_cast<uint8_t*>(x_codes), x_scales, lora_act);
 }
