@@ -226,6 +226,42 @@ def bench_awq(S, workloads, steps, warmup, M=1):
                          "avg_launch_us": round(gemv_ms * 1e3, 2), "algorithmic_bytes_per_launch": nbytes}}
 
 
+SWEEP_RANKS = (0, 16, 32, 64, 128)
+SWEEP_ROWS = 64
+
+
+def rank_sweep(wl, Lr, desc, build_layer, run, x, M, K, N, args):
+    """Step time per rank and the relative Frobenius error of the layer's
+    bf16 output against fp64 X W^T on SWEEP_ROWS seeded rows (rank 0 is
+    plain smoothed W4A4)."""
+    import torch
+    import workloads
+    rows = np.sort(np.random.default_rng(2024).choice(M, SWEEP_ROWS, replace=False))
+    ref = workloads.bf16_bits_to_f64(wl.x_bits[rows]) @ Lr.weight.T
+    if Lr.bias is not None:
+        ref = ref + Lr.bias
+    out = []
+    for rr in SWEEP_RANKS:
+        lin = build_layer(rr)
+        res = run(lin, args.steps, args.warmup)
+        ms = res["wall_s"] * 1e3 / args.steps
+        y = lin(x)
+        torch.cuda.synchronize()
+        yr = y[torch.from_numpy(rows).cuda()].float().cpu().numpy().astype(np.float64)
+        err = float(np.linalg.norm(yr - ref) / np.linalg.norm(ref))
+        out.append({"rank": rr, "ms_per_step": round(ms, 5),
+                    "effective_tops": round(2.0 * M * N * K / (ms * 1e-3) / 1e12, 2),
+                    "rel_fro_err_vs_fp64": round(err, 6)})
+        del lin, y
+    ms0 = out[0]["ms_per_step"]
+    for o in out:
+        o["overhead_vs_rank0"] = round(o["ms_per_step"] / ms0 - 1.0, 4)
+    return {"rank_sweep": {"workload": desc + f" ({args.precision})", "M": M, "K": K, "N": N,
+                           "steps": args.steps, "warmup": args.warmup, "settle_s": SETTLE_S,
+                           "sampled_rows": SWEEP_ROWS, "ranks": out,
+                           "context": "pages: an unfused rank-32 branch costs +57% latency (NVIDIA, model card)"}}
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__)
     ap.add_argument("--gpus", type=int, default=1)
@@ -240,6 +276,10 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-variants", action="store_true", help="skip the MXFP4 variant run")
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
+    ap.add_argument("--rank-sweep", action="store_true",
+                    help="instead of the bench line: the batched rank sweep (16384x3072x12288, ranks "
+                         "0/16/32/64/128) with step time, overhead against rank 0 and error against "
+                         "fp64 X W on sampled rows, as one JSON line")
     ap.add_argument("--copy-probe", type=int, default=0, metavar="MIB",
                     help="only run a plain device copy of MIB MiB (HBM counter calibration)")
     args = ap.parse_args()
@@ -272,6 +312,8 @@ def main():
         return
     L.check(S.device_check(0), "device check")
 
+    if args.rank_sweep:
+        args.workload = "rank_sweep"
     gen_name, layer, act, desc = BENCH_WORKLOADS[args.workload]
     wl = workloads.make_workload(gen_name)
     Lr = wl.layers[layer]
@@ -393,6 +435,10 @@ def main():
                             "avg_launch_us": round(res["k1_ms"] * 1e3, 2),
                             "algorithmic_bytes_per_launch": k1_bytes(M, K, r, precision)},
         }
+
+    if args.rank_sweep:
+        print(json.dumps(rank_sweep(wl, Lr, desc, build_layer, run, x, M, K, N, args)))
+        return
 
     lin, ms_per_step, main_m = measure(args.precision)
     value = main_m["value"]
