@@ -696,12 +696,59 @@ static_assert(KT_WAVES * KT_WM * KT_WN * 2 <= KT_NS * KT_STAGE, "the output tile
 static_assert(2 * (KT_BM + KT_BN) == 2 * KT_THREADS, "two scale conversions per thread per stage");
 
 // Start values of the large form's accumulators: bias, then the up
-// projection (X_hat L1) L2 on bf16 MFMA.  Computed before the K loop, while
-// the first stages load, so that the latency of these reads is not exposed
-// at the end of the tile.  acc[a][b][e] is output row m0 + 64 wm + 16b +
-// (lane & 15), column n0 + 128 wn + 16a + 4(lane >> 4) + e.
+// projection (X_hat L1) L2 on bf16 MFMA.  acc[a][b][e] is output row m0 +
+// 64 wm + 16b + (lane & 15), column n0 + 128 wn + 16a + 4(lane >> 4) + e.
+// The loads of the first 32 ranks and of the bias are issued before the
+// first stages' DMA (kt_init_load) and consumed after it (kt_init_acc), so
+// that their latency overlaps those loads.  Every load is unconditional at
+// a clamped in-bounds address and masked afterwards: loads under per-lane
+// branches would each be waited for before the next is issued.
+struct KtInit {
+  uint2 bv[KT_TA];           // bias, columns 16a + 4lq .. + 3
+  float4 la[KT_TB][2];       // lora_act, row 16b + lr, ranks 8lq .. + 7 of the slice
+  uint4 lu[KT_TA];           // lora_up, row (output column) 16a + lr, same ranks
+};
+
 template <int NT>
-__device__ __forceinline__ void kt_init_acc(v4f (&acc)[KT_TA][KT_TB], int m0, int n0,
+__device__ __forceinline__ void kt_init_rank_loads(KtInit& R, int kk, int mw, int nw, const float* __restrict__ lora_act,
+                                                   const uint16_t* __restrict__ lora_up, int M, int N, int rank) {
+  const int lane = threadIdx.x & 63;
+  const int lr = lane & 15, lq = lane >> 4;
+  const int kl = kk + lq * 8;
+  const int klc = kl < rank ? kl : 0;
+#pragma unroll
+  for (int b = 0; b < KT_TB; ++b) {
+    const int r = min(mw + b * 16 + lr, M - 1);
+    const float4* p = reinterpret_cast<const float4*>(lora_act + static_cast<size_t>(r) * rank + klc);
+    R.la[b][0] = p[0];
+    R.la[b][1] = p[1];
+  }
+#pragma unroll
+  for (int a = 0; a < KT_TA; ++a) {
+    const int c = min(nw + a * 16 + lr, N - 1);
+    R.lu[a] = *reinterpret_cast<const uint4*>(lora_up + static_cast<size_t>(c) * rank + klc);
+  }
+}
+
+template <int NT>
+__device__ __forceinline__ void kt_init_load(KtInit& R, int m0, int n0, const float* __restrict__ lora_act,
+                                             const uint16_t* __restrict__ lora_up,
+                                             const uint16_t* __restrict__ bias, int M, int N, int rank) {
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(static_cast<int>(threadIdx.x) >> 6);
+  const int wm = wave >> 1, wn = wave & 1;
+  const int lq = lane >> 4;
+  const int mw = m0 + wm * KT_WM, nw = n0 + wn * KT_WN;
+  if (bias) {                                   // uniform
+#pragma unroll
+    for (int a = 0; a < KT_TA; ++a)             // N % 8 == 0: four columns all in or all out
+      R.bv[a] = *reinterpret_cast<const uint2*>(bias + min(nw + a * 16 + 4 * lq, N - 4));
+  }
+  if constexpr (NT > 0) kt_init_rank_loads<NT>(R, 0, mw, nw, lora_act, lora_up, M, N, rank);
+}
+
+template <int NT>
+__device__ __forceinline__ void kt_init_acc(v4f (&acc)[KT_TA][KT_TB], KtInit& R, int m0, int n0,
                                             const float* __restrict__ lora_act,
                                             const uint16_t* __restrict__ lora_up,
                                             const uint16_t* __restrict__ bias, int M, int N, int rank) {
@@ -711,48 +758,37 @@ __device__ __forceinline__ void kt_init_acc(v4f (&acc)[KT_TA][KT_TB], int m0, in
   const int lr = lane & 15, lq = lane >> 4;
   const int mw = m0 + wm * KT_WM, nw = n0 + wn * KT_WN;
 #pragma unroll
-  for (int a = 0; a < KT_TA; ++a)
-#pragma unroll
-    for (int b = 0; b < KT_TB; ++b) acc[a][b] = v4f{0.f, 0.f, 0.f, 0.f};
-  if (bias) {
-#pragma unroll
-    for (int a = 0; a < KT_TA; ++a) {
-      const int c = nw + a * 16 + 4 * lq;      // N % 8 == 0: all four in or out
-      if (c >= N) continue;
-      const uint2 bv = *reinterpret_cast<const uint2*>(bias + c);
-      const float b4[4] = {bf16_bits_to_f32(bv.x & 0xFFFFu), bf16_bits_to_f32(bv.x >> 16),
-                           bf16_bits_to_f32(bv.y & 0xFFFFu), bf16_bits_to_f32(bv.y >> 16)};
-#pragma unroll
-      for (int b = 0; b < KT_TB; ++b)
-#pragma unroll
-        for (int e = 0; e < 4; ++e) acc[a][b][e] = b4[e];
+  for (int a = 0; a < KT_TA; ++a) {
+    float b4[4] = {0.f, 0.f, 0.f, 0.f};
+    if (bias && nw + a * 16 + 4 * lq < N) {
+      b4[0] = bf16_bits_to_f32(R.bv[a].x & 0xFFFFu);
+      b4[1] = bf16_bits_to_f32(R.bv[a].x >> 16);
+      b4[2] = bf16_bits_to_f32(R.bv[a].y & 0xFFFFu);
+      b4[3] = bf16_bits_to_f32(R.bv[a].y >> 16);
     }
+#pragma unroll
+    for (int b = 0; b < KT_TB; ++b) acc[a][b] = v4f{b4[0], b4[1], b4[2], b4[3]};
   }
   // up projection: bf16 MFMA 16x16x32 over the rank in slices of 32 (ranks
-  // are multiples of 16, so the lanes of a slice past the rank load zeros);
-  // lora_up rows are the A operand, lora_act rows the B operand
+  // are multiples of 16, so the lanes of a slice past the rank contribute
+  // zeros); lora_up rows are the A operand, lora_act rows the B operand
   if constexpr (NT > 0) {
     for (int kk = 0; kk < rank; kk += 32) {
-      const int kl = kk + lq * 8;
-      const bool kin = kl < rank;
+      if (kk > 0) kt_init_rank_loads<NT>(R, kk, mw, nw, lora_act, lora_up, M, N, rank);
+      const bool kin = kk + lq * 8 < rank;
       v8bf la[KT_TB];
 #pragma unroll
       for (int b = 0; b < KT_TB; ++b) {
-        const int r = mw + b * 16 + lr;
-        float v[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
-        if (kin && r < M) {
-          const float4* p = reinterpret_cast<const float4*>(lora_act + static_cast<size_t>(r) * rank + kl);
-          const float4 v0 = p[0], v1 = p[1];
-          v[0] = v0.x; v[1] = v0.y; v[2] = v0.z; v[3] = v0.w;
-          v[4] = v1.x; v[5] = v1.y; v[6] = v1.z; v[7] = v1.w;
-        }
+        const bool ok = kin && mw + b * 16 + lr < M;
+        const float4 v0 = R.la[b][0], v1 = R.la[b][1];
+        const float v[8] = {ok ? v0.x : 0.f, ok ? v0.y : 0.f, ok ? v0.z : 0.f, ok ? v0.w : 0.f,
+                            ok ? v1.x : 0.f, ok ? v1.y : 0.f, ok ? v1.z : 0.f, ok ? v1.w : 0.f};
         la[b] = pack_bf16x8(v);
       }
 #pragma unroll
       for (int a = 0; a < KT_TA; ++a) {
-        const int c = nw + a * 16 + lr;
-        uint4 u = make_uint4(0, 0, 0, 0);
-        if (kin && c < N) u = *reinterpret_cast<const uint4*>(lora_up + static_cast<size_t>(c) * rank + kl);
+        const bool ok = kin && nw + a * 16 + lr < N;
+        const uint4 u = ok ? R.lu[a] : make_uint4(0, 0, 0, 0);
         const v8bf ub = __builtin_bit_cast(v8bf, u);
 #pragma unroll
         for (int b = 0; b < KT_TB; ++b)
@@ -780,30 +816,32 @@ __device__ __forceinline__ void kt_epilogue(v4f (&acc)[KT_TA][KT_TB], unsigned c
     // then K heads, then V heads, which are left as projected.
     const int HD = N / 3;
     const bool rot = qa.cos != nullptr;                        // uniform
-    // The rotary factors of the block's 256 rows go to LDS with coalesced
-    // 16-byte loads, all issued before any is stored: 16-byte chunk c of row
+    // The rotary factors of the block's 256 rows go to LDS by LDS-DMA (no
+    // registers; the accumulators hold most of them): 16-byte chunk c of row
     // r sits at chunk c ^ (r & 15) of its 256-byte row, which keeps the
-    // per-lane reads below free of bank conflicts.  Rows past M read row
-    // M - 1 (never stored).  Blocks whose columns are all V skip it.
+    // per-lane reads below free of bank conflicts.  A DMA load of a wave
+    // fills four rows: lane l lands at row l / 16, position l % 16, and so
+    // fetches chunk (l % 16) ^ (row & 15).  Rows past M read zeros (never
+    // stored).  Blocks whose columns are all V skip it.
     float4* lcs = reinterpret_cast<float4*>(smem);              // [256][16] cos
     float4* lsn = lcs + KT_BM * 16;                             // [256][16] sin
     const bool stage = rot && n0 < 2 * HD;                      // uniform per block
     if (stage) {
-      constexpr int IT = KT_BM * 16 / KT_THREADS;
-      float4 cv[IT], sv[IT];
+      constexpr int Q = KT_BM / 4 / KT_WAVES;                   // DMA loads per wave per table
+      const uint32_t tbytes = static_cast<uint32_t>(M) * 256u;
+      const DmaRsrc crs = dma_rsrc(qa.cos, tbytes), srs = dma_rsrc(qa.sin, tbytes);
+      const uint32_t l0 = static_cast<uint32_t>(reinterpret_cast<uintptr_t>(smem));
 #pragma unroll
-      for (int j = 0; j < IT; ++j) {
-        const int i = tid + j * KT_THREADS, r = i >> 4, c = i & 15;
-        const size_t row = static_cast<size_t>(min(m0 + r, M - 1));
-        cv[j] = reinterpret_cast<const float4*>(qa.cos + row * 64)[c];
-        sv[j] = reinterpret_cast<const float4*>(qa.sin + row * 64)[c];
+      for (int j = 0; j < Q; ++j) {
+        const int q = wave * Q + j;
+        const int r = 4 * q + (lane >> 4);
+        const uint32_t voff = m0 + r < M ? static_cast<uint32_t>(m0 + r) * 256u + 16u * ((lane & 15) ^ (r & 15))
+                                         : 0x80000000u;
+        const uint32_t la = __builtin_amdgcn_readfirstlane(l0 + 1024u * q);
+        dma16(crs, la, voff);
+        dma16(srs, la + KT_BM * 256u, voff);
       }
-#pragma unroll
-      for (int j = 0; j < IT; ++j) {
-        const int i = tid + j * KT_THREADS, r = i >> 4, c = i & 15;
-        lcs[r * 16 + (c ^ (r & 15))] = cv[j];
-        lsn[r * 16 + (c ^ (r & 15))] = sv[j];
-      }
+      __builtin_amdgcn_s_waitcnt(waitcnt_vm_lgkm0(0));
       __syncthreads();
     }
     if (nw < 2 * HD) {
@@ -1066,11 +1104,14 @@ __global__ __launch_bounds__(KT_THREADS, 1) void k_gemm_w4a4_lora_up(
     deq(xc[gi][b], swr[a & 3], dr[q & 3], acc[a][b]);
   };
 
-  // stages 0 .. 2 in flight; bias and up projection into the accumulators
-  // meanwhile; stage 0 landed and its scales converted
+  // bias and up-projection operands requested, then stages 0 .. 2; the
+  // accumulators start while the stages load; stage 0 landed and its
+  // scales converted
+  KtInit init;
+  kt_init_load<NT>(init, m0, n0, lora_act, lora_up, bias, M, N, rank);
 #pragma unroll
   for (int st = 0; st < KT_NS - 1; ++st) issue_stage(st, st);
-  kt_init_acc<NT>(acc, m0, n0, lora_act, lora_up, bias, M, N, rank);
+  kt_init_acc<NT>(acc, init, m0, n0, lora_act, lora_up, bias, M, N, rank);
   __builtin_amdgcn_s_waitcnt(waitcnt_vm_lgkm0(KT_P * (KT_NS - 2)));
   __builtin_amdgcn_s_barrier();
   asm volatile("" ::: "memory");

@@ -180,53 +180,74 @@ __global__ __launch_bounds__(MxCfg<BM>::THREADS, BM == 256 ? 1 : 2) void k_gemm_
   const int fr = lane & 31;      // fragment row within a 32-row tile
   const int fk = lane >> 5;      // which 32-k block of the k-step
 
-#pragma unroll
-  for (int st = 0; st < C::NS - 1; ++st) issue_stage(st, st);
-
   // The accumulators start as bias + bf16(lora_act) L2, computed while the
   // first stages load: a lane holds output row m0 + 64 wm + 32 i + fr and
   // columns 32 j + 8 bb + 4 fk + (0..3) of each 32-column tile.  The up
   // projection runs on bf16 MFMA 32x32x16 (K = rank in slices of 16),
-  // transposed like the main product.
+  // transposed like the main product.  The bias and the first slice's
+  // operands are requested before the stages' DMA, unconditionally at
+  // clamped in-bounds addresses and masked afterwards (loads under per-lane
+  // branches would each be waited for before the next is issued).
+  const int mw = m0 + wm * MX_WM, nw = n0 + wn * MX_WN;
+  uint2 bvr[MX_TJ][4];
+  float4 lar[MX_TI][2];
+  uint4 lur[MX_TJ];
+  if (bias) {                                            // uniform; N % 8 == 0
+#pragma unroll
+    for (int j = 0; j < MX_TJ; ++j)
+#pragma unroll
+      for (int bb = 0; bb < 4; ++bb)
+        bvr[j][bb] = *reinterpret_cast<const uint2*>(bias + min(nw + j * 32 + 8 * bb + 4 * fk, N - 4));
+  }
+  auto rank_loads = [&](int kk) {                        // kk + 16 <= rank
+    const int kl = kk + fk * 8;
+#pragma unroll
+    for (int i = 0; i < MX_TI; ++i) {
+      const float4* p =
+          reinterpret_cast<const float4*>(lora_act + static_cast<size_t>(min(mw + i * 32 + fr, M - 1)) * rank + kl);
+      lar[i][0] = p[0];
+      lar[i][1] = p[1];
+    }
+#pragma unroll
+    for (int j = 0; j < MX_TJ; ++j)
+      lur[j] = *reinterpret_cast<const uint4*>(lora_up + static_cast<size_t>(min(nw + j * 32 + fr, N - 1)) * rank + kl);
+  };
+  if constexpr (HAS_RANK) rank_loads(0);
+
+#pragma unroll
+  for (int st = 0; st < C::NS - 1; ++st) issue_stage(st, st);
+
 #pragma unroll
   for (int i = 0; i < MX_TI; ++i)
 #pragma unroll
     for (int j = 0; j < MX_TJ; ++j)
 #pragma unroll
       for (int bb = 0; bb < 4; ++bb) {
-        const int c = n0 + wn * MX_WN + j * 32 + 8 * bb + 4 * fk;
         float b4[4] = {0.f, 0.f, 0.f, 0.f};
-        if (bias && c < N) {
-          const uint2 bv = *reinterpret_cast<const uint2*>(bias + c);
-          b4[0] = bf16_bits_to_f32(bv.x & 0xFFFFu);
-          b4[1] = bf16_bits_to_f32(bv.x >> 16);
-          b4[2] = bf16_bits_to_f32(bv.y & 0xFFFFu);
-          b4[3] = bf16_bits_to_f32(bv.y >> 16);
+        if (bias && nw + j * 32 + 8 * bb + 4 * fk < N) {
+          b4[0] = bf16_bits_to_f32(bvr[j][bb].x & 0xFFFFu);
+          b4[1] = bf16_bits_to_f32(bvr[j][bb].x >> 16);
+          b4[2] = bf16_bits_to_f32(bvr[j][bb].y & 0xFFFFu);
+          b4[3] = bf16_bits_to_f32(bvr[j][bb].y >> 16);
         }
 #pragma unroll
         for (int e = 0; e < 4; ++e) acc[i][j][4 * bb + e] = b4[e];
       }
   if constexpr (HAS_RANK) {
     for (int kk = 0; kk < rank; kk += 16) {
-      const int kl = kk + fk * 8;
+      if (kk > 0) rank_loads(kk);
       v8bf la[MX_TI];
 #pragma unroll
       for (int i = 0; i < MX_TI; ++i) {
-        const int r = m0 + wm * MX_WM + i * 32 + fr;
-        float v[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
-        if (r < M) {
-          const float4* p = reinterpret_cast<const float4*>(lora_act + static_cast<size_t>(r) * rank + kl);
-          const float4 v0 = p[0], v1 = p[1];
-          v[0] = v0.x; v[1] = v0.y; v[2] = v0.z; v[3] = v0.w;
-          v[4] = v1.x; v[5] = v1.y; v[6] = v1.z; v[7] = v1.w;
-        }
+        const bool ok = mw + i * 32 + fr < M;
+        const float4 v0 = lar[i][0], v1 = lar[i][1];
+        const float v[8] = {ok ? v0.x : 0.f, ok ? v0.y : 0.f, ok ? v0.z : 0.f, ok ? v0.w : 0.f,
+                            ok ? v1.x : 0.f, ok ? v1.y : 0.f, ok ? v1.z : 0.f, ok ? v1.w : 0.f};
         la[i] = pack_bf16x8(v);
       }
 #pragma unroll
       for (int j = 0; j < MX_TJ; ++j) {
-        const int c = n0 + wn * MX_WN + j * 32 + fr;
-        uint4 u = make_uint4(0, 0, 0, 0);
-        if (c < N) u = *reinterpret_cast<const uint4*>(lora_up + static_cast<size_t>(c) * rank + kl);
+        const uint4 u = nw + j * 32 + fr < N ? lur[j] : make_uint4(0, 0, 0, 0);
         const v8bf ub = __builtin_bit_cast(v8bf, u);
 #pragma unroll
         for (int i = 0; i < MX_TI; ++i)
