@@ -328,31 +328,48 @@ __device__ __forceinline__ void k2_epilogue(v4f (&acc)[K2_TA][K2_TB], unsigned c
   const int lr = lane & 15, lq = lane >> 4;
   // ---- epilogue: up projection (bf16 MFMA 16x16x32, K = rank in slices of
   // 32; ranks are multiples of 16, so the lanes of a slice past the rank
-  // load zeros), transposed like the main product: lora_up rows are the A
-  // operand, lora_act rows the B operand.
+  // contribute zeros), transposed like the main product: lora_up rows are
+  // the A operand, lora_act rows the B operand; then the bias.  All loads
+  // are unconditional at clamped in-bounds addresses and masked afterwards
+  // (loads under per-lane branches would each be waited for in turn).
+  uint2 bv[K2_TA];
+  if (bias) {                                    // uniform; N % 8 == 0
+#pragma unroll
+    for (int a = 0; a < K2_TA; ++a)
+      bv[a] = *reinterpret_cast<const uint2*>(bias + min(n0 + wn * K2_WN + a * 16 + 4 * lq, N - 4));
+  }
   if constexpr (NT > 0) {
     for (int kk = 0; kk < rank; kk += 32) {
       const int kl = kk + lq * 8;          // this lane's 8 k values
       const bool kin = kl < rank;
+      const int klc = kin ? kl : 0;
+      float4 lv[K2_TB][2];
+      uint4 uv[K2_TA];
+#pragma unroll
+      for (int b = 0; b < K2_TB; ++b) {
+        const int r = min(m0 + wm * K2_WM + b * 16 + lr, M - 1);
+        const float4* p = reinterpret_cast<const float4*>(lora_act + static_cast<size_t>(r) * rank + klc);
+        lv[b][0] = p[0];
+        lv[b][1] = p[1];
+      }
+#pragma unroll
+      for (int a = 0; a < K2_TA; ++a) {
+        const int c = min(n0 + wn * K2_WN + a * 16 + lr, N - 1);
+        uv[a] = *reinterpret_cast<const uint4*>(lora_up + static_cast<size_t>(c) * rank + klc);
+      }
       v8bf la[K2_TB];
 #pragma unroll
       for (int b = 0; b < K2_TB; ++b) {
-        const int r = m0 + wm * K2_WM + b * 16 + lr;
-        float v[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
-        if (kin && r < M) {
-          const float4* p = reinterpret_cast<const float4*>(lora_act + static_cast<size_t>(r) * rank + kl);
-          const float4 v0 = p[0], v1 = p[1];
-          v[0] = v0.x; v[1] = v0.y; v[2] = v0.z; v[3] = v0.w;
-          v[4] = v1.x; v[5] = v1.y; v[6] = v1.z; v[7] = v1.w;
-        }
+        const bool ok = kin && m0 + wm * K2_WM + b * 16 + lr < M;
+        const float4 v0 = lv[b][0], v1 = lv[b][1];
+        const float v[8] = {ok ? v0.x : 0.f, ok ? v0.y : 0.f, ok ? v0.z : 0.f, ok ? v0.w : 0.f,
+                            ok ? v1.x : 0.f, ok ? v1.y : 0.f, ok ? v1.z : 0.f, ok ? v1.w : 0.f};
         la[b] = pack_bf16x8(v);
       }
 #pragma unroll
       for (int a = 0; a < K2_TA; ++a) {
-        const int c = n0 + wn * K2_WN + a * 16 + lr;
-        uint4 u = make_uint4(0, 0, 0, 0);
-        if (kin && c < N) u = *reinterpret_cast<const uint4*>(lora_up + static_cast<size_t>(c) * rank + kl);
-        const v8bf ub = __builtin_bit_cast(v8bf, u);
+        const bool ok = kin && n0 + wn * K2_WN + a * 16 + lr < N;
+        const v8bf ub = __builtin_bit_cast(v8bf, ok ? uv[a] : make_uint4(0, 0, 0, 0));
 #pragma unroll
         for (int b = 0; b < K2_TB; ++b)
           acc[a][b] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ub, la[b], acc[a][b], 0, 0, 0);
@@ -366,11 +383,9 @@ __device__ __forceinline__ void k2_epilogue(v4f (&acc)[K2_TA][K2_TB], unsigned c
   if (bias) {
 #pragma unroll
     for (int a = 0; a < K2_TA; ++a) {
-      const int c = n0 + wn * K2_WN + a * 16 + 4 * lq;   // N % 8 == 0: all four in or out
-      if (c >= N) continue;
-      const uint2 bv = *reinterpret_cast<const uint2*>(bias + c);
-      const float b4[4] = {bf16_bits_to_f32(bv.x & 0xFFFFu), bf16_bits_to_f32(bv.x >> 16),
-                           bf16_bits_to_f32(bv.y & 0xFFFFu), bf16_bits_to_f32(bv.y >> 16)};
+      if (n0 + wn * K2_WN + a * 16 + 4 * lq >= N) continue;
+      const float b4[4] = {bf16_bits_to_f32(bv[a].x & 0xFFFFu), bf16_bits_to_f32(bv[a].x >> 16),
+                           bf16_bits_to_f32(bv[a].y & 0xFFFFu), bf16_bits_to_f32(bv[a].y >> 16)};
 #pragma unroll
       for (int b = 0; b < K2_TB; ++b)
 #pragma unroll
@@ -399,19 +414,24 @@ __device__ __forceinline__ void k2_epilogue(v4f (&acc)[K2_TA][K2_TB], unsigned c
         t += __shfl_xor(t, 32);
         if (lq == 0) red[((wm * K2_TB + b) * 2 + wn) * 16 + lr] = t;
       }
+      // the lane's norm weights (the same for every row), loaded once
+      uint2 gv[K2_TA];
+#pragma unroll
+      for (int a = 0; a < K2_TA; ++a) gv[a] = *reinterpret_cast<const uint2*>(g + wn * K2_WN + a * 16 + 4 * lq);
+      const bool rot = qa.cos != nullptr;                 // uniform
       __syncthreads();
 #pragma unroll
       for (int b = 0; b < K2_TB; ++b) {
         const float tot = red[((wm * K2_TB + b) * 2 + 0) * 16 + lr] + red[((wm * K2_TB + b) * 2 + 1) * 16 + lr];
         const float scale = 1.0f / sqrtf(tot * (1.0f / QKV_HEAD) + qa.eps);
-        const int row = m0 + wm * K2_WM + b * 16 + lr;
-        const bool rot = qa.cos != nullptr && row < M;
+        // rows past M are never stored: they read row M - 1's factors, so
+        // the rotation's loads need no per-lane branch
+        const int row = min(m0 + wm * K2_WM + b * 16 + lr, M - 1);
 #pragma unroll
         for (int a = 0; a < K2_TA; ++a) {
           const int ch = wn * K2_WN + a * 16 + 4 * lq;        // column within the head
-          const uint2 gv = *reinterpret_cast<const uint2*>(g + ch);
-          const float g4[4] = {bf16_bits_to_f32(gv.x & 0xFFFFu), bf16_bits_to_f32(gv.x >> 16),
-                               bf16_bits_to_f32(gv.y & 0xFFFFu), bf16_bits_to_f32(gv.y >> 16)};
+          const float g4[4] = {bf16_bits_to_f32(gv[a].x & 0xFFFFu), bf16_bits_to_f32(gv[a].x >> 16),
+                               bf16_bits_to_f32(gv[a].y & 0xFFFFu), bf16_bits_to_f32(gv[a].y >> 16)};
           float o[4];
 #pragma unroll
           for (int e = 0; e < 4; ++e) o[e] = acc[a][b][e] * scale * g4[e];
