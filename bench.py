@@ -243,7 +243,7 @@ def rank_sweep(wl, Lr, desc, build_layer, run, x, M, K, N, args):
     out = []
     for rr in SWEEP_RANKS:
         lin = build_layer(rr)
-        res = run(lin, args.steps, args.warmup)
+        res = run(lin, args.steps, args.warmup, events=True)
         ms = res["wall_s"] * 1e3 / args.steps
         y = lin(x)
         torch.cuda.synchronize()
@@ -251,6 +251,7 @@ def rank_sweep(wl, Lr, desc, build_layer, run, x, M, K, N, args):
         err = float(np.linalg.norm(yr - ref) / np.linalg.norm(ref))
         out.append({"rank": rr, "ms_per_step": round(ms, 5),
                     "effective_tops": round(2.0 * M * N * K / (ms * 1e-3) / 1e12, 2),
+                    "k1_us": round(res["k1_ms"] * 1e3, 1), "k2_us": round(res["k2_ms"] * 1e3, 1),
                     "rel_fro_err_vs_fp64": round(err, 6)})
         del lin, y
     ms0 = out[0]["ms_per_step"]
