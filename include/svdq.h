@@ -181,7 +181,8 @@ int svdq_gemm_w4a4_lora_up(const void* x_codes, const void* x_scales,
  *   rope_cos, rope_sin [M][64] fp32 (both NULL: no rotation)
  *   eps >= 0 (finite)
  * Other arguments, layouts and errors as svdq_gemm_w4a4_lora_up; N not a
- * multiple of 384 returns SVDQ_ERR_UNSUPPORTED_SHAPE. */
+ * multiple of 384, or rotary tables of 2 GiB or more (M * 256 bytes), return
+ * SVDQ_ERR_UNSUPPORTED_SHAPE. */
 int svdq_gemm_w4a4_lora_up_qkv(const void* x_codes, const void* x_scales,
                                const void* w_codes, const void* w_scales,
                                const float* lora_act, const void* lora_up, const void* bias,

@@ -91,6 +91,9 @@ def test_device_entry_validation_precedes_device_use():
     assert qk(p[0], p[1], p[2], p[3], p[4], p[5], None, p[6], p[7], p[8], None, 1e-6, 16, 384, 128, 16, 64, 0, p[6], None) == L.SVDQ_ERR_INVALID_ARG
     assert qk(p[0], p[1], p[2], p[3], p[4], p[5], None, p[6], p[7], p[8], p[9], -1.0, 16, 384, 128, 16, 64, 0, p[6], None) == L.SVDQ_ERR_INVALID_ARG
     assert qk(p[0], p[1], p[2], p[3], p[4], p[5], None, p[6], p[7] + 2, None, None, 1e-6, 16, 384, 128, 16, 64, 0, p[6], None) == L.SVDQ_ERR_INVALID_ARG
+    # rotary tables of 2 GiB or more (M * 256 bytes) are refused before any device use
+    big = (1 << 23) + 16
+    assert qk(p[0], p[1], p[2], p[3], p[4], p[5], None, p[6], p[7], p[8], p[9], 1e-6, big, 384, 128, 16, 64, 0, p[6], None) == L.SVDQ_ERR_UNSUPPORTED_SHAPE
     d = L.lib().svdq_lora_down
     u = L.lib().svdq_lora_up_add
     assert d(p[0], p[1], p[2], 16, 128, 0, 64, 0, p[3], None) == L.SVDQ_ERR_INVALID_ARG       # rank 0

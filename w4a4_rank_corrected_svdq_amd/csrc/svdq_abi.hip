@@ -208,6 +208,7 @@ extern "C" int svdq_gemm_w4a4_lora_up_qkv(const void* x_codes, const void* x_sca
       (rank > 0 && (!aligned16(lora_act) || !aligned16(lora_up))))
     return SVDQ_ERR_INVALID_ARG;
   if (!fits_buffer(M, K / 2) || !fits_buffer(N, K / 2)) return SVDQ_ERR_UNSUPPORTED_SHAPE;
+  if (rope_cos && !fits_buffer(M, 64 * sizeof(float))) return SVDQ_ERR_UNSUPPORTED_SHAPE;
   st = current_device_check();
   if (st != SVDQ_OK) return st;
   if (M == 0) return SVDQ_OK;
