@@ -62,9 +62,15 @@ BENCH_WORKLOADS = {
 
 
 def kernel_source_hash() -> str:
+    """Hash of the kernel sources with comments and whitespace removed, so
+    that the stored counter figures stay valid across comment-only edits."""
+    import re
     h = hashlib.sha256()
     for f in ("svdq_kernels.hip", "svdq_mx_kernels.hip", "svdq_device.h"):
-        h.update(open(os.path.join(ROOT, "w4a4_rank_corrected_svdq_amd", "csrc", f), "rb").read())
+        src = open(os.path.join(ROOT, "w4a4_rank_corrected_svdq_amd", "csrc", f)).read()
+        src = re.sub(r"/\*.*?\*/", " ", src, flags=re.S)
+        src = re.sub(r"//[^\n]*", " ", src)
+        h.update(" ".join(src.split()).encode())
     return h.hexdigest()[:16]
 
 

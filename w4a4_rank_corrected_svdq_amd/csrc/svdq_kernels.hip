@@ -7,8 +7,9 @@
 //   quantizer and the down projection share their input).
 // Kernel 2 (k_gemm_w4a4_lora_up): INT4 x INT4 GEMM on int8 MFMA with exact
 //   int32 per-group products, per-group dequantization, and the up projection
-//   (X_hat L1) L2 plus bias in the epilogue (same section: the up projection
-//   and the 4-bit compute share their output).
+//   (X_hat L1) L2 plus bias in the same fp32 accumulators (same section: the
+//   up projection and the 4-bit compute share their output) -- before the K
+//   loop in the 256 x 256 form, in the epilogue of the 128 x 128 form.
 //
 // MFMA operand layouts used (16x16 tiles, wave64):
 //   A operand: lane l holds row (l % 16) and one K slice chosen by (l / 16);
