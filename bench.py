@@ -232,6 +232,46 @@ def bench_awq(S, workloads, steps, warmup, M=1):
                          "avg_launch_us": round(gemv_ms * 1e3, 2), "algorithmic_bytes_per_launch": nbytes}}
 
 
+def measure_peaks():
+    """Dense int8 and FP4 MFMA rates (the library's register-only probe
+    kernels, include/svdq_probe.h) and the device-to-device copy rate of
+    1 GiB (read + write bytes), each after the same settle phase, averaged
+    over 10 launches between HIP events."""
+    import torch
+    from w4a4_rank_corrected_svdq_amd import _lib as L
+    st = torch.cuda.current_stream()
+    res = {}
+
+    def timed(fn, n=10):
+        settle(fn)
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(n):
+            fn()
+        e1.record()
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / n
+
+    blocks, iters = 2048, 4096
+    sink = torch.empty(blocks * 256 * 64, dtype=torch.uint8, device="cuda")
+    for kind, key in ((L.SVDQ_PROBE_MFMA_I8, "int8_mfma_tops"), (L.SVDQ_PROBE_MFMA_FP4, "fp4_mfma_tflops")):
+        def probe(kind=kind):
+            L.check(L.lib().svdq_probe_mfma(kind, blocks, iters, sink.data_ptr(), st.cuda_stream), "peak probe")
+        ms = timed(probe)
+        res[key] = round(L.lib().svdq_probe_mfma_ops(kind, blocks, iters) / (ms * 1e-3) / 1e12, 1)
+    del sink
+    n = 1 << 30
+    src = torch.ones(n, dtype=torch.uint8, device="cuda")
+    dst = torch.empty_like(src)
+    ms = timed(lambda: dst.copy_(src))
+    res["hbm_copy_gbs"] = round(2.0 * n / (ms * 1e-3) / 1e9, 1)
+    del src, dst
+    res["how"] = ("register-only MFMA loops (v_mfma_i32_32x32x32_i8, one chain per wave; FP4 "
+                  "v_mfma_scale_f32_32x32x64_f8f6f4, four chains) over 2048 blocks of 4 waves, and a 1 GiB "
+                  "device copy counted as read + write, after the settle phase")
+    return res
+
+
 SWEEP_RANKS = (0, 16, 32, 64, 128)
 SWEEP_ROWS = 64
 
@@ -281,6 +321,7 @@ def main():
                          "mxfp4: E2M1 codes with E8M0 scales per 32 on the block-scaled FP4 MFMA")
     ap.add_argument("--no-overhead", action="store_true", help="skip the rank-0 comparison run")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-peaks", action="store_true", help="skip measuring the MFMA and copy peaks")
     ap.add_argument("--no-variants", action="store_true", help="skip the MXFP4 variant run")
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
     ap.add_argument("--rank-sweep", action="store_true",
@@ -492,6 +533,20 @@ def main():
     if args.precision == "int4" and not args.no_variants:
         out["qkv_fused_epilogue"] = bench_qkv(S, L, workloads, r, args.steps, args.warmup)
         out["awq_w4a16"] = bench_awq(S, workloads, max(args.steps, 20), args.warmup)
+    if not args.no_peaks:
+        # the same rooflines against the peaks measured on this device
+        pk = measure_peaks()
+        out["measured_peaks"] = pk
+        mfma_pk = pk["int8_mfma_tops"] if args.precision == "int4" else pk["fp4_mfma_tflops"]
+        out["roofline"]["frac_of_measured_peak"] = round(out["roofline"]["achieved"] / mfma_pk, 4)
+        out["roofline_k1"]["frac_of_measured_peak"] = round(out["roofline_k1"]["achieved"] / pk["hbm_copy_gbs"], 4)
+        if "mxfp4_variant" in out:
+            mv = out["mxfp4_variant"]
+            mv["roofline"]["frac_of_measured_peak"] = round(mv["roofline"]["achieved"] / pk["fp4_mfma_tflops"], 4)
+            mv["roofline_k1"]["frac_of_measured_peak"] = round(mv["roofline_k1"]["achieved"] / pk["hbm_copy_gbs"], 4)
+        if "awq_w4a16" in out:
+            aw = out["awq_w4a16"]["roofline"]
+            aw["frac_of_measured_peak"] = round(aw["achieved"] / pk["hbm_copy_gbs"], 4)
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(wl, layer, r, args.cpu_seconds, args.precision)
     print(json.dumps(out))

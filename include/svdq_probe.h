@@ -1,0 +1,34 @@
+/* Peak-rate probes for the benchmark harness.  They are not part of the
+ * layer: they measure, on the device at hand, the dense matrix-core rates
+ * that the layer's kernels are priced against, so that achieved rates can be
+ * stated against both the published peak and the measured one. */
+#ifndef SVDQ_PROBE_H
+#define SVDQ_PROBE_H
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define SVDQ_PROBE_MFMA_I8 0  /* v_mfma_i32_32x32x32_i8 (int8, the INT4 layer's product type) */
+#define SVDQ_PROBE_MFMA_FP4 1 /* v_mfma_scale_f32_32x32x64_f8f6f4, both operands FP4 E2M1 */
+
+/* Device, asynchronous.  Launches `blocks` blocks of 256 threads on `stream`
+ * (NULL: the default stream); each wave runs `iters` iterations of
+ * independent accumulation chains of the MFMA form `kind` on register
+ * operands (no memory traffic in the loop) and writes its accumulators to
+ * `sink`: a caller-owned device buffer, 16-byte aligned, of at least
+ * blocks * 256 * 64 bytes, whose contents are unspecified afterwards.  The
+ * dense operations performed are svdq_probe_mfma_ops(kind, blocks, iters).
+ * Errors: SVDQ_ERR_INVALID_ARG (unknown kind, blocks or iters below 1, null
+ * or misaligned sink), SVDQ_ERR_UNSUPPORTED_DEVICE, SVDQ_ERR_HIP. */
+int svdq_probe_mfma(int kind, int blocks, int iters, void* sink, void* stream);
+
+/* Host.  Dense operations (two per multiply-add) of one svdq_probe_mfma
+ * launch; 0 for an unknown kind or a count below 1. */
+double svdq_probe_mfma_ops(int kind, int blocks, int iters);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* SVDQ_PROBE_H */

@@ -1,6 +1,7 @@
 """CPU tests of the C ABI library: symbols, argument validation, the device
 refusal path, and host preparation against the oracle."""
 import ctypes
+import glob
 import os
 import re
 import subprocess
@@ -20,9 +21,11 @@ ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 
 
 def _declared_functions():
-    src = open(os.path.join(ROOT, "include", "svdq.h")).read()
-    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
-    return sorted(set(re.findall(r"\b(svdq_[a-z0-9_]+)\s*\(", src)))
+    names = set()
+    for h in sorted(glob.glob(os.path.join(ROOT, "include", "*.h"))):
+        src = re.sub(r"/\*.*?\*/", "", open(h).read(), flags=re.S)
+        names |= set(re.findall(r"\b(svdq_[a-z0-9_]+)\s*\(", src))
+    return sorted(names)
 
 
 def test_library_exports_every_declared_symbol():
@@ -94,6 +97,15 @@ def test_device_entry_validation_precedes_device_use():
     # rotary tables of 2 GiB or more (M * 256 bytes) are refused before any device use
     big = (1 << 23) + 16
     assert qk(p[0], p[1], p[2], p[3], p[4], p[5], None, p[6], p[7], p[8], p[9], 1e-6, big, 384, 128, 16, 64, 0, p[6], None) == L.SVDQ_ERR_UNSUPPORTED_SHAPE
+    pr = L.lib().svdq_probe_mfma
+    assert pr(2, 1, 1, p[0], None) == L.SVDQ_ERR_INVALID_ARG          # unknown kind
+    assert pr(0, 0, 1, p[0], None) == L.SVDQ_ERR_INVALID_ARG          # no blocks
+    assert pr(1, 1, 0, p[0], None) == L.SVDQ_ERR_INVALID_ARG          # no iterations
+    assert pr(0, 1, 1, p[0] + 4, None) == L.SVDQ_ERR_INVALID_ARG      # misaligned sink
+    ops = L.lib().svdq_probe_mfma_ops
+    assert ops(0, 3, 5) == 3 * 4 * 5 * 1 * 2 * 32 * 32 * 32
+    assert ops(1, 3, 5) == 3 * 4 * 5 * 4 * 2 * 32 * 32 * 64
+    assert ops(7, 3, 5) == 0.0
     d = L.lib().svdq_lora_down
     u = L.lib().svdq_lora_up_add
     assert d(p[0], p[1], p[2], 16, 128, 0, 64, 0, p[3], None) == L.SVDQ_ERR_INVALID_ARG       # rank 0

@@ -545,3 +545,22 @@ def test_qkv_full_size_sampled_rows():
     ref = O.forward_qkv(wl.x[rows], po, Lr.bias, qv, kv, cos[rows], sin[rows])
     assert O.rel_fro(to_np_bf16(y[torch.from_numpy(rows).cuda()]), ref) < Y_TOL
     assert torch.isfinite(y.float()).all()
+
+
+@pytest.mark.parametrize("kind", [L.SVDQ_PROBE_MFMA_I8, L.SVDQ_PROBE_MFMA_FP4])
+def test_peak_probe_runs_and_is_deterministic(kind):
+    """The benchmark's MFMA peak probe (include/svdq_probe.h): it launches,
+    writes its whole sink, and two launches write the same bytes (the
+    accumulations have a fixed order)."""
+    blocks, iters = 64, 16
+    per = 64
+    sinks = []
+    for _ in range(2):
+        sink = torch.full((blocks * 256 * per + 256,), 0xA5, dtype=torch.uint8, device="cuda")
+        L.check(L.lib().svdq_probe_mfma(kind, blocks, iters, sink.data_ptr(), torch.cuda.current_stream().cuda_stream),
+                "probe")
+        torch.cuda.synchronize()
+        sinks.append(sink.cpu())
+    assert torch.equal(sinks[0], sinks[1])
+    assert torch.all(sinks[0][blocks * 256 * per:] == 0xA5)      # nothing written past the sink
+    assert L.lib().svdq_probe_mfma_ops(kind, blocks, iters) > 0

@@ -28,7 +28,7 @@ _p = ctypes.c_void_p
 _i = ctypes.c_int
 _f = ctypes.c_float
 
-# name -> (restype, argtypes); every function declared in include/svdq.h
+# name -> (restype, argtypes); every function declared in include/*.h
 SIGNATURES = {
     "svdq_status_string": (ctypes.c_char_p, [_i]),
     "svdq_version": (_i, []),
@@ -51,7 +51,12 @@ SIGNATURES = {
                                         _p, _p, _p, _p, _p, _p]),
     "svdq_quant_act_lora_down_mxfp4": (_i, [_p, _p, _p, _i, _i, _i, _i, _p, _p, _p, _p]),
     "svdq_gemm_mxfp4_lora_up": (_i, [_p, _p, _p, _p, _p, _p, _p, _i, _i, _i, _i, _i, _p, _p]),
+    # include/svdq_probe.h (benchmark harness)
+    "svdq_probe_mfma": (_i, [_i, _i, _i, _p, _p]),
+    "svdq_probe_mfma_ops": (ctypes.c_double, [_i, _i, _i]),
 }
+SVDQ_PROBE_MFMA_I8 = 0
+SVDQ_PROBE_MFMA_FP4 = 1
 
 
 class SVDQError(RuntimeError):

@@ -11,6 +11,7 @@
 
 #include "svdq.h"
 #include "svdq_internal.h"
+#include "svdq_probe.h"
 
 namespace {
 
@@ -240,4 +241,17 @@ extern "C" int svdq_awq_gemv(const void* x_hat, const float* xsum, const void* w
   if (st != SVDQ_OK) return st;
   if (M == 0) return SVDQ_OK;
   return svdq::launch_awq_gemv(x_hat, xsum, w_codes, w_scales, w_zeros, bias, M, N, K, y, stream);
+}
+
+extern "C" int svdq_probe_mfma(int kind, int blocks, int iters, void* sink, void* stream) {
+  if (kind != SVDQ_PROBE_MFMA_I8 && kind != SVDQ_PROBE_MFMA_FP4) return SVDQ_ERR_INVALID_ARG;
+  if (blocks < 1 || iters < 1 || !sink || !aligned16(sink)) return SVDQ_ERR_INVALID_ARG;
+  const int st = current_device_check();
+  if (st != SVDQ_OK) return st;
+  return svdq::launch_probe_mfma(kind, blocks, iters, sink, stream);
+}
+
+extern "C" double svdq_probe_mfma_ops(int kind, int blocks, int iters) {
+  if ((kind != SVDQ_PROBE_MFMA_I8 && kind != SVDQ_PROBE_MFMA_FP4) || blocks < 1 || iters < 1) return 0.0;
+  return svdq::probe_mfma_ops(kind, blocks, iters);
 }

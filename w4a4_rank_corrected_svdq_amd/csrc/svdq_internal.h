@@ -41,4 +41,7 @@ int launch_awq_quant_act(const void* x, const float* inv_scale, int M, int K, vo
 int launch_awq_gemv(const void* x_hat, const float* xsum, const void* w_codes, const void* w_scales,
                     const void* w_zeros, const void* bias, int M, int N, int K, void* y, void* stream);
 
+// svdq_probes.hip
+int launch_probe_mfma(int kind, int blocks, int iters, void* sink, void* stream);
+double probe_mfma_ops(int kind, int blocks, int iters);
 }  // namespace svdq

@@ -1,0 +1,91 @@
+// Peak-rate probes for the measurement harness (not part of the layer): the
+// dense matrix-core rates that the layer's kernels are priced against,
+// measured on the device at hand next to the published figures.
+//
+// Each wave runs accumulation chains of one MFMA form for `iters`
+// iterations on register operands (no memory traffic in the loop) and
+// writes its accumulators to a sink buffer, so nothing is optimized away.
+// The forms and chain counts are the fastest measured on gfx950 with every
+// SIMD holding several waves: int8 peaks with the 32x32x32 form and one
+// chain per wave (the 16x16x64 form stays near three quarters of that), FP4
+// with the 32x32x64 form and four chains.
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "svdq.h"
+#include "svdq_internal.h"
+#include "svdq_probe.h"
+
+#include "svdq_device.h"
+
+namespace {
+
+constexpr int PROBE_THREADS = 256;
+constexpr int I8_CHAINS = 1;     // 32x32x32 int8: 16-register results
+constexpr int FP4_CHAINS = 4;    // 32x32x64 FP4: 16-register results
+
+__global__ __launch_bounds__(PROBE_THREADS) void k_probe_mfma_i8(int iters, v16i* __restrict__ sink) {
+  const int t = threadIdx.x;
+  const v4i a = v4i{t + 1, 3 * t + 5, 7, t ^ 0x55};
+  const v4i b = v4i{2 * t + 3, 11, t ^ 0x33, t + 9};
+  v16i d[I8_CHAINS];
+#pragma unroll
+  for (int c = 0; c < I8_CHAINS; ++c)
+#pragma unroll
+    for (int e = 0; e < 16; ++e) d[c][e] = c + e;
+  for (int it = 0; it < iters; ++it) {
+#pragma unroll
+    for (int c = 0; c < I8_CHAINS; ++c) d[c] = __builtin_amdgcn_mfma_i32_32x32x32_i8(a, b, d[c], 0, 0, 0);
+  }
+  v16i s = d[0];
+#pragma unroll
+  for (int c = 1; c < I8_CHAINS; ++c) s += d[c];
+  sink[static_cast<size_t>(blockIdx.x) * PROBE_THREADS + t] = s;
+}
+
+__global__ __launch_bounds__(PROBE_THREADS) void k_probe_mfma_fp4(int iters, v16f* __restrict__ sink) {
+  const int t = threadIdx.x;
+  v8i a, b;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    a[i] = (t * 0x01010101) ^ (i * 0x12345);
+    b[i] = (t * 0x00FF00FF) ^ (i * 0x6789);
+  }
+  v16f d[FP4_CHAINS];
+#pragma unroll
+  for (int c = 0; c < FP4_CHAINS; ++c)
+#pragma unroll
+    for (int e = 0; e < 16; ++e) d[c][e] = 0.f;
+  for (int it = 0; it < iters; ++it) {
+#pragma unroll
+    for (int c = 0; c < FP4_CHAINS; ++c)
+      // cbsz = blgp = 4: both operands FP4 E2M1; E8M0 scales 127 (= 1)
+      d[c] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, b, d[c], 4, 4, 0, 127, 0, 127);
+  }
+  v16f s = d[0];
+#pragma unroll
+  for (int c = 1; c < FP4_CHAINS; ++c) s += d[c];
+  sink[static_cast<size_t>(blockIdx.x) * PROBE_THREADS + t] = s;
+}
+
+}  // namespace
+
+namespace svdq {
+
+int launch_probe_mfma(int kind, int blocks, int iters, void* sink, void* stream) {
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  if (kind == SVDQ_PROBE_MFMA_I8)
+    hipLaunchKernelGGL(k_probe_mfma_i8, dim3(blocks), dim3(PROBE_THREADS), 0, st, iters, static_cast<v16i*>(sink));
+  else
+    hipLaunchKernelGGL(k_probe_mfma_fp4, dim3(blocks), dim3(PROBE_THREADS), 0, st, iters, static_cast<v16f*>(sink));
+  return hipGetLastError() == hipSuccess ? SVDQ_OK : SVDQ_ERR_HIP;
+}
+
+double probe_mfma_ops(int kind, int blocks, int iters) {
+  const double waves = static_cast<double>(blocks) * (PROBE_THREADS / 64);
+  if (kind == SVDQ_PROBE_MFMA_I8) return waves * iters * I8_CHAINS * (2.0 * 32 * 32 * 32);
+  return waves * iters * FP4_CHAINS * (2.0 * 32 * 32 * 64);
+}
+
+}  // namespace svdq
