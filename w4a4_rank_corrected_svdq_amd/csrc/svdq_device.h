@@ -45,13 +45,11 @@ __device__ __forceinline__ float gelu_tanh(float x) {
   return 0.5f * x * (1.0f + tanhf(u));
 }
 
-// FP4 E2M1 code of v: nearest of 0, 0.5, 1, 1.5, 2, 3, 4, 6 with ties to the
-// even code (mantissa bit 0), saturating at 6; the sign bit is set only for
-// a nonzero result, so values that round to zero give code 0.
-__device__ __forceinline__ uint32_t e2m1_code(float v) {
-  const float a = fabsf(v);
-  uint32_t c = (a > 0.25f) + (a >= 0.75f) + (a > 1.25f) + (a >= 1.75f) + (a > 2.5f) + (a >= 3.5f) + (a > 5.0f);
-  return c | ((v < 0.f && c != 0u) ? 8u : 0u);
+// Eight packed E2M1 codes: every -0 (nibble 1000b) becomes +0.  A nibble's
+// low three bits plus 7 carry into its bit 3 exactly when they are nonzero.
+__device__ __forceinline__ uint32_t e2m1_clear_neg_zero(uint32_t x) {
+  const uint32_t nz = ((x & 0x77777777u) + 0x77777777u) & 0x88888888u;
+  return x ^ (x & 0x88888888u & ~nz);
 }
 
 // Map the linear block index to an output tile so that the blocks of one

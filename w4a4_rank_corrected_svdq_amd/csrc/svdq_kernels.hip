@@ -154,13 +154,23 @@ __global__ __launch_bounds__(k1_waves<NT>() * 64) void k_quant_act_lora_down(
         const int ebits = static_cast<int>(__float_as_uint(amax) >> 23);   // amax >= 0
         const int e = max(ebits - 129, -127);
         const float f = __uint_as_float(static_cast<uint32_t>(127 - e) << 23);
+        // E2M1 code of x_hat * 2^-e: nearest of 0, 0.5, 1, 1.5, 2, 3, 4, 6,
+        // ties to the even code, saturating at 6, +0 for anything that
+        // rounds to zero.  gfx950's packed conversion rounds this way
+        // (checked on the device over every rounding boundary) except that
+        // values rounding to zero from below come out as -0; those are
+        // cleared.
         uint32_t p0 = 0, p1 = 0;
-#pragma unroll
-        for (int i = 0; i < 16; ++i) {
-          const uint32_t c = e2m1_code(xh[i] * f);
-          if (i < 8) p0 |= c << (4 * i);
-          else p1 |= c << (4 * (i - 8));
-        }
+        p0 = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(p0, xh[0] * f, xh[1] * f, 1.0f, 0);
+        p0 = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(p0, xh[2] * f, xh[3] * f, 1.0f, 1);
+        p0 = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(p0, xh[4] * f, xh[5] * f, 1.0f, 2);
+        p0 = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(p0, xh[6] * f, xh[7] * f, 1.0f, 3);
+        p1 = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(p1, xh[8] * f, xh[9] * f, 1.0f, 0);
+        p1 = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(p1, xh[10] * f, xh[11] * f, 1.0f, 1);
+        p1 = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(p1, xh[12] * f, xh[13] * f, 1.0f, 2);
+        p1 = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(p1, xh[14] * f, xh[15] * f, 1.0f, 3);
+        p0 = e2m1_clear_neg_zero(p0);
+        p1 = e2m1_clear_neg_zero(p1);
         if (row_ok) {
           *reinterpret_cast<uint2*>(x_codes + static_cast<size_t>(row) * (K / 2) + (k0 >> 1)) = make_uint2(p0, p1);
           if (((lane >> 4) & 1) == 0)
