@@ -36,9 +36,10 @@ namespace {
 // elements, E8M0 scale per 32) or none, which leaves only the down
 // projection (the unfused reference path, which reads X a second time).
 //
-// Block: 16 token rows, 16 waves (8 for ranks above 64, and when the grid
-// has more blocks than the device has CUs: two 8-wave blocks then share a CU
-// instead of leaving a second round of blocks); wave w handles
+// Block: 16 token rows (32 when the 16-row blocks would outnumber the CUs,
+// below), 16 waves (8 for ranks above 64, and for a grid larger than the CU
+// count: two 8-wave blocks then share a CU instead of leaving a second round
+// of blocks); wave w handles
 // groups w, w+W, ... of K in batches of up to 2 groups whose loads are all
 // issued before any is used, so a CU keeps enough bytes in flight to stream HBM.  smooth_inv is
 // staged once per block in LDS.  Lane l works on row (l % 16) and the 16
@@ -56,45 +57,56 @@ template <int NT> constexpr int k1_waves() { return NT <= 4 ? 16 : 8; }
 
 enum { Q_NONE = 0, Q_INT4 = 1, Q_MXFP4 = 2 };
 
-template <int ACT, int NT, int QM>
+template <int ACT, int NT, int QM, int RT>
 __global__ __launch_bounds__(k1_waves<NT>() * 64) void k_quant_act_lora_down(
     const uint16_t* __restrict__ x, const float* __restrict__ smooth_inv,
     const uint16_t* __restrict__ lora_down, int M, int K, int rank,
     uint8_t* __restrict__ x_codes, void* __restrict__ x_scales_v, float* __restrict__ lora_act) {
   extern __shared__ __align__(16) unsigned char k1_smem_raw[];
-  float* s_si = reinterpret_cast<float*>(k1_smem_raw);                  // [K]
-  float(*red)[2][16][16] = reinterpret_cast<float(*)[2][16][16]>(s_si + K);  // [waves][2][16][16]
+  float* s_si = reinterpret_cast<float*>(k1_smem_raw);   // [K]
+  float* red = s_si + K;                                   // [waves][2][16 RT][16]
 
   const int nwaves = blockDim.x >> 6;                   // k1_waves<NT>() or 8 (uniform)
   const int lane = threadIdx.x & 63;
   const int wave = threadIdx.x >> 6;
-  const int m0 = blockIdx.x * K1_ROWS;
-  const int row = m0 + (lane & 15);
-  const bool row_ok = row < M;
+  const int m0 = blockIdx.x * (K1_ROWS * RT);
   const int kq = (lane >> 4) * 16;
   const int G = K / GROUP;
   const int ntiles = rank >> 4;
+  int row[RT];
+  bool row_ok[RT];
+  const uint16_t* xrow[RT];
+#pragma unroll
+  for (int rt = 0; rt < RT; ++rt) {
+    row[rt] = m0 + K1_ROWS * rt + (lane & 15);
+    row_ok[rt] = row[rt] < M;
+    xrow[rt] = x + static_cast<size_t>(row_ok[rt] ? row[rt] : 0) * K;
+  }
 
   for (int k = threadIdx.x * 4; k < K; k += blockDim.x * 4)
     *reinterpret_cast<float4*>(s_si + k) = *reinterpret_cast<const float4*>(smooth_inv + k);
   __syncthreads();
 
-  v4f acc[NT > 0 ? NT : 1];
+  v4f acc[RT][NT > 0 ? NT : 1];
 #pragma unroll
-  for (int t = 0; t < (NT > 0 ? NT : 1); ++t) acc[t] = v4f{0.f, 0.f, 0.f, 0.f};
+  for (int rt = 0; rt < RT; ++rt)
+#pragma unroll
+    for (int t = 0; t < (NT > 0 ? NT : 1); ++t) acc[rt][t] = v4f{0.f, 0.f, 0.f, 0.f};
 
-  const uint16_t* xrow = x + static_cast<size_t>(row_ok ? row : 0) * K;
-  constexpr int K1_BATCH = NT <= 2 ? 2 : 1;
+  constexpr int K1_BATCH = (NT <= 2 && RT == 1) ? 2 : 1;
 
   for (int g0 = wave; g0 < G; g0 += nwaves * K1_BATCH) {
-    uint4 raw[K1_BATCH][2];
+    uint4 raw[K1_BATCH][RT][2];
 #pragma unroll
     for (int b = 0; b < K1_BATCH; ++b) {
       const int g = g0 + b * nwaves;
-      raw[b][0] = raw[b][1] = make_uint4(0, 0, 0, 0);
-      if (row_ok && g < G) {
-        raw[b][0] = *reinterpret_cast<const uint4*>(xrow + g * GROUP + kq);
-        raw[b][1] = *reinterpret_cast<const uint4*>(xrow + g * GROUP + kq + 8);
+#pragma unroll
+      for (int rt = 0; rt < RT; ++rt) {
+        raw[b][rt][0] = raw[b][rt][1] = make_uint4(0, 0, 0, 0);
+        if (row_ok[rt] && g < G) {
+          raw[b][rt][0] = *reinterpret_cast<const uint4*>(xrow[rt] + g * GROUP + kq);
+          raw[b][rt][1] = *reinterpret_cast<const uint4*>(xrow[rt] + g * GROUP + kq + 8);
+        }
       }
     }
 #pragma unroll
@@ -105,89 +117,101 @@ __global__ __launch_bounds__(k1_waves<NT>() * 64) void k_quant_act_lora_down(
       const float4* sp = reinterpret_cast<const float4*>(s_si + k0);
       float4 s4[4] = {sp[0], sp[1], sp[2], sp[3]};
       const float* sv = reinterpret_cast<const float*>(s4);
-      const uint32_t w[8] = {raw[b][0].x, raw[b][0].y, raw[b][0].z, raw[b][0].w,
-                             raw[b][1].x, raw[b][1].y, raw[b][1].z, raw[b][1].w};
-      float xh[16];
+      v8bf a0[RT], a1[RT];
 #pragma unroll
-      for (int i = 0; i < 8; ++i) {
-        float lo = bf16_bits_to_f32(w[i] & 0xFFFFu);
-        float hi = bf16_bits_to_f32(w[i] >> 16);
-        if (ACT == SVDQ_ACT_GELU_TANH) {
-          lo = gelu_tanh(lo);
-          hi = gelu_tanh(hi);
-        }
-        xh[2 * i] = lo * sv[2 * i];
-        xh[2 * i + 1] = hi * sv[2 * i + 1];
-      }
-      if constexpr (QM == Q_INT4) {
-        _Float16* x_scales = static_cast<_Float16*>(x_scales_v);
-        float amax = 0.f;
-#pragma unroll
-        for (int i = 0; i < 16; ++i) amax = fmaxf(amax, fabsf(xh[i]));
-        amax = fmaxf(amax, __shfl_xor(amax, 16));
-        amax = fmaxf(amax, __shfl_xor(amax, 32));
-        const float s32 = amax / 7.0f;
-        const _Float16 sh = static_cast<_Float16>(s32);
-        const float sf = static_cast<float>(sh);
-        const float rcp = (sf == 0.f) ? 0.f : 1.0f / sf;
-        uint32_t p0 = 0, p1 = 0;
+      for (int rt = 0; rt < RT; ++rt) {
+        const uint32_t w[8] = {raw[b][rt][0].x, raw[b][rt][0].y, raw[b][rt][0].z, raw[b][rt][0].w,
+                               raw[b][rt][1].x, raw[b][rt][1].y, raw[b][rt][1].z, raw[b][rt][1].w};
+        float xh[16];
 #pragma unroll
         for (int i = 0; i < 8; ++i) {
-          const float q0 = fminf(fmaxf(rintf(xh[i] * rcp), -8.f), 7.f);
-          const float q1 = fminf(fmaxf(rintf(xh[8 + i] * rcp), -8.f), 7.f);
-          p0 |= (static_cast<uint32_t>(static_cast<int>(q0)) & 0xFu) << (4 * i);
-          p1 |= (static_cast<uint32_t>(static_cast<int>(q1)) & 0xFu) << (4 * i);
+          float lo = bf16_bits_to_f32(w[i] & 0xFFFFu);
+          float hi = bf16_bits_to_f32(w[i] >> 16);
+          if (ACT == SVDQ_ACT_GELU_TANH) {
+            lo = gelu_tanh(lo);
+            hi = gelu_tanh(hi);
+          }
+          xh[2 * i] = lo * sv[2 * i];
+          xh[2 * i + 1] = hi * sv[2 * i + 1];
         }
-        if (row_ok) {
-          *reinterpret_cast<uint2*>(x_codes + static_cast<size_t>(row) * (K / 2) + (k0 >> 1)) = make_uint2(p0, p1);
-          if (lane < 16) x_scales[static_cast<size_t>(g) * M + row] = sh;
-        }
-      } else if constexpr (QM == Q_MXFP4) {
-        // MXFP4: blocks of 32 k are the lane pairs (l, l ^ 16).  Scale
-        // 2^e with e = floor(log2 amax) - 2 read off the exponent field,
-        // clamped at -127 (zero and tiny blocks); x_hat * 2^-e is exact.
-        uint8_t* x_scales = static_cast<uint8_t*>(x_scales_v);
-        float amax = 0.f;
+        if constexpr (QM == Q_INT4) {
+          _Float16* x_scales = static_cast<_Float16*>(x_scales_v);
+          float amax = 0.f;
 #pragma unroll
-        for (int i = 0; i < 16; ++i) amax = fmaxf(amax, fabsf(xh[i]));
-        amax = fmaxf(amax, __shfl_xor(amax, 16));
-        const int ebits = static_cast<int>(__float_as_uint(amax) >> 23);   // amax >= 0
-        const int e = max(ebits - 129, -127);
-        const float f = __uint_as_float(static_cast<uint32_t>(127 - e) << 23);
-        // E2M1 code of x_hat * 2^-e: nearest of 0, 0.5, 1, 1.5, 2, 3, 4, 6,
-        // ties to the even code, saturating at 6, +0 for anything that
-        // rounds to zero.  gfx950's packed conversion rounds this way
-        // (checked on the device over every rounding boundary) except that
-        // values rounding to zero from below come out as -0; those are
-        // cleared.
-        uint32_t p0 = 0, p1 = 0;
-        p0 = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(p0, xh[0] * f, xh[1] * f, 1.0f, 0);
-        p0 = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(p0, xh[2] * f, xh[3] * f, 1.0f, 1);
-        p0 = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(p0, xh[4] * f, xh[5] * f, 1.0f, 2);
-        p0 = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(p0, xh[6] * f, xh[7] * f, 1.0f, 3);
-        p1 = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(p1, xh[8] * f, xh[9] * f, 1.0f, 0);
-        p1 = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(p1, xh[10] * f, xh[11] * f, 1.0f, 1);
-        p1 = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(p1, xh[12] * f, xh[13] * f, 1.0f, 2);
-        p1 = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(p1, xh[14] * f, xh[15] * f, 1.0f, 3);
-        p0 = e2m1_clear_neg_zero(p0);
-        p1 = e2m1_clear_neg_zero(p1);
-        if (row_ok) {
-          *reinterpret_cast<uint2*>(x_codes + static_cast<size_t>(row) * (K / 2) + (k0 >> 1)) = make_uint2(p0, p1);
-          if (((lane >> 4) & 1) == 0)
-            x_scales[static_cast<size_t>(row) * (K / 32) + (k0 >> 5)] = static_cast<uint8_t>(e + 127);
+          for (int i = 0; i < 16; ++i) amax = fmaxf(amax, fabsf(xh[i]));
+          amax = fmaxf(amax, __shfl_xor(amax, 16));
+          amax = fmaxf(amax, __shfl_xor(amax, 32));
+          const float s32 = amax / 7.0f;
+          const _Float16 sh = static_cast<_Float16>(s32);
+          const float sf = static_cast<float>(sh);
+          const float rcp = (sf == 0.f) ? 0.f : 1.0f / sf;
+          uint32_t p0 = 0, p1 = 0;
+#pragma unroll
+          for (int i = 0; i < 8; ++i) {
+            const float q0 = fminf(fmaxf(rintf(xh[i] * rcp), -8.f), 7.f);
+            const float q1 = fminf(fmaxf(rintf(xh[8 + i] * rcp), -8.f), 7.f);
+            p0 |= (static_cast<uint32_t>(static_cast<int>(q0)) & 0xFu) << (4 * i);
+            p1 |= (static_cast<uint32_t>(static_cast<int>(q1)) & 0xFu) << (4 * i);
+          }
+          if (row_ok[rt]) {
+            *reinterpret_cast<uint2*>(x_codes + static_cast<size_t>(row[rt]) * (K / 2) + (k0 >> 1)) =
+                make_uint2(p0, p1);
+            if (lane < 16) x_scales[static_cast<size_t>(g) * M + row[rt]] = sh;
+          }
+        } else if constexpr (QM == Q_MXFP4) {
+          // MXFP4: blocks of 32 k are the lane pairs (l, l ^ 16).  Scale
+          // 2^e with e = floor(log2 amax) - 2 read off the exponent field,
+          // clamped at -127 (zero and tiny blocks); x_hat * 2^-e is exact.
+          uint8_t* x_scales = static_cast<uint8_t*>(x_scales_v);
+          float amax = 0.f;
+#pragma unroll
+          for (int i = 0; i < 16; ++i) amax = fmaxf(amax, fabsf(xh[i]));
+          amax = fmaxf(amax, __shfl_xor(amax, 16));
+          const int ebits = static_cast<int>(__float_as_uint(amax) >> 23);   // amax >= 0
+          const int e = max(ebits - 129, -127);
+          const float f = __uint_as_float(static_cast<uint32_t>(127 - e) << 23);
+          // E2M1 code of x_hat * 2^-e: nearest of 0, 0.5, 1, 1.5, 2, 3, 4, 6,
+          // ties to the even code, saturating at 6, +0 for anything that
+          // rounds to zero.  gfx950's packed conversion rounds this way
+          // (checked on the device over every rounding boundary) except that
+          // values rounding to zero from below come out as -0; those are
+          // cleared.
+          uint32_t p0 = 0, p1 = 0;
+          p0 = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(p0, xh[0] * f, xh[1] * f, 1.0f, 0);
+          p0 = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(p0, xh[2] * f, xh[3] * f, 1.0f, 1);
+          p0 = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(p0, xh[4] * f, xh[5] * f, 1.0f, 2);
+          p0 = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(p0, xh[6] * f, xh[7] * f, 1.0f, 3);
+          p1 = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(p1, xh[8] * f, xh[9] * f, 1.0f, 0);
+          p1 = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(p1, xh[10] * f, xh[11] * f, 1.0f, 1);
+          p1 = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(p1, xh[12] * f, xh[13] * f, 1.0f, 2);
+          p1 = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(p1, xh[14] * f, xh[15] * f, 1.0f, 3);
+          p0 = e2m1_clear_neg_zero(p0);
+          p1 = e2m1_clear_neg_zero(p1);
+          if (row_ok[rt]) {
+            *reinterpret_cast<uint2*>(x_codes + static_cast<size_t>(row[rt]) * (K / 2) + (k0 >> 1)) =
+                make_uint2(p0, p1);
+            if (((lane >> 4) & 1) == 0)
+              x_scales[static_cast<size_t>(row[rt]) * (K / 32) + (k0 >> 5)] = static_cast<uint8_t>(e + 127);
+          }
+        }
+        if constexpr (NT > 0) {
+          a0[rt] = pack_bf16x8(xh);
+          a1[rt] = pack_bf16x8(xh + 8);
         }
       }
       if constexpr (NT > 0) {
-        const v8bf a0 = pack_bf16x8(xh);
-        const v8bf a1 = pack_bf16x8(xh + 8);
+        // each L1 fragment serves every row tile of the block
 #pragma unroll
         for (int t = 0; t < NT; ++t) {
           if (t < ntiles) {
             const uint16_t* bp = lora_down + static_cast<size_t>(t * 16 + (lane & 15)) * K + k0;
             const v8bf b0 = __builtin_bit_cast(v8bf, *reinterpret_cast<const uint4*>(bp));
             const v8bf b1 = __builtin_bit_cast(v8bf, *reinterpret_cast<const uint4*>(bp + 8));
-            acc[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a0, b0, acc[t], 0, 0, 0);
-            acc[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a1, b1, acc[t], 0, 0, 0);
+#pragma unroll
+            for (int rt = 0; rt < RT; ++rt) {
+              acc[rt][t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a0[rt], b0, acc[rt][t], 0, 0, 0);
+              acc[rt][t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a1[rt], b1, acc[rt][t], 0, 0, 0);
+            }
           }
         }
       }
@@ -196,7 +220,9 @@ __global__ __launch_bounds__(k1_waves<NT>() * 64) void k_quant_act_lora_down(
 
   if constexpr (NT > 0) {
     // Deterministic cross-wave reduction of the down projection, two rank
-    // tiles (32 ranks) at a time, summed in wave order.
+    // tiles (32 ranks) at a time, summed in wave order.  red[w][tt][r][c]:
+    // wave w's partial of row r (of the block's 16 RT), rank 16 (t0 + tt) + c.
+    constexpr int RR = K1_ROWS * RT;
     for (int t0 = 0; t0 < ntiles; t0 += 2) {
 #pragma unroll
       for (int tt = 0; tt < 2; ++tt) {
@@ -204,18 +230,28 @@ __global__ __launch_bounds__(k1_waves<NT>() * 64) void k_quant_act_lora_down(
         for (int t = 0; t < NT; ++t) {
           if (t == t0 + tt) {
 #pragma unroll
-            for (int i = 0; i < 4; ++i) red[wave][tt][4 * (lane >> 4) + i][lane & 15] = acc[t][i];
+            for (int rt = 0; rt < RT; ++rt)
+#pragma unroll
+              for (int i = 0; i < 4; ++i)
+                red[((wave * 2 + tt) * RR + K1_ROWS * rt + 4 * (lane >> 4) + i) * 16 + (lane & 15)] = acc[rt][t][i];
           }
         }
       }
       __syncthreads();
-      if (threadIdx.x < 512) {
-        const int tt = threadIdx.x >> 8;         // 0..1
-        const int r = (threadIdx.x >> 4) & 15;   // row in tile
-        const int c = threadIdx.x & 15;          // col in tile
+      for (int o = threadIdx.x; o < 2 * RR * 16; o += blockDim.x) {
+        const int tt = o / (RR * 16);
+        const int r = (o >> 4) % RR;
+        const int c = o & 15;
         if (t0 + tt < ntiles && m0 + r < M) {
+          // in wave order, eight loads in flight at a time (8 or 16 waves)
           float s = 0.f;
-          for (int wv = 0; wv < nwaves; ++wv) s += red[wv][tt][r][c];
+          for (int w8 = 0; w8 < nwaves; w8 += 8) {
+            float v[8];
+#pragma unroll
+            for (int j = 0; j < 8; ++j) v[j] = red[(((w8 + j) * 2 + tt) * RR + r) * 16 + c];
+#pragma unroll
+            for (int j = 0; j < 8; ++j) s += v[j];
+          }
           lora_act[static_cast<size_t>(m0 + r) * rank + (t0 + tt) * 16 + c] = s;
         }
       }
@@ -1214,33 +1250,54 @@ int device_cu_count() {
   return cached[dev];
 }
 
-template <int ACT, int NT, int QM>
+template <int ACT, int NT, int QM, int RT>
 void launch_k1_kernel(const void* x, const float* smooth_inv, const void* lora_down, int M, int K, int rank,
                       void* x_codes, void* x_scales, float* lora_act, size_t smem, hipStream_t st) {
-  auto kern = k_quant_act_lora_down<ACT, NT, QM>;
+  auto kern = k_quant_act_lora_down<ACT, NT, QM, RT>;
   if (smem > 64 * 1024)
     (void)hipFuncSetAttribute(reinterpret_cast<const void*>(kern), hipFuncAttributeMaxDynamicSharedMemorySize,
                               static_cast<int>(smem));
   // Grids larger than the CU count run 8-wave blocks, two per CU, instead of
   // a second round of 16-wave blocks.
-  const int blocks = (M + K1_ROWS - 1) / K1_ROWS;
+  const int blocks = (M + K1_ROWS * RT - 1) / (K1_ROWS * RT);
   const int waves = (k1_waves<NT>() == 16 && blocks > device_cu_count()) ? 8 : k1_waves<NT>();
   hipLaunchKernelGGL(kern, dim3(blocks), dim3(waves * 64), smem, st,
                      static_cast<const uint16_t*>(x), smooth_inv, static_cast<const uint16_t*>(lora_down), M, K,
                      rank, static_cast<uint8_t*>(x_codes), x_scales, lora_act);
 }
 
+// Every block reads all of L1 (K x rank bf16), twice its own X bytes at rank
+// 32, so once the 16-row blocks outnumber the CUs (M = 4608 and up) blocks of
+// 32 rows, which use each L1 fragment for both row tiles, move a third fewer
+// bytes per CU.  Up to rank 64, while the doubled reduction buffer fits LDS,
+// and without the GELU prologue (its registers would spill).
+template <int ACT, int QM, int NT>
+void launch_k1_nt(const void* x, const float* smooth_inv, const void* lora_down, int M, int K, int rank,
+                  void* x_codes, void* x_scales, float* lora_act, hipStream_t st) {
+  const size_t red1 = sizeof(float) * K1_MAX_WAVES * 2 * K1_ROWS * 16;
+  const size_t smem1 = static_cast<size_t>(K) * sizeof(float) + red1;
+  if constexpr (NT > 0 && NT <= 4 && ACT == SVDQ_ACT_NONE) {
+    const bool many = (M + K1_ROWS - 1) / K1_ROWS > device_cu_count();
+    if (many && smem1 + red1 <= 160 * 1024) {
+      launch_k1_kernel<ACT, NT, QM, 2>(x, smooth_inv, lora_down, M, K, rank, x_codes, x_scales, lora_act,
+                                       smem1 + red1, st);
+      return;
+    }
+  }
+  launch_k1_kernel<ACT, NT, QM, 1>(x, smooth_inv, lora_down, M, K, rank, x_codes, x_scales, lora_act, smem1, st);
+}
+
 template <int ACT, int QM>
 int launch_k1(const void* x, const float* smooth_inv, const void* lora_down, int M, int K, int rank,
               void* x_codes, void* x_scales, float* lora_act, hipStream_t st) {
-  const size_t smem = static_cast<size_t>(K) * sizeof(float) + sizeof(float) * K1_MAX_WAVES * 2 * 16 * 16;
+  const size_t smem = static_cast<size_t>(K) * sizeof(float) + sizeof(float) * K1_MAX_WAVES * 2 * K1_ROWS * 16;
   if (smem > 160 * 1024) return SVDQ_ERR_UNSUPPORTED_SHAPE;
   const int nt = rank / 16;
-  if (nt == 0) launch_k1_kernel<ACT, 0, QM>(x, smooth_inv, lora_down, M, K, rank, x_codes, x_scales, lora_act, smem, st);
-  else if (nt <= 2) launch_k1_kernel<ACT, 2, QM>(x, smooth_inv, lora_down, M, K, rank, x_codes, x_scales, lora_act, smem, st);
-  else if (nt <= 4) launch_k1_kernel<ACT, 4, QM>(x, smooth_inv, lora_down, M, K, rank, x_codes, x_scales, lora_act, smem, st);
-  else if (nt <= 8) launch_k1_kernel<ACT, 8, QM>(x, smooth_inv, lora_down, M, K, rank, x_codes, x_scales, lora_act, smem, st);
-  else launch_k1_kernel<ACT, 16, QM>(x, smooth_inv, lora_down, M, K, rank, x_codes, x_scales, lora_act, smem, st);
+  if (nt == 0) launch_k1_nt<ACT, QM, 0>(x, smooth_inv, lora_down, M, K, rank, x_codes, x_scales, lora_act, st);
+  else if (nt <= 2) launch_k1_nt<ACT, QM, 2>(x, smooth_inv, lora_down, M, K, rank, x_codes, x_scales, lora_act, st);
+  else if (nt <= 4) launch_k1_nt<ACT, QM, 4>(x, smooth_inv, lora_down, M, K, rank, x_codes, x_scales, lora_act, st);
+  else if (nt <= 8) launch_k1_nt<ACT, QM, 8>(x, smooth_inv, lora_down, M, K, rank, x_codes, x_scales, lora_act, st);
+  else launch_k1_nt<ACT, QM, 16>(x, smooth_inv, lora_down, M, K, rank, x_codes, x_scales, lora_act, st);
   return hipGetLastError() == hipSuccess ? SVDQ_OK : SVDQ_ERR_HIP;
 }
 
