@@ -13,8 +13,8 @@
  * Two device entry points follow the fusion the model card's "Nunchaku
  * Engine Design" describes: the down projection runs in the same kernel as
  * the activation quantizer (both read the 16-bit input), and the up
- * projection runs in the epilogue of the 4-bit GEMM (both write the 16-bit
- * output).
+ * projection runs in the 4-bit GEMM kernel, into the same fp32 accumulators
+ * (both write the 16-bit output).
  *
  * Conventions for every function:
  *  - Return value: SVDQ_OK (0) or a negative svdq_status.  Arguments are
@@ -144,8 +144,8 @@ int svdq_quant_act_lora_down(const void* x, const float* smooth_inv, const void*
 
 /* Device, asynchronous.  Kernel 2: W4A4 GEMM on int8 MFMA with exact int32
  * per-group products, per-group dequantization, and the up projection plus
- * bias in the epilogue (model card, "Nunchaku Engine Design": the up
- * projection and the 4-bit compute share their output).
+ * bias in the same fp32 accumulators (model card, "Nunchaku Engine Design":
+ * the up projection and the 4-bit compute share their output).
  *
  *   x_codes  [M][K/2] u8, x_scales [K/64][M] fp16  (from kernel 1)
  *   w_codes  [N][K/2] u8, w_scales [K/64][N] fp16  (from preparation)
@@ -157,7 +157,11 @@ int svdq_quant_act_lora_down(const void* x, const float* smooth_inv, const void*
  *                + sum_j bf16(lora_act[m,j]) lora_up[n][j] + bias[n],
  *            P_g = sum over the 64 k of group g of q_x q_w (exact int32),
  *            accumulated in fp32 over g in increasing order, rounded to the
- *            output type to nearest even. */
+ *            output type to nearest even.  Where the bias and the up
+ *            projection enter that fp32 sum depends on the tile form the
+ *            launch picks (first for 256 x 256 tiles, used when M is even and
+ *            there are at least 192 of them; last for 128 x 128 tiles); both
+ *            orders are within the rounding of the fp32 sum. */
 int svdq_gemm_w4a4_lora_up(const void* x_codes, const void* x_scales,
                            const void* w_codes, const void* w_scales,
                            const float* lora_act, const void* lora_up, const void* bias,
