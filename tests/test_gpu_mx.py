@@ -74,8 +74,10 @@ def run_k2(xc, xs, abi, la, bias_bits, M, out_dtype=L.SVDQ_OUT_BF16):
 
 
 # ------------------------------------------------------------------ kernel 1 (MXFP4 quantizer)
+# (4200, 256, 32): more 16-row blocks than an MI355X has CUs, so kernel 1
+# runs its 32-row blocks
 @pytest.mark.parametrize("M,K,rank", [(300, 512, 32), (1, 128, 16), (16, 256, 0), (257, 1024, 48),
-                                      (33, 384, 128)])
+                                      (33, 384, 128), (4200, 256, 32)])
 def test_k1_mx_codes_scales_bit_exact(M, K, rank):
     N = max(64, ((rank + 7) // 8) * 8)
     wl, Lr, po, abi = _case(M, K, N, rank, seed=90 + M)

@@ -117,7 +117,7 @@ def _small_case(M=300, K=512, N=264, rank=32, seed=41, bias=False, n_out=4):
 
 
 # (4200, 256, 32) and (4111, 192, 64): more 16-row blocks than an MI355X has
-# CUs, so kernel 1 runs its 8-wave blocks
+# CUs, so kernel 1 runs its 32-row blocks
 @pytest.mark.parametrize("M,K,rank", [(300, 512, 32), (1, 64, 16), (16, 128, 0), (257, 1024, 48),
                                       (64, 512, 128), (33, 256, 256), (4200, 256, 32), (4111, 192, 64)])
 def test_k1_codes_scales_lora_act(M, K, rank):
