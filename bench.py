@@ -61,16 +61,21 @@ BENCH_WORKLOADS = {
 }
 
 
+def code_tokens(src: str) -> str:
+    """C/C++ source with comments removed and whitespace runs collapsed."""
+    import re
+    src = re.sub(r"/\*.*?\*/", " ", src, flags=re.S)
+    src = re.sub(r"//[^\n]*", " ", src)
+    return " ".join(src.split())
+
+
 def kernel_source_hash() -> str:
     """Hash of the kernel sources with comments and whitespace removed, so
     that the stored counter figures stay valid across comment-only edits."""
-    import re
     h = hashlib.sha256()
     for f in ("svdq_kernels.hip", "svdq_mx_kernels.hip", "svdq_device.h"):
         src = open(os.path.join(ROOT, "w4a4_rank_corrected_svdq_amd", "csrc", f)).read()
-        src = re.sub(r"/\*.*?\*/", " ", src, flags=re.S)
-        src = re.sub(r"//[^\n]*", " ", src)
-        h.update(" ".join(src.split()).encode())
+        h.update(code_tokens(src).encode())
     return h.hexdigest()[:16]
 
 
