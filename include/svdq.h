@@ -214,6 +214,82 @@ int svdq_lora_up_add(const float* lora_act, const void* lora_up, int M, int N, i
                      void* stream);
 
 /* ------------------------------------------------------------------------
+ * The INT4 layer on the 6-bit matrix cores.  gfx950 has no INT4 MFMA; its
+ * int8 MFMA is the 5.0 POPS path, its 6-bit float MFMA
+ * (v_mfma_scale_f32_32x32x64_f8f6f4) the 10 PFLOPS path.  Every INT4 code
+ * q in [-8, 7] is exactly a value of the 6-bit float format E3M2 (sign,
+ * 3 exponent bits with bias 3, 2 mantissa bits), and the MFMA's 64 exact
+ * products of one group sum exactly in its fp32 accumulator, so the
+ * per-group integer product P_g of the W4A4 GEMM (model card, "Nunchaku
+ * Engine Design": 4-bit compute fused with the up projection) comes out bit
+ * for bit as the integer result.  The entry points below compute the same
+ * layer as svdq_quant_act_lora_down + svdq_gemm_w4a4_lora_up -- the same
+ * codes, scales, products and dequantization -- with the codes carried in
+ * 6-bit fields (0.75 byte per code instead of 0.5) laid out as the MFMA
+ * reads them.
+ *
+ * Fragment layout of a [rows][K] code matrix: [K/64][RB][1536 bytes], one
+ * 1536-byte fragment per (group g of 64 k, row block rb of 32 rows).  Lane
+ * l = r + 32 h (r = 0..31, h = 0..1) of a fragment holds the 32 codes
+ * k = 64 g + 32 h + j (j = 0..31) of the row in slot r, as a 192-bit
+ * little-endian string with code j in bits 6j .. 6j + 5; the string's
+ * dwords 0..3 are stored at byte 16 l of the fragment and dwords 4..5 at
+ * byte 1024 + 8 l.  Code values: E3M2 bit patterns (0 = +0 for q = 0).
+ *   SVDQ_FP6_ACTIVATIONS: slot r of row block rb is row 32 rb + r;
+ *       RB = ceil(rows / 32).
+ *   SVDQ_FP6_WEIGHTS: rows are grouped in panels of 128; slot r of row
+ *       block 4 p + t is row 128 p + 4 r + t; RB = 4 ceil(rows / 128).
+ * Slots past the last row hold +0.
+ * ------------------------------------------------------------------------ */
+enum { SVDQ_FP6_ACTIVATIONS = 0, SVDQ_FP6_WEIGHTS = 1 };
+
+/* Bytes of a fragment-layout buffer: (K/64) * RB * 1536.  K % 64 != 0 returns
+ * SVDQ_ERR_UNSUPPORTED_SHAPE; rows < 0, K <= 0, an unknown layout or a NULL
+ * bytes_out SVDQ_ERR_INVALID_ARG. */
+int svdq_fp6_operand_bytes(int rows, int K, int layout, size_t* bytes_out);
+
+/* Host, synchronous.  Re-packs nibble codes (codes [rows][K/2] u8, two's
+ * complement, low nibble = even k, as svdq_prepare_weights writes w_codes)
+ * into the fragment layout `layout` (out: caller-owned host buffer of
+ * svdq_fp6_operand_bytes bytes).  Used once per layer for the weights
+ * (layout SVDQ_FP6_WEIGHTS). */
+int svdq_pack_fp6_operand(const uint8_t* codes, int rows, int K, int layout, uint8_t* out);
+
+/* Device, asynchronous.  Kernel 1 writing the codes in the fragment layout:
+ * the same smoothing, quantizer, scales and down projection as
+ * svdq_quant_act_lora_down (the same kernel, another store of the codes).
+ *   x [M][K] bf16, smooth_inv [K] fp32, lora_down [rank][K] bf16 (NULL if
+ *   rank == 0), act SVDQ_ACT_NONE or SVDQ_ACT_GELU_TANH.
+ * Outputs:
+ *   x_fp6    fragment layout SVDQ_FP6_ACTIVATIONS, (K/64) * ceil(M/32) * 1536
+ *            bytes; rows M .. 32 ceil(M/32) - 1 are written as +0 codes
+ *   x_scales [K/64][Mp] fp16 with Mp = 32 ceil(M/32) (padded rows: 0)
+ *   lora_act [M][rank] fp32 (NULL if rank == 0)
+ * Errors as svdq_quant_act_lora_down; buffers of 2 GiB or more return
+ * SVDQ_ERR_UNSUPPORTED_SHAPE. */
+int svdq_quant_act_lora_down_fp6(const void* x, const float* smooth_inv, const void* lora_down,
+                                 int M, int K, int rank, int group, int act,
+                                 void* x_fp6, void* x_scales, float* lora_act, void* stream);
+
+/* Device, asynchronous.  Kernel 2 on the 6-bit MFMA: the output of
+ * svdq_gemm_w4a4_lora_up for the same codes and scales,
+ *   y = sum_g s_x[m,g] s_w[g,n] P_g[m,n] + sum_j bf16(lora_act[m,j]) lora_up[n][j] + bias[n],
+ * accumulated in fp32 starting from bias + up projection and adding the
+ * groups in increasing g, each as fma(P_g * s_x, s_w, acc) (P_g * s_x is
+ * exact), rounded to bf16 to nearest even (or stored fp32).
+ *   x_fp6    SVDQ_FP6_ACTIVATIONS layout of the activation codes,
+ *   x_scales [K/64][Mp] fp16, Mp = 32 ceil(M/32)   (both from kernel 1)
+ *   w_fp6    SVDQ_FP6_WEIGHTS layout of the weight codes (svdq_pack_fp6_operand),
+ *   w_scales [K/64][N] fp16, lora_act [M][rank] fp32, lora_up [N][rank]
+ *   bf16 (NULL if rank == 0), bias [N] bf16 or NULL.
+ * Shape rules and errors as svdq_gemm_w4a4_lora_up. */
+int svdq_gemm_w4a4_fp6_lora_up(const void* x_fp6, const void* x_scales,
+                               const void* w_fp6, const void* w_scales,
+                               const float* lora_act, const void* lora_up, const void* bias,
+                               int M, int N, int K, int rank, int group, int out_dtype,
+                               void* y, void* stream);
+
+/* ------------------------------------------------------------------------
  * 4-bit float variant (MXFP4).  The pages offer the layer with INT4 and with
  * 4-bit float operands ("Bringing Nunchaku 4-bit Diffusion Inference to
  * Diffusers", "Background: SVDQuant and Nunchaku"; the ``precision`` field

@@ -23,6 +23,8 @@ SVDQ_OUT_BF16 = 0
 SVDQ_OUT_F32 = 1
 SVDQ_GROUP = 64
 SVDQ_MAX_RANK = 256
+SVDQ_FP6_ACTIVATIONS = 0
+SVDQ_FP6_WEIGHTS = 1
 
 _p = ctypes.c_void_p
 _i = ctypes.c_int
@@ -51,6 +53,10 @@ SIGNATURES = {
                                         _p, _p, _p, _p, _p, _p]),
     "svdq_quant_act_lora_down_mxfp4": (_i, [_p, _p, _p, _i, _i, _i, _i, _p, _p, _p, _p]),
     "svdq_gemm_mxfp4_lora_up": (_i, [_p, _p, _p, _p, _p, _p, _p, _i, _i, _i, _i, _i, _p, _p]),
+    "svdq_fp6_operand_bytes": (_i, [_i, _i, _i, ctypes.POINTER(ctypes.c_size_t)]),
+    "svdq_pack_fp6_operand": (_i, [_p, _i, _i, _i, _p]),
+    "svdq_quant_act_lora_down_fp6": (_i, [_p, _p, _p, _i, _i, _i, _i, _i, _p, _p, _p, _p]),
+    "svdq_gemm_w4a4_fp6_lora_up": (_i, [_p, _p, _p, _p, _p, _p, _p, _i, _i, _i, _i, _i, _i, _p, _p]),
     # include/svdq_probe.h (benchmark harness)
     "svdq_probe_mfma": (_i, [_i, _i, _i, _p, _p]),
     "svdq_probe_mfma_ops": (ctypes.c_double, [_i, _i, _i]),

@@ -122,6 +122,53 @@ extern "C" int svdq_gemm_w4a4_lora_up(const void* x_codes, const void* x_scales,
                                         N, K, rank, out_dtype, y, stream);
 }
 
+extern "C" int svdq_quant_act_lora_down_fp6(const void* x, const float* smooth_inv, const void* lora_down, int M,
+                                            int K, int rank, int group, int act, void* x_fp6, void* x_scales,
+                                            float* lora_act, void* stream) {
+  if (M < 0 || K <= 0 || rank < 0 || rank > K || group <= 0) return SVDQ_ERR_INVALID_ARG;
+  if (group != SVDQ_GROUP || K % group != 0 || rank % 16 != 0 || rank > SVDQ_MAX_RANK || K > 32768)
+    return SVDQ_ERR_UNSUPPORTED_SHAPE;
+  if (act != SVDQ_ACT_NONE && act != SVDQ_ACT_GELU_TANH) return SVDQ_ERR_INVALID_ARG;
+  if (!x || !smooth_inv || !x_fp6 || !x_scales) return SVDQ_ERR_INVALID_ARG;
+  if (rank > 0 && (!lora_down || !lora_act)) return SVDQ_ERR_INVALID_ARG;
+  if (!aligned16(x) || !aligned16(smooth_inv) || !aligned16(x_fp6) || !aligned16(x_scales) ||
+      (rank > 0 && (!aligned16(lora_down) || !aligned16(lora_act))))
+    return SVDQ_ERR_INVALID_ARG;
+  const int64_t RB = (static_cast<int64_t>(M) + 31) / 32;
+  if (!fits_buffer(static_cast<int64_t>(K / SVDQ_GROUP) * RB, 1536) || !fits_buffer(M, 2LL * K))
+    return SVDQ_ERR_UNSUPPORTED_SHAPE;
+  const int st = current_device_check();
+  if (st != SVDQ_OK) return st;
+  if (M == 0) return SVDQ_OK;
+  return svdq::launch_quant_act_lora_down_fp6(x, smooth_inv, lora_down, M, K, rank, act, x_fp6, x_scales, lora_act,
+                                              stream);
+}
+
+extern "C" int svdq_gemm_w4a4_fp6_lora_up(const void* x_fp6, const void* x_scales, const void* w_fp6,
+                                          const void* w_scales, const float* lora_act, const void* lora_up,
+                                          const void* bias, int M, int N, int K, int rank, int group,
+                                          int out_dtype, void* y, void* stream) {
+  if (M < 0) return SVDQ_ERR_INVALID_ARG;
+  int st = svdq::validate_shape(K, N, rank, group);
+  if (st != SVDQ_OK) return st;
+  if (out_dtype != SVDQ_OUT_BF16 && out_dtype != SVDQ_OUT_F32) return SVDQ_ERR_INVALID_ARG;
+  if (!x_fp6 || !x_scales || !w_fp6 || !w_scales || !y) return SVDQ_ERR_INVALID_ARG;
+  if (rank > 0 && (!lora_act || !lora_up)) return SVDQ_ERR_INVALID_ARG;
+  if (!aligned16(x_fp6) || !aligned16(x_scales) || !aligned16(w_fp6) || !aligned16(w_scales) || !aligned16(y) ||
+      (bias && !aligned16(bias)) || (rank > 0 && (!aligned16(lora_act) || !aligned16(lora_up))))
+    return SVDQ_ERR_INVALID_ARG;
+  const int64_t G = K / SVDQ_GROUP;
+  const int64_t RBa = (static_cast<int64_t>(M) + 31) / 32, RBb = 4 * ((static_cast<int64_t>(N) + 127) / 128);
+  if (!fits_buffer(G * RBa, 1536) || !fits_buffer(G * RBb, 1536) || !fits_buffer(G, 64LL * RBa) ||
+      !fits_buffer(G, 2LL * N))
+    return SVDQ_ERR_UNSUPPORTED_SHAPE;
+  st = current_device_check();
+  if (st != SVDQ_OK) return st;
+  if (M == 0) return SVDQ_OK;
+  return svdq::launch_gemm_w4a4_fp6(x_fp6, x_scales, w_fp6, w_scales, lora_act, lora_up, bias, M, N, K, rank,
+                                    out_dtype, y, stream);
+}
+
 extern "C" int svdq_lora_down(const void* x, const float* smooth_inv, const void* lora_down, int M, int K,
                               int rank, int group, int act, float* lora_act, void* stream) {
   if (M < 0 || K <= 0 || rank <= 0 || rank > K || group <= 0) return SVDQ_ERR_INVALID_ARG;

@@ -1,0 +1,519 @@
+// INT4 layer on gfx950's 6-bit float matrix cores.
+//
+// The W4A4 product of the layer (svdq-int4-flux.1-depth-dev model card,
+// "Nunchaku Engine Design": 4-bit compute fused with the up projection) is a
+// sum of products of integer codes in [-8, 7].  Every such integer is a
+// value of the 6-bit float format E3M2 (sign, 3 exponent bits with bias 3,
+// 2 mantissa bits: 1 = 1.0 x 2^0, 5 = 1.25 x 2^2, 7 = 1.75 x 2^2,
+// 8 = 1.0 x 2^3), and gfx950's v_mfma_scale_f32_32x32x64_f8f6f4 multiplies
+// E3M2 operands exactly and accumulates their 64 products in fp32, where an
+// integer sum of magnitude <= 4096 is exact.  So the per-group integer
+// product P_g comes out of one 6-bit MFMA per 32 x 32 tile, bit for bit the
+// integer result, at the 6-bit rate (about 1.75 times the int8 rate per
+// 64-k group measured on MI355X).  The codes are the layer's INT4 codes; only
+// their container changes, from a nibble to a 6-bit field.
+//
+// Operand container ("fragment layout"), for a [rows][K] code matrix:
+//   buffer [K/64][RB][1536 bytes], one 1536-byte fragment per (group g,
+//   row block rb of 32 rows).  Lane l = r + 32 h of a fragment holds row r of
+//   the block and the 32 codes of k = 64 g + 32 h + j, j = 0..31, packed as
+//   a 192-bit little-endian string with code j at bits 6j .. 6j + 5 --
+//   exactly the MFMA operand of lane l.  Its dwords 0..3 sit at byte 16 l of
+//   the fragment and dwords 4..5 at byte 1024 + 8 l, so that a wave reads a
+//   fragment with one 16-byte and one 8-byte LDS read per lane, both
+//   conflict-free.
+//   Activations: row block rb holds rows 32 rb .. 32 rb + 31 (RB =
+//   ceil(M / 32); rows past M hold +0).  Weights: rows are grouped in panels
+//   of 128 output channels, and row block 4 p + t holds channels
+//   128 p + 4 r + t (r = 0..31), so that in kernel 2 a lane's four output
+//   columns of a wave tile are adjacent (RB = 4 ceil(N / 128); channels past
+//   N hold +0).
+//
+// Kernel 1 is k_quant_act_lora_down in its FP6 mode (svdq_kernels.hip): the
+//   nibble kernel's smoothing, quantizer, scales and down projection, with
+//   the codes written in the fragment layout.
+// Kernel 2 (k_gemm_w4a4_fp6, below): P_g on the 6-bit MFMA, per-group
+//   dequantization in fp32, bias and up projection in the same accumulators.
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "svdq.h"
+#include "svdq_internal.h"
+
+#include "svdq_device.h"
+
+namespace {
+
+constexpr int FRAG = 1536;
+
+// 32x32 MFMA layouts (wave64) used below:
+//   A operand: lane l holds row l % 32 and the k slice l / 32 (32 codes for
+//              the 6-bit MFMA with K = 64, 8 values for the bf16 MFMA with
+//              K = 16);
+//   B operand: lane l holds column l % 32 and the same k slice;
+//   C/D:       lane l holds column l % 32, rows 8 b + 4 (l / 32) + i in
+//              register 4 b + i (b, i = 0..3).
+// Checked on the device with random integer operands against a host sum.
+
+// =====================================================================
+// Kernel 2
+// =====================================================================
+// Output tile 256 (m) x 256 (n), 8 waves in a 4 (m) x 2 (n) grid, one block
+// per CU (two waves per SIMD); each wave owns 64 x 128 outputs = 2 x 4
+// tiles of 32 x 32.  The activation fragment is the MFMA A operand and the
+// weight fragment the B operand, so a lane holds one output column per tile
+// and 16 rows; with the weights' panel order the four tiles of a wave give a
+// lane the four adjacent columns n_w + 4 (l % 32) .. + 3.
+//
+// One group of 64 k is one 6-bit MFMA per tile (C = 0), giving P_g exactly
+// in fp32.  Dequantization: t = P_g s_x (exact: 13 x 11 significant bits)
+// and acc = fma(t, s_w, acc), one rounding per group -- the same two fp32
+// operations per output and group as the int8 kernel, without its
+// magic-constant conversion.
+//
+// Persistent grid: one block per CU walks the output tiles t = blockIdx.x,
+// blockIdx.x + gridDim.x, ... as one continuous sequence of stages.  A
+// tile's stages are its K / 64 groups, then one stage per 16 ranks of the
+// low-rank branch (at least four stages per tile; empty ones pad).  Every
+// stage moves 24 KB from HBM into a ring of F_NS LDS slots by LDS-DMA
+// buffer loads, issued F_NS - 1 stages ahead, three 1 KB loads per wave:
+//   group stage:     the tile's 8 activation and 8 weight fragments of the
+//                    group (contiguous 12 KB runs in the fragment layout);
+//   low-rank stage:  lora_act [256 rows][16 ranks] fp32 and lora_up
+//                    [256 columns][16 ranks] bf16, added into the same
+//                    accumulators on bf16 MFMA;
+// plus one 256-byte load per wave that carries the next stage's raw fp16
+// scales (waves 0-1 activation, 2-3 weight) and the stage's tile's bias
+// (waves 4-5; 6-7 duplicate it).  So at the top of stage s only stage s's loads must
+// have landed; the barrier publishes them and the fp32 scales converted
+// during stage s - 1, and frees the slot of stage s - 1 for stage s + 4.
+// After a tile's last stage the wave adds the bias, rounds, and stores its
+// 64 x 128 outputs with buffer stores (32 per lane; rows past M and columns
+// past N fall outside the buffer and are dropped), then starts the next
+// tile, whose first stages are already loading: the store overlaps them.
+// Stores count in the same vmcnt as the loads, so the wait at a stage adds
+// 32 to its count when a tile ended within the last four stages (at most
+// one can, with four or more stages per tile).
+constexpr int F_BM = 256;
+constexpr int F_BN = 256;
+constexpr int F_WAVES = 8;
+constexpr int F_THREADS = F_WAVES * 64;
+constexpr int F_NS = 5;                               // ring slots, one stage each
+constexpr int F_A = 8 * FRAG;                         // 12288: activation fragments of a stage
+constexpr int F_OPS = 24 * 1024;                      // operand bytes of a stage
+constexpr int F_SC = F_OPS;                           // raw fp16 scales of the next stage: x [256], w [256]
+constexpr int F_BIAS = F_SC + 1024;                   // the tile's bias [256] bf16 (+512 B duplicate)
+constexpr int F_SLOT = F_BIAS + 1024;
+constexpr int F_LA = 0;                               // low-rank stage: lora_act [256][16] fp32 (64 B rows)
+constexpr int F_LU = 16384;                           //                 lora_up [256][16] bf16 (32 B rows)
+constexpr int F_DMA = 4;                              // DMA loads per wave per stage
+constexpr int F_STORES = 32;                          // buffer stores per lane at a tile's end
+constexpr int F_MIN_STAGES = 4;
+constexpr int F_MAX_TILES = 512;                      // tiles per block (host: grid >= tiles / 512)
+static_assert(F_OPS / 1024 == 3 * F_WAVES, "three 1 KB operand loads per wave per stage");
+static_assert(F_LU + 256 * 32 == F_OPS, "a low-rank stage fills the operand area");
+static_assert(F_SLOT % 16 == 0, "slots stay 16-byte aligned");
+static_assert(F_NS == F_MIN_STAGES + 1, "stages s .. s + 4 are live at once");
+static_assert(F_DMA * (F_NS - 2) + F_STORES <= 63, "wait counts fit vmcnt");
+
+// Output tile of tile index t: the XCD-aware order of xcd_tile, applied to t
+// (the block that runs tile t sits on XCD t % 8, as t = blockIdx.x + j *
+// gridDim.x with gridDim.x a multiple of 8).
+__device__ __forceinline__ void tile_of(int t, int nM, int nN, int& tm, int& tn) {
+  const int nb = nM * nN;
+  int u = t;
+  if ((nb & 7) == 0) u = (t & 7) * (nb >> 3) + (t >> 3);
+  constexpr int GM = 4;
+  const int per = GM * nN;
+  const int grp = u / per;
+  const int first = grp * GM;
+  const int gm = min(GM, nM - first);
+  const int r = u - grp * per;
+  tm = first + r % gm;
+  tn = r / gm;
+}
+
+template <int OUT_F32>
+__global__ __launch_bounds__(F_THREADS, 1) void k_gemm_w4a4_fp6(
+    const uint8_t* __restrict__ x_fp6, const _Float16* __restrict__ x_scales,
+    const uint8_t* __restrict__ w_fp6, const _Float16* __restrict__ w_scales,
+    const float* __restrict__ lora_act, const uint16_t* __restrict__ lora_up,
+    const uint16_t* __restrict__ bias, int M, int N, int K, int rank, void* __restrict__ y) {
+  __shared__ __align__(16) unsigned char ring[F_NS][F_SLOT];
+  __shared__ __align__(16) float conv[2][F_BM + F_BN];   // fp32 scales: x [256] | w [256]
+  __shared__ int tiles[F_MAX_TILES];                      // this block's tiles: tm << 16 | tn
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int wm = wave & 3, wn = wave >> 2;
+  const int c = lane & 31, h = lane >> 5;
+  const int nM = (M + F_BM - 1) / F_BM, nN = (N + F_BN - 1) / F_BN;
+  const int ntiles = nM * nN;
+  const int G = K / GROUP;
+  const int NR = rank / 16;
+  const int SPT = max(G + NR, F_MIN_STAGES);                 // stages per tile
+  const int my_tiles = (ntiles - static_cast<int>(blockIdx.x) + static_cast<int>(gridDim.x) - 1) /
+                       static_cast<int>(gridDim.x);
+  const int S = my_tiles * SPT;
+  const int RBa = (M + 31) / 32;
+  const int Mp = 32 * RBa;
+  const int RBb = 4 * ((N + 127) / 128);
+  constexpr uint32_t OOB = 0x80000000u;
+  constexpr int ELEM = OUT_F32 ? 4 : 2;
+
+  // Buffer resources: each wave moves one operand in group stages
+  // (activations for waves 0-3, weights for 4-7) and one auxiliary array
+  // (activation scales for waves 0-1, weight scales for 2-3, bias for 4-7).
+  const bool opA = wave < 4;
+  const DmaRsrc op_rs = dma_rsrc(opA ? static_cast<const void*>(x_fp6) : static_cast<const void*>(w_fp6),
+                                 static_cast<uint32_t>(static_cast<size_t>(G) * (opA ? RBa : RBb) * FRAG));
+  const DmaRsrc aux_rs =
+      wave < 2 ? dma_rsrc(x_scales, static_cast<uint32_t>(static_cast<size_t>(G) * Mp * 2))
+               : (wave < 4 ? dma_rsrc(w_scales, static_cast<uint32_t>(static_cast<size_t>(G) * N * 2))
+                           : dma_rsrc(bias, bias ? static_cast<uint32_t>(N) * 2u : 0u));
+  const DmaRsrc la_rs = dma_rsrc(lora_act, static_cast<uint32_t>(static_cast<size_t>(M) * rank * 4));
+  const DmaRsrc lu_rs = dma_rsrc(lora_up, static_cast<uint32_t>(static_cast<size_t>(N) * rank * 2));
+  const uint32_t y_bytes = static_cast<uint32_t>(static_cast<size_t>(M) * N * ELEM);
+  const __amdgpu_buffer_rsrc_t y_rs = __builtin_amdgcn_make_buffer_rsrc(y, 0, static_cast<int>(y_bytes), 0x00020000);
+
+  const uint32_t ring0 = static_cast<uint32_t>(reinterpret_cast<uintptr_t>(&ring[0][0]));
+
+  // The block's tiles, t = blockIdx.x + j gridDim.x, in LDS (read at tile
+  // changes, not recomputed in the loop).
+  for (int j = tid; j < my_tiles; j += F_THREADS) {
+    int tm, tn;
+    tile_of(static_cast<int>(blockIdx.x) + j * static_cast<int>(gridDim.x), nM, nN, tm, tn);
+    tiles[j] = (tm << 16) | tn;
+  }
+  __syncthreads();
+  auto tile_at = [&](int j) { return __builtin_amdgcn_readfirstlane(tiles[j < my_tiles ? j : 0]); };
+
+  // DMA roles (wave-uniform).  In a group stage waves 0-3 move the 12 KB of
+  // activation fragments and waves 4-7 the 12 KB of weight fragments, three
+  // 1 KB runs each (run r of the operand: bytes 1024 r .. + 1023 of its
+  // contiguous 12 KB); in a low-rank stage runs 0..15 of the 24 are
+  // lora_act (16 rows of 64 bytes each) and 16..23 lora_up (32 rows of 32
+  // bytes).  The fourth load: waves 0-1 the activation scales and 2-3 the
+  // weight scales of the stage after the issued one, waves 4-7 the issued
+  // stage's bias (two 256-byte halves, duplicated).
+  const uint32_t op_run0 = 1024u * static_cast<uint32_t>(opA ? 3 * wave : 3 * wave - 12);
+  const uint32_t op_gstride = static_cast<uint32_t>(opA ? RBa : RBb) * FRAG;
+  const uint32_t op_lds = __builtin_amdgcn_readfirstlane(ring0 + 1024 * 3 * wave);
+  const uint32_t aux_lds = __builtin_amdgcn_readfirstlane(ring0 + F_SC + 256 * (wave < 4 ? wave : 4 + (wave & 1)));
+  const uint32_t aux_part = 256u * (wave & 1);
+  // The lane index, recomputed where it is used outside the group section
+  // (an empty asm hides that it is loop-invariant), so that the compiler
+  // does not keep every per-lane offset of the DMA, low-rank and store
+  // paths in registers across the loop.
+  auto fresh_lane = [&]() {
+    int l = lane;
+    asm volatile("" : "+v"(l));
+    return l;
+  };
+  const uint32_t lane16 = 16u * lane;
+
+  // Issue cursor: the stage being issued is stage li of tile ji (tile
+  // coordinates ti; tn_ of the following tile), slot si.
+  int ji = 0, li = 0, si = 0;
+  int ti = tile_at(0), tnx = tile_at(1);
+  auto issue = [&]() {
+    const uint32_t so = static_cast<uint32_t>(si) * F_SLOT;
+    const bool live = ji < my_tiles;
+    // per-lane parts of the addresses (the rest is wave-uniform); rows past
+    // M or N lie past the end of their buffer and read as zero
+    const int ln = fresh_lane();
+    const uint32_t l16 = 16u * ln, l4 = 4u * ln;
+    const int tmi = ti >> 16, tni = ti & 0xFFFF;
+    if (li < G || !live) {
+      const uint32_t base = __builtin_amdgcn_readfirstlane(
+          live ? 8u * FRAG * static_cast<uint32_t>(opA ? tmi : tni) + static_cast<uint32_t>(li) * op_gstride + op_run0
+               : OOB);
+#pragma unroll
+      for (int i = 0; i < 3; ++i)
+        dma16(op_rs, __builtin_amdgcn_readfirstlane(op_lds + 1024 * i + so), base + 1024u * i + l16);
+    } else {
+      const int ch = li - G;                                   // rank chunk; >= NR: padding stage
+#pragma unroll
+      for (int i = 0; i < 3; ++i) {
+        const int q = 3 * wave + i;
+        const bool isla = q < 16;
+        const int row0 = isla ? F_BM * tmi + 16 * q : F_BN * tni + 32 * (q - 16);
+        const uint32_t base = __builtin_amdgcn_readfirstlane(
+            ch < NR ? (static_cast<uint32_t>(row0) * rank + 16u * ch) * (isla ? 4u : 2u) : OOB);
+        if (isla)
+          dma16(la_rs, __builtin_amdgcn_readfirstlane(op_lds + 1024 * i + so),
+                base + static_cast<uint32_t>(ln >> 2) * static_cast<uint32_t>(rank * 4) + 16u * (ln & 3));
+        else
+          dma16(lu_rs, __builtin_amdgcn_readfirstlane(op_lds + 1024 * i + so),
+                base + static_cast<uint32_t>(ln >> 1) * static_cast<uint32_t>(rank * 2) + 16u * (ln & 1));
+      }
+    }
+    uint32_t abase;
+    if (wave < 4) {
+      // scales of the following stage: group li + 1 of this tile, or group 0
+      // of the next tile
+      const bool isx = wave < 2;
+      const int lnext = li + 1;
+      const bool same = lnext < G, nxt = lnext == SPT && ji + 1 < my_tiles;
+      const int tile = same ? ti : tnx;
+      const uint32_t lim = isx ? 2u * Mp : 2u * N;
+      const uint32_t b0 = isx ? 2u * F_BM * static_cast<uint32_t>(tile >> 16) : 2u * F_BN * static_cast<uint32_t>(tile & 0xFFFF);
+      abase = live && (same || nxt) ? (same ? static_cast<uint32_t>(lnext) * lim : 0u) + b0 + aux_part : OOB;
+    } else {
+      abase = live && bias != nullptr ? 2u * F_BN * static_cast<uint32_t>(tni) + aux_part : OOB;
+    }
+    dma4(aux_rs, __builtin_amdgcn_readfirstlane(aux_lds + so), __builtin_amdgcn_readfirstlane(abase) + l4);
+    // advance
+    si = si == F_NS - 1 ? 0 : si + 1;
+    if (++li == SPT) {
+      li = 0;
+      ++ji;
+      ti = tnx;
+      tnx = tile_at(ji + 1);
+    }
+  };
+  // Thread t converts activation scale t (t < 256) or weight scale t - 256
+  // of the raw scales in slot `slot` to fp32.  No bounds: rows M .. Mp - 1
+  // hold zero scales; rows and columns past the operands read other groups'
+  // scales or zeros, and their outputs are never stored.
+  auto convert_scales = [&](int slot, int buf) {
+    int t = tid;
+    asm volatile("" : "+v"(t));
+    const _Float16* raw = reinterpret_cast<const _Float16*>(&ring[slot][F_SC]);
+    conv[buf][t] = static_cast<float>(raw[t]);
+  };
+
+  v16f acc[2][4];
+#pragma unroll
+  for (int a = 0; a < 2; ++a)
+#pragma unroll
+    for (int t = 0; t < 4; ++t)
+#pragma unroll
+      for (int e = 0; e < 16; ++e) acc[a][t][e] = 0.f;
+
+  // per-lane LDS byte offsets in a slot
+  const uint32_t a_off = (2 * wm) * FRAG + lane16;             // + a * FRAG; dwords 4-5 at + 1024 - 8 lane
+  const uint32_t b_off = F_A + (4 * wn) * FRAG + lane16;
+  const v16f zero = {};
+
+  // Stage 0's scales into slot F_NS - 1's scale area (free until stage
+  // F_NS - 1 is issued): the issue path's scale load with the cursor one
+  // stage back; then stages 0 .. F_NS - 2.
+  {
+    const bool isx = wave < 2;
+    const uint32_t b0 = isx ? 2u * F_BM * static_cast<uint32_t>(ti >> 16) : 2u * F_BN * static_cast<uint32_t>(ti & 0xFFFF);
+    const uint32_t abase = wave < 4 ? b0 + aux_part : OOB;
+    dma4(aux_rs, __builtin_amdgcn_readfirstlane(aux_lds + (F_NS - 1) * F_SLOT),
+         __builtin_amdgcn_readfirstlane(abase) + 4u * lane);
+  }
+#pragma unroll
+  for (int k = 0; k < F_NS - 1; ++k) issue();
+  __builtin_amdgcn_s_waitcnt(waitcnt_vm_lgkm0(F_DMA * (F_NS - 2)));   // stage 0's scales and stage 0
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+  convert_scales(F_NS - 1, 0);
+
+  int s = 0;                 // stage index in the block's sequence
+  int sc = 0;                // its slot
+  int since_end = 8;         // stages since the last tile end (its stores outstanding if < 4)
+  // Top of stage s: its loads landed (stages s + 1 .. s + 3 may be in flight,
+  // and the stores of a tile that ended in the last four stages); the
+  // barrier publishes them; then stage s + 4 is issued and stage s + 1's
+  // scales converted.
+  auto stage_top = [&]() {
+    if (since_end < 4) __builtin_amdgcn_s_waitcnt(waitcnt_vm(F_DMA * (F_NS - 2) + F_STORES));
+    else __builtin_amdgcn_s_waitcnt(waitcnt_vm(F_DMA * (F_NS - 2)));
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
+    issue();
+    convert_scales(sc, (s + 1) & 1);
+  };
+  auto stage_end = [&]() {
+    ++s;
+    sc = sc == F_NS - 1 ? 0 : sc + 1;
+    ++since_end;
+  };
+
+  for (int j = 0; j < my_tiles; ++j) {
+    const int tt = __builtin_amdgcn_readfirstlane(tiles[j]);
+    const int mw = F_BM * (tt >> 16) + 64 * wm, cw = F_BN * (tt & 0xFFFF) + 128 * wn;   // wave-uniform
+
+    // ---- the tile's groups: P_g on the 6-bit MFMA, then dequantization ----
+    for (int l = 0; l < G; ++l, stage_end()) {
+      stage_top();
+      const unsigned char* sl = ring[sc];
+      const float* cv = conv[s & 1];
+      const float4 sw = *reinterpret_cast<const float4*>(cv + F_BM + 128 * wn + 4 * c);
+      const float swv[4] = {sw.x, sw.y, sw.z, sw.w};
+      auto rd_frag = [&](uint32_t off) {
+        const uint4 lo = *reinterpret_cast<const uint4*>(sl + off);
+        const uint2 hi = *reinterpret_cast<const uint2*>(sl + off + 1024 - 8 * lane);
+        return v8i{static_cast<int>(lo.x), static_cast<int>(lo.y), static_cast<int>(lo.z), static_cast<int>(lo.w),
+                   static_cast<int>(hi.x), static_cast<int>(hi.y), 0, 0};
+      };
+      // Tiles in the order (n tile 0, m tile 0), (0, 1), (1, 0), ...: a
+      // weight fragment serves two consecutive tiles and is read one tile
+      // pair ahead; a tile's row scales are read from LDS four at a time as
+      // it is dequantized (two distinct addresses per read: broadcast).  The
+      // MFMA of tile u + 1 is issued before tile u is dequantized (results
+      // in a ring of two).
+      const float* sxp = cv + 64 * wm + 4 * h;
+      v8i afr[2];
+      afr[0] = rd_frag(a_off);
+      afr[1] = rd_frag(a_off + FRAG);
+      v8i bfr[4];
+      bfr[0] = rd_frag(b_off);
+      v16f dr[2];
+#pragma unroll
+      for (int u = 0; u < 9; ++u) {
+        if (u < 8) {
+          const int t = u >> 1, a = u & 1;
+          if (a == 0 && t < 3) bfr[t + 1] = rd_frag(b_off + (t + 1) * FRAG);
+          // cbsz = blgp = 3: both operands E3M2; E8M0 scales 127 (= 1)
+          dr[u & 1] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(afr[a], bfr[t], zero, 3, 3, 0, 127, 0, 127);
+        }
+        if (u > 0) {
+          const int v = u - 1, t = v >> 1, a = v & 1;
+#pragma unroll
+          for (int b = 0; b < 4; ++b) {
+            const float4 s4 = *reinterpret_cast<const float4*>(sxp + 32 * a + 8 * b);
+            const float sv[4] = {s4.x, s4.y, s4.z, s4.w};
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+              const int e = 4 * b + i;
+              acc[a][t][e] = __builtin_fmaf(dr[v & 1][e] * sv[i], swv[t], acc[a][t][e]);
+            }
+          }
+        }
+      }
+    }
+
+    // ---- the up projection, 16 ranks per stage; padding stages ----
+    for (int l = G; l < SPT; ++l, stage_end()) {
+      stage_top();
+      const unsigned char* sl = ring[sc];
+      if (l < G + NR) {
+        // A = bf16(lora_act) rows (lane row l % 32 of m tile a, ranks
+        // 8h .. 8h + 7 of the chunk), B = lora_up rows (columns
+        // n_w + 4 (l % 32) + t, the same ranks); products into a ring of
+        // two, added like the group results (the accumulators stay single
+        // registers for the dequantization FMAs)
+        const int ln = fresh_lane();
+        const int lc = ln & 31, lh = ln >> 5;
+        v8bf la[2], lu[4];
+#pragma unroll
+        for (int a = 0; a < 2; ++a) {
+          const float4* p = reinterpret_cast<const float4*>(sl + F_LA + (64 * wm + 32 * a + lc) * 64 + 32 * lh);
+          const float4 v0 = p[0], v1 = p[1];
+          const float v[8] = {v0.x, v0.y, v0.z, v0.w, v1.x, v1.y, v1.z, v1.w};
+          la[a] = pack_bf16x8(v);
+        }
+#pragma unroll
+        for (int t = 0; t < 4; ++t)
+          lu[t] = __builtin_bit_cast(v8bf, *reinterpret_cast<const uint4*>(sl + F_LU + (128 * wn + 4 * lc + t) * 32 + 16 * lh));
+        v16f dr[2];
+#pragma unroll
+        for (int u = 0; u < 9; ++u) {
+          if (u < 8) dr[u & 1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(la[u >> 2], lu[u & 3], zero, 0, 0, 0);
+          if (u > 0) {
+            const int v = u - 1;
+#pragma unroll
+            for (int e = 0; e < 16; ++e) acc[v >> 2][v & 3][e] += dr[v & 1][e];
+          }
+        }
+      }
+    }
+
+    // ---- end of the tile, after its last stage ----
+    {
+      // The stage's slot still holds the tile's bias (every stage carries
+      // its tile's bias; slot (s - 1) % F_NS is reused only after the next
+      // barrier).
+      const unsigned char* sl = ring[sc == 0 ? F_NS - 1 : sc - 1];
+      // end of the tile: bias, rounding, store.  The lane holds rows
+      // mw + 32 a + 8 b + 4 h + i and columns cw + 4 c .. + 3; rows past M
+      // fall past the end of y, columns past N (N % 8 == 0: a lane's four
+      // are all in or all out) are sent past it.
+      const int ln = fresh_lane();
+      const int lc = ln & 31, lh = ln >> 5;
+      const uint2 bu = *reinterpret_cast<const uint2*>(sl + F_BIAS + 2 * (128 * wn + 4 * lc));
+      const float bv[4] = {bf16_bits_to_f32(bu.x & 0xFFFFu), bf16_bits_to_f32(bu.x >> 16),
+                           bf16_bits_to_f32(bu.y & 0xFFFFu), bf16_bits_to_f32(bu.y >> 16)};
+      // one per-lane base (row mw + 4 h, columns cw + 4 c); each store adds
+      // its wave-uniform row offset.  A base past the end stays past it
+      // (y is under 2 GiB, the added offsets under 32 rows).
+      const uint32_t vbase = 4 * lc < N - cw
+                                 ? ((static_cast<uint32_t>(mw) + 4u * lh) * static_cast<uint32_t>(N) +
+                                    static_cast<uint32_t>(cw) + 4u * lc) * ELEM
+                                 : OOB;
+#pragma unroll
+      for (int a = 0; a < 2; ++a)
+#pragma unroll
+        for (int b = 0; b < 4; ++b)
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            const int e = 4 * b + i;
+            const uint32_t off = vbase + static_cast<uint32_t>(32 * a + 8 * b + i) * static_cast<uint32_t>(N) * ELEM;
+            if (OUT_F32) {
+              const v4f o = v4f{acc[a][0][e] + bv[0], acc[a][1][e] + bv[1], acc[a][2][e] + bv[2],
+                                acc[a][3][e] + bv[3]};
+              __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(v4i, o), y_rs, off, 0, 0);
+            } else {
+              typedef int v2i_ __attribute__((ext_vector_type(2)));
+              const v2i_ o = v2i_{static_cast<int>(bf16x2_bits(acc[a][0][e] + bv[0], acc[a][1][e] + bv[1])),
+                                  static_cast<int>(bf16x2_bits(acc[a][2][e] + bv[2], acc[a][3][e] + bv[3]))};
+              __builtin_amdgcn_raw_buffer_store_b64(o, y_rs, off, 0, 0);
+            }
+          }
+#pragma unroll
+      for (int a = 0; a < 2; ++a)
+#pragma unroll
+        for (int t = 0; t < 4; ++t)
+#pragma unroll
+          for (int e = 0; e < 16; ++e) acc[a][t][e] = 0.f;
+      since_end = 0;
+    }
+  }
+  // drain the padding loads issued past the last stage (and the stores)
+  __builtin_amdgcn_s_waitcnt(waitcnt_vm_lgkm0(0));
+}
+
+int cu_count() {
+  static int cached[64] = {};
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
+  if (cached[dev] == 0) {
+    int n = 0;
+    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0) n = 256;
+    cached[dev] = n;
+  }
+  return cached[dev];
+}
+
+}  // namespace
+
+namespace svdq {
+
+int launch_gemm_w4a4_fp6(const void* x_fp6, const void* x_scales, const void* w_fp6, const void* w_scales,
+                         const float* lora_act, const void* lora_up, const void* bias, int M, int N, int K, int rank,
+                         int out_dtype, void* y, void* stream) {
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  const int tiles = ((M + F_BM - 1) / F_BM) * ((N + F_BN - 1) / F_BN);
+  // one block per CU, a multiple of 8 (the XCD count) so that a block's
+  // tiles stay on its XCD; never more blocks than tiles
+  const int cus = cu_count() & ~7;
+  const int grid = tiles < cus ? tiles : (cus > 0 ? cus : tiles);
+#define SVDQ_K2F(OF)                                                                                          \
+  hipLaunchKernelGGL((k_gemm_w4a4_fp6<OF>), dim3(grid), dim3(F_THREADS), 0, st,                               \
+                     static_cast<const uint8_t*>(x_fp6), static_cast<const _Float16*>(x_scales),              \
+                     static_cast<const uint8_t*>(w_fp6), static_cast<const _Float16*>(w_scales), lora_act,    \
+                     static_cast<const uint16_t*>(lora_up), static_cast<const uint16_t*>(bias), M, N, K, rank, y)
+  if (out_dtype == SVDQ_OUT_F32) SVDQ_K2F(1);
+  else SVDQ_K2F(0);
+#undef SVDQ_K2F
+  return hipGetLastError() == hipSuccess ? SVDQ_OK : SVDQ_ERR_HIP;
+}
+
+}  // namespace svdq

@@ -1,5 +1,6 @@
 // Internal declarations shared by the library's translation units.
 #pragma once
+#include <cstddef>
 #include <cstdint>
 
 namespace svdq {
@@ -40,6 +41,13 @@ int launch_awq_quant_act(const void* x, const float* inv_scale, int M, int K, vo
                          void* stream);
 int launch_awq_gemv(const void* x_hat, const float* xsum, const void* w_codes, const void* w_scales,
                     const void* w_zeros, const void* bias, int M, int N, int K, void* y, void* stream);
+
+// svdq_fp6_kernels.hip (kernel 1's FP6 mode is in svdq_kernels.hip)
+int launch_quant_act_lora_down_fp6(const void* x, const float* smooth_inv, const void* lora_down, int M, int K,
+                                   int rank, int act, void* x_fp6, void* x_scales, float* lora_act, void* stream);
+int launch_gemm_w4a4_fp6(const void* x_fp6, const void* x_scales, const void* w_fp6, const void* w_scales,
+                         const float* lora_act, const void* lora_up, const void* bias, int M, int N, int K, int rank,
+                         int out_dtype, void* y, void* stream);
 
 // svdq_probes.hip
 int launch_probe_mfma(int kind, int blocks, int iters, void* sink, void* stream);

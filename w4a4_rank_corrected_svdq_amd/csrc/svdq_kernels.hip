@@ -32,9 +32,11 @@ namespace {
 // =====================================================================
 // Kernel 1
 // =====================================================================
-// QM selects the quantizer: INT4 (group 64, fp16 scale), MXFP4 (E2M1
-// elements, E8M0 scale per 32) or none, which leaves only the down
-// projection (the unfused reference path, which reads X a second time).
+// QM selects the quantizer: INT4 (group 64, fp16 scale), the same INT4
+// codes written as E3M2 values in the 6-bit MFMA fragment layout (FP6; see
+// svdq_fp6_kernels.hip), MXFP4 (E2M1 elements, E8M0 scale per 32) or none,
+// which leaves only the down projection (the unfused reference path, which
+// reads X a second time).
 //
 // Block: 16 token rows (32 when the 16-row blocks would outnumber the CUs,
 // below), 16 waves (8 for ranks above 64, and for a grid larger than the CU
@@ -55,7 +57,7 @@ constexpr int K1_MAX_WAVES = 16;
 // registers.
 template <int NT> constexpr int k1_waves() { return NT <= 4 ? 16 : 8; }
 
-enum { Q_NONE = 0, Q_INT4 = 1, Q_MXFP4 = 2 };
+enum { Q_NONE = 0, Q_INT4 = 1, Q_MXFP4 = 2, Q_FP6 = 3 };
 
 template <int ACT, int NT, int QM, int RT>
 __global__ __launch_bounds__(k1_waves<NT>() * 64) void k_quant_act_lora_down(
@@ -134,7 +136,7 @@ __global__ __launch_bounds__(k1_waves<NT>() * 64) void k_quant_act_lora_down(
           xh[2 * i] = lo * sv[2 * i];
           xh[2 * i + 1] = hi * sv[2 * i + 1];
         }
-        if constexpr (QM == Q_INT4) {
+        if constexpr (QM == Q_INT4 || QM == Q_FP6) {
           _Float16* x_scales = static_cast<_Float16*>(x_scales_v);
           float amax = 0.f;
 #pragma unroll
@@ -145,18 +147,53 @@ __global__ __launch_bounds__(k1_waves<NT>() * 64) void k_quant_act_lora_down(
           const _Float16 sh = static_cast<_Float16>(s32);
           const float sf = static_cast<float>(sh);
           const float rcp = (sf == 0.f) ? 0.f : 1.0f / sf;
-          uint32_t p0 = 0, p1 = 0;
+          if constexpr (QM == Q_INT4) {
+            uint32_t p0 = 0, p1 = 0;
 #pragma unroll
-          for (int i = 0; i < 8; ++i) {
-            const float q0 = fminf(fmaxf(rintf(xh[i] * rcp), -8.f), 7.f);
-            const float q1 = fminf(fmaxf(rintf(xh[8 + i] * rcp), -8.f), 7.f);
-            p0 |= (static_cast<uint32_t>(static_cast<int>(q0)) & 0xFu) << (4 * i);
-            p1 |= (static_cast<uint32_t>(static_cast<int>(q1)) & 0xFu) << (4 * i);
-          }
-          if (row_ok[rt]) {
-            *reinterpret_cast<uint2*>(x_codes + static_cast<size_t>(row[rt]) * (K / 2) + (k0 >> 1)) =
-                make_uint2(p0, p1);
-            if (lane < 16) x_scales[static_cast<size_t>(g) * M + row[rt]] = sh;
+            for (int i = 0; i < 8; ++i) {
+              const float q0 = fminf(fmaxf(rintf(xh[i] * rcp), -8.f), 7.f);
+              const float q1 = fminf(fmaxf(rintf(xh[8 + i] * rcp), -8.f), 7.f);
+              p0 |= (static_cast<uint32_t>(static_cast<int>(q0)) & 0xFu) << (4 * i);
+              p1 |= (static_cast<uint32_t>(static_cast<int>(q1)) & 0xFu) << (4 * i);
+            }
+            if (row_ok[rt]) {
+              *reinterpret_cast<uint2*>(x_codes + static_cast<size_t>(row[rt]) * (K / 2) + (k0 >> 1)) =
+                  make_uint2(p0, p1);
+              if (lane < 16) x_scales[static_cast<size_t>(g) * M + row[rt]] = sh;
+            }
+          } else {
+            // The lane's 16 codes are codes 16 (q % 2) .. + 15 of fragment
+            // lane (row % 32) + 32 (q / 2), q = lane / 16: 96 bits, dwords
+            // 0..2 or 3..5 of that lane's string.  The packed conversion
+            // puts its first source in the even positions and its second in
+            // the odd ones; positions 16..31 are zeros (dwords 3..5 unused).
+            // Rows M .. Mp - 1 of the padded last row block are written as
+            // zeros (codes +0, scale 0).
+            const int RB = (M + 31) >> 5, Mp = RB << 5;
+            typedef float v16f_ __attribute__((ext_vector_type(16)));
+            v16f_ ev, od;
+#pragma unroll
+            for (int i = 0; i < 8; ++i) {
+              // + 0.0f turns -0 into +0 (the codes are integers)
+              ev[i] = fminf(fmaxf(rintf(xh[2 * i] * rcp), -8.f), 7.f) + 0.0f;
+              od[i] = fminf(fmaxf(rintf(xh[2 * i + 1] * rcp), -8.f), 7.f) + 0.0f;
+              ev[8 + i] = 0.f;
+              od[8 + i] = 0.f;
+            }
+            typedef int v6i_ __attribute__((ext_vector_type(6)));
+            const v6i_ pk = __builtin_amdgcn_cvt_scalef32_2xpk16_bf6_f32(ev, od, 1.0f);
+            if (row[rt] < Mp) {
+              const int qq = lane >> 4;
+              const int fl = (row[rt] & 31) + 32 * (qq >> 1);
+              uint8_t* fr = x_codes + (static_cast<size_t>(g) * RB + (row[rt] >> 5)) * 1536;
+              if ((qq & 1) == 0) {
+                *reinterpret_cast<uint3*>(fr + 16 * fl) = make_uint3(pk[0], pk[1], pk[2]);
+              } else {
+                *reinterpret_cast<uint32_t*>(fr + 16 * fl + 12) = static_cast<uint32_t>(pk[0]);
+                *reinterpret_cast<uint2*>(fr + 1024 + 8 * fl) = make_uint2(pk[1], pk[2]);
+              }
+              if (lane < 16) x_scales[static_cast<size_t>(g) * Mp + row[rt]] = sh;
+            }
           }
         } else if constexpr (QM == Q_MXFP4) {
           // MXFP4: blocks of 32 k are the lane pairs (l, l ^ 16).  Scale
@@ -1259,7 +1296,8 @@ void launch_k1_kernel(const void* x, const float* smooth_inv, const void* lora_d
                               static_cast<int>(smem));
   // Grids larger than the CU count run 8-wave blocks, two per CU, instead of
   // a second round of 16-wave blocks.
-  const int blocks = (M + K1_ROWS * RT - 1) / (K1_ROWS * RT);
+  const int rows = QM == Q_FP6 ? 32 * ((M + 31) / 32) : M;   // FP6: the padded last row block too
+  const int blocks = (rows + K1_ROWS * RT - 1) / (K1_ROWS * RT);
   const int waves = (k1_waves<NT>() == 16 && blocks > device_cu_count()) ? 8 : k1_waves<NT>();
   hipLaunchKernelGGL(kern, dim3(blocks), dim3(waves * 64), smem, st,
                      static_cast<const uint16_t*>(x), smooth_inv, static_cast<const uint16_t*>(lora_down), M, K,
@@ -1451,6 +1489,14 @@ int launch_quant_act_lora_down_mxfp4(const void* x, const float* smooth_inv, con
   if (act == SVDQ_ACT_GELU_TANH)
     return launch_k1<SVDQ_ACT_GELU_TANH, Q_MXFP4>(x, smooth_inv, lora_down, M, K, rank, x_codes, x_scales, lora_act, st);
   return launch_k1<SVDQ_ACT_NONE, Q_MXFP4>(x, smooth_inv, lora_down, M, K, rank, x_codes, x_scales, lora_act, st);
+}
+
+int launch_quant_act_lora_down_fp6(const void* x, const float* smooth_inv, const void* lora_down, int M, int K,
+                                   int rank, int act, void* x_fp6, void* x_scales, float* lora_act, void* stream) {
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  if (act == SVDQ_ACT_GELU_TANH)
+    return launch_k1<SVDQ_ACT_GELU_TANH, Q_FP6>(x, smooth_inv, lora_down, M, K, rank, x_fp6, x_scales, lora_act, st);
+  return launch_k1<SVDQ_ACT_NONE, Q_FP6>(x, smooth_inv, lora_down, M, K, rank, x_fp6, x_scales, lora_act, st);
 }
 
 int launch_lora_down(const void* x, const float* smooth_inv, const void* lora_down, int M, int K, int rank,

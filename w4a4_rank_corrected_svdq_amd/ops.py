@@ -17,7 +17,8 @@ from . import _lib as L
 __all__ = ["prepare_weights", "quant_act_lora_down", "gemm_w4a4_lora_up", "prepared_bytes",
            "device_check", "lora_down", "lora_up_add", "prepared_bytes_mxfp4", "prepare_weights_mxfp4",
            "quant_act_lora_down_mxfp4", "gemm_mxfp4_lora_up", "gemm_w4a4_lora_up_qkv", "awq_prepare",
-           "awq_quant_act", "awq_gemv"]
+           "awq_quant_act", "awq_gemv", "fp6_operand_bytes", "pack_fp6_operand",
+           "quant_act_lora_down_fp6", "gemm_w4a4_fp6_lora_up"]
 
 
 def _ptr(t) -> Optional[int]:
@@ -157,6 +158,77 @@ def gemm_w4a4_lora_up(x_codes, x_scales, w_codes, w_scales, lora_act, lora_up, b
         _dev_arg("bias", bias, torch.bfloat16, (N,), dev),
         M, N, K, rank, group, out_dtype, _dev_arg("y", out, dt, (M, N), dev), _stream(dev))
     L.check(st, "svdq_gemm_w4a4_lora_up")
+    return out
+
+
+# ------------------------------------------------- INT4 codes on the 6-bit MFMA
+def fp6_operand_bytes(rows: int, K: int, layout: int) -> int:
+    out = ctypes.c_size_t(0)
+    L.check(L.lib().svdq_fp6_operand_bytes(rows, K, layout, ctypes.byref(out)), "svdq_fp6_operand_bytes")
+    return int(out.value)
+
+
+def pack_fp6_operand(codes, layout: int = L.SVDQ_FP6_WEIGHTS) -> np.ndarray:
+    """Host re-pack of nibble codes [rows][K/2] u8 into the fragment layout
+    (svdq_pack_fp6_operand); returns u8 [K/64][RB][1536]."""
+    c = np.ascontiguousarray(np.asarray(codes, dtype=np.uint8))
+    rows, K = c.shape[0], 2 * c.shape[1]
+    nbytes = fp6_operand_bytes(rows, K, layout)
+    out = np.empty(nbytes, np.uint8)
+    L.check(L.lib().svdq_pack_fp6_operand(_ptr(c), rows, K, layout, _ptr(out)), "svdq_pack_fp6_operand")
+    return out.reshape(K // 64, -1, 1536)
+
+
+def quant_act_lora_down_fp6(x: torch.Tensor, smooth_inv: torch.Tensor, lora_down: Optional[torch.Tensor],
+                            rank: int, group: int = 64, act: int = L.SVDQ_ACT_NONE, out=None):
+    """Kernel 1 with the codes in the 6-bit fragment layout.  Returns
+    (x_fp6 u8 [K/64][ceil(M/32)][1536], x_scales f16 [K/64][Mp], lora_act
+    f32 [M][rank]), Mp = 32 ceil(M/32)."""
+    if x.dtype != torch.bfloat16 or x.dim() != 2 or not x.is_cuda:
+        raise TypeError("x must be a 2-D bfloat16 CUDA tensor")
+    x = x.contiguous()
+    M, K = x.shape
+    dev = x.device
+    G = K // group if group > 0 else 0
+    RB = (M + 31) // 32
+    if out is None:
+        xf = torch.empty((G, RB, 1536), dtype=torch.uint8, device=dev)
+        xs = torch.empty((G, 32 * RB), dtype=torch.float16, device=dev)
+        la = torch.empty((M, rank), dtype=torch.float32, device=dev) if rank else None
+    else:
+        xf, xs, la = out
+    st = L.lib().svdq_quant_act_lora_down_fp6(
+        _dev_arg("x", x, torch.bfloat16, (M, K), dev),
+        _dev_arg("smooth_inv", smooth_inv, torch.float32, (K,), dev),
+        _dev_arg("lora_down", lora_down, torch.bfloat16, (rank, K), dev) if rank else None,
+        M, K, rank, group, act,
+        _dev_arg("x_fp6", xf, torch.uint8, (G, RB, 1536), dev),
+        _dev_arg("x_scales", xs, torch.float16, (G, 32 * RB), dev),
+        _dev_arg("lora_act", la, torch.float32, (M, rank), dev) if rank else None, _stream(dev))
+    L.check(st, "svdq_quant_act_lora_down_fp6")
+    return xf, xs, la
+
+
+def gemm_w4a4_fp6_lora_up(x_fp6, x_scales, w_fp6, w_scales, lora_act, lora_up, bias,
+                          M: int, N: int, K: int, rank: int, group: int = 64,
+                          out_dtype: int = L.SVDQ_OUT_BF16, out: Optional[torch.Tensor] = None):
+    """Kernel 2 on the 6-bit MFMA; returns y [M][N]."""
+    dev = x_fp6.device
+    dt = torch.float32 if out_dtype == L.SVDQ_OUT_F32 else torch.bfloat16
+    if out is None:
+        out = torch.empty((M, N), dtype=dt, device=dev)
+    G = K // group if group > 0 else 0
+    RBa, RBb = (M + 31) // 32, 4 * ((N + 127) // 128)
+    st = L.lib().svdq_gemm_w4a4_fp6_lora_up(
+        _dev_arg("x_fp6", x_fp6, torch.uint8, (G, RBa, 1536), dev),
+        _dev_arg("x_scales", x_scales, torch.float16, (G, 32 * RBa), dev),
+        _dev_arg("w_fp6", w_fp6, torch.uint8, (G, RBb, 1536), dev),
+        _dev_arg("w_scales", w_scales, torch.float16, (G, N), dev),
+        _dev_arg("lora_act", lora_act, torch.float32, (M, rank), dev) if rank else None,
+        _dev_arg("lora_up", lora_up, torch.bfloat16, (N, rank), dev) if rank else None,
+        _dev_arg("bias", bias, torch.bfloat16, (N,), dev),
+        M, N, K, rank, group, out_dtype, _dev_arg("y", out, dt, (M, N), dev), _stream(dev))
+    L.check(st, "svdq_gemm_w4a4_fp6_lora_up")
     return out
 
 
