@@ -68,6 +68,22 @@ def test_smoothing_closed_form():
     np.testing.assert_allclose(W_hat, (lam[:, None] * w.T), rtol=0)
 
 
+def test_smoothing_alpha_golden():
+    # alpha != 0.5 takes the general power form; hand-worked closed forms
+    for al, a, w, inv in _read_golden("smoothing_alpha.txt"):
+        si, lam = O.smoothing_factors(np.array([float(a)], np.float32),
+                                      np.array([[float(w)]]), alpha=float(al))
+        assert si[0] == float(np.float32(float(inv))), (al, a, w, si[0], inv)
+        assert lam[0] * si[0] == pytest.approx(1.0, rel=2 ** -52)
+    # alpha = 0.5 through the general form agrees with the square root form
+    rng = np.random.default_rng(9)
+    a = np.float32(rng.uniform(0.01, 50, 64))
+    w = rng.standard_normal((8, 64))
+    s_sqrt, _ = O.smoothing_factors(a, w, alpha=0.5)
+    s_pow, _ = O.smoothing_factors(a, w, alpha=0.5 + 1e-15)
+    np.testing.assert_allclose(s_pow, s_sqrt, rtol=1e-6)
+
+
 # ---------------------------------------------------------------- invariants
 def _pow2_lambda_case(M=24, K=128, N=40, seed=5):
     rng = np.random.default_rng(seed)

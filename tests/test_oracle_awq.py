@@ -3,6 +3,7 @@ force, alpha = 0 reduces to plain round-to-nearest, the search's choice."""
 import os
 
 import numpy as np
+import pytest
 
 import oracle as O
 import workloads
@@ -83,3 +84,33 @@ def test_awq_scale_cancels_without_quantization():
     t = 1.0 / p["inv_scale"]
     lhs = (wl["x"] * p["inv_scale"][None, :]) @ (wl["weight"] * t[None, :]).T
     np.testing.assert_allclose(lhs, wl["x"] @ wl["weight"].T, rtol=1e-12, atol=1e-15)
+
+
+def test_awq_channel_scale_golden():
+    x = np.array([[1.0, -4.0, 0.0], [-2.0, 8.0, 0.0], [3.0, 0.0, 0.0]])
+    for al, t in _rows("awq_channel_scale.txt"):
+        got = A.awq_channel_scale(x, float(al))
+        np.testing.assert_allclose(got, [float(v) for v in t.split()], rtol=1e-14)
+    # two channels: t = 2^-alpha/2, 2^alpha/2 for mean |x| = 2, 4 and alpha = 0.5
+    got = A.awq_channel_scale(x[:, :2], 0.5)
+    np.testing.assert_allclose(got, [2 ** -0.25, 2 ** 0.25], rtol=1e-15)
+
+
+def test_awq_search_loss_golden():
+    w = np.zeros((1, 64))
+    w[0, :16], w[0, 16:32], w[0, 32:] = 1.0, -1.0, 0.296875
+    x = np.zeros((1, 64))
+    x[0, :32], x[0, 32:] = 1.0, 16.0
+    p = A.awq_prepare(w, x)
+    for al, idx, err, loss in _rows("awq_search_loss.txt"):
+        assert A.ALPHA_GRID[int(idx)] == float(al)
+        assert p["losses"][int(idx)] == pytest.approx(float(loss), rel=1e-12)
+        assert float(err) ** 2 == float(loss)
+    # the chosen alpha does no worse than either worked alpha
+    best = min(p["losses"])
+    assert best <= 6.890625
+    assert p["losses"][int(round(p["alpha"] * 20))] == best
+    # the worked alpha = 0.5 codes of the group: B channels 15, A channels 14 / 0
+    q = A.awq_prepare(w, x, alpha=0.5)
+    assert q["z"][0, 0] == 7 and q["s"][0, 0] == 1195 / 16384
+    np.testing.assert_array_equal(q["q"][0], [14] * 16 + [0] * 16 + [15] * 32)
