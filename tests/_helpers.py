@@ -33,3 +33,54 @@ def oracle_prep_to_abi(p) -> dict:
         lora_up=f64_to_bf16_bits(p["L2"].T) if r else np.zeros((N, 0), np.uint16),
         rank=r, K=K, N=N,
     )
+
+
+def abi_to_oracle_prep(p, group: int = 64) -> dict:
+    """Library-prepared arrays (ABI storage layouts) -> the oracle's keys
+    (qw [K][N] ints, sw [K/64][N], L1 [K][r], L2 [r][N], smooth_inv), so
+    that the oracle's forward runs on exactly the arrays a layer holds."""
+    K, N, r = int(p["K"]), int(p["N"]), int(p["rank"])
+    return dict(
+        smooth_inv=np.asarray(p["smooth_inv"], np.float32).astype(np.float64).reshape(K),
+        qw=O.unpack_int4(np.asarray(p["w_codes"], np.uint8).reshape(N, K // 2)).T,
+        sw=np.asarray(p["w_scales"], np.float16).astype(np.float64).reshape(K // group, N),
+        L1=bf16_bits_to_f64(np.asarray(p["lora_down"]).reshape(r, K)).T if r else np.zeros((K, 0)),
+        L2=bf16_bits_to_f64(np.asarray(p["lora_up"]).reshape(N, r)).T if r else np.zeros((0, N)),
+        group=group,
+    )
+
+
+def ulp_bf16(v) -> np.ndarray:
+    """Spacing of bf16 values at |v| (normal range)."""
+    v = np.abs(np.asarray(v, np.float64))
+    e = np.floor(np.log2(np.maximum(v, 2.0 ** -126)))
+    return np.exp2(e - 7)
+
+
+def check_bf16_elementwise(yg, yo, frac: float = 1e-4, atol=0.0) -> None:
+    """|GPU - oracle| within one bf16 ulp of the oracle's value (plus
+    ``atol``, a per-element bound on the kernel's own fp32 rounding where a
+    path's arithmetic makes it larger than an ulp) for all but a ``frac``
+    fraction of the elements: fp32 accumulation in another order can move a
+    value across one bf16 rounding boundary, rarely two."""
+    yg, yo = np.asarray(yg, np.float64), np.asarray(yo, np.float64)
+    assert yg.shape == yo.shape
+    d = np.maximum(np.abs(yg - yo) - atol, 0.0) / ulp_bf16(yo)
+    bad = d > 1 + 1e-12
+    if bad.mean() > frac:
+        worst = np.argsort(d, axis=None)[::-1][:6]
+        rows = [f"{np.unravel_index(i, d.shape)}: gpu {yg.flat[i]!r} oracle {yo.flat[i]!r} ({d.flat[i]:.2f} ulp)"
+                for i in worst]
+        raise AssertionError(f"{bad.sum()} of {bad.size} elements differ by more than one bf16 ulp:\n"
+                             + "\n".join(rows))
+
+
+def check_f32_elementwise(yg, yo, rel: float = 2.0 ** -14) -> None:
+    """fp32 outputs: every element within rel * (|y| + rms(y)) of the
+    oracle's value (the kernel's fp32 sums over at most a few hundred
+    groups stay far inside this; a wrong tile or strip does not)."""
+    yg, yo = np.asarray(yg, np.float64), np.asarray(yo, np.float64)
+    assert yg.shape == yo.shape
+    rms = np.sqrt(np.mean(yo * yo)) if yo.size else 0.0
+    bad = np.abs(yg - yo) > rel * (np.abs(yo) + rms)
+    assert not bad.any(), f"{bad.sum()} of {bad.size} fp32 elements outside the bound"

@@ -2,7 +2,9 @@
 
 Bars: x_hat bit-exact; xsum equal to the fp32 sum in increasing k; output
 within 1e-3 relative Frobenius of the oracle's bf16 output (the inner sums
-run on bf16 MFMA with fp32 accumulation; the oracle sums in fp64).
+run on bf16 MFMA with fp32 accumulation; the oracle sums in fp64), and
+elementwise within one bf16 ulp plus the first-order bound of the kernel's
+fp32 rounding (see ``fp32_allowance``).
 """
 import numpy as np
 import pytest
@@ -11,7 +13,7 @@ import torch
 import oracle as O
 import workloads
 from oracle import awq_oracle as A
-from tests._helpers import bf16_bits_to_f64
+from tests._helpers import bf16_bits_to_f64, check_bf16_elementwise
 
 S = pytest.importorskip("w4a4_rank_corrected_svdq_amd")
 
@@ -59,6 +61,21 @@ def _run(wl, po, bias=True):
     return xh, xs, y
 
 
+def fp32_allowance(x_hat, po, bias):
+    """First-order worst-case rounding of the kernel's fp32 sums, n u sum|t|,
+    for the form it evaluates: sum_g s_g (sum_k (128 + q) x_hat - (128 + z_g)
+    X_g) + bias, whose terms are about 128 times larger than the result, so
+    that a small output can move by more than one bf16 ulp.  n = 4 product
+    blocks per group + G groups + 8 wave partials + 2 (scale and bias)."""
+    M, K = x_hat.shape
+    G = K // 64
+    ax = np.abs(x_hat)
+    t1 = ax @ ((128.0 + po["q"]) * np.repeat(po["s"], 64, axis=1)).T
+    t2 = ax.reshape(M, G, 64).sum(-1) @ (po["s"] * (128.0 + po["z"])).T
+    mag = t1 + t2 + (0.0 if bias is None else np.abs(bias)[None, :])
+    return (4 + G + 8 + 2) * 2.0 ** -24 * mag
+
+
 @pytest.mark.parametrize("M,K", [(1, 512), (5, 3072), (16, 192)])
 def test_awq_quant_act_exact(M, K):
     wl, po = _case(M, K, 32, seed=60 + M, alpha=0.5)
@@ -78,6 +95,8 @@ def test_awq_gemv_parity(M, K, N, bias):
     _, _, y = _run(wl, po, bias)
     ref = A.awq_forward(wl["x"], po, bias=wl["bias"] if bias else None)
     assert O.rel_fro(to_np_bf16(y), ref) < Y_TOL
+    x_hat = O.bf16(O.fp32(wl["x"] * po["inv_scale"][None, :]))
+    check_bf16_elementwise(to_np_bf16(y), ref, atol=fp32_allowance(x_hat, po, wl["bias"] if bias else None))
 
 
 @pytest.mark.parametrize("M", [1, 2])
@@ -88,6 +107,8 @@ def test_awq_full_size_modulation(M):
     _, _, y = _run(wl, po)
     ref = A.awq_forward(wl["x"], po, bias=wl["bias"])
     assert O.rel_fro(to_np_bf16(y), ref) < Y_TOL
+    x_hat = O.bf16(O.fp32(wl["x"] * po["inv_scale"][None, :]))
+    check_bf16_elementwise(to_np_bf16(y), ref, atol=fp32_allowance(x_hat, po, wl["bias"]))
     assert torch.isfinite(y.float()).all()
 
 

@@ -14,7 +14,8 @@ import torch
 import oracle as O
 import workloads
 from tests._fp6 import ACT, WGT, decode_fp6
-from tests._helpers import bf16_bits_to_f64, f64_to_bf16_bits, oracle_prep_to_abi
+from tests._helpers import (bf16_bits_to_f64, check_bf16_elementwise, f64_to_bf16_bits,  # noqa: F401
+                            oracle_prep_to_abi, ulp_bf16)
 
 S = pytest.importorskip("w4a4_rank_corrected_svdq_amd")
 from w4a4_rank_corrected_svdq_amd import _lib as L  # noqa: E402
@@ -56,18 +57,6 @@ def pad_scales(sx_gm, M):
     out = np.zeros((G, Mp), np.float16)
     out[:, :M] = sx_gm
     return out
-
-
-def ulp_bf16(v):
-    """Spacing of bf16 values at |v| (normal range)."""
-    v = np.abs(np.asarray(v, np.float64))
-    e = np.floor(np.log2(np.maximum(v, 2.0 ** -126)))
-    return np.exp2(e - 7)
-
-
-def check_bf16_elementwise(yg, yo, frac=1e-4):
-    bad = np.abs(yg - yo) > ulp_bf16(yo) * (1 + 1e-12)
-    assert bad.mean() <= frac, f"{bad.sum()} of {bad.size} elements differ by more than one bf16 ulp"
 
 
 def run_gemm(xf, xs, wf, ws, la, lu, bias, M, N, K, rank, out_dtype=L.SVDQ_OUT_BF16):

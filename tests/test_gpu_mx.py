@@ -11,7 +11,7 @@ import torch
 
 import oracle as O
 import workloads
-from tests._helpers import bf16_bits_to_f64, f64_to_bf16_bits
+from tests._helpers import bf16_bits_to_f64, check_bf16_elementwise, check_f32_elementwise, f64_to_bf16_bits
 from tests.test_mx_host import mx_prep_to_abi
 
 S = pytest.importorskip("w4a4_rank_corrected_svdq_amd")
@@ -166,6 +166,9 @@ def test_k2_mx_output_parity(rank, bias, out):
     assert e < Y_TOL, e
     if out == "f32":
         assert e < 1e-5, e
+        check_f32_elementwise(y_to_np(y), Yo)
+    else:
+        check_bf16_elementwise(y_to_np(y), Yo)
 
 
 @pytest.mark.parametrize("shape", [(300, 512, 264), (128, 1024, 512), (5, 256, 1032), (1, 128, 8)])
@@ -175,7 +178,9 @@ def test_mx_end_to_end_parity(shape):
     wl, Lr, po, abi = _case(M, K, N, rank, seed=99 + M, bias=True)
     xc, xs, la = run_k1(wl.x_bits, abi)
     y = run_k2(xc, xs, abi, la, Lr.bias_bits, M)
-    assert O.rel_fro(y_to_np(y), MX.forward_mx(wl.x, po, bias=Lr.bias)) < Y_TOL
+    Yo = MX.forward_mx(wl.x, po, bias=Lr.bias)
+    assert O.rel_fro(y_to_np(y), Yo) < Y_TOL
+    check_bf16_elementwise(y_to_np(y), Yo)
 
 
 def test_mx_full_size_sampled_rows():
@@ -199,6 +204,7 @@ def test_mx_full_size_sampled_rows():
     np.testing.assert_array_equal(xc.cpu().numpy()[rows], O.pack_int4(MX.e2m1_encode(parts["qx"])))
     np.testing.assert_array_equal(xs.cpu().numpy()[rows], (parts["ex"] + 127).astype(np.uint8))
     assert O.rel_fro(to_np_bf16(y[torch.from_numpy(rows).cuda()]), Yo) < Y_TOL
+    check_bf16_elementwise(to_np_bf16(y[torch.from_numpy(rows).cuda()]), Yo)
     assert torch.isfinite(y.float()).all()
 
 

@@ -11,7 +11,8 @@ import torch
 
 import oracle as O
 import workloads
-from tests._helpers import bf16_bits_to_f64, f64_to_bf16_bits, oracle_prep_to_abi
+from tests._helpers import (abi_to_oracle_prep, bf16_bits_to_f64, check_bf16_elementwise,
+                            check_f32_elementwise, f64_to_bf16_bits, oracle_prep_to_abi)
 
 S = pytest.importorskip("w4a4_rank_corrected_svdq_amd")
 from w4a4_rank_corrected_svdq_amd import _lib as L  # noqa: E402
@@ -63,6 +64,35 @@ def run_k2(xc, xs, abi, la, bias_bits, M, out_dtype=L.SVDQ_OUT_BF16):
 
 def y_to_np(y):
     return y.double().cpu().numpy() if y.dtype == torch.float32 else to_np_bf16(y)
+
+
+def check_y(y, yo, tol=Y_TOL):
+    """Relative Frobenius error within ``tol`` and the elementwise bound of
+    the output type (one bf16 ulp but for a 1e-4 fraction; fp32 within
+    2^-14 (|y| + rms y))."""
+    yg = y if isinstance(y, np.ndarray) else y_to_np(y)
+    e = O.rel_fro(yg, yo)
+    assert e < tol, e
+    if isinstance(y, torch.Tensor) and y.dtype == torch.float32:
+        check_f32_elementwise(yg, yo)
+    else:
+        check_bf16_elementwise(yg, yo)
+    return e
+
+
+def y_from_k1_outputs(xc, xs, la, po, bias=None, rows=None, out="bf16"):
+    """The oracle's kernel-2 arithmetic on kernel 1's own outputs (codes,
+    scales, lora_act): isolates kernel 2 where kernel 1 may legitimately
+    differ from the oracle (tanh-GELU codes on a rounding boundary)."""
+    rows = slice(None) if rows is None else rows
+    qx = O.unpack_int4(xc.cpu().numpy()[rows])
+    sx = xs.cpu().numpy().astype(np.float64).T[rows]
+    y = O.w4a4_product(qx, sx, po["qw"], po["sw"], 64)
+    if po["L1"].shape[1]:
+        y = y + O.bf16(la.double().cpu().numpy()[rows]) @ po["L2"]
+    if bias is not None:
+        y = y + np.asarray(bias, np.float64)[None, :]
+    return O.bf16(y) if out == "bf16" else O.fp32(y)
 
 
 # ------------------------------------------------------------------ kernel 2: integer core
@@ -179,8 +209,7 @@ def test_k2_output_parity(rank, bias, out):
     la = dev(parts["lora_act"].astype(np.float32)) if rank else None
     y = run_k2(xc, xs, abi, la, Lr.bias_bits if bias else None, M,
                out_dtype=L.SVDQ_OUT_F32 if out == "f32" else L.SVDQ_OUT_BF16)
-    e = O.rel_fro(y_to_np(y), Yo)
-    assert e < Y_TOL, e
+    e = check_y(y, Yo)
     if out == "f32":
         assert e < 1e-5, e
 
@@ -207,8 +236,7 @@ def test_k2_large_form_parity(rank, bias, out, K):
     la = dev(parts["lora_act"].astype(np.float32)) if rank else None
     od = L.SVDQ_OUT_F32 if out == "f32" else L.SVDQ_OUT_BF16
     y = run_k2(xc, xs, abi, la, Lr.bias_bits if bias else None, M, out_dtype=od)
-    e = O.rel_fro(y_to_np(y), Yo)
-    assert e < Y_TOL, e
+    e = check_y(y, Yo)
     if out == "f32":
         assert e < 1e-5, e
     again = run_k2(xc, xs, abi, la, Lr.bias_bits if bias else None, M, out_dtype=od)
@@ -223,7 +251,8 @@ def test_end_to_end_parity(shape):
     xc, xs, la = run_k1(wl.x_bits, abi["smooth_inv"], abi["lora_down"], 32)
     y = run_k2(xc, xs, abi, la, Lr.bias_bits, M)
     Yo = O.forward(wl.x, po, bias=Lr.bias)
-    assert O.rel_fro(y_to_np(y), Yo) < Y_TOL
+    check_y(y, Yo)
+    np.testing.assert_array_equal(xc.cpu().numpy(), O.pack_int4(O.quantize_activation(wl.x, po["smooth_inv"], 64)[0]))
 
 
 def test_determinism_bitwise():
@@ -255,11 +284,13 @@ def test_mlp_chain_gelu_small():
     au, ad = oracle_prep_to_abi(pu), oracle_prep_to_abi(pd)
     xc, xs, la = run_k1(wl.x_bits, au["smooth_inv"], au["lora_down"], 32)
     y_up = run_k2(xc, xs, au, la, None, M)
-    assert O.rel_fro(y_to_np(y_up), y_up_o) < Y_TOL
+    check_y(y_up, y_up_o)
     x2 = S.quant_act_lora_down(y_up, dev(ad["smooth_inv"]), dev_bf16(ad["lora_down"]), 32,
                                act=L.SVDQ_ACT_GELU_TANH)
     y_dn = run_k2(*x2[:2], ad, x2[2], None, M)
     assert O.rel_fro(y_to_np(y_dn), y_dn_o) < Y_TOL
+    # elementwise: the down layer's kernel 2 on its own kernel 1's outputs
+    check_bf16_elementwise(y_to_np(y_dn), y_from_k1_outputs(*x2, pd))
 
 
 # ------------------------------------------------------------------ unfused comparison path
@@ -295,7 +326,7 @@ def test_unfused_branch_parity(M, K, N, rank, bias):
     q, s, xh = O.quantize_activation(wl.x, po["smooth_inv"], 64)
     assert O.rel_fro(la.double().cpu().numpy(), O.lora_down(xh, po["L1"])) < LORA_TOL
     Yo = O.forward_unfused(wl.x, po, bias=Lr.bias if bias else None)
-    assert O.rel_fro(to_np_bf16(y), Yo) < Y_TOL
+    check_y(to_np_bf16(y), Yo)
 
 
 def test_lora_up_add_in_place_parity():
@@ -311,7 +342,7 @@ def test_lora_up_add_in_place_parity():
     torch.cuda.synchronize()
     ref = O.bf16(y0 + O.bf16(la) @ po["L2"])
     got = to_np_bf16(y)
-    assert O.rel_fro(got, ref) < Y_TOL
+    check_y(got, ref)
     # at most a 1-ulp flip where fp32 summation order meets a rounding boundary
     assert (got != ref).mean() < 0.01
 
@@ -331,16 +362,18 @@ def test_unfused_full_size_sampled_rows():
     xc, xs, la, y = run_unfused(wl.x_bits, abi, Lr.bias_bits, M)
     rows = _sample_rows(M, rng)
     Yo = O.forward_unfused(wl.x[rows], po, bias=Lr.bias)
-    assert O.rel_fro(to_np_bf16(y[torch.from_numpy(rows).cuda()]), Yo) < Y_TOL
+    check_y(to_np_bf16(y[torch.from_numpy(rows).cuda()]), Yo)
     assert torch.isfinite(y.float()).all()
 
 
 # ------------------------------------------------------------------ FLUX shapes, sampled rows
 FULL = {
-    "attn_out": dict(name="attn_out"),
-    "joint_qkv": dict(name="joint_qkv"),
-    "mlp_up": dict(name="mlp_pair"),
-    "rank_sweep_r32": dict(name="rank_sweep"),
+    "attn_out": dict(name="attn_out", rank=32),
+    "joint_qkv": dict(name="joint_qkv", rank=32),
+    "mlp_up": dict(name="mlp_pair", rank=32),
+    "rank_sweep_r32": dict(name="rank_sweep", rank=32),
+    "rank_sweep_r64": dict(name="rank_sweep", rank=64),
+    "rank_sweep_r128": dict(name="rank_sweep", rank=128),
 }
 
 
@@ -358,14 +391,15 @@ def _synthetic_factors(K, N, r, rng, scale):
 @pytest.mark.parametrize("case", list(FULL))
 def test_full_size_sampled_rows(case):
     """Both kernels at the FLUX shape, in the launch configuration the
-    benchmark times; the oracle recomputes a sample of rows (first, last and
+    benchmark times.  Codes and scales of every row against the oracle's
+    quantizer; lora_act and the output on a sample of rows (first, last and
     random ones).  The factors are seeded synthetic bf16 matrices so that the
     oracle's preparation needs no full-size SVD (the split itself is pinned
     at small sizes)."""
     wl = workloads.make_workload(FULL[case]["name"])
     Lr = wl.layers[0]
     M, K, N = wl.M, Lr.K, Lr.N
-    r = 32
+    r = FULL[case]["rank"]
     rng = np.random.default_rng(7)
     a = wl.act_absmax()
     si, lam = O.smoothing_factors(a, Lr.weight)
@@ -374,14 +408,16 @@ def test_full_size_sampled_rows(case):
     abi = oracle_prep_to_abi(po)
     xc, xs, la = run_k1(wl.x_bits, abi["smooth_inv"], abi["lora_down"], r)
     y = run_k2(xc, xs, abi, la, Lr.bias_bits, M)
+    q_all, s_all, _ = O.quantize_activation(wl.x, po["smooth_inv"], 64)
+    np.testing.assert_array_equal(xc.cpu().numpy(), O.pack_int4(q_all))
+    np.testing.assert_array_equal(xs.cpu().numpy().astype(np.float64), s_all.T)
+    del q_all, s_all
     rows = _sample_rows(M, rng)
     xr = wl.x[rows]
     Yo, parts = O.forward(xr, po, bias=Lr.bias, return_parts=True)
-    np.testing.assert_array_equal(xc.cpu().numpy()[rows], O.pack_int4(parts["qx"]))
-    np.testing.assert_array_equal(xs.cpu().numpy()[:, rows].astype(np.float64), parts["sx"].T)
     assert O.rel_fro(la.double().cpu().numpy()[rows], parts["lora_act"]) < LORA_TOL
     yr = to_np_bf16(y[torch.from_numpy(rows).cuda()])
-    assert O.rel_fro(yr, Yo) < Y_TOL
+    check_y(yr, Yo)
     assert torch.isfinite(y.float()).all()
 
 
@@ -399,11 +435,15 @@ def test_full_size_mlp_down_gelu_sampled_rows():
     abi = oracle_prep_to_abi(po)
     xc, xs, la = run_k1(wl.x_bits, abi["smooth_inv"], abi["lora_down"], r, act=L.SVDQ_ACT_GELU_TANH)
     y = run_k2(xc, xs, abi, la, None, M)
+    q_all, _, _ = O.quantize_activation(wl.x, po["smooth_inv"], 64, act="gelu_tanh")
+    mism = O.unpack_int4(xc.cpu().numpy()) != q_all
+    assert mism.mean() <= 1e-4
+    del q_all
     rows = _sample_rows(M, rng, 32)
-    Yo, parts = O.forward(wl.x[rows], po, act="gelu_tanh", return_parts=True)
-    qg = O.unpack_int4(xc.cpu().numpy()[rows])
-    assert (qg != parts["qx"]).mean() <= 1e-4
-    assert O.rel_fro(to_np_bf16(y[torch.from_numpy(rows).cuda()]), Yo) < Y_TOL
+    Yo = O.forward(wl.x[rows], po, act="gelu_tanh")
+    yr = to_np_bf16(y[torch.from_numpy(rows).cuda()])
+    assert O.rel_fro(yr, Yo) < Y_TOL
+    check_bf16_elementwise(yr, y_from_k1_outputs(xc, xs, la, po, rows=rows))
 
 
 def test_error_story_product_path():
@@ -435,7 +475,22 @@ def test_linear_module_with_oracle_prepared_arrays():
     lin = S.SVDQW4A4Linear(prep, bias, "cuda:0")
     y = lin(dev_bf16(wl.x_bits))
     torch.cuda.synchronize()
-    assert O.rel_fro(to_np_bf16(y), O.forward(wl.x, po, bias=Lr.bias)) < Y_TOL
+    check_y(to_np_bf16(y), O.forward(wl.x, po, bias=Lr.bias))
+
+
+def test_library_prepared_layer_against_oracle():
+    """Library preparation (smoothing, SVD split, INT4 residual) feeding both
+    kernels, against the oracle's forward on the very arrays the library
+    prepared, at three ranks and with bias."""
+    for M, K, N, r in ((300, 512, 264, 32), (64, 1024, 520, 0), (129, 256, 392, 64)):
+        wl = workloads.custom_workload(M, K, N, seed=64 + r, n_out=4, bias=True)
+        Lr = wl.layers[0]
+        p = S.prepare_weights(Lr.weight_bits, wl.act_absmax(), rank=r)
+        po = abi_to_oracle_prep(p)
+        lin = S.SVDQW4A4Linear(p, torch.from_numpy(Lr.bias_bits.view(np.int16).copy()).view(torch.bfloat16), "cuda")
+        y = lin(dev_bf16(wl.x_bits))
+        torch.cuda.synchronize()
+        check_y(to_np_bf16(y), O.forward(wl.x, po, bias=Lr.bias))
 
 
 def test_checkpoint_round_trip_forward(tmp_path):
@@ -454,6 +509,32 @@ def test_checkpoint_round_trip_forward(tmp_path):
     y0, y1 = lin0(x), lin1(x)
     torch.cuda.synchronize()
     np.testing.assert_array_equal(y0.view(torch.int16).cpu().numpy(), y1.view(torch.int16).cpu().numpy())
+    _, loaded = C.load_prepared(path)
+    check_y(to_np_bf16(y1), O.forward(wl.x, abi_to_oracle_prep(loaded["proj"][0]), bias=Lr.bias))
+
+
+def test_checkpoint_round_trip_mxfp4_and_awq(tmp_path):
+    """MXFP4 and AWQ layers saved to one checkpoint and loaded back compute
+    bit-identical outputs to the layers they were saved from."""
+    from w4a4_rank_corrected_svdq_amd import checkpoint as C
+    wl = workloads.custom_workload(64, 512, 264, seed=65, n_out=4, bias=True)
+    Lr = wl.layers[0]
+    pm = S.prepare_weights_mxfp4(Lr.weight_bits, wl.act_absmax(), rank=32)
+    aw = workloads.awq_workload(3, K=512, N=256, Mc=8, seed=66)
+    pa = S.awq_prepare(aw["weight_bits"], aw["x_cal_bits"])
+    path = str(tmp_path / "ckpt.safetensors")
+    C.save_prepared(path, {"proj": pm}, {"proj": Lr.bias_bits, "mod": aw["bias_bits"]}, awq_layers={"mod": pa})
+    got = C.load_linears(path)
+    bf = lambda b: torch.from_numpy(b.view(np.int16).copy()).view(torch.bfloat16)  # noqa: E731
+    ref_m = S.SVDQW4A4Linear(pm, bf(Lr.bias_bits), "cuda")
+    ref_a = S.AWQW4A16Linear(pa, bf(aw["bias_bits"]), "cuda")
+    assert isinstance(got["mod"], S.AWQW4A16Linear) and got["proj"].precision == "mxfp4"
+    x = dev_bf16(wl.x_bits)
+    xa = dev_bf16(aw["x_bits"])
+    pairs = ((ref_m(x), got["proj"](x)), (ref_a(xa), got["mod"](xa)))
+    torch.cuda.synchronize()
+    for a, b in pairs:
+        np.testing.assert_array_equal(a.view(torch.int16).cpu().numpy(), b.view(torch.int16).cpu().numpy())
 
 
 # ------------------------------------------------------------------ fused QKV epilogue
@@ -496,8 +577,7 @@ def test_qkv_epilogue_parity(M, heads, rank, bias, rope, out):
     la = dev(parts["lora_act"].astype(np.float32)) if rank else None
     od = L.SVDQ_OUT_F32 if out == "f32" else L.SVDQ_OUT_BF16
     y = run_qkv(xc, xs, abi, la, Lr.bias_bits if bias else None, M, qb, kb, cos, sin, out_dtype=od)
-    e = O.rel_fro(y_to_np(y), ref)
-    assert e < (1e-5 if out == "f32" else Y_TOL), e
+    check_y(y, ref, tol=(1e-5 if out == "f32" else Y_TOL))
     plain = run_k2(xc, xs, abi, la, Lr.bias_bits if bias else None, M, out_dtype=od)
     v0 = 2 * heads * 128
     np.testing.assert_array_equal(y[:, v0:].float().cpu().numpy(), plain[:, v0:].float().cpu().numpy())
@@ -522,8 +602,7 @@ def test_qkv_large_form_parity(M, heads, out):
     la = dev(parts["lora_act"].astype(np.float32))
     od = L.SVDQ_OUT_F32 if out == "f32" else L.SVDQ_OUT_BF16
     y = run_qkv(xc, xs, abi, la, Lr.bias_bits, M, qb, kb, cos, sin, out_dtype=od)
-    e = O.rel_fro(y_to_np(y), ref)
-    assert e < (1e-5 if out == "f32" else Y_TOL), e
+    check_y(y, ref, tol=(1e-5 if out == "f32" else Y_TOL))
     plain = run_k2(xc, xs, abi, la, Lr.bias_bits, M, out_dtype=od)
     v0 = 2 * heads * 128
     np.testing.assert_array_equal(y[:, v0:].float().cpu().numpy(), plain[:, v0:].float().cpu().numpy())
@@ -548,7 +627,7 @@ def test_qkv_full_size_sampled_rows():
     y = run_qkv(xc, xs, abi, la, Lr.bias_bits, M, qb, kb, cos, sin)
     rows = _sample_rows(M, rng)
     ref = O.forward_qkv(wl.x[rows], po, Lr.bias, qv, kv, cos[rows], sin[rows])
-    assert O.rel_fro(to_np_bf16(y[torch.from_numpy(rows).cuda()]), ref) < Y_TOL
+    check_y(to_np_bf16(y[torch.from_numpy(rows).cuda()]), ref)
     assert torch.isfinite(y.float()).all()
 
 

@@ -23,7 +23,7 @@ CXX_SOURCES = ["svdq_prepare.cpp", "svdq_fp6_layout.cpp"]
 # Packed-fp32 VALU forms are disabled for all device code; hipcc's host pass
 # warns that it does not know the feature, which is harmless.
 HIP_FLAGS = ["--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC", "-Wall",
-             "-ffp-contract=fast", "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops"]
+             "-ffp-contract=off", "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops"]
 CXX_FLAGS = ["-O3", "-std=c++17", "-fPIC", "-Wall", "-ffp-contract=off", "-mavx2", "-mfma"]
 
 

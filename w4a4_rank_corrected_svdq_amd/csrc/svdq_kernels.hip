@@ -1288,12 +1288,15 @@ int device_cu_count() {
 }
 
 template <int ACT, int NT, int QM, int RT>
-void launch_k1_kernel(const void* x, const float* smooth_inv, const void* lora_down, int M, int K, int rank,
-                      void* x_codes, void* x_scales, float* lora_act, size_t smem, hipStream_t st) {
+int launch_k1_kernel(const void* x, const float* smooth_inv, const void* lora_down, int M, int K, int rank,
+                     void* x_codes, void* x_scales, float* lora_act, size_t smem, hipStream_t st) {
   auto kern = k_quant_act_lora_down<ACT, NT, QM, RT>;
-  if (smem > 64 * 1024)
-    (void)hipFuncSetAttribute(reinterpret_cast<const void*>(kern), hipFuncAttributeMaxDynamicSharedMemorySize,
-                              static_cast<int>(smem));
+  // Dynamic LDS above the default 64 KB needs an opt-in; it is made once per
+  // instantiation for the whole 160 KB a CU offers (the size depends on K).
+  static const bool attr_ok =
+      hipFuncSetAttribute(reinterpret_cast<const void*>(kern), hipFuncAttributeMaxDynamicSharedMemorySize,
+                          160 * 1024) == hipSuccess;
+  if (!attr_ok && smem > 64 * 1024) return SVDQ_ERR_HIP;
   // Grids larger than the CU count run 8-wave blocks, two per CU, instead of
   // a second round of 16-wave blocks.
   const int rows = QM == Q_FP6 ? 32 * ((M + 31) / 32) : M;   // FP6: the padded last row block too
@@ -1302,6 +1305,7 @@ void launch_k1_kernel(const void* x, const float* smooth_inv, const void* lora_d
   hipLaunchKernelGGL(kern, dim3(blocks), dim3(waves * 64), smem, st,
                      static_cast<const uint16_t*>(x), smooth_inv, static_cast<const uint16_t*>(lora_down), M, K,
                      rank, static_cast<uint8_t*>(x_codes), x_scales, lora_act);
+  return SVDQ_OK;
 }
 
 // Every block reads all of L1 (K x rank bf16), twice its own X bytes at rank
@@ -1310,19 +1314,18 @@ void launch_k1_kernel(const void* x, const float* smooth_inv, const void* lora_d
 // bytes per CU.  Up to rank 64, while the doubled reduction buffer fits LDS,
 // and without the GELU prologue (its registers would spill).
 template <int ACT, int QM, int NT>
-void launch_k1_nt(const void* x, const float* smooth_inv, const void* lora_down, int M, int K, int rank,
+int launch_k1_nt(const void* x, const float* smooth_inv, const void* lora_down, int M, int K, int rank,
                   void* x_codes, void* x_scales, float* lora_act, hipStream_t st) {
   const size_t red1 = sizeof(float) * K1_MAX_WAVES * 2 * K1_ROWS * 16;
   const size_t smem1 = static_cast<size_t>(K) * sizeof(float) + red1;
   if constexpr (NT > 0 && NT <= 4 && ACT == SVDQ_ACT_NONE) {
     const bool many = (M + K1_ROWS - 1) / K1_ROWS > device_cu_count();
-    if (many && smem1 + red1 <= 160 * 1024) {
-      launch_k1_kernel<ACT, NT, QM, 2>(x, smooth_inv, lora_down, M, K, rank, x_codes, x_scales, lora_act,
-                                       smem1 + red1, st);
-      return;
-    }
+    if (many && smem1 + red1 <= 160 * 1024)
+      return launch_k1_kernel<ACT, NT, QM, 2>(x, smooth_inv, lora_down, M, K, rank, x_codes, x_scales, lora_act,
+                                              smem1 + red1, st);
   }
-  launch_k1_kernel<ACT, NT, QM, 1>(x, smooth_inv, lora_down, M, K, rank, x_codes, x_scales, lora_act, smem1, st);
+  return launch_k1_kernel<ACT, NT, QM, 1>(x, smooth_inv, lora_down, M, K, rank, x_codes, x_scales, lora_act,
+                                          smem1, st);
 }
 
 template <int ACT, int QM>
@@ -1331,11 +1334,13 @@ int launch_k1(const void* x, const float* smooth_inv, const void* lora_down, int
   const size_t smem = static_cast<size_t>(K) * sizeof(float) + sizeof(float) * K1_MAX_WAVES * 2 * K1_ROWS * 16;
   if (smem > 160 * 1024) return SVDQ_ERR_UNSUPPORTED_SHAPE;
   const int nt = rank / 16;
-  if (nt == 0) launch_k1_nt<ACT, QM, 0>(x, smooth_inv, lora_down, M, K, rank, x_codes, x_scales, lora_act, st);
-  else if (nt <= 2) launch_k1_nt<ACT, QM, 2>(x, smooth_inv, lora_down, M, K, rank, x_codes, x_scales, lora_act, st);
-  else if (nt <= 4) launch_k1_nt<ACT, QM, 4>(x, smooth_inv, lora_down, M, K, rank, x_codes, x_scales, lora_act, st);
-  else if (nt <= 8) launch_k1_nt<ACT, QM, 8>(x, smooth_inv, lora_down, M, K, rank, x_codes, x_scales, lora_act, st);
-  else launch_k1_nt<ACT, QM, 16>(x, smooth_inv, lora_down, M, K, rank, x_codes, x_scales, lora_act, st);
+  int rc;
+  if (nt == 0) rc = launch_k1_nt<ACT, QM, 0>(x, smooth_inv, lora_down, M, K, rank, x_codes, x_scales, lora_act, st);
+  else if (nt <= 2) rc = launch_k1_nt<ACT, QM, 2>(x, smooth_inv, lora_down, M, K, rank, x_codes, x_scales, lora_act, st);
+  else if (nt <= 4) rc = launch_k1_nt<ACT, QM, 4>(x, smooth_inv, lora_down, M, K, rank, x_codes, x_scales, lora_act, st);
+  else if (nt <= 8) rc = launch_k1_nt<ACT, QM, 8>(x, smooth_inv, lora_down, M, K, rank, x_codes, x_scales, lora_act, st);
+  else rc = launch_k1_nt<ACT, QM, 16>(x, smooth_inv, lora_down, M, K, rank, x_codes, x_scales, lora_act, st);
+  if (rc != SVDQ_OK) return rc;
   return hipGetLastError() == hipSuccess ? SVDQ_OK : SVDQ_ERR_HIP;
 }
 
@@ -1420,7 +1425,7 @@ constexpr size_t K2_SMEM_EPI = static_cast<size_t>(K2_WAVES) * K2_WM * K2_WN * 2
 constexpr size_t K2_SMEM = sizeof(K2Smem) > K2_SMEM_EPI ? sizeof(K2Smem) : K2_SMEM_EPI;
 
 template <int OUT_F32, int NT, int EPI>
-void launch_k2_t128(const void* xc, const void* xs, const void* wc, const void* ws, const float* la,
+int launch_k2_t128(const void* xc, const void* xs, const void* wc, const void* ws, const float* la,
                     const void* lu, const void* bias, int M, int N, int K, int rank, void* y,
                     const QkvArgs& qa, hipStream_t st) {
   // the stage buffers exceed the default 64 KB of dynamic LDS: opt in once
@@ -1429,12 +1434,13 @@ void launch_k2_t128(const void* xc, const void* xs, const void* wc, const void* 
                                hipFuncAttributeMaxDynamicSharedMemorySize,
                                static_cast<int>(K2_SMEM)) == hipSuccess;
   }();
-  (void)attr_ok;
+  if (!attr_ok) return SVDQ_ERR_HIP;
   const int nb = ((N + K2_BN - 1) / K2_BN) * ((M + K2_BM - 1) / K2_BM);
   hipLaunchKernelGGL((k_gemm_w4a4_lora_up_t128<OUT_F32, NT, EPI>), dim3(nb), dim3(K2_THREADS), K2_SMEM, st,
                      static_cast<const uint8_t*>(xc), static_cast<const _Float16*>(xs),
                      static_cast<const uint8_t*>(wc), static_cast<const _Float16*>(ws), la,
                      static_cast<const uint16_t*>(lu), static_cast<const uint16_t*>(bias), M, N, K, rank, y, qa);
+  return SVDQ_OK;
 }
 
 template <int OUT_F32, int NT, int EPI>
@@ -1463,8 +1469,10 @@ int launch_k2(const void* xc, const void* xs, const void* wc, const void* ws, co
     if (rank == 0) launch_k2_t256<OUT_F32, 0, EPI>(xc, xs, wc, ws, la, lu, bias, M, N, K, rank, y, qa, st);
     else launch_k2_t256<OUT_F32, 1, EPI>(xc, xs, wc, ws, la, lu, bias, M, N, K, rank, y, qa, st);
   } else {
-    if (rank == 0) launch_k2_t128<OUT_F32, 0, EPI>(xc, xs, wc, ws, la, lu, bias, M, N, K, rank, y, qa, st);
-    else launch_k2_t128<OUT_F32, 1, EPI>(xc, xs, wc, ws, la, lu, bias, M, N, K, rank, y, qa, st);
+    const int rc = rank == 0
+        ? launch_k2_t128<OUT_F32, 0, EPI>(xc, xs, wc, ws, la, lu, bias, M, N, K, rank, y, qa, st)
+        : launch_k2_t128<OUT_F32, 1, EPI>(xc, xs, wc, ws, la, lu, bias, M, N, K, rank, y, qa, st);
+    if (rc != SVDQ_OK) return rc;
   }
   return hipGetLastError() == hipSuccess ? SVDQ_OK : SVDQ_ERR_HIP;
 }

@@ -134,7 +134,8 @@ def custom_workload(M, K, N, *, seed=0, n_out=4, factor=30.0, bias=False,
     rng = np.random.default_rng(seed)
     row_std = np.ones(M)
     if text_rows:
-        row_std[M - text_rows:] = text_std
+        # joint stream: the text tokens come first, then the image tokens
+        row_std[:text_rows] = text_std
     xb, idx, fac = _draw_activation(rng, M, K, row_std, n_out, factor)
     layers = [Layer("up" if second_N else "linear", K, N, _draw_weight(rng, N, K))]
     if second_N:
