@@ -24,11 +24,19 @@
  *    (uint16_t / void*), packed INT4 codes as bytes holding two codes each,
  *    low nibble = even k, two's complement (-8 .. 7).
  *  - Weight layouts follow torch.nn.Linear: [out_features][in_features].
+ *  - The low-rank factors are stored transposed with respect to the
+ *    formula above, in the same [out][in] layout as the weight:
+ *    lora_down = L1^T [rank][K] (the down projection as a Linear(K -> rank))
+ *    and lora_up = L2^T [N][rank] (the up projection as a Linear(rank -> N)).
+ *    Kernel 1 then reads each rank row as a contiguous run along K next to
+ *    the activation row it multiplies, and kernel 2 reads each output
+ *    column's rank values as one contiguous run, as it reads its codes.
  *  - The library never allocates or frees memory and keeps no pointer after
- *    returning.  Device functions are asynchronous on the caller's stream
- *    (a hipStream_t passed as void*; NULL = the default stream); buffers
- *    must stay alive until the stream has finished.  Faults during execution
- *    surface at the caller's next synchronization.
+ *    returning.  Device functions are asynchronous on the caller's stream,
+ *    a hipStream_t passed as void* (NULL = the default stream) so that this
+ *    header compiles without the HIP headers (plain C and ctypes callers);
+ *    buffers must stay alive until the stream has finished.  Faults during
+ *    execution surface at the caller's next synchronization.
  *  - Only group = 64 is supported.  K must be a positive multiple of 64,
  *    N a positive multiple of 8, 0 <= rank <= min(K, N), rank % 16 == 0 and
  *    rank <= SVDQ_MAX_RANK.  M >= 0 (M == 0 launches nothing).
