@@ -73,49 +73,69 @@ constexpr int FRAG = 1536;
 // magic-constant conversion.
 //
 // Persistent grid: one block per CU walks the output tiles t = blockIdx.x,
-// blockIdx.x + gridDim.x, ... as one continuous sequence of stages.  A
-// tile's stages are its K / 64 groups, then one stage per 16 ranks of the
-// low-rank branch (at least four stages per tile; empty ones pad).  Every
-// stage moves 24 KB from HBM into a ring of F_NS LDS slots by LDS-DMA
-// buffer loads, issued F_NS - 1 stages ahead, three 1 KB loads per wave:
-//   group stage:     the tile's 8 activation and 8 weight fragments of the
-//                    group (contiguous 12 KB runs in the fragment layout);
-//   low-rank stage:  lora_act [256 rows][16 ranks] fp32 and lora_up
-//                    [256 columns][16 ranks] bf16, added into the same
-//                    accumulators on bf16 MFMA;
-// plus one 256-byte load per wave that carries the next stage's raw fp16
-// scales (waves 0-1 activation, 2-3 weight) and the stage's tile's bias
-// (waves 4-5; 6-7 duplicate it).  So at the top of stage s only stage s's loads must
-// have landed; the barrier publishes them and the fp32 scales converted
-// during stage s - 1, and frees the slot of stage s - 1 for stage s + 4.
+// blockIdx.x + gridDim.x, ... as one continuous sequence of stages.  A stage
+// carries two groups of 64 k (the second may be past K when K / 64 is odd),
+// or two 16-rank chunks of the low-rank branch; a tile's stages are its
+// ceil(G / 2) group stages, then ceil(rank / 32) low-rank stages (at least
+// two stages per tile; empty ones pad).  Every stage moves 48 KB from HBM
+// into a ring of F_NS LDS slots by LDS-DMA buffer loads, issued F_NS - 1
+// stages ahead, seven per wave:
+//   group half h:    the tile's 8 activation and 8 weight fragments of
+//                    group 2 j + h (contiguous 12 KB runs in the fragment
+//                    layout), three 1 KB runs per wave;
+//   low-rank half h: lora_act [256 rows][16 ranks] fp32 and lora_up
+//                    [256 columns][16 ranks] bf16 of chunk 2 j + h, added
+//                    into the same accumulators on bf16 MFMA;
+// plus one auxiliary load: wave 0 the raw fp16 activation scales and wave 1
+// the weight scales of the stage after the issued one (1 KB each: a lane
+// half per group), waves 2-7 the issued stage's tile's bias into a ring of
+// two per-tile entries (every stage of a tile reloads the same bytes).  So
+// at the top of stage s only stage s's loads must have landed; the barrier
+// publishes them and the fp32 scales converted during stage s - 1, and
+// frees the slot of stage s - 1 for stage s + 2.
 // After a tile's last stage the wave adds the bias, rounds, and stores its
 // 64 x 128 outputs with buffer stores (32 per lane; rows past M and columns
 // past N fall outside the buffer and are dropped), then starts the next
 // tile, whose first stages are already loading: the store overlaps them.
 // Stores count in the same vmcnt as the loads, so the wait at a stage adds
-// 32 to its count when a tile ended within the last four stages (at most
-// one can, with four or more stages per tile).
+// 32 to its count when a tile ended within the last F_NS - 1 stages (at
+// most one can, with F_NS - 1 or more stages per tile).
 constexpr int F_BM = 256;
 constexpr int F_BN = 256;
 constexpr int F_WAVES = 8;
 constexpr int F_THREADS = F_WAVES * 64;
-constexpr int F_NS = 5;                               // ring slots, one stage each
-constexpr int F_A = 8 * FRAG;                         // 12288: activation fragments of a stage
-constexpr int F_OPS = 24 * 1024;                      // operand bytes of a stage
-constexpr int F_SC = F_OPS;                           // raw fp16 scales of the next stage: x [256], w [256]
-constexpr int F_BIAS = F_SC + 1024;                   // the tile's bias [256] bf16 (+512 B duplicate)
-constexpr int F_SLOT = F_BIAS + 1024;
-constexpr int F_LA = 0;                               // low-rank stage: lora_act [256][16] fp32 (64 B rows)
-constexpr int F_LU = 16384;                           //                 lora_up [256][16] bf16 (32 B rows)
-constexpr int F_DMA = 4;                              // DMA loads per wave per stage
+constexpr int F_GPS = 2;                              // groups (or 16-rank chunks) per stage
+constexpr int F_NS = 3;                               // ring slots, one stage each
+constexpr int F_A = 8 * FRAG;                         // 12288: activation fragments of a group
+constexpr int F_HALF = 24 * 1024;                     // operand bytes of one group (or rank chunk)
+constexpr int F_OPS = F_GPS * F_HALF;                 // operand bytes of a stage
+constexpr int F_SC = F_OPS;                           // raw fp16 scales of the next stage: x [2][256] | w [2][256]
+constexpr int F_SLOT = F_SC + 2048;
+constexpr int F_LA = 0;                               // low-rank half: lora_act [256][16] fp32 (64 B rows)
+constexpr int F_LU = 16384;                           //                lora_up [256][16] bf16 (32 B rows)
+constexpr int F_CONV = F_GPS * (F_BM + F_BN);         // fp32 scales of a stage: x [2][256] | w [2][256]
+constexpr int F_DMA = 2 * 3 + 1;                      // loads per wave per stage
 constexpr int F_STORES = 32;                          // buffer stores per lane at a tile's end
-constexpr int F_MIN_STAGES = 4;
-constexpr int F_MAX_TILES = 512;                      // tiles per block (host: grid >= tiles / 512)
-static_assert(F_OPS / 1024 == 3 * F_WAVES, "three 1 KB operand loads per wave per stage");
-static_assert(F_LU + 256 * 32 == F_OPS, "a low-rank stage fills the operand area");
+constexpr int F_MIN_STAGES = F_NS - 1;
+constexpr int F_MAX_TILES = 256;                      // tiles per block (the host checks)
+static_assert(F_HALF / 1024 == 3 * F_WAVES, "three 1 KB operand loads per wave per group");
+static_assert(F_LU + 256 * 32 == F_HALF, "a low-rank chunk fills a group's operand area");
 static_assert(F_SLOT % 16 == 0, "slots stay 16-byte aligned");
-static_assert(F_NS == F_MIN_STAGES + 1, "stages s .. s + 4 are live at once");
 static_assert(F_DMA * (F_NS - 2) + F_STORES <= 63, "wait counts fit vmcnt");
+static_assert(F_NS * F_SLOT + 2 * F_CONV * 4 + 2 * F_BN * 2 + F_MAX_TILES * 4 <= 160 * 1024, "LDS of one CU");
+
+// Three consecutive 1 KB LDS-DMA runs (16 bytes per lane each) under one M0
+// write: the instruction offsets 0, 1024, 2048 advance the buffer offset and
+// the LDS address alike, and the buffer range check sees voff + offset, so a
+// voff past the end drops all three.
+__device__ __forceinline__ void dma16x3(const DmaRsrc& r, uint32_t lds_addr, uint32_t voff) {
+  asm volatile(
+      "s_mov_b32 m0, %0\n\ts_nop 4\n\t"
+      "buffer_load_dwordx4 %1, %2, 0 offen lds\n\t"
+      "buffer_load_dwordx4 %1, %2, 0 offen offset:1024 lds\n\t"
+      "buffer_load_dwordx4 %1, %2, 0 offen offset:2048 lds"
+      :: "s"(lds_addr), "v"(voff), "s"(r.w) : "memory", "m0");
+}
 
 // Output tile of tile index t: the XCD-aware order of xcd_tile, applied to t
 // (the block that runs tile t sits on XCD t % 8, as t = blockIdx.x + j *
@@ -141,7 +161,8 @@ __global__ __launch_bounds__(F_THREADS, 1) void k_gemm_w4a4_fp6(
     const float* __restrict__ lora_act, const uint16_t* __restrict__ lora_up,
     const uint16_t* __restrict__ bias, int M, int N, int K, int rank, void* __restrict__ y) {
   __shared__ __align__(16) unsigned char ring[F_NS][F_SLOT];
-  __shared__ __align__(16) float conv[2][F_BM + F_BN];   // fp32 scales: x [256] | w [256]
+  __shared__ __align__(16) float conv[2][F_CONV];
+  __shared__ __align__(16) uint16_t bias_ring[2][F_BN];   // bias of the tiles with even / odd index j
   __shared__ int tiles[F_MAX_TILES];                      // this block's tiles: tm << 16 | tn
 
   const int tid = threadIdx.x;
@@ -153,10 +174,10 @@ __global__ __launch_bounds__(F_THREADS, 1) void k_gemm_w4a4_fp6(
   const int ntiles = nM * nN;
   const int G = K / GROUP;
   const int NR = rank / 16;
-  const int SPT = max(G + NR, F_MIN_STAGES);                 // stages per tile
+  const int GS = (G + 1) / 2;                                 // group stages per tile
+  const int SPT = max(GS + (NR + 1) / 2, F_MIN_STAGES);      // stages per tile
   const int my_tiles = (ntiles - static_cast<int>(blockIdx.x) + static_cast<int>(gridDim.x) - 1) /
                        static_cast<int>(gridDim.x);
-  const int S = my_tiles * SPT;
   const int RBa = (M + 31) / 32;
   const int Mp = 32 * RBa;
   const int RBb = 4 * ((N + 127) / 128);
@@ -165,20 +186,21 @@ __global__ __launch_bounds__(F_THREADS, 1) void k_gemm_w4a4_fp6(
 
   // Buffer resources: each wave moves one operand in group stages
   // (activations for waves 0-3, weights for 4-7) and one auxiliary array
-  // (activation scales for waves 0-1, weight scales for 2-3, bias for 4-7).
+  // (activation scales for wave 0, weight scales for wave 1, bias for 2-7).
   const bool opA = wave < 4;
   const DmaRsrc op_rs = dma_rsrc(opA ? static_cast<const void*>(x_fp6) : static_cast<const void*>(w_fp6),
                                  static_cast<uint32_t>(static_cast<size_t>(G) * (opA ? RBa : RBb) * FRAG));
   const DmaRsrc aux_rs =
-      wave < 2 ? dma_rsrc(x_scales, static_cast<uint32_t>(static_cast<size_t>(G) * Mp * 2))
-               : (wave < 4 ? dma_rsrc(w_scales, static_cast<uint32_t>(static_cast<size_t>(G) * N * 2))
-                           : dma_rsrc(bias, bias ? static_cast<uint32_t>(N) * 2u : 0u));
+      wave == 0 ? dma_rsrc(x_scales, static_cast<uint32_t>(static_cast<size_t>(G) * Mp * 2))
+                : (wave == 1 ? dma_rsrc(w_scales, static_cast<uint32_t>(static_cast<size_t>(G) * N * 2))
+                             : dma_rsrc(bias, bias ? static_cast<uint32_t>(N) * 2u : 0u));
   const DmaRsrc la_rs = dma_rsrc(lora_act, static_cast<uint32_t>(static_cast<size_t>(M) * rank * 4));
   const DmaRsrc lu_rs = dma_rsrc(lora_up, static_cast<uint32_t>(static_cast<size_t>(N) * rank * 2));
   const uint32_t y_bytes = static_cast<uint32_t>(static_cast<size_t>(M) * N * ELEM);
   const __amdgpu_buffer_rsrc_t y_rs = __builtin_amdgcn_make_buffer_rsrc(y, 0, static_cast<int>(y_bytes), 0x00020000);
 
   const uint32_t ring0 = static_cast<uint32_t>(reinterpret_cast<uintptr_t>(&ring[0][0]));
+  const uint32_t bias0 = static_cast<uint32_t>(reinterpret_cast<uintptr_t>(&bias_ring[0][0]));
 
   // The block's tiles, t = blockIdx.x + j gridDim.x, in LDS (read at tile
   // changes, not recomputed in the loop).
@@ -190,19 +212,21 @@ __global__ __launch_bounds__(F_THREADS, 1) void k_gemm_w4a4_fp6(
   __syncthreads();
   auto tile_at = [&](int j) { return __builtin_amdgcn_readfirstlane(tiles[j < my_tiles ? j : 0]); };
 
-  // DMA roles (wave-uniform).  In a group stage waves 0-3 move the 12 KB of
+  // DMA roles (wave-uniform).  In a group half waves 0-3 move the 12 KB of
   // activation fragments and waves 4-7 the 12 KB of weight fragments, three
   // 1 KB runs each (run r of the operand: bytes 1024 r .. + 1023 of its
-  // contiguous 12 KB); in a low-rank stage runs 0..15 of the 24 are
-  // lora_act (16 rows of 64 bytes each) and 16..23 lora_up (32 rows of 32
-  // bytes).  The fourth load: waves 0-1 the activation scales and 2-3 the
-  // weight scales of the stage after the issued one, waves 4-7 the issued
-  // stage's bias (two 256-byte halves, duplicated).
+  // contiguous 12 KB); in a low-rank half runs 0..15 of the 24 are lora_act
+  // (16 rows of 64 bytes each) and 16..23 lora_up (32 rows of 32 bytes).
+  // The auxiliary load: wave 0 the activation scales and wave 1 the weight
+  // scales of the two groups of the stage after the issued one (lane half
+  // hl = lane / 32 takes the second group's 512 bytes), waves 2-7 a 256-byte
+  // half of the issued tile's bias (waves 4-7 repeat 2-3).
   const uint32_t op_run0 = 1024u * static_cast<uint32_t>(opA ? 3 * wave : 3 * wave - 12);
   const uint32_t op_gstride = static_cast<uint32_t>(opA ? RBa : RBb) * FRAG;
   const uint32_t op_lds = __builtin_amdgcn_readfirstlane(ring0 + 1024 * 3 * wave);
-  const uint32_t aux_lds = __builtin_amdgcn_readfirstlane(ring0 + F_SC + 256 * (wave < 4 ? wave : 4 + (wave & 1)));
-  const uint32_t aux_part = 256u * (wave & 1);
+  const uint32_t aux_lds = __builtin_amdgcn_readfirstlane(ring0 + F_SC + 1024 * wave);   // waves 0-1
+  const uint32_t bias_lds = __builtin_amdgcn_readfirstlane(bias0 + 256u * (wave & 1));   // waves 2-7
+  const uint32_t aux_lim = wave == 0 ? 2u * Mp : 2u * N;         // bytes per group of a scale array
   // The lane index, recomputed where it is used outside the group section
   // (an empty asm hides that it is loop-invariant), so that the compiler
   // does not keep every per-lane offset of the DMA, low-rank and store
@@ -213,76 +237,123 @@ __global__ __launch_bounds__(F_THREADS, 1) void k_gemm_w4a4_fp6(
     return l;
   };
   const uint32_t lane16 = 16u * lane;
+  // scale-array byte offset of group g of tile t (waves 0-1)
+  auto scale_off = [&](int t, int g) {
+    const uint32_t b0 = wave == 0 ? 2u * F_BM * static_cast<uint32_t>(t >> 16)
+                                  : 2u * F_BN * static_cast<uint32_t>(t & 0xFFFF);
+    return static_cast<uint32_t>(g) * aux_lim + b0;
+  };
+  auto bias_off = [&](int t) {
+    return bias != nullptr ? 2u * F_BN * static_cast<uint32_t>(t & 0xFFFF) + 256u * (wave & 1) : OOB;
+  };
+  // the auxiliary load of waves 0-1: groups g0, g0 + 1 (lane halves);
+  // groups past G, or g0 < 0, read as zeros
+  auto scale_load = [&](uint32_t lds, int t, int g0) {
+    const int ln = fresh_lane();
+    const int g = g0 + (ln >> 5);
+    const uint32_t v = g0 >= 0 && g < G ? scale_off(t, g) + 16u * (ln & 31) : OOB;
+    dma16(aux_rs, lds, v);
+  };
 
   // Issue cursor: the stage being issued is stage li of tile ji (tile
-  // coordinates ti; tn_ of the following tile), slot si.
-  int ji = 0, li = 0, si = 0;
+  // coordinates ti; those of the following tile tnx), at slot byte offset
+  // so.  In the common case -- the issued stage and the one after it are
+  // full group stages of a live tile -- the operand runs start at op_cur
+  // and the scale load at aux_cur, both advanced by two groups per stage;
+  // every other stage takes the general path, which also re-bases both at
+  // a tile change.
+  int ji = 0, li = 0;
+  uint32_t so = 0;
   int ti = tile_at(0), tnx = tile_at(1);
-  auto issue = [&]() {
-    const uint32_t so = static_cast<uint32_t>(si) * F_SLOT;
-    const bool live = ji < my_tiles;
-    // per-lane parts of the addresses (the rest is wave-uniform); rows past
-    // M or N lie past the end of their buffer and read as zero
-    const int ln = fresh_lane();
-    const uint32_t l16 = 16u * ln, l4 = 4u * ln;
-    const int tmi = ti >> 16, tni = ti & 0xFFFF;
-    if (li < G || !live) {
-      const uint32_t base = __builtin_amdgcn_readfirstlane(
-          live ? 8u * FRAG * static_cast<uint32_t>(opA ? tmi : tni) + static_cast<uint32_t>(li) * op_gstride + op_run0
-               : OOB);
-#pragma unroll
-      for (int i = 0; i < 3; ++i)
-        dma16(op_rs, __builtin_amdgcn_readfirstlane(op_lds + 1024 * i + so), base + 1024u * i + l16);
-    } else {
-      const int ch = li - G;                                   // rank chunk; >= NR: padding stage
-#pragma unroll
-      for (int i = 0; i < 3; ++i) {
-        const int q = 3 * wave + i;
-        const bool isla = q < 16;
-        const int row0 = isla ? F_BM * tmi + 16 * q : F_BN * tni + 32 * (q - 16);
-        const uint32_t base = __builtin_amdgcn_readfirstlane(
-            ch < NR ? (static_cast<uint32_t>(row0) * rank + 16u * ch) * (isla ? 4u : 2u) : OOB);
-        if (isla)
-          dma16(la_rs, __builtin_amdgcn_readfirstlane(op_lds + 1024 * i + so),
-                base + static_cast<uint32_t>(ln >> 2) * static_cast<uint32_t>(rank * 4) + 16u * (ln & 3));
-        else
-          dma16(lu_rs, __builtin_amdgcn_readfirstlane(op_lds + 1024 * i + so),
-                base + static_cast<uint32_t>(ln >> 1) * static_cast<uint32_t>(rank * 2) + 16u * (ln & 1));
-      }
-    }
-    uint32_t abase;
-    if (wave < 4) {
-      // scales of the following stage: group li + 1 of this tile, or group 0
-      // of the next tile
-      const bool isx = wave < 2;
-      const int lnext = li + 1;
-      const bool same = lnext < G, nxt = lnext == SPT && ji + 1 < my_tiles;
-      const int tile = same ? ti : tnx;
-      const uint32_t lim = isx ? 2u * Mp : 2u * N;
-      const uint32_t b0 = isx ? 2u * F_BM * static_cast<uint32_t>(tile >> 16) : 2u * F_BN * static_cast<uint32_t>(tile & 0xFFFF);
-      abase = live && (same || nxt) ? (same ? static_cast<uint32_t>(lnext) * lim : 0u) + b0 + aux_part : OOB;
-    } else {
-      abase = live && bias != nullptr ? 2u * F_BN * static_cast<uint32_t>(tni) + aux_part : OOB;
-    }
-    dma4(aux_rs, __builtin_amdgcn_readfirstlane(aux_lds + so), __builtin_amdgcn_readfirstlane(abase) + l4);
-    // advance
-    si = si == F_NS - 1 ? 0 : si + 1;
+  auto op_base_of = [&](int t) {
+    return 8u * FRAG * static_cast<uint32_t>(opA ? (t >> 16) : (t & 0xFFFF)) + op_run0;
+  };
+  uint32_t op_cur = op_base_of(ti);
+  uint32_t aux_cur = wave < 2 ? scale_off(ti, 2) : bias_off(ti);
+  const uint32_t aux_step = wave < 2 ? 2u * aux_lim : 0u;
+  auto advance = [&]() {
+    so = so == (F_NS - 1) * F_SLOT ? 0u : so + F_SLOT;
     if (++li == SPT) {
       li = 0;
       ++ji;
       ti = tnx;
       tnx = tile_at(ji + 1);
+      op_cur = op_base_of(ti);
+      aux_cur = wave < 2 ? scale_off(ti, 2) : bias_off(ti);
+    } else {
+      op_cur += 2u * op_gstride;
+      aux_cur += aux_step;
     }
   };
-  // Thread t converts activation scale t (t < 256) or weight scale t - 256
-  // of the raw scales in slot `slot` to fp32.  No bounds: rows M .. Mp - 1
-  // hold zero scales; rows and columns past the operands read other groups'
-  // scales or zeros, and their outputs are never stored.
+  auto issue = [&]() {
+    const bool live = ji < my_tiles;
+    const uint32_t blds = __builtin_amdgcn_readfirstlane(bias_lds + 512u * static_cast<uint32_t>(ji & 1));
+    if (live && 2 * (li + 2) <= G) {
+      const int ln = fresh_lane();
+      dma16x3(op_rs, __builtin_amdgcn_readfirstlane(op_lds + so), op_cur + 16u * ln);
+      dma16x3(op_rs, __builtin_amdgcn_readfirstlane(op_lds + so + F_HALF), op_cur + op_gstride + 16u * ln);
+      if (wave < 2)
+        dma16(aux_rs, __builtin_amdgcn_readfirstlane(aux_lds + so),
+              aux_cur + static_cast<uint32_t>(ln >> 5) * aux_lim + 16u * (ln & 31));
+      else
+        dma4(aux_rs, blds, aux_cur + 4u * ln);
+      advance();
+      return;
+    }
+    // per-lane parts of the addresses (the rest is wave-uniform); rows past
+    // M or N lie past the end of their buffer and read as zero
+    const int ln = fresh_lane();
+    const uint32_t l16 = 16u * ln;
+    const int tmi = ti >> 16, tni = ti & 0xFFFF;
+    if (li < GS || !live) {
+#pragma unroll
+      for (int hh = 0; hh < 2; ++hh) {
+        const int g = 2 * li + hh;
+        const uint32_t base = __builtin_amdgcn_readfirstlane(
+            live && g < G ? op_base_of(ti) + static_cast<uint32_t>(g) * op_gstride : OOB);
+        dma16x3(op_rs, __builtin_amdgcn_readfirstlane(op_lds + so + F_HALF * hh), base + l16);
+      }
+    } else {
+#pragma unroll
+      for (int hh = 0; hh < 2; ++hh) {
+        const int ch = 2 * (li - GS) + hh;                     // rank chunk; >= NR: padding
+#pragma unroll
+        for (int i = 0; i < 3; ++i) {
+          const int q = 3 * wave + i;
+          const bool isla = q < 16;
+          const int row0 = isla ? F_BM * tmi + 16 * q : F_BN * tni + 32 * (q - 16);
+          const uint32_t base = __builtin_amdgcn_readfirstlane(
+              ch < NR ? (static_cast<uint32_t>(row0) * rank + 16u * ch) * (isla ? 4u : 2u) : OOB);
+          const uint32_t lds = __builtin_amdgcn_readfirstlane(op_lds + 1024 * i + so + F_HALF * hh);
+          if (isla)
+            dma16(la_rs, lds, base + static_cast<uint32_t>(ln >> 2) * static_cast<uint32_t>(rank * 4) + 16u * (ln & 3));
+          else
+            dma16(lu_rs, lds, base + static_cast<uint32_t>(ln >> 1) * static_cast<uint32_t>(rank * 2) + 16u * (ln & 1));
+        }
+      }
+    }
+    if (wave < 2) {
+      // scales of the following stage: groups 2 (li + 1), + 1 of this tile,
+      // or groups 0, 1 of the next tile
+      const int lnext = li + 1;
+      const bool same = live && lnext < GS, nxt = live && lnext == SPT && ji + 1 < my_tiles;
+      scale_load(__builtin_amdgcn_readfirstlane(aux_lds + so), same ? ti : tnx, same ? 2 * lnext : (nxt ? 0 : -1));
+    } else {
+      dma4(aux_rs, blds, (live ? bias_off(ti) : OOB) + 4u * ln);
+    }
+    advance();
+  };
+  // Thread t converts raw scales t and t + 512 of slot `slot` to fp32.  No
+  // bounds: rows M .. Mp - 1 hold zero scales; rows and columns past the
+  // operands read other groups' scales or zeros, and their outputs are
+  // never stored.
   auto convert_scales = [&](int slot, int buf) {
     int t = tid;
     asm volatile("" : "+v"(t));
     const _Float16* raw = reinterpret_cast<const _Float16*>(&ring[slot][F_SC]);
-    conv[buf][t] = static_cast<float>(raw[t]);
+    const float lo = static_cast<float>(raw[t]), hi = static_cast<float>(raw[t + F_THREADS]);
+    conv[buf][t] = lo;
+    conv[buf][t + F_THREADS] = hi;
   };
 
   v16f acc[2][4];
@@ -293,21 +364,14 @@ __global__ __launch_bounds__(F_THREADS, 1) void k_gemm_w4a4_fp6(
 #pragma unroll
       for (int e = 0; e < 16; ++e) acc[a][t][e] = 0.f;
 
-  // per-lane LDS byte offsets in a slot
+  // per-lane LDS byte offsets in a group half of a slot
   const uint32_t a_off = (2 * wm) * FRAG + lane16;             // + a * FRAG; dwords 4-5 at + 1024 - 8 lane
   const uint32_t b_off = F_A + (4 * wn) * FRAG + lane16;
   const v16f zero = {};
 
   // Stage 0's scales into slot F_NS - 1's scale area (free until stage
-  // F_NS - 1 is issued): the issue path's scale load with the cursor one
-  // stage back; then stages 0 .. F_NS - 2.
-  {
-    const bool isx = wave < 2;
-    const uint32_t b0 = isx ? 2u * F_BM * static_cast<uint32_t>(ti >> 16) : 2u * F_BN * static_cast<uint32_t>(ti & 0xFFFF);
-    const uint32_t abase = wave < 4 ? b0 + aux_part : OOB;
-    dma4(aux_rs, __builtin_amdgcn_readfirstlane(aux_lds + (F_NS - 1) * F_SLOT),
-         __builtin_amdgcn_readfirstlane(abase) + 4u * lane);
-  }
+  // F_NS - 1 is issued); then stages 0 .. F_NS - 2.
+  if (wave < 2) scale_load(__builtin_amdgcn_readfirstlane(aux_lds + (F_NS - 1) * F_SLOT), ti, 0);
 #pragma unroll
   for (int k = 0; k < F_NS - 1; ++k) issue();
   __builtin_amdgcn_s_waitcnt(waitcnt_vm_lgkm0(F_DMA * (F_NS - 2)));   // stage 0's scales and stage 0
@@ -317,13 +381,13 @@ __global__ __launch_bounds__(F_THREADS, 1) void k_gemm_w4a4_fp6(
 
   int s = 0;                 // stage index in the block's sequence
   int sc = 0;                // its slot
-  int since_end = 8;         // stages since the last tile end (its stores outstanding if < 4)
-  // Top of stage s: its loads landed (stages s + 1 .. s + 3 may be in flight,
-  // and the stores of a tile that ended in the last four stages); the
-  // barrier publishes them; then stage s + 4 is issued and stage s + 1's
-  // scales converted.
+  int since_end = 8;         // stages since the last tile end (its stores outstanding if < F_NS - 1)
+  // Top of stage s: its loads landed (stage s + 1 may be in flight, and the
+  // stores of a tile that ended in the last F_NS - 1 stages); the barrier
+  // publishes them; then stage s + 2 is issued and stage s + 1's scales
+  // converted.
   auto stage_top = [&]() {
-    if (since_end < 4) __builtin_amdgcn_s_waitcnt(waitcnt_vm(F_DMA * (F_NS - 2) + F_STORES));
+    if (since_end < F_NS - 1) __builtin_amdgcn_s_waitcnt(waitcnt_vm(F_DMA * (F_NS - 2) + F_STORES));
     else __builtin_amdgcn_s_waitcnt(waitcnt_vm(F_DMA * (F_NS - 2)));
     __builtin_amdgcn_s_barrier();
     asm volatile("" ::: "memory");
@@ -341,60 +405,66 @@ __global__ __launch_bounds__(F_THREADS, 1) void k_gemm_w4a4_fp6(
     const int mw = F_BM * (tt >> 16) + 64 * wm, cw = F_BN * (tt & 0xFFFF) + 128 * wn;   // wave-uniform
 
     // ---- the tile's groups: P_g on the 6-bit MFMA, then dequantization ----
-    for (int l = 0; l < G; ++l, stage_end()) {
+    for (int l = 0; l < GS; ++l, stage_end()) {
       stage_top();
-      const unsigned char* sl = ring[sc];
-      const float* cv = conv[s & 1];
-      const float4 sw = *reinterpret_cast<const float4*>(cv + F_BM + 128 * wn + 4 * c);
-      const float swv[4] = {sw.x, sw.y, sw.z, sw.w};
-      auto rd_frag = [&](uint32_t off) {
-        const uint4 lo = *reinterpret_cast<const uint4*>(sl + off);
-        const uint2 hi = *reinterpret_cast<const uint2*>(sl + off + 1024 - 8 * lane);
-        return v8i{static_cast<int>(lo.x), static_cast<int>(lo.y), static_cast<int>(lo.z), static_cast<int>(lo.w),
-                   static_cast<int>(hi.x), static_cast<int>(hi.y), 0, 0};
-      };
-      // Tiles in the order (n tile 0, m tile 0), (0, 1), (1, 0), ...: a
-      // weight fragment serves two consecutive tiles and is read one tile
-      // pair ahead; a tile's row scales are read from LDS four at a time as
-      // it is dequantized (two distinct addresses per read: broadcast).  The
-      // MFMA of tile u + 1 is issued before tile u is dequantized (results
-      // in a ring of two).
-      const float* sxp = cv + 64 * wm + 4 * h;
-      v8i afr[2];
-      afr[0] = rd_frag(a_off);
-      afr[1] = rd_frag(a_off + FRAG);
-      v8i bfr[4];
-      bfr[0] = rd_frag(b_off);
-      v16f dr[2];
 #pragma unroll
-      for (int u = 0; u < 9; ++u) {
-        if (u < 8) {
-          const int t = u >> 1, a = u & 1;
-          if (a == 0 && t < 3) bfr[t + 1] = rd_frag(b_off + (t + 1) * FRAG);
-          // cbsz = blgp = 3: both operands E3M2; E8M0 scales 127 (= 1)
-          dr[u & 1] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(afr[a], bfr[t], zero, 3, 3, 0, 127, 0, 127);
-        }
-        if (u > 0) {
-          const int v = u - 1, t = v >> 1, a = v & 1;
+      for (int hg = 0; hg < 2; ++hg) {
+        if (hg == 1 && 2 * l + 1 >= G) break;                 // K / 64 odd: the last stage holds one group
+        const unsigned char* sl = ring[sc] + F_HALF * hg;
+        const float* cv = conv[s & 1];
+        const float4 sw = *reinterpret_cast<const float4*>(cv + F_GPS * F_BM + F_BN * hg + 128 * wn + 4 * c);
+        const float swv[4] = {sw.x, sw.y, sw.z, sw.w};
+        auto rd_frag = [&](uint32_t off) {
+          const uint4 lo = *reinterpret_cast<const uint4*>(sl + off);
+          const uint2 hi = *reinterpret_cast<const uint2*>(sl + off + 1024 - 8 * lane);
+          return v8i{static_cast<int>(lo.x), static_cast<int>(lo.y), static_cast<int>(lo.z), static_cast<int>(lo.w),
+                     static_cast<int>(hi.x), static_cast<int>(hi.y), 0, 0};
+        };
+        // Tiles in the order (n tile 0, m tile 0), (0, 1), (1, 0), ...: a
+        // weight fragment serves two consecutive tiles and is read one tile
+        // pair ahead; a tile's row scales are read from LDS four at a time
+        // as it is dequantized (two distinct addresses per read: broadcast).
+        // The MFMA of tile u + 1 is issued before tile u is dequantized
+        // (results in a ring of two).
+        const float* sxp = cv + F_BM * hg + 64 * wm + 4 * h;
+        v8i afr[2];
+        afr[0] = rd_frag(a_off);
+        afr[1] = rd_frag(a_off + FRAG);
+        v8i bfr[4];
+        bfr[0] = rd_frag(b_off);
+        v16f dr[2];
 #pragma unroll
-          for (int b = 0; b < 4; ++b) {
-            const float4 s4 = *reinterpret_cast<const float4*>(sxp + 32 * a + 8 * b);
-            const float sv[4] = {s4.x, s4.y, s4.z, s4.w};
+        for (int u = 0; u < 9; ++u) {
+          if (u < 8) {
+            const int t = u >> 1, a = u & 1;
+            if (a == 0 && t < 3) bfr[t + 1] = rd_frag(b_off + (t + 1) * FRAG);
+            // cbsz = blgp = 3: both operands E3M2; E8M0 scales 127 (= 1)
+            dr[u & 1] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(afr[a], bfr[t], zero, 3, 3, 0, 127, 0, 127);
+          }
+          if (u > 0) {
+            const int v = u - 1, t = v >> 1, a = v & 1;
 #pragma unroll
-            for (int i = 0; i < 4; ++i) {
-              const int e = 4 * b + i;
-              acc[a][t][e] = __builtin_fmaf(dr[v & 1][e] * sv[i], swv[t], acc[a][t][e]);
+            for (int b = 0; b < 4; ++b) {
+              const float4 s4 = *reinterpret_cast<const float4*>(sxp + 32 * a + 8 * b);
+              const float sv[4] = {s4.x, s4.y, s4.z, s4.w};
+#pragma unroll
+              for (int i = 0; i < 4; ++i) {
+                const int e = 4 * b + i;
+                acc[a][t][e] = __builtin_fmaf(dr[v & 1][e] * sv[i], swv[t], acc[a][t][e]);
+              }
             }
           }
         }
       }
     }
 
-    // ---- the up projection, 16 ranks per stage; padding stages ----
-    for (int l = G; l < SPT; ++l, stage_end()) {
+    // ---- the up projection, two 16-rank chunks per stage; padding stages ----
+    for (int l = GS; l < SPT; ++l, stage_end()) {
       stage_top();
-      const unsigned char* sl = ring[sc];
-      if (l < G + NR) {
+#pragma unroll
+      for (int hh = 0; hh < 2; ++hh) {
+        if (2 * (l - GS) + hh >= NR) break;
+        const unsigned char* sl = ring[sc] + F_HALF * hh;
         // A = bf16(lora_act) rows (lane row l % 32 of m tile a, ranks
         // 8h .. 8h + 7 of the chunk), B = lora_up rows (columns
         // n_w + 4 (l % 32) + t, the same ranks); products into a ring of
@@ -428,17 +498,15 @@ __global__ __launch_bounds__(F_THREADS, 1) void k_gemm_w4a4_fp6(
 
     // ---- end of the tile, after its last stage ----
     {
-      // The stage's slot still holds the tile's bias (every stage carries
-      // its tile's bias; slot (s - 1) % F_NS is reused only after the next
-      // barrier).
-      const unsigned char* sl = ring[sc == 0 ? F_NS - 1 : sc - 1];
+      // The bias ring entry of tile j is rewritten only by the stages of
+      // tile j + 2, issued after the next barrier.
       // end of the tile: bias, rounding, store.  The lane holds rows
       // mw + 32 a + 8 b + 4 h + i and columns cw + 4 c .. + 3; rows past M
       // fall past the end of y, columns past N (N % 8 == 0: a lane's four
       // are all in or all out) are sent past it.
       const int ln = fresh_lane();
       const int lc = ln & 31, lh = ln >> 5;
-      const uint2 bu = *reinterpret_cast<const uint2*>(sl + F_BIAS + 2 * (128 * wn + 4 * lc));
+      const uint2 bu = *reinterpret_cast<const uint2*>(&bias_ring[j & 1][128 * wn + 4 * lc]);
       const float bv[4] = {bf16_bits_to_f32(bu.x & 0xFFFFu), bf16_bits_to_f32(bu.x >> 16),
                            bf16_bits_to_f32(bu.y & 0xFFFFu), bf16_bits_to_f32(bu.y >> 16)};
       // one per-lane base (row mw + 4 h, columns cw + 4 c); each store adds
@@ -505,6 +573,7 @@ int launch_gemm_w4a4_fp6(const void* x_fp6, const void* x_scales, const void* w_
   // tiles stay on its XCD; never more blocks than tiles
   const int cus = cu_count() & ~7;
   const int grid = tiles < cus ? tiles : (cus > 0 ? cus : tiles);
+  if ((tiles + grid - 1) / grid > F_MAX_TILES) return SVDQ_ERR_UNSUPPORTED_SHAPE;
 #define SVDQ_K2F(OF)                                                                                          \
   hipLaunchKernelGGL((k_gemm_w4a4_fp6<OF>), dim3(grid), dim3(F_THREADS), 0, st,                               \
                      static_cast<const uint8_t*>(x_fp6), static_cast<const _Float16*>(x_scales),              \
