@@ -407,51 +407,59 @@ __global__ __launch_bounds__(F_THREADS, 1) void k_gemm_w4a4_fp6(
     // ---- the tile's groups: P_g on the 6-bit MFMA, then dequantization ----
     for (int l = 0; l < GS; ++l, stage_end()) {
       stage_top();
+      // The stage's 16 tiles (two groups x 8) in one sequence u = 0..15:
+      // group u / 8, then (n tile 0, m tile 0), (0, 1), (1, 0), ...  A
+      // weight fragment serves two consecutive tiles and is read one tile
+      // pair ahead; the second group's first fragments are read right after
+      // the MFMA that last uses the first group's.  A tile's row scales are
+      // read from LDS four at a time as it is dequantized (two distinct
+      // addresses per read: broadcast).  The MFMA of tile u + 1 is issued
+      // before tile u is dequantized (results in a ring of two).  When K / 64
+      // is odd the last stage's second group is all zero codes and zero
+      // scales and adds nothing.
+      const unsigned char* sl = ring[sc];
+      const float* cv = conv[s & 1];
+      auto rd_frag = [&](uint32_t off) {
+        const uint4 lo = *reinterpret_cast<const uint4*>(sl + off);
+        const uint2 hi = *reinterpret_cast<const uint2*>(sl + off + 1024 - 8 * lane);
+        return v8i{static_cast<int>(lo.x), static_cast<int>(lo.y), static_cast<int>(lo.z), static_cast<int>(lo.w),
+                   static_cast<int>(hi.x), static_cast<int>(hi.y), 0, 0};
+      };
+      v8i afr[2];
+      afr[0] = rd_frag(a_off);
+      afr[1] = rd_frag(a_off + FRAG);
+      v8i bfr[4];
+      bfr[0] = rd_frag(b_off);
+      v16f dr[2];
+      float swv[4];
 #pragma unroll
-      for (int hg = 0; hg < 2; ++hg) {
-        if (hg == 1 && 2 * l + 1 >= G) break;                 // K / 64 odd: the last stage holds one group
-        const unsigned char* sl = ring[sc] + F_HALF * hg;
-        const float* cv = conv[s & 1];
-        const float4 sw = *reinterpret_cast<const float4*>(cv + F_GPS * F_BM + F_BN * hg + 128 * wn + 4 * c);
-        const float swv[4] = {sw.x, sw.y, sw.z, sw.w};
-        auto rd_frag = [&](uint32_t off) {
-          const uint4 lo = *reinterpret_cast<const uint4*>(sl + off);
-          const uint2 hi = *reinterpret_cast<const uint2*>(sl + off + 1024 - 8 * lane);
-          return v8i{static_cast<int>(lo.x), static_cast<int>(lo.y), static_cast<int>(lo.z), static_cast<int>(lo.w),
-                     static_cast<int>(hi.x), static_cast<int>(hi.y), 0, 0};
-        };
-        // Tiles in the order (n tile 0, m tile 0), (0, 1), (1, 0), ...: a
-        // weight fragment serves two consecutive tiles and is read one tile
-        // pair ahead; a tile's row scales are read from LDS four at a time
-        // as it is dequantized (two distinct addresses per read: broadcast).
-        // The MFMA of tile u + 1 is issued before tile u is dequantized
-        // (results in a ring of two).
-        const float* sxp = cv + F_BM * hg + 64 * wm + 4 * h;
-        v8i afr[2];
-        afr[0] = rd_frag(a_off);
-        afr[1] = rd_frag(a_off + FRAG);
-        v8i bfr[4];
-        bfr[0] = rd_frag(b_off);
-        v16f dr[2];
-#pragma unroll
-        for (int u = 0; u < 9; ++u) {
-          if (u < 8) {
-            const int t = u >> 1, a = u & 1;
-            if (a == 0 && t < 3) bfr[t + 1] = rd_frag(b_off + (t + 1) * FRAG);
-            // cbsz = blgp = 3: both operands E3M2; E8M0 scales 127 (= 1)
-            dr[u & 1] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(afr[a], bfr[t], zero, 3, 3, 0, 127, 0, 127);
+      for (int u = 0; u < 17; ++u) {
+        if (u < 16) {
+          const int hg = u >> 3, t = (u >> 1) & 3, a = u & 1;
+          if (a == 0 && t < 3) bfr[t + 1] = rd_frag(F_HALF * hg + b_off + (t + 1) * FRAG);
+          // cbsz = blgp = 3: both operands E3M2; E8M0 scales 127 (= 1)
+          dr[u & 1] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(afr[a], bfr[t], zero, 3, 3, 0, 127, 0, 127);
+          if (u == 7) {
+            afr[0] = rd_frag(F_HALF + a_off);
+            afr[1] = rd_frag(F_HALF + a_off + FRAG);
+            bfr[0] = rd_frag(F_HALF + b_off);
           }
-          if (u > 0) {
-            const int v = u - 1, t = v >> 1, a = v & 1;
+        }
+        if (u > 0) {
+          const int v = u - 1, hv = v >> 3, t = (v >> 1) & 3, a = v & 1;
+          if ((v & 7) == 0) {
+            const float4 sw = *reinterpret_cast<const float4*>(cv + F_GPS * F_BM + F_BN * hv + 128 * wn + 4 * c);
+            swv[0] = sw.x; swv[1] = sw.y; swv[2] = sw.z; swv[3] = sw.w;
+          }
+          const float* sxp = cv + F_BM * hv + 64 * wm + 4 * h;
 #pragma unroll
-            for (int b = 0; b < 4; ++b) {
-              const float4 s4 = *reinterpret_cast<const float4*>(sxp + 32 * a + 8 * b);
-              const float sv[4] = {s4.x, s4.y, s4.z, s4.w};
+          for (int b = 0; b < 4; ++b) {
+            const float4 s4 = *reinterpret_cast<const float4*>(sxp + 32 * a + 8 * b);
+            const float sv[4] = {s4.x, s4.y, s4.z, s4.w};
 #pragma unroll
-              for (int i = 0; i < 4; ++i) {
-                const int e = 4 * b + i;
-                acc[a][t][e] = __builtin_fmaf(dr[v & 1][e] * sv[i], swv[t], acc[a][t][e]);
-              }
+            for (int i = 0; i < 4; ++i) {
+              const int e = 4 * b + i;
+              acc[a][t][e] = __builtin_fmaf(dr[v & 1][e] * sv[i], swv[t], acc[a][t][e]);
             }
           }
         }
