@@ -8,11 +8,16 @@ dequant + up projection + bias), on the FLUX MLP up-projection layer
 says otherwise.  Weight preparation (smoothing, SVD, 4-bit residual) is a
 one-time offline transform and runs before the timed region.
 
-Prints one JSON line.  value = effective TOPS = 2*M*N*K / (time per step);
-the low-rank flops are not credited.  --precision int4 (default) measures
-the INT4 layer (group 64, fp16 scales); the same line carries the MXFP4
-variant (E2M1 codes, E8M0 scale per 32, block-scaled FP4 MFMA) measured on
-the same workload, unless --no-variants.
+The INT4 layer runs on one of two engines: "fp6" (default; the INT4 codes in
+E3M2 containers on the 6-bit float MFMA) or "int8" (nibble codes on the int8
+MFMA); both compute the same layer.  Prints one JSON line.  value = effective
+TOPS = 2*M*N*K / (time per step); the low-rank flops are not credited.  The
+line also carries, each timed here: the int8 engine on the same layer, the
+tiny layer (µs), the attention-output projection, the MLP down projection
+with tanh-GELU fused into kernel 1, the batched rank sweep (ranks 0..128:
+overhead per rank and error against fp64 X W), the MXFP4 variant, the fused
+QKV epilogue, the AWQ modulation GEMV, the measured peaks and the CPU oracle
+baseline (skip groups with the --no-* flags).
 """
 from __future__ import annotations
 
@@ -20,6 +25,7 @@ import argparse
 import hashlib
 import json
 import os
+import platform
 import sys
 import time
 
@@ -55,10 +61,21 @@ def settle(step, seconds=SETTLE_S):
 # name -> (generator workload, layer index, act, description)
 BENCH_WORKLOADS = {
     "mlp_up": ("mlp_pair", 0, "none", "FLUX MLP up-projection 4096x3072x12288"),
+    "mlp_down": ("mlp_pair", 1, "gelu_tanh", "FLUX MLP down-projection 4096x12288x3072 (tanh-GELU in kernel 1)"),
     "attn_out": ("attn_out", 0, "none", "FLUX attention-output projection 4096x3072x3072"),
     "joint_qkv": ("joint_qkv", 0, "none", "FLUX joint-stream fused QKV 4608x3072x9216 (+bias)"),
     "rank_sweep": ("rank_sweep", 0, "none", "4 images x 4096 tokens, 16384x3072x12288"),
+    "tiny": ("tiny", 0, "none", "single linear 256x512x512"),
 }
+
+# kernel-2 sources per engine: the stored traffic figures of an engine stay
+# valid while these are unchanged
+ENGINE_SOURCES = {
+    "fp6": ("svdq_fp6_kernels.hip", "svdq_device.h"),
+    "int8": ("svdq_kernels.hip", "svdq_device.h"),
+    "mxfp4": ("svdq_mx_kernels.hip", "svdq_device.h"),
+}
+K2_KERNEL = {"fp6": "k_gemm_w4a4_fp6", "int8": "k_gemm_w4a4_lora_up", "mxfp4": "k_gemm_mxfp4_lora_up"}
 
 
 def code_tokens(src: str) -> str:
@@ -69,11 +86,12 @@ def code_tokens(src: str) -> str:
     return " ".join(src.split())
 
 
-def kernel_source_hash() -> str:
-    """Hash of the kernel sources with comments and whitespace removed, so
-    that the stored counter figures stay valid across comment-only edits."""
+def kernel_source_hash(engine: str = "fp6") -> str:
+    """Hash of an engine's kernel-2 sources with comments and whitespace
+    removed, so that the stored counter figures stay valid across
+    comment-only edits."""
     h = hashlib.sha256()
-    for f in ("svdq_kernels.hip", "svdq_mx_kernels.hip", "svdq_device.h"):
+    for f in ENGINE_SOURCES[engine]:
         src = open(os.path.join(ROOT, "w4a4_rank_corrected_svdq_amd", "csrc", f)).read()
         h.update(code_tokens(src).encode())
     return h.hexdigest()[:16]
@@ -86,65 +104,100 @@ def scale_bytes(K, precision):
 
 def k1_bytes(M, K, r, precision="int4"):
     """Compulsory HBM bytes of kernel 1: read X (bf16), smooth_inv, L1; write
-    codes, scales and lora_act."""
+    codes (4 bits each), scales and lora_act."""
     return 2 * M * K + 4 * K + 2 * r * K + M * K // 2 + scale_bytes(K, precision) * M + 4 * M * r
 
 
 def k2_bytes(M, N, K, r, bias, precision="int4"):
+    """Compulsory HBM bytes of kernel 2: codes (4 bits), scales, lora_act,
+    lora_up, bias; write Y (bf16)."""
     sb = scale_bytes(K, precision)
     return (M * K // 2 + sb * M + N * K // 2 + sb * N + 4 * M * r
             + 2 * N * r + (2 * N if bias else 0) + 2 * M * N)
 
 
-def load_traffic(workload: str, rank: int, precision: str = "int4"):
+def fp6_container_bytes(M, N, K):
+    """Bytes of the 6-bit route's code containers (6 bits per code, rows
+    padded to 32 activations / 128 weights) and padded activation scales."""
+    G = K // 64
+    RBa, RBb = (M + 31) // 32, 4 * ((N + 127) // 128)
+    return {"x_codes": G * RBa * 1536, "x_scales": G * 32 * RBa * 2, "w_codes": G * RBb * 1536}
+
+
+def load_traffic(workload: str, rank: int, engine: str = "fp6"):
     """HBM traffic of kernel 2 measured by rocprofv3 PMC counters (committed
-    under profiles/), used only while the kernel source is unchanged."""
-    tag = "" if precision == "int4" else f"_{precision}"
-    p = os.path.join(ROOT, "profiles", f"traffic_{workload}_r{rank}{tag}.json")
+    under profiles/), used only while the engine's kernel source is
+    unchanged."""
+    p = os.path.join(ROOT, "profiles", f"traffic_{workload}_r{rank}_{engine}.json")
     if not os.path.exists(p):
         return None
     d = json.load(open(p))
-    if d.get("kernel_source_sha") != kernel_source_hash():
+    if d.get("kernel_source_sha") != kernel_source_hash(engine):
         return None
     return d.get("k2_hbm_bytes")
 
 
-def cpu_baseline(wl, layer, rank, target_s, precision="int4"):
-    """The oracle (as it stands) on a bounded sample of rows of the same
-    workload, timed on this host's cores."""
-    import oracle as O
+def cpu_model() -> str:
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return platform.processor() or "unknown"
+
+
+def blas_info():
     try:
         from threadpoolctl import threadpool_info
-        threads = max([d.get("num_threads", 1) for d in threadpool_info()] + [1])
+        return [{k: d.get(k) for k in ("internal_api", "version", "num_threads", "threading_layer")}
+                | {"library": os.path.basename(d.get("filepath", ""))}
+                for d in threadpool_info() if d.get("user_api") == "blas"]
     except Exception:  # pragma: no cover
-        threads = os.cpu_count()
+        return []
+
+
+def cpu_baseline(wl, layer, rank, target_s, precision="int4"):
+    """The oracle (as it stands) on a bounded sample of rows of the same
+    workload, timed on this host's cores: once with the BLAS thread pool as
+    configured, once limited to one thread."""
+    import oracle as O
+    from threadpoolctl import threadpool_limits
+    blas = blas_info()
+    threads = max([b.get("num_threads") or 1 for b in blas] + [1])
     Lr = wl.layers[layer]
     K, N = Lr.K, Lr.N
     a = wl.act_absmax()
-    # preparation needs the SVD; rank-r factors from the oracle's own split
     t0 = time.perf_counter()
     po = O.prepare(Lr.weight, a, rank=rank) if precision == "int4" else O.mx.prepare_mx(Lr.weight, a, rank=rank)
     fwd = O.forward if precision == "int4" else O.mx.forward_mx
     t_prep = time.perf_counter() - t0
-    # chunks of 128 rows, in order, wrapping round the workload's rows until
-    # about target_s of forward time (at most four passes)
-    rows_per_chunk = 128
-    done_rows = 0
-    t_fwd = 0.0
-    x = wl.x
-    while t_fwd < target_s and done_rows < 4 * wl.M:
-        start = done_rows % wl.M
-        xr = x[start:start + rows_per_chunk]
-        t0 = time.perf_counter()
-        fwd(xr, po, bias=Lr.bias)
-        t_fwd += time.perf_counter() - t0
-        done_rows += xr.shape[0]
-    tops = 2.0 * done_rows * N * K / t_fwd / 1e12
+
+    def timed_rows(budget_s, max_passes):
+        # chunks of 128 rows, in order, wrapping round the workload's rows
+        rows_per_chunk, done, t_fwd = 128, 0, 0.0
+        while t_fwd < budget_s and done < max_passes * wl.M:
+            start = done % wl.M
+            xr = wl.x[start:start + rows_per_chunk]
+            t1 = time.perf_counter()
+            fwd(xr, po, bias=Lr.bias)
+            t_fwd += time.perf_counter() - t1
+            done += xr.shape[0]
+        return done, t_fwd
+
+    rows, t_fwd = timed_rows(target_s, 4)
+    with threadpool_limits(limits=1, user_api="blas"):
+        rows1, t_fwd1 = timed_rows(target_s / 3, 1)
+    tops = 2.0 * rows * N * K / t_fwd / 1e12
     return {"value": tops, "unit": "TOPS", "cores": int(threads), "kind": "oracle",
-            "sample": f"oracle forward ({precision}, fp64 numpy emulation) on {done_rows} rows (128-row chunks "
-                      f"taken in order from the workload's {wl.M}, wrapping round), {t_fwd:.1f} s; oracle "
-                      f"prepare (LAPACK SVD) took {t_prep:.1f} s and is not counted",
-            "host_cpu_count": os.cpu_count()}
+            "sample": f"oracle forward ({precision}, fp64 numpy emulation) on {rows} rows (128-row chunks "
+                      f"taken in order from the workload's {wl.M}, wrapping round), {t_fwd:.1f} s",
+            "single_thread": {"value": 2.0 * rows1 * N * K / t_fwd1 / 1e12, "unit": "TOPS",
+                              "rows": rows1, "seconds": round(t_fwd1, 2)},
+            "prepare_s": round(t_prep, 2),
+            "prepare": "oracle prepare of the layer (LAPACK SVD), not counted in value",
+            "cpu_model": cpu_model(), "blas": blas, "host_cpu_count": os.cpu_count()}
 
 
 def bench_qkv(S, L, workloads, r, steps, warmup):
@@ -156,7 +209,8 @@ def bench_qkv(S, L, workloads, r, steps, warmup):
     Lr = wl.layers[0]
     M, K, N = wl.M, Lr.K, Lr.N
     prep = S.prepare_weights(Lr.weight_bits, wl.act_absmax(), rank=r)
-    lin = S.SVDQW4A4Linear(prep, torch.from_numpy(Lr.bias_bits.view(np.int16).copy()).view(torch.bfloat16), "cuda")
+    lin = S.SVDQW4A4Linear(prep, torch.from_numpy(Lr.bias_bits.view(np.int16).copy()).view(torch.bfloat16), "cuda",
+                           engine="int8")
     (qb, _), (kb, _) = workloads.norm_weights()
     cos, sin = workloads.rope_tables(512, 64)
     gq = torch.from_numpy(qb.view(np.int16).copy()).view(torch.bfloat16).cuda()
@@ -284,37 +338,210 @@ SWEEP_RANKS = (0, 16, 32, 64, 128)
 SWEEP_ROWS = 64
 
 
-def rank_sweep(wl, Lr, desc, build_layer, run, x, M, K, N, args):
-    """Step time per rank and the relative Frobenius error of the layer's
-    bf16 output against fp64 X W^T on SWEEP_ROWS seeded rows (rank 0 is
-    plain smoothed W4A4)."""
+class Runner:
+    """One layer's forward step on one engine with preallocated buffers:
+    "fp6", "int8" and "mxfp4" run kernel 1 then kernel 2; "unfused" runs
+    the int8 engine at rank 0, then the separate down projection (re-reads x)
+    and up projection (reads and rewrites y)."""
+
+    def __init__(self, S, lin, x, act_id, engine):
+        import torch
+        self.S, self.lin, self.x, self.act, self.engine = S, lin, x, act_id, engine
+        M, K = x.shape
+        N, r = lin.N, lin.rank
+        self.M, self.N, self.K = M, N, K
+        dev = "cuda"
+        self.la = torch.empty((M, r), dtype=torch.float32, device=dev) if r else None
+        self.y = torch.empty((M, N), dtype=torch.bfloat16, device=dev)
+        if engine == "fp6":
+            G, RB = K // 64, (M + 31) // 32
+            self.xc = torch.empty((G, RB, 1536), dtype=torch.uint8, device=dev)
+            self.xs = torch.empty((G, 32 * RB), dtype=torch.float16, device=dev)
+            if lin.w_fp6 is None:
+                raise ValueError("the layer holds no 6-bit weight container")
+        elif engine == "mxfp4":
+            self.xc = torch.empty((M, K // 2), dtype=torch.uint8, device=dev)
+            self.xs = torch.empty((M, K // 32), dtype=torch.uint8, device=dev)
+        else:
+            self.xc = torch.empty((M, K // 2), dtype=torch.uint8, device=dev)
+            self.xs = torch.empty((K // 64, M), dtype=torch.float16, device=dev)
+
+    def step(self, mid=None):
+        S, lin, x, M, N, K, r = self.S, self.lin, self.x, self.M, self.N, self.K, self.lin.rank
+        if self.engine == "unfused":
+            S.quant_act_lora_down(x, lin.smooth_inv, None, 0, act=self.act, out=(self.xc, self.xs, None))
+            S.gemm_w4a4_lora_up(self.xc, self.xs, lin.w_codes, lin.w_scales, None, None, lin.bias, M, N, K, 0,
+                                out=self.y)
+            S.lora_down(x, lin.smooth_inv, lin.lora_down, r, act=self.act, out=self.la)
+            S.lora_up_add(self.la, lin.lora_up, self.y)
+            return
+        if self.engine == "fp6":
+            S.quant_act_lora_down_fp6(x, lin.smooth_inv, lin.lora_down, r, act=self.act, out=(self.xc, self.xs, self.la))
+            if mid is not None:
+                mid.record()
+            S.gemm_w4a4_fp6_lora_up(self.xc, self.xs, lin.w_fp6, lin.w_scales, self.la, lin.lora_up, lin.bias,
+                                    M, N, K, r, out=self.y)
+        elif self.engine == "mxfp4":
+            S.quant_act_lora_down_mxfp4(x, lin.smooth_inv, lin.lora_down, r, act=self.act, out=(self.xc, self.xs, self.la))
+            if mid is not None:
+                mid.record()
+            S.gemm_mxfp4_lora_up(self.xc, self.xs, lin.w_codes, lin.w_scales, self.la, lin.lora_up, lin.bias,
+                                 M, N, K, r, out=self.y)
+        else:
+            S.quant_act_lora_down(x, lin.smooth_inv, lin.lora_down, r, act=self.act, out=(self.xc, self.xs, self.la))
+            if mid is not None:
+                mid.record()
+            S.gemm_w4a4_lora_up(self.xc, self.xs, lin.w_codes, lin.w_scales, self.la, lin.lora_up, lin.bias,
+                                M, N, K, r, out=self.y)
+
+    def time(self, steps, warmup, events=True, cold_iters=0):
+        """Wall time of `steps` back-to-back steps after the settle phase and
+        `warmup` steps; then (events) a second pass of the same length with
+        HIP events around each kernel for the breakdown, and (cold_iters)
+        single steps each after evicting the Infinity Cache."""
+        import torch
+        settle(self.step)
+        for _ in range(warmup):
+            self.step()
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for _ in range(steps):
+            self.step()
+        torch.cuda.synchronize()
+        res = {"wall_s": time.perf_counter() - t0, "ms": (time.perf_counter() - t0) * 1e3 / steps}
+        if events and self.engine != "unfused":
+            ev = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(steps)]
+            for i in range(steps):
+                ev[i][0].record()
+                self.step(ev[i][1])
+                ev[i][2].record()
+            torch.cuda.synchronize()
+            res["k1_ms"] = float(np.mean([e[0].elapsed_time(e[1]) for e in ev]))
+            res["k2_ms"] = float(np.mean([e[1].elapsed_time(e[2]) for e in ev]))
+        if cold_iters:
+            # writing 1 GiB first evicts the 256 MB Infinity Cache, so codes,
+            # scales and X come from HBM; the write is outside each step's
+            # events
+            scratch = torch.empty(COLD_EVICT_BYTES, dtype=torch.uint8, device="cuda")
+            cev = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(cold_iters)]
+            for i in range(cold_iters):
+                scratch.fill_(i & 0xFF)
+                cev[i][0].record()
+                self.step()
+                cev[i][1].record()
+            torch.cuda.synchronize()
+            res["cold_ms"] = float(np.median([e[0].elapsed_time(e[1]) for e in cev]))
+            del scratch
+        return res
+
+
+def figures(res, M, N, K, r, bias, engine, workload=None):
+    """Step rate, kernel-2 roofline (MFMA) and kernel-1 roofline (HBM) of a
+    timed step."""
+    ops = 2.0 * M * N * K
+    precision = "mxfp4" if engine == "mxfp4" else "int4"
+    out = {"ms_per_step": round(res["ms"], 5), "value": round(ops / (res["ms"] * 1e-3) / 1e12, 2)}
+    if "k2_ms" in res:
+        k2_rate = ops / (res["k2_ms"] * 1e-3) / 1e12
+        k1_gbs = k1_bytes(M, K, r, precision) / (res["k1_ms"] * 1e-3) / 1e9
+        peak, unit = (FP4_PEAK_TFLOPS, "TFLOP/s") if engine == "mxfp4" else (INT8_PEAK_TOPS, "TOPS")
+        out["roofline"] = {"bound": "mfma", "kernel": K2_KERNEL[engine], "achieved": round(k2_rate, 2),
+                           "peak": peak, "unit": unit, "frac": round(k2_rate / peak, 4),
+                           "traffic": load_traffic(workload, r, engine) if workload else None,
+                           "avg_launch_us": round(res["k2_ms"] * 1e3, 2), "algorithmic_ops_per_launch": ops,
+                           "algorithmic_hbm_bytes_per_launch": k2_bytes(M, N, K, r, bias, precision)}
+        k1 = {"bound": "hbm", "kernel": "k_quant_act_lora_down" + (" (6-bit container output)" if engine == "fp6" else ""),
+              "achieved": round(k1_gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+              "frac": round(k1_gbs / HBM_PEAK_GBS, 4), "avg_launch_us": round(res["k1_ms"] * 1e3, 2),
+              "algorithmic_bytes_per_launch": k1_bytes(M, K, r, precision)}
+        if engine == "fp6":
+            cb = fp6_container_bytes(M, N, K)
+            k1["container_bytes_per_launch"] = (k1_bytes(M, K, r) - M * K // 2 - scale_bytes(K, "int4") * M
+                                                + cb["x_codes"] + cb["x_scales"])
+        out["roofline_k1"] = k1
+    if "cold_ms" in res:
+        out["cold"] = {"ms_per_step": round(res["cold_ms"], 5), "value": round(ops / (res["cold_ms"] * 1e-3) / 1e12, 2),
+                       "steps": COLD_ITERS, "evict_bytes": COLD_EVICT_BYTES,
+                       "how": "median of single steps, each after writing a 1 GiB buffer that evicts the "
+                              "256 MB Infinity Cache (step time between HIP events, the write excluded)"}
+    return out
+
+
+def make_layer(S, weight_bits, act_absmax, rank, bias_bits=None, precision="int4", factors=None, engine="fp6"):
     import torch
-    import workloads
+    if precision == "mxfp4":
+        prep = S.prepare_weights_mxfp4(weight_bits, act_absmax, rank=rank)
+    else:
+        prep = S.prepare_weights(weight_bits, act_absmax, rank=rank, factors=factors)
+    bias = None
+    if bias_bits is not None:
+        bias = torch.from_numpy(bias_bits.view(np.int16).copy()).view(torch.bfloat16)
+    return S.SVDQW4A4Linear(prep, bias, "cuda", engine=engine), prep
+
+
+def dev_bf16(bits):
+    import torch
+    return torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).view(torch.bfloat16).cuda()
+
+
+def layer_input(S, wl, layer, act, rank):
+    """The layer's bf16 input on the device and its calibration statistic
+    max |input| per channel (after tanh-GELU when kernel 1 applies it).
+    The MLP down projection's input is the up projection's output on the
+    6-bit engine."""
+    import torch
+    if layer == 0:
+        x = dev_bf16(wl.x_bits)
+        a = wl.act_absmax()
+    else:
+        up, _ = make_layer(S, wl.layers[0].weight_bits, wl.act_absmax(), rank)
+        x = up(dev_bf16(wl.x_bits))
+        torch.cuda.synchronize()
+        del up
+        a = x.float().abs().amax(0).cpu().numpy()
+    if act == "gelu_tanh":
+        a = torch.nn.functional.gelu(x.float(), approximate="tanh").abs().amax(0).cpu().numpy()
+    return x, np.asarray(a, np.float32)
+
+
+def rank_sweep(S, workloads, steps, warmup):
+    """The batched layer (4 x 4096 tokens, 3072 -> 12288) on the 6-bit
+    engine at ranks 0, 16, 32, 64, 128: step time, overhead against rank 0,
+    and the relative Frobenius error of the bf16 output against fp64 X W^T on
+    SWEEP_ROWS seeded rows.  One rank-128 split of the smoothed weight is
+    truncated per rank (the residual is recomputed per rank)."""
+    import torch
+    wl = workloads.make_workload("rank_sweep")
+    Lr = wl.layers[0]
+    M, K, N = wl.M, Lr.K, Lr.N
+    a = wl.act_absmax()
+    x = dev_bf16(wl.x_bits)
     rows = np.sort(np.random.default_rng(2024).choice(M, SWEEP_ROWS, replace=False))
     ref = workloads.bf16_bits_to_f64(wl.x_bits[rows]) @ Lr.weight.T
-    if Lr.bias is not None:
-        ref = ref + Lr.bias
+    t0 = time.perf_counter()
+    full = S.prepare_weights(Lr.weight_bits, a, rank=max(SWEEP_RANKS))
+    t_svd = time.perf_counter() - t0
     out = []
     for rr in SWEEP_RANKS:
-        lin = build_layer(rr)
-        res = run(lin, args.steps, args.warmup, events=True)
-        ms = res["wall_s"] * 1e3 / args.steps
+        fac = (full["lora_down"][:rr], full["lora_up"][:, :rr]) if rr else None
+        lin, _ = make_layer(S, Lr.weight_bits, a, rr, factors=fac)
+        res = Runner(S, lin, x, 0, "fp6").time(steps, warmup)
         y = lin(x)
         torch.cuda.synchronize()
         yr = y[torch.from_numpy(rows).cuda()].float().cpu().numpy().astype(np.float64)
         err = float(np.linalg.norm(yr - ref) / np.linalg.norm(ref))
-        out.append({"rank": rr, "ms_per_step": round(ms, 5),
-                    "effective_tops": round(2.0 * M * N * K / (ms * 1e-3) / 1e12, 2),
-                    "k1_us": round(res["k1_ms"] * 1e3, 1), "k2_us": round(res["k2_ms"] * 1e3, 1),
+        f = figures(res, M, N, K, rr, False, "fp6")
+        out.append({"rank": rr, "ms_per_step": f["ms_per_step"], "effective_tops": f["value"],
+                    "k1_us": f["roofline_k1"]["avg_launch_us"], "k2_us": f["roofline"]["avg_launch_us"],
                     "rel_fro_err_vs_fp64": round(err, 6)})
         del lin, y
     ms0 = out[0]["ms_per_step"]
     for o in out:
         o["overhead_vs_rank0"] = round(o["ms_per_step"] / ms0 - 1.0, 4)
-    return {"rank_sweep": {"workload": desc + f" ({args.precision})", "M": M, "K": K, "N": N,
-                           "steps": args.steps, "warmup": args.warmup, "settle_s": SETTLE_S,
-                           "sampled_rows": SWEEP_ROWS, "ranks": out,
-                           "context": "pages: an unfused rank-32 branch costs +57% latency (NVIDIA, model card)"}}
+    return {"workload": "4 images x 4096 tokens, 16384x3072x12288, 6-bit engine", "M": M, "K": K, "N": N,
+            "steps": steps, "warmup": warmup, "sampled_rows": SWEEP_ROWS, "svd_rank128_prepare_s": round(t_svd, 2),
+            "ranks": out,
+            "context": "pages: an unfused rank-32 branch costs +57% latency (NVIDIA, model card)"}
 
 
 def main():
@@ -327,15 +554,18 @@ def main():
     ap.add_argument("--precision", default="int4", choices=["int4", "mxfp4"],
                     help="int4: INT4 group 64 with fp16 scales (the headline layer); "
                          "mxfp4: E2M1 codes with E8M0 scales per 32 on the block-scaled FP4 MFMA")
-    ap.add_argument("--no-overhead", action="store_true", help="skip the rank-0 comparison run")
+    ap.add_argument("--engine", default="fp6", choices=["fp6", "int8"],
+                    help="engine of the INT4 layer: the 6-bit float MFMA (default) or the int8 MFMA")
+    ap.add_argument("--no-overhead", action="store_true", help="skip the rank-0 and unfused comparison runs")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-peaks", action="store_true", help="skip measuring the MFMA and copy peaks")
-    ap.add_argument("--no-variants", action="store_true", help="skip the MXFP4 variant run")
+    ap.add_argument("--no-variants", action="store_true",
+                    help="skip the int8 engine, MXFP4, QKV-epilogue and AWQ runs")
+    ap.add_argument("--no-configs", action="store_true",
+                    help="skip the tiny, attention-output, MLP-down and rank-sweep entries")
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
     ap.add_argument("--rank-sweep", action="store_true",
-                    help="instead of the bench line: the batched rank sweep (16384x3072x12288, ranks "
-                         "0/16/32/64/128) with step time, overhead against rank 0 and error against "
-                         "fp64 X W on sampled rows, as one JSON line")
+                    help="only the batched rank sweep (16384x3072x12288, ranks 0/16/32/64/128), as one JSON line")
     ap.add_argument("--copy-probe", type=int, default=0, metavar="MIB",
                     help="only run a plain device copy of MIB MiB (HBM counter calibration)")
     args = ap.parse_args()
@@ -369,183 +599,103 @@ def main():
     L.check(S.device_check(0), "device check")
 
     if args.rank_sweep:
-        args.workload = "rank_sweep"
+        print(json.dumps({"rank_sweep": rank_sweep(S, workloads, args.steps, args.warmup)}))
+        return
+
     gen_name, layer, act, desc = BENCH_WORKLOADS[args.workload]
     wl = workloads.make_workload(gen_name)
     Lr = wl.layers[layer]
     M, K, N, r = wl.M, Lr.K, Lr.N, args.rank
     act_id = L.SVDQ_ACT_GELU_TANH if act == "gelu_tanh" else L.SVDQ_ACT_NONE
-
-    prec = args.precision
-
-    def build_layer(rank):
-        if prec == "mxfp4":
-            prep = S.prepare_weights_mxfp4(Lr.weight_bits, wl.act_absmax(), rank=rank)
-        else:
-            prep = S.prepare_weights(Lr.weight_bits, wl.act_absmax(), rank=rank)
-        bias = None
-        if Lr.bias_bits is not None:
-            bias = torch.from_numpy(Lr.bias_bits.view(np.int16).copy()).view(torch.bfloat16)
-        return S.SVDQW4A4Linear(prep, bias, "cuda")
-
-    x = torch.from_numpy(wl.x_bits.view(np.int16).copy()).view(torch.bfloat16).cuda()
-
-    def run(lin, steps, warmup, events=False, unfused=False, cold_iters=0):
-        xc = torch.empty((M, K // 2), dtype=torch.uint8, device="cuda")
-        if lin.precision == "mxfp4":
-            xs = torch.empty((M, K // 32), dtype=torch.uint8, device="cuda")
-        else:
-            xs = torch.empty((K // 64, M), dtype=torch.float16, device="cuda")
-        la = torch.empty((M, lin.rank), dtype=torch.float32, device="cuda") if lin.rank else None
-        y = torch.empty((M, N), dtype=torch.bfloat16, device="cuda")
-
-        def step(mid=None):
-            if unfused:
-                # the low-rank branch as two extra passes: 4-bit path at
-                # rank 0, then down projection (re-reads x) and up
-                # projection (reads and rewrites y)
-                S.quant_act_lora_down(x, lin.smooth_inv, None, 0, act=act_id, out=(xc, xs, None))
-                S.gemm_w4a4_lora_up(xc, xs, lin.w_codes, lin.w_scales, None, None, lin.bias,
-                                    M, N, K, 0, out=y)
-                S.lora_down(x, lin.smooth_inv, lin.lora_down, lin.rank, act=act_id, out=la)
-                S.lora_up_add(la, lin.lora_up, y)
-                return
-            if lin.precision == "mxfp4":
-                S.quant_act_lora_down_mxfp4(x, lin.smooth_inv, lin.lora_down, lin.rank, act=act_id,
-                                            out=(xc, xs, la))
-                if mid is not None:
-                    mid.record()
-                S.gemm_mxfp4_lora_up(xc, xs, lin.w_codes, lin.w_scales, la, lin.lora_up, lin.bias,
-                                     M, N, K, lin.rank, out=y)
-                return
-            S.quant_act_lora_down(x, lin.smooth_inv, lin.lora_down, lin.rank, act=act_id, out=(xc, xs, la))
-            if mid is not None:
-                mid.record()
-            S.gemm_w4a4_lora_up(xc, xs, lin.w_codes, lin.w_scales, la, lin.lora_up, lin.bias,
-                                M, N, K, lin.rank, out=y)
-
-        settle(step)
-        for _ in range(warmup):
-            step()
-        # the timed steps carry no instrumentation; a second pass of the same
-        # length records HIP events around each kernel for the breakdown
-        torch.cuda.synchronize()
-        t0 = time.perf_counter()
-        for i in range(steps):
-            step()
-        torch.cuda.synchronize()
-        wall = time.perf_counter() - t0
-        res = {"wall_s": wall}
-        if events:
-            ev = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(steps)]
-            for i in range(steps):
-                ev[i][0].record()
-                step(ev[i][1])
-                ev[i][2].record()
-            torch.cuda.synchronize()
-            res["k1_ms"] = float(np.mean([e[0].elapsed_time(e[1]) for e in ev]))
-            res["k2_ms"] = float(np.mean([e[1].elapsed_time(e[2]) for e in ev]))
-        if cold_iters:
-            # cold steps: writing 1 GiB first evicts the 256 MB Infinity
-            # Cache, so codes, scales and X come from HBM; the write is
-            # outside each step's events
-            scratch = torch.empty(COLD_EVICT_BYTES, dtype=torch.uint8, device="cuda")
-            cev = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(cold_iters)]
-            for i in range(cold_iters):
-                scratch.fill_(i & 0xFF)
-                cev[i][0].record()
-                step()
-                cev[i][1].record()
-            torch.cuda.synchronize()
-            res["cold_ms"] = float(np.median([e[0].elapsed_time(e[1]) for e in cev]))
-            del scratch
-        return res
-
-    def measure(precision):
-        nonlocal prec
-        prec = precision
-        lin = build_layer(r)
-        res = run(lin, args.steps, args.warmup, events=True, cold_iters=COLD_ITERS)
-        ms = res["wall_s"] * 1e3 / args.steps
-        ops = 2.0 * M * N * K
-        k2_rate = ops / (res["k2_ms"] * 1e-3) / 1e12
-        k1_gbs = k1_bytes(M, K, r, precision) / (res["k1_ms"] * 1e-3) / 1e9
-        peak, unit = (INT8_PEAK_TOPS, "TOPS") if precision == "int4" else (FP4_PEAK_TFLOPS, "TFLOP/s")
-        kname = "k_gemm_w4a4_lora_up" if precision == "int4" else "k_gemm_mxfp4_lora_up"
-        return lin, ms, {
-            "value": ops / (ms * 1e-3) / 1e12,
-            "cold": {"ms_per_step": round(res["cold_ms"], 5), "value": round(ops / (res["cold_ms"] * 1e-3) / 1e12, 2),
-                     "steps": COLD_ITERS, "evict_bytes": COLD_EVICT_BYTES,
-                     "how": "median of single steps, each after writing a 1 GiB buffer that evicts the "
-                            "256 MB Infinity Cache (step time between HIP events, the write excluded)"},
-            "roofline": {"bound": "mfma", "kernel": kname,
-                         "achieved": round(k2_rate, 2), "peak": peak, "unit": unit,
-                         "frac": round(k2_rate / peak, 4), "traffic": load_traffic(args.workload, r, precision),
-                         "avg_launch_us": round(res["k2_ms"] * 1e3, 2),
-                         "algorithmic_ops_per_launch": ops,
-                         "algorithmic_hbm_bytes_per_launch": k2_bytes(M, N, K, r, Lr.bias_bits is not None,
-                                                                      precision)},
-            "roofline_k1": {"bound": "hbm", "kernel": "k_quant_act_lora_down",
-                            "achieved": round(k1_gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                            "frac": round(k1_gbs / HBM_PEAK_GBS, 4),
-                            "avg_launch_us": round(res["k1_ms"] * 1e3, 2),
-                            "algorithmic_bytes_per_launch": k1_bytes(M, K, r, precision)},
-        }
-
-    if args.rank_sweep:
-        print(json.dumps(rank_sweep(wl, Lr, desc, build_layer, run, x, M, K, N, args)))
-        return
-
-    lin, ms_per_step, main_m = measure(args.precision)
+    engine = "mxfp4" if args.precision == "mxfp4" else args.engine
+    x, a = layer_input(S, wl, layer, act, r)
+    M = x.shape[0]
+    has_bias = Lr.bias_bits is not None
+    lin, _ = make_layer(S, Lr.weight_bits, a, r, Lr.bias_bits, args.precision,
+                        engine="int8" if engine == "int8" else "fp6")
+    res = Runner(S, lin, x, act_id, engine).time(args.steps, args.warmup, cold_iters=COLD_ITERS)
+    main_m = figures(res, M, N, K, r, has_bias, engine, args.workload)
     value = main_m["value"]
     out = {
         "metric": METRIC,
-        "value": round(value, 2),
+        "value": value,
         "unit": "TOPS",
         "n_gpus": 1,
         "steps": args.steps,
         "warmup": args.warmup,
         "settle_s": SETTLE_S,
-        "ms_per_step": round(ms_per_step, 5),
+        "ms_per_step": main_m["ms_per_step"],
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "int4" if args.precision == "int4" else "fp4 (mxfp4)",
+        "dtype": "int4 codes on fp6 (e3m2) MFMA" if engine == "fp6" else ("int4" if engine == "int8" else "fp4 (mxfp4)"),
         "data": "synthetic",
-        "config": {"workload": f"{desc}, rank {r}, " + ("INT4 group 64" if args.precision == "int4"
-                                                        else "MXFP4 block 32"),
-                   "M": M, "K": K, "N": N, "rank": r, "precision": args.precision,
-                   "group": 64 if args.precision == "int4" else 32,
-                   "bias": Lr.bias_bits is not None, "parallelism": "single GPU"},
+        "config": {"workload": f"{desc}, rank {r}, " + ("INT4 group 64" if args.precision == "int4" else "MXFP4 block 32"),
+                   "M": M, "K": K, "N": N, "rank": r, "precision": args.precision, "engine": engine,
+                   "group": 64 if args.precision == "int4" else 32, "act": act,
+                   "bias": has_bias, "parallelism": "single GPU"},
         "pct_int8_peak": round(100.0 * value / INT8_PEAK_TOPS, 2),
         "roofline": main_m["roofline"],
         "roofline_k1": main_m["roofline_k1"],
         "cold": main_m["cold"],
     }
-    if not args.no_overhead and r > 0:
-        lin0 = build_layer(0)
-        res0 = run(lin0, args.steps, args.warmup, events=True)
-        ms0 = res0["wall_s"] * 1e3 / args.steps
-        ov = {"rank0_ms_per_step": round(ms0, 5), "overhead_frac": round(ms_per_step / ms0 - 1.0, 4)}
-        if args.precision == "int4":
-            resu = run(lin, args.steps, args.warmup, unfused=True)
-            msu = resu["wall_s"] * 1e3 / args.steps
-            ov.update(unfused_ms_per_step=round(msu, 5), unfused_overhead_frac=round(msu / ms0 - 1.0, 4))
-        ov["context"] = "pages: an unfused rank-32 branch costs +57% latency (NVIDIA, model card)"
-        out["low_rank_overhead"] = ov
+    if not args.no_overhead and r > 0 and args.precision == "int4":
+        lin0, _ = make_layer(S, Lr.weight_bits, a, 0, Lr.bias_bits, engine="fp6")
+        ms0 = Runner(S, lin0, x, act_id, engine).time(args.steps, args.warmup, events=False)["ms"]
+        ms0_int8 = Runner(S, lin0, x, act_id, "int8").time(args.steps, args.warmup, events=False)["ms"]
+        msu = Runner(S, lin, x, act_id, "unfused").time(args.steps, args.warmup, events=False)["ms"]
+        out["low_rank_overhead"] = {
+            "rank0_ms_per_step": round(ms0, 5), "overhead_frac": round(main_m["ms_per_step"] / ms0 - 1.0, 4),
+            "unfused_ms_per_step": round(msu, 5), "int8_rank0_ms_per_step": round(ms0_int8, 5),
+            "unfused_overhead_frac": round(msu / ms0_int8 - 1.0, 4),
+            "how": "overhead_frac: this engine at rank r against rank 0; unfused_overhead_frac: the int8 "
+                   "engine at rank 0 plus a separate down projection and a separate up projection "
+                   "(read-modify-write of y), against the int8 engine at rank 0",
+            "context": "pages: an unfused rank-32 branch costs +57% latency (NVIDIA, model card)"}
+        del lin0
     if args.precision == "int4" and not args.no_variants:
-        _, ms_mx, mx_m = measure("mxfp4")
-        out["mxfp4_variant"] = {"value": round(mx_m["value"], 2), "unit": "TFLOP/s (effective, 2MNK)",
-                                "ms_per_step": round(ms_mx, 5), "cold": mx_m["cold"], "roofline": mx_m["roofline"],
+        res8 = Runner(S, lin, x, act_id, "int8").time(args.steps, args.warmup)
+        f8 = figures(res8, M, N, K, r, has_bias, "int8", args.workload)
+        out["int8_engine"] = {"value": f8["value"], "ms_per_step": f8["ms_per_step"], "roofline": f8["roofline"],
+                              "roofline_k1": f8["roofline_k1"]}
+    configs = {}
+    if args.precision == "int4" and not args.no_configs:
+        for name in ("tiny", "attn_out", "mlp_down"):
+            gname, li, cact, cdesc = BENCH_WORKLOADS[name]
+            cw = workloads.make_workload(gname)
+            cL = cw.layers[li]
+            cact_id = L.SVDQ_ACT_GELU_TANH if cact == "gelu_tanh" else L.SVDQ_ACT_NONE
+            cx, ca = layer_input(S, cw, li, cact, r)
+            clin, _ = make_layer(S, cL.weight_bits, ca, r, cL.bias_bits)
+            cres = Runner(S, clin, cx, cact_id, "fp6").time(args.steps, args.warmup)
+            cM, cK, cN = cx.shape[0], cL.K, cL.N
+            f = figures(cres, cM, cN, cK, r, cL.bias_bits is not None, "fp6", name)
+            entry = {"workload": cdesc + f", rank {r}, 6-bit engine", "M": cM, "K": cK, "N": cN,
+                     "ms_per_step": f["ms_per_step"], "value": f["value"], "unit": "TOPS",
+                     "pct_int8_peak": round(100.0 * f["value"] / INT8_PEAK_TOPS, 2),
+                     "k1_us": f["roofline_k1"]["avg_launch_us"], "k2_us": f["roofline"]["avg_launch_us"],
+                     "roofline": f["roofline"]}
+            if name == "tiny":
+                entry["us_per_step"] = round(f["ms_per_step"] * 1e3, 2)
+            configs[name] = entry
+            del clin, cx
+        configs["rank_sweep"] = rank_sweep(S, workloads, args.steps, args.warmup)
+        out["configs"] = configs
+    if args.precision == "int4" and not args.no_variants:
+        lin_mx, _ = make_layer(S, Lr.weight_bits, a, r, Lr.bias_bits, "mxfp4")
+        resm = Runner(S, lin_mx, x, act_id, "mxfp4").time(args.steps, args.warmup, cold_iters=COLD_ITERS)
+        mx_m = figures(resm, M, N, K, r, has_bias, "mxfp4", args.workload)
+        out["mxfp4_variant"] = {"value": mx_m["value"], "unit": "TFLOP/s (effective, 2MNK)",
+                                "ms_per_step": mx_m["ms_per_step"], "cold": mx_m["cold"], "roofline": mx_m["roofline"],
                                 "roofline_k1": mx_m["roofline_k1"]}
-    if args.precision == "int4" and not args.no_variants:
+        del lin_mx
         out["qkv_fused_epilogue"] = bench_qkv(S, L, workloads, r, args.steps, args.warmup)
         out["awq_w4a16"] = bench_awq(S, workloads, max(args.steps, 20), args.warmup)
     if not args.no_peaks:
         # the same rooflines against the peaks measured on this device
         pk = measure_peaks()
         out["measured_peaks"] = pk
-        mfma_pk = pk["int8_mfma_tops"] if args.precision == "int4" else pk["fp4_mfma_tflops"]
+        mfma_pk = pk["fp4_mfma_tflops"] if engine == "mxfp4" else pk["int8_mfma_tops"]
         out["roofline"]["frac_of_measured_peak"] = round(out["roofline"]["achieved"] / mfma_pk, 4)
         out["roofline_k1"]["frac_of_measured_peak"] = round(out["roofline_k1"]["achieved"] / pk["hbm_copy_gbs"], 4)
         if "mxfp4_variant" in out:

@@ -21,8 +21,9 @@ def test_code_tokens_see_code_changes():
 
 
 def test_stored_traffic_files_name_a_source_hash():
-    for name in ("traffic_mlp_up_r32.json", "traffic_mlp_up_r32_mxfp4.json"):
+    for name in sorted(f for f in os.listdir(os.path.join(ROOT, "profiles")) if f.startswith("traffic_")):
         d = json.load(open(os.path.join(ROOT, "profiles", name)))
         assert len(d["kernel_source_sha"]) == 16
         assert d["fetch_size_kib_per_dispatch"] > 0 and d["write_size_kib_per_dispatch"] > 0
-    assert len(bench.kernel_source_hash()) == 16
+    for e in bench.ENGINE_SOURCES:
+        assert len(bench.kernel_source_hash(e)) == 16

@@ -28,13 +28,25 @@ def _to_dev(a: np.ndarray, device) -> torch.Tensor:
 
 class SVDQW4A4Linear:
     """One prepared layer.  ``precision`` is "int4" (group 64, fp16 scales)
-    or "mxfp4" (E2M1 codes, E8M0 scale per 32), as in the prepared dict."""
+    or "mxfp4" (E2M1 codes, E8M0 scale per 32), as in the prepared dict.
 
-    def __init__(self, prepared: dict, bias: Optional[torch.Tensor], device):
+    An int4 layer runs on one of two engines: "fp6" (default) feeds the INT4
+    codes to the 6-bit float MFMA in their E3M2 containers
+    (``svdq_quant_act_lora_down_fp6`` + ``svdq_gemm_w4a4_fp6_lora_up``;
+    the weights are re-packed once here), "int8" to the int8 MFMA from the
+    nibble layout (``svdq_quant_act_lora_down`` +
+    ``svdq_gemm_w4a4_lora_up``).  Both compute the same layer; the nibble
+    codes stay resident for the int8 engine, the unfused comparison path and
+    the fused QKV epilogue."""
+
+    def __init__(self, prepared: dict, bias: Optional[torch.Tensor], device, engine: str = "fp6"):
         dev = torch.device(device)
         self.precision = prepared.get("precision", "int4")
         if self.precision not in ("int4", "mxfp4"):
             raise ValueError(f"unknown precision {self.precision!r}")
+        if engine not in ("fp6", "int8"):
+            raise ValueError(f"unknown engine {engine!r}")
+        self.engine = engine if self.precision == "int4" else "mxfp4"
         self.K, self.N = prepared["K"], prepared["N"]
         self.rank, self.group = prepared["rank"], prepared["group"]
         self.smooth_inv = _to_dev(np.asarray(prepared["smooth_inv"], np.float32), dev)
@@ -44,10 +56,14 @@ class SVDQW4A4Linear:
         self.lora_down = _bits_to_bf16(prepared["lora_down"], dev) if self.rank else None
         self.lora_up = _bits_to_bf16(prepared["lora_up"], dev) if self.rank else None
         self.bias = None if bias is None else bias.detach().to(dev, torch.bfloat16).contiguous()
+        self.w_fp6 = None
+        if self.engine == "fp6":
+            codes = np.asarray(prepared["w_codes"], np.uint8).reshape(self.N, self.K // 2)
+            self.w_fp6 = _to_dev(ops.pack_fp6_operand(codes, L.SVDQ_FP6_WEIGHTS), dev)
 
     @classmethod
     def from_linear(cls, linear: torch.nn.Linear, act_absmax, rank: int = 32, group: int = 64,
-                    alpha: float = 0.5, device="cuda", precision: str = "int4"):
+                    alpha: float = 0.5, device="cuda", precision: str = "int4", engine: str = "fp6"):
         """Quantize a ``torch.nn.Linear`` (weight [out][in], bf16) given the
         calibration statistic ``act_absmax`` [in] (max |x| per input channel)."""
         w = linear.weight.detach().to(torch.bfloat16).cpu()
@@ -58,10 +74,14 @@ class SVDQW4A4Linear:
             prep = ops.prepare_weights(w, a, rank, group, alpha)
         else:
             raise ValueError(f"unknown precision {precision!r}")
-        return cls(prep, linear.bias, device)
+        return cls(prep, linear.bias, device, engine)
 
     def forward(self, x: torch.Tensor, act: int = L.SVDQ_ACT_NONE, out_dtype: int = L.SVDQ_OUT_BF16):
         M = x.shape[0]
+        if self.engine == "fp6":
+            xf, xs, la = ops.quant_act_lora_down_fp6(x, self.smooth_inv, self.lora_down, self.rank, self.group, act)
+            return ops.gemm_w4a4_fp6_lora_up(xf, xs, self.w_fp6, self.w_scales, la, self.lora_up, self.bias,
+                                             M, self.N, self.K, self.rank, self.group, out_dtype)
         if self.precision == "mxfp4":
             xc, xs, la = ops.quant_act_lora_down_mxfp4(x, self.smooth_inv, self.lora_down, self.rank, act)
             return ops.gemm_mxfp4_lora_up(xc, xs, self.w_codes, self.w_scales, la, self.lora_up, self.bias,
