@@ -478,16 +478,19 @@ def test_linear_module_with_oracle_prepared_arrays():
     check_y(to_np_bf16(y), O.forward(wl.x, po, bias=Lr.bias))
 
 
-def test_library_prepared_layer_against_oracle():
+@pytest.mark.parametrize("engine", ["fp6", "int8"])
+def test_library_prepared_layer_against_oracle(engine):
     """Library preparation (smoothing, SVD split, INT4 residual) feeding both
-    kernels, against the oracle's forward on the very arrays the library
-    prepared, at three ranks and with bias."""
+    kernels of either engine, against the oracle's forward on the very
+    arrays the library prepared, at three ranks and with bias."""
     for M, K, N, r in ((300, 512, 264, 32), (64, 1024, 520, 0), (129, 256, 392, 64)):
         wl = workloads.custom_workload(M, K, N, seed=64 + r, n_out=4, bias=True)
         Lr = wl.layers[0]
         p = S.prepare_weights(Lr.weight_bits, wl.act_absmax(), rank=r)
         po = abi_to_oracle_prep(p)
-        lin = S.SVDQW4A4Linear(p, torch.from_numpy(Lr.bias_bits.view(np.int16).copy()).view(torch.bfloat16), "cuda")
+        lin = S.SVDQW4A4Linear(p, torch.from_numpy(Lr.bias_bits.view(np.int16).copy()).view(torch.bfloat16), "cuda",
+                               engine=engine)
+        assert lin.engine == engine
         y = lin(dev_bf16(wl.x_bits))
         torch.cuda.synchronize()
         check_y(to_np_bf16(y), O.forward(wl.x, po, bias=Lr.bias))
