@@ -544,6 +544,70 @@ def rank_sweep(S, workloads, steps, warmup):
             "context": "pages: an unfused rank-32 branch costs +57% latency (NVIDIA, model card)"}
 
 
+def _pmc_per_dispatch(d, counter):
+    """{kernel name: [per-dispatch value]} of one counter from a rocprofv3
+    --pmc csv directory (values of one dispatch summed)."""
+    import csv
+    import collections
+    per = collections.defaultdict(float)
+    names = {}
+    with open(os.path.join(d, "pmc_counter_collection.csv")) as f:
+        for row in csv.DictReader(f):
+            if row["Counter_Name"] != counter:
+                continue
+            per[row["Dispatch_Id"]] += float(row["Counter_Value"])
+            names[row["Dispatch_Id"]] = row["Kernel_Name"]
+    out = collections.defaultdict(list)
+    for did, v in per.items():
+        out[names[did]].append(v)
+    return out
+
+
+def traffic_summary(engine, workload, rank, pmc_dir, copy_mib):
+    """Kernel 2's HBM bytes per launch from rocprofv3 counter runs of this
+    script under pmc_dir: fetch/ and write/ (FETCH_SIZE, WRITE_SIZE of a
+    single-layer run of `engine`), copy_fetch/ and copy_write/ (the same
+    counters of --copy-probe copy_mib).  Each counter is scaled by what it
+    reads for the plain copy of known size.  Writes
+    profiles/traffic_<workload>_r<rank>_<engine>.json."""
+    kname = K2_KERNEL[engine]
+
+    def mean_of(d, counter, key):
+        vals = [v for k, lst in _pmc_per_dispatch(os.path.join(pmc_dir, d), counter).items() if key(k) for v in lst]
+        return float(np.mean(vals)), len(vals)
+
+    # demangled ("k_gemm_mxfp4_lora_up<0, 1, 256>") or mangled names
+    fetch, n = mean_of("fetch", "FETCH_SIZE", lambda k: kname in k)
+    write, _ = mean_of("write", "WRITE_SIZE", lambda k: kname in k)
+    if not n:
+        raise SystemExit(f"no {kname} dispatches under {pmc_dir}")
+    cdir = pmc_dir if os.path.isdir(os.path.join(pmc_dir, "copy_fetch")) else os.path.dirname(pmc_dir.rstrip("/"))
+    copy_f = max(np.mean(v) for v in _pmc_per_dispatch(os.path.join(cdir, "copy_fetch"), "FETCH_SIZE").values())
+    copy_w = max(np.mean(v) for v in _pmc_per_dispatch(os.path.join(cdir, "copy_write"), "WRITE_SIZE").values())
+    copy_bytes = copy_mib * (1 << 20)
+    rf, wf = copy_bytes / 1024.0 / copy_f, copy_bytes / 1024.0 / copy_w
+    gen, layer, _, desc = BENCH_WORKLOADS[workload]
+    import workloads
+    wl = workloads.make_workload(gen)
+    Lr = wl.layers[layer]
+    M, K, N = wl.M, Lr.K, Lr.N
+    precision = "mxfp4" if engine == "mxfp4" else "int4"
+    alg_w = 2 * M * N
+    d = {"kernel": kname, "engine": engine, "workload": f"{desc}, rank {rank}",
+         "kernel_source_sha": kernel_source_hash(engine), "dispatches_averaged": n,
+         "fetch_size_kib_per_dispatch": fetch, "write_size_kib_per_dispatch": write,
+         "calibration": {"copy_bytes": copy_bytes, "fetch_size_kib": copy_f, "write_size_kib": copy_w,
+                         "read_factor": round(rf, 4), "write_factor": round(wf, 4)},
+         "k2_hbm_read_bytes": fetch * 1024 * rf, "k2_hbm_write_bytes": write * 1024 * wf,
+         "k2_hbm_bytes": fetch * 1024 * rf + write * 1024 * wf,
+         "algorithmic_read_bytes": k2_bytes(M, N, K, rank, Lr.bias_bits is not None, precision) - alg_w,
+         "algorithmic_write_bytes": alg_w}
+    p = os.path.join(ROOT, "profiles", f"traffic_{workload}_r{rank}_{engine}.json")
+    with open(p, "w") as f:
+        json.dump(d, f, indent=1)
+    print(json.dumps({"wrote": p, **{k: d[k] for k in ("k2_hbm_bytes", "dispatches_averaged")}}))
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__)
     ap.add_argument("--gpus", type=int, default=1)
@@ -568,7 +632,15 @@ def main():
                     help="only the batched rank sweep (16384x3072x12288, ranks 0/16/32/64/128), as one JSON line")
     ap.add_argument("--copy-probe", type=int, default=0, metavar="MIB",
                     help="only run a plain device copy of MIB MiB (HBM counter calibration)")
+    ap.add_argument("--traffic-summary", metavar="PMC_DIR",
+                    help="no GPU work: write profiles/traffic_<workload>_r<rank>_<engine>.json from the "
+                         "rocprofv3 counter runs under PMC_DIR (fetch/, write/; copy_fetch/, copy_write/ "
+                         "there or one level up: the copy runs of --copy-probe 256)")
     args = ap.parse_args()
+    if args.traffic_summary:
+        traffic_summary("mxfp4" if args.precision == "mxfp4" else args.engine, args.workload, args.rank,
+                        args.traffic_summary, 256)
+        return
 
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}); this layer's "
