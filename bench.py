@@ -334,6 +334,44 @@ def measure_peaks():
     return res
 
 
+def mix_probe(iters=2000):
+    """The 6-bit route's inner loop on registers (include/svdq_probe.h kinds
+    2-4): FP6 MFMAs only, the fp32 dequantization only, and both interleaved
+    as kernel 2 issues them, at one and two waves per SIMD (1 x and 2 x CUs
+    blocks of four waves).  Per kind: time per 32 x 32 tile on one SIMD."""
+    import torch
+    from w4a4_rank_corrected_svdq_amd import _lib as L
+    cus = torch.cuda.get_device_properties(0).multi_processor_count
+    st = torch.cuda.current_stream()
+    out = {"iters": iters, "tiles_per_wave_iteration": 8, "cus": cus, "runs": []}
+    names = {L.SVDQ_PROBE_MFMA_FP6: "fp6_mfma_only", L.SVDQ_PROBE_DEQUANT: "dequant_valu_only",
+             L.SVDQ_PROBE_FP6_DEQUANT: "fp6_mfma_plus_dequant"}
+    for wps in (1, 2):
+        blocks = cus * wps
+        sink = torch.empty(blocks * 256 * 64, dtype=torch.uint8, device="cuda")
+        for kind, name in names.items():
+            def launch(kind=kind):
+                L.check(L.lib().svdq_probe_mfma(kind, blocks, iters, sink.data_ptr(), st.cuda_stream), "mix probe")
+            settle(launch)
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record()
+            for _ in range(5):
+                launch()
+            e1.record()
+            torch.cuda.synchronize()
+            ms = e0.elapsed_time(e1) / 5
+            ns_tile = ms * 1e6 / (wps * iters * 8)
+            run = {"kind": name, "waves_per_simd": wps, "ms": round(ms, 4),
+                   "ns_per_tile_per_simd": round(ns_tile, 3), "cycles_per_tile_at_2.4GHz": round(ns_tile * 2.4, 1)}
+            if kind != L.SVDQ_PROBE_DEQUANT:
+                run["fp6_mfma_tflops"] = round(L.lib().svdq_probe_mfma_ops(kind, blocks, iters) / (ms * 1e-3) / 1e12, 1)
+            else:
+                run["valu_fp32_instr_per_simd_cycle_at_2.4GHz"] = round(32.0 / (ns_tile * 2.4), 3)
+            out["runs"].append(run)
+        del sink
+    return out
+
+
 SWEEP_RANKS = (0, 16, 32, 64, 128)
 SWEEP_ROWS = 64
 
@@ -632,6 +670,9 @@ def main():
                     help="only the batched rank sweep (16384x3072x12288, ranks 0/16/32/64/128), as one JSON line")
     ap.add_argument("--copy-probe", type=int, default=0, metavar="MIB",
                     help="only run a plain device copy of MIB MiB (HBM counter calibration)")
+    ap.add_argument("--mix-probe", action="store_true",
+                    help="only the register-only probe of the 6-bit route's inner loop (FP6 MFMA, fp32 "
+                         "dequantization, both), as one JSON line")
     ap.add_argument("--traffic-summary", metavar="PMC_DIR",
                     help="no GPU work: write profiles/traffic_<workload>_r<rank>_<engine>.json from the "
                          "rocprofv3 counter runs under PMC_DIR (fetch/, write/; copy_fetch/, copy_write/ "
@@ -672,6 +713,9 @@ def main():
 
     if args.rank_sweep:
         print(json.dumps({"rank_sweep": rank_sweep(S, workloads, args.steps, args.warmup)}))
+        return
+    if args.mix_probe:
+        print(json.dumps({"mix_probe": mix_probe()}))
         return
 
     gen_name, layer, act, desc = BENCH_WORKLOADS[args.workload]

@@ -98,13 +98,16 @@ def test_device_entry_validation_precedes_device_use():
     big = (1 << 23) + 16
     assert qk(p[0], p[1], p[2], p[3], p[4], p[5], None, p[6], p[7], p[8], p[9], 1e-6, big, 384, 128, 16, 64, 0, p[6], None) == L.SVDQ_ERR_UNSUPPORTED_SHAPE
     pr = L.lib().svdq_probe_mfma
-    assert pr(2, 1, 1, p[0], None) == L.SVDQ_ERR_INVALID_ARG          # unknown kind
+    assert pr(5, 1, 1, p[0], None) == L.SVDQ_ERR_INVALID_ARG          # unknown kind
+    assert pr(-1, 1, 1, p[0], None) == L.SVDQ_ERR_INVALID_ARG
     assert pr(0, 0, 1, p[0], None) == L.SVDQ_ERR_INVALID_ARG          # no blocks
     assert pr(1, 1, 0, p[0], None) == L.SVDQ_ERR_INVALID_ARG          # no iterations
     assert pr(0, 1, 1, p[0] + 4, None) == L.SVDQ_ERR_INVALID_ARG      # misaligned sink
     ops = L.lib().svdq_probe_mfma_ops
     assert ops(0, 3, 5) == 3 * 4 * 5 * 1 * 2 * 32 * 32 * 32
     assert ops(1, 3, 5) == 3 * 4 * 5 * 4 * 2 * 32 * 32 * 64
+    assert ops(L.SVDQ_PROBE_MFMA_FP6, 3, 5) == ops(L.SVDQ_PROBE_FP6_DEQUANT, 3, 5) == 3 * 4 * 5 * 8 * 2 * 32 * 32 * 64
+    assert ops(L.SVDQ_PROBE_DEQUANT, 3, 5) == 3 * 4 * 5 * 8 * 3 * 32 * 32
     assert ops(7, 3, 5) == 0.0
     d = L.lib().svdq_lora_down
     u = L.lib().svdq_lora_up_add

@@ -634,7 +634,8 @@ def test_qkv_full_size_sampled_rows():
     assert torch.isfinite(y.float()).all()
 
 
-@pytest.mark.parametrize("kind", [L.SVDQ_PROBE_MFMA_I8, L.SVDQ_PROBE_MFMA_FP4])
+@pytest.mark.parametrize("kind", [L.SVDQ_PROBE_MFMA_I8, L.SVDQ_PROBE_MFMA_FP4, L.SVDQ_PROBE_MFMA_FP6,
+                                  L.SVDQ_PROBE_DEQUANT, L.SVDQ_PROBE_FP6_DEQUANT])
 def test_peak_probe_runs_and_is_deterministic(kind):
     """The benchmark's MFMA peak probe (include/svdq_probe.h): it launches,
     writes its whole sink, and two launches write the same bytes (the

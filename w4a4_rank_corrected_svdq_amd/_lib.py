@@ -63,6 +63,9 @@ SIGNATURES = {
 }
 SVDQ_PROBE_MFMA_I8 = 0
 SVDQ_PROBE_MFMA_FP4 = 1
+SVDQ_PROBE_MFMA_FP6 = 2
+SVDQ_PROBE_DEQUANT = 3
+SVDQ_PROBE_FP6_DEQUANT = 4
 
 
 class SVDQError(RuntimeError):

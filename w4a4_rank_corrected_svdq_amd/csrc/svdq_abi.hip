@@ -291,7 +291,7 @@ extern "C" int svdq_awq_gemv(const void* x_hat, const float* xsum, const void* w
 }
 
 extern "C" int svdq_probe_mfma(int kind, int blocks, int iters, void* sink, void* stream) {
-  if (kind != SVDQ_PROBE_MFMA_I8 && kind != SVDQ_PROBE_MFMA_FP4) return SVDQ_ERR_INVALID_ARG;
+  if (kind < SVDQ_PROBE_MFMA_I8 || kind > SVDQ_PROBE_FP6_DEQUANT) return SVDQ_ERR_INVALID_ARG;
   if (blocks < 1 || iters < 1 || !sink || !aligned16(sink)) return SVDQ_ERR_INVALID_ARG;
   const int st = current_device_check();
   if (st != SVDQ_OK) return st;
@@ -299,6 +299,6 @@ extern "C" int svdq_probe_mfma(int kind, int blocks, int iters, void* sink, void
 }
 
 extern "C" double svdq_probe_mfma_ops(int kind, int blocks, int iters) {
-  if ((kind != SVDQ_PROBE_MFMA_I8 && kind != SVDQ_PROBE_MFMA_FP4) || blocks < 1 || iters < 1) return 0.0;
+  if (kind < SVDQ_PROBE_MFMA_I8 || kind > SVDQ_PROBE_FP6_DEQUANT || blocks < 1 || iters < 1) return 0.0;
   return svdq::probe_mfma_ops(kind, blocks, iters);
 }
