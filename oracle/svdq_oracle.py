@@ -72,7 +72,7 @@ __all__ = [
     "quantize_weight_residual", "prepare", "gelu_tanh", "quantize_activation",
     "pack_int4", "unpack_int4", "lora_down", "w4a4_product",
     "w4a4_product_bruteforce", "forward", "forward_unfused", "reference_fp64", "rel_fro",
-    "rms_norm", "rope", "forward_qkv",
+    "rms_norm", "rope", "forward_qkv", "forward_mlp_chain",
     "prepared_bytes",
 ]
 
@@ -379,6 +379,40 @@ def forward_unfused(x, prep, bias=None, act: str = "none", semantics: str = "gpu
         return y0
     la = lora_down(x_hat, prep["L1"])
     return bf16(y0 + bf16(la) @ prep["L2"])
+
+
+def forward_mlp_chain(x, prep_up, prep_down, bias_up=None, bias_down=None, slice_cols: int = 256,
+                      return_parts: bool = False):
+    """The MLP pair as one chain ("Introducing Nunchaku Lite": the fused
+    GELU/MLP kernels of the original engine; reading C1): the up layer's
+    output Y_up = forward(x, up) rounded to bf16 once, tanh-GELU and the down
+    layer's smoothing and per-(token, group) INT4 quantizer applied to it,
+    the down layer's down projection bf16(x_hat) L1 formed as a sum of
+    per-column-slice partials of ``slice_cols`` columns of Y_up, each rounded
+    to fp32 and added in slice order in fp32 (the chain's one rounding point
+    beyond the two-layer composition), then the down layer's 4-bit product,
+    up projection and bias.  With one slice it is the composition
+    forward(forward(x, up), down, act="gelu_tanh")."""
+    y_up = forward(x, prep_up, bias=bias_up)                           # bf16 values
+    group = prep_down["group"]
+    qx, sx, x_hat = quantize_activation(y_up, prep_down["smooth_inv"], group, act="gelu_tanh")
+    L1 = np.asarray(prep_down["L1"], dtype=np.float64)
+    K = y_up.shape[1]
+    la = None
+    if L1.shape[1]:
+        la = np.zeros((y_up.shape[0], L1.shape[1]))
+        for c0 in range(0, K, slice_cols):
+            part = fp32(bf16(x_hat[:, c0:c0 + slice_cols]) @ L1[c0:c0 + slice_cols])
+            la = fp32(la + part)
+    acc = w4a4_product(qx, sx, prep_down["qw"], prep_down["sw"], group)
+    y = acc + (bf16(la) @ prep_down["L2"] if la is not None else 0.0)
+    if bias_down is not None:
+        y = y + np.asarray(bias_down, dtype=np.float64)[None, :]
+    Y = bf16(y)
+    if return_parts:
+        return Y, dict(y_up=y_up, qx=qx, sx=sx, x_hat=x_hat,
+                       lora_act=la if la is not None else np.zeros((y_up.shape[0], 0)))
+    return Y
 
 
 def rms_norm(v, g, eps: float = 1e-6) -> np.ndarray:

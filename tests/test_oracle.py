@@ -399,3 +399,47 @@ def test_forward_qkv_composition():
     ang = np.random.default_rng(31).uniform(0, 6, (40, 64))
     Yr = O.forward_qkv(wl.x, p, L.bias, ones, ones, np.cos(ang), np.sin(ang), out="f64")
     np.testing.assert_allclose(np.sqrt(np.mean(Yr[:, :512].reshape(40, 4, 128) ** 2, axis=-1)), 1.0, rtol=1e-5)
+
+
+# ---------------------------------------------------------------- MLP chain
+def _chain_case(M=48, K=128, N=256, N2=192, seed=21, rank=16):
+    wl = workloads.custom_workload(M, K, N, seed=seed, n_out=3, bias=True, second_N=N2)
+    up, dn = wl.layers
+    pu = O.prepare(up.weight, wl.act_absmax(), rank=rank)
+    y_up = O.forward(wl.x, pu, bias=up.bias)
+    a_dn = np.abs(O.gelu_tanh(y_up)).max(0).astype(np.float32)
+    pd = O.prepare(dn.weight, a_dn, rank=rank)
+    return wl, up, dn, pu, pd
+
+
+def test_mlp_chain_one_slice_is_the_composition():
+    wl, up, dn, pu, pd = _chain_case()
+    ref = O.forward(O.forward(wl.x, pu, bias=up.bias), pd, act="gelu_tanh", bias=dn.bias)
+    got = O.forward_mlp_chain(wl.x, pu, pd, up.bias, dn.bias, slice_cols=256)
+    np.testing.assert_array_equal(got, ref)
+
+
+def test_mlp_chain_slices_round_once_each():
+    """With slices, lora_act differs from the whole-row down projection only
+    by the fp32 rounding of the partials and of their running sum: at most
+    one fp32 unit per slice and addition relative to the sum of magnitudes."""
+    wl, up, dn, pu, pd = _chain_case(N=512)
+    _, parts = O.forward_mlp_chain(wl.x, pu, pd, up.bias, dn.bias, slice_cols=128, return_parts=True)
+    whole = O.lora_down(parts["x_hat"], pd["L1"])
+    mag = O.bf16(np.abs(parts["x_hat"])) @ np.abs(pd["L1"])
+    assert np.all(np.abs(parts["lora_act"] - whole) <= 2 * 4 * 2.0 ** -24 * mag + 1e-30)
+    # and the codes are those of the composition's down layer
+    q, s, _ = O.quantize_activation(O.forward(wl.x, pu, bias=up.bias), pd["smooth_inv"], 64, act="gelu_tanh")
+    np.testing.assert_array_equal(parts["qx"], q)
+    np.testing.assert_array_equal(parts["sx"], s)
+
+
+def test_mlp_chain_rank0_and_partial_slice():
+    # rank 0 skips the branch; a last slice narrower than slice_cols works
+    wl, up, dn, pu, pd0 = _chain_case(rank=0, N=320)
+    ref = O.forward(O.forward(wl.x, pu, bias=up.bias), pd0, act="gelu_tanh", bias=dn.bias)
+    np.testing.assert_array_equal(O.forward_mlp_chain(wl.x, pu, pd0, up.bias, dn.bias, slice_cols=256), ref)
+    wl, up, dn, pu, pd = _chain_case(N=320)
+    y = O.forward_mlp_chain(wl.x, pu, pd, up.bias, dn.bias, slice_cols=256)
+    ref = O.forward(O.forward(wl.x, pu, bias=up.bias), pd, act="gelu_tanh", bias=dn.bias)
+    assert O.rel_fro(y, ref) < 1e-5
