@@ -282,9 +282,10 @@ int svdq_quant_act_lora_down_fp6(const void* x, const float* smooth_inv, const v
 /* Device, asynchronous.  Kernel 2 on the 6-bit MFMA: the output of
  * svdq_gemm_w4a4_lora_up for the same codes and scales,
  *   y = sum_g s_x[m,g] s_w[g,n] P_g[m,n] + sum_j bf16(lora_act[m,j]) lora_up[n][j] + bias[n],
- * accumulated in fp32 starting from bias + up projection and adding the
- * groups in increasing g, each as fma(P_g * s_x, s_w, acc) (P_g * s_x is
- * exact), rounded to bf16 to nearest even (or stored fp32).
+ * accumulated in fp32: the groups in increasing g, each as
+ * fma(P_g * s_x, s_w, acc) (P_g * s_x is exact), then the up projection 16
+ * ranks at a time, then the bias; rounded to bf16 to nearest even (or
+ * stored fp32).
  *   x_fp6    SVDQ_FP6_ACTIVATIONS layout of the activation codes,
  *   x_scales [K/64][Mp] fp16, Mp = 32 ceil(M/32)   (both from kernel 1)
  *   w_fp6    SVDQ_FP6_WEIGHTS layout of the weight codes (svdq_pack_fp6_operand),
@@ -296,6 +297,53 @@ int svdq_gemm_w4a4_fp6_lora_up(const void* x_fp6, const void* x_scales,
                                const float* lora_act, const void* lora_up, const void* bias,
                                int M, int N, int K, int rank, int group, int out_dtype,
                                void* y, void* stream);
+
+/* ------------------------------------------------------------------------
+ * The MLP chain (SVDQuant pages: "Introducing Nunchaku Lite", the fused
+ * GELU/MLP kernels of the original engine).  An MLP pair is an up layer
+ * (K -> N) whose output, through tanh-GELU, is the input of a down layer
+ * (N -> N2).  The chain runs the up layer's kernel 2 on the 6-bit MFMA and,
+ * in its epilogue, the down layer's kernel 1 on the tile it just computed:
+ * Y_up never goes to memory.  For every row m and group g of 64 of the up
+ * layer's N columns:
+ *   x = bf16(Y_up[m, n])  (Y_up as svdq_gemm_w4a4_fp6_lora_up computes it),
+ *   x_hat = fp32(gelu_tanh(x) * smooth_inv_dn[n]), then the INT4 quantizer
+ *   of svdq_quant_act_lora_down_fp6: codes into x_fp6_dn, scales into
+ *   x_scales_dn -- bit for bit what the two-layer path writes;
+ * and lora_act_dn = sum over the column slices c of 256 columns, in slice
+ * order in fp32, of fp32( bf16(x_hat[:, c]) lora_down_dn[:, c]^T ) -- the
+ * whole-row down projection up to the fp32 rounding of each slice's partial.
+ * The down layer then runs svdq_gemm_w4a4_fp6_lora_up on these outputs.
+ * ------------------------------------------------------------------------ */
+
+/* Host.  Workspace bytes of svdq_gemm_w4a4_fp6_mlp_chain: the partial down
+ * projections, ceil(N/256) * M * rank_dn fp32 (0 when rank_dn == 0).
+ * SVDQ_ERR_INVALID_ARG for negative sizes or a NULL bytes_out. */
+int svdq_mlp_chain_workspace_bytes(int M, int N, int rank_dn, size_t* bytes_out);
+
+/* Device, asynchronous; two kernels on `stream`.  Up layer (shapes and
+ * layouts as svdq_gemm_w4a4_fp6_lora_up): x_fp6, x_scales, w_fp6,
+ * w_scales, lora_act, lora_up, bias, M, N, K, rank, group.  Down layer:
+ *   smooth_inv_dn  [N] fp32          its 1 / lambda
+ *   lora_down_dn   [rank_dn][N] bf16 its L1^T (NULL if rank_dn == 0)
+ * Outputs (caller-owned device memory, the down layer's kernel-1 outputs):
+ *   x_fp6_dn    SVDQ_FP6_ACTIVATIONS layout, [N/64][ceil(M/32)][1536] u8
+ *   x_scales_dn [N/64][Mp] fp16, Mp = 32 ceil(M/32) (rows M..Mp-1 zero)
+ *   lora_act_dn [M][rank_dn] fp32 (NULL if rank_dn == 0)
+ *   workspace   svdq_mlp_chain_workspace_bytes() bytes, 16-byte aligned
+ *               (NULL if rank_dn == 0); its contents afterwards are
+ *               unspecified.  Calls that share a workspace must not overlap.
+ * Requires N % 64 == 0 (the down layer's K), rank_dn % 16 == 0,
+ * 0 <= rank_dn <= min(N, SVDQ_MAX_RANK); other shape rules and errors as
+ * svdq_gemm_w4a4_fp6_lora_up; SVDQ_ERR_INVALID_ARG for a workspace smaller
+ * than required. */
+int svdq_gemm_w4a4_fp6_mlp_chain(const void* x_fp6, const void* x_scales,
+                                 const void* w_fp6, const void* w_scales,
+                                 const float* lora_act, const void* lora_up, const void* bias,
+                                 int M, int N, int K, int rank, int group,
+                                 const float* smooth_inv_dn, const void* lora_down_dn, int rank_dn,
+                                 void* x_fp6_dn, void* x_scales_dn, float* lora_act_dn,
+                                 void* workspace, size_t workspace_bytes, void* stream);
 
 /* ------------------------------------------------------------------------
  * 4-bit float variant (MXFP4).  The pages offer the layer with INT4 and with

@@ -181,6 +181,20 @@ static void device_argument_checks() {
                                                   nullptr)));
   EXPECT(svdq_gemm_w4a4_fp6_lora_up(p, p, p, p, f, p, nullptr, M, N, 96, r, 64, SVDQ_OUT_F32, p, nullptr) !=
          SVDQ_OK);
+  // the MLP chain
+  size_t ws = 0;
+  EXPECT(svdq_mlp_chain_workspace_bytes(M, 512, 32, &ws) == SVDQ_OK && ws == 2u * M * 32 * 4);
+  EXPECT(svdq_mlp_chain_workspace_bytes(M, 512, 32, nullptr) == SVDQ_ERR_INVALID_ARG);
+  EXPECT(passed_checks(svdq_gemm_w4a4_fp6_mlp_chain(p, p, p, p, f, p, nullptr, M, 512, K, r, 64, f, p, 32, p, p, f,
+                                                    p, ws, nullptr)));
+  EXPECT(svdq_gemm_w4a4_fp6_mlp_chain(p, p, p, p, f, p, nullptr, M, 512, K, r, 64, f, p, 32, p, p, f, p, ws - 16,
+                                      nullptr) == SVDQ_ERR_INVALID_ARG);          // workspace too small
+  EXPECT(svdq_gemm_w4a4_fp6_mlp_chain(p, p, p, p, f, p, nullptr, M, 520, K, r, 64, f, p, 32, p, p, f, p, 1 << 20,
+                                      nullptr) == SVDQ_ERR_UNSUPPORTED_SHAPE);    // N not a multiple of 64
+  EXPECT(svdq_gemm_w4a4_fp6_mlp_chain(p, p, p, p, f, p, nullptr, M, 512, K, r, 64, nullptr, p, 32, p, p, f, p, ws,
+                                      nullptr) == SVDQ_ERR_INVALID_ARG);
+  EXPECT(passed_checks(svdq_gemm_w4a4_fp6_mlp_chain(p, p, p, p, f, p, nullptr, M, 512, K, r, 64, f, nullptr, 0, p, p,
+                                                    nullptr, nullptr, 0, nullptr)));
   // MXFP4
   EXPECT(passed_checks(svdq_quant_act_lora_down_mxfp4(p, f, p, M, K, r, SVDQ_ACT_NONE, p, p, f, nullptr)));
   EXPECT(svdq_quant_act_lora_down_mxfp4(p, f, p, M, 64, r, SVDQ_ACT_NONE, p, p, f, nullptr) != SVDQ_OK);

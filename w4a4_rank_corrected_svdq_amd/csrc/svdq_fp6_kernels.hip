@@ -154,12 +154,29 @@ __device__ __forceinline__ void tile_of(int t, int nM, int nN, int& tm, int& tn)
   tn = r / gm;
 }
 
-template <int OUT_F32>
+// The MLP chain's epilogue (CHAIN = 1): instead of storing Y, the block
+// turns its output tile into the next layer's kernel-1 outputs -- bf16(Y),
+// tanh-GELU, the next layer's smoothing and per-(row, group of 64) INT4
+// quantizer, codes in the 6-bit containers -- and the tile's 256-column
+// slice of the next layer's down projection, a partial that a second kernel
+// sums over the column slices in order.  The next layer's K is this layer's N.
+struct ChainArgs {
+  const float* smooth_inv;   // [N] the next layer's 1 / lambda
+  const uint16_t* lora_down; // [rank][N] bf16, the next layer's L1^T
+  int rank;                  // the next layer's rank
+  uint8_t* x_fp6;            // [N/64][ceil(M/32)][1536] codes of the next layer's input
+  _Float16* x_scales;        // [N/64][32 ceil(M/32)]
+  float* partials;           // [ceil(N/256)][M][rank]
+};
+constexpr int C_TS = 2 * F_BN + 16;                   // staging row stride in bytes (bank spread)
+static_assert(F_BM * C_TS <= F_NS * F_SLOT, "the chain's staging tile fits the idle ring");
+
+template <int OUT_F32, int CHAIN>
 __global__ __launch_bounds__(F_THREADS, 1) void k_gemm_w4a4_fp6(
     const uint8_t* __restrict__ x_fp6, const _Float16* __restrict__ x_scales,
     const uint8_t* __restrict__ w_fp6, const _Float16* __restrict__ w_scales,
     const float* __restrict__ lora_act, const uint16_t* __restrict__ lora_up,
-    const uint16_t* __restrict__ bias, int M, int N, int K, int rank, void* __restrict__ y) {
+    const uint16_t* __restrict__ bias, int M, int N, int K, int rank, void* __restrict__ y, ChainArgs ca) {
   __shared__ __align__(16) unsigned char ring[F_NS][F_SLOT];
   __shared__ __align__(16) float conv[2][F_CONV];
   __shared__ __align__(16) uint16_t bias_ring[2][F_BN];   // bias of the tiles with even / odd index j
@@ -400,6 +417,136 @@ __global__ __launch_bounds__(F_THREADS, 1) void k_gemm_w4a4_fp6(
     ++since_end;
   };
 
+  // The chain's epilogue (one tile per block): once every load of the ring
+  // has landed, the ring holds the output tile as bf16 (E1); each thread then
+  // takes two (row, group of 64) pairs through tanh-GELU, the next layer's
+  // smoothing and INT4 quantizer -- the arithmetic of kernel 1 -- writes
+  // their codes into the 6-bit containers and their fp16 scales, and puts
+  // bf16(x_hat) back in place (E2); each wave then forms 32 rows of the
+  // tile's partial down projection, bf16(x_hat) [256 x 256] L1 slice, on
+  // bf16 MFMA (E3).  Rows M .. Mp - 1 get zero codes and scales, as kernel 1
+  // writes them; rows and groups past the operands are not written.
+  auto chain_epilogue = [&](int tt) {
+    if constexpr (CHAIN) {
+      const int tmc = tt >> 16, tnc = tt & 0xFFFF;
+      __builtin_amdgcn_s_waitcnt(waitcnt_vm_lgkm0(0));
+      __syncthreads();
+      unsigned char* T = &ring[0][0];
+      float* si_s = &conv[0][0];
+      {
+        const int ln = fresh_lane();
+        const int lc = ln & 31, lh = ln >> 5;
+        const uint2 bu = *reinterpret_cast<const uint2*>(&bias_ring[0][128 * wn + 4 * lc]);
+        const float bv[4] = {bf16_bits_to_f32(bu.x & 0xFFFFu), bf16_bits_to_f32(bu.x >> 16),
+                             bf16_bits_to_f32(bu.y & 0xFFFFu), bf16_bits_to_f32(bu.y >> 16)};
+#pragma unroll
+        for (int a = 0; a < 2; ++a)
+#pragma unroll
+          for (int b = 0; b < 4; ++b)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+              const int e = 4 * b + i;
+              const int rl = 64 * wm + 32 * a + 8 * b + 4 * lh + i;
+              *reinterpret_cast<uint2*>(T + rl * C_TS + 2 * (128 * wn + 4 * lc)) =
+                  make_uint2(bf16x2_bits(acc[a][0][e] + bv[0], acc[a][1][e] + bv[1]),
+                             bf16x2_bits(acc[a][2][e] + bv[2], acc[a][3][e] + bv[3]));
+            }
+        if (tid < F_BN) {
+          const int k = F_BN * tnc + tid;
+          si_s[tid] = k < N ? ca.smooth_inv[k] : 0.f;
+        }
+      }
+      __syncthreads();
+      const int RBd = (M + 31) >> 5, Mpd = RBd << 5;
+      const int Gd = N / GROUP;
+#pragma unroll 1
+      for (int k2 = 0; k2 < 2; ++k2) {
+        const int p = tid + F_THREADS * k2;
+        const int rl = p >> 2, g = p & 3;
+        const int row = F_BM * tmc + rl;
+        const int gd = 4 * tnc + g;
+        if (gd >= Gd || row >= Mpd) continue;
+        unsigned char* tr = T + rl * C_TS + 2 * GROUP * g;
+        float xh[GROUP];
+#pragma unroll
+        for (int c8 = 0; c8 < 8; ++c8) {
+          const uint4 u = *reinterpret_cast<const uint4*>(tr + 16 * c8);
+          const uint32_t w[4] = {u.x, u.y, u.z, u.w};
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            const int j = 8 * c8 + 2 * i;
+            xh[j] = row < M ? gelu_tanh(bf16_bits_to_f32(w[i] & 0xFFFFu)) * si_s[GROUP * g + j] : 0.f;
+            xh[j + 1] = row < M ? gelu_tanh(bf16_bits_to_f32(w[i] >> 16)) * si_s[GROUP * g + j + 1] : 0.f;
+          }
+        }
+        float amax = 0.f;
+#pragma unroll
+        for (int j = 0; j < GROUP; ++j) amax = fmaxf(amax, fabsf(xh[j]));
+        const float s32 = amax / 7.0f;
+        const _Float16 sh = static_cast<_Float16>(s32);
+        const float sf = static_cast<float>(sh);
+        const float rcp = (sf == 0.f) ? 0.f : 1.0f / sf;
+        uint8_t* fr = ca.x_fp6 + (static_cast<size_t>(gd) * RBd + (row >> 5)) * FRAG;
+#pragma unroll
+        for (int hh = 0; hh < 2; ++hh) {
+          // codes j = 0..31 of half hh: even positions from the first source,
+          // odd from the second; + 0.0f turns -0 into +0
+          v16f ev, od;
+#pragma unroll
+          for (int i = 0; i < 16; ++i) {
+            ev[i] = fminf(fmaxf(rintf(xh[32 * hh + 2 * i] * rcp), -8.f), 7.f) + 0.0f;
+            od[i] = fminf(fmaxf(rintf(xh[32 * hh + 2 * i + 1] * rcp), -8.f), 7.f) + 0.0f;
+          }
+          typedef int v6i_ __attribute__((ext_vector_type(6)));
+          const v6i_ pk = __builtin_amdgcn_cvt_scalef32_2xpk16_bf6_f32(ev, od, 1.0f);
+          const int fl = (row & 31) + 32 * hh;
+          *reinterpret_cast<uint4*>(fr + 16 * fl) = make_uint4(pk[0], pk[1], pk[2], pk[3]);
+          *reinterpret_cast<uint2*>(fr + 1024 + 8 * fl) = make_uint2(pk[4], pk[5]);
+        }
+        ca.x_scales[static_cast<size_t>(gd) * Mpd + row] = sh;
+#pragma unroll
+        for (int c8 = 0; c8 < 8; ++c8)
+          *reinterpret_cast<uint4*>(tr + 16 * c8) =
+              make_uint4(bf16x2_bits(xh[8 * c8], xh[8 * c8 + 1]), bf16x2_bits(xh[8 * c8 + 2], xh[8 * c8 + 3]),
+                         bf16x2_bits(xh[8 * c8 + 4], xh[8 * c8 + 5]), bf16x2_bits(xh[8 * c8 + 6], xh[8 * c8 + 7]));
+      }
+      __syncthreads();
+      if (ca.rank > 0) {
+        // A = 8 bf16(x_hat) of row 32 w + l % 32 at k = 16 kk + 8 (l / 32);
+        // B = the same k of L1^T row (rank) rc + l % 32; D lane l: rank
+        // rc + l % 32, rows 8 b + 4 (l / 32) + i of the wave's 32
+        const int ln = fresh_lane();
+        const int lc = ln & 31, lh = ln >> 5;
+        const int rl = 32 * wave + lc;
+#pragma unroll 1
+        for (int rc = 0; rc < ca.rank; rc += 32) {
+          const int rr = rc + lc;
+          v16f d = zero;
+#pragma unroll 4
+          for (int kk = 0; kk < F_BN / 16; ++kk) {
+            const int kl = 16 * kk + 8 * lh;
+            const v8bf av = __builtin_bit_cast(v8bf, *reinterpret_cast<const uint4*>(T + rl * C_TS + 2 * kl));
+            const int kg = F_BN * tnc + kl;
+            uint4 bw = make_uint4(0, 0, 0, 0);
+            if (rr < ca.rank && kg < N)
+              bw = *reinterpret_cast<const uint4*>(ca.lora_down + static_cast<size_t>(rr) * N + kg);
+            d = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av, __builtin_bit_cast(v8bf, bw), d, 0, 0, 0);
+          }
+          if (rr < ca.rank) {
+#pragma unroll
+            for (int b = 0; b < 4; ++b)
+#pragma unroll
+              for (int i = 0; i < 4; ++i) {
+                const int row = F_BM * tmc + 32 * wave + 8 * b + 4 * lh + i;
+                if (row < M)
+                  ca.partials[(static_cast<size_t>(tnc) * M + row) * ca.rank + rr] = d[4 * b + i];
+              }
+          }
+        }
+      }
+    }
+  };
+
   for (int j = 0; j < my_tiles; ++j) {
     const int tt = __builtin_amdgcn_readfirstlane(tiles[j]);
     const int mw = F_BM * (tt >> 16) + 64 * wm, cw = F_BN * (tt & 0xFFFF) + 128 * wn;   // wave-uniform
@@ -505,7 +652,9 @@ __global__ __launch_bounds__(F_THREADS, 1) void k_gemm_w4a4_fp6(
     }
 
     // ---- end of the tile, after its last stage ----
-    {
+    if constexpr (CHAIN) {
+      chain_epilogue(tt);
+    } else {
       // The bias ring entry of tile j is rewritten only by the stages of
       // tile j + 2, issued after the next barrier.
       // end of the tile: bias, rounding, store.  The lane holds rows
@@ -556,6 +705,23 @@ __global__ __launch_bounds__(F_THREADS, 1) void k_gemm_w4a4_fp6(
   __builtin_amdgcn_s_waitcnt(waitcnt_vm_lgkm0(0));
 }
 
+// lora_act = the column slices' partial down projections summed in slice
+// order (the chain's second pass); four ranks per thread.
+__global__ __launch_bounds__(256) void k_partials_reduce(const float4* __restrict__ partials, int S, size_t n4,
+                                                       float4* __restrict__ lora_act) {
+  const size_t i = static_cast<size_t>(blockIdx.x) * 256 + threadIdx.x;
+  if (i >= n4) return;
+  float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
+  for (int s = 0; s < S; ++s) {
+    const float4 v = partials[static_cast<size_t>(s) * n4 + i];
+    acc.x += v.x;
+    acc.y += v.y;
+    acc.z += v.z;
+    acc.w += v.w;
+  }
+  lora_act[i] = acc;
+}
+
 int cu_count() {
   static int cached[64] = {};
   int dev = 0;
@@ -583,13 +749,37 @@ int launch_gemm_w4a4_fp6(const void* x_fp6, const void* x_scales, const void* w_
   const int grid = tiles < cus ? tiles : (cus > 0 ? cus : tiles);
   if ((tiles + grid - 1) / grid > F_MAX_TILES) return SVDQ_ERR_UNSUPPORTED_SHAPE;
 #define SVDQ_K2F(OF)                                                                                          \
-  hipLaunchKernelGGL((k_gemm_w4a4_fp6<OF>), dim3(grid), dim3(F_THREADS), 0, st,                               \
+  hipLaunchKernelGGL((k_gemm_w4a4_fp6<OF, 0>), dim3(grid), dim3(F_THREADS), 0, st,                            \
                      static_cast<const uint8_t*>(x_fp6), static_cast<const _Float16*>(x_scales),              \
                      static_cast<const uint8_t*>(w_fp6), static_cast<const _Float16*>(w_scales), lora_act,    \
-                     static_cast<const uint16_t*>(lora_up), static_cast<const uint16_t*>(bias), M, N, K, rank, y)
+                     static_cast<const uint16_t*>(lora_up), static_cast<const uint16_t*>(bias), M, N, K, rank, y, \
+                     ChainArgs{})
   if (out_dtype == SVDQ_OUT_F32) SVDQ_K2F(1);
   else SVDQ_K2F(0);
 #undef SVDQ_K2F
+  return hipGetLastError() == hipSuccess ? SVDQ_OK : SVDQ_ERR_HIP;
+}
+
+int launch_mlp_chain_fp6(const void* x_fp6, const void* x_scales, const void* w_fp6, const void* w_scales,
+                         const float* lora_act, const void* lora_up, const void* bias, int M, int N, int K, int rank,
+                         const float* smooth_inv_dn, const void* lora_down_dn, int rank_dn, void* x_fp6_dn,
+                         void* x_scales_dn, float* lora_act_dn, float* partials, void* stream) {
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  const int tiles = ((M + F_BM - 1) / F_BM) * ((N + F_BN - 1) / F_BN);
+  ChainArgs ca{smooth_inv_dn, static_cast<const uint16_t*>(lora_down_dn), rank_dn, static_cast<uint8_t*>(x_fp6_dn),
+               static_cast<_Float16*>(x_scales_dn), partials};
+  // one tile per block: the ring is free for the staging tile at its end
+  hipLaunchKernelGGL((k_gemm_w4a4_fp6<0, 1>), dim3(tiles), dim3(F_THREADS), 0, st,
+                     static_cast<const uint8_t*>(x_fp6), static_cast<const _Float16*>(x_scales),
+                     static_cast<const uint8_t*>(w_fp6), static_cast<const _Float16*>(w_scales), lora_act,
+                     static_cast<const uint16_t*>(lora_up), static_cast<const uint16_t*>(bias), M, N, K, rank,
+                     nullptr, ca);
+  if (rank_dn > 0) {
+    const int S = (N + F_BN - 1) / F_BN;
+    const size_t n4 = static_cast<size_t>(M) * rank_dn / 4;
+    hipLaunchKernelGGL(k_partials_reduce, dim3(static_cast<unsigned>((n4 + 255) / 256)), dim3(256), 0, st,
+                       reinterpret_cast<const float4*>(partials), S, n4, reinterpret_cast<float4*>(lora_act_dn));
+  }
   return hipGetLastError() == hipSuccess ? SVDQ_OK : SVDQ_ERR_HIP;
 }
 

@@ -49,6 +49,13 @@ int launch_gemm_w4a4_fp6(const void* x_fp6, const void* x_scales, const void* w_
                          const float* lora_act, const void* lora_up, const void* bias, int M, int N, int K, int rank,
                          int out_dtype, void* y, void* stream);
 
+// The MLP chain (svdq_fp6_kernels.hip): kernel 2 of the up layer with the
+// down layer's kernel-1 work in its epilogue, then the partials' reduction.
+int launch_mlp_chain_fp6(const void* x_fp6, const void* x_scales, const void* w_fp6, const void* w_scales,
+                         const float* lora_act, const void* lora_up, const void* bias, int M, int N, int K, int rank,
+                         const float* smooth_inv_dn, const void* lora_down_dn, int rank_dn, void* x_fp6_dn,
+                         void* x_scales_dn, float* lora_act_dn, float* partials, void* stream);
+
 // svdq_probes.hip
 int launch_probe_mfma(int kind, int blocks, int iters, void* sink, void* stream);
 double probe_mfma_ops(int kind, int blocks, int iters);

@@ -93,6 +93,38 @@ class SVDQW4A4Linear:
     __call__ = forward
 
 
+class SVDQMLPChain:
+    """An MLP pair (up layer, tanh-GELU, down layer), both on the 6-bit
+    engine, run as a chain: kernel 1 of the up layer, the up layer's kernel 2
+    with the down layer's kernel 1 in its epilogue (the up output never goes
+    to memory), then the down layer's kernel 2.  The result is the two-layer
+    path's ``down(up(x), act=GELU)`` up to the fp32 rounding of the down
+    projection's per-slice partials."""
+
+    def __init__(self, up: SVDQW4A4Linear, down: SVDQW4A4Linear):
+        if up.engine != "fp6" or down.engine != "fp6":
+            raise ValueError("the chain runs both layers on the 6-bit engine")
+        if down.K != up.N:
+            raise ValueError(f"the down layer's K ({down.K}) is not the up layer's N ({up.N})")
+        self.up, self.down = up, down
+        self._ws = None
+
+    def forward(self, x: torch.Tensor, out_dtype: int = L.SVDQ_OUT_BF16):
+        up, dn = self.up, self.down
+        M = x.shape[0]
+        xf, xs, la = ops.quant_act_lora_down_fp6(x, up.smooth_inv, up.lora_down, up.rank, up.group)
+        need = ops.mlp_chain_workspace_bytes(M, up.N, dn.rank)
+        if need and (self._ws is None or self._ws.numel() < need or self._ws.device != x.device):
+            self._ws = torch.empty(need, dtype=torch.uint8, device=x.device)
+        xf2, xs2, la2 = ops.gemm_w4a4_fp6_mlp_chain(xf, xs, up.w_fp6, up.w_scales, la, up.lora_up, up.bias,
+                                                    M, up.N, up.K, up.rank, dn.smooth_inv, dn.lora_down, dn.rank,
+                                                    up.group, workspace=self._ws if need else None)
+        return ops.gemm_w4a4_fp6_lora_up(xf2, xs2, dn.w_fp6, dn.w_scales, la2, dn.lora_up, dn.bias,
+                                         M, dn.N, dn.K, dn.rank, dn.group, out_dtype)
+
+    __call__ = forward
+
+
 class AWQW4A16Linear:
     """AWQ W4A16 layer (the pages' runtime layer name for the modulation
     projections): 4-bit weights with activation-aware channel scales, bf16

@@ -232,6 +232,51 @@ def gemm_w4a4_fp6_lora_up(x_fp6, x_scales, w_fp6, w_scales, lora_act, lora_up, b
     return out
 
 
+def mlp_chain_workspace_bytes(M: int, N: int, rank_dn: int) -> int:
+    out = ctypes.c_size_t(0)
+    L.check(L.lib().svdq_mlp_chain_workspace_bytes(M, N, rank_dn, ctypes.byref(out)), "svdq_mlp_chain_workspace_bytes")
+    return int(out.value)
+
+
+def gemm_w4a4_fp6_mlp_chain(x_fp6, x_scales, w_fp6, w_scales, lora_act, lora_up, bias, M: int, N: int, K: int,
+                            rank: int, smooth_inv_dn, lora_down_dn, rank_dn: int, group: int = 64,
+                            out=None, workspace: Optional[torch.Tensor] = None):
+    """The up layer's kernel 2 with the down layer's kernel 1 in its epilogue
+    (svdq_gemm_w4a4_fp6_mlp_chain).  Returns the down layer's (x_fp6
+    [N/64][ceil(M/32)][1536] u8, x_scales [N/64][Mp] f16, lora_act [M][rank_dn]
+    f32)."""
+    dev = x_fp6.device
+    G, Gd, RB = K // group, N // 64, (M + 31) // 32
+    if out is None:
+        xf = torch.empty((Gd, RB, 1536), dtype=torch.uint8, device=dev)
+        xs = torch.empty((Gd, 32 * RB), dtype=torch.float16, device=dev)
+        la = torch.empty((M, rank_dn), dtype=torch.float32, device=dev) if rank_dn else None
+    else:
+        xf, xs, la = out
+    need = mlp_chain_workspace_bytes(M, N, rank_dn)
+    if workspace is None and need:
+        workspace = torch.empty(need, dtype=torch.uint8, device=dev)
+    RBb = 4 * ((N + 127) // 128)
+    st = L.lib().svdq_gemm_w4a4_fp6_mlp_chain(
+        _dev_arg("x_fp6", x_fp6, torch.uint8, (G, RB, 1536), dev),
+        _dev_arg("x_scales", x_scales, torch.float16, (G, 32 * RB), dev),
+        _dev_arg("w_fp6", w_fp6, torch.uint8, (G, RBb, 1536), dev),
+        _dev_arg("w_scales", w_scales, torch.float16, (G, N), dev),
+        _dev_arg("lora_act", lora_act, torch.float32, (M, rank), dev) if rank else None,
+        _dev_arg("lora_up", lora_up, torch.bfloat16, (N, rank), dev) if rank else None,
+        _dev_arg("bias", bias, torch.bfloat16, (N,), dev),
+        M, N, K, rank, group,
+        _dev_arg("smooth_inv_dn", smooth_inv_dn, torch.float32, (N,), dev),
+        _dev_arg("lora_down_dn", lora_down_dn, torch.bfloat16, (rank_dn, N), dev) if rank_dn else None, rank_dn,
+        _dev_arg("x_fp6_dn", xf, torch.uint8, (Gd, RB, 1536), dev),
+        _dev_arg("x_scales_dn", xs, torch.float16, (Gd, 32 * RB), dev),
+        _dev_arg("lora_act_dn", la, torch.float32, (M, rank_dn), dev) if rank_dn else None,
+        _ptr(workspace) if need else None, int(workspace.numel()) if (need and workspace is not None) else 0,
+        _stream(dev))
+    L.check(st, "svdq_gemm_w4a4_fp6_mlp_chain")
+    return xf, xs, la
+
+
 def lora_down(x: torch.Tensor, smooth_inv: torch.Tensor, lora_down_w: torch.Tensor, rank: int,
               group: int = 64, act: int = L.SVDQ_ACT_NONE, out: Optional[torch.Tensor] = None):
     """Unfused down projection (reads x again): lora_act [M][rank] fp32."""
