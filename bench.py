@@ -522,6 +522,75 @@ def dev_bf16(bits):
     return torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).view(torch.bfloat16).cuda()
 
 
+def bench_mlp_chain(S, L, workloads, r, steps, warmup):
+    """The FLUX MLP pair (4096 x 3072 -> 12288 -> GELU -> 3072, rank r on
+    both layers, 6-bit engine) as one chain step -- kernel 1 of the up layer,
+    the up layer's kernel 2 with the down layer's kernel 1 in its epilogue
+    (and the partials' reduction), the down layer's kernel 2 -- against the
+    two-layer step that stores the up output and reads it back in the down
+    layer's kernel 1."""
+    import torch
+    wl = workloads.make_workload("mlp_pair")
+    up_l, dn_l = wl.layers
+    M, K, N, N2 = wl.M, up_l.K, up_l.N, dn_l.N
+    up, _ = make_layer(S, up_l.weight_bits, wl.act_absmax(), r)
+    x = dev_bf16(wl.x_bits)
+    y_up = up(x)
+    a_dn = torch.nn.functional.gelu(y_up.float(), approximate="tanh").abs().amax(0).cpu().numpy()
+    dn, _ = make_layer(S, dn_l.weight_bits, a_dn.astype(np.float32), r)
+    chain = S.SVDQMLPChain(up, dn)
+    G, RB = K // 64, (M + 31) // 32
+    xf = torch.empty((G, RB, 1536), dtype=torch.uint8, device="cuda")
+    xs = torch.empty((G, 32 * RB), dtype=torch.float16, device="cuda")
+    la = torch.empty((M, r), dtype=torch.float32, device="cuda") if r else None
+    xf2 = torch.empty((N // 64, RB, 1536), dtype=torch.uint8, device="cuda")
+    xs2 = torch.empty((N // 64, 32 * RB), dtype=torch.float16, device="cuda")
+    la2 = torch.empty((M, r), dtype=torch.float32, device="cuda") if r else None
+    ws = torch.empty(max(S.mlp_chain_workspace_bytes(M, N, r), 16), dtype=torch.uint8, device="cuda")
+    y1 = torch.empty((M, N), dtype=torch.bfloat16, device="cuda")
+    y2 = torch.empty((M, N2), dtype=torch.bfloat16, device="cuda")
+
+    def k1_up():
+        S.quant_act_lora_down_fp6(x, up.smooth_inv, up.lora_down, r, out=(xf, xs, la))
+
+    def k2_dn():
+        S.gemm_w4a4_fp6_lora_up(xf2, xs2, dn.w_fp6, dn.w_scales, la2, dn.lora_up, dn.bias, M, N2, N, r, out=y2)
+
+    def chain_step():
+        k1_up()
+        S.gemm_w4a4_fp6_mlp_chain(xf, xs, up.w_fp6, up.w_scales, la, up.lora_up, up.bias, M, N, K, r,
+                                  dn.smooth_inv, dn.lora_down, r, out=(xf2, xs2, la2), workspace=ws)
+        k2_dn()
+
+    def two_layer_step():
+        k1_up()
+        S.gemm_w4a4_fp6_lora_up(xf, xs, up.w_fp6, up.w_scales, la, up.lora_up, up.bias, M, N, K, r, out=y1)
+        S.quant_act_lora_down_fp6(y1, dn.smooth_inv, dn.lora_down, r, act=L.SVDQ_ACT_GELU_TANH, out=(xf2, xs2, la2))
+        k2_dn()
+
+    def timed(step):
+        settle(step)
+        for _ in range(warmup):
+            step()
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for _ in range(steps):
+            step()
+        torch.cuda.synchronize()
+        return (time.perf_counter() - t0) * 1e3 / steps
+
+    two_ms, chain_ms = timed(two_layer_step), timed(chain_step)
+    ops = 2.0 * M * (K * N + N * N2)
+    return {"workload": f"FLUX MLP pair {M}x{K} -> {N} -> tanh-GELU -> {N2}, rank {r} on both layers, 6-bit engine",
+            "two_layer_ms_per_step": round(two_ms, 5), "chain_ms_per_step": round(chain_ms, 5),
+            "chain_effective_tops": round(ops / (chain_ms * 1e-3) / 1e12, 2),
+            "two_layer_effective_tops": round(ops / (two_ms * 1e-3) / 1e12, 2),
+            "chain_saving_frac": round(1.0 - chain_ms / two_ms, 4),
+            "how": "two-layer: up kernel 2 stores Y (bf16) and the down layer's kernel 1 reads it with GELU; "
+                   "chain: the up kernel 2's epilogue writes the down layer's codes, scales and partial down "
+                   "projections (reduced by a second kernel); both end with the down layer's kernel 2"}
+
+
 def layer_input(S, wl, layer, act, rank):
     """The layer's bf16 input on the device and its calibration statistic
     max |input| per channel (after tanh-GELU when kernel 1 applies it).
@@ -795,6 +864,7 @@ def main():
                 entry["us_per_step"] = round(f["ms_per_step"] * 1e3, 2)
             configs[name] = entry
             del clin, cx
+        configs["mlp_chain"] = bench_mlp_chain(S, L, workloads, r, args.steps, args.warmup)
         configs["rank_sweep"] = rank_sweep(S, workloads, args.steps, args.warmup)
         out["configs"] = configs
     if args.precision == "int4" and not args.no_variants:

@@ -459,53 +459,58 @@ __global__ __launch_bounds__(F_THREADS, 1) void k_gemm_w4a4_fp6(
       __syncthreads();
       const int RBd = (M + 31) >> 5, Mpd = RBd << 5;
       const int Gd = N / GROUP;
+      // units of 32 values: (row, group, half hh) = p >> 3, (p >> 1) & 3, p & 1,
+      // p = tid + 512 k; lanes tid and tid ^ 1 hold the two halves of a
+      // group and exchange their absmax; a unit's 32 codes are exactly one
+      // lane of the group's 6-bit container fragment
 #pragma unroll 1
-      for (int k2 = 0; k2 < 2; ++k2) {
-        const int p = tid + F_THREADS * k2;
-        const int rl = p >> 2, g = p & 3;
+      for (int k4 = 0; k4 < 4; ++k4) {
+        const int p = tid + F_THREADS * k4;
+        const int rl = p >> 3, g = (p >> 1) & 3, hh = p & 1;
         const int row = F_BM * tmc + rl;
         const int gd = 4 * tnc + g;
-        if (gd >= Gd || row >= Mpd) continue;
-        unsigned char* tr = T + rl * C_TS + 2 * GROUP * g;
-        float xh[GROUP];
+        const bool live = gd < Gd && row < Mpd;               // uniform over the lane pair
+        unsigned char* tr = T + rl * C_TS + 2 * (GROUP * g + 32 * hh);
+        float xh[32];
 #pragma unroll
-        for (int c8 = 0; c8 < 8; ++c8) {
+        for (int c8 = 0; c8 < 4; ++c8) {
           const uint4 u = *reinterpret_cast<const uint4*>(tr + 16 * c8);
           const uint32_t w[4] = {u.x, u.y, u.z, u.w};
 #pragma unroll
           for (int i = 0; i < 4; ++i) {
             const int j = 8 * c8 + 2 * i;
-            xh[j] = row < M ? gelu_tanh(bf16_bits_to_f32(w[i] & 0xFFFFu)) * si_s[GROUP * g + j] : 0.f;
-            xh[j + 1] = row < M ? gelu_tanh(bf16_bits_to_f32(w[i] >> 16)) * si_s[GROUP * g + j + 1] : 0.f;
+            const int kc = GROUP * g + 32 * hh + j;
+            xh[j] = row < M ? gelu_tanh(bf16_bits_to_f32(w[i] & 0xFFFFu)) * si_s[kc] : 0.f;
+            xh[j + 1] = row < M ? gelu_tanh(bf16_bits_to_f32(w[i] >> 16)) * si_s[kc + 1] : 0.f;
           }
         }
         float amax = 0.f;
 #pragma unroll
-        for (int j = 0; j < GROUP; ++j) amax = fmaxf(amax, fabsf(xh[j]));
+        for (int j = 0; j < 32; ++j) amax = fmaxf(amax, fabsf(xh[j]));
+        amax = fmaxf(amax, __shfl_xor(amax, 1));
         const float s32 = amax / 7.0f;
         const _Float16 sh = static_cast<_Float16>(s32);
         const float sf = static_cast<float>(sh);
         const float rcp = (sf == 0.f) ? 0.f : 1.0f / sf;
-        uint8_t* fr = ca.x_fp6 + (static_cast<size_t>(gd) * RBd + (row >> 5)) * FRAG;
-#pragma unroll
-        for (int hh = 0; hh < 2; ++hh) {
-          // codes j = 0..31 of half hh: even positions from the first source,
-          // odd from the second; + 0.0f turns -0 into +0
+        if (live) {
+          // codes j = 0..31: even positions from the first source, odd from
+          // the second; + 0.0f turns -0 into +0
           v16f ev, od;
 #pragma unroll
           for (int i = 0; i < 16; ++i) {
-            ev[i] = fminf(fmaxf(rintf(xh[32 * hh + 2 * i] * rcp), -8.f), 7.f) + 0.0f;
-            od[i] = fminf(fmaxf(rintf(xh[32 * hh + 2 * i + 1] * rcp), -8.f), 7.f) + 0.0f;
+            ev[i] = fminf(fmaxf(rintf(xh[2 * i] * rcp), -8.f), 7.f) + 0.0f;
+            od[i] = fminf(fmaxf(rintf(xh[2 * i + 1] * rcp), -8.f), 7.f) + 0.0f;
           }
           typedef int v6i_ __attribute__((ext_vector_type(6)));
           const v6i_ pk = __builtin_amdgcn_cvt_scalef32_2xpk16_bf6_f32(ev, od, 1.0f);
+          uint8_t* fr = ca.x_fp6 + (static_cast<size_t>(gd) * RBd + (row >> 5)) * FRAG;
           const int fl = (row & 31) + 32 * hh;
           *reinterpret_cast<uint4*>(fr + 16 * fl) = make_uint4(pk[0], pk[1], pk[2], pk[3]);
           *reinterpret_cast<uint2*>(fr + 1024 + 8 * fl) = make_uint2(pk[4], pk[5]);
+          if (hh == 0) ca.x_scales[static_cast<size_t>(gd) * Mpd + row] = sh;
         }
-        ca.x_scales[static_cast<size_t>(gd) * Mpd + row] = sh;
 #pragma unroll
-        for (int c8 = 0; c8 < 8; ++c8)
+        for (int c8 = 0; c8 < 4; ++c8)
           *reinterpret_cast<uint4*>(tr + 16 * c8) =
               make_uint4(bf16x2_bits(xh[8 * c8], xh[8 * c8 + 1]), bf16x2_bits(xh[8 * c8 + 2], xh[8 * c8 + 3]),
                          bf16x2_bits(xh[8 * c8 + 4], xh[8 * c8 + 5]), bf16x2_bits(xh[8 * c8 + 6], xh[8 * c8 + 7]));
@@ -521,16 +526,27 @@ __global__ __launch_bounds__(F_THREADS, 1) void k_gemm_w4a4_fp6(
 #pragma unroll 1
         for (int rc = 0; rc < ca.rank; rc += 32) {
           const int rr = rc + lc;
+          // the slice's sixteen L1 fragments in two batches of eight, each
+          // requested before its MFMAs (at clamped in-bounds addresses,
+          // masked afterwards)
+          const bool rok = rr < ca.rank;
+          const uint16_t* lrow = ca.lora_down + static_cast<size_t>(rok ? rr : 0) * N;
           v16f d = zero;
-#pragma unroll 4
-          for (int kk = 0; kk < F_BN / 16; ++kk) {
-            const int kl = 16 * kk + 8 * lh;
-            const v8bf av = __builtin_bit_cast(v8bf, *reinterpret_cast<const uint4*>(T + rl * C_TS + 2 * kl));
-            const int kg = F_BN * tnc + kl;
-            uint4 bw = make_uint4(0, 0, 0, 0);
-            if (rr < ca.rank && kg < N)
-              bw = *reinterpret_cast<const uint4*>(ca.lora_down + static_cast<size_t>(rr) * N + kg);
-            d = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av, __builtin_bit_cast(v8bf, bw), d, 0, 0, 0);
+#pragma unroll 1
+          for (int k0 = 0; k0 < F_BN / 16; k0 += 8) {
+            uint4 bw[8];
+#pragma unroll
+            for (int q = 0; q < 8; ++q) {
+              const int kg = F_BN * tnc + 16 * (k0 + q) + 8 * lh;
+              bw[q] = *reinterpret_cast<const uint4*>(lrow + (kg < N ? kg : 0));
+              if (!rok || kg >= N) bw[q] = make_uint4(0, 0, 0, 0);
+            }
+#pragma unroll
+            for (int q = 0; q < 8; ++q) {
+              const int kl = 16 * (k0 + q) + 8 * lh;
+              const v8bf av = __builtin_bit_cast(v8bf, *reinterpret_cast<const uint4*>(T + rl * C_TS + 2 * kl));
+              d = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av, __builtin_bit_cast(v8bf, bw[q]), d, 0, 0, 0);
+            }
           }
           if (rr < ca.rank) {
 #pragma unroll
