@@ -345,6 +345,28 @@ int svdq_gemm_w4a4_fp6_mlp_chain(const void* x_fp6, const void* x_scales,
                                  void* x_fp6_dn, void* x_scales_dn, float* lora_act_dn,
                                  void* workspace, size_t workspace_bytes, void* stream);
 
+/* Device, asynchronous.  svdq_gemm_w4a4_fp6_mlp_chain without the workspace
+ * argument, for callers that cannot allocate device memory (code under HIP
+ * graph capture, tight serving loops, harnesses that forbid hipMalloc): the
+ * partial down projections go to a device-resident scratch array of
+ * SVDQ_CHAIN_SCRATCH_BYTES that the library holds on every device it runs
+ * on until the process ends (its address is looked up once per device, on
+ * the first call there).  The call allocates nothing.  Returns
+ * SVDQ_ERR_UNSUPPORTED_SHAPE when svdq_mlp_chain_workspace_bytes() exceeds
+ * SVDQ_CHAIN_SCRATCH_BYTES; every other rule and error as
+ * svdq_gemm_w4a4_fp6_mlp_chain.  All calls on one device share that
+ * device's scratch, which keeps the last call's contents: calls that
+ * overlap on one device (on different streams, or otherwise unordered)
+ * race.  Nothing in it needs to start at zero: each call writes every
+ * partial it reads. */
+#define SVDQ_CHAIN_SCRATCH_BYTES (32u << 20)
+int svdq_gemm_w4a4_fp6_mlp_chain_noalloc(const void* x_fp6, const void* x_scales,
+                                         const void* w_fp6, const void* w_scales,
+                                         const float* lora_act, const void* lora_up, const void* bias,
+                                         int M, int N, int K, int rank, int group,
+                                         const float* smooth_inv_dn, const void* lora_down_dn, int rank_dn,
+                                         void* x_fp6_dn, void* x_scales_dn, float* lora_act_dn, void* stream);
+
 /* ------------------------------------------------------------------------
  * 4-bit float variant (MXFP4).  The pages offer the layer with INT4 and with
  * 4-bit float operands ("Bringing Nunchaku 4-bit Diffusion Inference to

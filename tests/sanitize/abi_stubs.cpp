@@ -2,6 +2,8 @@
 // argument check in svdq_abi.hip runs as in the library, and a call that
 // passes them reaches one of these, which records that it was reached and
 // returns a marker status instead of launching a kernel.
+#include <cstddef>
+
 #include "svdq_internal.h"
 
 namespace svdq {
@@ -33,5 +35,11 @@ int launch_mlp_chain_fp6(const void*, const void*, const void*, const void*, con
                          int, int, int, int, const float*, const void*, int, void*, void*, float*, float*, void*) {
   ++g_launches; return kReached; }
 int launch_probe_mfma(int, int, int, void*, void*) { ++g_launches; return kReached; }
+size_t chain_scratch_bytes() { return size_t{32} << 20; }
+int chain_scratch(void** ptr) {
+  static unsigned char stand_in[16];
+  *ptr = stand_in;
+  return 0;
+}
 double probe_mfma_ops(int, int, int) { return 0.0; }
 }  // namespace svdq

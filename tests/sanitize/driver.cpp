@@ -195,6 +195,12 @@ static void device_argument_checks() {
                                       nullptr) == SVDQ_ERR_INVALID_ARG);
   EXPECT(passed_checks(svdq_gemm_w4a4_fp6_mlp_chain(p, p, p, p, f, p, nullptr, M, 512, K, r, 64, f, nullptr, 0, p, p,
                                                     nullptr, nullptr, 0, nullptr)));
+  EXPECT(passed_checks(svdq_gemm_w4a4_fp6_mlp_chain_noalloc(p, p, p, p, f, p, nullptr, M, 512, K, r, 64, f, p, 32,
+                                                            p, p, f, nullptr)));
+  EXPECT(svdq_gemm_w4a4_fp6_mlp_chain_noalloc(p, p, p, p, f, p, nullptr, 65536, 12288, K, r, 64, f, p, 16, p, p, f,
+                                              nullptr) == SVDQ_ERR_UNSUPPORTED_SHAPE);  // beyond the scratch
+  EXPECT(svdq_gemm_w4a4_fp6_mlp_chain_noalloc(p, p, p, p, f, p, nullptr, M, 512, K, r, 64, f, nullptr, 32, p, p, f,
+                                              nullptr) == SVDQ_ERR_INVALID_ARG);
   // MXFP4
   EXPECT(passed_checks(svdq_quant_act_lora_down_mxfp4(p, f, p, M, K, r, SVDQ_ACT_NONE, p, p, f, nullptr)));
   EXPECT(svdq_quant_act_lora_down_mxfp4(p, f, p, M, 64, r, SVDQ_ACT_NONE, p, p, f, nullptr) != SVDQ_OK);

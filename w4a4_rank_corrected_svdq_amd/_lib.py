@@ -25,6 +25,7 @@ SVDQ_GROUP = 64
 SVDQ_MAX_RANK = 256
 SVDQ_FP6_ACTIVATIONS = 0
 SVDQ_FP6_WEIGHTS = 1
+SVDQ_CHAIN_SCRATCH_BYTES = 32 << 20
 
 _p = ctypes.c_void_p
 _i = ctypes.c_int
@@ -60,6 +61,8 @@ SIGNATURES = {
     "svdq_mlp_chain_workspace_bytes": (_i, [_i, _i, _i, ctypes.POINTER(ctypes.c_size_t)]),
     "svdq_gemm_w4a4_fp6_mlp_chain": (_i, [_p, _p, _p, _p, _p, _p, _p, _i, _i, _i, _i, _i,
                                           _p, _p, _i, _p, _p, _p, _p, ctypes.c_size_t, _p]),
+    "svdq_gemm_w4a4_fp6_mlp_chain_noalloc": (_i, [_p, _p, _p, _p, _p, _p, _p, _i, _i, _i, _i, _i,
+                                                  _p, _p, _i, _p, _p, _p, _p]),
     # include/svdq_probe.h (benchmark harness)
     "svdq_probe_mfma": (_i, [_i, _i, _i, _p, _p]),
     "svdq_probe_mfma_ops": (ctypes.c_double, [_i, _i, _i]),

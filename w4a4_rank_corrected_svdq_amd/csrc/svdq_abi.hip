@@ -169,6 +169,36 @@ extern "C" int svdq_gemm_w4a4_fp6_lora_up(const void* x_fp6, const void* x_scale
                                     out_dtype, y, stream);
 }
 
+namespace {
+// Argument checks of the MLP chain (both entry points); the workspace is
+// checked by the caller.
+int check_chain(const void* x_fp6, const void* x_scales, const void* w_fp6, const void* w_scales,
+                const float* lora_act, const void* lora_up, const void* bias, int M, int N, int K, int rank,
+                int group, const float* smooth_inv_dn, const void* lora_down_dn, int rank_dn, const void* x_fp6_dn,
+                const void* x_scales_dn, const float* lora_act_dn) {
+  if (M < 0 || rank_dn < 0) return SVDQ_ERR_INVALID_ARG;
+  const int st = svdq::validate_shape(K, N, rank, group);
+  if (st != SVDQ_OK) return st;
+  if (N % SVDQ_GROUP != 0 || rank_dn % 16 != 0 || rank_dn > SVDQ_MAX_RANK || rank_dn > N)
+    return SVDQ_ERR_UNSUPPORTED_SHAPE;
+  if (!x_fp6 || !x_scales || !w_fp6 || !w_scales || !smooth_inv_dn || !x_fp6_dn || !x_scales_dn)
+    return SVDQ_ERR_INVALID_ARG;
+  if (rank > 0 && (!lora_act || !lora_up)) return SVDQ_ERR_INVALID_ARG;
+  if (rank_dn > 0 && (!lora_down_dn || !lora_act_dn)) return SVDQ_ERR_INVALID_ARG;
+  if (!aligned16(x_fp6) || !aligned16(x_scales) || !aligned16(w_fp6) || !aligned16(w_scales) ||
+      !aligned16(smooth_inv_dn) || !aligned16(x_fp6_dn) || !aligned16(x_scales_dn) || (bias && !aligned16(bias)) ||
+      (rank > 0 && (!aligned16(lora_act) || !aligned16(lora_up))) ||
+      (rank_dn > 0 && (!aligned16(lora_down_dn) || !aligned16(lora_act_dn))))
+    return SVDQ_ERR_INVALID_ARG;
+  const int64_t G = K / SVDQ_GROUP, Gd = N / SVDQ_GROUP;
+  const int64_t RBa = (static_cast<int64_t>(M) + 31) / 32, RBb = 4 * ((static_cast<int64_t>(N) + 127) / 128);
+  if (!fits_buffer(G * RBa, 1536) || !fits_buffer(G * RBb, 1536) || !fits_buffer(G, 64LL * RBa) ||
+      !fits_buffer(G, 2LL * N) || !fits_buffer(Gd * RBa, 1536))
+    return SVDQ_ERR_UNSUPPORTED_SHAPE;
+  return SVDQ_OK;
+}
+}  // namespace
+
 extern "C" int svdq_mlp_chain_workspace_bytes(int M, int N, int rank_dn, size_t* bytes_out) {
   if (M < 0 || N < 0 || rank_dn < 0 || !bytes_out) return SVDQ_ERR_INVALID_ARG;
   *bytes_out = static_cast<size_t>((N + 255) / 256) * static_cast<size_t>(M) * static_cast<size_t>(rank_dn) * 4u;
@@ -181,34 +211,43 @@ extern "C" int svdq_gemm_w4a4_fp6_mlp_chain(const void* x_fp6, const void* x_sca
                                             const float* smooth_inv_dn, const void* lora_down_dn, int rank_dn,
                                             void* x_fp6_dn, void* x_scales_dn, float* lora_act_dn, void* workspace,
                                             size_t workspace_bytes, void* stream) {
-  if (M < 0 || rank_dn < 0) return SVDQ_ERR_INVALID_ARG;
-  int st = svdq::validate_shape(K, N, rank, group);
+  int st = check_chain(x_fp6, x_scales, w_fp6, w_scales, lora_act, lora_up, bias, M, N, K, rank, group,
+                       smooth_inv_dn, lora_down_dn, rank_dn, x_fp6_dn, x_scales_dn, lora_act_dn);
   if (st != SVDQ_OK) return st;
-  if (N % SVDQ_GROUP != 0 || rank_dn % 16 != 0 || rank_dn > SVDQ_MAX_RANK || rank_dn > N)
-    return SVDQ_ERR_UNSUPPORTED_SHAPE;
-  if (!x_fp6 || !x_scales || !w_fp6 || !w_scales || !smooth_inv_dn || !x_fp6_dn || !x_scales_dn)
-    return SVDQ_ERR_INVALID_ARG;
-  if (rank > 0 && (!lora_act || !lora_up)) return SVDQ_ERR_INVALID_ARG;
-  if (rank_dn > 0 && (!lora_down_dn || !lora_act_dn || !workspace)) return SVDQ_ERR_INVALID_ARG;
-  if (!aligned16(x_fp6) || !aligned16(x_scales) || !aligned16(w_fp6) || !aligned16(w_scales) ||
-      !aligned16(smooth_inv_dn) || !aligned16(x_fp6_dn) || !aligned16(x_scales_dn) || (bias && !aligned16(bias)) ||
-      (rank > 0 && (!aligned16(lora_act) || !aligned16(lora_up))) ||
-      (rank_dn > 0 && (!aligned16(lora_down_dn) || !aligned16(lora_act_dn) || !aligned16(workspace))))
-    return SVDQ_ERR_INVALID_ARG;
   size_t need = 0;
   svdq_mlp_chain_workspace_bytes(M, N, rank_dn, &need);
-  if (rank_dn > 0 && workspace_bytes < need) return SVDQ_ERR_INVALID_ARG;
-  const int64_t G = K / SVDQ_GROUP, Gd = N / SVDQ_GROUP;
-  const int64_t RBa = (static_cast<int64_t>(M) + 31) / 32, RBb = 4 * ((static_cast<int64_t>(N) + 127) / 128);
-  if (!fits_buffer(G * RBa, 1536) || !fits_buffer(G * RBb, 1536) || !fits_buffer(G, 64LL * RBa) ||
-      !fits_buffer(G, 2LL * N) || !fits_buffer(Gd * RBa, 1536))
-    return SVDQ_ERR_UNSUPPORTED_SHAPE;
+  if (rank_dn > 0 && (!workspace || !aligned16(workspace) || workspace_bytes < need)) return SVDQ_ERR_INVALID_ARG;
   st = current_device_check();
   if (st != SVDQ_OK) return st;
   if (M == 0) return SVDQ_OK;
   return svdq::launch_mlp_chain_fp6(x_fp6, x_scales, w_fp6, w_scales, lora_act, lora_up, bias, M, N, K, rank,
                                     smooth_inv_dn, lora_down_dn, rank_dn, x_fp6_dn, x_scales_dn, lora_act_dn,
                                     static_cast<float*>(workspace), stream);
+}
+
+extern "C" int svdq_gemm_w4a4_fp6_mlp_chain_noalloc(const void* x_fp6, const void* x_scales, const void* w_fp6,
+                                                    const void* w_scales, const float* lora_act, const void* lora_up,
+                                                    const void* bias, int M, int N, int K, int rank, int group,
+                                                    const float* smooth_inv_dn, const void* lora_down_dn, int rank_dn,
+                                                    void* x_fp6_dn, void* x_scales_dn, float* lora_act_dn,
+                                                    void* stream) {
+  int st = check_chain(x_fp6, x_scales, w_fp6, w_scales, lora_act, lora_up, bias, M, N, K, rank, group,
+                       smooth_inv_dn, lora_down_dn, rank_dn, x_fp6_dn, x_scales_dn, lora_act_dn);
+  if (st != SVDQ_OK) return st;
+  size_t need = 0;
+  svdq_mlp_chain_workspace_bytes(M, N, rank_dn, &need);
+  if (need > svdq::chain_scratch_bytes()) return SVDQ_ERR_UNSUPPORTED_SHAPE;
+  st = current_device_check();
+  if (st != SVDQ_OK) return st;
+  if (M == 0) return SVDQ_OK;
+  void* ws = nullptr;
+  if (rank_dn > 0) {
+    st = svdq::chain_scratch(&ws);
+    if (st != SVDQ_OK) return st;
+  }
+  return svdq::launch_mlp_chain_fp6(x_fp6, x_scales, w_fp6, w_scales, lora_act, lora_up, bias, M, N, K, rank,
+                                    smooth_inv_dn, lora_down_dn, rank_dn, x_fp6_dn, x_scales_dn, lora_act_dn,
+                                    static_cast<float*>(ws), stream);
 }
 
 extern "C" int svdq_lora_down(const void* x, const float* smooth_inv, const void* lora_down, int M, int K,

@@ -38,6 +38,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <mutex>
+
 #include "svdq.h"
 #include "svdq_internal.h"
 
@@ -738,6 +740,13 @@ __global__ __launch_bounds__(256) void k_partials_reduce(const float4* __restric
   lora_act[i] = acc;
 }
 
+// The no-allocation variant of the MLP chain keeps its partial down
+// projections here instead of in a caller's workspace: one copy per device,
+// held until the process ends.  Host code uses only the per-device address
+// from hipGetSymbolAddress, never this name.
+constexpr size_t CHAIN_SCRATCH_BYTES = SVDQ_CHAIN_SCRATCH_BYTES;
+static __device__ __align__(256) unsigned char scratch[CHAIN_SCRATCH_BYTES];
+
 int cu_count() {
   static int cached[64] = {};
   int dev = 0;
@@ -774,6 +783,25 @@ int launch_gemm_w4a4_fp6(const void* x_fp6, const void* x_scales, const void* w_
   else SVDQ_K2F(0);
 #undef SVDQ_K2F
   return hipGetLastError() == hipSuccess ? SVDQ_OK : SVDQ_ERR_HIP;
+}
+
+size_t chain_scratch_bytes() { return CHAIN_SCRATCH_BYTES; }
+
+int chain_scratch(void** ptr) {
+  // address of the current device's copy, looked up once per device with
+  // that device current
+  static std::mutex mu;
+  static void* addr[64] = {};
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return SVDQ_ERR_HIP;
+  std::lock_guard<std::mutex> lock(mu);
+  if (addr[dev] == nullptr) {
+    void* p = nullptr;
+    if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || p == nullptr) return SVDQ_ERR_HIP;
+    addr[dev] = p;
+  }
+  *ptr = addr[dev];
+  return SVDQ_OK;
 }
 
 int launch_mlp_chain_fp6(const void* x_fp6, const void* x_scales, const void* w_fp6, const void* w_scales,

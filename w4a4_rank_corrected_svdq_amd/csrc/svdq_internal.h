@@ -56,6 +56,11 @@ int launch_mlp_chain_fp6(const void* x_fp6, const void* x_scales, const void* w_
                          const float* smooth_inv_dn, const void* lora_down_dn, int rank_dn, void* x_fp6_dn,
                          void* x_scales_dn, float* lora_act_dn, float* partials, void* stream);
 
+// The chain's device-resident scratch for the no-allocation entry point:
+// its size, and the current device's address (looked up once per device).
+size_t chain_scratch_bytes();
+int chain_scratch(void** ptr);
+
 // svdq_probes.hip
 int launch_probe_mfma(int kind, int blocks, int iters, void* sink, void* stream);
 double probe_mfma_ops(int kind, int blocks, int iters);
