@@ -135,11 +135,12 @@ def run_k1(x_bits, smooth_inv, lora_down_bits, rank, act=L.SVDQ_ACT_NONE):
     return xf, xs, la
 
 
-# (4200, 256, 32) and (4111, 192, 64): more 16-row blocks than an MI355X has
-# CUs, so kernel 1 runs its 32-row blocks; odd M leaves padded rows
+# (4200, 256, 32), (4111, 192, 64) and, at ranks 65-128, (8200, 128, 128):
+# enough rows for kernel 1's 32-row blocks; odd M leaves padded rows
 @pytest.mark.parametrize("M,K,rank", [(300, 512, 32), (1, 64, 16), (16, 128, 0), (257, 1024, 48),
                                       (64, 512, 128), (33, 256, 256), (77, 3072, 32), (40, 12288, 64),
-                                      (1000, 1088, 16), (129, 2112, 256), (4200, 256, 32), (4111, 192, 64)])
+                                      (1000, 1088, 16), (129, 2112, 256), (4200, 256, 32), (4111, 192, 64),
+                                      (8200, 128, 128)])
 def test_k1_codes_scales_lora_act(M, K, rank):
     N = max(64, ((rank + 7) // 8) * 8)
     wl, Lr, po, abi = _case(M, K, N, rank, seed=42 + M)
@@ -182,12 +183,13 @@ def test_k1_matches_nibble_kernel():
     np.testing.assert_array_equal(xs.cpu().numpy()[:, :M], xs2.cpu().numpy())
 
 
-def test_k1_gelu_statistical():
+@pytest.mark.parametrize("M,K,rank", [(256, 3072, 32), (8200, 256, 128)])
+def test_k1_gelu_statistical(M, K, rank):
     """GELU on load: GPU tanhf and fp64 tanh differ by a few ulps, so codes
     may differ at rounding boundaries (by 1, in at most 1e-4 of them) and
-    scales by at most one fp16 ulp."""
-    M, K, rank = 256, 3072, 32
-    wl, Lr, po, abi = _case(M, K, 64, rank, seed=11)
+    scales by at most one fp16 ulp.  (8200, 256, 128) runs the 32-row
+    blocks of ranks 65-128."""
+    wl, Lr, po, abi = _case(M, K, max(64, rank), rank, seed=11)
     xb = f64_to_bf16_bits(wl.x)
     xf, xs, la = run_k1(xb, abi["smooth_inv"], abi["lora_down"], rank, act=L.SVDQ_ACT_GELU_TANH)
     q, s, xh = O.quantize_activation(wl.x, po["smooth_inv"], 64, act="gelu_tanh")

@@ -149,7 +149,8 @@ def _small_case(M=300, K=512, N=264, rank=32, seed=41, bias=False, n_out=4):
 # (4200, 256, 32) and (4111, 192, 64): more 16-row blocks than an MI355X has
 # CUs, so kernel 1 runs its 32-row blocks
 @pytest.mark.parametrize("M,K,rank", [(300, 512, 32), (1, 64, 16), (16, 128, 0), (257, 1024, 48),
-                                      (64, 512, 128), (33, 256, 256), (4200, 256, 32), (4111, 192, 64)])
+                                      (64, 512, 128), (33, 256, 256), (4200, 256, 32), (4111, 192, 64),
+                                      (8200, 128, 128)])
 def test_k1_codes_scales_lora_act(M, K, rank):
     N = max(8, ((rank + 7) // 8) * 8, 64)
     wl, Lr, po, abi = _small_case(M, K, N, rank, seed=42 + M)

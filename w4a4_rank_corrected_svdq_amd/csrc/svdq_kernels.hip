@@ -1318,6 +1318,16 @@ int launch_k1_nt(const void* x, const float* smooth_inv, const void* lora_down, 
                   void* x_codes, void* x_scales, float* lora_act, hipStream_t st) {
   const size_t red1 = sizeof(float) * K1_MAX_WAVES * 2 * K1_ROWS * 16;
   const size_t smem1 = static_cast<size_t>(K) * sizeof(float) + red1;
+  if constexpr (NT == 8) {
+    // ranks 65..128 (8-wave blocks, 256 registers): 32-row blocks while they
+    // still fill the chip read half the L1 bytes per row (at M = 16384 each
+    // 16-row block would read 786 KB of L1 for 96 KB of X); 64-row blocks
+    // would spill
+    const size_t smem2 = static_cast<size_t>(K) * sizeof(float) + sizeof(float) * 8 * 2 * K1_ROWS * 2 * 16;
+    if ((M + 2 * K1_ROWS - 1) / (2 * K1_ROWS) >= device_cu_count() && smem2 <= 160 * 1024)
+      return launch_k1_kernel<ACT, NT, QM, 2>(x, smooth_inv, lora_down, M, K, rank, x_codes, x_scales, lora_act,
+                                              smem2, st);
+  }
   if constexpr (NT > 0 && NT <= 4 && ACT == SVDQ_ACT_NONE) {
     const bool many = (M + K1_ROWS - 1) / K1_ROWS > device_cu_count();
     if (many && smem1 + red1 <= 160 * 1024)
