@@ -135,12 +135,14 @@ def run_k1(x_bits, smooth_inv, lora_down_bits, rank, act=L.SVDQ_ACT_NONE):
     return xf, xs, la
 
 
-# (4200, 256, 32), (4111, 192, 64) and, at ranks 65-128, (8200, 128, 128):
-# enough rows for kernel 1's 32-row blocks; odd M leaves padded rows
+# (4200, 256, 32), at ranks 49-64 (8230, 192, 64) (more 32-row blocks than
+# CUs: the 8-wave form) and, at ranks 65-128, (8200, 128, 128): enough rows
+# for kernel 1's 32-row blocks; (4111, 192, 64) stays on 16-row blocks; odd
+# M leaves padded rows
 @pytest.mark.parametrize("M,K,rank", [(300, 512, 32), (1, 64, 16), (16, 128, 0), (257, 1024, 48),
                                       (64, 512, 128), (33, 256, 256), (77, 3072, 32), (40, 12288, 64),
                                       (1000, 1088, 16), (129, 2112, 256), (4200, 256, 32), (4111, 192, 64),
-                                      (8200, 128, 128)])
+                                      (8230, 192, 64), (8200, 128, 128)])
 def test_k1_codes_scales_lora_act(M, K, rank):
     N = max(64, ((rank + 7) // 8) * 8)
     wl, Lr, po, abi = _case(M, K, N, rank, seed=42 + M)

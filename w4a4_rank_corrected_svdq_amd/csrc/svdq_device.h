@@ -39,10 +39,18 @@ __device__ __forceinline__ v8bf pack_bf16x8(const float* v) {
   return __builtin_bit_cast(v8bf, u);
 }
 
+// Tanh-form GELU, 0.5 x (1 + tanh u) with u = sqrt(2/pi) (x + 0.044715 x^3),
+// evaluated through the identity 0.5 (1 + tanh u) = 1 / (1 + e^(-2u)):
+// x / (1 + 2^(x (c1 + c3 x^2))), c1 = -2 sqrt(2/pi) / ln 2, c3 = 0.044715 c1.
+// One hardware exp2 and one reciprocal (about 1 ulp each) in place of a
+// tanh, and no cancellation in 1 + tanh u for negative x (the tanh form
+// loses up to ~1e-4 relative there in fp32; this one stays near 1e-6).
+// Large negative x gives e = +inf and a signed zero.
 __device__ __forceinline__ float gelu_tanh(float x) {
-  const float k0 = 0.7978845608028654f;  // sqrt(2/pi)
-  const float u = k0 * (x + 0.044715f * x * x * x);
-  return 0.5f * x * (1.0f + tanhf(u));
+  constexpr float c1 = -2.302208198144325f;
+  constexpr float c3 = -0.1029432395800235f;
+  const float e = __builtin_amdgcn_exp2f(x * (c1 + c3 * (x * x)));
+  return x * __builtin_amdgcn_rcpf(1.0f + e);
 }
 
 // Eight packed E2M1 codes: every -0 (nibble 1000b) becomes +0.  A nibble's

@@ -59,8 +59,10 @@ template <int NT> constexpr int k1_waves() { return NT <= 4 ? 16 : 8; }
 
 enum { Q_NONE = 0, Q_INT4 = 1, Q_MXFP4 = 2, Q_FP6 = 3 };
 
-template <int ACT, int NT, int QM, int RT>
-__global__ __launch_bounds__(k1_waves<NT>() * 64) void k_quant_act_lora_down(
+// WB is the largest block the instance is launched with (its register
+// budget: 128 VGPRs at 16 waves, 256 at 8).
+template <int ACT, int NT, int QM, int RT, int WB>
+__global__ __launch_bounds__(WB * 64) void k_quant_act_lora_down(
     const uint16_t* __restrict__ x, const float* __restrict__ smooth_inv,
     const uint16_t* __restrict__ lora_down, int M, int K, int rank,
     uint8_t* __restrict__ x_codes, void* __restrict__ x_scales_v, float* __restrict__ lora_act) {
@@ -68,7 +70,7 @@ __global__ __launch_bounds__(k1_waves<NT>() * 64) void k_quant_act_lora_down(
   float* s_si = reinterpret_cast<float*>(k1_smem_raw);   // [K]
   float* red = s_si + K;                                   // [waves][2][16 RT][16]
 
-  const int nwaves = blockDim.x >> 6;                   // k1_waves<NT>() or 8 (uniform)
+  const int nwaves = blockDim.x >> 6;                   // WB or 8 (uniform)
   const int lane = threadIdx.x & 63;
   const int wave = threadIdx.x >> 6;
   const int m0 = blockIdx.x * (K1_ROWS * RT);
@@ -1287,25 +1289,40 @@ int device_cu_count() {
   return cached[dev];
 }
 
-template <int ACT, int NT, int QM, int RT>
-int launch_k1_kernel(const void* x, const float* smooth_inv, const void* lora_down, int M, int K, int rank,
-                     void* x_codes, void* x_scales, float* lora_act, size_t smem, hipStream_t st) {
-  auto kern = k_quant_act_lora_down<ACT, NT, QM, RT>;
+template <int ACT, int NT, int QM, int RT, int WB>
+int launch_k1_instance(const void* x, const float* smooth_inv, const void* lora_down, int M, int K, int rank,
+                       void* x_codes, void* x_scales, float* lora_act, size_t smem, int blocks, int waves,
+                       hipStream_t st) {
+  auto kern = k_quant_act_lora_down<ACT, NT, QM, RT, WB>;
   // Dynamic LDS above the default 64 KB needs an opt-in; it is made once per
   // instantiation for the whole 160 KB a CU offers (the size depends on K).
   static const bool attr_ok =
       hipFuncSetAttribute(reinterpret_cast<const void*>(kern), hipFuncAttributeMaxDynamicSharedMemorySize,
                           160 * 1024) == hipSuccess;
   if (!attr_ok && smem > 64 * 1024) return SVDQ_ERR_HIP;
+  hipLaunchKernelGGL(kern, dim3(blocks), dim3(waves * 64), smem, st,
+                     static_cast<const uint16_t*>(x), smooth_inv, static_cast<const uint16_t*>(lora_down), M, K,
+                     rank, static_cast<uint8_t*>(x_codes), x_scales, lora_act);
+  return SVDQ_OK;
+}
+
+template <int ACT, int NT, int QM, int RT>
+int launch_k1_kernel(const void* x, const float* smooth_inv, const void* lora_down, int M, int K, int rank,
+                     void* x_codes, void* x_scales, float* lora_act, size_t smem, hipStream_t st) {
   // Grids larger than the CU count run 8-wave blocks, two per CU, instead of
   // a second round of 16-wave blocks.
   const int rows = QM == Q_FP6 ? 32 * ((M + 31) / 32) : M;   // FP6: the padded last row block too
   const int blocks = (rows + K1_ROWS * RT - 1) / (K1_ROWS * RT);
   const int waves = (k1_waves<NT>() == 16 && blocks > device_cu_count()) ? 8 : k1_waves<NT>();
-  hipLaunchKernelGGL(kern, dim3(blocks), dim3(waves * 64), smem, st,
-                     static_cast<const uint16_t*>(x), smooth_inv, static_cast<const uint16_t*>(lora_down), M, K,
-                     rank, static_cast<uint8_t*>(x_codes), x_scales, lora_act);
-  return SVDQ_OK;
+  // 32-row blocks of the 16-wave ranks launched as 8-wave blocks get the
+  // 8-wave register budget (the 6-bit mode would spill in 128 VGPRs).
+  if constexpr (RT == 2 && k1_waves<NT>() == 16) {
+    if (waves == 8)
+      return launch_k1_instance<ACT, NT, QM, RT, 8>(x, smooth_inv, lora_down, M, K, rank, x_codes, x_scales,
+                                                    lora_act, smem, blocks, waves, st);
+  }
+  return launch_k1_instance<ACT, NT, QM, RT, k1_waves<NT>()>(x, smooth_inv, lora_down, M, K, rank, x_codes,
+                                                              x_scales, lora_act, smem, blocks, waves, st);
 }
 
 // Every block reads all of L1 (K x rank bf16), twice its own X bytes at rank
@@ -1329,7 +1346,10 @@ int launch_k1_nt(const void* x, const float* smooth_inv, const void* lora_down, 
                                               smem2, st);
   }
   if constexpr (NT > 0 && NT <= 4 && ACT == SVDQ_ACT_NONE) {
-    const bool many = (M + K1_ROWS - 1) / K1_ROWS > device_cu_count();
+    bool many = (M + K1_ROWS - 1) / K1_ROWS > device_cu_count();
+    // the 6-bit mode at ranks 49..64 fits its registers only as 8-wave
+    // blocks, i.e. when the 32-row blocks themselves outnumber the CUs
+    if (QM == Q_FP6 && NT == 4) many = (M + 2 * K1_ROWS - 1) / (2 * K1_ROWS) > device_cu_count();
     if (many && smem1 + red1 <= 160 * 1024)
       return launch_k1_kernel<ACT, NT, QM, 2>(x, smooth_inv, lora_down, M, K, rank, x_codes, x_scales, lora_act,
                                               smem1 + red1, st);
