@@ -132,7 +132,12 @@ int svdq_prepare_weights_ex(const uint16_t* weight, int K, int N,
  * the down projection and the quantizer share their input).
  *
  *   x          [M][K]      bf16  input activations (with act = GELU_TANH,
- *                                tanh-GELU is applied to x first, in fp32)
+ *                                tanh-GELU is applied to x first, in fp32,
+ *                                as x / (1 + 2^(x (c1 + c3 x^2))) with the
+ *                                hardware exp2 and reciprocal: the same
+ *                                function, ~1e-6 relative, so a code may
+ *                                differ by one from an fp64 GELU's where a
+ *                                value sits on a rounding boundary)
  *   smooth_inv [K]         fp32
  *   lora_down  [rank][K]   bf16  (NULL allowed when rank == 0)
  * Outputs:
