@@ -168,10 +168,10 @@ def test_k1_codes_scales_lora_act(M, K, rank):
 
 @pytest.mark.parametrize("M,K", [(512, 1024), (4200, 256)])
 def test_k1_gelu_statistical(M, K):
-    """tanh-GELU on load: GPU tanhf and the oracle's fp64 tanh differ by a few
-    ulps, so a code can differ where a value sits on a rounding boundary.
-    M = 4200 has more 16-row blocks than an MI355X has CUs, which with the
-    GELU prologue run as 8-wave blocks, two per CU."""
+    """tanh-GELU on load: the device GELU and the oracle's fp64 tanh differ by
+    a few ulps, so a code can differ where a value sits on a rounding
+    boundary.  M = 4200 has more 16-row blocks than an MI355X has CUs, so
+    kernel 1 runs 32-row blocks of 8 waves, with the GELU prologue."""
     rank = 32
     wl, Lr, po, abi = _small_case(M, K, 64, rank, seed=43)
     xc, xs, la = run_k1(wl.x_bits, abi["smooth_inv"], abi["lora_down"], rank, act=L.SVDQ_ACT_GELU_TANH)

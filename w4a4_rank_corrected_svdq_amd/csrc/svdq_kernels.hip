@@ -1328,8 +1328,9 @@ int launch_k1_kernel(const void* x, const float* smooth_inv, const void* lora_do
 // Every block reads all of L1 (K x rank bf16), twice its own X bytes at rank
 // 32, so once the 16-row blocks outnumber the CUs (M = 4608 and up) blocks of
 // 32 rows, which use each L1 fragment for both row tiles, move a third fewer
-// bytes per CU.  Up to rank 64, while the doubled reduction buffer fits LDS,
-// and without the GELU prologue (its registers would spill).
+// bytes per CU.  Up to rank 64 while the doubled reduction buffer fits LDS
+// (with the GELU prologue too: its exp2-and-reciprocal form fits the same
+// registers).
 template <int ACT, int QM, int NT>
 int launch_k1_nt(const void* x, const float* smooth_inv, const void* lora_down, int M, int K, int rank,
                   void* x_codes, void* x_scales, float* lora_act, hipStream_t st) {
@@ -1345,7 +1346,7 @@ int launch_k1_nt(const void* x, const float* smooth_inv, const void* lora_down, 
       return launch_k1_kernel<ACT, NT, QM, 2>(x, smooth_inv, lora_down, M, K, rank, x_codes, x_scales, lora_act,
                                               smem2, st);
   }
-  if constexpr (NT > 0 && NT <= 4 && ACT == SVDQ_ACT_NONE) {
+  if constexpr (NT > 0 && NT <= 4) {
     bool many = (M + K1_ROWS - 1) / K1_ROWS > device_cu_count();
     // the 6-bit mode at ranks 49..64 fits its registers only as 8-wave
     // blocks, i.e. when the 32-row blocks themselves outnumber the CUs
