@@ -96,8 +96,9 @@ def test_k1_mx_codes_scales_bit_exact(M, K, rank):
 
 
 def test_k1_mx_gelu_statistical():
-    """tanh-GELU on load: device tanh vs fp64 tanh may move a value across a
-    rounding boundary; codes differ rarely and by one grid step."""
+    """tanh-GELU on load: the device GELU (exp2 and reciprocal, fp32) vs the
+    oracle's fp64 tanh may move a value across a rounding boundary; codes
+    differ rarely and by one grid step."""
     M, K = 256, 1024
     wl, Lr, po, abi = _case(M, K, 128, 32, seed=96)
     xc, xs, la = run_k1(wl.x_bits, abi, act=L.SVDQ_ACT_GELU_TANH)
