@@ -66,7 +66,10 @@ def fp32_allowance(x_hat, po, bias):
     for the form it evaluates: sum_g s_g (sum_k (128 + q) x_hat - (128 + z_g)
     X_g) + bias, whose terms are about 128 times larger than the result, so
     that a small output can move by more than one bf16 ulp.  n = 4 product
-    blocks per group + G groups + 8 wave partials + 2 (scale and bias)."""
+    blocks per group + G groups + 8 wave partials + 2 (scale and bias) for
+    the MFMA forms; the single-row form (M = 1) rounds each term at most
+    4 (dot-product chain) + 2 + 1 (lane pair) + 1 (zero point) + K/2048
+    (chunks) + 5 (lane tree) + 1 (bias) times, never more than that n."""
     M, K = x_hat.shape
     G = K // 64
     ax = np.abs(x_hat)

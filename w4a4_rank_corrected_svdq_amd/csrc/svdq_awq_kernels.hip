@@ -345,6 +345,120 @@ __global__ __launch_bounds__(256) void k_awq_gemv_stream(
   }
 }
 
+// ---------------------------------------------------------------------
+// Single-row form (M = 1, K <= 8192: the one conditioning vector of the
+// modulation layers).  Nothing is shared between output channels but x_hat,
+// so each wave streams whole weight rows with the vector ALUs: lane l owns
+// bytes 16 l of every 1 KB chunk c of a row, i.e. codes k0 = 2048 c + 32 l
+// .. + 31, half of group g = 32 c + l / 2; its x_hat values stay in
+// registers (packed bf16) for every row.  A wave takes awv_rows consecutive
+// output channels with all their loads issued first.  Per lane and chunk
+// d = sum (128 + q) x_hat over its 32 codes -- the MFMA form's offset codes,
+// here as bf16 pairs in bf16 dot products into fp32 (four chains over the
+// byte positions of its four code dwords, then added pairwise); the two
+// lanes of a group add their d (lane ^ 1), t = d - (128 + z) X_g, and the
+// even lanes sum s t over their chunks; a fixed tree over the even lanes and
+// the bias give the output.
+// Output channels per wave: six while a row is at most two 1 KB chunks
+// (three waves per SIMD: at N = 18432 the 3072 waves are all resident in
+// one round), two beyond (two waves per SIMD).
+template <int CH> constexpr int awv_rows() { return CH <= 2 ? 6 : 2; }
+
+template <int CH>                              // 1 KB chunks per weight row (K <= 2048 CH)
+__global__ __launch_bounds__(256, CH <= 2 ? 3 : 2) void k_awq_gemv_row1(
+    const uint16_t* __restrict__ x_hat, const float* __restrict__ xsum, const uint8_t* __restrict__ w_codes,
+    const _Float16* __restrict__ w_scales, const uint8_t* __restrict__ w_zeros, const uint16_t* __restrict__ bias,
+    int N, int K, uint16_t* __restrict__ y) {
+  const int lane = threadIdx.x & 63;
+  const int gw = blockIdx.x * (blockDim.x >> 6) + (threadIdx.x >> 6);
+  constexpr int AWV_ROWS = awv_rows<CH>();
+  const int n0 = AWV_ROWS * gw;
+  const int Kb = K / 2;
+  const int G = K / AWQ_GROUP;
+  uint32_t xb[CH][16];                         // x_hat[k0 + 2 i] | x_hat[k0 + 2 i + 1] << 16
+  float xs[CH];
+  bool ok[CH];
+#pragma unroll
+  for (int c = 0; c < CH; ++c) {
+    ok[c] = 1024 * c + 16 * lane < Kb;
+    const int k0 = 2048 * c + 32 * lane;
+    uint4 v[4] = {};
+    xs[c] = 0.f;
+    if (ok[c]) {
+      const uint4* p = reinterpret_cast<const uint4*>(x_hat + k0);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) v[i] = p[i];
+      xs[c] = xsum[(k0 / AWQ_GROUP) * AWQ_MAX_ROWS];
+    }
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      xb[c][4 * i] = v[i].x;
+      xb[c][4 * i + 1] = v[i].y;
+      xb[c][4 * i + 2] = v[i].z;
+      xb[c][4 * i + 3] = v[i].w;
+    }
+  }
+  // Every load of the wave's rows is issued before any is used, at clamped
+  // in-bounds addresses (rows past N read row N - 1, byte ranges past K the
+  // row's first chunk), and masked afterwards: a load under a per-lane
+  // branch would be waited for before the next one is issued.
+  uint4 wq[AWV_ROWS][CH];
+  uint16_t sr[AWV_ROWS][CH];
+  uint8_t zr[AWV_ROWS][CH];
+  uint16_t br[AWV_ROWS];
+#pragma unroll
+  for (int j = 0; j < AWV_ROWS; ++j) {
+    const size_t n = static_cast<size_t>(min(n0 + j, N - 1));
+    br[j] = bias ? bias[n] : 0;
+#pragma unroll
+    for (int c = 0; c < CH; ++c) {
+      const int gi = ok[c] ? 32 * c + (lane >> 1) : 0;
+      const int bo = ok[c] ? 1024 * c + 16 * lane : 0;
+      wq[j][c] = *reinterpret_cast<const uint4*>(w_codes + n * Kb + bo);
+      sr[j][c] = reinterpret_cast<const uint16_t*>(w_scales)[n * G + gi];
+      zr[j][c] = w_zeros[n * G + gi];
+    }
+  }
+#pragma unroll
+  for (int j = 0; j < AWV_ROWS; ++j) {
+    float acc = 0.f;
+#pragma unroll
+    for (int c = 0; c < CH; ++c) {
+      if (!ok[c]) wq[j][c] = make_uint4(0, 0, 0, 0);
+      const float scv = ok[c] ? static_cast<float>(__builtin_bit_cast(_Float16, sr[j][c])) : 0.f;
+      const float zcv = static_cast<float>(zr[j][c]);
+      const uint32_t w[4] = {wq[j][c].x, wq[j][c].y, wq[j][c].z, wq[j][c].w};
+      // Byte b of a code dword holds codes 2 b (low nibble) and 2 b + 1; as
+      // the bf16 pair (128 + q_2b, 128 + q_2b+1) -- 0x4300 | q is the bf16
+      // value 128 + q -- it meets the packed x_hat pair of the same two k in
+      // one bf16 dot product into fp32.  Four independent chains, one per
+      // byte position, then (d0 + d1) + (d2 + d3).
+      float dp[4] = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const uint32_t lo = w[i] & 0x0F0F0F0Fu, hi = (w[i] >> 4) & 0x0F0F0F0Fu;
+#pragma unroll
+        for (int b = 0; b < 4; ++b) {
+          // bytes (lo.b, 0, hi.b, 0), then 0x43 into bytes 1 and 3
+          const uint32_t sel = 0x0C000C00u | (static_cast<uint32_t>(4 + b) << 16) | static_cast<uint32_t>(b);
+          const uint32_t qp = __builtin_amdgcn_perm(hi, lo, sel) | 0x43004300u;
+          dp[b] = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(v2bf, qp), __builtin_bit_cast(v2bf, xb[c][4 * i + b]),
+                                                  dp[b], false);
+        }
+      }
+      float d = (dp[0] + dp[1]) + (dp[2] + dp[3]);
+      d += __shfl_xor(d, 1);
+      // d = sum (128 + q) x_hat; t = d - (128 + z) X_g
+      acc = fmaf(scv, fmaf(-(128.0f + zcv), xs[c], d), acc);
+    }
+    acc = (lane & 1) ? 0.f : acc;
+#pragma unroll
+    for (int o = 32; o >= 2; o >>= 1) acc += __shfl_xor(acc, o);
+    const int n = n0 + j;
+    if (lane == 0 && n < N) y[n] = static_cast<uint16_t>(f32_to_bf16_bits(acc + bf16_bits_to_f32(br[j])));
+  }
+}
+
 }  // namespace
 
 namespace svdq {
@@ -361,6 +475,19 @@ int launch_awq_quant_act(const void* x, const float* inv_scale, int M, int K, vo
 int launch_awq_gemv(const void* x_hat, const float* xsum, const void* w_codes, const void* w_scales,
                     const void* w_zeros, const void* bias, int M, int N, int K, void* y, void* stream) {
   hipStream_t st = static_cast<hipStream_t>(stream);
+  if (M == 1 && K <= 4 * 2048) {
+    // one row: awv_rows output channels per wave, four waves per block
+    const int ch = (K / 2 + 1023) / 1024;
+    const int rows = ch <= 2 ? awv_rows<2>() : awv_rows<3>();
+    const int blocks = (N + 4 * rows - 1) / (4 * rows);
+    auto kern = ch == 1 ? k_awq_gemv_row1<1> : ch == 2 ? k_awq_gemv_row1<2> : ch == 3 ? k_awq_gemv_row1<3>
+                                                                                    : k_awq_gemv_row1<4>;
+    hipLaunchKernelGGL(kern, dim3(blocks), dim3(256), 0, st, static_cast<const uint16_t*>(x_hat), xsum,
+                       static_cast<const uint8_t*>(w_codes), static_cast<const _Float16*>(w_scales),
+                       static_cast<const uint8_t*>(w_zeros), static_cast<const uint16_t*>(bias), N, K,
+                       static_cast<uint16_t*>(y));
+    return hipGetLastError() == hipSuccess ? SVDQ_OK : SVDQ_ERR_HIP;
+  }
   if ((K / AWQ_GROUP) % 4 == 0) {
     hipLaunchKernelGGL(k_awq_gemv_stream, dim3(N / 32), dim3(256), 0, st, static_cast<const uint16_t*>(x_hat), xsum,
                        static_cast<const uint8_t*>(w_codes), static_cast<const _Float16*>(w_scales),
