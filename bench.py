@@ -250,19 +250,23 @@ def bench_qkv(S, L, workloads, r, steps, warmup):
 
 def bench_awq(S, workloads, steps, warmup, M=1):
     """AWQ W4A16 on the FLUX double-block modulation projection (3072 ->
-    18432, bias), M conditioning rows: HBM-bound on the weight read."""
+    18432, bias), M conditioning rows: HBM-bound on the weight read.  One
+    row runs the single-launch form (svdq_awq_linear_row: activation scaling
+    fused into the GEMV); the two-launch path (svdq_awq_quant_act +
+    svdq_awq_gemv) is timed beside it."""
     import torch
     wl = workloads.awq_workload(M, K=3072, N=18432, Mc=16, seed=7)
     K, N = wl["K"], wl["N"]
+    G = K // 64
     prep = S.awq_prepare(wl["weight_bits"], wl["x_cal_bits"])
     lin = S.AWQW4A16Linear(prep, torch.from_numpy(wl["bias_bits"].view(np.int16).copy()).view(torch.bfloat16), "cuda")
     x = torch.from_numpy(wl["x_bits"].view(np.int16).copy()).view(torch.bfloat16).cuda()
     xh = torch.empty((M, K), dtype=torch.bfloat16, device="cuda")
-    xs = torch.empty((K // 64, 16), dtype=torch.float32, device="cuda")
+    xs = torch.empty((G, 16), dtype=torch.float32, device="cuda")
     y = torch.empty((M, N), dtype=torch.bfloat16, device="cuda")
     st = torch.cuda.current_stream()
 
-    def step(ev=None):
+    def two_launch(ev=None):
         S.awq_quant_act(x, lin.inv_scale, out=(xh, xs))
         if ev is not None:
             ev[0].record(st)
@@ -270,28 +274,51 @@ def bench_awq(S, workloads, steps, warmup, M=1):
         if ev is not None:
             ev[1].record(st)
 
-    settle(step)
-    for _ in range(warmup):
-        step()
-    torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    for i in range(steps):
-        step()
-    torch.cuda.synchronize()
-    ms = (time.perf_counter() - t0) * 1e3 / steps
-    # kernel time from a second, event-instrumented pass
-    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(steps)]
-    for i in range(steps):
-        step(evs[i])
-    torch.cuda.synchronize()
-    gemv_ms = float(np.mean([e[0].elapsed_time(e[1]) for e in evs]))
-    nbytes = N * K // 2 + 2 * N * (K // 64) + N * (K // 64) + 2 * M * K + 4 * (K // 64) * 16 + 2 * N + 2 * M * N
-    gbs = nbytes / (gemv_ms * 1e-3) / 1e9
-    return {"workload": f"FLUX modulation projection 3072 -> 18432 (+bias), M = {M}, AWQ INT4 group 64",
-            "alpha": prep["alpha"], "ms_per_step": round(ms, 5),
-            "roofline": {"bound": "hbm", "kernel": "k_awq_gemv_stream", "achieved": round(gbs, 1),
-                         "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(gbs / HBM_PEAK_GBS, 4),
-                         "avg_launch_us": round(gemv_ms * 1e3, 2), "algorithmic_bytes_per_launch": nbytes}}
+    def one_launch(ev=None):
+        if ev is not None:
+            ev[0].record(st)
+        S.awq_linear_row(x, lin.inv_scale, lin.w_codes, lin.w_scales, lin.w_zeros, lin.bias, N, K, out=y)
+        if ev is not None:
+            ev[1].record(st)
+
+    def timed(step):
+        settle(step)
+        for _ in range(warmup):
+            step()
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for _ in range(steps):
+            step()
+        torch.cuda.synchronize()
+        ms = (time.perf_counter() - t0) * 1e3 / steps
+        # kernel time from a second, event-instrumented pass
+        evs = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(steps)]
+        for i in range(steps):
+            step(evs[i])
+        torch.cuda.synchronize()
+        return ms, float(np.mean([e[0].elapsed_time(e[1]) for e in evs]))
+
+    weights = N * K // 2 + 2 * N * G + N * G + 2 * N
+    fused = M == 1
+    ms2, gemv_ms = timed(two_launch)
+    if fused:
+        ms, k_ms = timed(one_launch)
+        nbytes = weights + 2 * K + 4 * K + 2 * N            # x and inv_scale in, y out
+        kernel = "k_awq_gemv_row1 (activation scaling fused)"
+    else:
+        ms, k_ms = ms2, gemv_ms
+        nbytes = weights + 2 * M * K + 4 * G * 16 + 2 * M * N
+        kernel = "k_awq_gemv_stream"
+    gbs = nbytes / (k_ms * 1e-3) / 1e9
+    out = {"workload": f"FLUX modulation projection 3072 -> 18432 (+bias), M = {M}, AWQ INT4 group 64",
+           "alpha": prep["alpha"], "ms_per_step": round(ms, 5),
+           "roofline": {"bound": "hbm", "kernel": kernel, "achieved": round(gbs, 1),
+                        "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(gbs / HBM_PEAK_GBS, 4),
+                        "avg_launch_us": round(k_ms * 1e3, 2), "algorithmic_bytes_per_launch": nbytes}}
+    if fused:
+        out["two_launch_ms_per_step"] = round(ms2, 5)
+        out["two_launch_gemv_us"] = round(gemv_ms * 1e3, 2)
+    return out
 
 
 def measure_peaks():

@@ -64,7 +64,8 @@ typedef enum svdq_status {
 
 enum { SVDQ_ACT_NONE = 0, SVDQ_ACT_GELU_TANH = 1 };
 enum { SVDQ_OUT_BF16 = 0, SVDQ_OUT_F32 = 1 };
-enum { SVDQ_GROUP = 64, SVDQ_MAX_RANK = 256, SVDQ_QKV_HEAD_DIM = 128, SVDQ_AWQ_MAX_ROWS = 16 };
+enum { SVDQ_GROUP = 64, SVDQ_MAX_RANK = 256, SVDQ_QKV_HEAD_DIM = 128, SVDQ_AWQ_MAX_ROWS = 16,
+       SVDQ_AWQ_ROW_MAX_K = 8192 };
 
 /* Human-readable name of a status code (static storage, never NULL). */
 const char* svdq_status_string(int status);
@@ -458,10 +459,20 @@ int svdq_awq_quant_act(const void* x, const float* inv_scale, int M, int K, void
 
 /* Device, asynchronous.  y [M][N] bf16 = bf16(sum_g s[n][g] (sum_{k in g}
  * q[n][k] x_hat[m][k] - z[n][g] xsum[g][m]) + bias[n]) with fp32 sums; the
- * inner sums run on bf16 MFMA.  M <= 16, N % 32 == 0, K % 64 == 0; bias
- * nullable. */
+ * inner sums run on bf16 MFMA, or for one row with K <= 8192 on bf16 dot
+ * products into fp32 (as sum (128 + q) x_hat - (128 + z) xsum in both).
+ * M <= 16, N % 32 == 0, K % 64 == 0; bias nullable. */
 int svdq_awq_gemv(const void* x_hat, const float* xsum, const void* w_codes, const void* w_scales,
                   const void* w_zeros, const void* bias, int M, int N, int K, void* y, void* stream);
+
+/* Device, asynchronous.  One row (the modulation layers' single
+ * conditioning vector): y [N] bf16 = what svdq_awq_quant_act followed by
+ * svdq_awq_gemv produce for M = 1 from x [K] bf16 and inv_scale [K] fp32,
+ * bit for bit, in one launch (x_hat and the group sums are formed on the
+ * device per block, in the same arithmetic and order).  K <= SVDQ_AWQ_ROW_MAX_K,
+ * K % 64 == 0, N % 32 == 0; bias nullable; buffers 16-byte aligned. */
+int svdq_awq_linear_row(const void* x, const float* inv_scale, const void* w_codes, const void* w_scales,
+                        const void* w_zeros, const void* bias, int N, int K, void* y, void* stream);
 
 #ifdef __cplusplus
 }

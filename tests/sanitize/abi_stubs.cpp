@@ -27,6 +27,8 @@ int launch_gemm_mxfp4_lora_up(const void*, const void*, const void*, const void*
 int launch_awq_quant_act(const void*, const float*, int, int, void*, float*, void*) { ++g_launches; return kReached; }
 int launch_awq_gemv(const void*, const float*, const void*, const void*, const void*, const void*, int, int, int,
                     void*, void*) { ++g_launches; return kReached; }
+int launch_awq_linear_row(const void*, const float*, const void*, const void*, const void*, const void*, int, int,
+                          void*, void*) { ++g_launches; return kReached; }
 int launch_quant_act_lora_down_fp6(const void*, const float*, const void*, int, int, int, int, void*, void*, float*,
                                    void*) { ++g_launches; return kReached; }
 int launch_gemm_w4a4_fp6(const void*, const void*, const void*, const void*, const float*, const void*, const void*,

@@ -210,6 +210,10 @@ static void device_argument_checks() {
   EXPECT(svdq_awq_quant_act(p, f, 17, K, p, f, nullptr) != SVDQ_OK);
   EXPECT(passed_checks(svdq_awq_gemv(p, f, p, p, p, nullptr, 4, 64, K, p, nullptr)));
   EXPECT(svdq_awq_gemv(p, f, p, p, p, nullptr, 4, 48, K, p, nullptr) != SVDQ_OK);
+  EXPECT(passed_checks(svdq_awq_linear_row(p, f, p, p, p, nullptr, 64, K, p, nullptr)));
+  EXPECT(svdq_awq_linear_row(p, f, p, p, p, nullptr, 64, 8256, p, nullptr) == SVDQ_ERR_UNSUPPORTED_SHAPE);
+  EXPECT(svdq_awq_linear_row(p, f, p, p, p, nullptr, 48, K, p, nullptr) == SVDQ_ERR_UNSUPPORTED_SHAPE);
+  EXPECT(svdq_awq_linear_row(nullptr, f, p, p, p, nullptr, 64, K, p, nullptr) == SVDQ_ERR_INVALID_ARG);
   // status strings for every code, and an unknown one
   for (int s = -6; s <= 1; ++s) EXPECT(svdq_status_string(s) != nullptr);
   EXPECT(svdq_version() > 0);

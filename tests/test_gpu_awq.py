@@ -102,6 +102,38 @@ def test_awq_gemv_parity(M, K, N, bias):
     check_bf16_elementwise(to_np_bf16(y), ref, atol=fp32_allowance(x_hat, po, wl["bias"] if bias else None))
 
 
+@pytest.mark.parametrize("K,N,bias", [(64, 32, True), (512, 288, True), (2048, 96, False), (3072, 18432, True),
+                                      (4160, 64, True), (8192, 32, False)])
+def test_awq_linear_row_equals_two_kernels(K, N, bias):
+    """svdq_awq_linear_row (one row, scaling and GEMV in one launch) against
+    svdq_awq_quant_act + svdq_awq_gemv at M = 1: bit for bit (one, two,
+    three and four 1 KB code chunks per row; N not a multiple of a block's
+    24 channels), and against the oracle."""
+    wl, po = _case(1, K, N, seed=90 + K // 64 + N)
+    xh, xs, y2 = _run(wl, po, bias)
+    y1 = S.awq_linear_row(dev_bf16(wl["x_bits"]), dev(po["inv_scale"].astype(np.float32)), dev(_pack(po["q"])),
+                          dev(po["s"].astype(np.float16)), dev(po["z"].astype(np.uint8)),
+                          dev_bf16(wl["bias_bits"]) if bias else None, N, K)
+    torch.cuda.synchronize()
+    assert torch.equal(y1.view(torch.int16), y2.view(torch.int16))
+    ref = A.awq_forward(wl["x"], po, bias=wl["bias"] if bias else None)
+    x_hat = O.bf16(O.fp32(wl["x"] * po["inv_scale"][None, :]))
+    check_bf16_elementwise(to_np_bf16(y1), ref, atol=fp32_allowance(x_hat, po, wl["bias"] if bias else None))
+
+
+def test_awq_linear_row_argument_errors():
+    import ctypes
+    from w4a4_rank_corrected_svdq_amd import _lib as L
+    t = torch.empty(1 << 16, dtype=torch.uint8, device="cuda")
+    p = ctypes.c_void_p(t.data_ptr())
+    fn = L.lib().svdq_awq_linear_row
+    assert fn(p, p, p, p, p, None, 64, 8256, p, None) == L.SVDQ_ERR_UNSUPPORTED_SHAPE   # K past the row form
+    assert fn(p, p, p, p, p, None, 48, 128, p, None) == L.SVDQ_ERR_UNSUPPORTED_SHAPE    # N % 32
+    assert fn(p, p, p, p, p, None, 64, 96, p, None) == L.SVDQ_ERR_UNSUPPORTED_SHAPE     # K % 64
+    assert fn(None, p, p, p, p, None, 64, 128, p, None) == L.SVDQ_ERR_INVALID_ARG
+    assert fn(p, p, p, p, p, None, 0, 128, p, None) == L.SVDQ_ERR_INVALID_ARG
+
+
 @pytest.mark.parametrize("M", [1, 2])
 def test_awq_full_size_modulation(M):
     """FLUX double-block modulation projection 3072 -> 18432 with bias, the

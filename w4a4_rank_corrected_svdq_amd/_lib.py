@@ -26,6 +26,8 @@ SVDQ_MAX_RANK = 256
 SVDQ_FP6_ACTIVATIONS = 0
 SVDQ_FP6_WEIGHTS = 1
 SVDQ_CHAIN_SCRATCH_BYTES = 32 << 20
+SVDQ_AWQ_MAX_ROWS = 16
+SVDQ_AWQ_ROW_MAX_K = 8192
 
 _p = ctypes.c_void_p
 _i = ctypes.c_int
@@ -49,6 +51,7 @@ SIGNATURES = {
     "svdq_awq_prepare": (_i, [_p, _i, _i, _p, _i, ctypes.c_double, _i, _p, _p, _p, _p, _p]),
     "svdq_awq_quant_act": (_i, [_p, _p, _i, _i, _p, _p, _p]),
     "svdq_awq_gemv": (_i, [_p, _p, _p, _p, _p, _p, _i, _i, _i, _p, _p]),
+    "svdq_awq_linear_row": (_i, [_p, _p, _p, _p, _p, _p, _i, _i, _p, _p]),
     "svdq_prepared_bytes_mxfp4": (_i, [_i, _i, _i, ctypes.POINTER(ctypes.c_size_t)]),
     "svdq_prepare_weights_mxfp4": (_i, [_p, _i, _i, _p, ctypes.c_float, _i, _p, _p, _i, ctypes.c_uint64,
                                         _p, _p, _p, _p, _p, _p]),

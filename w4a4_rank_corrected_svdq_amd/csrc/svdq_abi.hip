@@ -371,6 +371,20 @@ extern "C" int svdq_awq_gemv(const void* x_hat, const float* xsum, const void* w
   return svdq::launch_awq_gemv(x_hat, xsum, w_codes, w_scales, w_zeros, bias, M, N, K, y, stream);
 }
 
+extern "C" int svdq_awq_linear_row(const void* x, const float* inv_scale, const void* w_codes, const void* w_scales,
+                                   const void* w_zeros, const void* bias, int N, int K, void* y, void* stream) {
+  if (N <= 0 || K <= 0) return SVDQ_ERR_INVALID_ARG;
+  if (K % SVDQ_GROUP != 0 || N % 32 != 0 || K > SVDQ_AWQ_ROW_MAX_K) return SVDQ_ERR_UNSUPPORTED_SHAPE;
+  if (!x || !inv_scale || !w_codes || !w_scales || !w_zeros || !y) return SVDQ_ERR_INVALID_ARG;
+  if (!aligned16(x) || !aligned16(inv_scale) || !aligned16(w_codes) || !aligned16(w_scales) || !aligned16(w_zeros) ||
+      !aligned16(y) || (bias && !aligned16(bias)))
+    return SVDQ_ERR_INVALID_ARG;
+  if (!fits_buffer(N, K / 2)) return SVDQ_ERR_UNSUPPORTED_SHAPE;
+  const int st = current_device_check();
+  if (st != SVDQ_OK) return st;
+  return svdq::launch_awq_linear_row(x, inv_scale, w_codes, w_scales, w_zeros, bias, N, K, y, stream);
+}
+
 extern "C" int svdq_probe_mfma(int kind, int blocks, int iters, void* sink, void* stream) {
   if (kind < SVDQ_PROBE_MFMA_I8 || kind > SVDQ_PROBE_FP6_DEQUANT) return SVDQ_ERR_INVALID_ARG;
   if (blocks < 1 || iters < 1 || !sink || !aligned16(sink)) return SVDQ_ERR_INVALID_ARG;

@@ -364,13 +364,23 @@ __global__ __launch_bounds__(256) void k_awq_gemv_stream(
 // one round), two beyond (two waves per SIMD).
 template <int CH> constexpr int awv_rows() { return CH <= 2 ? 6 : 2; }
 
-template <int CH>                              // 1 KB chunks per weight row (K <= 2048 CH)
+// FUSED = 1 folds k_awq_act in: from x [K] and inv_scale [K] every block
+// forms x_hat and the group sums X_g in LDS with the same arithmetic and
+// order (x_hat = bf16(fp32(x * inv_scale)); X_g summed in fp32 in increasing
+// k), so the output equals the two-kernel path's bit for bit.  Its x loads
+// are issued first and the weight loads right behind them, so that forming
+// x_hat waits only for the former, and the LDS barriers wait only for LDS.
+template <int CH, int FUSED>                   // 1 KB chunks per weight row (K <= 2048 CH)
 __global__ __launch_bounds__(256, CH <= 2 ? 3 : 2) void k_awq_gemv_row1(
-    const uint16_t* __restrict__ x_hat, const float* __restrict__ xsum, const uint8_t* __restrict__ w_codes,
+    const uint16_t* __restrict__ xin, const float* __restrict__ xaux, const uint8_t* __restrict__ w_codes,
     const _Float16* __restrict__ w_scales, const uint8_t* __restrict__ w_zeros, const uint16_t* __restrict__ bias,
     int N, int K, uint16_t* __restrict__ y) {
-  const int lane = threadIdx.x & 63;
-  const int gw = blockIdx.x * (blockDim.x >> 6) + (threadIdx.x >> 6);
+  // xin: FUSED ? x : x_hat (one row, bf16); xaux: FUSED ? inv_scale [K] : xsum [K/64][16]
+  __shared__ __align__(16) uint32_t xh_s[FUSED ? 1024 * CH : 4];   // x_hat pairs (k, k + 1)
+  __shared__ float xg_s[FUSED ? 32 * CH : 1];        // X_g
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int gw = blockIdx.x * (blockDim.x >> 6) + (tid >> 6);
   constexpr int AWV_ROWS = awv_rows<CH>();
   const int n0 = AWV_ROWS * gw;
   const int Kb = K / 2;
@@ -378,24 +388,37 @@ __global__ __launch_bounds__(256, CH <= 2 ? 3 : 2) void k_awq_gemv_row1(
   uint32_t xb[CH][16];                         // x_hat[k0 + 2 i] | x_hat[k0 + 2 i + 1] << 16
   float xs[CH];
   bool ok[CH];
+  constexpr int XP = FUSED ? 4 * CH : 1;       // x pairs per thread: K / 2 <= 1024 CH over 256 threads
+  uint32_t xr[XP];
+  float2 ir[XP];
 #pragma unroll
-  for (int c = 0; c < CH; ++c) {
-    ok[c] = 1024 * c + 16 * lane < Kb;
-    const int k0 = 2048 * c + 32 * lane;
-    uint4 v[4] = {};
-    xs[c] = 0.f;
-    if (ok[c]) {
-      const uint4* p = reinterpret_cast<const uint4*>(x_hat + k0);
+  for (int c = 0; c < CH; ++c) ok[c] = 1024 * c + 16 * lane < Kb;
+  if constexpr (FUSED) {
 #pragma unroll
-      for (int i = 0; i < 4; ++i) v[i] = p[i];
-      xs[c] = xsum[(k0 / AWQ_GROUP) * AWQ_MAX_ROWS];
+    for (int i = 0; i < XP; ++i) {
+      const int pi = min(tid + 256 * i, Kb - 1);          // clamped; pairs past K / 2 are not stored
+      xr[i] = reinterpret_cast<const uint32_t*>(xin)[pi];
+      ir[i] = reinterpret_cast<const float2*>(xaux)[pi];
     }
+  } else {
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      xb[c][4 * i] = v[i].x;
-      xb[c][4 * i + 1] = v[i].y;
-      xb[c][4 * i + 2] = v[i].z;
-      xb[c][4 * i + 3] = v[i].w;
+    for (int c = 0; c < CH; ++c) {
+      const int k0 = 2048 * c + 32 * lane;
+      uint4 v[4] = {};
+      xs[c] = 0.f;
+      if (ok[c]) {
+        const uint4* p = reinterpret_cast<const uint4*>(xin + k0);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) v[i] = p[i];
+        xs[c] = xaux[(k0 / AWQ_GROUP) * AWQ_MAX_ROWS];
+      }
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        xb[c][4 * i] = v[i].x;
+        xb[c][4 * i + 1] = v[i].y;
+        xb[c][4 * i + 2] = v[i].z;
+        xb[c][4 * i + 3] = v[i].w;
+      }
     }
   }
   // Every load of the wave's rows is issued before any is used, at clamped
@@ -406,10 +429,14 @@ __global__ __launch_bounds__(256, CH <= 2 ? 3 : 2) void k_awq_gemv_row1(
   uint16_t sr[AWV_ROWS][CH];
   uint8_t zr[AWV_ROWS][CH];
   uint16_t br[AWV_ROWS];
+  // without a bias the loads read the scales (masked to +0 below), so that
+  // no load sits under a branch
+  const uint16_t* bsrc = bias ? bias : reinterpret_cast<const uint16_t*>(w_scales);
+  const uint32_t bmask = bias ? 0xFFFFu : 0u;
 #pragma unroll
   for (int j = 0; j < AWV_ROWS; ++j) {
     const size_t n = static_cast<size_t>(min(n0 + j, N - 1));
-    br[j] = bias ? bias[n] : 0;
+    br[j] = bsrc[n];
 #pragma unroll
     for (int c = 0; c < CH; ++c) {
       const int gi = ok[c] ? 32 * c + (lane >> 1) : 0;
@@ -417,6 +444,42 @@ __global__ __launch_bounds__(256, CH <= 2 ? 3 : 2) void k_awq_gemv_row1(
       wq[j][c] = *reinterpret_cast<const uint4*>(w_codes + n * Kb + bo);
       sr[j][c] = reinterpret_cast<const uint16_t*>(w_scales)[n * G + gi];
       zr[j][c] = w_zeros[n * G + gi];
+    }
+  }
+  if constexpr (FUSED) {
+#pragma unroll
+    for (int i = 0; i < XP; ++i) {
+      const int pi = tid + 256 * i;
+      if (pi < Kb)
+        xh_s[pi] = bf16x2_bits(bf16_bits_to_f32(xr[i] & 0xFFFFu) * ir[i].x, bf16_bits_to_f32(xr[i] >> 16) * ir[i].y);
+    }
+    __builtin_amdgcn_s_waitcnt(waitcnt_vm_lgkm0(63));
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
+    if (tid < G) {
+      float sum = 0.f;
+      for (int i = 0; i < AWQ_GROUP / 2; ++i) {
+        const uint32_t pr = xh_s[(AWQ_GROUP / 2) * tid + i];
+        sum += bf16_bits_to_f32(pr & 0xFFFFu);
+        sum += bf16_bits_to_f32(pr >> 16);
+      }
+      xg_s[tid] = sum;
+    }
+    __builtin_amdgcn_s_waitcnt(waitcnt_vm_lgkm0(63));
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
+#pragma unroll
+    for (int c = 0; c < CH; ++c) {
+      const int p0 = ok[c] ? 1024 * c + 16 * lane : 0;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const uint4 v = *reinterpret_cast<const uint4*>(&xh_s[p0 + 4 * i]);
+        xb[c][4 * i] = v.x;
+        xb[c][4 * i + 1] = v.y;
+        xb[c][4 * i + 2] = v.z;
+        xb[c][4 * i + 3] = v.w;
+      }
+      xs[c] = ok[c] ? xg_s[p0 / (AWQ_GROUP / 2)] : 0.f;
     }
   }
 #pragma unroll
@@ -455,7 +518,7 @@ __global__ __launch_bounds__(256, CH <= 2 ? 3 : 2) void k_awq_gemv_row1(
 #pragma unroll
     for (int o = 32; o >= 2; o >>= 1) acc += __shfl_xor(acc, o);
     const int n = n0 + j;
-    if (lane == 0 && n < N) y[n] = static_cast<uint16_t>(f32_to_bf16_bits(acc + bf16_bits_to_f32(br[j])));
+    if (lane == 0 && n < N) y[n] = static_cast<uint16_t>(f32_to_bf16_bits(acc + bf16_bits_to_f32(br[j] & bmask)));
   }
 }
 
@@ -472,6 +535,21 @@ int launch_awq_quant_act(const void* x, const float* inv_scale, int M, int K, vo
   return hipGetLastError() == hipSuccess ? SVDQ_OK : SVDQ_ERR_HIP;
 }
 
+int launch_awq_linear_row(const void* x, const float* inv_scale, const void* w_codes, const void* w_scales,
+                          const void* w_zeros, const void* bias, int N, int K, void* y, void* stream) {
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  const int ch = (K / 2 + 1023) / 1024;
+  const int rows = ch <= 2 ? awv_rows<2>() : awv_rows<3>();
+  const int blocks = (N + 4 * rows - 1) / (4 * rows);
+  auto kern = ch == 1 ? k_awq_gemv_row1<1, 1> : ch == 2 ? k_awq_gemv_row1<2, 1> : ch == 3 ? k_awq_gemv_row1<3, 1>
+                                                                                        : k_awq_gemv_row1<4, 1>;
+  hipLaunchKernelGGL(kern, dim3(blocks), dim3(256), 0, st, static_cast<const uint16_t*>(x), inv_scale,
+                     static_cast<const uint8_t*>(w_codes), static_cast<const _Float16*>(w_scales),
+                     static_cast<const uint8_t*>(w_zeros), static_cast<const uint16_t*>(bias), N, K,
+                     static_cast<uint16_t*>(y));
+  return hipGetLastError() == hipSuccess ? SVDQ_OK : SVDQ_ERR_HIP;
+}
+
 int launch_awq_gemv(const void* x_hat, const float* xsum, const void* w_codes, const void* w_scales,
                     const void* w_zeros, const void* bias, int M, int N, int K, void* y, void* stream) {
   hipStream_t st = static_cast<hipStream_t>(stream);
@@ -480,8 +558,8 @@ int launch_awq_gemv(const void* x_hat, const float* xsum, const void* w_codes, c
     const int ch = (K / 2 + 1023) / 1024;
     const int rows = ch <= 2 ? awv_rows<2>() : awv_rows<3>();
     const int blocks = (N + 4 * rows - 1) / (4 * rows);
-    auto kern = ch == 1 ? k_awq_gemv_row1<1> : ch == 2 ? k_awq_gemv_row1<2> : ch == 3 ? k_awq_gemv_row1<3>
-                                                                                    : k_awq_gemv_row1<4>;
+    auto kern = ch == 1 ? k_awq_gemv_row1<1, 0> : ch == 2 ? k_awq_gemv_row1<2, 0> : ch == 3 ? k_awq_gemv_row1<3, 0>
+                                                                                          : k_awq_gemv_row1<4, 0>;
     hipLaunchKernelGGL(kern, dim3(blocks), dim3(256), 0, st, static_cast<const uint16_t*>(x_hat), xsum,
                        static_cast<const uint8_t*>(w_codes), static_cast<const _Float16*>(w_scales),
                        static_cast<const uint8_t*>(w_zeros), static_cast<const uint16_t*>(bias), N, K,

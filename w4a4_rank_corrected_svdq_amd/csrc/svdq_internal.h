@@ -41,6 +41,10 @@ int launch_awq_quant_act(const void* x, const float* inv_scale, int M, int K, vo
                          void* stream);
 int launch_awq_gemv(const void* x_hat, const float* xsum, const void* w_codes, const void* w_scales,
                     const void* w_zeros, const void* bias, int M, int N, int K, void* y, void* stream);
+// One row (M = 1, K <= 8192), activation scaling fused in: y = the two
+// kernels' output from x and inv_scale directly.
+int launch_awq_linear_row(const void* x, const float* inv_scale, const void* w_codes, const void* w_scales,
+                          const void* w_zeros, const void* bias, int N, int K, void* y, void* stream);
 
 // svdq_fp6_kernels.hip (kernel 1's FP6 mode is in svdq_kernels.hip)
 int launch_quant_act_lora_down_fp6(const void* x, const float* smooth_inv, const void* lora_down, int M, int K,

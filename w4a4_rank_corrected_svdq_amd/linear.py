@@ -150,6 +150,10 @@ class AWQW4A16Linear:
 
     def forward(self, x: torch.Tensor):
         M = x.shape[0]
+        if M == 1 and self.K <= L.SVDQ_AWQ_ROW_MAX_K:
+            # one conditioning vector: scaling and GEMV in one launch
+            return ops.awq_linear_row(x, self.inv_scale, self.w_codes, self.w_scales, self.w_zeros, self.bias,
+                                      self.N, self.K)
         xh, xs = ops.awq_quant_act(x, self.inv_scale)
         return ops.awq_gemv(xh, xs, self.w_codes, self.w_scales, self.w_zeros, self.bias, M, self.N, self.K)
 

@@ -481,3 +481,26 @@ def awq_gemv(x_hat, xsum, w_codes, w_scales, w_zeros, bias, M: int, N: int, K: i
         M, N, K, _dev_arg("y", out, torch.bfloat16, (M, N), dev), _stream(dev))
     L.check(st, "svdq_awq_gemv")
     return out
+
+
+def awq_linear_row(x, inv_scale, w_codes, w_scales, w_zeros, bias, N: int, K: int,
+                   out: Optional[torch.Tensor] = None):
+    """y [1][N] bf16 from one row x [1][K] (svdq_awq_linear_row: the
+    activation scaling and the GEMV in one launch, bit for bit their output)."""
+    if x.dtype != torch.bfloat16 or not x.is_cuda or x.numel() != K:
+        raise TypeError("x must be one bfloat16 CUDA row of K values")
+    x = x.contiguous().view(1, K)
+    dev = x.device
+    if out is None:
+        out = torch.empty((1, N), dtype=torch.bfloat16, device=dev)
+    G = K // 64
+    st = L.lib().svdq_awq_linear_row(
+        _dev_arg("x", x, torch.bfloat16, (1, K), dev),
+        _dev_arg("inv_scale", inv_scale, torch.float32, (K,), dev),
+        _dev_arg("w_codes", w_codes, torch.uint8, (N, K // 2), dev),
+        _dev_arg("w_scales", w_scales, torch.float16, (N, G), dev),
+        _dev_arg("w_zeros", w_zeros, torch.uint8, (N, G), dev),
+        _dev_arg("bias", bias, torch.bfloat16, (N,), dev),
+        N, K, _dev_arg("y", out, torch.bfloat16, (1, N), dev), _stream(dev))
+    L.check(st, "svdq_awq_linear_row")
+    return out
