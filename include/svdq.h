@@ -297,7 +297,9 @@ int svdq_quant_act_lora_down_fp6(const void* x, const float* smooth_inv, const v
  *   w_fp6    SVDQ_FP6_WEIGHTS layout of the weight codes (svdq_pack_fp6_operand),
  *   w_scales [K/64][N] fp16, lora_act [M][rank] fp32, lora_up [N][rank]
  *   bf16 (NULL if rank == 0), bias [N] bf16 or NULL.
- * Shape rules and errors as svdq_gemm_w4a4_lora_up. */
+ * Shape rules and errors as svdq_gemm_w4a4_lora_up; every buffer, y
+ * included, must be under 2 GiB (the kernel addresses them with 32-bit
+ * offsets), else SVDQ_ERR_UNSUPPORTED_SHAPE. */
 int svdq_gemm_w4a4_fp6_lora_up(const void* x_fp6, const void* x_scales,
                                const void* w_fp6, const void* w_scales,
                                const float* lora_act, const void* lora_up, const void* bias,

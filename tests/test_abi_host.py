@@ -97,6 +97,12 @@ def test_device_entry_validation_precedes_device_use():
     # rotary tables of 2 GiB or more (M * 256 bytes) are refused before any device use
     big = (1 << 23) + 16
     assert qk(p[0], p[1], p[2], p[3], p[4], p[5], None, p[6], p[7], p[8], p[9], 1e-6, big, 384, 128, 16, 64, 0, p[6], None) == L.SVDQ_ERR_UNSUPPORTED_SHAPE
+    # the 6-bit kernel 2 addresses y and lora_act with 32-bit offsets: an
+    # output of 2 GiB or more is refused before any device use
+    g6 = L.lib().svdq_gemm_w4a4_fp6_lora_up
+    #       x6    xs    w6    ws    la    lu    bias  M        N      K    r   g   out y
+    assert g6(p[0], p[1], p[2], p[3], p[4], p[5], None, 1 << 17, 8192, 128, 16, 64, 0, p[6], None) == L.SVDQ_ERR_UNSUPPORTED_SHAPE
+    assert g6(p[0], p[1], p[2], p[3], p[4], p[5], None, 1 << 16, 8192, 128, 16, 64, 1, p[6], None) == L.SVDQ_ERR_UNSUPPORTED_SHAPE
     pr = L.lib().svdq_probe_mfma
     assert pr(5, 1, 1, p[0], None) == L.SVDQ_ERR_INVALID_ARG          # unknown kind
     assert pr(-1, 1, 1, p[0], None) == L.SVDQ_ERR_INVALID_ARG

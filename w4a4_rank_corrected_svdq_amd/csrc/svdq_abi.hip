@@ -159,8 +159,11 @@ extern "C" int svdq_gemm_w4a4_fp6_lora_up(const void* x_fp6, const void* x_scale
     return SVDQ_ERR_INVALID_ARG;
   const int64_t G = K / SVDQ_GROUP;
   const int64_t RBa = (static_cast<int64_t>(M) + 31) / 32, RBb = 4 * ((static_cast<int64_t>(N) + 127) / 128);
+  // every operand and the output are addressed through buffer descriptors
+  // with 32-bit offsets
   if (!fits_buffer(G * RBa, 1536) || !fits_buffer(G * RBb, 1536) || !fits_buffer(G, 64LL * RBa) ||
-      !fits_buffer(G, 2LL * N))
+      !fits_buffer(G, 2LL * N) || !fits_buffer(M, 4LL * rank) ||
+      !fits_buffer(M, static_cast<int64_t>(N) * (out_dtype == SVDQ_OUT_F32 ? 4 : 2)))
     return SVDQ_ERR_UNSUPPORTED_SHAPE;
   st = current_device_check();
   if (st != SVDQ_OK) return st;
@@ -193,7 +196,7 @@ int check_chain(const void* x_fp6, const void* x_scales, const void* w_fp6, cons
   const int64_t G = K / SVDQ_GROUP, Gd = N / SVDQ_GROUP;
   const int64_t RBa = (static_cast<int64_t>(M) + 31) / 32, RBb = 4 * ((static_cast<int64_t>(N) + 127) / 128);
   if (!fits_buffer(G * RBa, 1536) || !fits_buffer(G * RBb, 1536) || !fits_buffer(G, 64LL * RBa) ||
-      !fits_buffer(G, 2LL * N) || !fits_buffer(Gd * RBa, 1536))
+      !fits_buffer(G, 2LL * N) || !fits_buffer(Gd * RBa, 1536) || !fits_buffer(M, 4LL * rank))
     return SVDQ_ERR_UNSUPPORTED_SHAPE;
   return SVDQ_OK;
 }
