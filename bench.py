@@ -203,49 +203,74 @@ def cpu_baseline(wl, layer, rank, target_s, precision="int4"):
 def bench_qkv(S, L, workloads, r, steps, warmup):
     """The joint-stream QKV projection (4608 x 3072 -> 9216, bias) with the
     fused per-head Q/K RMSNorm + rotary epilogue, against the same step with
-    the plain epilogue."""
+    the plain epilogue, on both INT4 engines (the 6-bit one first)."""
     import torch
     wl = workloads.make_workload("joint_qkv")
     Lr = wl.layers[0]
     M, K, N = wl.M, Lr.K, Lr.N
+    G, RBa = K // 64, (M + 31) // 32
     prep = S.prepare_weights(Lr.weight_bits, wl.act_absmax(), rank=r)
-    lin = S.SVDQW4A4Linear(prep, torch.from_numpy(Lr.bias_bits.view(np.int16).copy()).view(torch.bfloat16), "cuda",
-                           engine="int8")
+    bias = torch.from_numpy(Lr.bias_bits.view(np.int16).copy()).view(torch.bfloat16)
     (qb, _), (kb, _) = workloads.norm_weights()
     cos, sin = workloads.rope_tables(512, 64)
     gq = torch.from_numpy(qb.view(np.int16).copy()).view(torch.bfloat16).cuda()
     gk = torch.from_numpy(kb.view(np.int16).copy()).view(torch.bfloat16).cuda()
     cos_d, sin_d = torch.from_numpy(cos).cuda(), torch.from_numpy(sin).cuda()
     x = torch.from_numpy(wl.x_bits.view(np.int16).copy()).view(torch.bfloat16).cuda()
-    xc = torch.empty((M, K // 2), dtype=torch.uint8, device="cuda")
-    xs = torch.empty((K // 64, M), dtype=torch.float16, device="cuda")
     la = torch.empty((M, r), dtype=torch.float32, device="cuda") if r else None
     y = torch.empty((M, N), dtype=torch.bfloat16, device="cuda")
-
-    def timed(fused):
-        def step():
-            S.quant_act_lora_down(x, lin.smooth_inv, lin.lora_down, r, out=(xc, xs, la))
-            if fused:
-                S.gemm_w4a4_lora_up_qkv(xc, xs, lin.w_codes, lin.w_scales, la, lin.lora_up, lin.bias, gq, gk,
-                                        cos_d, sin_d, M, N, K, r, out=y)
-            else:
-                S.gemm_w4a4_lora_up(xc, xs, lin.w_codes, lin.w_scales, la, lin.lora_up, lin.bias, M, N, K, r, out=y)
-        settle(step)
-        for _ in range(warmup):
-            step()
-        torch.cuda.synchronize()
-        t0 = time.perf_counter()
-        for _ in range(steps):
-            step()
-        torch.cuda.synchronize()
-        return (time.perf_counter() - t0) * 1e3 / steps
-
-    plain_ms, fused_ms = timed(False), timed(True)
+    res = {"workload": "FLUX joint-stream QKV 4608x3072x9216 (+bias), rank 32, 24 heads of 128"}
     ops = 2.0 * M * N * K
-    return {"workload": "FLUX joint-stream QKV 4608x3072x9216 (+bias), rank 32, 24 heads of 128",
-            "plain_ms_per_step": round(plain_ms, 5), "fused_ms_per_step": round(fused_ms, 5),
-            "fused_effective_tops": round(ops / (fused_ms * 1e-3) / 1e12, 2),
-            "epilogue_overhead_frac": round(fused_ms / plain_ms - 1.0, 4)}
+
+    for engine in ("fp6", "int8"):
+        lin = S.SVDQW4A4Linear(prep, bias, "cuda", engine=engine)
+        if engine == "fp6":
+            xc = torch.empty((G, RBa, 1536), dtype=torch.uint8, device="cuda")
+            xs = torch.empty((G, 32 * RBa), dtype=torch.float16, device="cuda")
+        else:
+            xc = torch.empty((M, K // 2), dtype=torch.uint8, device="cuda")
+            xs = torch.empty((G, M), dtype=torch.float16, device="cuda")
+
+        def step_of(fused, lin=lin, engine=engine, xc=xc, xs=xs):
+            if engine == "fp6":
+                def step():
+                    S.quant_act_lora_down_fp6(x, lin.smooth_inv, lin.lora_down, r, out=(xc, xs, la))
+                    if fused:
+                        S.gemm_w4a4_fp6_lora_up_qkv(xc, xs, lin.w_fp6, lin.w_scales, la, lin.lora_up, lin.bias,
+                                                    gq, gk, cos_d, sin_d, M, N, K, r, out=y)
+                    else:
+                        S.gemm_w4a4_fp6_lora_up(xc, xs, lin.w_fp6, lin.w_scales, la, lin.lora_up, lin.bias,
+                                                M, N, K, r, out=y)
+            else:
+                def step():
+                    S.quant_act_lora_down(x, lin.smooth_inv, lin.lora_down, r, out=(xc, xs, la))
+                    if fused:
+                        S.gemm_w4a4_lora_up_qkv(xc, xs, lin.w_codes, lin.w_scales, la, lin.lora_up, lin.bias,
+                                                gq, gk, cos_d, sin_d, M, N, K, r, out=y)
+                    else:
+                        S.gemm_w4a4_lora_up(xc, xs, lin.w_codes, lin.w_scales, la, lin.lora_up, lin.bias,
+                                            M, N, K, r, out=y)
+            return step
+
+        def timed(step):
+            settle(step)
+            for _ in range(warmup):
+                step()
+            torch.cuda.synchronize()
+            t0 = time.perf_counter()
+            for _ in range(steps):
+                step()
+            torch.cuda.synchronize()
+            return (time.perf_counter() - t0) * 1e3 / steps
+
+        plain_ms, fused_ms = timed(step_of(False)), timed(step_of(True))
+        pre = "" if engine == "fp6" else "int8_"
+        res.update({pre + "plain_ms_per_step": round(plain_ms, 5), pre + "fused_ms_per_step": round(fused_ms, 5),
+                    pre + "fused_effective_tops": round(ops / (fused_ms * 1e-3) / 1e12, 2),
+                    pre + "epilogue_overhead_frac": round(fused_ms / plain_ms - 1.0, 4)})
+        del lin, xc, xs
+    res["engine"] = "fp6 (int8_* keys: the int8 engine)"
+    return res
 
 
 def bench_awq(S, workloads, steps, warmup, M=1):

@@ -306,6 +306,25 @@ int svdq_gemm_w4a4_fp6_lora_up(const void* x_fp6, const void* x_scales,
                                int M, int N, int K, int rank, int group, int out_dtype,
                                void* y, void* stream);
 
+/* Device, asynchronous.  The fused QKV operator of svdq_gemm_w4a4_lora_up_qkv
+ * (the same per-head RMSNorm of the Q and K heads and rotary embedding of
+ * their adjacent pairs, the same argument meanings) on the 6-bit MFMA: the
+ * projection is that of svdq_gemm_w4a4_fp6_lora_up in every bit, bias
+ * included, so the V columns equal its output exactly; the Q and K heads
+ * are then normalized and rotated in fp32 before the one rounding.
+ *   x_fp6, x_scales, w_fp6, w_scales, lora_act, lora_up, bias as
+ *   svdq_gemm_w4a4_fp6_lora_up; norm_q, norm_k, rope_cos, rope_sin, eps as
+ *   svdq_gemm_w4a4_lora_up_qkv.
+ * Errors: those of both; rotary tables of 2 GiB or more (M * 256 bytes)
+ * return SVDQ_ERR_UNSUPPORTED_SHAPE. */
+int svdq_gemm_w4a4_fp6_lora_up_qkv(const void* x_fp6, const void* x_scales,
+                                   const void* w_fp6, const void* w_scales,
+                                   const float* lora_act, const void* lora_up, const void* bias,
+                                   const void* norm_q, const void* norm_k,
+                                   const float* rope_cos, const float* rope_sin, float eps,
+                                   int M, int N, int K, int rank, int group, int out_dtype,
+                                   void* y, void* stream);
+
 /* ------------------------------------------------------------------------
  * The MLP chain (SVDQuant pages: "Introducing Nunchaku Lite", the fused
  * GELU/MLP kernels of the original engine).  An MLP pair is an up layer

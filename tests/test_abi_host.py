@@ -103,6 +103,15 @@ def test_device_entry_validation_precedes_device_use():
     #       x6    xs    w6    ws    la    lu    bias  M        N      K    r   g   out y
     assert g6(p[0], p[1], p[2], p[3], p[4], p[5], None, 1 << 17, 8192, 128, 16, 64, 0, p[6], None) == L.SVDQ_ERR_UNSUPPORTED_SHAPE
     assert g6(p[0], p[1], p[2], p[3], p[4], p[5], None, 1 << 16, 8192, 128, 16, 64, 1, p[6], None) == L.SVDQ_ERR_UNSUPPORTED_SHAPE
+    q6 = L.lib().svdq_gemm_w4a4_fp6_lora_up_qkv
+    #       x6    xs    w6    ws    la    lu    bias  nq    nk    cos   sin   eps   M   N    K    r   g   out y
+    assert q6(p[0], p[1], p[2], p[3], p[4], p[5], None, p[6], p[7], p[8], p[9], 1e-6, 16, 256, 128, 16, 64, 0, p[6], None) == L.SVDQ_ERR_UNSUPPORTED_SHAPE
+    assert q6(p[0], p[1], p[2], p[3], p[4], p[5], None, p[6], None, p[8], p[9], 1e-6, 16, 384, 128, 16, 64, 0, p[6], None) == L.SVDQ_ERR_INVALID_ARG
+    assert q6(p[0], p[1], p[2], p[3], p[4], p[5], None, p[6], p[7], None, p[9], 1e-6, 16, 384, 128, 16, 64, 0, p[6], None) == L.SVDQ_ERR_INVALID_ARG
+    assert q6(p[0], p[1], p[2], p[3], p[4], p[5], None, p[6], p[7], p[8], p[9], float("nan"), 16, 384, 128, 16, 64, 0, p[6], None) == L.SVDQ_ERR_INVALID_ARG
+    assert q6(p[0], p[1], p[2], p[3], p[4], p[5], None, p[6] + 2, p[7], None, None, 1e-6, 16, 384, 128, 16, 64, 0, p[6], None) == L.SVDQ_ERR_INVALID_ARG
+    assert q6(p[0], p[1], p[2], p[3], p[4], p[5], None, p[6], p[7], p[8], p[9], 1e-6, big, 384, 128, 16, 64, 0, p[6], None) == L.SVDQ_ERR_UNSUPPORTED_SHAPE
+    assert q6(p[0], p[1], p[2], p[3], p[4], p[5], None, p[6], p[7], None, None, 1e-6, 1 << 17, 8448, 128, 16, 64, 0, p[6], None) == L.SVDQ_ERR_UNSUPPORTED_SHAPE
     pr = L.lib().svdq_probe_mfma
     assert pr(5, 1, 1, p[0], None) == L.SVDQ_ERR_INVALID_ARG          # unknown kind
     assert pr(-1, 1, 1, p[0], None) == L.SVDQ_ERR_INVALID_ARG

@@ -14,8 +14,8 @@ import torch
 import oracle as O
 import workloads
 from tests._fp6 import ACT, WGT, decode_fp6
-from tests._helpers import (bf16_bits_to_f64, check_bf16_elementwise, f64_to_bf16_bits,  # noqa: F401
-                            oracle_prep_to_abi, ulp_bf16)
+from tests._helpers import (bf16_bits_to_f64, check_bf16_elementwise, check_f32_elementwise, f64_to_bf16_bits,  # noqa: F401,E501
+                            abi_to_oracle_prep, oracle_prep_to_abi, ulp_bf16)
 
 S = pytest.importorskip("w4a4_rank_corrected_svdq_amd")
 from w4a4_rank_corrected_svdq_amd import _lib as L  # noqa: E402
@@ -257,3 +257,126 @@ def test_repeat_runs_bitwise_equal():
                              dev_bf16(Lr.bias_bits), M, N, K, rank).view(torch.int16).cpu().numpy())
     for o in outs[1:]:
         np.testing.assert_array_equal(o, outs[0])
+
+
+# ------------------------------------------------------------------ fused QKV epilogue
+def _check(yg, yo, out):
+    """The output bars of this file: 1e-3 relative Frobenius and one bf16 ulp
+    elementwise (bf16), or 1e-5 and 2^-14 (|y| + rms y) elementwise (fp32)."""
+    err = O.rel_fro(yg, yo)
+    if out == "f32":
+        assert err <= 1e-5, err
+        check_f32_elementwise(yg, yo)
+    else:
+        assert err <= Y_TOL, err
+        check_bf16_elementwise(yg, yo)
+
+
+def _qkv_tables(M, seed, rope):
+    (qb, qv), (kb, kv) = workloads.norm_weights(seed=seed)
+    cos = sin = None
+    if rope:
+        ang = np.random.default_rng(seed).uniform(-np.pi, np.pi, (M, 64))
+        cos, sin = np.cos(ang).astype(np.float32), np.sin(ang).astype(np.float32)
+    return qb, qv, kb, kv, cos, sin
+
+
+def run_qkv6(xf, xs, wf, abi, la, bias_bits, M, qb, kb, cos, sin, out_dtype=L.SVDQ_OUT_BF16):
+    r = abi["rank"]
+    y = S.gemm_w4a4_fp6_lora_up_qkv(xf, xs, wf, dev(abi["w_scales"]), la, dev_bf16(abi["lora_up"]) if r else None,
+                                    dev_bf16(bias_bits) if bias_bits is not None else None,
+                                    dev_bf16(qb), dev_bf16(kb),
+                                    dev(cos) if cos is not None else None, dev(sin) if sin is not None else None,
+                                    M, abi["N"], abi["K"], r, out_dtype=out_dtype)
+    torch.cuda.synchronize()
+    return y
+
+
+# heads = 3 puts the Q / K boundary inside a 256-column tile (its first wave
+# Q, its second K); 11 heads on M = 4000 leave the last tile column half past
+# N and the last tile row 160 rows deep (rotary rows past M read as zeros and
+# never stored); M = 1 is a single row.  K = 64 and 128 (two stages per tile)
+# and K = 256 at rank 16 (three) put the staged rotary factors into ring
+# slots that the first stages use.
+@pytest.mark.parametrize("M,K,heads,rank,bias,rope,out", [
+    (300, 512, 2, 32, True, True, "bf16"), (300, 512, 2, 32, True, True, "f32"), (64, 512, 1, 0, False, False, "bf16"),
+    (129, 512, 3, 16, True, False, "f32"), (513, 512, 3, 32, True, True, "bf16"), (1, 512, 1, 16, True, True, "bf16"),
+    (4000, 256, 11, 16, True, True, "bf16"), (200, 64, 2, 0, True, True, "bf16"), (300, 128, 3, 16, False, True, "f32"),
+    (520, 256, 1, 16, True, True, "bf16")])
+def test_qkv_epilogue_vs_oracle(M, K, heads, rank, bias, rope, out):
+    """The 6-bit kernel 2 with the fused QKV epilogue (per-head RMSNorm of Q
+    and K, rotary embedding of their adjacent pairs) against the oracle's
+    fused QKV operator on the oracle's own codes, scales and lora_act; the V
+    columns bit-identical to the plain 6-bit kernel."""
+    N = 3 * heads * 128
+    wl, Lr, po, abi = _case(M, K, N, rank, seed=70 + M + heads, bias=bias)
+    qb, qv, kb, kv, cos, sin = _qkv_tables(M, 71 + M, rope)
+    _, parts = O.forward(wl.x, po, bias=Lr.bias if bias else None, out="f64", return_parts=True)
+    ref = O.forward_qkv(wl.x, po, Lr.bias if bias else None, qv, kv, cos, sin, out=out)
+    xf = dev(S.pack_fp6_operand(O.pack_int4(parts["qx"]), ACT))
+    xs = dev(pad_scales(parts["sx"].T.astype(np.float16), M))
+    wf = dev(S.pack_fp6_operand(abi["w_codes"], WGT))
+    la = dev(parts["lora_act"].astype(np.float32)) if rank else None
+    od = L.SVDQ_OUT_F32 if out == "f32" else L.SVDQ_OUT_BF16
+    bb = Lr.bias_bits if bias else None
+    y = run_qkv6(xf, xs, wf, abi, la, bb, M, qb, kb, cos, sin, out_dtype=od)
+    _check(y_to_np(y), ref, out)
+    plain = run_gemm(xf, xs, wf, dev(abi["w_scales"]), la, dev_bf16(abi["lora_up"]) if rank else None,
+                     dev_bf16(bb) if bb is not None else None, M, N, K, rank, od)
+    v0 = 2 * heads * 128
+    np.testing.assert_array_equal(y[:, v0:].view(torch.int16 if out == "bf16" else torch.int32).cpu().numpy(),
+                                  plain[:, v0:].view(torch.int16 if out == "bf16" else torch.int32).cpu().numpy())
+
+
+def test_qkv_full_size_sampled_rows():
+    """The joint-stream QKV shape (4096 image + 512 text rows, 3072 -> 9216,
+    rank 32, bias) with rotary tables of the FLUX form, through both 6-bit
+    kernels in the launch configuration the benchmark times: sampled rows
+    (first, last, random) against the oracle's fused QKV operator, every V
+    column bit-identical to the plain 6-bit kernel."""
+    wl = workloads.make_workload("joint_qkv")
+    Lr = wl.layers[0]
+    M, K, N, r = wl.M, Lr.K, Lr.N, 32
+    rng = np.random.default_rng(13)
+    a = wl.act_absmax()
+    _, lam = O.smoothing_factors(a, Lr.weight)
+    l1 = O.bf16(rng.standard_normal((K, r)) * float(np.abs(lam).mean() * 0.02))
+    l2 = O.bf16(rng.standard_normal((r, N)) / np.sqrt(N))
+    po = O.prepare(Lr.weight, a, rank=r, factors=(l1, l2))
+    abi = oracle_prep_to_abi(po)
+    (qb, qv), (kb, kv) = workloads.norm_weights(seed=14)
+    cos, sin = workloads.rope_tables(512, 64)
+    xf, xs, la = run_k1(wl.x_bits, abi["smooth_inv"], abi["lora_down"], r)
+    wf = dev(S.pack_fp6_operand(abi["w_codes"], WGT))
+    y = run_qkv6(xf, xs, wf, abi, la, Lr.bias_bits, M, qb, kb, cos, sin)
+    rows = np.unique(np.concatenate([np.arange(8), rng.choice(M, 32, replace=False), np.arange(M - 8, M)]))
+    ref = O.forward_qkv(wl.x[rows], po, Lr.bias, qv, kv, cos[rows], sin[rows])
+    _check(to_np_bf16(y[torch.from_numpy(rows).cuda()]), ref, "bf16")
+    assert torch.isfinite(y.float()).all()
+    plain = run_gemm(xf, xs, wf, dev(abi["w_scales"]), la, dev_bf16(abi["lora_up"]), dev_bf16(Lr.bias_bits),
+                     M, N, K, r)
+    v0 = 2 * N // 3
+    assert torch.equal(y[:, v0:].view(torch.int16), plain[:, v0:].view(torch.int16))
+
+
+@pytest.mark.parametrize("engine", ["fp6", "int8"])
+def test_linear_forward_qkv(engine):
+    """SVDQW4A4Linear.forward_qkv (its own kernel 1, then the fused QKV
+    kernel 2 of the engine) against the oracle's fused QKV operator on the
+    library-prepared arrays; its V columns equal the module's plain forward."""
+    M, K, heads, r = 300, 512, 2, 32
+    N = 3 * heads * 128
+    wl = workloads.custom_workload(M, K, N, seed=83, n_out=4, bias=True)
+    Lr = wl.layers[0]
+    p = S.prepare_weights(Lr.weight_bits, wl.act_absmax(), rank=r)
+    po = abi_to_oracle_prep(p)
+    lin = S.SVDQW4A4Linear(p, torch.from_numpy(Lr.bias_bits.view(np.int16).copy()).view(torch.bfloat16), "cuda",
+                           engine=engine)
+    qb, qv, kb, kv, cos, sin = _qkv_tables(M, 84, True)
+    x = dev_bf16(wl.x_bits)
+    y = lin.forward_qkv(x, dev_bf16(qb), dev_bf16(kb), dev(cos), dev(sin))
+    plain = lin(x)
+    torch.cuda.synchronize()
+    _check(to_np_bf16(y), O.forward_qkv(wl.x, po, Lr.bias, qv, kv, cos, sin), "bf16")
+    v0 = 2 * heads * 128
+    assert torch.equal(y[:, v0:].view(torch.int16), plain[:, v0:].view(torch.int16))

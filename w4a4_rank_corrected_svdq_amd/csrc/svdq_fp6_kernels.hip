@@ -156,7 +156,7 @@ __device__ __forceinline__ void tile_of(int t, int nM, int nN, int& tm, int& tn)
   tn = r / gm;
 }
 
-// The MLP chain's epilogue (CHAIN = 1): instead of storing Y, the block
+// The MLP chain's epilogue (EPI = 1): instead of storing Y, the block
 // turns its output tile into the next layer's kernel-1 outputs -- bf16(Y),
 // tanh-GELU, the next layer's smoothing and per-(row, group of 64) INT4
 // quantizer, codes in the 6-bit containers -- and the tile's 256-column
@@ -171,14 +171,51 @@ struct ChainArgs {
   float* partials;           // [ceil(N/256)][M][rank]
 };
 constexpr int C_TS = 2 * F_BN + 16;                   // staging row stride in bytes (bank spread)
+
+// The fused QKV epilogue (EPI = 2; "Nunchaku Engine Design": normalization
+// and rotary embedding fused into the QKV projection).  The output columns
+// are Q heads, then K heads, then V heads of 128 columns (N = 3 heads 128);
+// a wave's 128 columns are one head.  After bias, each Q or K row is scaled
+// by 1 / sqrt(mean of its 128 squares + eps) and the head's bf16 norm
+// weights, then adjacent column pairs (2 j, 2 j + 1) are rotated by
+// cos / sin[row][j] when the tables are given; V is stored as projected.
+struct QkvArgs6 {
+  const uint16_t* gq;        // [128] bf16 norm weights of the Q heads
+  const uint16_t* gk;        // [128] bf16 norm weights of the K heads
+  const float* cos;          // [M][64] fp32 or NULL (no rotation)
+  const float* sin;          // [M][64] fp32
+  float eps;
+};
+constexpr int Q_HEAD = 128;
+constexpr int Q_TAB = F_BM * 256;                     // bytes of one staged rotary table (256 rows x 64 fp32)
+static_assert(2 * Q_TAB <= F_NS * F_SLOT, "both rotary tables fit the idle ring");
+
+template <int CTRL>
+__device__ __forceinline__ float dpp_f(float x) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, x), CTRL, 0xF, 0xF, true));
+}
+// Sum over the 32 lanes of each wave half, the same value in all of them:
+// quad swaps (lane ^ 1, ^ 2), then the mirrors within 8 and within 16 lanes
+// (each pairs a lane with one in the other half of its 8 or 16), then lane
+// ^ 16 by swizzle (bit-mask mode: and 0x1F, xor 0x10).
+__device__ __forceinline__ float sum32(float v) {
+  v += dpp_f<0xB1>(v);
+  v += dpp_f<0x4E>(v);
+  v += dpp_f<0x141>(v);
+  v += dpp_f<0x140>(v);
+  v += __builtin_bit_cast(float, __builtin_amdgcn_ds_swizzle(__builtin_bit_cast(int, v), 0x401F));
+  return v;
+}
 static_assert(F_BM * C_TS <= F_NS * F_SLOT, "the chain's staging tile fits the idle ring");
 
-template <int OUT_F32, int CHAIN>
+// EPI: 0 store Y, 1 the MLP chain's epilogue, 2 the fused QKV epilogue.
+template <int OUT_F32, int EPI>
 __global__ __launch_bounds__(F_THREADS, 1) void k_gemm_w4a4_fp6(
     const uint8_t* __restrict__ x_fp6, const _Float16* __restrict__ x_scales,
     const uint8_t* __restrict__ w_fp6, const _Float16* __restrict__ w_scales,
     const float* __restrict__ lora_act, const uint16_t* __restrict__ lora_up,
-    const uint16_t* __restrict__ bias, int M, int N, int K, int rank, void* __restrict__ y, ChainArgs ca) {
+    const uint16_t* __restrict__ bias, int M, int N, int K, int rank, void* __restrict__ y, ChainArgs ca,
+    QkvArgs6 qa) {
   __shared__ __align__(16) unsigned char ring[F_NS][F_SLOT];
   __shared__ __align__(16) float conv[2][F_CONV];
   __shared__ __align__(16) uint16_t bias_ring[2][F_BN];   // bias of the tiles with even / odd index j
@@ -304,6 +341,36 @@ __global__ __launch_bounds__(F_THREADS, 1) void k_gemm_w4a4_fp6(
       aux_cur += aux_step;
     }
   };
+  // The fused QKV epilogue's rotary factors (one tile per block; a tile with
+  // Q / K columns and tables given): rows 64 g .. 64 g + 63 of the tile (the
+  // rows of the waves with wm = g) of each table form a 16 KB piece, moved by
+  // LDS-DMA (a load of a wave fills four 256-byte rows; rows past M read
+  // zeros) in three parts into ring slots as they fall free: part 0 (cos and
+  // sin of g = 0, cos of g = 3) and part 1 (cos and sin of g = 1, sin of
+  // g = 3) take the places of the two padding stages issued during the
+  // tile's last two stages, six loads per wave each (with the auxiliary load,
+  // the usual seven); part 2 (cos and sin of g = 2) goes into the slot of
+  // the last stage once the tile has ended.
+  const bool qkv_rot = EPI == 2 && qa.cos != nullptr && F_BN * (ti & 0xFFFF) < 2 * (N / 3);   // uniform
+  const int qkv_m0 = F_BM * (ti >> 16);
+  auto qkv_table_dma = [&](int part, uint32_t slot_lds) {
+    const int ln = fresh_lane();
+    const uint32_t tbytes = static_cast<uint32_t>(M) * 256u;
+    const int per = part < 2 ? 6 : 4;
+#pragma unroll
+    for (int k = 0; k < 6; ++k) {
+      if (k < per) {
+        const int q = per * wave + k;
+        const int pc = q >> 4, c = q & 15;
+        const bool is_sin = pc == 1 || (part == 1 && pc == 2);
+        const int g = part == 2 ? 2 : (pc < 2 ? part : 3);
+        const int row = qkv_m0 + 64 * g + 4 * c + (ln >> 4);
+        const uint32_t voff = row < M ? static_cast<uint32_t>(row) * 256u + 16u * (ln & 15) : OOB;
+        dma16(dma_rsrc(is_sin ? qa.sin : qa.cos, tbytes),
+              __builtin_amdgcn_readfirstlane(slot_lds + 16384u * pc + 1024u * c), voff);
+      }
+    }
+  };
   auto issue = [&]() {
     const bool live = ji < my_tiles;
     const uint32_t blds = __builtin_amdgcn_readfirstlane(bias_lds + 512u * static_cast<uint32_t>(ji & 1));
@@ -324,7 +391,9 @@ __global__ __launch_bounds__(F_THREADS, 1) void k_gemm_w4a4_fp6(
     const int ln = fresh_lane();
     const uint32_t l16 = 16u * ln;
     const int tmi = ti >> 16, tni = ti & 0xFFFF;
-    if (li < GS || !live) {
+    if (EPI == 2 && qkv_rot && !live && li < 2) {
+      qkv_table_dma(li, __builtin_amdgcn_readfirstlane(ring0 + so));
+    } else if (li < GS || !live) {
 #pragma unroll
       for (int hh = 0; hh < 2; ++hh) {
         const int g = 2 * li + hh;
@@ -429,7 +498,7 @@ __global__ __launch_bounds__(F_THREADS, 1) void k_gemm_w4a4_fp6(
   // bf16 MFMA (E3).  Rows M .. Mp - 1 get zero codes and scales, as kernel 1
   // writes them; rows and groups past the operands are not written.
   auto chain_epilogue = [&](int tt) {
-    if constexpr (CHAIN) {
+    if constexpr (EPI == 1) {
       const int tmc = tt >> 16, tnc = tt & 0xFFFF;
       __builtin_amdgcn_s_waitcnt(waitcnt_vm_lgkm0(0));
       __syncthreads();
@@ -565,6 +634,85 @@ __global__ __launch_bounds__(F_THREADS, 1) void k_gemm_w4a4_fp6(
     }
   };
 
+  // The QKV epilogue (one tile per block): bias into the accumulators, then
+  // for a wave whose 128 columns are a Q or K head, per row the sum of
+  // squares over the head (the lane's four columns, then the 32 lanes of its
+  // half), the scale 1 / sqrt(sum / 128 + eps), the norm weights, and the
+  // rotation.  Two thirds of the rotary factors are in the ring already
+  // (parts 0 and 1 above); part 2 is loaded while the norms are formed.  A
+  // lane's pairs are columns (4 c, 4 c + 1) and (4 c + 2, 4 c + 3) of the
+  // head: factors 2 c and 2 c + 1 of its row, one 8-byte read per table (32
+  // lanes read a row's 256 contiguous bytes) from its wave's pieces.  Tiles whose
+  // columns are all V (2 H 128 is a multiple of 256, so a tile is all Q / K
+  // or all V) only add the bias.
+  auto qkv_epilogue = [&](int tt, const float (&bv)[4]) {
+    if constexpr (EPI == 2) {
+      const int HD = N / 3;
+      const int cw = F_BN * (tt & 0xFFFF) + 128 * wn;
+      // slots of the tile's stages SPT (part 0), SPT + 1 (part 1), SPT - 1 (part 2)
+      const uint32_t sA = static_cast<uint32_t>(SPT % F_NS) * F_SLOT;
+      const uint32_t sB = static_cast<uint32_t>((SPT + 1) % F_NS) * F_SLOT;
+      const uint32_t sC = static_cast<uint32_t>((SPT - 1) % F_NS) * F_SLOT;
+      if (qkv_rot) {
+        // every wave is past its reads of the last stage's slot (their values
+        // are in the accumulators); parts 0 and 1 may still be landing
+        __builtin_amdgcn_s_barrier();
+        asm volatile("" ::: "memory");
+        qkv_table_dma(2, __builtin_amdgcn_readfirstlane(ring0 + sC));
+      }
+#pragma unroll
+      for (int a = 0; a < 2; ++a)
+#pragma unroll
+        for (int t = 0; t < 4; ++t)
+#pragma unroll
+          for (int e = 0; e < 16; ++e) acc[a][t][e] += bv[t];
+      const bool qk = cw < 2 * HD;                            // wave-uniform
+      const int ln = fresh_lane();
+      const int lc = ln & 31, lh = ln >> 5;
+      if (qk) {
+        const uint16_t* g = cw < HD ? qa.gq : qa.gk;
+        const uint2 gu = *reinterpret_cast<const uint2*>(g + 4 * lc);
+        const float g4[4] = {bf16_bits_to_f32(gu.x & 0xFFFFu), bf16_bits_to_f32(gu.x >> 16),
+                             bf16_bits_to_f32(gu.y & 0xFFFFu), bf16_bits_to_f32(gu.y >> 16)};
+#pragma unroll
+        for (int a = 0; a < 2; ++a)
+#pragma unroll
+          for (int e = 0; e < 16; ++e) {
+            float ss = 0.f;
+#pragma unroll
+            for (int t = 0; t < 4; ++t) ss = __builtin_fmaf(acc[a][t][e], acc[a][t][e], ss);
+            ss = sum32(ss);
+            // hardware reciprocal square root (1 ulp)
+            const float scale = __builtin_amdgcn_rsqf(ss * (1.0f / Q_HEAD) + qa.eps);
+#pragma unroll
+            for (int t = 0; t < 4; ++t) acc[a][t][e] = acc[a][t][e] * scale * g4[t];
+          }
+      }
+      if (qkv_rot) {
+        __builtin_amdgcn_s_waitcnt(waitcnt_vm_lgkm0(0));
+        __builtin_amdgcn_s_barrier();
+        asm volatile("" ::: "memory");
+        const uint32_t cb = wm == 0 ? sA : (wm == 1 ? sB : (wm == 2 ? sC : sA + 32768u));
+        const uint32_t sb = wm == 0 ? sA + 16384u : (wm == 1 ? sB + 16384u : (wm == 2 ? sC + 16384u : sB + 32768u));
+        const unsigned char* tc = &ring[0][0] + cb;
+        const unsigned char* ts = &ring[0][0] + sb;
+#pragma unroll
+        for (int a = 0; a < 2; ++a)
+#pragma unroll
+          for (int e = 0; e < 16; ++e) {
+            const int rl = 32 * a + 8 * (e >> 2) + 4 * lh + (e & 3);   // row within the wave's 64
+            const float2 cs = *reinterpret_cast<const float2*>(tc + rl * 256 + 8 * lc);
+            const float2 sn = *reinterpret_cast<const float2*>(ts + rl * 256 + 8 * lc);
+            const float o0 = acc[a][0][e], o1 = acc[a][1][e], o2 = acc[a][2][e], o3 = acc[a][3][e];
+            acc[a][0][e] = o0 * cs.x - o1 * sn.x;
+            acc[a][1][e] = o1 * cs.x + o0 * sn.x;
+            acc[a][2][e] = o2 * cs.y - o3 * sn.y;
+            acc[a][3][e] = o3 * cs.y + o2 * sn.y;
+          }
+      }
+    }
+  };
+
   for (int j = 0; j < my_tiles; ++j) {
     const int tt = __builtin_amdgcn_readfirstlane(tiles[j]);
     const int mw = F_BM * (tt >> 16) + 64 * wm, cw = F_BN * (tt & 0xFFFF) + 128 * wn;   // wave-uniform
@@ -670,7 +818,7 @@ __global__ __launch_bounds__(F_THREADS, 1) void k_gemm_w4a4_fp6(
     }
 
     // ---- end of the tile, after its last stage ----
-    if constexpr (CHAIN) {
+    if constexpr (EPI == 1) {
       chain_epilogue(tt);
     } else {
       // The bias ring entry of tile j is rewritten only by the stages of
@@ -684,6 +832,7 @@ __global__ __launch_bounds__(F_THREADS, 1) void k_gemm_w4a4_fp6(
       const uint2 bu = *reinterpret_cast<const uint2*>(&bias_ring[j & 1][128 * wn + 4 * lc]);
       const float bv[4] = {bf16_bits_to_f32(bu.x & 0xFFFFu), bf16_bits_to_f32(bu.x >> 16),
                            bf16_bits_to_f32(bu.y & 0xFFFFu), bf16_bits_to_f32(bu.y >> 16)};
+      if constexpr (EPI == 2) qkv_epilogue(tt, bv);
       // one per-lane base (row mw + 4 h, columns cw + 4 c); each store adds
       // its wave-uniform row offset.  A base past the end stays past it
       // (y is under 2 GiB, the added offsets under 32 rows).
@@ -699,15 +848,17 @@ __global__ __launch_bounds__(F_THREADS, 1) void k_gemm_w4a4_fp6(
           for (int i = 0; i < 4; ++i) {
             const int e = 4 * b + i;
             const uint32_t off = vbase + static_cast<uint32_t>(32 * a + 8 * b + i) * static_cast<uint32_t>(N) * ELEM;
+            // (the QKV epilogue has added the bias already)
+            float o[4];
+#pragma unroll
+            for (int t = 0; t < 4; ++t) o[t] = EPI == 2 ? acc[a][t][e] : acc[a][t][e] + bv[t];
             if (OUT_F32) {
-              const v4f o = v4f{acc[a][0][e] + bv[0], acc[a][1][e] + bv[1], acc[a][2][e] + bv[2],
-                                acc[a][3][e] + bv[3]};
-              __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(v4i, o), y_rs, off, 0, 0);
+              const v4f ov = v4f{o[0], o[1], o[2], o[3]};
+              __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(v4i, ov), y_rs, off, 0, 0);
             } else {
               typedef int v2i_ __attribute__((ext_vector_type(2)));
-              const v2i_ o = v2i_{static_cast<int>(bf16x2_bits(acc[a][0][e] + bv[0], acc[a][1][e] + bv[1])),
-                                  static_cast<int>(bf16x2_bits(acc[a][2][e] + bv[2], acc[a][3][e] + bv[3]))};
-              __builtin_amdgcn_raw_buffer_store_b64(o, y_rs, off, 0, 0);
+              const v2i_ ov = v2i_{static_cast<int>(bf16x2_bits(o[0], o[1])), static_cast<int>(bf16x2_bits(o[2], o[3]))};
+              __builtin_amdgcn_raw_buffer_store_b64(ov, y_rs, off, 0, 0);
             }
           }
 #pragma unroll
@@ -778,10 +929,31 @@ int launch_gemm_w4a4_fp6(const void* x_fp6, const void* x_scales, const void* w_
                      static_cast<const uint8_t*>(x_fp6), static_cast<const _Float16*>(x_scales),              \
                      static_cast<const uint8_t*>(w_fp6), static_cast<const _Float16*>(w_scales), lora_act,    \
                      static_cast<const uint16_t*>(lora_up), static_cast<const uint16_t*>(bias), M, N, K, rank, y, \
-                     ChainArgs{})
+                     ChainArgs{}, QkvArgs6{})
   if (out_dtype == SVDQ_OUT_F32) SVDQ_K2F(1);
   else SVDQ_K2F(0);
 #undef SVDQ_K2F
+  return hipGetLastError() == hipSuccess ? SVDQ_OK : SVDQ_ERR_HIP;
+}
+
+int launch_gemm_w4a4_fp6_qkv(const void* x_fp6, const void* x_scales, const void* w_fp6, const void* w_scales,
+                             const float* lora_act, const void* lora_up, const void* bias, const void* norm_q,
+                             const void* norm_k, const float* rope_cos, const float* rope_sin, float eps, int M, int N,
+                             int K, int rank, int out_dtype, void* y, void* stream) {
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  const int tiles = ((M + F_BM - 1) / F_BM) * ((N + F_BN - 1) / F_BN);
+  const QkvArgs6 qa{static_cast<const uint16_t*>(norm_q), static_cast<const uint16_t*>(norm_k), rope_cos, rope_sin,
+                    eps};
+  // one tile per block: the ring is free for the rotary tables at its end
+#define SVDQ_K2Q(OF)                                                                                          \
+  hipLaunchKernelGGL((k_gemm_w4a4_fp6<OF, 2>), dim3(tiles), dim3(F_THREADS), 0, st,                           \
+                     static_cast<const uint8_t*>(x_fp6), static_cast<const _Float16*>(x_scales),              \
+                     static_cast<const uint8_t*>(w_fp6), static_cast<const _Float16*>(w_scales), lora_act,    \
+                     static_cast<const uint16_t*>(lora_up), static_cast<const uint16_t*>(bias), M, N, K, rank, y, \
+                     ChainArgs{}, qa)
+  if (out_dtype == SVDQ_OUT_F32) SVDQ_K2Q(1);
+  else SVDQ_K2Q(0);
+#undef SVDQ_K2Q
   return hipGetLastError() == hipSuccess ? SVDQ_OK : SVDQ_ERR_HIP;
 }
 
@@ -817,7 +989,7 @@ int launch_mlp_chain_fp6(const void* x_fp6, const void* x_scales, const void* w_
                      static_cast<const uint8_t*>(x_fp6), static_cast<const _Float16*>(x_scales),
                      static_cast<const uint8_t*>(w_fp6), static_cast<const _Float16*>(w_scales), lora_act,
                      static_cast<const uint16_t*>(lora_up), static_cast<const uint16_t*>(bias), M, N, K, rank,
-                     nullptr, ca);
+                     nullptr, ca, QkvArgs6{});
   if (rank_dn > 0) {
     const int S = (N + F_BN - 1) / F_BN;
     const size_t n4 = static_cast<size_t>(M) * rank_dn / 4;

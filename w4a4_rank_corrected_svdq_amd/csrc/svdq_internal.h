@@ -52,6 +52,11 @@ int launch_quant_act_lora_down_fp6(const void* x, const float* smooth_inv, const
 int launch_gemm_w4a4_fp6(const void* x_fp6, const void* x_scales, const void* w_fp6, const void* w_scales,
                          const float* lora_act, const void* lora_up, const void* bias, int M, int N, int K, int rank,
                          int out_dtype, void* y, void* stream);
+// The same kernel with the fused QKV epilogue (one tile per block).
+int launch_gemm_w4a4_fp6_qkv(const void* x_fp6, const void* x_scales, const void* w_fp6, const void* w_scales,
+                             const float* lora_act, const void* lora_up, const void* bias, const void* norm_q,
+                             const void* norm_k, const float* rope_cos, const float* rope_sin, float eps, int M, int N,
+                             int K, int rank, int out_dtype, void* y, void* stream);
 
 // The MLP chain (svdq_fp6_kernels.hip): kernel 2 of the up layer with the
 // down layer's kernel-1 work in its epilogue, then the partials' reduction.

@@ -92,6 +92,27 @@ class SVDQW4A4Linear:
 
     __call__ = forward
 
+    def forward_qkv(self, x: torch.Tensor, norm_q: torch.Tensor, norm_k: torch.Tensor,
+                    rope_cos: Optional[torch.Tensor] = None, rope_sin: Optional[torch.Tensor] = None,
+                    eps: float = 1e-6, out_dtype: int = L.SVDQ_OUT_BF16):
+        """The fused QKV operator of a layer whose weight is [W_q; W_k; W_v]
+        (N = 3 heads 128): the projection, then per-head RMSNorm of the Q and
+        K heads (bf16 weights norm_q, norm_k [128]) and, given rope_cos /
+        rope_sin [M][64] fp32, the rotary embedding of their adjacent pairs;
+        V as projected.  INT4 layers only (either engine)."""
+        M = x.shape[0]
+        if self.engine == "fp6":
+            xf, xs, la = ops.quant_act_lora_down_fp6(x, self.smooth_inv, self.lora_down, self.rank, self.group)
+            return ops.gemm_w4a4_fp6_lora_up_qkv(xf, xs, self.w_fp6, self.w_scales, la, self.lora_up, self.bias,
+                                                 norm_q, norm_k, rope_cos, rope_sin, M, self.N, self.K, self.rank,
+                                                 eps, self.group, out_dtype)
+        if self.precision != "int4":
+            raise ValueError("the fused QKV epilogue runs on INT4 layers")
+        xc, xs, la = ops.quant_act_lora_down(x, self.smooth_inv, self.lora_down, self.rank, self.group)
+        return ops.gemm_w4a4_lora_up_qkv(xc, xs, self.w_codes, self.w_scales, la, self.lora_up, self.bias,
+                                         norm_q, norm_k, rope_cos, rope_sin, M, self.N, self.K, self.rank,
+                                         eps, self.group, out_dtype)
+
 
 class SVDQMLPChain:
     """An MLP pair (up layer, tanh-GELU, down layer), both on the 6-bit

@@ -232,6 +232,35 @@ def gemm_w4a4_fp6_lora_up(x_fp6, x_scales, w_fp6, w_scales, lora_act, lora_up, b
     return out
 
 
+def gemm_w4a4_fp6_lora_up_qkv(x_fp6, x_scales, w_fp6, w_scales, lora_act, lora_up, bias, norm_q, norm_k,
+                              rope_cos, rope_sin, M: int, N: int, K: int, rank: int, eps: float = 1e-6,
+                              group: int = 64, out_dtype: int = L.SVDQ_OUT_BF16,
+                              out: Optional[torch.Tensor] = None):
+    """Kernel 2 on the 6-bit MFMA with the fused QKV epilogue (per-head Q/K
+    RMSNorm + rotary embedding); returns y [M][N] with N = 3 * heads * 128."""
+    dev = x_fp6.device
+    dt = torch.float32 if out_dtype == L.SVDQ_OUT_F32 else torch.bfloat16
+    if out is None:
+        out = torch.empty((M, N), dtype=dt, device=dev)
+    G = K // group if group > 0 else 0
+    RBa, RBb = (M + 31) // 32, 4 * ((N + 127) // 128)
+    st = L.lib().svdq_gemm_w4a4_fp6_lora_up_qkv(
+        _dev_arg("x_fp6", x_fp6, torch.uint8, (G, RBa, 1536), dev),
+        _dev_arg("x_scales", x_scales, torch.float16, (G, 32 * RBa), dev),
+        _dev_arg("w_fp6", w_fp6, torch.uint8, (G, RBb, 1536), dev),
+        _dev_arg("w_scales", w_scales, torch.float16, (G, N), dev),
+        _dev_arg("lora_act", lora_act, torch.float32, (M, rank), dev) if rank else None,
+        _dev_arg("lora_up", lora_up, torch.bfloat16, (N, rank), dev) if rank else None,
+        _dev_arg("bias", bias, torch.bfloat16, (N,), dev),
+        _dev_arg("norm_q", norm_q, torch.bfloat16, (128,), dev),
+        _dev_arg("norm_k", norm_k, torch.bfloat16, (128,), dev),
+        _dev_arg("rope_cos", rope_cos, torch.float32, (M, 64), dev),
+        _dev_arg("rope_sin", rope_sin, torch.float32, (M, 64), dev),
+        float(eps), M, N, K, rank, group, out_dtype, _dev_arg("y", out, dt, (M, N), dev), _stream(dev))
+    L.check(st, "svdq_gemm_w4a4_fp6_lora_up_qkv")
+    return out
+
+
 def mlp_chain_workspace_bytes(M: int, N: int, rank_dn: int) -> int:
     out = ctypes.c_size_t(0)
     L.check(L.lib().svdq_mlp_chain_workspace_bytes(M, N, rank_dn, ctypes.byref(out)), "svdq_mlp_chain_workspace_bytes")
