@@ -799,6 +799,9 @@ def main():
     ap.add_argument("--mix-probe", action="store_true",
                     help="only the register-only probe of the 6-bit route's inner loop (FP6 MFMA, fp32 "
                          "dequantization, both), as one JSON line")
+    ap.add_argument("--qkv-only", action="store_true",
+                    help="only the joint-stream QKV step with and without the fused epilogue, both INT4 "
+                         "engines, as one JSON line")
     ap.add_argument("--traffic-summary", metavar="PMC_DIR",
                     help="no GPU work: write profiles/traffic_<workload>_r<rank>_<engine>.json from the "
                          "rocprofv3 counter runs under PMC_DIR (fetch/, write/; copy_fetch/, copy_write/ "
@@ -842,6 +845,9 @@ def main():
         return
     if args.mix_probe:
         print(json.dumps({"mix_probe": mix_probe()}))
+        return
+    if args.qkv_only:
+        print(json.dumps({"qkv_fused_epilogue": bench_qkv(S, L, workloads, args.rank, args.steps, args.warmup)}))
         return
 
     gen_name, layer, act, desc = BENCH_WORKLOADS[args.workload]
