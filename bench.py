@@ -469,8 +469,7 @@ class Runner:
             S.quant_act_lora_down_fp6(x, lin.smooth_inv, lin.lora_down, r, act=self.act, out=(self.xc, self.xs, self.la))
             if mid is not None:
                 mid.record()
-            S.gemm_w4a4_fp6_lora_up(self.xc, self.xs, lin.w_fp6, lin.w_scales, self.la, lin.lora_up, lin.bias,
-                                    M, N, K, r, out=self.y)
+            lin.kernel2_fp6(self.xc, self.xs, self.la, M, out=self.y)
         elif self.engine == "mxfp4":
             S.quant_act_lora_down_mxfp4(x, lin.smooth_inv, lin.lora_down, r, act=self.act, out=(self.xc, self.xs, self.la))
             if mid is not None:
@@ -611,7 +610,7 @@ def bench_mlp_chain(S, L, workloads, r, steps, warmup):
         S.quant_act_lora_down_fp6(x, up.smooth_inv, up.lora_down, r, out=(xf, xs, la))
 
     def k2_dn():
-        S.gemm_w4a4_fp6_lora_up(xf2, xs2, dn.w_fp6, dn.w_scales, la2, dn.lora_up, dn.bias, M, N2, N, r, out=y2)
+        dn.kernel2_fp6(xf2, xs2, la2, M, out=y2)
 
     def chain_step():
         k1_up()
@@ -621,7 +620,7 @@ def bench_mlp_chain(S, L, workloads, r, steps, warmup):
 
     def two_layer_step():
         k1_up()
-        S.gemm_w4a4_fp6_lora_up(xf, xs, up.w_fp6, up.w_scales, la, up.lora_up, up.bias, M, N, K, r, out=y1)
+        up.kernel2_fp6(xf, xs, la, M, out=y1)
         S.quant_act_lora_down_fp6(y1, dn.smooth_inv, dn.lora_down, r, act=L.SVDQ_ACT_GELU_TANH, out=(xf2, xs2, la2))
         k2_dn()
 

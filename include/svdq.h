@@ -306,6 +306,28 @@ int svdq_gemm_w4a4_fp6_lora_up(const void* x_fp6, const void* x_scales,
                                int M, int N, int K, int rank, int group, int out_dtype,
                                void* y, void* stream);
 
+/* Device, asynchronous.  The same layer as svdq_gemm_w4a4_fp6_lora_up (the
+ * same sum, each group as fma(P_g * s_w, s_x, acc), then the up projection
+ * 16 ranks at a time, then the bias; one rounding), computed in 256 x 192
+ * output tiles: for layers whose 256 x 256 tiles would leave CUs idle (N =
+ * 3072 at M = 4096: 192 tiles of 256 x 256, 256 of 256 x 192).
+ *   w_fp6    the weight codes in the SVDQ_FP6_ACTIVATIONS layout (plain row
+ *            blocks of 32 channels; svdq_pack_fp6_operand with that layout),
+ *   other arguments and layouts as svdq_gemm_w4a4_fp6_lora_up.
+ * N must be a multiple of 192, else SVDQ_ERR_UNSUPPORTED_SHAPE; other errors
+ * as svdq_gemm_w4a4_fp6_lora_up. */
+int svdq_gemm_w4a4_fp6_lora_up_n192(const void* x_fp6, const void* x_scales,
+                                    const void* w_fp6, const void* w_scales,
+                                    const float* lora_act, const void* lora_up, const void* bias,
+                                    int M, int N, int K, int rank, int group, int out_dtype,
+                                    void* y, void* stream);
+
+/* Host.  1 when svdq_gemm_w4a4_fp6_lora_up_n192 is expected to be faster
+ * than svdq_gemm_w4a4_fp6_lora_up for an M x N output on the current device
+ * (N % 192 == 0 and less time in rounds of tiles over the CUs, counting a
+ * 256 x 192 tile as 0.875 of a 256 x 256 one), else 0. */
+int svdq_fp6_n192_preferred(int M, int N);
+
 /* Device, asynchronous.  The fused QKV operator of svdq_gemm_w4a4_lora_up_qkv
  * (the same per-head RMSNorm of the Q and K heads and rotary embedding of
  * their adjacent pairs, the same argument meanings) on the 6-bit MFMA: the

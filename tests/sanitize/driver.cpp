@@ -181,6 +181,12 @@ static void device_argument_checks() {
                                                   nullptr)));
   EXPECT(svdq_gemm_w4a4_fp6_lora_up(p, p, p, p, f, p, nullptr, M, N, 96, r, 64, SVDQ_OUT_F32, p, nullptr) !=
          SVDQ_OK);
+  EXPECT(passed_checks(svdq_gemm_w4a4_fp6_lora_up_n192(p, p, p, p, f, p, nullptr, M, 384, K, r, 64, SVDQ_OUT_BF16, p,
+                                                       nullptr)));
+  EXPECT(svdq_gemm_w4a4_fp6_lora_up_n192(p, p, p, p, f, p, nullptr, M, 256, K, r, 64, SVDQ_OUT_BF16, p, nullptr) ==
+         SVDQ_ERR_UNSUPPORTED_SHAPE);
+  EXPECT(svdq_gemm_w4a4_fp6_lora_up_n192(p, p, p, nullptr, f, p, nullptr, M, 384, K, r, 64, SVDQ_OUT_BF16, p,
+                                         nullptr) == SVDQ_ERR_INVALID_ARG);
   EXPECT(passed_checks(svdq_gemm_w4a4_fp6_lora_up_qkv(p, p, p, p, f, p, nullptr, p, p, f, f, 1e-6f, M, 384, K, r,
                                                       64, SVDQ_OUT_BF16, p, nullptr)));
   EXPECT(svdq_gemm_w4a4_fp6_lora_up_qkv(p, p, p, p, f, p, nullptr, p, p, f, nullptr, 1e-6f, M, 384, K, r, 64,

@@ -103,6 +103,14 @@ def test_device_entry_validation_precedes_device_use():
     #       x6    xs    w6    ws    la    lu    bias  M        N      K    r   g   out y
     assert g6(p[0], p[1], p[2], p[3], p[4], p[5], None, 1 << 17, 8192, 128, 16, 64, 0, p[6], None) == L.SVDQ_ERR_UNSUPPORTED_SHAPE
     assert g6(p[0], p[1], p[2], p[3], p[4], p[5], None, 1 << 16, 8192, 128, 16, 64, 1, p[6], None) == L.SVDQ_ERR_UNSUPPORTED_SHAPE
+    n6 = L.lib().svdq_gemm_w4a4_fp6_lora_up_n192
+    #       x6    xs    w6    ws    la    lu    bias  M        N      K    r   g   out y
+    assert n6(p[0], p[1], p[2], p[3], p[4], p[5], None, 16, 256, 128, 16, 64, 0, p[6], None) == L.SVDQ_ERR_UNSUPPORTED_SHAPE
+    assert n6(p[0], p[1], p[2], p[3], p[4], p[5], None, 16, 384, 96, 16, 64, 0, p[6], None) == L.SVDQ_ERR_UNSUPPORTED_SHAPE
+    assert n6(p[0], p[1], None, p[3], p[4], p[5], None, 16, 384, 128, 16, 64, 0, p[6], None) == L.SVDQ_ERR_INVALID_ARG
+    assert n6(p[0], p[1], p[2], p[3], p[4], p[5], None, 16, 384, 128, 16, 64, 3, p[6], None) == L.SVDQ_ERR_INVALID_ARG
+    assert n6(p[0], p[1], p[2], p[3] + 4, p[4], p[5], None, 16, 384, 128, 16, 64, 0, p[6], None) == L.SVDQ_ERR_INVALID_ARG
+    assert n6(p[0], p[1], p[2], p[3], p[4], p[5], None, 1 << 17, 8448, 128, 16, 64, 0, p[6], None) == L.SVDQ_ERR_UNSUPPORTED_SHAPE
     q6 = L.lib().svdq_gemm_w4a4_fp6_lora_up_qkv
     #       x6    xs    w6    ws    la    lu    bias  nq    nk    cos   sin   eps   M   N    K    r   g   out y
     assert q6(p[0], p[1], p[2], p[3], p[4], p[5], None, p[6], p[7], p[8], p[9], 1e-6, 16, 256, 128, 16, 64, 0, p[6], None) == L.SVDQ_ERR_UNSUPPORTED_SHAPE

@@ -188,6 +188,27 @@ def test_k2_fp6_guarded(M, K, N, rank, out):
     _check_out(gy.t, parts["y"], out)
 
 
+@pytest.mark.parametrize("M,K,N,rank,out", [(300, 256, 384, 32, "bf16"), (4001, 128, 3072, 16, "bf16"),
+                                             (129, 192, 576, 0, "f32")])
+def test_k2_fp6_n192_guarded(M, K, N, rank, out):
+    """The 256 x 192 form of the 6-bit kernel 2: ragged M (4001 rows leave
+    the last tile row 161 deep), fp32 and bf16 outputs."""
+    wl, Lr, po, abi, parts = _k2_inputs(M, K, N, rank, seed=131 + M + rank)
+    G, Mp = K // 64, 32 * ((M + 31) // 32)
+    xs = np.zeros((G, Mp), np.float16)
+    xs[:, :M] = parts["sx"].T
+    od = L.SVDQ_OUT_F32 if out == "f32" else L.SVDQ_OUT_BF16
+    gy = Guarded((M, N), torch.float32 if out == "f32" else torch.bfloat16)
+    S.gemm_w4a4_fp6_lora_up_n192(dev(S.pack_fp6_operand(O.pack_int4(parts["qx"]), ACT)), dev(xs),
+                                 dev(S.pack_fp6_operand(abi["w_codes"], ACT)), dev(abi["w_scales"]),
+                                 dev(parts["lora_act"].astype(np.float32)) if rank else None,
+                                 dev_bf16(abi["lora_up"]) if rank else None, dev_bf16(Lr.bias_bits),
+                                 M, N, K, rank, out_dtype=od, out=gy.t)
+    torch.cuda.synchronize()
+    gy.check()
+    _check_out(gy.t, parts["y"], out)
+
+
 # ------------------------------------------------------------ MXFP4 and AWQ
 def test_mxfp4_guarded_equals_plain():
     M, K, N, rank = 301, 512, 264, 32

@@ -380,3 +380,114 @@ def test_linear_forward_qkv(engine):
     _check(to_np_bf16(y), O.forward_qkv(wl.x, po, Lr.bias, qv, kv, cos, sin), "bf16")
     v0 = 2 * heads * 128
     assert torch.equal(y[:, v0:].view(torch.int16), plain[:, v0:].view(torch.int16))
+
+
+# ------------------------------------------------------------------ 256 x 192 tile form
+def run_n192(xf, xs, wr, ws, la, lu, bias, M, N, K, rank, out_dtype=L.SVDQ_OUT_BF16):
+    y = S.gemm_w4a4_fp6_lora_up_n192(xf, xs, wr, ws, la, lu, bias, M, N, K, rank, out_dtype=out_dtype)
+    torch.cuda.synchronize()
+    return y
+
+
+@pytest.mark.parametrize("M,N,K", [(300, 192, 256), (16, 384, 64), (1, 192, 192), (520, 576, 320),
+                                   (4000, 768, 320), (200, 1152, 12288), (257, 3072, 128)])
+def test_n192_int32_group_products_bit_exact(M, N, K):
+    """The 256 x 192 form with unit scales, rank 0, fp32 output: bit for bit
+    the oracle's integer products (-8 extremes included), so the transposed
+    operand roles and the plain row-block weight layout meet every (token,
+    channel) pair exactly once."""
+    rng = np.random.default_rng(M * 11 + N + K)
+    qx = rng.integers(-8, 8, (M, K))
+    qw = rng.integers(-8, 8, (K, N))
+    qx[0, :64] = -8
+    qw[:64, 0] = -8
+    G = K // 64
+    ref = O.w4a4_product(qx, np.ones((M, G)), qw, np.ones((G, N)), 64)
+    y = run_n192(dev(S.pack_fp6_operand(O.pack_int4(qx), ACT)), dev(pad_scales(np.ones((G, M), np.float16), M)),
+                 dev(S.pack_fp6_operand(O.pack_int4(qw.T), ACT)), dev(np.ones((G, N), np.float16)),
+                 None, None, None, M, N, K, 0, L.SVDQ_OUT_F32)
+    np.testing.assert_array_equal(y.double().cpu().numpy(), ref)
+
+
+def test_n192_dequant_scales_exact_fp32():
+    """Power-of-two scales keep every product and sum exact in fp32: the
+    scaled result equals the oracle's exactly, which pins which token scale
+    and which channel scale meet which element in the transposed form."""
+    M, N, K = 96, 384, 256
+    rng = np.random.default_rng(19)
+    G = K // 64
+    qx = rng.integers(-8, 8, (M, K))
+    qw = rng.integers(-8, 8, (K, N))
+    sx = np.exp2(rng.integers(-3, 4, (M, G))).astype(np.float16)
+    sw = np.exp2(rng.integers(-3, 4, (G, N))).astype(np.float16)
+    ref = O.w4a4_product(qx, sx.astype(np.float64), qw, sw.astype(np.float64), 64)
+    y = run_n192(dev(S.pack_fp6_operand(O.pack_int4(qx), ACT)), dev(pad_scales(sx.T, M)),
+                 dev(S.pack_fp6_operand(O.pack_int4(qw.T), ACT)), dev(sw), None, None, None, M, N, K, 0,
+                 L.SVDQ_OUT_F32)
+    np.testing.assert_array_equal(y.double().cpu().numpy(), ref)
+
+
+@pytest.mark.parametrize("M,K,N,rank,bias,out", [
+    (300, 512, 192, 32, False, "bf16"), (300, 512, 384, 32, True, "f32"), (257, 1024, 576, 0, True, "bf16"),
+    (64, 3072, 3072, 32, True, "bf16"), (1, 256, 192, 16, False, "bf16"), (513, 2048, 1152, 128, True, "bf16"),
+    (520, 640, 768, 256, False, "f32"), (4000, 192, 3072, 48, True, "bf16")])
+def test_n192_forward_vs_oracle(M, K, N, rank, bias, out):
+    """Kernel 1 then the 256 x 192 form against the oracle's forward: ranks
+    0 to 256, ragged M, bias, bf16 and fp32 outputs."""
+    wl, Lr, po, abi = _case(M, K, N, rank, seed=M + K + N + 5, bias=bias)
+    xb = f64_to_bf16_bits(wl.x)
+    xf, xs, la = run_k1(xb, abi["smooth_inv"], abi["lora_down"], rank)
+    wr = dev(S.pack_fp6_operand(abi["w_codes"], ACT))
+    od = L.SVDQ_OUT_F32 if out == "f32" else L.SVDQ_OUT_BF16
+    y = run_n192(xf, xs, wr, dev(abi["w_scales"]), la, dev_bf16(abi["lora_up"]) if rank else None,
+                 dev_bf16(Lr.bias_bits) if bias else None, M, N, K, rank, od)
+    yo = O.forward(wl.x, po, bias=Lr.bias if bias else None, out="f32" if out == "f32" else "bf16")
+    _check(y_to_np(y), yo, out)
+
+
+def test_n192_matches_256_form():
+    """Both tile forms add the same exact group products with the same two
+    scales, each group rounded once (the 256 x 256 form scales by s_x first,
+    the 256 x 192 form by s_w first), so their fp32 outputs agree within
+    fp32 summation error."""
+    M, K, N, rank = 512, 1024, 768, 32
+    wl, Lr, po, abi = _case(M, K, N, rank, seed=23, bias=True)
+    xf, xs, la = run_k1(f64_to_bf16_bits(wl.x), abi["smooth_inv"], abi["lora_down"], rank)
+    args = (dev(abi["w_scales"]), la, dev_bf16(abi["lora_up"]), dev_bf16(Lr.bias_bits), M, N, K, rank,
+            L.SVDQ_OUT_F32)
+    y192 = run_n192(xf, xs, dev(S.pack_fp6_operand(abi["w_codes"], ACT)), *args)
+    y256 = run_gemm(xf, xs, dev(S.pack_fp6_operand(abi["w_codes"], WGT)), *args)
+    assert O.rel_fro(y192.double().cpu().numpy(), y256.double().cpu().numpy()) <= 1e-6
+
+
+def test_n192_full_size_attention_out_sampled_rows():
+    """The attention output projection (4096 x 3072 -> 3072, rank 32, bias)
+    through the module, which takes the 256 x 192 form on a 256-CU device
+    (256 tiles against 192 of 256 x 256): sampled rows (first, last, random)
+    against the oracle, repeat runs bitwise equal."""
+    wl = workloads.make_workload("attn_out")
+    Lr = wl.layers[0]
+    M, K, N, r = wl.M, Lr.K, Lr.N, 32
+    rng = np.random.default_rng(17)
+    a = wl.act_absmax()
+    _, lam = O.smoothing_factors(a, Lr.weight)
+    l1 = O.bf16(rng.standard_normal((K, r)) * float(np.abs(lam).mean() * 0.02))
+    l2 = O.bf16(rng.standard_normal((r, N)) / np.sqrt(N))
+    po = O.prepare(Lr.weight, a, rank=r, factors=(l1, l2))
+    abi = oracle_prep_to_abi(po)
+    prep = dict(smooth_inv=abi["smooth_inv"], w_codes=abi["w_codes"], w_scales=abi["w_scales"],
+                lora_down=abi["lora_down"], lora_up=abi["lora_up"], rank=r, group=64, K=K, N=N)
+    bias = torch.from_numpy(Lr.bias_bits.view(np.int16).copy()).view(torch.bfloat16) if Lr.bias_bits is not None \
+        else None
+    lin = S.SVDQW4A4Linear(prep, bias, "cuda")
+    assert lin.w_fp6_rows is not None
+    if torch.cuda.get_device_properties(0).multi_processor_count == 256:
+        assert S.fp6_n192_preferred(M, N) and not S.fp6_n192_preferred(M, 12288)
+    x = dev_bf16(wl.x_bits)
+    y = lin(x)
+    y2 = lin(x)
+    torch.cuda.synchronize()
+    assert torch.equal(y.view(torch.int16), y2.view(torch.int16))
+    rows = np.unique(np.concatenate([np.arange(8), rng.choice(M, 32, replace=False), np.arange(M - 8, M)]))
+    ref = O.forward(wl.x[rows], po, bias=Lr.bias)
+    _check(to_np_bf16(y[torch.from_numpy(rows).cuda()]), ref, "bf16")

@@ -17,7 +17,7 @@ INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(PKG, "libsvdq.so")
 BUILD = os.path.join(ROOT, "_build")
 
-HIP_SOURCES = ["svdq_kernels.hip", "svdq_fp6_kernels.hip", "svdq_mx_kernels.hip", "svdq_awq_kernels.hip", "svdq_probes.hip", "svdq_abi.hip"]
+HIP_SOURCES = ["svdq_kernels.hip", "svdq_fp6_kernels.hip", "svdq_fp6_n192_kernels.hip", "svdq_mx_kernels.hip", "svdq_awq_kernels.hip", "svdq_probes.hip", "svdq_abi.hip"]
 CXX_SOURCES = ["svdq_prepare.cpp", "svdq_fp6_layout.cpp"]
 
 # Packed-fp32 VALU forms are disabled for all device code; hipcc's host pass

@@ -172,6 +172,35 @@ extern "C" int svdq_gemm_w4a4_fp6_lora_up(const void* x_fp6, const void* x_scale
                                     out_dtype, y, stream);
 }
 
+extern "C" int svdq_gemm_w4a4_fp6_lora_up_n192(const void* x_fp6, const void* x_scales, const void* w_fp6,
+                                               const void* w_scales, const float* lora_act, const void* lora_up,
+                                               const void* bias, int M, int N, int K, int rank, int group,
+                                               int out_dtype, void* y, void* stream) {
+  if (M < 0) return SVDQ_ERR_INVALID_ARG;
+  int st = svdq::validate_shape(K, N, rank, group);
+  if (st != SVDQ_OK) return st;
+  if (N % 192 != 0) return SVDQ_ERR_UNSUPPORTED_SHAPE;
+  if (out_dtype != SVDQ_OUT_BF16 && out_dtype != SVDQ_OUT_F32) return SVDQ_ERR_INVALID_ARG;
+  if (!x_fp6 || !x_scales || !w_fp6 || !w_scales || !y) return SVDQ_ERR_INVALID_ARG;
+  if (rank > 0 && (!lora_act || !lora_up)) return SVDQ_ERR_INVALID_ARG;
+  if (!aligned16(x_fp6) || !aligned16(x_scales) || !aligned16(w_fp6) || !aligned16(w_scales) || !aligned16(y) ||
+      (bias && !aligned16(bias)) || (rank > 0 && (!aligned16(lora_act) || !aligned16(lora_up))))
+    return SVDQ_ERR_INVALID_ARG;
+  const int64_t G = K / SVDQ_GROUP;
+  const int64_t RBa = (static_cast<int64_t>(M) + 31) / 32, RBw = N / 32;
+  if (!fits_buffer(G * RBa, 1536) || !fits_buffer(G * RBw, 1536) || !fits_buffer(G, 64LL * RBa) ||
+      !fits_buffer(G, 2LL * N) || !fits_buffer(M, 4LL * rank) ||
+      !fits_buffer(M, static_cast<int64_t>(N) * (out_dtype == SVDQ_OUT_F32 ? 4 : 2)))
+    return SVDQ_ERR_UNSUPPORTED_SHAPE;
+  st = current_device_check();
+  if (st != SVDQ_OK) return st;
+  if (M == 0) return SVDQ_OK;
+  return svdq::launch_gemm_w4a4_fp6_n192(x_fp6, x_scales, w_fp6, w_scales, lora_act, lora_up, bias, M, N, K, rank,
+                                         out_dtype, y, stream);
+}
+
+extern "C" int svdq_fp6_n192_preferred(int M, int N) { return svdq::fp6_n192_preferred(M, N); }
+
 extern "C" int svdq_gemm_w4a4_fp6_lora_up_qkv(const void* x_fp6, const void* x_scales, const void* w_fp6,
                                               const void* w_scales, const float* lora_act, const void* lora_up,
                                               const void* bias, const void* norm_q, const void* norm_k,

@@ -52,6 +52,13 @@ int launch_quant_act_lora_down_fp6(const void* x, const float* smooth_inv, const
 int launch_gemm_w4a4_fp6(const void* x_fp6, const void* x_scales, const void* w_fp6, const void* w_scales,
                          const float* lora_act, const void* lora_up, const void* bias, int M, int N, int K, int rank,
                          int out_dtype, void* y, void* stream);
+// 256 x 192 tiles in the transposed form (svdq_fp6_n192_kernels.hip); w_fp6
+// in the plain fragment layout, N % 192 == 0.
+int launch_gemm_w4a4_fp6_n192(const void* x_fp6, const void* x_scales, const void* w_fp6, const void* w_scales,
+                              const float* lora_act, const void* lora_up, const void* bias, int M, int N, int K,
+                              int rank, int out_dtype, void* y, void* stream);
+// 1 when the 256 x 192 form is expected to be faster for this M and N.
+int fp6_n192_preferred(int M, int N);
 // The same kernel with the fused QKV epilogue (one tile per block).
 int launch_gemm_w4a4_fp6_qkv(const void* x_fp6, const void* x_scales, const void* w_fp6, const void* w_scales,
                              const float* lora_act, const void* lora_up, const void* bias, const void* norm_q,

@@ -57,9 +57,14 @@ class SVDQW4A4Linear:
         self.lora_up = _bits_to_bf16(prepared["lora_up"], dev) if self.rank else None
         self.bias = None if bias is None else bias.detach().to(dev, torch.bfloat16).contiguous()
         self.w_fp6 = None
+        self.w_fp6_rows = None
         if self.engine == "fp6":
             codes = np.asarray(prepared["w_codes"], np.uint8).reshape(self.N, self.K // 2)
             self.w_fp6 = _to_dev(ops.pack_fp6_operand(codes, L.SVDQ_FP6_WEIGHTS), dev)
+            if self.N % 192 == 0:
+                # the plain row-block copy for the 256 x 192 tile form, taken
+                # where it fills the CUs in fewer rounds (svdq_fp6_n192_preferred)
+                self.w_fp6_rows = _to_dev(ops.pack_fp6_operand(codes, L.SVDQ_FP6_ACTIVATIONS), dev)
 
     @classmethod
     def from_linear(cls, linear: torch.nn.Linear, act_absmax, rank: int = 32, group: int = 64,
@@ -80,8 +85,7 @@ class SVDQW4A4Linear:
         M = x.shape[0]
         if self.engine == "fp6":
             xf, xs, la = ops.quant_act_lora_down_fp6(x, self.smooth_inv, self.lora_down, self.rank, self.group, act)
-            return ops.gemm_w4a4_fp6_lora_up(xf, xs, self.w_fp6, self.w_scales, la, self.lora_up, self.bias,
-                                             M, self.N, self.K, self.rank, self.group, out_dtype)
+            return self.kernel2_fp6(xf, xs, la, M, out_dtype)
         if self.precision == "mxfp4":
             xc, xs, la = ops.quant_act_lora_down_mxfp4(x, self.smooth_inv, self.lora_down, self.rank, act)
             return ops.gemm_mxfp4_lora_up(xc, xs, self.w_codes, self.w_scales, la, self.lora_up, self.bias,
@@ -91,6 +95,17 @@ class SVDQW4A4Linear:
                                      M, self.N, self.K, self.rank, self.group, out_dtype)
 
     __call__ = forward
+
+    def kernel2_fp6(self, x_fp6, x_scales, lora_act, M: int, out_dtype: int = L.SVDQ_OUT_BF16,
+                    out: Optional[torch.Tensor] = None):
+        """Kernel 2 of the 6-bit engine on kernel 1's outputs: the 256 x 192
+        tile form where it fills the CUs in fewer rounds, else 256 x 256."""
+        if self.w_fp6_rows is not None and ops.fp6_n192_preferred(M, self.N):
+            return ops.gemm_w4a4_fp6_lora_up_n192(x_fp6, x_scales, self.w_fp6_rows, self.w_scales, lora_act,
+                                                  self.lora_up, self.bias, M, self.N, self.K, self.rank, self.group,
+                                                  out_dtype, out=out)
+        return ops.gemm_w4a4_fp6_lora_up(x_fp6, x_scales, self.w_fp6, self.w_scales, lora_act, self.lora_up,
+                                         self.bias, M, self.N, self.K, self.rank, self.group, out_dtype, out=out)
 
     def forward_qkv(self, x: torch.Tensor, norm_q: torch.Tensor, norm_k: torch.Tensor,
                     rope_cos: Optional[torch.Tensor] = None, rope_sin: Optional[torch.Tensor] = None,
@@ -140,8 +155,7 @@ class SVDQMLPChain:
         xf2, xs2, la2 = ops.gemm_w4a4_fp6_mlp_chain(xf, xs, up.w_fp6, up.w_scales, la, up.lora_up, up.bias,
                                                     M, up.N, up.K, up.rank, dn.smooth_inv, dn.lora_down, dn.rank,
                                                     up.group, workspace=self._ws if need else None)
-        return ops.gemm_w4a4_fp6_lora_up(xf2, xs2, dn.w_fp6, dn.w_scales, la2, dn.lora_up, dn.bias,
-                                         M, dn.N, dn.K, dn.rank, dn.group, out_dtype)
+        return dn.kernel2_fp6(xf2, xs2, la2, M, out_dtype)
 
     __call__ = forward
 

@@ -232,6 +232,36 @@ def gemm_w4a4_fp6_lora_up(x_fp6, x_scales, w_fp6, w_scales, lora_act, lora_up, b
     return out
 
 
+def gemm_w4a4_fp6_lora_up_n192(x_fp6, x_scales, w_fp6_rows, w_scales, lora_act, lora_up, bias,
+                               M: int, N: int, K: int, rank: int, group: int = 64,
+                               out_dtype: int = L.SVDQ_OUT_BF16, out: Optional[torch.Tensor] = None):
+    """Kernel 2 on the 6-bit MFMA in 256 x 192 tiles (weights in the plain
+    fragment layout, N % 192 == 0); returns y [M][N]."""
+    dev = x_fp6.device
+    dt = torch.float32 if out_dtype == L.SVDQ_OUT_F32 else torch.bfloat16
+    if out is None:
+        out = torch.empty((M, N), dtype=dt, device=dev)
+    G = K // group if group > 0 else 0
+    RBa, RBw = (M + 31) // 32, (N + 31) // 32
+    st = L.lib().svdq_gemm_w4a4_fp6_lora_up_n192(
+        _dev_arg("x_fp6", x_fp6, torch.uint8, (G, RBa, 1536), dev),
+        _dev_arg("x_scales", x_scales, torch.float16, (G, 32 * RBa), dev),
+        _dev_arg("w_fp6_rows", w_fp6_rows, torch.uint8, (G, RBw, 1536), dev),
+        _dev_arg("w_scales", w_scales, torch.float16, (G, N), dev),
+        _dev_arg("lora_act", lora_act, torch.float32, (M, rank), dev) if rank else None,
+        _dev_arg("lora_up", lora_up, torch.bfloat16, (N, rank), dev) if rank else None,
+        _dev_arg("bias", bias, torch.bfloat16, (N,), dev),
+        M, N, K, rank, group, out_dtype, _dev_arg("y", out, dt, (M, N), dev), _stream(dev))
+    L.check(st, "svdq_gemm_w4a4_fp6_lora_up_n192")
+    return out
+
+
+def fp6_n192_preferred(M: int, N: int) -> bool:
+    """Whether the 256 x 192 form of the 6-bit kernel 2 is expected to be the
+    faster one for an M x N output on the current device."""
+    return bool(L.lib().svdq_fp6_n192_preferred(int(M), int(N)))
+
+
 def gemm_w4a4_fp6_lora_up_qkv(x_fp6, x_scales, w_fp6, w_scales, lora_act, lora_up, bias, norm_q, norm_k,
                               rope_cos, rope_sin, M: int, N: int, K: int, rank: int, eps: float = 1e-6,
                               group: int = 64, out_dtype: int = L.SVDQ_OUT_BF16,
