@@ -524,9 +524,18 @@ class Runner:
         return res
 
 
-def figures(res, M, N, K, r, bias, engine, workload=None):
+def k2_kernel_name(S, lin, engine, M):
+    """The kernel-2 kernel a step of this layer launches (the 6-bit engine
+    takes the 256 x 192 tile form where the module's dispatch does)."""
+    if engine == "fp6" and getattr(lin, "w_fp6_rows", None) is not None and S.fp6_n192_preferred(M, lin.N):
+        return "k_gemm_w4a4_fp6_n192"
+    return K2_KERNEL[engine]
+
+
+def figures(res, M, N, K, r, bias, engine, workload=None, kname=None):
     """Step rate, kernel-2 roofline (MFMA) and kernel-1 roofline (HBM) of a
     timed step."""
+    kname = kname or K2_KERNEL[engine]
     ops = 2.0 * M * N * K
     precision = "mxfp4" if engine == "mxfp4" else "int4"
     out = {"ms_per_step": round(res["ms"], 5), "value": round(ops / (res["ms"] * 1e-3) / 1e12, 2)}
@@ -534,9 +543,10 @@ def figures(res, M, N, K, r, bias, engine, workload=None):
         k2_rate = ops / (res["k2_ms"] * 1e-3) / 1e12
         k1_gbs = k1_bytes(M, K, r, precision) / (res["k1_ms"] * 1e-3) / 1e9
         peak, unit = (FP4_PEAK_TFLOPS, "TFLOP/s") if engine == "mxfp4" else (INT8_PEAK_TOPS, "TOPS")
-        out["roofline"] = {"bound": "mfma", "kernel": K2_KERNEL[engine], "achieved": round(k2_rate, 2),
+        out["roofline"] = {"bound": "mfma", "kernel": kname, "achieved": round(k2_rate, 2),
                            "peak": peak, "unit": unit, "frac": round(k2_rate / peak, 4),
-                           "traffic": load_traffic(workload, r, engine) if workload else None,
+                           "traffic": load_traffic(workload, r, engine) if workload and kname == K2_KERNEL[engine]
+                           else None,
                            "avg_launch_us": round(res["k2_ms"] * 1e3, 2), "algorithmic_ops_per_launch": ops,
                            "algorithmic_hbm_bytes_per_launch": k2_bytes(M, N, K, r, bias, precision)}
         if engine == "fp6":
@@ -740,8 +750,9 @@ def traffic_summary(engine, workload, rank, pmc_dir, copy_mib):
         return float(np.mean(vals)), len(vals)
 
     # demangled ("k_gemm_mxfp4_lora_up<0, 1, 256>") or mangled names
-    fetch, n = mean_of("fetch", "FETCH_SIZE", lambda k: kname in k)
-    write, _ = mean_of("write", "WRITE_SIZE", lambda k: kname in k)
+    # (the 256 x 192 form's name extends the 6-bit kernel's: not counted here)
+    fetch, n = mean_of("fetch", "FETCH_SIZE", lambda k: kname in k and "_n192" not in k)
+    write, _ = mean_of("write", "WRITE_SIZE", lambda k: kname in k and "_n192" not in k)
     if not n:
         raise SystemExit(f"no {kname} dispatches under {pmc_dir}")
     cdir = pmc_dir if os.path.isdir(os.path.join(pmc_dir, "copy_fetch")) else os.path.dirname(pmc_dir.rstrip("/"))
@@ -861,7 +872,7 @@ def main():
     lin, _ = make_layer(S, Lr.weight_bits, a, r, Lr.bias_bits, args.precision,
                         engine="int8" if engine == "int8" else "fp6")
     res = Runner(S, lin, x, act_id, engine).time(args.steps, args.warmup, cold_iters=COLD_ITERS)
-    main_m = figures(res, M, N, K, r, has_bias, engine, args.workload)
+    main_m = figures(res, M, N, K, r, has_bias, engine, args.workload, k2_kernel_name(S, lin, engine, M))
     value = main_m["value"]
     out = {
         "metric": METRIC,
@@ -916,7 +927,7 @@ def main():
             clin, _ = make_layer(S, cL.weight_bits, ca, r, cL.bias_bits)
             cres = Runner(S, clin, cx, cact_id, "fp6").time(args.steps, args.warmup)
             cM, cK, cN = cx.shape[0], cL.K, cL.N
-            f = figures(cres, cM, cN, cK, r, cL.bias_bits is not None, "fp6", name)
+            f = figures(cres, cM, cN, cK, r, cL.bias_bits is not None, "fp6", name, k2_kernel_name(S, clin, "fp6", cM))
             entry = {"workload": cdesc + f", rank {r}, 6-bit engine", "M": cM, "K": cK, "N": cN,
                      "ms_per_step": f["ms_per_step"], "value": f["value"], "unit": "TOPS",
                      "pct_int8_peak": round(100.0 * f["value"] / INT8_PEAK_TOPS, 2),
