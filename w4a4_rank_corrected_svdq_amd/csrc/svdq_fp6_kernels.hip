@@ -482,6 +482,20 @@ __global__ __launch_bounds__(F_THREADS, 1) void k_gemm_w4a4_fp6(
     issue();
     convert_scales(sc, (s + 1) & 1);
   };
+  // The same in two parts, so that a group stage reads its first
+  // fragments between them: their LDS latency then overlaps the DMA issue and
+  // the scale conversion (the DMA's inline assembly keeps every LDS access in
+  // program order around it).
+  auto stage_wait = [&]() {
+    if (since_end < F_NS - 1) __builtin_amdgcn_s_waitcnt(waitcnt_vm(F_DMA * (F_NS - 2) + F_STORES));
+    else __builtin_amdgcn_s_waitcnt(waitcnt_vm(F_DMA * (F_NS - 2)));
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
+  };
+  auto stage_issue = [&]() {
+    issue();
+    convert_scales(sc, (s + 1) & 1);
+  };
   auto stage_end = [&]() {
     ++s;
     sc = sc == F_NS - 1 ? 0 : sc + 1;
@@ -719,7 +733,9 @@ __global__ __launch_bounds__(F_THREADS, 1) void k_gemm_w4a4_fp6(
 
     // ---- the tile's groups: P_g on the 6-bit MFMA, then dequantization ----
     for (int l = 0; l < GS; ++l, stage_end()) {
-      stage_top();
+      // (the chain's epilogue leaves no registers for the early reads)
+      if constexpr (EPI == 1) stage_top();
+      else stage_wait();
       // The stage's 16 tiles (two groups x 8) in one sequence u = 0..15:
       // group u / 8, then (n tile 0, m tile 0), (0, 1), (1, 0), ...  A
       // weight fragment serves two consecutive tiles and is read one tile
@@ -743,6 +759,7 @@ __global__ __launch_bounds__(F_THREADS, 1) void k_gemm_w4a4_fp6(
       afr[1] = rd_frag(a_off + FRAG);
       v8i bfr[4];
       bfr[0] = rd_frag(b_off);
+      if constexpr (EPI != 1) stage_issue();
       v16f dr[2];
       float swv[4];
 #pragma unroll

@@ -296,6 +296,20 @@ __global__ __launch_bounds__(T_THREADS, 1) void k_gemm_w4a4_fp6_n192(
     issue();
     convert_scales(sc, (s + 1) & 1);
   };
+  // The same in two parts, so that a group stage reads its first
+  // fragments between them: their LDS latency then overlaps the DMA issue and
+  // the scale conversion (the DMA's inline assembly keeps every LDS access in
+  // program order around it).
+  auto stage_wait = [&]() {
+    if (since_end < T_NS - 1) __builtin_amdgcn_s_waitcnt(waitcnt_vm(T_DMA * (T_NS - 2) + T_STORES));
+    else __builtin_amdgcn_s_waitcnt(waitcnt_vm(T_DMA * (T_NS - 2)));
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
+  };
+  auto stage_issue = [&]() {
+    issue();
+    convert_scales(sc, (s + 1) & 1);
+  };
   auto stage_end = [&]() {
     ++s;
     sc = sc == T_NS - 1 ? 0 : sc + 1;
@@ -308,7 +322,7 @@ __global__ __launch_bounds__(T_THREADS, 1) void k_gemm_w4a4_fp6_n192(
 
     // ---- the tile's groups ----
     for (int l = 0; l < GS; ++l, stage_end()) {
-      stage_top();
+      stage_wait();
       // The stage's 12 tiles (two groups x 6) in one sequence u: group u / 6,
       // then (channel tile 0, token tile 0), (0, 1), (1, 0), ...  A weight
       // fragment serves two consecutive tiles and is read one tile pair
@@ -328,6 +342,7 @@ __global__ __launch_bounds__(T_THREADS, 1) void k_gemm_w4a4_fp6_n192(
       xfr[1] = rd_frag(x_off + FRAG);
       v8i wfr[3];
       wfr[0] = rd_frag(w_off);
+      stage_issue();
       v16f dr[2];
       float swv[4][4];
       float sxv[2];
