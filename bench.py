@@ -58,6 +58,35 @@ def settle(step, seconds=SETTLE_S):
         if time.perf_counter() - t0 >= seconds:
             return
 
+def graph_time(fn, n: int) -> float:
+    """Average GPU time in ms of one fn() over n back-to-back calls: the n
+    calls are captured once into a HIP graph (the library launches on the
+    current stream, which is the capture stream there) and the graph is
+    replayed between two HIP events.  For kernels shorter than the host's
+    time to enqueue one (the AWQ GEMV, ~11 µs): events around each eager
+    launch would time the GPU waiting for the host."""
+    import torch
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        fn()
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        for _ in range(n):
+            fn()
+    g.replay()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    g.replay()
+    e1.record()
+    torch.cuda.synchronize()
+    del g
+    return e0.elapsed_time(e1) / n
+
+
 # name -> (generator workload, layer index, act, description)
 BENCH_WORKLOADS = {
     "mlp_up": ("mlp_pair", 0, "none", "FLUX MLP up-projection 4096x3072x12288"),
@@ -289,24 +318,18 @@ def bench_awq(S, workloads, steps, warmup, M=1):
     xh = torch.empty((M, K), dtype=torch.bfloat16, device="cuda")
     xs = torch.empty((G, 16), dtype=torch.float32, device="cuda")
     y = torch.empty((M, N), dtype=torch.bfloat16, device="cuda")
-    st = torch.cuda.current_stream()
 
-    def two_launch(ev=None):
-        S.awq_quant_act(x, lin.inv_scale, out=(xh, xs))
-        if ev is not None:
-            ev[0].record(st)
+    def gemv():
         S.awq_gemv(xh, xs, lin.w_codes, lin.w_scales, lin.w_zeros, lin.bias, M, N, K, out=y)
-        if ev is not None:
-            ev[1].record(st)
 
-    def one_launch(ev=None):
-        if ev is not None:
-            ev[0].record(st)
+    def two_launch():
+        S.awq_quant_act(x, lin.inv_scale, out=(xh, xs))
+        gemv()
+
+    def one_launch():
         S.awq_linear_row(x, lin.inv_scale, lin.w_codes, lin.w_scales, lin.w_zeros, lin.bias, N, K, out=y)
-        if ev is not None:
-            ev[1].record(st)
 
-    def timed(step):
+    def timed(step, kernel):
         settle(step)
         for _ in range(warmup):
             step()
@@ -316,18 +339,15 @@ def bench_awq(S, workloads, steps, warmup, M=1):
             step()
         torch.cuda.synchronize()
         ms = (time.perf_counter() - t0) * 1e3 / steps
-        # kernel time from a second, event-instrumented pass
-        evs = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(steps)]
-        for i in range(steps):
-            step(evs[i])
-        torch.cuda.synchronize()
-        return ms, float(np.mean([e[0].elapsed_time(e[1]) for e in evs]))
+        # the kernel's average launch time: `steps` back-to-back launches
+        # from a HIP graph between two events on its stream
+        return ms, graph_time(kernel, steps)
 
     weights = N * K // 2 + 2 * N * G + N * G + 2 * N
     fused = M == 1
-    ms2, gemv_ms = timed(two_launch)
+    ms2, gemv_ms = timed(two_launch, gemv)
     if fused:
-        ms, k_ms = timed(one_launch)
+        ms, k_ms = timed(one_launch, one_launch)
         nbytes = weights + 2 * K + 4 * K + 2 * N            # x and inv_scale in, y out
         kernel = "k_awq_gemv_row1 (activation scaling fused)"
     else:
@@ -456,6 +476,26 @@ class Runner:
             self.xc = torch.empty((M, K // 2), dtype=torch.uint8, device=dev)
             self.xs = torch.empty((K // 64, M), dtype=torch.float16, device=dev)
 
+    def k1(self):
+        S, lin, x, r = self.S, self.lin, self.x, self.lin.rank
+        if self.engine == "fp6":
+            S.quant_act_lora_down_fp6(x, lin.smooth_inv, lin.lora_down, r, act=self.act, out=(self.xc, self.xs, self.la))
+        elif self.engine == "mxfp4":
+            S.quant_act_lora_down_mxfp4(x, lin.smooth_inv, lin.lora_down, r, act=self.act, out=(self.xc, self.xs, self.la))
+        else:
+            S.quant_act_lora_down(x, lin.smooth_inv, lin.lora_down, r, act=self.act, out=(self.xc, self.xs, self.la))
+
+    def k2(self):
+        S, lin, M, N, K, r = self.S, self.lin, self.M, self.N, self.K, self.lin.rank
+        if self.engine == "fp6":
+            lin.kernel2_fp6(self.xc, self.xs, self.la, M, out=self.y)
+        elif self.engine == "mxfp4":
+            S.gemm_mxfp4_lora_up(self.xc, self.xs, lin.w_codes, lin.w_scales, self.la, lin.lora_up, lin.bias,
+                                 M, N, K, r, out=self.y)
+        else:
+            S.gemm_w4a4_lora_up(self.xc, self.xs, lin.w_codes, lin.w_scales, self.la, lin.lora_up, lin.bias,
+                                M, N, K, r, out=self.y)
+
     def step(self, mid=None):
         S, lin, x, M, N, K, r = self.S, self.lin, self.x, self.M, self.N, self.K, self.lin.rank
         if self.engine == "unfused":
@@ -465,29 +505,20 @@ class Runner:
             S.lora_down(x, lin.smooth_inv, lin.lora_down, r, act=self.act, out=self.la)
             S.lora_up_add(self.la, lin.lora_up, self.y)
             return
-        if self.engine == "fp6":
-            S.quant_act_lora_down_fp6(x, lin.smooth_inv, lin.lora_down, r, act=self.act, out=(self.xc, self.xs, self.la))
-            if mid is not None:
-                mid.record()
-            lin.kernel2_fp6(self.xc, self.xs, self.la, M, out=self.y)
-        elif self.engine == "mxfp4":
-            S.quant_act_lora_down_mxfp4(x, lin.smooth_inv, lin.lora_down, r, act=self.act, out=(self.xc, self.xs, self.la))
-            if mid is not None:
-                mid.record()
-            S.gemm_mxfp4_lora_up(self.xc, self.xs, lin.w_codes, lin.w_scales, self.la, lin.lora_up, lin.bias,
-                                 M, N, K, r, out=self.y)
-        else:
-            S.quant_act_lora_down(x, lin.smooth_inv, lin.lora_down, r, act=self.act, out=(self.xc, self.xs, self.la))
-            if mid is not None:
-                mid.record()
-            S.gemm_w4a4_lora_up(self.xc, self.xs, lin.w_codes, lin.w_scales, self.la, lin.lora_up, lin.bias,
-                                M, N, K, r, out=self.y)
+        self.k1()
+        if mid is not None:
+            mid.record()
+        self.k2()
 
     def time(self, steps, warmup, events=True, cold_iters=0):
         """Wall time of `steps` back-to-back steps after the settle phase and
         `warmup` steps; then (events) a second pass of the same length with
-        HIP events around each kernel for the breakdown, and (cold_iters)
-        single steps each after evicting the Infinity Cache."""
+        HIP events before kernel 1, between the kernels and after kernel 2 of
+        every step, for the kernels' average launch times (the GPU runs about
+        a step behind the host there, so no host gap enters them; each event
+        keeps the kernel after it from overlapping the one before, as a
+        profiler's kernel trace does); then (cold_iters) single steps each
+        after evicting the Infinity Cache."""
         import torch
         settle(self.step)
         for _ in range(warmup):
@@ -548,7 +579,8 @@ def figures(res, M, N, K, r, bias, engine, workload=None, kname=None):
                            "traffic": load_traffic(workload, r, engine) if workload and kname == K2_KERNEL[engine]
                            else None,
                            "avg_launch_us": round(res["k2_ms"] * 1e3, 2), "algorithmic_ops_per_launch": ops,
-                           "algorithmic_hbm_bytes_per_launch": k2_bytes(M, N, K, r, bias, precision)}
+                           "algorithmic_hbm_bytes_per_launch": k2_bytes(M, N, K, r, bias, precision),
+                           "how": "mean over the timed steps of the HIP-event interval around kernel 2"}
         if engine == "fp6":
             # the INT4 contraction runs on the 6-bit float MFMA: its own
             # instruction peak beside the INT8 peak the metric is quoted on
@@ -557,7 +589,8 @@ def figures(res, M, N, K, r, bias, engine, workload=None, kname=None):
         k1 = {"bound": "hbm", "kernel": "k_quant_act_lora_down" + (" (6-bit container output)" if engine == "fp6" else ""),
               "achieved": round(k1_gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
               "frac": round(k1_gbs / HBM_PEAK_GBS, 4), "avg_launch_us": round(res["k1_ms"] * 1e3, 2),
-              "algorithmic_bytes_per_launch": k1_bytes(M, K, r, precision)}
+              "algorithmic_bytes_per_launch": k1_bytes(M, K, r, precision),
+              "how": "mean over the timed steps of the HIP-event interval around kernel 1"}
         if engine == "fp6":
             cb = fp6_container_bytes(M, N, K)
             k1["container_bytes_per_launch"] = (k1_bytes(M, K, r) - M * K // 2 - scale_bytes(K, "int4") * M

@@ -58,6 +58,7 @@ class SVDQW4A4Linear:
         self.bias = None if bias is None else bias.detach().to(dev, torch.bfloat16).contiguous()
         self.w_fp6 = None
         self.w_fp6_rows = None
+        self._n192_choice = {}
         if self.engine == "fp6":
             codes = np.asarray(prepared["w_codes"], np.uint8).reshape(self.N, self.K // 2)
             self.w_fp6 = _to_dev(ops.pack_fp6_operand(codes, L.SVDQ_FP6_WEIGHTS), dev)
@@ -96,11 +97,18 @@ class SVDQW4A4Linear:
 
     __call__ = forward
 
+    def _n192(self, M: int) -> bool:
+        # the tile-form choice per row count, asked of the library once
+        hit = self._n192_choice.get(M)
+        if hit is None:
+            hit = self._n192_choice[M] = ops.fp6_n192_preferred(M, self.N)
+        return hit
+
     def kernel2_fp6(self, x_fp6, x_scales, lora_act, M: int, out_dtype: int = L.SVDQ_OUT_BF16,
                     out: Optional[torch.Tensor] = None):
         """Kernel 2 of the 6-bit engine on kernel 1's outputs: the 256 x 192
         tile form where it fills the CUs in fewer rounds, else 256 x 256."""
-        if self.w_fp6_rows is not None and ops.fp6_n192_preferred(M, self.N):
+        if self.w_fp6_rows is not None and self._n192(M):
             return ops.gemm_w4a4_fp6_lora_up_n192(x_fp6, x_scales, self.w_fp6_rows, self.w_scales, lora_act,
                                                   self.lora_up, self.bias, M, self.N, self.K, self.rank, self.group,
                                                   out_dtype, out=out)
