@@ -491,3 +491,21 @@ def test_n192_full_size_attention_out_sampled_rows():
     rows = np.unique(np.concatenate([np.arange(8), rng.choice(M, 32, replace=False), np.arange(M - 8, M)]))
     ref = O.forward(wl.x[rows], po, bias=Lr.bias)
     _check(to_np_bf16(y[torch.from_numpy(rows).cuda()]), ref, "bf16")
+
+
+def test_n192_copy_optional():
+    """n192=False keeps no plain-layout copy and runs the 256 x 256 form:
+    the same output as with the copy within fp32 summation order (both forms
+    against each other at bf16: within one ulp)."""
+    M, K, N, rank = 300, 512, 384, 32
+    wl = workloads.custom_workload(M, K, N, seed=91, n_out=4, bias=True)
+    Lr = wl.layers[0]
+    p = S.prepare_weights(Lr.weight_bits, wl.act_absmax(), rank=rank)
+    bias = torch.from_numpy(Lr.bias_bits.view(np.int16).copy()).view(torch.bfloat16)
+    a = S.SVDQW4A4Linear(p, bias, "cuda")
+    b = S.SVDQW4A4Linear(p, bias, "cuda", n192=False)
+    assert a.w_fp6_rows is not None and b.w_fp6_rows is None
+    x = dev_bf16(wl.x_bits)
+    ya, yb = a(x), b(x)
+    torch.cuda.synchronize()
+    check_bf16_elementwise(to_np_bf16(ya), to_np_bf16(yb), frac=0.0)

@@ -37,9 +37,13 @@ class SVDQW4A4Linear:
     nibble layout (``svdq_quant_act_lora_down`` +
     ``svdq_gemm_w4a4_lora_up``).  Both compute the same layer; the nibble
     codes stay resident for the int8 engine, the unfused comparison path and
-    the fused QKV epilogue."""
+    the fused QKV epilogue.  With N % 192 == 0 the 6-bit engine also keeps
+    the weights in the plain row-block layout for its 256 x 192 tile form
+    (``svdq_gemm_w4a4_fp6_lora_up_n192``), used per call where
+    ``svdq_fp6_n192_preferred`` says so; ``n192=False`` drops that copy."""
 
-    def __init__(self, prepared: dict, bias: Optional[torch.Tensor], device, engine: str = "fp6"):
+    def __init__(self, prepared: dict, bias: Optional[torch.Tensor], device, engine: str = "fp6",
+                 n192: bool = True):
         dev = torch.device(device)
         self.precision = prepared.get("precision", "int4")
         if self.precision not in ("int4", "mxfp4"):
@@ -62,14 +66,17 @@ class SVDQW4A4Linear:
         if self.engine == "fp6":
             codes = np.asarray(prepared["w_codes"], np.uint8).reshape(self.N, self.K // 2)
             self.w_fp6 = _to_dev(ops.pack_fp6_operand(codes, L.SVDQ_FP6_WEIGHTS), dev)
-            if self.N % 192 == 0:
+            if n192 and self.N % 192 == 0:
                 # the plain row-block copy for the 256 x 192 tile form, taken
-                # where it fills the CUs in fewer rounds (svdq_fp6_n192_preferred)
+                # where it fills the CUs in fewer rounds (svdq_fp6_n192_preferred);
+                # a second 6-bit weight copy (0.75 K N bytes): n192=False
+                # leaves it out and always runs the 256 x 256 form
                 self.w_fp6_rows = _to_dev(ops.pack_fp6_operand(codes, L.SVDQ_FP6_ACTIVATIONS), dev)
 
     @classmethod
     def from_linear(cls, linear: torch.nn.Linear, act_absmax, rank: int = 32, group: int = 64,
-                    alpha: float = 0.5, device="cuda", precision: str = "int4", engine: str = "fp6"):
+                    alpha: float = 0.5, device="cuda", precision: str = "int4", engine: str = "fp6",
+                    n192: bool = True):
         """Quantize a ``torch.nn.Linear`` (weight [out][in], bf16) given the
         calibration statistic ``act_absmax`` [in] (max |x| per input channel)."""
         w = linear.weight.detach().to(torch.bfloat16).cpu()
@@ -80,7 +87,7 @@ class SVDQW4A4Linear:
             prep = ops.prepare_weights(w, a, rank, group, alpha)
         else:
             raise ValueError(f"unknown precision {precision!r}")
-        return cls(prep, linear.bias, device, engine)
+        return cls(prep, linear.bias, device, engine, n192)
 
     def forward(self, x: torch.Tensor, act: int = L.SVDQ_ACT_NONE, out_dtype: int = L.SVDQ_OUT_BF16):
         M = x.shape[0]
