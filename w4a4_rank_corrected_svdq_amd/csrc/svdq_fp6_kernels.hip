@@ -172,8 +172,10 @@ struct ChainArgs {
 };
 constexpr int C_TS = 2 * F_BN + 16;                   // staging row stride in bytes (bank spread)
 
-// The fused QKV epilogue (EPI = 2; "Nunchaku Engine Design": normalization
-// and rotary embedding fused into the QKV projection).  The output columns
+// The fused QKV epilogue (EPI = 2; "Bringing Nunchaku 4-bit Diffusion
+// Inference to Diffusers", "Quantizing models with structural rewrites": one
+// operator takes the QKV projection, the Q / K normalization and the rotary
+// embedding together).  The output columns
 // are Q heads, then K heads, then V heads of 128 columns (N = 3 heads 128);
 // a wave's 128 columns are one head.  After bias, each Q or K row is scaled
 // by 1 / sqrt(mean of its 128 squares + eps) and the head's bf16 norm
