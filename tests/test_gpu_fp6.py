@@ -509,3 +509,34 @@ def test_n192_copy_optional():
     ya, yb = a(x), b(x)
     torch.cuda.synchronize()
     check_bf16_elementwise(to_np_bf16(ya), to_np_bf16(yb), frac=0.0)
+
+
+def test_empty_batch_launches_nothing():
+    """M = 0 (an empty batch) through every kernel entry point of the INT4
+    layer: status OK and no byte of the (canary-filled) outputs written."""
+    K, N, r = 128, 384, 16
+    dev_u8 = lambda n: torch.full((n,), 0xA5, dtype=torch.uint8, device="cuda")  # noqa: E731
+    b = [dev_u8(1 << 16) for _ in range(12)]
+    p = [t.data_ptr() for t in b]
+    st = torch.cuda.current_stream().cuda_stream
+    lib = L.lib()
+    calls = {
+        "quant_act_lora_down": lib.svdq_quant_act_lora_down(p[0], p[1], p[2], 0, K, r, 64, 0, p[3], p[4], p[5], st),
+        "quant_act_lora_down_fp6": lib.svdq_quant_act_lora_down_fp6(p[0], p[1], p[2], 0, K, r, 64, 0, p[3], p[4],
+                                                                    p[5], st),
+        "gemm_w4a4_lora_up": lib.svdq_gemm_w4a4_lora_up(p[0], p[1], p[2], p[3], p[4], p[5], None, 0, N, K, r, 64, 0,
+                                                        p[6], st),
+        "gemm_w4a4_fp6_lora_up": lib.svdq_gemm_w4a4_fp6_lora_up(p[0], p[1], p[2], p[3], p[4], p[5], None, 0, N, K, r,
+                                                                64, 0, p[6], st),
+        "gemm_w4a4_fp6_lora_up_n192": lib.svdq_gemm_w4a4_fp6_lora_up_n192(p[0], p[1], p[2], p[3], p[4], p[5], None, 0,
+                                                                          N, K, r, 64, 0, p[6], st),
+        "gemm_w4a4_lora_up_qkv": lib.svdq_gemm_w4a4_lora_up_qkv(p[0], p[1], p[2], p[3], p[4], p[5], None, p[7], p[8],
+                                                                None, None, 1e-6, 0, N, K, r, 64, 0, p[6], st),
+        "gemm_w4a4_fp6_lora_up_qkv": lib.svdq_gemm_w4a4_fp6_lora_up_qkv(p[0], p[1], p[2], p[3], p[4], p[5], None,
+                                                                        p[7], p[8], p[9], p[10], 1e-6, 0, N, K, r, 64,
+                                                                        0, p[6], st),
+    }
+    torch.cuda.synchronize()
+    assert all(v == 0 for v in calls.values()), calls
+    for t in b:
+        assert bool((t == 0xA5).all())
