@@ -456,8 +456,11 @@ class Runner:
 
     def __init__(self, S, lin, x, act_id, engine):
         import torch
-        self.S, self.lin, self.x, self.act, self.engine = S, lin, x, act_id, engine
+        self.S, self.lin, self.x, self.act = S, lin, x, act_id
         M, K = x.shape
+        # a 6-bit layer's step runs the kernels its forward() would (the
+        # int8 engine's for few rows: SVDQW4A4Linear.route)
+        self.engine = engine = lin.route(M) if engine == "fp6" else engine
         N, r = lin.N, lin.rank
         self.M, self.N, self.K = M, N, K
         dev = "cuda"
@@ -557,7 +560,10 @@ class Runner:
 
 def k2_kernel_name(S, lin, engine, M):
     """The kernel-2 kernel a step of this layer launches (the 6-bit engine
-    takes the 256 x 192 tile form where the module's dispatch does)."""
+    takes the 256 x 192 tile form, or the int8 engine's kernels for few
+    rows, where the module's dispatch does)."""
+    if engine == "fp6" and lin.route(M) == "int8":
+        return K2_KERNEL["int8"]
     if engine == "fp6" and getattr(lin, "w_fp6_rows", None) is not None and S.fp6_n192_preferred(M, lin.N):
         return "k_gemm_w4a4_fp6_n192"
     return K2_KERNEL[engine]
@@ -904,8 +910,9 @@ def main():
     has_bias = Lr.bias_bits is not None
     lin, _ = make_layer(S, Lr.weight_bits, a, r, Lr.bias_bits, args.precision,
                         engine="int8" if engine == "int8" else "fp6")
-    res = Runner(S, lin, x, act_id, engine).time(args.steps, args.warmup, cold_iters=COLD_ITERS)
-    main_m = figures(res, M, N, K, r, has_bias, engine, args.workload, k2_kernel_name(S, lin, engine, M))
+    run = Runner(S, lin, x, act_id, engine)
+    res = run.time(args.steps, args.warmup, cold_iters=COLD_ITERS)
+    main_m = figures(res, M, N, K, r, has_bias, run.engine, args.workload, k2_kernel_name(S, lin, engine, M))
     value = main_m["value"]
     out = {
         "metric": METRIC,
@@ -958,10 +965,13 @@ def main():
             cact_id = L.SVDQ_ACT_GELU_TANH if cact == "gelu_tanh" else L.SVDQ_ACT_NONE
             cx, ca = layer_input(S, cw, li, cact, r)
             clin, _ = make_layer(S, cL.weight_bits, ca, r, cL.bias_bits)
-            cres = Runner(S, clin, cx, cact_id, "fp6").time(args.steps, args.warmup)
+            crun = Runner(S, clin, cx, cact_id, "fp6")
+            cres = crun.time(args.steps, args.warmup)
             cM, cK, cN = cx.shape[0], cL.K, cL.N
-            f = figures(cres, cM, cN, cK, r, cL.bias_bits is not None, "fp6", name, k2_kernel_name(S, clin, "fp6", cM))
-            entry = {"workload": cdesc + f", rank {r}, 6-bit engine", "M": cM, "K": cK, "N": cN,
+            f = figures(cres, cM, cN, cK, r, cL.bias_bits is not None, crun.engine, name,
+                        k2_kernel_name(S, clin, "fp6", cM))
+            routed = " (few rows: the int8 engine's kernels)" if crun.engine == "int8" else ""
+            entry = {"workload": cdesc + f", rank {r}, 6-bit engine{routed}", "M": cM, "K": cK, "N": cN,
                      "ms_per_step": f["ms_per_step"], "value": f["value"], "unit": "TOPS",
                      "pct_int8_peak": round(100.0 * f["value"] / INT8_PEAK_TOPS, 2),
                      "k1_us": f["roofline_k1"]["avg_launch_us"], "k2_us": f["roofline"]["avg_launch_us"],

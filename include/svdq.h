@@ -328,6 +328,15 @@ int svdq_gemm_w4a4_fp6_lora_up_n192(const void* x_fp6, const void* x_scales,
  * 256 x 192 tile as 0.875 of a 256 x 256 one), else 0. */
 int svdq_fp6_n192_preferred(int M, int N);
 
+/* Host.  The kernels expected to be fastest for an INT4 layer's M x N output
+ * on the current device: 0 = svdq_quant_act_lora_down_fp6 +
+ * svdq_gemm_w4a4_fp6_lora_up (256 x 256 tiles), 1 = the same kernel 1 +
+ * svdq_gemm_w4a4_fp6_lora_up_n192, 2 = the int8 engine
+ * (svdq_quant_act_lora_down + svdq_gemm_w4a4_lora_up, whose 128 x 128 form
+ * keeps more CUs busy when 256 x 256 tiles would cover fewer than half of
+ * them).  All three compute the same layer. */
+int svdq_int4_route(int M, int N);
+
 /* Device, asynchronous.  The fused QKV operator of svdq_gemm_w4a4_lora_up_qkv
  * (the same per-head RMSNorm of the Q and K heads and rotary embedding of
  * their adjacent pairs, the same argument meanings) on the 6-bit MFMA: the

@@ -36,6 +36,7 @@ int launch_gemm_w4a4_fp6(const void*, const void*, const void*, const void*, con
 int launch_gemm_w4a4_fp6_n192(const void*, const void*, const void*, const void*, const float*, const void*,
                               const void*, int, int, int, int, int, void*, void*) { ++g_launches; return kReached; }
 int fp6_n192_preferred(int, int) { return 0; }
+int fp6_route(int, int) { return 0; }
 int launch_gemm_w4a4_fp6_qkv(const void*, const void*, const void*, const void*, const float*, const void*,
                              const void*, const void*, const void*, const float*, const float*, float, int, int, int,
                              int, int, void*, void*) { ++g_launches; return kReached; }

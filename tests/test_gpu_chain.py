@@ -169,17 +169,21 @@ def test_chain_matches_two_layer_path_and_oracle(M, K, N, N2, r_up, r_dn):
 
 
 def test_chain_module_and_repeat_runs():
-    """SVDQMLPChain (library-prepared layers) against the two-layer modules,
-    and two calls bit-identical (fixed reduction order)."""
+    """SVDQMLPChain (library-prepared layers) against the two-layer modules
+    on the 6-bit kernels (auto_route off: at this M their forward would take
+    the int8 engine's kernels), and two calls bit-identical (fixed reduction
+    order)."""
     M, K, N, N2 = 200, 256, 512, 256
     wl = workloads.custom_workload(M, K, N, seed=77, n_out=4, bias=True, second_N=N2)
     up, dn = wl.layers
     bf = lambda b: torch.from_numpy(b.view(np.int16).copy()).view(torch.bfloat16)  # noqa: E731
-    lu = S.SVDQW4A4Linear(S.prepare_weights(up.weight_bits, wl.act_absmax(), rank=32), bf(up.bias_bits), "cuda")
+    lu = S.SVDQW4A4Linear(S.prepare_weights(up.weight_bits, wl.act_absmax(), rank=32), bf(up.bias_bits), "cuda",
+                          auto_route=False)
     x = dev_bf16(wl.x_bits)
     y_up = lu(x)
     a_dn = torch.nn.functional.gelu(y_up.float(), approximate="tanh").abs().amax(0).cpu().numpy()
-    ld = S.SVDQW4A4Linear(S.prepare_weights(dn.weight_bits, a_dn, rank=32), bf(dn.bias_bits), "cuda")
+    ld = S.SVDQW4A4Linear(S.prepare_weights(dn.weight_bits, a_dn, rank=32), bf(dn.bias_bits), "cuda",
+                          auto_route=False)
     two = ld(y_up, act=L.SVDQ_ACT_GELU_TANH)
     chain = S.SVDQMLPChain(lu, ld)
     y1, y2 = chain(x), chain(x)

@@ -370,8 +370,10 @@ def test_linear_forward_qkv(engine):
     Lr = wl.layers[0]
     p = S.prepare_weights(Lr.weight_bits, wl.act_absmax(), rank=r)
     po = abi_to_oracle_prep(p)
+    # auto_route off: the plain forward stays on the engine's own kernels, so
+    # its V columns are the fused kernel's bit for bit
     lin = S.SVDQW4A4Linear(p, torch.from_numpy(Lr.bias_bits.view(np.int16).copy()).view(torch.bfloat16), "cuda",
-                           engine=engine)
+                           engine=engine, auto_route=False)
     qb, qv, kb, kv, cos, sin = _qkv_tables(M, 84, True)
     x = dev_bf16(wl.x_bits)
     y = lin.forward_qkv(x, dev_bf16(qb), dev_bf16(kb), dev(cos), dev(sin))
@@ -502,8 +504,8 @@ def test_n192_copy_optional():
     Lr = wl.layers[0]
     p = S.prepare_weights(Lr.weight_bits, wl.act_absmax(), rank=rank)
     bias = torch.from_numpy(Lr.bias_bits.view(np.int16).copy()).view(torch.bfloat16)
-    a = S.SVDQW4A4Linear(p, bias, "cuda")
-    b = S.SVDQW4A4Linear(p, bias, "cuda", n192=False)
+    a = S.SVDQW4A4Linear(p, bias, "cuda", auto_route=False)
+    b = S.SVDQW4A4Linear(p, bias, "cuda", n192=False, auto_route=False)
     assert a.w_fp6_rows is not None and b.w_fp6_rows is None
     x = dev_bf16(wl.x_bits)
     ya, yb = a(x), b(x)
@@ -540,3 +542,27 @@ def test_empty_batch_launches_nothing():
     assert all(v == 0 for v in calls.values()), calls
     for t in b:
         assert bool((t == 0xA5).all())
+
+
+@pytest.mark.parametrize("M,K,N", [(256, 512, 512), (1024, 3072, 3072), (4096, 256, 3072), (2048, 256, 12288)])
+def test_int4_route(M, K, N):
+    """A 6-bit layer's forward() runs the int8 engine's kernels where 256-row
+    tiles would cover fewer than half the CUs (svdq_int4_route == 2) and the
+    6-bit kernels otherwise; either way the output matches the oracle, and
+    with auto_route off it matches the 6-bit kernels' own output within one
+    bf16 ulp (fp32 sums in another order)."""
+    wl = workloads.custom_workload(M, K, N, seed=97, n_out=4, bias=True)
+    Lr = wl.layers[0]
+    p = S.prepare_weights(Lr.weight_bits, wl.act_absmax(), rank=32)
+    bias = torch.from_numpy(Lr.bias_bits.view(np.int16).copy()).view(torch.bfloat16)
+    lin = S.SVDQW4A4Linear(p, bias, "cuda")
+    fixed = S.SVDQW4A4Linear(p, bias, "cuda", auto_route=False)
+    cus = torch.cuda.get_device_properties(0).multi_processor_count
+    small = 2 * ((M + 255) // 256) * ((N + 255) // 256) < cus
+    assert (S.int4_route(M, N) == 2) == small
+    assert lin.route(M) == ("int8" if small else "fp6") and fixed.route(M) == "fp6"
+    x = dev_bf16(wl.x_bits)
+    y, y6 = lin(x), fixed(x)
+    torch.cuda.synchronize()
+    _check(to_np_bf16(y), O.forward(wl.x, abi_to_oracle_prep(p), bias=Lr.bias), "bf16")
+    check_bf16_elementwise(to_np_bf16(y), to_np_bf16(y6), frac=1e-4)

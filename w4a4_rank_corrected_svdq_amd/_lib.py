@@ -63,6 +63,7 @@ SIGNATURES = {
     "svdq_gemm_w4a4_fp6_lora_up": (_i, [_p, _p, _p, _p, _p, _p, _p, _i, _i, _i, _i, _i, _i, _p, _p]),
     "svdq_gemm_w4a4_fp6_lora_up_n192": (_i, [_p, _p, _p, _p, _p, _p, _p, _i, _i, _i, _i, _i, _i, _p, _p]),
     "svdq_fp6_n192_preferred": (_i, [_i, _i]),
+    "svdq_int4_route": (_i, [_i, _i]),
     "svdq_gemm_w4a4_fp6_lora_up_qkv": (_i, [_p, _p, _p, _p, _p, _p, _p, _p, _p, _p, _p, ctypes.c_float,
                                             _i, _i, _i, _i, _i, _i, _p, _p]),
     "svdq_mlp_chain_workspace_bytes": (_i, [_i, _i, _i, ctypes.POINTER(ctypes.c_size_t)]),

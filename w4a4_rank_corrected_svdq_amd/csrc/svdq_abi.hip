@@ -201,6 +201,8 @@ extern "C" int svdq_gemm_w4a4_fp6_lora_up_n192(const void* x_fp6, const void* x_
 
 extern "C" int svdq_fp6_n192_preferred(int M, int N) { return svdq::fp6_n192_preferred(M, N); }
 
+extern "C" int svdq_int4_route(int M, int N) { return svdq::fp6_route(M, N); }
+
 extern "C" int svdq_gemm_w4a4_fp6_lora_up_qkv(const void* x_fp6, const void* x_scales, const void* w_fp6,
                                               const void* w_scales, const float* lora_act, const void* lora_up,
                                               const void* bias, const void* norm_q, const void* norm_k,

@@ -515,4 +515,16 @@ int fp6_n192_preferred(int M, int N) {
   return 0.875 * static_cast<double>(r192) < static_cast<double>(r256) ? 1 : 0;
 }
 
+int fp6_route(int M, int N) {
+  // Below half a round of 256 x 256 tiles the int8 engine's 128 x 128 form
+  // (two blocks per CU) keeps more CUs busy than either 6-bit form: measured
+  // on MI355X at M = 256-2048, N = 3072 (K = 512-12288) it takes 0.67-0.87 of
+  // the 6-bit time, while at 192 or more tiles of 256 x 256 (M = 1024 and
+  // 2048 at N = 12288) the 6-bit engine is faster (0.77-0.81 of int8's).
+  if (M <= 0 || N <= 0) return 0;
+  const long long tiles256 = static_cast<long long>((M + 255) / 256) * ((N + 255) / 256);
+  if (2 * tiles256 < cu_count_t()) return 2;
+  return fp6_n192_preferred(M, N);
+}
+
 }  // namespace svdq

@@ -59,6 +59,9 @@ int launch_gemm_w4a4_fp6_n192(const void* x_fp6, const void* x_scales, const voi
                               int rank, int out_dtype, void* y, void* stream);
 // 1 when the 256 x 192 form is expected to be faster for this M and N.
 int fp6_n192_preferred(int M, int N);
+// The kernels an INT4 layer expected to be fastest for an M x N output: 0 the
+// 6-bit kernel 2 in 256 x 256 tiles, 1 in 256 x 192 tiles, 2 the int8 engine.
+int fp6_route(int M, int N);
 // The same kernel with the fused QKV epilogue (one tile per block).
 int launch_gemm_w4a4_fp6_qkv(const void* x_fp6, const void* x_scales, const void* w_fp6, const void* w_scales,
                              const float* lora_act, const void* lora_up, const void* bias, const void* norm_q,

@@ -40,10 +40,14 @@ class SVDQW4A4Linear:
     the fused QKV epilogue.  With N % 192 == 0 the 6-bit engine also keeps
     the weights in the plain row-block layout for its 256 x 192 tile form
     (``svdq_gemm_w4a4_fp6_lora_up_n192``), used per call where
-    ``svdq_fp6_n192_preferred`` says so; ``n192=False`` drops that copy."""
+    ``svdq_fp6_n192_preferred`` says so; ``n192=False`` drops that copy.
+    For few rows (256-row tiles covering fewer than half the CUs) forward()
+    of a 6-bit layer runs the int8 engine's kernels, whose 128 x 128 form
+    keeps more CUs busy (``route``); ``auto_route=False`` keeps it on the
+    6-bit kernels."""
 
     def __init__(self, prepared: dict, bias: Optional[torch.Tensor], device, engine: str = "fp6",
-                 n192: bool = True):
+                 n192: bool = True, auto_route: bool = True):
         dev = torch.device(device)
         self.precision = prepared.get("precision", "int4")
         if self.precision not in ("int4", "mxfp4"):
@@ -63,6 +67,8 @@ class SVDQW4A4Linear:
         self.w_fp6 = None
         self.w_fp6_rows = None
         self._n192_choice = {}
+        self._route_choice = {}
+        self.auto_route = auto_route
         if self.engine == "fp6":
             codes = np.asarray(prepared["w_codes"], np.uint8).reshape(self.N, self.K // 2)
             self.w_fp6 = _to_dev(ops.pack_fp6_operand(codes, L.SVDQ_FP6_WEIGHTS), dev)
@@ -76,7 +82,7 @@ class SVDQW4A4Linear:
     @classmethod
     def from_linear(cls, linear: torch.nn.Linear, act_absmax, rank: int = 32, group: int = 64,
                     alpha: float = 0.5, device="cuda", precision: str = "int4", engine: str = "fp6",
-                    n192: bool = True):
+                    n192: bool = True, auto_route: bool = True):
         """Quantize a ``torch.nn.Linear`` (weight [out][in], bf16) given the
         calibration statistic ``act_absmax`` [in] (max |x| per input channel)."""
         w = linear.weight.detach().to(torch.bfloat16).cpu()
@@ -87,11 +93,23 @@ class SVDQW4A4Linear:
             prep = ops.prepare_weights(w, a, rank, group, alpha)
         else:
             raise ValueError(f"unknown precision {precision!r}")
-        return cls(prep, linear.bias, device, engine, n192)
+        return cls(prep, linear.bias, device, engine, n192, auto_route)
+
+    def route(self, M: int) -> str:
+        """The engine whose kernels forward() runs for M rows: the layer's
+        own, except that an "fp6" layer with auto_route takes the int8
+        engine's kernels where its 256-row tiles would cover fewer than half
+        the CUs (svdq_int4_route; the nibble codes are resident anyway)."""
+        if self.engine != "fp6" or not self.auto_route:
+            return self.engine
+        hit = self._route_choice.get(M)
+        if hit is None:
+            hit = self._route_choice[M] = "int8" if ops.int4_route(M, self.N) == 2 else "fp6"
+        return hit
 
     def forward(self, x: torch.Tensor, act: int = L.SVDQ_ACT_NONE, out_dtype: int = L.SVDQ_OUT_BF16):
         M = x.shape[0]
-        if self.engine == "fp6":
+        if self.route(M) == "fp6":
             xf, xs, la = ops.quant_act_lora_down_fp6(x, self.smooth_inv, self.lora_down, self.rank, self.group, act)
             return self.kernel2_fp6(xf, xs, la, M, out_dtype)
         if self.precision == "mxfp4":
@@ -148,9 +166,9 @@ class SVDQMLPChain:
     """An MLP pair (up layer, tanh-GELU, down layer), both on the 6-bit
     engine, run as a chain: kernel 1 of the up layer, the up layer's kernel 2
     with the down layer's kernel 1 in its epilogue (the up output never goes
-    to memory), then the down layer's kernel 2.  The result is the two-layer
-    path's ``down(up(x), act=GELU)`` up to the fp32 rounding of the down
-    projection's per-slice partials."""
+    to memory), then the down layer's kernel 2.  The result is the 6-bit
+    two-layer path's ``down(up(x), act=GELU)`` (modules with auto_route off)
+    up to the fp32 rounding of the down projection's per-slice partials."""
 
     def __init__(self, up: SVDQW4A4Linear, down: SVDQW4A4Linear):
         if up.engine != "fp6" or down.engine != "fp6":

@@ -262,6 +262,13 @@ def fp6_n192_preferred(M: int, N: int) -> bool:
     return bool(L.lib().svdq_fp6_n192_preferred(int(M), int(N)))
 
 
+def int4_route(M: int, N: int) -> int:
+    """The kernels expected to be fastest for an INT4 layer's M x N output on
+    the current device: 0 6-bit kernel 2 in 256 x 256 tiles, 1 in 256 x 192
+    tiles, 2 the int8 engine (svdq_int4_route)."""
+    return int(L.lib().svdq_int4_route(int(M), int(N)))
+
+
 def gemm_w4a4_fp6_lora_up_qkv(x_fp6, x_scales, w_fp6, w_scales, lora_act, lora_up, bias, norm_q, norm_k,
                               rope_cos, rope_sin, M: int, N: int, K: int, rank: int, eps: float = 1e-6,
                               group: int = 64, out_dtype: int = L.SVDQ_OUT_BF16,
