@@ -115,6 +115,29 @@ def quantize_activation_mx(x, smooth_inv, act: str = "none"):
     return q, e, x_hat
 
 
+def activation_decision_band_mx(x_hat, rel: float, exponents=None):
+    """The activation side's MXFP4 decisions (readings M2, M4) when every
+    value of x_hat may be off by a relative ``rel`` (another correct fp32
+    evaluation of the input function, such as the tanh-GELU on load).  The
+    block exponent and the E2M1 rounding are monotone in what they round, so
+    each decision lies between its results at the two ends of the band:
+      exponents (e_lo, e_hi) [M x K/32] from the block absmax times (1 -+ rel);
+      element values (q_lo, q_hi) [M x K] from x_hat 2^-e -+ |.| rel, with e
+        the exponents actually used (``exponents``; e_lo when None).
+    With rel = 0 this is quantize_activation_mx's quantizer exactly."""
+    x_hat = np.asarray(x_hat, dtype=np.float64)
+    M, K = x_hat.shape
+    xb = x_hat.reshape(M, K // BLOCK, BLOCK)
+    amax = np.abs(xb).max(axis=-1)
+    e_lo = mx_block_exponent(amax * (1.0 - rel))
+    e_hi = mx_block_exponent(amax * (1.0 + rel))
+    e = e_lo if exponents is None else np.asarray(exponents, dtype=np.int64).reshape(e_lo.shape)
+    v = xb * np.ldexp(1.0, -e)[..., None]
+    q_lo = e2m1_round(v - np.abs(v) * rel).reshape(M, K)
+    q_hi = e2m1_round(v + np.abs(v) * rel).reshape(M, K)
+    return e_lo, e_hi, q_lo, q_hi
+
+
 def prepare_mx(weight_nk, act_absmax, rank: int, alpha: float = 0.5, factors=None):
     """Preparation as ``svdq_oracle.prepare`` (smoothing, split, residual) with
     the residual quantized to MXFP4 along K per output channel."""

@@ -57,6 +57,10 @@ Readings where the pages are silent (each also listed in the design doc):
   R10 The unfused comparison path (``forward_unfused``) stores the 4-bit
       GEMM's output plus bias as bf16 before the up projection adds to it,
       and rounds to bf16 again: the 16-bit output is written twice.
+  G1  The tanh-GELU of R9 may be evaluated anywhere within a relative 4e-6 of
+      the exact function; where that can move a group's scale or a code
+      across its rounding boundary, both results are valid
+      (``activation_decision_band`` states the band).
 
 Emulating one fp32 operation by computing it in fp64 and rounding once to
 fp32 gives the correctly rounded fp32 result for +, -, *, / and sqrt, since
@@ -70,6 +74,7 @@ __all__ = [
     "round_to_bits", "bf16", "fp16", "fp32",
     "smoothing_factors", "smooth_weight", "low_rank_split", "quantize_groups",
     "quantize_weight_residual", "prepare", "gelu_tanh", "quantize_activation",
+    "activation_decision_band",
     "pack_int4", "unpack_int4", "lora_down", "w4a4_product",
     "w4a4_product_bruteforce", "forward", "forward_unfused", "reference_fp64", "rel_fro",
     "rms_norm", "rope", "forward_qkv", "forward_mlp_chain",
@@ -254,6 +259,36 @@ def quantize_activation(x, smooth_inv, group: int = 64, act: str = "none",
     rcp = np.where(np.isinf(s), 0.0, rcp)
     q = np.clip(np.rint(fp32(xg * rcp[..., None])), INT4_MIN, INT4_MAX).astype(np.int64)
     return q.reshape(M, K), s, x_hat
+
+
+def activation_decision_band(x_hat, rel: float, group: int = 64, scales=None):
+    """The activation quantizer's decisions (reading R5) when every value of
+    x_hat may be off by a relative ``rel``: what another correct evaluation
+    of the same input function (the tanh-GELU on load, evaluated in fp32 to
+    ~1e-6 relative) may legitimately produce.
+
+    Both decisions are monotone in the value they round, so each lies between
+    its results at the two ends of the band:
+      scales (s_lo, s_hi) [M x G]: fp16(fp32(a (1 -+ rel) / 7)), a the group absmax;
+      codes (q_lo, q_hi) [M x K]: clamp(rne(fp32(v -+ |v| rel)), -8, 7), with
+        v = x_hat * fp32(1 / s) for the scales s actually used (``scales``
+        [M x G]; the band's own lower scales when None).
+    Where lo == hi the decision is unique; elsewhere either end is valid.
+    With rel = 0 this is quantize_activation's quantizer exactly."""
+    x_hat = np.asarray(x_hat, dtype=np.float64)
+    M, K = x_hat.shape
+    G = K // group
+    xg = x_hat.reshape(M, G, group)
+    a = np.abs(xg).max(axis=-1)
+    s_lo = fp16(fp32(a * (1.0 - rel) / QMAX))
+    s_hi = fp16(fp32(a * (1.0 + rel) / QMAX))
+    s = s_lo if scales is None else np.asarray(scales, dtype=np.float64).reshape(M, G)
+    with np.errstate(divide="ignore"):
+        rcp = np.where(s == 0, 0.0, fp32(1.0 / np.where(s == 0, 1.0, s)))
+    v = xg * rcp[..., None]
+    q_lo = np.clip(np.rint(fp32(v - np.abs(v) * rel)), INT4_MIN, INT4_MAX).astype(np.int64)
+    q_hi = np.clip(np.rint(fp32(v + np.abs(v) * rel)), INT4_MIN, INT4_MAX).astype(np.int64)
+    return s_lo, s_hi, q_lo.reshape(M, K), q_hi.reshape(M, K)
 
 
 def pack_int4(q) -> np.ndarray:

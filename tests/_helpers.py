@@ -1,5 +1,6 @@
 """Shared test helpers: layout conversions between the oracle's math layout
-and the C ABI's storage layout.  No method arithmetic lives here."""
+and the C ABI's storage layout, and the comparison bars.  No method
+arithmetic lives here (the decision bands come from the oracle)."""
 import numpy as np
 
 import oracle as O
@@ -84,3 +85,40 @@ def check_f32_elementwise(yg, yo, rel: float = 2.0 ** -14) -> None:
     rms = np.sqrt(np.mean(yo * yo)) if yo.size else 0.0
     bad = np.abs(yg - yo) > rel * (np.abs(yo) + rms)
     assert not bad.any(), f"{bad.sum()} of {bad.size} fp32 elements outside the bound"
+
+
+# The device's tanh-GELU on load (fp32, hardware exp2 and reciprocal) is
+# within ~1.3e-6 relative of the oracle's fp64 tanh form after the fp32
+# roundings of x_hat; the bands below allow three times that.
+GELU_REL = 4e-6
+
+
+def check_int4_codes_in_band(q_dev, s_dev, x_hat, rel: float = GELU_REL, group: int = 64):
+    """Kernel 1's INT4 scales [M][G] and codes [M][K] against the oracle's
+    decisions on x_hat under a relative band: equal wherever the oracle's
+    decision is unique, one of the band's two ends elsewhere (each code
+    checked against the scale the device used).  Returns the numbers of
+    ambiguous scales and codes."""
+    s_dev = np.asarray(s_dev, np.float64)
+    s_lo, s_hi, _, _ = O.activation_decision_band(x_hat, rel, group)
+    bad = (s_dev < s_lo) | (s_dev > s_hi)
+    assert not bad.any(), f"{bad.sum()} scales outside the band, first at {np.argwhere(bad)[:4].tolist()}"
+    _, _, q_lo, q_hi = O.activation_decision_band(x_hat, rel, group, scales=s_dev)
+    q_dev = np.asarray(q_dev)
+    bad = (q_dev < q_lo) | (q_dev > q_hi)
+    assert not bad.any(), f"{bad.sum()} codes outside the band, first at {np.argwhere(bad)[:4].tolist()}"
+    return int(np.count_nonzero(s_lo != s_hi)), int(np.count_nonzero(q_lo != q_hi))
+
+
+def check_mx_codes_in_band(v_dev, e_dev, x_hat, rel: float = GELU_REL):
+    """The MXFP4 counterpart: block exponents [M][K/32] and element values
+    [M][K] (decoded E2M1) against the oracle's decisions under the band."""
+    e_dev = np.asarray(e_dev, np.int64)
+    e_lo, e_hi, _, _ = O.mx.activation_decision_band_mx(x_hat, rel)
+    bad = (e_dev < e_lo) | (e_dev > e_hi)
+    assert not bad.any(), f"{bad.sum()} exponents outside the band"
+    _, _, q_lo, q_hi = O.mx.activation_decision_band_mx(x_hat, rel, exponents=e_dev)
+    v_dev = np.asarray(v_dev, np.float64)
+    bad = (v_dev < q_lo) | (v_dev > q_hi)
+    assert not bad.any(), f"{bad.sum()} element values outside the band"
+    return int(np.count_nonzero(e_lo != e_hi)), int(np.count_nonzero(q_lo != q_hi))

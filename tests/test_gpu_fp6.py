@@ -15,7 +15,7 @@ import oracle as O
 import workloads
 from tests._fp6 import ACT, WGT, decode_fp6
 from tests._helpers import (bf16_bits_to_f64, check_bf16_elementwise, check_f32_elementwise, f64_to_bf16_bits,  # noqa: F401,E501
-                            abi_to_oracle_prep, oracle_prep_to_abi, ulp_bf16)
+                            abi_to_oracle_prep, check_int4_codes_in_band, oracle_prep_to_abi, ulp_bf16)
 
 S = pytest.importorskip("w4a4_rank_corrected_svdq_amd")
 from w4a4_rank_corrected_svdq_amd import _lib as L  # noqa: E402
@@ -186,10 +186,11 @@ def test_k1_matches_nibble_kernel():
 
 
 @pytest.mark.parametrize("M,K,rank", [(256, 3072, 32), (4200, 512, 32), (8200, 256, 128)])
-def test_k1_gelu_statistical(M, K, rank):
-    """GELU on load: the device GELU and the oracle's fp64 tanh differ by a
-    few ulps, so codes may differ at rounding boundaries (by 1, in at most
-    1e-4 of them) and scales by at most one fp16 ulp.  (4200, 512, 32) and
+def test_k1_gelu_codes_in_band(M, K, rank):
+    """GELU on load: the device GELU and the oracle's fp64 tanh differ by
+    ~1e-6 relative, so a scale or code may differ only where the oracle's
+    value lies that close to its rounding boundary (then either candidate is
+    valid); everywhere else they are equal.  (4200, 512, 32) and
     (8200, 256, 128) run kernel 1's 32-row blocks (more 16-row blocks than
     CUs)."""
     wl, Lr, po, abi = _case(M, K, max(64, rank), rank, seed=11)
@@ -197,10 +198,8 @@ def test_k1_gelu_statistical(M, K, rank):
     xf, xs, la = run_k1(xb, abi["smooth_inv"], abi["lora_down"], rank, act=L.SVDQ_ACT_GELU_TANH)
     q, s, xh = O.quantize_activation(wl.x, po["smooth_inv"], 64, act="gelu_tanh")
     codes, _ = decode_fp6(xf.cpu().numpy(), M, K, ACT)
-    d = codes - q
-    assert np.abs(d).max() <= 1 and np.count_nonzero(d) <= 1e-4 * d.size + 1
-    sg = xs.cpu().numpy()[:, :M].astype(np.float64)
-    assert np.all(np.abs(sg - s.T) <= np.abs(s.T) * 2.0 ** -10 + 1e-12)
+    amb_s, amb_q = check_int4_codes_in_band(codes, xs.cpu().numpy()[:, :M].astype(np.float64).T, xh)
+    assert amb_s <= 0.03 * s.size and amb_q <= 1e-4 * q.size   # the band is narrow
 
 
 # ------------------------------------------------------------------ whole layer

@@ -11,7 +11,8 @@ import torch
 
 import oracle as O
 import workloads
-from tests._helpers import bf16_bits_to_f64, check_bf16_elementwise, check_f32_elementwise, f64_to_bf16_bits
+from tests._helpers import (bf16_bits_to_f64, check_bf16_elementwise, check_f32_elementwise, check_mx_codes_in_band,
+                            f64_to_bf16_bits)
 from tests.test_mx_host import mx_prep_to_abi
 
 S = pytest.importorskip("w4a4_rank_corrected_svdq_amd")
@@ -95,10 +96,11 @@ def test_k1_mx_codes_scales_bit_exact(M, K, rank):
         assert O.rel_fro(la.double().cpu().numpy(), O.lora_down(xh, po["L1"])) < LORA_TOL
 
 
-def test_k1_mx_gelu_statistical():
-    """tanh-GELU on load: the device GELU (exp2 and reciprocal, fp32) vs the
-    oracle's fp64 tanh may move a value across a rounding boundary; codes
-    differ rarely and by one grid step."""
+def test_k1_mx_gelu_codes_in_band():
+    """tanh-GELU on load: the device GELU (exp2 and reciprocal, fp32) and the
+    oracle's fp64 tanh differ by ~1e-6 relative, so a block exponent or an
+    element may differ only where the oracle's value lies that close to its
+    rounding boundary (either candidate is then valid); elsewhere equal."""
     M, K = 256, 1024
     wl, Lr, po, abi = _case(M, K, 128, 32, seed=96)
     xc, xs, la = run_k1(wl.x_bits, abi, act=L.SVDQ_ACT_GELU_TANH)
@@ -106,10 +108,8 @@ def test_k1_mx_gelu_statistical():
     codes = O.unpack_int4(xc.cpu().numpy()) & 15
     qg = MX.e2m1_decode(codes)
     eg = xs.cpu().numpy().astype(np.int64) - 127
-    same_scale = np.repeat(eg == e, 32, axis=1)
-    assert (eg != e).mean() <= 1e-3
-    mism = (qg != q) & same_scale
-    assert mism.mean() <= 1e-3
+    amb_e, amb_q = check_mx_codes_in_band(qg, eg, xh)
+    assert amb_e <= 1e-3 * e.size and amb_q <= 1e-3 * q.size   # the band is narrow
 
 
 # ------------------------------------------------------------------ kernel 2: exact products

@@ -12,7 +12,7 @@ import torch
 import oracle as O
 import workloads
 from tests._helpers import (abi_to_oracle_prep, bf16_bits_to_f64, check_bf16_elementwise,
-                            check_f32_elementwise, f64_to_bf16_bits, oracle_prep_to_abi)
+                            check_f32_elementwise, check_int4_codes_in_band, f64_to_bf16_bits, oracle_prep_to_abi)
 
 S = pytest.importorskip("w4a4_rank_corrected_svdq_amd")
 from w4a4_rank_corrected_svdq_amd import _lib as L  # noqa: E402
@@ -167,21 +167,20 @@ def test_k1_codes_scales_lora_act(M, K, rank):
 
 
 @pytest.mark.parametrize("M,K", [(512, 1024), (4200, 256)])
-def test_k1_gelu_statistical(M, K):
+def test_k1_gelu_codes_in_band(M, K):
     """tanh-GELU on load: the device GELU and the oracle's fp64 tanh differ by
-    a few ulps, so a code can differ where a value sits on a rounding
-    boundary.  M = 4200 has more 16-row blocks than an MI355X has CUs, so
-    kernel 1 runs 32-row blocks of 8 waves, with the GELU prologue."""
+    ~1e-6 relative, so a scale or code may differ only where the oracle's
+    value lies that close to its rounding boundary: every scale and code
+    equals the oracle's where its decision is unique and is one of the two
+    candidates elsewhere.  M = 4200 has more 16-row blocks than an MI355X has
+    CUs, so kernel 1 runs 32-row blocks of 8 waves, with the GELU prologue."""
     rank = 32
     wl, Lr, po, abi = _small_case(M, K, 64, rank, seed=43)
     xc, xs, la = run_k1(wl.x_bits, abi["smooth_inv"], abi["lora_down"], rank, act=L.SVDQ_ACT_GELU_TANH)
     q, s, xh = O.quantize_activation(wl.x, po["smooth_inv"], 64, act="gelu_tanh")
     qg = O.unpack_int4(xc.cpu().numpy())
-    mism = qg != q
-    assert mism.mean() <= 1e-4
-    assert np.all(np.abs(qg - q)[mism] == 1)
-    sg = xs.cpu().numpy().astype(np.float64).T
-    assert np.all(np.abs(sg - s) <= np.abs(s) * 2 ** -10)
+    amb_s, amb_q = check_int4_codes_in_band(qg, xs.cpu().numpy().astype(np.float64).T, xh)
+    assert amb_s <= 0.03 * s.size and amb_q <= 1e-4 * q.size   # the band is narrow
     assert O.rel_fro(la.double().cpu().numpy(), O.lora_down(xh, po["L1"])) < 1e-4
 
 
@@ -436,10 +435,9 @@ def test_full_size_mlp_down_gelu_sampled_rows():
     abi = oracle_prep_to_abi(po)
     xc, xs, la = run_k1(wl.x_bits, abi["smooth_inv"], abi["lora_down"], r, act=L.SVDQ_ACT_GELU_TANH)
     y = run_k2(xc, xs, abi, la, None, M)
-    q_all, _, _ = O.quantize_activation(wl.x, po["smooth_inv"], 64, act="gelu_tanh")
-    mism = O.unpack_int4(xc.cpu().numpy()) != q_all
-    assert mism.mean() <= 1e-4
-    del q_all
+    _, _, xh_all = O.quantize_activation(wl.x, po["smooth_inv"], 64, act="gelu_tanh")
+    check_int4_codes_in_band(O.unpack_int4(xc.cpu().numpy()), xs.cpu().numpy().astype(np.float64).T, xh_all)
+    del xh_all
     rows = _sample_rows(M, rng, 32)
     Yo = O.forward(wl.x[rows], po, act="gelu_tanh")
     yr = to_np_bf16(y[torch.from_numpy(rows).cuda()])

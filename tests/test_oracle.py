@@ -443,3 +443,43 @@ def test_mlp_chain_rank0_and_partial_slice():
     y = O.forward_mlp_chain(wl.x, pu, pd, up.bias, dn.bias, slice_cols=256)
     ref = O.forward(O.forward(wl.x, pu, bias=up.bias), pd, act="gelu_tanh", bias=dn.bias)
     assert O.rel_fro(y, ref) < 1e-5
+
+
+# ---------------------------------------------------------------- decision band
+def test_decision_band_hand_worked():
+    """Activation quantizer decisions under a relative input band, worked by
+    hand.  Group absmax 7 (1 + 2^-11): a / 7 = 1 + 2^-11 is the midpoint of the
+    fp16 values 1 and 1 + 2^-10, which rounds to even (1); a hair above, to
+    1 + 2^-10.  With scale 1 the codes are rne of the values themselves:
+    2.5 -> 2 and -2.5 -> -2 (ties to even), 6.5 -> 6, 0.5 -> 0, 2.4 -> 2; a
+    band of 1e-6 around a tie admits both neighbours, around 2.4 only 2."""
+    x = np.zeros((1, 64))
+    x[0, :6] = [7.00341796875, 2.5, -2.5, 2.4, 6.5, 0.5]
+    s_lo, s_hi, q_lo, q_hi = O.activation_decision_band(x, 0.0)
+    assert s_lo[0, 0] == s_hi[0, 0] == 1.0
+    assert list(q_lo[0, :6]) == list(q_hi[0, :6]) == [7, 2, -2, 2, 6, 0]
+    s_lo, s_hi, q_lo, q_hi = O.activation_decision_band(x, 1e-6)
+    assert (s_lo[0, 0], s_hi[0, 0]) == (1.0, 1.0 + 2.0 ** -10)
+    assert list(q_lo[0, :6]) == [7, 2, -3, 2, 6, 0]
+    assert list(q_hi[0, :6]) == [7, 3, -2, 2, 7, 1]
+    assert not q_lo[0, 6:].any() and not q_hi[0, 6:].any()
+    # with the upper scale every value shrinks by ~2^-10: no tie is left
+    _, _, q_lo, q_hi = O.activation_decision_band(x, 1e-6, scales=s_hi)
+    assert list(q_lo[0, :6]) == list(q_hi[0, :6]) == [7, 2, -2, 2, 6, 0]
+
+
+def test_decision_band_zero_width_is_the_quantizer():
+    """rel = 0 gives quantize_activation's scales and codes, element for element."""
+    rng = np.random.default_rng(5)
+    x = O.bf16(rng.standard_normal((48, 256)) * np.where(rng.random(256) < 0.05, 30.0, 1.0))
+    si = O.fp32(1.0 / (0.5 + rng.random(256)))
+    q, s, xh = O.quantize_activation(x, si, 64, act="gelu_tanh")
+    s_lo, s_hi, q_lo, q_hi = O.activation_decision_band(xh, 0.0)
+    np.testing.assert_array_equal(s_lo, s)
+    np.testing.assert_array_equal(s_hi, s)
+    np.testing.assert_array_equal(q_lo, q)
+    np.testing.assert_array_equal(q_hi, q)
+    # and a band that is wide enough to matter stays ordered and within one step
+    s_lo, s_hi, q_lo, q_hi = O.activation_decision_band(xh, 1e-3, scales=s)
+    assert np.all(s_lo <= s) and np.all(s <= s_hi)
+    assert np.all(q_lo <= q) and np.all(q <= q_hi) and np.all(q_hi - q_lo <= 1)

@@ -142,3 +142,32 @@ def test_prepared_bytes_mx_closed_form():
     # FLUX MLP-up layer: the same ~3.6x reduction from bf16 as the INT4 layer
     ratio = 2 * 3072 * 12288 / MX.prepared_bytes_mx(3072, 12288, 32)
     assert 3.5 < ratio < 3.7
+
+
+def test_mx_decision_band_hand_worked():
+    """Block absmax exactly 4 = 2^2: exponent 2 - 2 = 0; a hair below, 1 - 2 =
+    -1.  With exponent 0 the values round on the E2M1 grid 0, 0.5, 1, 1.5, 2,
+    3, 4, 6 with ties to the even code: 2.5 -> 2, 0.25 -> 0, 3.5 -> 4,
+    -1.25 -> -1, 1.75 -> 2; a band of 1e-6 around each tie admits both
+    neighbours."""
+    x = np.zeros((1, 32))
+    x[0, :6] = [4.0, 2.5, 0.25, 3.5, -1.25, 1.75]
+    e_lo, e_hi, q_lo, q_hi = MX.activation_decision_band_mx(x, 0.0)
+    assert e_lo[0, 0] == e_hi[0, 0] == 0
+    assert list(q_lo[0, :6]) == list(q_hi[0, :6]) == [4.0, 2.0, 0.0, 4.0, -1.0, 2.0]
+    e_lo, e_hi, q_lo, q_hi = MX.activation_decision_band_mx(x, 1e-6, exponents=np.zeros((1, 1)))
+    assert (e_lo[0, 0], e_hi[0, 0]) == (-1, 0)
+    assert list(q_lo[0, :6]) == [4.0, 2.0, 0.0, 3.0, -1.5, 1.5]
+    assert list(q_hi[0, :6]) == [4.0, 3.0, 0.5, 4.0, -1.0, 2.0]
+
+
+def test_mx_decision_band_zero_width_is_the_quantizer():
+    rng = np.random.default_rng(6)
+    x = O.bf16(rng.standard_normal((40, 256)) * np.where(rng.random(256) < 0.05, 30.0, 1.0))
+    si = O.fp32(1.0 / (0.5 + rng.random(256)))
+    q, e, xh = MX.quantize_activation_mx(x, si, act="gelu_tanh")
+    e_lo, e_hi, q_lo, q_hi = MX.activation_decision_band_mx(xh, 0.0)
+    np.testing.assert_array_equal(e_lo, e)
+    np.testing.assert_array_equal(e_hi, e)
+    np.testing.assert_array_equal(q_lo, q)
+    np.testing.assert_array_equal(q_hi, q)
