@@ -894,13 +894,31 @@ __global__ __launch_bounds__(F_THREADS, 1) void k_gemm_w4a4_fp6(
 }
 
 // lora_act = the column slices' partial down projections summed in slice
-// order (the chain's second pass); four ranks per thread.
-__global__ __launch_bounds__(256) void k_partials_reduce(const float4* __restrict__ partials, int S, size_t n4,
-                                                       float4* __restrict__ lora_act) {
-  const size_t i = static_cast<size_t>(blockIdx.x) * 256 + threadIdx.x;
+// order (the chain's second pass); four ranks per thread.  The loads of 16
+// slices go out before their sums (the sum stays in slice order), and
+// 64-thread blocks spread the few outputs over every CU: the pass is a
+// read of the partials, bound by how many loads are in flight.
+constexpr int R_THREADS = 64;
+constexpr int R_BATCH = 16;
+__global__ __launch_bounds__(R_THREADS) void k_partials_reduce(const float4* __restrict__ partials, int S,
+                                                             size_t n4, float4* __restrict__ lora_act) {
+  const size_t i = static_cast<size_t>(blockIdx.x) * R_THREADS + threadIdx.x;
   if (i >= n4) return;
   float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
-  for (int s = 0; s < S; ++s) {
+  int s = 0;
+  for (; s + R_BATCH <= S; s += R_BATCH) {
+    float4 v[R_BATCH];
+#pragma unroll
+    for (int u = 0; u < R_BATCH; ++u) v[u] = partials[static_cast<size_t>(s + u) * n4 + i];
+#pragma unroll
+    for (int u = 0; u < R_BATCH; ++u) {
+      acc.x += v[u].x;
+      acc.y += v[u].y;
+      acc.z += v[u].z;
+      acc.w += v[u].w;
+    }
+  }
+  for (; s < S; ++s) {
     const float4 v = partials[static_cast<size_t>(s) * n4 + i];
     acc.x += v.x;
     acc.y += v.y;
@@ -1012,7 +1030,8 @@ int launch_mlp_chain_fp6(const void* x_fp6, const void* x_scales, const void* w_
   if (rank_dn > 0) {
     const int S = (N + F_BN - 1) / F_BN;
     const size_t n4 = static_cast<size_t>(M) * rank_dn / 4;
-    hipLaunchKernelGGL(k_partials_reduce, dim3(static_cast<unsigned>((n4 + 255) / 256)), dim3(256), 0, st,
+    hipLaunchKernelGGL(k_partials_reduce, dim3(static_cast<unsigned>((n4 + R_THREADS - 1) / R_THREADS)),
+                       dim3(R_THREADS), 0, st,
                        reinterpret_cast<const float4*>(partials), S, n4, reinterpret_cast<float4*>(lora_act_dn));
   }
   return hipGetLastError() == hipSuccess ? SVDQ_OK : SVDQ_ERR_HIP;
