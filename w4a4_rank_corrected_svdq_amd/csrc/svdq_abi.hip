@@ -54,6 +54,22 @@ inline bool fits_buffer(int64_t rows, int64_t bytes_per_row) { return rows * byt
 
 }  // namespace
 
+namespace svdq {
+
+int device_cu_count() {
+  static std::atomic<int> cached[kMaxDevices];
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return 256;
+  int n = cached[dev].load(std::memory_order_relaxed);
+  if (n == 0) {
+    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0) n = 256;
+    cached[dev].store(n, std::memory_order_relaxed);
+  }
+  return n;
+}
+
+}  // namespace svdq
+
 extern "C" const char* svdq_status_string(int status) {
   switch (status) {
     case SVDQ_OK: return "SVDQ_OK";

@@ -935,18 +935,6 @@ __global__ __launch_bounds__(R_THREADS) void k_partials_reduce(const float4* __r
 constexpr size_t CHAIN_SCRATCH_BYTES = SVDQ_CHAIN_SCRATCH_BYTES;
 static __device__ __align__(256) unsigned char scratch[CHAIN_SCRATCH_BYTES];
 
-int cu_count() {
-  static int cached[64] = {};
-  int dev = 0;
-  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
-  if (cached[dev] == 0) {
-    int n = 0;
-    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0) n = 256;
-    cached[dev] = n;
-  }
-  return cached[dev];
-}
-
 }  // namespace
 
 namespace svdq {
@@ -958,7 +946,7 @@ int launch_gemm_w4a4_fp6(const void* x_fp6, const void* x_scales, const void* w_
   const int tiles = ((M + F_BM - 1) / F_BM) * ((N + F_BN - 1) / F_BN);
   // one block per CU, a multiple of 8 (the XCD count) so that a block's
   // tiles stay on its XCD; never more blocks than tiles
-  const int cus = cu_count() & ~7;
+  const int cus = device_cu_count() & ~7;
   const int grid = tiles < cus ? tiles : (cus > 0 ? cus : tiles);
   if ((tiles + grid - 1) / grid > F_MAX_TILES) return SVDQ_ERR_UNSUPPORTED_SHAPE;
 #define SVDQ_K2F(OF)                                                                                          \

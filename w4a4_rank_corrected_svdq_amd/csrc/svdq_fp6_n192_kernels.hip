@@ -466,18 +466,6 @@ __global__ __launch_bounds__(T_THREADS, 1) void k_gemm_w4a4_fp6_n192(
   __builtin_amdgcn_s_waitcnt(waitcnt_vm_lgkm0(0));
 }
 
-int cu_count_t() {
-  static int cached[64] = {};
-  int dev = 0;
-  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
-  if (cached[dev] == 0) {
-    int n = 0;
-    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0) n = 256;
-    cached[dev] = n;
-  }
-  return cached[dev];
-}
-
 }  // namespace
 
 namespace svdq {
@@ -487,7 +475,7 @@ int launch_gemm_w4a4_fp6_n192(const void* x_fp6, const void* x_scales, const voi
                               int rank, int out_dtype, void* y, void* stream) {
   hipStream_t st = static_cast<hipStream_t>(stream);
   const int tiles = ((M + T_BM - 1) / T_BM) * (N / T_BN);
-  const int cus = cu_count_t() & ~7;
+  const int cus = device_cu_count() & ~7;
   const int grid = tiles < cus ? tiles : (cus > 0 ? cus : tiles);
   if ((tiles + grid - 1) / grid > T_MAX_TILES) return SVDQ_ERR_UNSUPPORTED_SHAPE;
 #define SVDQ_K2T(OF)                                                                                          \
@@ -508,7 +496,7 @@ int fp6_n192_preferred(int M, int N) {
   // over 3 and 4 full rounds at 16384 x 3072 -> 3072: the per-stage barrier,
   // DMA issue and waits do not shrink with the tile's 3/4 of the work)
   if (N <= 0 || N % T_BN != 0 || M <= 0) return 0;
-  const int cus = cu_count_t();
+  const int cus = device_cu_count();
   const long long nM = (M + 255) / 256;
   const long long r256 = (nM * ((N + 255) / 256) + cus - 1) / cus;
   const long long r192 = (nM * (N / T_BN) + cus - 1) / cus;
@@ -523,7 +511,7 @@ int fp6_route(int M, int N) {
   // 2048 at N = 12288) the 6-bit engine is faster (0.77-0.81 of int8's).
   if (M <= 0 || N <= 0) return 0;
   const long long tiles256 = static_cast<long long>((M + 255) / 256) * ((N + 255) / 256);
-  if (2 * tiles256 < cu_count_t()) return 2;
+  if (2 * tiles256 < device_cu_count()) return 2;
   return fp6_n192_preferred(M, N);
 }
 

@@ -7,6 +7,10 @@ namespace svdq {
 
 // Shape rules common to every entry point (see svdq.h).
 int validate_shape(int K, int N, int rank, int group);
+
+// Compute units of the current device, looked up once per device (256 when
+// the runtime cannot tell); safe to call from several host threads.
+int device_cu_count();
 // Shape rules of the MXFP4 entry points (K a multiple of 128).
 int validate_shape_mx(int K, int N, int rank);
 

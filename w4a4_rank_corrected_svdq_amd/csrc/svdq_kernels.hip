@@ -1276,19 +1276,6 @@ __global__ __launch_bounds__(KT_THREADS, 1) void k_gemm_w4a4_lora_up(
   kt_epilogue<OUT_F32, EPI>(acc, &ring[0][0], m0, n0, M, N, y, qa);
 }
 
-// Compute units of the current device (cached per device).
-int device_cu_count() {
-  static int cached[64] = {};
-  int dev = 0;
-  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
-  if (cached[dev] == 0) {
-    int n = 0;
-    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0) n = 256;
-    cached[dev] = n;
-  }
-  return cached[dev];
-}
-
 template <int ACT, int NT, int QM, int RT, int WB>
 int launch_k1_instance(const void* x, const float* smooth_inv, const void* lora_down, int M, int K, int rank,
                        void* x_codes, void* x_scales, float* lora_act, size_t smem, int blocks, int waves,
@@ -1313,7 +1300,7 @@ int launch_k1_kernel(const void* x, const float* smooth_inv, const void* lora_do
   // a second round of 16-wave blocks.
   const int rows = QM == Q_FP6 ? 32 * ((M + 31) / 32) : M;   // FP6: the padded last row block too
   const int blocks = (rows + K1_ROWS * RT - 1) / (K1_ROWS * RT);
-  const int waves = (k1_waves<NT>() == 16 && blocks > device_cu_count()) ? 8 : k1_waves<NT>();
+  const int waves = (k1_waves<NT>() == 16 && blocks > svdq::device_cu_count()) ? 8 : k1_waves<NT>();
   // 32-row blocks of the 16-wave ranks launched as 8-wave blocks get the
   // 8-wave register budget (the 6-bit mode would spill in 128 VGPRs).
   if constexpr (RT == 2 && k1_waves<NT>() == 16) {
@@ -1342,15 +1329,15 @@ int launch_k1_nt(const void* x, const float* smooth_inv, const void* lora_down, 
     // 16-row block would read 786 KB of L1 for 96 KB of X); 64-row blocks
     // would spill
     const size_t smem2 = static_cast<size_t>(K) * sizeof(float) + sizeof(float) * 8 * 2 * K1_ROWS * 2 * 16;
-    if ((M + 2 * K1_ROWS - 1) / (2 * K1_ROWS) >= device_cu_count() && smem2 <= 160 * 1024)
+    if ((M + 2 * K1_ROWS - 1) / (2 * K1_ROWS) >= svdq::device_cu_count() && smem2 <= 160 * 1024)
       return launch_k1_kernel<ACT, NT, QM, 2>(x, smooth_inv, lora_down, M, K, rank, x_codes, x_scales, lora_act,
                                               smem2, st);
   }
   if constexpr (NT > 0 && NT <= 4) {
-    bool many = (M + K1_ROWS - 1) / K1_ROWS > device_cu_count();
+    bool many = (M + K1_ROWS - 1) / K1_ROWS > svdq::device_cu_count();
     // the 6-bit mode at ranks 49..64 fits its registers only as 8-wave
     // blocks, i.e. when the 32-row blocks themselves outnumber the CUs
-    if (QM == Q_FP6 && NT == 4) many = (M + 2 * K1_ROWS - 1) / (2 * K1_ROWS) > device_cu_count();
+    if (QM == Q_FP6 && NT == 4) many = (M + 2 * K1_ROWS - 1) / (2 * K1_ROWS) > svdq::device_cu_count();
     if (many && smem1 + red1 <= 160 * 1024)
       return launch_k1_kernel<ACT, NT, QM, 2>(x, smooth_inv, lora_down, M, K, rank, x_codes, x_scales, lora_act,
                                               smem1 + red1, st);
