@@ -558,23 +558,33 @@ __global__ __launch_bounds__(F_THREADS, 1) void k_gemm_w4a4_fp6(
         const int gd = 4 * tnc + g;
         const bool live = gd < Gd && row < Mpd;               // uniform over the lane pair
         unsigned char* tr = T + rl * C_TS + 2 * (GROUP * g + 32 * hh);
+        const float4* sp = reinterpret_cast<const float4*>(si_s + GROUP * g + 32 * hh);
+        // every value is formed unconditionally (a per-value row test
+        // compiles to one branch per value, which serializes the GELU's
+        // exp2 and reciprocal); rows past M are zeroed through the scale
         float xh[32];
 #pragma unroll
         for (int c8 = 0; c8 < 4; ++c8) {
           const uint4 u = *reinterpret_cast<const uint4*>(tr + 16 * c8);
+          const float4 s0 = sp[2 * c8], s1 = sp[2 * c8 + 1];
           const uint32_t w[4] = {u.x, u.y, u.z, u.w};
+          const float sv[8] = {s0.x, s0.y, s0.z, s0.w, s1.x, s1.y, s1.z, s1.w};
 #pragma unroll
           for (int i = 0; i < 4; ++i) {
             const int j = 8 * c8 + 2 * i;
-            const int kc = GROUP * g + 32 * hh + j;
-            xh[j] = row < M ? gelu_tanh(bf16_bits_to_f32(w[i] & 0xFFFFu)) * si_s[kc] : 0.f;
-            xh[j + 1] = row < M ? gelu_tanh(bf16_bits_to_f32(w[i] >> 16)) * si_s[kc + 1] : 0.f;
+            xh[j] = gelu_tanh(bf16_bits_to_f32(w[i] & 0xFFFFu)) * sv[2 * i];
+            xh[j + 1] = gelu_tanh(bf16_bits_to_f32(w[i] >> 16)) * sv[2 * i + 1];
           }
         }
         float amax = 0.f;
 #pragma unroll
         for (int j = 0; j < 32; ++j) amax = fmaxf(amax, fabsf(xh[j]));
         amax = fmaxf(amax, __shfl_xor(amax, 1));
+        // Rows M .. Mp - 1 (their staged values are the bias alone, finite):
+        // scale 0 makes every code +0 below, as kernel 1 writes such rows.
+        // Their bf16(x_hat) left in the staging tile only reaches the down
+        // projection's rows past M, which are not stored.
+        if (row >= M) amax = 0.f;
         const float s32 = amax / 7.0f;
         const _Float16 sh = static_cast<_Float16>(s32);
         const float sf = static_cast<float>(sh);
