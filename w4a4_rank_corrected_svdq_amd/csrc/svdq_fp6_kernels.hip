@@ -208,7 +208,8 @@ __device__ __forceinline__ float sum32(float v) {
   v += __builtin_bit_cast(float, __builtin_amdgcn_ds_swizzle(__builtin_bit_cast(int, v), 0x401F));
   return v;
 }
-static_assert(F_BM * C_TS <= F_NS * F_SLOT, "the chain's staging tile fits the idle ring");
+static_assert((F_BM + 32) * C_TS <= F_NS * F_SLOT,
+              "the chain's staging tile and a 32-rank L1 slice fit the idle ring");
 
 // EPI: 0 store Y, 1 the MLP chain's epilogue, 2 the fused QKV epilogue.
 template <int OUT_F32, int EPI>
@@ -509,9 +510,10 @@ __global__ __launch_bounds__(F_THREADS, 1) void k_gemm_w4a4_fp6(
   // takes two (row, group of 64) pairs through tanh-GELU, the next layer's
   // smoothing and INT4 quantizer -- the arithmetic of kernel 1 -- writes
   // their codes into the 6-bit containers and their fp16 scales, and puts
-  // bf16(x_hat) back in place (E2); each wave then forms 32 rows of the
-  // tile's partial down projection, bf16(x_hat) [256 x 256] L1 slice, on
-  // bf16 MFMA (E3).  Rows M .. Mp - 1 get zero codes and scales, as kernel 1
+  // bf16(x_hat) back in place (E2); the block then stages the tile's
+  // 32-rank slice of L1 in the ring past the staging tile, and each wave
+  // forms 32 rows of the tile's partial down projection, bf16(x_hat)
+  // [256 x 256] L1 slice, on bf16 MFMA with both operands from LDS (E3).  Rows M .. Mp - 1 get zero codes and scales, as kernel 1
   // writes them; rows and groups past the operands are not written.
   auto chain_epilogue = [&](int tt) {
     if constexpr (EPI == 1) {
@@ -544,6 +546,31 @@ __global__ __launch_bounds__(F_THREADS, 1) void k_gemm_w4a4_fp6(
         }
       }
       __syncthreads();
+      // The tile's slice of L1^T, ranks rc .. rc + 31 by its 256 k, goes to
+      // the ring past the staging tile (row stride C_TS, so that the 16
+      // ranks one MFMA operand read touches fall on distinct banks): two
+      // coalesced 16-byte chunks per thread, ranks past the rank and k past
+      // N as zeros.  The first slice's loads are issued after E2's loop, so
+      // their latency overlaps the barrier that closes E2.
+      unsigned char* Ls = T + F_BM * C_TS;
+      auto l1_load = [&](int rc, uint4 (&v)[2]) {
+#pragma unroll
+        for (int j = 0; j < 2; ++j) {
+          const int f = tid + F_THREADS * j;
+          const int rr = rc + (f >> 5), kg = F_BN * tnc + 8 * (f & 31);
+          const bool ok = rr < ca.rank && kg < N;
+          v[j] = *reinterpret_cast<const uint4*>(ca.lora_down + static_cast<size_t>(ok ? rr : 0) * N + (ok ? kg : 0));
+          if (!ok) v[j] = make_uint4(0, 0, 0, 0);
+        }
+      };
+      auto l1_store = [&](const uint4 (&v)[2]) {
+#pragma unroll
+        for (int j = 0; j < 2; ++j) {
+          const int f = tid + F_THREADS * j;
+          *reinterpret_cast<uint4*>(Ls + (f >> 5) * C_TS + 16 * (f & 31)) = v[j];
+        }
+      };
+      uint4 lv[2];
       const int RBd = (M + 31) >> 5, Mpd = RBd << 5;
       const int Gd = N / GROUP;
       // units of 32 values: (row, group, half hh) = p >> 3, (p >> 1) & 3, p & 1,
@@ -612,38 +639,33 @@ __global__ __launch_bounds__(F_THREADS, 1) void k_gemm_w4a4_fp6(
               make_uint4(bf16x2_bits(xh[8 * c8], xh[8 * c8 + 1]), bf16x2_bits(xh[8 * c8 + 2], xh[8 * c8 + 3]),
                          bf16x2_bits(xh[8 * c8 + 4], xh[8 * c8 + 5]), bf16x2_bits(xh[8 * c8 + 6], xh[8 * c8 + 7]));
       }
+      if (ca.rank > 0) l1_load(0, lv);
       __syncthreads();
       if (ca.rank > 0) {
+        l1_store(lv);
+        __syncthreads();
         // A = 8 bf16(x_hat) of row 32 w + l % 32 at k = 16 kk + 8 (l / 32);
-        // B = the same k of L1^T row (rank) rc + l % 32; D lane l: rank
-        // rc + l % 32, rows 8 b + 4 (l / 32) + i of the wave's 32
+        // B = the same k of the staged L1^T row (rank) rc + l % 32; D lane
+        // l: rank rc + l % 32, rows 8 b + 4 (l / 32) + i of the wave's 32
         const int ln = fresh_lane();
         const int lc = ln & 31, lh = ln >> 5;
         const int rl = 32 * wave + lc;
 #pragma unroll 1
         for (int rc = 0; rc < ca.rank; rc += 32) {
+          if (rc > 0) {
+            l1_load(rc, lv);
+            __syncthreads();                                  // every wave is past the previous slice
+            l1_store(lv);
+            __syncthreads();
+          }
           const int rr = rc + lc;
-          // the slice's sixteen L1 fragments in two batches of eight, each
-          // requested before its MFMAs (at clamped in-bounds addresses,
-          // masked afterwards)
-          const bool rok = rr < ca.rank;
-          const uint16_t* lrow = ca.lora_down + static_cast<size_t>(rok ? rr : 0) * N;
           v16f d = zero;
-#pragma unroll 1
-          for (int k0 = 0; k0 < F_BN / 16; k0 += 8) {
-            uint4 bw[8];
-#pragma unroll
-            for (int q = 0; q < 8; ++q) {
-              const int kg = F_BN * tnc + 16 * (k0 + q) + 8 * lh;
-              bw[q] = *reinterpret_cast<const uint4*>(lrow + (kg < N ? kg : 0));
-              if (!rok || kg >= N) bw[q] = make_uint4(0, 0, 0, 0);
-            }
-#pragma unroll
-            for (int q = 0; q < 8; ++q) {
-              const int kl = 16 * (k0 + q) + 8 * lh;
-              const v8bf av = __builtin_bit_cast(v8bf, *reinterpret_cast<const uint4*>(T + rl * C_TS + 2 * kl));
-              d = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av, __builtin_bit_cast(v8bf, bw[q]), d, 0, 0, 0);
-            }
+#pragma unroll 8
+          for (int kk = 0; kk < F_BN / 16; ++kk) {
+            const int kl = 16 * kk + 8 * lh;
+            const v8bf av = __builtin_bit_cast(v8bf, *reinterpret_cast<const uint4*>(T + rl * C_TS + 2 * kl));
+            const v8bf bv = __builtin_bit_cast(v8bf, *reinterpret_cast<const uint4*>(Ls + lc * C_TS + 2 * kl));
+            d = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av, bv, d, 0, 0, 0);
           }
           if (rr < ca.rank) {
 #pragma unroll
